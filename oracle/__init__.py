@@ -1,0 +1,342 @@
+"""CPU oracle for the block-quantized MoE expert matmul -- TEST INFRASTRUCTURE.
+
+This package is the plain, slow, obviously-correct reference that the HIP path
+is checked against.  Only the tests, the smoke entry point and the benchmark's
+CPU-baseline leg may import it; the product path never calls it, and it shares
+no code with the HIP library (it decodes the on-disk blocks itself, it does not
+use the library's block splitter).
+
+Precision: every weight is decoded to fp32 by the format's formula (exact for
+every format, see each decoder), widened to fp64, and contracted in fp64.
+Output roundings to fp16 / bf16 are round-to-nearest-even written out below.
+
+Sources (web pages the method is described on):
+  [GGUF]  "feat(gguf,dsv4): GGUF block-dequant + DSv4 kernel surface (WIP)",
+          PR body sections "Design -- CPU-side decomposition" and "Kernels"
+          items 1-3, and the follow-up commit that fixes IQ2_XXS sign
+          reconstruction (two lookup tables).
+  [DSV4]  "metal: DSV4 M1 Ultra prefill/decode campaign", PR body (tiled MoE
+          prefill GEMM, q2_K SoA down twin, sum-folded q2_K down projection)
+          and the review-fix commit (moe_mm_id AoS qs base at 84*blk+16).
+  [BAGEL] "Everything Bagel 2", commits on the scalar-FMA top-K accumulator,
+          the GPU MoE router top-K and the expert-indexed int4 GEMV
+          ([nExperts, outDim, inDim/8] u32 weights with scales and biases),
+          and the fused swiglu commit (silu(g) * u).
+  [SHIM]  "WIP: metaltile shim -- Qwen3.6 mt_qmm_mma / mt_moe_gather dispatch
+          from VLLMBridge", PR body (dense qmm smoke cell M=32 N=256 K=2048).
+
+Readings where the pages are silent (each repeated at the function):
+  * Q2_K: low nibble of a scale byte is the sub-block scale, high nibble its
+    min; element e of a super-block sits in code byte 32*(e//128) + e%32 at bit
+    2*((e%128)//32); d then dmin follow the 64 code bytes.
+  * IQ2_XXS: the 4 scale bits are the top nibble of each group's aux word and
+    the group scale is d * (0.5 + s) / 4; fp16 d leads the 66-byte block.
+  * Sign table: entry i is i with bit 7 set iff i has an odd number of set
+    bits (the "even-parity 8th sign").
+  * int4: nibble i of word w is element 8*w + i (low nibble first).
+Parity pins for every function live in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "f16_to_f64", "bf16_to_f64", "act_to_f64", "round_f16", "round_bf16",
+    "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
+    "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
+    "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
+]
+
+# ---------------------------------------------------------------------------
+# scalar storage formats
+# ---------------------------------------------------------------------------
+
+def f16_to_f64(bits) -> np.ndarray:
+    """fp16 bit patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact): bf16 is the top half of an fp32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def act_to_f64(bits, dtype: str) -> np.ndarray:
+    return f16_to_f64(bits) if dtype == "f16" else bf16_to_f64(bits)
+
+
+def round_f16(v) -> np.ndarray:
+    """fp32/fp64 -> fp16 bit patterns, IEEE round to nearest even, subnormals kept."""
+    return np.asarray(v, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def round_bf16(v) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even; NaN stays NaN."""
+    f = np.asarray(v, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(f)
+    r[nan] = ((u[nan] >> 16).astype(np.uint16) | np.uint16(0x0040))
+    return r
+
+
+def round_out(v, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return round_f16(v)
+    if dtype == "bf16":
+        return round_bf16(v)
+    return np.asarray(v, dtype=np.float32)
+
+
+def out_to_f64(a, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    return act_to_f64(a, dtype)
+
+
+# ---------------------------------------------------------------------------
+# block formats -> fp32  [GGUF "Kernels" 1-3]
+# ---------------------------------------------------------------------------
+
+def _f16_field(blocks: np.ndarray, off: int) -> np.ndarray:
+    """fp16 little-endian field at byte offset `off` of every block, as fp32."""
+    b = np.ascontiguousarray(blocks[..., off:off + 2])
+    return b.view("<u2")[..., 0].view(np.float16).astype(np.float32)
+
+
+def dequant_q8_0(blocks: np.ndarray) -> np.ndarray:
+    """Q8_0 [GGUF "Kernels" 1]: 32 signed bytes share one scale;
+    value = code * scale.  On disk the fp16 scale precedes the 32 codes.
+    code * scale is exact in fp32 (8 x 11 significant bits).
+    blocks: uint8 [..., 34] -> fp32 [..., 32]."""
+    d = _f16_field(blocks, 0)
+    q = np.ascontiguousarray(blocks[..., 2:34]).view(np.int8).astype(np.float32)
+    return q * d[..., None]
+
+
+def dequant_q2_k(blocks: np.ndarray) -> np.ndarray:
+    """Q2_K [GGUF "Kernels" 2; DSV4 review fix: codes at byte 16 of 84]:
+    a 256-value super-block of 16 sub-blocks of 16 values.  Sub-block s has a
+    4-bit scale a_s (low nibble of byte s) and a 4-bit min m_s (high nibble);
+    the super-block has fp16 d and dmin.  value = (d*a_s)*q - (dmin*m_s) with the
+    2-bit code q of element e at code byte 32*(e//128) + e%32, bit 2*((e%128)//32).
+    d*a*q and dmin*m are exact in fp32, so only the subtraction rounds.
+    blocks: uint8 [..., 84] -> fp32 [..., 256]."""
+    sc = blocks[..., 0:16]
+    codes = blocks[..., 16:80]
+    d = _f16_field(blocks, 80)
+    dmin = _f16_field(blocks, 82)
+    e = np.arange(256)
+    byte = codes[..., 32 * (e // 128) + (e % 32)]
+    q = ((byte >> (2 * ((e % 128) // 32)).astype(np.uint8)) & 3).astype(np.float32)
+    sub = sc[..., e // 16]
+    a = (sub & 15).astype(np.float32)
+    m = (sub >> 4).astype(np.float32)
+    dl = d[..., None] * a
+    ml = dmin[..., None] * m
+    return dl * q - ml
+
+
+def iq2_signs() -> np.ndarray:
+    """The 128-entry IQ2_XXS sign-mask table [GGUF IQ2_XXS sign-fix commit]:
+    entry i keeps the 7 stored sign bits and adds an 8th sign bit so that the
+    number of negated values in the octet is even.  uint8 [128]."""
+    out = np.zeros(128, dtype=np.uint8)
+    for i in range(128):
+        ones = bin(i).count("1")
+        out[i] = i | ((ones % 2) << 7)
+    return out
+
+
+def dequant_iq2_xxs(blocks: np.ndarray, grid: np.ndarray, signs: np.ndarray | None = None) -> np.ndarray:
+    """IQ2_XXS [GGUF "Kernels" 3 and the sign-fix commit]: a 256-value
+    super-block with fp16 d, then 8 groups of 32 values.  Each group stores 4
+    grid-index bytes and a u32 aux word.  Octet j of the group takes its 8
+    magnitudes from grid row idx_j; its sign mask is signs[(aux >> 7j) & 127]
+    and bit l of the mask negates element l of the octet.  The group scale is
+    d * (0.5 + (aux >> 28)) / 4 (reading: top nibble of aux holds the scale).
+    d*(0.5+s)/4 * g is exact in fp32 (11 + 5 + 8 significant bits).
+    blocks: uint8 [..., 66] -> fp32 [..., 256]."""
+    if signs is None:
+        signs = iq2_signs()
+    d = _f16_field(blocks, 0)
+    grp = np.ascontiguousarray(blocks[..., 2:66]).reshape(blocks.shape[:-1] + (8, 8))
+    idx = grp[..., 0:4]                                     # [..., 8, 4]
+    aux = np.ascontiguousarray(grp[..., 4:8]).view("<u4")[..., 0].astype(np.uint32)  # [..., 8]
+    s = (aux >> 28).astype(np.float32)
+    db = d[..., None] * (np.float32(0.5) + s) * np.float32(0.25)   # [..., 8]
+    mag = grid[idx].astype(np.float32)                      # [..., 8, 4, 8]
+    j = np.arange(4, dtype=np.uint32)
+    field_ = (aux[..., None] >> (7 * j)) & 127              # [..., 8, 4]
+    mask = signs[field_]                                    # [..., 8, 4]
+    lbit = (mask[..., None] >> np.arange(8, dtype=np.uint8)) & 1   # [..., 8, 4, 8]
+    sgn = np.where(lbit == 1, np.float32(-1.0), np.float32(1.0))
+    w = db[..., None, None] * mag * sgn
+    return w.reshape(blocks.shape[:-1] + (256,))
+
+
+def dequant_int4(qs: np.ndarray, scale: np.ndarray, bias: np.ndarray, group: int) -> np.ndarray:
+    """int4 affine [BAGEL expert-indexed int4 GEMV commit: stacked
+    [nExperts, outDim, inDim/8] u32 weights plus per-group scales and biases]:
+    value = s * q + b per group of `group` values along K; nibble i of word w
+    is element 8w + i (reading: low nibble first).  s*q is exact in fp32, the
+    +b rounds once.  qs uint32 [..., K/8]; scale/bias fp16 bits [..., K/group]
+    -> fp32 [..., K]."""
+    K = qs.shape[-1] * 8
+    sh = (4 * np.arange(8, dtype=np.uint32))
+    q = ((qs[..., :, None] >> sh) & 15).astype(np.float32).reshape(qs.shape[:-1] + (K,))
+    s = np.asarray(scale, np.uint16).view(np.float16).astype(np.float32)
+    b = np.asarray(bias, np.uint16).view(np.float16).astype(np.float32)
+    s = np.repeat(s, group, axis=-1)
+    b = np.repeat(b, group, axis=-1)
+    return s * q + b
+
+
+def dequant(W) -> np.ndarray:
+    """Whole weight tensor (a synth.QWeights) -> fp32 [E, N, K]."""
+    if W.fmt == "int4":
+        return dequant_int4(W.qs, W.scale, W.bias, W.group)
+    if W.fmt == "q8_0":
+        v = dequant_q8_0(W.blocks)
+    elif W.fmt == "q2_k":
+        v = dequant_q2_k(W.blocks)
+    elif W.fmt == "iq2_xxs":
+        v = dequant_iq2_xxs(W.blocks, W.grid)
+    else:
+        raise ValueError(W.fmt)
+    return v.reshape(W.E, W.N, W.K)
+
+
+def dequant_rows(W, e: int, rows) -> np.ndarray:
+    """fp32 [len(rows), K] for expert e's given output rows."""
+    return dequant(W.expert_rows(e, rows))[0]
+
+
+# ---------------------------------------------------------------------------
+# matmuls
+# ---------------------------------------------------------------------------
+
+def qmm(x64: np.ndarray, W, e: int = 0) -> np.ndarray:
+    """Dense quantised matmul [SHIM dense qmm cell]: y = x . W[e]^T in fp64.
+    x64: fp64 [M, K]."""
+    return x64 @ dequant(W)[e].astype(np.float64).T
+
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) in fp64 [BAGEL fused swiglu commit]."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def plan(ids: np.ndarray, n_experts: int, bm: int):
+    """Expert-sorted routing plan [DSV4 PR body: the map0 work queue that
+    feeds tiles of routed tokens to the MoE prefill GEMM].
+
+    Pair p = t*k + j of ids[T, k].  Pairs whose id is outside [0, E) are dropped
+    and counted.  Pairs are listed expert by expert, ascending pair id within an
+    expert; each expert's run is cut into tiles of at most `bm` rows.
+    Returns dict(dropped, counts[E], offsets[E+1], sorted[P_valid],
+    tiles[n_tiles, 3] of (expert, row0, nrows))."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    valid = (flat >= 0) & (flat < n_experts)
+    counts = np.zeros(n_experts, dtype=np.int64)
+    buckets: list[list[int]] = [[] for _ in range(n_experts)]
+    for p in np.nonzero(valid)[0]:
+        buckets[flat[p]].append(int(p))
+        counts[flat[p]] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_ = np.array([p for b in buckets for p in b], dtype=np.int64)
+    tiles = []
+    for e in range(n_experts):
+        for r in range(0, int(counts[e]), bm):
+            tiles.append((e, int(offsets[e]) + r, min(bm, int(counts[e]) - r)))
+    return dict(dropped=int((~valid).sum()), counts=counts, offsets=offsets,
+                sorted=sorted_, tiles=np.array(tiles, dtype=np.int64).reshape(-1, 3))
+
+
+def _by_expert(ids: np.ndarray, E: int):
+    flat = np.asarray(ids).reshape(-1)
+    for e in range(E):
+        pairs = np.nonzero(flat == e)[0]
+        if len(pairs):
+            yield e, pairs
+
+
+def moe_gate_up(x64: np.ndarray, ids: np.ndarray, Wgu) -> np.ndarray:
+    """Gate/up stage for every routed pair p = t*k + j, e = ids[t, j]:
+    g = x_t . Wg[e]^T, u = x_t . Wu[e]^T (Wg = rows 0..I-1 and Wu = rows I..2I-1
+    of the fused weight), h_p = silu(g) * u.  fp64 [P, I] in pair order."""
+    T, k = ids.shape
+    I = Wgu.N // 2
+    h = np.zeros((T * k, I))
+    for e, pairs in _by_expert(ids, Wgu.E):
+        W = dequant_rows(Wgu, e, np.arange(Wgu.N)).astype(np.float64)
+        gu = x64[pairs // k] @ W.T
+        h[pairs] = silu(gu[:, :I]) * gu[:, I:]
+    return h
+
+
+def moe_down_combine(h64: np.ndarray, ids: np.ndarray, w: np.ndarray, Wd) -> np.ndarray:
+    """Down stage plus weighted combine [DSV4 sum-folded q2_K down; BAGEL
+    scalar-FMA top-K accumulator]: out_t = sum_j w[t,j] * (h_{t,j} . Wd[e]^T),
+    j ascending.  h64 fp64 [P, I] in pair order -> fp64 [T, H]."""
+    T, k = ids.shape
+    y = np.zeros((T * k, Wd.N))
+    for e, pairs in _by_expert(ids, Wd.E):
+        W = dequant_rows(Wd, e, np.arange(Wd.N)).astype(np.float64)
+        y[pairs] = h64[pairs] @ W.T
+    y = y.reshape(T, k, Wd.N)
+    out = np.zeros((T, Wd.N))
+    for j in range(k):
+        out += np.asarray(w, np.float64)[:, j, None] * y[:, j]
+    return out
+
+
+def moe_ffn(x64, ids, w, Wgu, Wd, h_dtype: str | None = None, shared=None):
+    """Whole MoE FFN.  If h_dtype is given, h is rounded to that storage dtype
+    between the two GEMMs (the storage point of the GPU path).  `shared` is an
+    optional (gate_up, down) pair of dense weights added with weight 1."""
+    h = moe_gate_up(x64, ids, Wgu)
+    if h_dtype is not None:
+        h = out_to_f64(round_out(h, h_dtype), h_dtype)
+    out = moe_down_combine(h, ids, w, Wd)
+    if shared is not None:
+        sgu, sd = shared
+        I = sgu.N // 2
+        gu = qmm(x64, sgu)
+        hs = silu(gu[:, :I]) * gu[:, I:]
+        if h_dtype is not None:
+            hs = out_to_f64(round_out(hs, h_dtype), h_dtype)
+        out = out + qmm(hs, sd)
+    return out
+
+
+def moe_gate_up_rows(x64, ids, Wgu, pairs, cols) -> np.ndarray:
+    """h[p, c] for selected pairs and columns only (for full-size sampling)."""
+    k = ids.shape[1]
+    I = Wgu.N // 2
+    cols = np.asarray(cols)
+    out = np.zeros((len(pairs), len(cols)))
+    for i, p in enumerate(pairs):
+        e = int(ids.reshape(-1)[p])
+        W = dequant_rows(Wgu, e, np.concatenate([cols, cols + I])).astype(np.float64)
+        gu = W @ x64[p // k]
+        out[i] = silu(gu[:len(cols)]) * gu[len(cols):]
+    return out
+
+
+def moe_down_rows(h64_pairs: dict, ids, w, Wd, tokens, cols) -> np.ndarray:
+    """out[t, c] for selected tokens and columns; h64_pairs maps pair id ->
+    fp64 [I] (the h the down stage consumed)."""
+    k = ids.shape[1]
+    cols = np.asarray(cols)
+    out = np.zeros((len(tokens), len(cols)))
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            e = int(ids[t, j])
+            W = dequant_rows(Wd, e, cols).astype(np.float64)
+            out[i] += np.float64(w[t, j]) * (W @ h64_pairs[t * k + j])
+    return out
