@@ -1,0 +1,298 @@
+"""Benchmark of the block-quantized MoE expert matmul on one MI355X.
+
+Step (the timed unit): one pass of the whole prefill MoE hot path over the
+Qwen3.6-A3B-shaped int4 workload -- routing plan, gathered gate/up GEMM with
+the SwiGLU epilogue, gathered down GEMM with the top-k weighted scatter-add,
+and the final cast -- for T = 2048 tokens, hidden 2048, 256 experts, top-8,
+expert intermediate 512, bf16 activations, int4 affine weights (group 64).
+The weights rotate over R copies so no step finds them in the 256 MB
+Infinity Cache.  `value` is algorithmic TFLOP/s of that step (routed pairs
+only; padding is not counted).
+
+The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers of weights rotated)
+and the CPU oracle baseline are reported in the same JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16 = 2.5166e15   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+PEAK_HBM = 8.0e12            # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def act_tensor(torch, bits):
+    """uint16 bf16 bit patterns -> a bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def upload(qm, W):
+    if W.fmt == "int4":
+        return qm.upload("int4", W.E, W.N, W.K, qs=W.qs, scale=W.scale, bias=W.bias, group=W.group)
+    return qm.upload(W.fmt, W.E, W.N, W.K, blocks=W.blocks, grid=W.grid)
+
+
+def prefill_inputs(T):
+    import synth
+    return synth.qwen_a3b_prefill(T)
+
+
+def algorithmic(inp):
+    """Flops and bytes of one prefill step (routed pairs only)."""
+    P = int(inp.ids.size)
+    H, I = inp.H, inp.I
+    flops_gu = 2.0 * P * (2 * I) * H
+    flops_dn = 2.0 * P * H * I
+    wbytes_gu = inp.w_gate_up.nbytes
+    wbytes_dn = inp.w_down.nbytes
+    act = 2  # bf16
+    bytes_gu = wbytes_gu + inp.T * H * act + P * I * act    # weights + x read + h write
+    bytes_dn = wbytes_dn + P * I * act + inp.T * H * act    # weights + h read + out write
+    return dict(P=P, flops=flops_gu + flops_dn, flops_gu=flops_gu, flops_dn=flops_dn,
+                bytes=bytes_gu + bytes_dn, bytes_gu=bytes_gu, bytes_dn=bytes_dn)
+
+
+def run_prefill(args, torch, qm):
+    inp = prefill_inputs(2048)
+    alg = algorithmic(inp)
+    dev = "cuda"
+    x = act_tensor(torch, inp.x)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
+    R = args.rotate
+    gus = [gu0] + [gu0.clone() for _ in range(R - 1)]
+    dns = [dn0] + [dn0.clone() for _ in range(R - 1)]
+    T, k, E, I = inp.T, inp.k, inp.E, inp.I
+    bm = 128
+    plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    acc = torch.zeros((T, inp.H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, inp.H), dtype=torch.bfloat16, device=dev)
+    n_valid = T * k
+
+    ev = {name: [] for name in ("plan", "gate_up", "down", "cast")}
+
+    def step(i, timed):
+        gu, dn = gus[i % R], dns[i % R]
+        marks = []
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
+        qm.moe_plan(ids, E, bm, plan=plan)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
+        qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
+        qm.moe_gather_qmm(dn, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, topk_w=w,
+                          epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
+        qm.combine_cast(acc, qm.BF16, out=out)
+        if timed:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
+        return marks
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # untimed-overhead-free pass: wall clock over K steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, False)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # per-kernel durations (events on the launch stream) over another K steps
+    all_marks = [step(i, True) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for m in all_marks:
+        for j, name in enumerate(("plan", "gate_up", "down", "cast")):
+            ev[name].append(m[j].elapsed_time(m[j + 1]) * 1e-3)
+    kern = {n: float(np.median(v)) for n, v in ev.items()}
+    return inp, alg, wall, kern
+
+
+def run_decode(args, torch, qm, B, layers):
+    import synth
+    inp = synth.qwen_a3b_decode(B)
+    dev = "cuda"
+    x = act_tensor(torch, inp.x)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
+    gus = [gu0] + [gu0.clone() for _ in range(layers - 1)]
+    dns = [dn0] + [dn0.clone() for _ in range(layers - 1)]
+    h = torch.empty((B, inp.k, inp.I), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, inp.H), dtype=torch.bfloat16, device=dev)
+    uniq = np.unique(inp.ids)
+    per_expert = (inp.w_gate_up.nbytes + inp.w_down.nbytes) // inp.E
+    nbytes = len(uniq) * per_expert + B * inp.H * 2 * 2 + B * inp.k * inp.I * 2 * 2
+    for _ in range(2):
+        for l in range(layers):
+            qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
+            qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+    torch.cuda.synchronize()
+    reps = max(1, args.decode_reps)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for l in range(layers):
+            qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
+            qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / (reps * layers)
+    # kernel durations with events around each launch
+    marks = []
+    for l in range(layers):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
+        e[1].record()
+        qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+        e[2].record()
+        marks.append(e)
+    torch.cuda.synchronize()
+    t_gu = float(np.median([m[0].elapsed_time(m[1]) for m in marks])) * 1e-3
+    t_dn = float(np.median([m[1].elapsed_time(m[2]) for m in marks])) * 1e-3
+    del gus, dns
+    torch.cuda.empty_cache()
+    return dict(B=B, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
+                kernel_s=t_gu + t_dn, gate_up_s=t_gu, down_s=t_dn, wall_s_per_layer=wall,
+                GBps_kernels=nbytes / (t_gu + t_dn) / 1e9,
+                hbm_frac_kernels=nbytes / (t_gu + t_dn) / PEAK_HBM,
+                GBps_wall=nbytes / wall / 1e9, tokens_per_s_per_layer=B / wall)
+
+
+def cpu_baseline(n_tokens):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    the full MoE FFN (gate/up + SwiGLU, down, weighted combine) for the first
+    n_tokens tokens, in fp64."""
+    import oracle
+    inp = prefill_inputs(2048)
+    ids = inp.ids[:n_tokens]
+    w = inp.w[:n_tokens]
+    x64 = oracle.act_to_f64(inp.x[:n_tokens], "bf16")
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.moe_ffn(x64, ids, w, inp.w_gate_up, inp.w_down, h_dtype="bf16")
+    dt = time.perf_counter() - t0
+    P = ids.size
+    flops = 2.0 * P * (3 * inp.I * inp.H)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"first {n_tokens} of 2048 tokens ({P} routed pairs) of the prefill workload, "
+                       f"fp64 oracle, {dt:.1f} s", tokens_per_s=n_tokens / dt, seconds=dt)
+
+
+def traffic_from_profiles():
+    """HBM bytes per gate/up launch measured with rocprofv3 counters, if the
+    committed measurement matches the current kernel source."""
+    import hashlib
+    p = os.path.join(ROOT, "profiles", "gate_up_qwen_prefill_traffic.json")
+    src = os.path.join(ROOT, "block_quantized_moe_amd", "csrc", "gemm.hip")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return rec.get("bytes_per_launch") if rec.get("gemm_sha256") == h else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--decode-layers", type=int, default=40)
+    ap.add_argument("--decode-reps", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU layout is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_quantized_moe_amd as qm
+
+    qm.check_device()
+    log("prefill: building inputs")
+    inp, alg, wall, kern = run_prefill(args, torch, qm)
+    t_step = wall
+    value = alg["flops"] / t_step / 1e12
+    t_gu = kern["gate_up"]
+    roofline = {
+        "kernel": "qmm_kernel<INT4, bf16, SWIGLU> (gate/up)",
+        "bound": "hbm",
+        "achieved": alg["bytes_gu"] / t_gu / 1e9,
+        "peak": PEAK_HBM / 1e9,
+        "unit": "GB/s",
+        "frac": alg["bytes_gu"] / t_gu / PEAK_HBM,
+        "traffic": traffic_from_profiles(),
+        "algorithmic_bytes_per_launch": alg["bytes_gu"],
+        "launch_s": t_gu,
+        "mfma_tflops": alg["flops_gu"] / t_gu / 1e12,
+        "mfma_frac": alg["flops_gu"] / t_gu / PEAK_MFMA_BF16,
+    }
+    log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; kernels {json.dumps(kern)}")
+    decode = []
+    if not args.no_decode:
+        for B in (1, 4, 8):
+            log(f"decode: B={B}")
+            decode.append(run_decode(args, torch, qm, B, args.decode_layers))
+            log(json.dumps(decode[-1]))
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline: oracle sample")
+        cpu = cpu_baseline(args.cpu_tokens)
+    line = {
+        "metric": "MoE qGEMM prefill TFLOP/s (% MFMA peak) + decode GEMV GB/s (% HBM peak)",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3.6-a3b-shaped int4 MoE prefill", "tokens": inp.T, "hidden": inp.H,
+                   "experts": inp.E, "top_k": inp.k, "intermediate": inp.I,
+                   "weights": "int4 affine, group 64, fp16 scale+bias", "activations": "bf16",
+                   "weight_copies_rotated": args.rotate},
+        "mfma_frac": value * 1e12 / PEAK_MFMA_BF16,
+        "tokens_per_s": inp.T / t_step,
+        "kernels_s": kern,
+        "algorithmic": {"flops": alg["flops"], "bytes": alg["bytes"]},
+        "roofline": roofline,
+        "decode": [{"B": d["B"], "GBps": d["GBps_kernels"], "hbm_frac": d["hbm_frac_kernels"],
+                    "GBps_wall": d["GBps_wall"], "us_per_layer_kernels": d["kernel_s"] * 1e6,
+                    "us_per_layer_wall": d["wall_s_per_layer"] * 1e6, "unique_experts": d["unique_experts"],
+                    "bytes_per_layer": d["bytes_per_layer"]} for d in decode],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,360 @@
+"""Python binding of libqmoe (the block-quantized MoE expert matmul for MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libqmoe.so,
+called through its C ABI (include/qmoe.h).  PyTorch provides device memory and
+the current stream.  There is no fallback: if the library is missing, or the
+device is not gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmoe.so")
+
+# enums mirrored from include/qmoe.h
+F32, F16, BF16 = 0, 1, 2
+Q8_0, Q2_K, IQ2_XXS, INT4 = 0, 1, 2, 3
+EPI_STORE, EPI_SWIGLU, EPI_WEIGHTED_COMBINE, EPI_ACCUMULATE = 0, 1, 2, 3
+A_GATHER_TOKENS, A_SORTED_ROWS = 0, 1
+FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4}
+MAX_TOPK, MAX_EXPERTS, MAX_GEMV_BATCH = 8, 1024, 64
+
+
+class QmoeError(RuntimeError):
+    pass
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("qs", ctypes.c_void_p), ("aux", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+        ("d", ctypes.c_void_p), ("dmin", ctypes.c_void_p),
+        ("grid", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+_SIGS = {
+    "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
+    "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 4,
+    "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3,
+    "qmoe_split_int4": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p],
+    "qmoe_iq2_signs_table": [ctypes.c_void_p],
+    "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_q2_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_iq2_xxs": [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_qmm_dense": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_plan_bytes": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
+    "qmoe_moe_plan": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
+    "qmoe_moe_gather_qmm": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_moe_combine": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_combine_cast": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_moe_gemv": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_check_device": [],
+    "qmoe_strerror": [ctypes.c_int],
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded libqmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QmoeError(f"libqmoe.so not built ({LIB_PATH}); run python -m block_quantized_moe_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.qmoe_plan_bytes.restype = ctypes.c_size_t
+        L.qmoe_strerror.restype = ctypes.c_char_p
+        L.qmoe_iq2_signs_table.restype = None
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise QmoeError(f"{what}: {lib().qmoe_strerror(status).decode()} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _np_ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ---------------------------------------------------------------------------
+# host-side split (C functions of the library)
+# ---------------------------------------------------------------------------
+
+def split_q8_0(aos: np.ndarray):
+    aos = np.ascontiguousarray(aos, dtype=np.uint8)
+    nb = aos.size // 34
+    qs = np.empty(nb * 32, np.int8)
+    d = np.empty(nb, np.uint16)
+    _check(lib().qmoe_split_q8_0(_np_ptr(aos), nb, _np_ptr(qs), _np_ptr(d)), "split_q8_0")
+    return qs, d
+
+
+def split_q2_k(aos: np.ndarray):
+    aos = np.ascontiguousarray(aos, dtype=np.uint8)
+    nb = aos.size // 84
+    qs = np.empty(nb * 16, np.uint32)
+    sc = np.empty(nb * 16, np.uint8)
+    d = np.empty(nb, np.uint16)
+    dmin = np.empty(nb, np.uint16)
+    _check(lib().qmoe_split_q2_k(_np_ptr(aos), nb, _np_ptr(qs), _np_ptr(sc), _np_ptr(d), _np_ptr(dmin)), "split_q2_k")
+    return qs, sc, d, dmin
+
+
+def split_iq2_xxs(aos: np.ndarray):
+    aos = np.ascontiguousarray(aos, dtype=np.uint8)
+    nb = aos.size // 66
+    idx = np.empty(nb * 8, np.uint32)
+    aux = np.empty(nb * 8, np.uint32)
+    d = np.empty(nb, np.uint16)
+    _check(lib().qmoe_split_iq2_xxs(_np_ptr(aos), nb, _np_ptr(idx), _np_ptr(aux), _np_ptr(d)), "split_iq2_xxs")
+    return idx, aux, d
+
+
+def split_int4(words: np.ndarray) -> np.ndarray:
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    out = np.empty_like(words)
+    _check(lib().qmoe_split_int4(_np_ptr(words), words.size, _np_ptr(out)), "split_int4")
+    return out
+
+
+def iq2_signs_table() -> np.ndarray:
+    out = np.zeros(128, np.uint8)
+    lib().qmoe_iq2_signs_table(_np_ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# device weights
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DeviceWeights:
+    """A stacked expert weight tensor in its GPU-resident split form."""
+    fmt: str
+    E: int
+    N: int
+    K: int
+    group: int = 0
+    tensors: dict = field(default_factory=dict)
+
+    def struct(self) -> _Weights:
+        t = self.tensors
+        return _Weights(FORMATS[self.fmt], self.E, self.N, self.K, self.group, 0,
+                        _ptr(t.get("qs")), _ptr(t.get("aux")), _ptr(t.get("scales")),
+                        _ptr(t.get("biases")), _ptr(t.get("d")), _ptr(t.get("dmin")),
+                        _ptr(t.get("grid")), _ptr(t.get("signs")))
+
+    @property
+    def nbytes(self) -> int:
+        return int(sum(v.numel() * v.element_size() for k, v in self.tensors.items() if k not in ("grid", "signs")))
+
+    def clone(self) -> "DeviceWeights":
+        return DeviceWeights(self.fmt, self.E, self.N, self.K, self.group,
+                             {k: (v if k in ("grid", "signs") else v.clone()) for k, v in self.tensors.items()})
+
+
+def _dev(a: np.ndarray, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=None, scale=None,
+           bias=None, group: int = 0, grid=None) -> DeviceWeights:
+    """Split on-disk weights on the host (library splitter) and copy them to the device.
+
+    blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs.
+    qs, scale, bias: MLX-style int4 arrays for int4.  grid: uint8 [256, 8] (iq2_xxs)."""
+    t = {}
+    if fmt == "q8_0":
+        q, d = split_q8_0(blocks)
+        t["qs"], t["scales"] = _dev(q, device), _dev(d, device)
+    elif fmt == "q2_k":
+        q, sc, d, dmin = split_q2_k(blocks)
+        t["qs"], t["scales"], t["d"], t["dmin"] = (_dev(q, device), _dev(sc, device), _dev(d, device), _dev(dmin, device))
+    elif fmt == "iq2_xxs":
+        idx, aux, d = split_iq2_xxs(blocks)
+        t["qs"], t["aux"], t["d"] = _dev(idx, device), _dev(aux, device), _dev(d, device)
+        t["grid"] = _dev(np.ascontiguousarray(grid, np.uint8).reshape(-1), device)
+        t["signs"] = _dev(iq2_signs_table(), device)
+    elif fmt == "int4":
+        t["qs"] = _dev(split_int4(qs.reshape(-1)), device)
+        t["scales"] = _dev(np.asarray(scale, np.uint16).reshape(-1), device)
+        t["biases"] = _dev(np.asarray(bias, np.uint16).reshape(-1), device)
+    else:
+        raise ValueError(fmt)
+    return DeviceWeights(fmt, E, N, K, group, t)
+
+
+# ---------------------------------------------------------------------------
+# compute entry points (same names as the C ABI, without the qmoe_ prefix)
+# ---------------------------------------------------------------------------
+
+_TORCH_DT = {}
+
+
+def _dt(code):
+    import torch
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[code]
+
+
+def _code(t):
+    import torch
+    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}[t.dtype]
+
+
+def check_device():
+    _check(lib().qmoe_check_device(), "check_device")
+
+
+def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
+    """Whole weight tensor -> dense [E, N, K] on the device (bit-exact)."""
+    import torch
+    if out is None:
+        out = torch.empty((w.E, w.N, w.K), dtype=_dt(out_dtype), device=w.tensors["qs"].device)
+    t = w.tensors
+    L = lib()
+    s = _stream()
+    if w.fmt == "q8_0":
+        st = L.qmoe_dequant_q8_0(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N * w.K // 32, _ptr(out), out_dtype, s)
+    elif w.fmt == "q2_k":
+        st = L.qmoe_dequant_q2_k(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["d"]), _ptr(t["dmin"]),
+                                 w.E * w.N * w.K // 256, _ptr(out), out_dtype, s)
+    elif w.fmt == "iq2_xxs":
+        st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["aux"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
+                                    w.E * w.N * w.K // 256, _ptr(out), out_dtype, s)
+    else:
+        st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["biases"]), w.E * w.N, w.K, w.group,
+                                 _ptr(out), out_dtype, s)
+    _check(st, f"dequant_{w.fmt}")
+    return out
+
+
+def qmm_dense(w: DeviceWeights, x, epilogue: int = EPI_STORE, out_dtype: int = F16, out=None):
+    import torch
+    M = x.shape[0]
+    if out is None:
+        n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+        out = torch.empty((M, n), dtype=_dt(out_dtype), device=x.device)
+    ws = w.struct()
+    _check(lib().qmoe_qmm_dense(ctypes.byref(ws), _ptr(x), _code(x), M, epilogue, _ptr(out), _code(out), _stream()),
+           "qmm_dense")
+    return out
+
+
+def plan_bytes(t: int, topk: int, E: int, bm: int) -> int:
+    return int(lib().qmoe_plan_bytes(t, topk, E, bm))
+
+
+def moe_plan(ids, E: int, bm: int = 128, plan=None):
+    import torch
+    T, k = ids.shape
+    nbytes = plan_bytes(T, k, E, bm)
+    if plan is None:
+        plan = torch.empty(nbytes // 4, dtype=torch.int32, device=ids.device)
+    _check(lib().qmoe_moe_plan(_ptr(ids), T, k, E, bm, _ptr(plan), plan.numel() * 4, _stream()), "moe_plan")
+    return plan
+
+
+def plan_views(plan, T: int, topk: int, E: int):
+    """Named views of a plan buffer (layout in include/qmoe.h)."""
+    P = T * topk
+    counts = 8
+    offsets = counts + E
+    sorted_ = offsets + E + 1
+    tiles = (sorted_ + P + 3) & ~3
+    max_tiles16 = min(P, E) + P // 16
+    inv = tiles + 4 * max_tiles16
+    return dict(header=plan[:8], counts=plan[counts:counts + E], offsets=plan[offsets:offsets + E + 1],
+                sorted=plan[sorted_:sorted_ + P], tiles=plan[tiles:tiles + 4 * max_tiles16].view(-1, 4),
+                inv=plan[inv:inv + P])
+
+
+def moe_gather_qmm(w: DeviceWeights, plan, T: int, topk: int, a, *, bm: int = 128,
+                   a_mode: int = A_GATHER_TOKENS, topk_w=None, epilogue: int = EPI_STORE,
+                   out_dtype: int = None, out=None, n_rows: int = None):
+    """Gathered MoE matmul.  For STORE / SWIGLU the output has one row per
+    sorted position (n_rows = number of valid pairs, default T * topk)."""
+    import torch
+    if out is None:
+        if epilogue == EPI_WEIGHTED_COMBINE:
+            out = torch.zeros((T, w.N), dtype=torch.float32, device=a.device)
+        else:
+            rows = T * topk if n_rows is None else n_rows
+            n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+            out = torch.empty((rows, n), dtype=_dt(out_dtype if out_dtype is not None else _code(a)), device=a.device)
+    ws = w.struct()
+    _check(lib().qmoe_moe_gather_qmm(ctypes.byref(ws), _ptr(plan), T, topk, bm, _ptr(a), _code(a), a_mode,
+                                     _ptr(topk_w), epilogue, _ptr(out), _code(out), _stream()), "moe_gather_qmm")
+    return out
+
+
+def moe_combine(y, plan, T: int, topk: int, E: int, topk_w, base=None, out_dtype: int = BF16, out=None):
+    import torch
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=_dt(out_dtype), device=y.device)
+    _check(lib().qmoe_moe_combine(_ptr(y), _code(y), _ptr(plan), T, topk, E, _ptr(topk_w), N, _ptr(base),
+                                  _ptr(out), _code(out), _stream()), "moe_combine")
+    return out
+
+
+def combine_cast(acc, out_dtype: int = BF16, out=None):
+    import torch
+    if out is None:
+        out = torch.empty(acc.shape, dtype=_dt(out_dtype), device=acc.device)
+    _check(lib().qmoe_combine_cast(_ptr(acc), acc.numel(), _ptr(out), _code(out), _stream()), "combine_cast")
+    return out
+
+
+def moe_gemv(w: DeviceWeights, a, ids, topk_w=None, *, epilogue: int = EPI_SWIGLU,
+             out_dtype: int = None, out=None):
+    """Decode GEMV.  STORE/SWIGLU: a = x [B, K] -> [B, topk, N or N/2];
+    WEIGHTED_COMBINE: a = h [B, topk, K] -> [B, N]."""
+    import torch
+    B, topk = ids.shape
+    od = out_dtype if out_dtype is not None else _code(a)
+    if out is None:
+        if epilogue == EPI_WEIGHTED_COMBINE:
+            out = torch.empty((B, w.N), dtype=_dt(od), device=a.device)
+        else:
+            n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+            out = torch.empty((B, topk, n), dtype=_dt(od), device=a.device)
+    ws = w.struct()
+    _check(lib().qmoe_moe_gemv(ctypes.byref(ws), _ptr(a), _code(a), B, _ptr(ids), _ptr(topk_w), topk, epilogue,
+                               _ptr(out), _code(out), _stream()), "moe_gemv")
+    return out

@@ -1,0 +1,308 @@
+// C ABI of libqmoe: argument validation on the host, then kernel launches on
+// the caller's stream.  Contracts are checked before any launch and reported
+// as status codes (the DSV4 campaign page's review fix moves such contracts to
+// host-checked launchers instead of silent zeros); nothing here synchronises
+// or allocates.
+#include <string.h>
+
+#include <atomic>
+
+#include "common.h"
+
+namespace qmoe {
+void launch_dequant_q8_0(const int8_t*, const uint16_t*, int64_t, void*, int, hipStream_t);
+void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const uint16_t*, int64_t,
+                         void*, int, hipStream_t);
+void launch_dequant_iq2_xxs(const uint32_t*, const uint32_t*, const uint16_t*, const uint8_t*,
+                            const uint8_t*, int64_t, void*, int, hipStream_t);
+void launch_dequant_int4(const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t, int,
+                         void*, int, hipStream_t);
+void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
+void launch_qmm(const qmoe_weights*, const void*, int, int, const int32_t*, int64_t, int, int,
+                int64_t, const float*, int, void*, int, hipStream_t);
+void launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
+                 int, void*, int, hipStream_t);
+void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
+void launch_moe_combine(const void*, int, const int32_t*, int64_t, int, int, const float*, int64_t,
+                        const float*, void*, int, hipStream_t);
+}  // namespace qmoe
+
+using namespace qmoe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_arch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QMOE_ERR_ARCH;
+  if (dev < 0 || dev >= kMaxDevices) return QMOE_ERR_ARCH;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return QMOE_ERR_ARCH;
+    v = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? QMOE_OK : QMOE_ERR_ARCH;
+}
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+inline bool dtype_ok(int d) { return d == QMOE_F32 || d == QMOE_F16 || d == QMOE_BF16; }
+inline bool act_ok(int d) { return d == QMOE_F16 || d == QMOE_BF16; }
+
+int launched() {
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_LAUNCH;
+}
+
+// Shared validation of a weight descriptor.  need_k64: matmul entry points
+// stage k in 64-wide tiles.
+int check_weights(const qmoe_weights* w, bool need_k64) {
+  if (!w) return QMOE_ERR_ARG;
+  if (w->n_experts < 1 || w->n < 1 || w->k < 1) return QMOE_ERR_ARG;
+  if (w->n_experts > QMOE_MAX_EXPERTS) return QMOE_ERR_LIMIT;
+  if (w->n > (1ll << 30) || w->k > (1ll << 24)) return QMOE_ERR_LIMIT;
+  if (need_k64 && w->k % 64) return QMOE_ERR_BLOCK;
+  if (!w->qs || !al16(w->qs)) return w->qs ? QMOE_ERR_ALIGN : QMOE_ERR_ARG;
+  switch (w->fmt) {
+    case QMOE_Q8_0:
+      if (w->k % 32) return QMOE_ERR_BLOCK;
+      if (!w->scales) return QMOE_ERR_ARG;
+      if (!al16(w->scales)) return QMOE_ERR_ALIGN;
+      break;
+    case QMOE_Q2_K:
+      if (w->k % 256) return QMOE_ERR_BLOCK;
+      if (!w->scales || !w->d || !w->dmin) return QMOE_ERR_ARG;
+      if (!al16(w->scales) || !al16(w->d) || !al16(w->dmin)) return QMOE_ERR_ALIGN;
+      break;
+    case QMOE_IQ2_XXS:
+      if (w->k % 256) return QMOE_ERR_BLOCK;
+      if (!w->aux || !w->d || !w->grid || !w->signs) return QMOE_ERR_ARG;
+      if (!al16(w->aux) || !al16(w->d) || !al16(w->grid) || !al16(w->signs)) return QMOE_ERR_ALIGN;
+      break;
+    case QMOE_INT4:
+      if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
+      if (w->k % w->group) return QMOE_ERR_BLOCK;
+      if (!w->scales || !w->biases) return QMOE_ERR_ARG;
+      if (!al16(w->scales) || !al16(w->biases)) return QMOE_ERR_ALIGN;
+      break;
+    default:
+      return QMOE_ERR_UNSUPPORTED;
+  }
+  return QMOE_OK;
+}
+
+}  // namespace
+
+#define QMOE_TRY(expr)            \
+  do {                            \
+    const int _st = (expr);       \
+    if (_st != QMOE_OK) return _st; \
+  } while (0)
+
+extern "C" {
+
+int qmoe_check_device(void) { return check_arch(); }
+
+const char* qmoe_strerror(int status) {
+  switch (status) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_ARG: return "invalid argument (NULL pointer, negative size or bad enum)";
+    case QMOE_ERR_UNSUPPORTED: return "unsupported format / dtype / epilogue combination";
+    case QMOE_ERR_BLOCK: return "size is not a multiple of the format block";
+    case QMOE_ERR_LIMIT: return "size limit exceeded (topk, experts, batch or dimension)";
+    case QMOE_ERR_WORKSPACE: return "plan or workspace buffer too small";
+    case QMOE_ERR_ALIGN: return "pointer not aligned as required";
+    case QMOE_ERR_ARCH: return "current HIP device is not gfx950";
+    case QMOE_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ dequant
+
+int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, void* out,
+                      int32_t out_dtype, void* stream) {
+  if (!qs || !d || !out || n_blocks < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (!al16(qs) || !al16(d) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (n_blocks == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_q8_0(qs, d, n_blocks, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t* d,
+                      const uint16_t* dmin, int64_t n_blocks, void* out, int32_t out_dtype,
+                      void* stream) {
+  if (!qs || !scales || !d || !dmin || !out || n_blocks < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (!al16(qs) || !al16(scales) || !al16(d) || !al16(dmin) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (n_blocks == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_q2_k(qs, scales, d, dmin, n_blocks, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
+                         const uint8_t* grid, const uint8_t* signs, int64_t n_blocks, void* out,
+                         int32_t out_dtype, void* stream) {
+  if (!idx || !aux || !d || !grid || !signs || !out || n_blocks < 0 || !dtype_ok(out_dtype))
+    return QMOE_ERR_ARG;
+  if (!al16(idx) || !al16(aux) || !al16(d) || !al16(grid) || !al16(signs) || !al16(out))
+    return QMOE_ERR_ALIGN;
+  if (n_blocks == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_iq2_xxs(idx, aux, d, grid, signs, n_blocks, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_int4(const uint32_t* qs, const uint16_t* scales, const uint16_t* biases,
+                      int64_t rows, int64_t k, int32_t group, void* out, int32_t out_dtype,
+                      void* stream) {
+  if (!qs || !scales || !biases || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (!(group == 32 || group == 64 || group == 128 || group == 256) || k % group) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(scales) || !al16(biases) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_int4(qs, scales, biases, rows, k, group, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+// ------------------------------------------------------------------ dense qmm
+
+int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int64_t m,
+                   int32_t epilogue, void* out, int32_t out_dtype, void* stream) {
+  QMOE_TRY(check_weights(w, true));
+  if (!x || !out || m < 0 || !act_ok(act_dtype) || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (w->n_experts != 1) return QMOE_ERR_ARG;
+  if (epilogue == QMOE_EPI_SWIGLU) {
+    if (w->n % 2) return QMOE_ERR_ARG;
+  } else if (epilogue == QMOE_EPI_ACCUMULATE) {
+    if (out_dtype != QMOE_F32) return QMOE_ERR_UNSUPPORTED;
+  } else if (epilogue != QMOE_EPI_STORE) {
+    return QMOE_ERR_UNSUPPORTED;
+  }
+  if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->group % 64) return QMOE_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (m > (1ll << 31) - 1) return QMOE_ERR_LIMIT;
+  if (m == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_qmm(w, x, act_dtype, 2 /*dense*/, nullptr, 0, 1, 128, m, nullptr, epilogue, out, out_dtype,
+             (hipStream_t)stream);
+  return launched();
+}
+
+// ------------------------------------------------------------------ plan
+
+size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm) {
+  (void)bm;
+  if (t < 0 || topk < 1 || n_experts < 1) return 0;
+  return (size_t)plan_layout(t * topk, n_experts).total * sizeof(int32_t);
+}
+
+static bool bm_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts, int32_t bm,
+                  int32_t* plan, size_t plan_bytes, void* stream) {
+  if (!ids || !plan || t < 0 || topk < 1 || n_experts < 1) return QMOE_ERR_ARG;
+  if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS) return QMOE_ERR_LIMIT;
+  if (t * topk > (1ll << 30)) return QMOE_ERR_LIMIT;
+  if (!bm_ok(bm)) return QMOE_ERR_ARG;
+  if (!al4(ids) || !al16(plan)) return QMOE_ERR_ALIGN;
+  if (plan_bytes < qmoe_plan_bytes(t, topk, n_experts, bm)) return QMOE_ERR_WORKSPACE;
+  QMOE_TRY(check_arch());
+  if (t == 0) return QMOE_OK;
+  launch_plan(ids, t, topk, n_experts, bm, plan, (hipStream_t)stream);
+  return launched();
+}
+
+// ------------------------------------------------------------------ gathered MoE qmm
+
+int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
+                        int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
+                        const float* topk_w, int32_t epilogue, void* out, int32_t out_dtype,
+                        void* stream) {
+  QMOE_TRY(check_weights(w, true));
+  if (!plan || !a || !out || t < 0 || topk < 1 || !act_ok(act_dtype) || !dtype_ok(out_dtype))
+    return QMOE_ERR_ARG;
+  if (topk > QMOE_MAX_TOPK) return QMOE_ERR_LIMIT;
+  if (t * topk > (1ll << 30)) return QMOE_ERR_LIMIT;
+  if (!bm_ok(bm)) return QMOE_ERR_ARG;
+  if (a_mode != QMOE_A_GATHER_TOKENS && a_mode != QMOE_A_SORTED_ROWS) return QMOE_ERR_ARG;
+  if (epilogue == QMOE_EPI_SWIGLU) {
+    if (w->n % 2) return QMOE_ERR_ARG;
+  } else if (epilogue == QMOE_EPI_WEIGHTED_COMBINE) {
+    if (!topk_w) return QMOE_ERR_ARG;
+    if (out_dtype != QMOE_F32) return QMOE_ERR_UNSUPPORTED;
+    if (!al4(topk_w)) return QMOE_ERR_ALIGN;
+  } else if (epilogue != QMOE_EPI_STORE) {
+    return QMOE_ERR_UNSUPPORTED;
+  }
+  if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->group % 64) return QMOE_ERR_UNSUPPORTED;
+  if (!al16(plan) || !al16(a) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (t == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_qmm(w, a, act_dtype, a_mode == QMOE_A_GATHER_TOKENS ? 0 : 1, plan, t, topk, bm, 0, topk_w,
+             epilogue, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t, int32_t topk,
+                     int32_t n_experts, const float* topk_w, int64_t n, const float* base, void* out,
+                     int32_t out_dtype, void* stream) {
+  if (!y || !plan || !topk_w || !out || t < 0 || n < 0 || topk < 1 || n_experts < 1) return QMOE_ERR_ARG;
+  if (!dtype_ok(y_dtype) || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS) return QMOE_ERR_LIMIT;
+  if (t * topk > (1ll << 30) || ((n + 255) / 256) * t > (1ll << 31) - 1) return QMOE_ERR_LIMIT;
+  if (!al16(y) || !al16(plan) || !al4(topk_w) || !al16(out) || (base && !al4(base))) return QMOE_ERR_ALIGN;
+  if (t == 0 || n == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_moe_combine(y, y_dtype, plan, t, topk, n_experts, topk_w, n, base, out, out_dtype,
+                     (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype, void* stream) {
+  if (!acc || !out || n_elems < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (!al16(acc) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (n_elems == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_combine_cast(acc, n_elems, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+// ------------------------------------------------------------------ decode GEMV
+
+int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64_t b,
+                  const int32_t* ids, const float* topk_w, int32_t topk, int32_t epilogue,
+                  void* out, int32_t out_dtype, void* stream) {
+  QMOE_TRY(check_weights(w, false));
+  if (!a || !ids || !out || b < 0 || topk < 1 || !act_ok(act_dtype) || !dtype_ok(out_dtype))
+    return QMOE_ERR_ARG;
+  if (topk > QMOE_MAX_TOPK || b > QMOE_MAX_GEMV_BATCH) return QMOE_ERR_LIMIT;
+  if (w->k % 32) return QMOE_ERR_BLOCK;
+  if (w->k > 4096) return QMOE_ERR_LIMIT;
+  {
+    // lanes per row must be a power of two: k/32 in {1, 2, 4, ..., 64} or 128 (two chunks per lane)
+    const int64_t c = w->k / 32;
+    if (c & (c - 1)) return QMOE_ERR_BLOCK;
+  }
+  if (epilogue == QMOE_EPI_SWIGLU) {
+    if (w->n % 2) return QMOE_ERR_ARG;
+  } else if (epilogue == QMOE_EPI_WEIGHTED_COMBINE) {
+    if (!topk_w) return QMOE_ERR_ARG;
+    if (!al4(topk_w)) return QMOE_ERR_ALIGN;
+    if (w->n > (1ll << 31) / 64) return QMOE_ERR_LIMIT;
+    if (w->k < 512) return QMOE_ERR_UNSUPPORTED;  // at most 4 rows per wave pass
+  } else if (epilogue != QMOE_EPI_STORE) {
+    return QMOE_ERR_UNSUPPORTED;
+  }
+  if (!al16(a) || !al4(ids) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (b == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_gemv(w, a, act_dtype, b, ids, topk_w, topk, epilogue, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+}  // extern "C"

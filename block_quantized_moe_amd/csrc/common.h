@@ -1,0 +1,130 @@
+// Shared device helpers of the qmoe HIP library (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+enum { ACT_F16 = 0, ACT_BF16 = 1 };
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+template <int ACT>
+__device__ __forceinline__ float act_to_f32(uint32_t bits) {
+  if constexpr (ACT == ACT_F16) return f16_to_f32(bits);
+  else return bf16_to_f32(bits);
+}
+// fp32 -> fp16, round to nearest even (hardware conversion; fp16 denormals kept).
+// The empty asm keeps the fp32 value opaque: otherwise a preceding multiply is
+// folded into a mixed-precision fma with a +0 addend, which turns a -0
+// product into +0.
+__device__ __forceinline__ uint16_t f32_to_f16(float v) {
+  asm("" : "+v"(v));
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ void store_out(void* out, int dtype, int64_t i, float v) {
+  if (dtype == QMOE_F32) ((float*)out)[i] = v;
+  else if (dtype == QMOE_F16) ((uint16_t*)out)[i] = f32_to_f16(v);
+  else ((uint16_t*)out)[i] = f32_to_bf16(v);
+}
+template <int OUT>
+__device__ __forceinline__ void store_out_t(void* out, int64_t i, float v) {
+  if constexpr (OUT == QMOE_F32) ((float*)out)[i] = v;
+  else if constexpr (OUT == QMOE_F16) ((uint16_t*)out)[i] = f32_to_f16(v);
+  else ((uint16_t*)out)[i] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
+// (selector 0..3 -> lo, 4..7 -> hi, 12 -> 0x00).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_{f16,bf16}: D[16x16] += A[16x32] * B[32x16].  Lane l
+// supplies row (l % 16) of A and column (l % 16) of B, eight k-values each for
+// the k-slot group (l / 16); D element (4 * (l / 16) + r, l % 16) is acc[r].
+__device__ __forceinline__ f4_t mfma(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4_t mfma(b8_t a, b8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int ACT> struct ActT;
+template <> struct ActT<ACT_F16> { typedef h8_t v8; typedef h2_t v2; };
+template <> struct ActT<ACT_BF16> { typedef b8_t v8; typedef b2_t v2; };
+
+template <int ACT>
+__device__ __forceinline__ typename ActT<ACT>::v8 as_v8(u4_t u) {
+  return __builtin_bit_cast(typename ActT<ACT>::v8, u);
+}
+
+// 2-element dot products with fp32 accumulation (v_dot2_f32_{f16,bf16}).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, int act) {
+  if (act == ACT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
+}
+template <int ACT>
+__device__ __forceinline__ float dot2t(uint32_t a, uint32_t b, float c) {
+  if constexpr (ACT == ACT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
+}
+
+// Blocks of a launch are dealt to the 8 XCDs round-robin.  Renumber them so
+// that consecutive virtual ids run on the same XCD (and share its L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return xcd * q + (xcd < r ? xcd : r) + slot;
+}
+
+// Plan buffer layout (int32 words), see qmoe_moe_plan in qmoe.h.  The tile
+// array is sized for the smallest tile height (16), so the layout does not
+// depend on bm.
+struct PlanLayout {
+  int64_t counts, offsets, sorted, tiles, inv, total;
+};
+__host__ __device__ inline int64_t plan_max_tiles(int64_t P, int E, int bm) {
+  return (P < E ? P : E) + P / bm;
+}
+__host__ __device__ inline PlanLayout plan_layout(int64_t P, int E) {
+  PlanLayout L;
+  L.counts = 8;
+  L.offsets = L.counts + E;
+  L.sorted = L.offsets + E + 1;
+  L.tiles = (L.sorted + P + 3) & ~(int64_t)3;
+  L.inv = L.tiles + 4 * plan_max_tiles(P, E, 16);
+  L.total = L.inv + P;
+  return L;
+}
+
+}  // namespace qmoe

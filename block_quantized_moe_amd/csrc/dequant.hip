@@ -1,0 +1,176 @@
+// Standalone dequantisation kernels (bit-exact).
+//
+// Formats as the GGUF block-dequant page defines them ("Kernels" 1-3 and the
+// IQ2_XXS sign-fix commit) plus the MLX-style int4 affine slabs of the
+// "Everything Bagel 2" expert-indexed GEMV.  Each value is formed in fp32 as
+// the format defines it -- every product there is exact in fp32, so at most
+// one rounding (the Q2_K subtraction, the int4 bias add) happens -- and is then
+// rounded once, to nearest even, to the output dtype.  One thread decodes one
+// 8-value unit and writes it with a single 16-byte (32-byte for fp32) store.
+#include "common.h"
+
+namespace qmoe {
+
+template <int OUT>
+__device__ __forceinline__ void store8(void* out, int64_t u, const float (&v)[8]) {
+  if constexpr (OUT == QMOE_F32) {
+    f4_t* o = (f4_t*)out + 2 * u;
+    o[0] = f4_t{v[0], v[1], v[2], v[3]};
+    o[1] = f4_t{v[4], v[5], v[6], v[7]};
+  } else {
+    u4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
+      if constexpr (OUT == QMOE_F16) { lo = f32_to_f16(v[2 * i]); hi = f32_to_f16(v[2 * i + 1]); }
+      else { lo = f32_to_bf16(v[2 * i]); hi = f32_to_bf16(v[2 * i + 1]); }
+      w[i] = lo | (hi << 16);
+    }
+    ((u4_t*)out)[u] = w;
+  }
+}
+
+// Q8_0: value = code * d over 32-value blocks.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restrict__ qs,
+                                                           const uint16_t* __restrict__ d,
+                                                           int64_t n_units, void* __restrict__ out) {
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const u2_t q = ((const u2_t*)qs)[u];
+    const float s = f16_to_f32(d[u >> 2]);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int8_t c = (int8_t)((q[i >> 2] >> (8 * (i & 3))) & 0xFF);
+      v[i] = (float)c * s;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
+// Q2_K: value = (d * a) * q - dmin * m with the sub-block's scale a (low
+// nibble) and min m (high nibble); element e's 2-bit code is in code byte
+// 32*(e/128) + e%32 at bit 2*((e%128)/32).
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_q2_k_kernel(const uint32_t* __restrict__ qs,
+                                                           const uint8_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ d,
+                                                           const uint16_t* __restrict__ dmin,
+                                                           int64_t n_units, void* __restrict__ out) {
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t b = u >> 5;
+    const int p = (int)(u & 31);            // elements 8p .. 8p+7 of the block
+    const int byte0 = 32 * (p >> 4) + 8 * (p & 3);
+    const int shift = 2 * ((p & 15) >> 2);
+    const u2_t q = *(const u2_t*)(qs + b * 16 + (byte0 >> 2));
+    const uint32_t s = sc[b * 16 + (p >> 1)];
+    const float dl = f16_to_f32(d[b]) * (float)(s & 15u);
+    const float ml = f16_to_f32(dmin[b]) * (float)(s >> 4);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (q[i >> 2] >> (8 * (i & 3) + shift)) & 3u;
+      v[i] = dl * (float)c - ml;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
+// IQ2_XXS: octet j of group g takes magnitudes grid[idx_j][0..7], signs from
+// signs[(aux >> 7j) & 127] (bit l negates element l), scale d*(0.5+aux>>28)/4.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_iq2_xxs_kernel(const uint32_t* __restrict__ idx,
+                                                              const uint32_t* __restrict__ aux,
+                                                              const uint16_t* __restrict__ d,
+                                                              const uint8_t* __restrict__ grid,
+                                                              const uint8_t* __restrict__ signs,
+                                                              int64_t n_units, void* __restrict__ out) {
+  __shared__ uint8_t lgrid[2048];
+  __shared__ uint8_t lsign[128];
+  for (int i = threadIdx.x; i < 512; i += 256) ((uint32_t*)lgrid)[i] = ((const uint32_t*)grid)[i];
+  if (threadIdx.x < 32) ((uint32_t*)lsign)[threadIdx.x] = ((const uint32_t*)signs)[threadIdx.x];
+  __syncthreads();
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t b = u >> 5;
+    const int p = (int)(u & 31);
+    const int g = p >> 2, j = p & 3;
+    const uint32_t ix = (idx[b * 8 + g] >> (8 * j)) & 0xFFu;
+    const uint32_t a = aux[b * 8 + g];
+    const uint32_t mask = lsign[(a >> (7 * j)) & 127u];
+    const float db = f16_to_f32(d[b]) * (0.5f + (float)(a >> 28)) * 0.25f;
+    float v[8];
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const float m = db * (float)lgrid[ix * 8 + l];
+      v[l] = ((mask >> l) & 1u) ? -m : m;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
+// int4 affine: value = s * q + b per group; GPU nibble order (see qmoe.h).
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ qs,
+                                                           const uint16_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ bi,
+                                                           int64_t n_units, int64_t words_per_row,
+                                                           int group, void* __restrict__ out) {
+  const int64_t groups_per_row = words_per_row * 8 / group;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t r = u / words_per_row;
+    const int64_t w = u - r * words_per_row;
+    const uint32_t word = qs[u];
+    const int64_t gi = r * groups_per_row + (w * 8) / group;
+    const float s = f16_to_f32(sc[gi]);
+    const float bb = f16_to_f32(bi[gi]);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = s * (float)((word >> (4 * i)) & 15u) + bb;
+      v[2 * i + 1] = s * (float)((word >> (4 * i + 16)) & 15u) + bb;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
+static inline unsigned grid_for(int64_t units) {
+  int64_t g = (units + 255) / 256;
+  if (g > (1 << 20)) g = 1 << 20;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+#define QMOE_DISPATCH_OUT(dtype, KERNEL, ...)                                         \
+  do {                                                                                \
+    if ((dtype) == QMOE_F32) hipLaunchKernelGGL(KERNEL<QMOE_F32>, __VA_ARGS__);       \
+    else if ((dtype) == QMOE_F16) hipLaunchKernelGGL(KERNEL<QMOE_F16>, __VA_ARGS__);  \
+    else hipLaunchKernelGGL(KERNEL<QMOE_BF16>, __VA_ARGS__);                          \
+  } while (0)
+
+void launch_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, void* out,
+                         int dtype, hipStream_t s) {
+  const int64_t units = n_blocks * 4;
+  QMOE_DISPATCH_OUT(dtype, dequant_q8_0_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, d,
+                    units, out);
+}
+void launch_dequant_q2_k(const uint32_t* qs, const uint8_t* sc, const uint16_t* d,
+                         const uint16_t* dmin, int64_t n_blocks, void* out, int dtype,
+                         hipStream_t s) {
+  const int64_t units = n_blocks * 32;
+  QMOE_DISPATCH_OUT(dtype, dequant_q2_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc,
+                    d, dmin, units, out);
+}
+void launch_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
+                            const uint8_t* grid, const uint8_t* signs, int64_t n_blocks,
+                            void* out, int dtype, hipStream_t s) {
+  const int64_t units = n_blocks * 32;
+  QMOE_DISPATCH_OUT(dtype, dequant_iq2_xxs_kernel, dim3(grid_for(units)), dim3(256), 0, s, idx,
+                    aux, d, grid, signs, units, out);
+}
+void launch_dequant_int4(const uint32_t* qs, const uint16_t* sc, const uint16_t* bi, int64_t rows,
+                         int64_t k, int group, void* out, int dtype, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_int4_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc,
+                    bi, units, k / 8, group, out);
+}
+
+}  // namespace qmoe

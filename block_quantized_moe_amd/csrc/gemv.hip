@@ -1,0 +1,453 @@
+// Decode GEMV for a handful of tokens routed to their top-k experts.
+//
+// The Everything Bagel 2 page's expert-indexed int4 GEMV reads the expert id
+// on the device to pick a slab of the stacked [nExperts, outDim, inDim/8]
+// weights; the DSV4 campaign page adds a small-batch qgemv and a "sum-folded"
+// q2_K down projection that fuses the GEMV with the top-k weighted sum.
+//
+// Two kernels, both bandwidth bound (every weight byte is read once per call):
+//  * gemv_rows_kernel (STORE / SWIGLU): one workgroup per (distinct expert,
+//    block of output rows).  A workgroup whose slot repeats an earlier slot's
+//    expert exits; the first one serves every token routed to that expert, so
+//    the weights stream once.  Lanes split K in 32-value chunks (a row of
+//    K = 2048 is one 16-byte load per lane), activations sit in registers, and
+//    dot2 instructions accumulate in fp32; a butterfly over the lanes of a row
+//    finishes each dot product.
+//  * gemv_combine_kernel (WEIGHTED_COMBINE): one workgroup per block of output
+//    rows; its four waves share out the distinct experts, each wave keeps
+//    per-token partial sums in LDS, and the waves' sums are added in a fixed
+//    order, so the result is bit-reproducible.
+// Integer codes are fed to the dot products exactly (as fp16 / bf16 values
+// with a known offset) and the per-block scale and bias are applied to the
+// fp32 partial sums.
+#include "common.h"
+
+namespace qmoe {
+
+constexpr int GV_MAXT = 4;  // tokens per pass over the weights
+
+struct GemvArgs {
+  const void* qs;
+  const void* aux;
+  const void* scales;
+  const void* biases;
+  const void* d;
+  const void* dmin;
+  const uint8_t* grid;
+  const uint8_t* signs;
+  int64_t N, K;
+  int group;
+  int E, topk, nslots;
+  const uint16_t* a;
+  const int32_t* ids;
+  const float* topk_w;
+  void* out;
+  int out_dtype;
+  int lpr;        // lanes per row (K / 32 / CPL, at most 64)
+  int units_per_wg;
+};
+
+// Activations of one 32-value chunk: 16 packed pairs plus the sums of its two
+// 16-value halves (in fp32).
+struct XChunk {
+  uint32_t p[16];
+  float s0, s1;
+};
+
+template <int ACT>
+__device__ __forceinline__ void load_x(const uint16_t* src, XChunk& x) {
+  const u4_t* v = (const u4_t*)src;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u4_t q = v[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x.p[4 * i + j] = q[j];
+      const float a = act_to_f32<ACT>(q[j] & 0xFFFFu) + act_to_f32<ACT>(q[j] >> 16);
+      if (i < 2) s0 += a; else s1 += a;
+    }
+  }
+  x.s0 = s0;
+  x.s1 = s1;
+}
+
+template <int ACT> struct Magic;
+template <> struct Magic<ACT_F16> { static constexpr uint32_t bits = 0x64006400u; static constexpr float v = 1024.f; static constexpr uint32_t byte = 0x64646464u; };
+template <> struct Magic<ACT_BF16> { static constexpr uint32_t bits = 0x43004300u; static constexpr float v = 128.f; static constexpr uint32_t byte = 0x43434343u; };
+
+// Exact conversion of four signed bytes to two packed pairs (fp16 or bf16).
+template <int ACT>
+__device__ __forceinline__ void i8x4_pairs(uint32_t w, uint32_t& p0, uint32_t& p1) {
+  uint32_t o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float lo = (float)(int8_t)((w >> (16 * h)) & 0xFFu);
+    const float hi = (float)(int8_t)((w >> (16 * h + 8)) & 0xFFu);
+    if constexpr (ACT == ACT_F16) o[h] = (uint32_t)f32_to_f16(lo) | ((uint32_t)f32_to_f16(hi) << 16);
+    else o[h] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
+  }
+  p0 = o[0];
+  p1 = o[1];
+}
+
+// Dot products of one 32-value weight chunk (global row R, chunk c) with the
+// activations of nt tokens; results added to res[].
+template <int FMT, int ACT>
+__device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t c, const XChunk* x,
+                                          int nt, float* res, const uint32_t* lut_grid,
+                                          const uint32_t* lut_sign) {
+  const int64_t K = g.K;
+  if constexpr (FMT == QMOE_INT4) {
+    const u4_t q = *(const u4_t*)((const uint32_t*)g.qs + R * (K / 8) + 4 * c);
+    const int64_t gi = R * (K / g.group) + (32 * c) / g.group;
+    const float s = f16_to_f32(((const uint16_t*)g.scales)[gi]);
+    const float b = f16_to_f32(((const uint16_t*)g.biases)[gi]);
+    uint32_t cp[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cp[4 * w + i] = ((q[w] >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
+    const float cb = b - Magic<ACT>::v * s;
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        res[t] += s * p + cb * (x[t].s0 + x[t].s1);
+      }
+    }
+  } else if constexpr (FMT == QMOE_Q8_0) {
+    const int8_t* base = (const int8_t*)g.qs + R * K + 32 * c;
+    const u4_t q0 = *(const u4_t*)base;
+    const u4_t q1 = *(const u4_t*)(base + 16);
+    const float dd = f16_to_f32(((const uint16_t*)g.scales)[R * (K / 32) + c]);
+    uint32_t cp[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      i8x4_pairs<ACT>(q0[w], cp[2 * w], cp[2 * w + 1]);
+      i8x4_pairs<ACT>(q1[w], cp[8 + 2 * w], cp[8 + 2 * w + 1]);
+    }
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        res[t] += dd * p;
+      }
+    }
+  } else if constexpr (FMT == QMOE_Q2_K) {
+    const int64_t B = R * (K / 256) + c / 8;
+    const int cc = (int)(c & 7);
+    const uint32_t* qb = (const uint32_t*)g.qs + B * 16 + 8 * (cc >> 2);
+    const u4_t q0 = *(const u4_t*)qb;
+    const u4_t q1 = *(const u4_t*)(qb + 4);
+    const uint32_t shift = 2u * (uint32_t)(cc & 3);
+    const uint32_t sc0 = ((const uint8_t*)g.scales)[B * 16 + 2 * cc];
+    const uint32_t sc1 = ((const uint8_t*)g.scales)[B * 16 + 2 * cc + 1];
+    const float d = f16_to_f32(((const uint16_t*)g.d)[B]);
+    const float dm = f16_to_f32(((const uint16_t*)g.dmin)[B]);
+    const float dl0 = d * (float)(sc0 & 15u), ml0 = dm * (float)(sc0 >> 4);
+    const float dl1 = d * (float)(sc1 & 15u), ml1 = dm * (float)(sc1 >> 4);
+    uint32_t cp[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t t0 = (q0[w] >> shift) & 0x03030303u;
+      const uint32_t t1 = (q1[w] >> shift) & 0x03030303u;
+      cp[2 * w] = perm_b32(Magic<ACT>::byte, t0, 0x04010400u) & 0xFF03FF03u;
+      cp[2 * w + 1] = perm_b32(Magic<ACT>::byte, t0, 0x04030402u) & 0xFF03FF03u;
+      cp[8 + 2 * w] = perm_b32(Magic<ACT>::byte, t1, 0x04010400u) & 0xFF03FF03u;
+      cp[8 + 2 * w + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u) & 0xFF03FF03u;
+    }
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0 = dot2t<ACT>(x[t].p[i], cp[i], p0);
+          p1 = dot2t<ACT>(x[t].p[8 + i], cp[8 + i], p1);
+        }
+        res[t] += dl0 * (p0 - Magic<ACT>::v * x[t].s0) - ml0 * x[t].s0 +
+                  dl1 * (p1 - Magic<ACT>::v * x[t].s1) - ml1 * x[t].s1;
+      }
+    }
+  } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8
+    const int64_t B = R * (K / 256) + c / 8;
+    const int G = (int)(c & 7);
+    const uint32_t idx = ((const uint32_t*)g.qs)[B * 8 + G];
+    const uint32_t aux = ((const uint32_t*)g.aux)[B * 8 + G];
+    const float db = f16_to_f32(((const uint16_t*)g.d)[B]) * (0.5f + (float)(aux >> 28)) * 0.25f;
+    uint32_t cp[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u4_t row = *(const u4_t*)(lut_grid + 4 * ((idx >> (8 * j)) & 0xFFu));
+      const u4_t msk = *(const u4_t*)(lut_sign + 4 * ((aux >> (7 * j)) & 0x7Fu));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cp[4 * j + i] = row[i] ^ msk[i];
+    }
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        res[t] += db * p;
+      }
+    }
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ void build_iq2_luts(const uint8_t* grid, const uint8_t* signs,
+                                               uint32_t* lut_grid, uint32_t* lut_sign) {
+  const int tid = threadIdx.x;
+  {
+    const u2_t b = *(const u2_t*)(grid + 8 * tid);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = b[i >> 1] >> (16 * (i & 1));
+      const float lo = (float)(w & 0xFFu), hi = (float)((w >> 8) & 0xFFu);
+      uint32_t packed;
+      if constexpr (ACT == ACT_F16) packed = (uint32_t)f32_to_f16(lo) | ((uint32_t)f32_to_f16(hi) << 16);
+      else packed = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
+      lut_grid[4 * tid + i] = packed;
+    }
+  }
+  if (tid < 128) {
+    const uint32_t m = signs[tid];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lut_sign[4 * tid + i] = (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+  }
+}
+
+// Butterfly sum over the `lpr` lanes that share a row.
+__device__ __forceinline__ float row_reduce(float v, int lpr) {
+  for (int off = lpr >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// STORE / SWIGLU.  grid = (row blocks, slots).
+template <int FMT, int ACT, int EPI, int CPL>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
+  constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
+  __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
+  __shared__ int list[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
+  __shared__ int nlist, dup;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = blockIdx.y;
+  const int e = g.ids[slot];
+  if (e < 0 || e >= g.E) return;
+  if (tid == 0) { nlist = 0; dup = 0; }
+  if constexpr (IQ2) build_iq2_luts<ACT>(g.grid, g.signs, lut_grid, lut_sign);
+  __syncthreads();
+  for (int p = tid; p < g.nslots; p += 256) {
+    if (g.ids[p] == e) {
+      if (p < slot) dup = 1;
+      else list[atomicAdd(&nlist, 1)] = p;
+    }
+  }
+  __syncthreads();
+  if (dup) return;
+  const int n = nlist;
+
+  const int lpr = g.lpr;
+  const int rpw = 64 / lpr;                 // row units per wave pass
+  const int sub = lane / lpr, li = lane % lpr;
+  const bool swiglu = (EPI == QMOE_EPI_SWIGLU);
+  const int64_t Nunits = swiglu ? g.N / 2 : g.N;
+  const int64_t u0 = (int64_t)blockIdx.x * g.units_per_wg;
+
+  for (int tb = 0; tb < n; tb += GV_MAXT) {
+    const int nt = min(GV_MAXT, n - tb);
+    XChunk x[GV_MAXT][CPL];
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        const int s2 = list[tb + t];
+        const uint16_t* xr = g.a + (int64_t)(s2 / g.topk) * g.K;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) load_x<ACT>(xr + 32 * (int64_t)(li + c * lpr), x[t][c]);
+      }
+    }
+    for (int ub = 4 * rpw * 0 + wave * rpw; ub < g.units_per_wg; ub += 4 * rpw) {
+      const int64_t unit = u0 + ub + sub;
+      const bool valid = (ub + sub < g.units_per_wg) && unit < Nunits;
+      const int64_t uc = valid ? unit : 0;
+      float r0[GV_MAXT], r1[GV_MAXT];
+#pragma unroll
+      for (int t = 0; t < GV_MAXT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
+      const int64_t Rg = (int64_t)e * g.N + uc;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        XChunk xc[GV_MAXT];
+#pragma unroll
+        for (int t = 0; t < GV_MAXT; ++t) xc[t] = x[t][c];
+        chunk_dot<FMT, ACT>(g, Rg, li + c * lpr, xc, nt, r0, lut_grid, lut_sign);
+        if (swiglu) chunk_dot<FMT, ACT>(g, Rg + g.N / 2, li + c * lpr, xc, nt, r1, lut_grid, lut_sign);
+      }
+#pragma unroll
+      for (int t = 0; t < GV_MAXT; ++t) {
+        if (t < nt) {
+          const float y0 = row_reduce(r0[t], lpr);
+          const float y1 = swiglu ? row_reduce(r1[t], lpr) : 0.f;
+          if (valid && li == 0) {
+            const int s2 = list[tb + t];
+            if (swiglu) store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, silu_f32(y0) * y1);
+            else store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, y0);
+          }
+        }
+      }
+    }
+  }
+}
+
+// WEIGHTED_COMBINE (sum-folded down projection).  grid = row blocks.
+template <int FMT, int ACT, int CPL>
+__global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
+  constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
+  __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
+  __shared__ int sid[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
+  __shared__ int first[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
+  __shared__ int dlist[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
+  __shared__ int ndist;
+  __shared__ float part[4][QMOE_MAX_GEMV_BATCH][4];  // [wave][token][row in block]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = g.nslots;
+  if constexpr (IQ2) build_iq2_luts<ACT>(g.grid, g.signs, lut_grid, lut_sign);
+  for (int p = tid; p < P; p += 256) sid[p] = g.ids[p];
+  for (int i = tid; i < 4 * QMOE_MAX_GEMV_BATCH * 4; i += 256) (&part[0][0][0])[i] = 0.f;
+  __syncthreads();
+  for (int p = tid; p < P; p += 256) {
+    const int e = sid[p];
+    int f = (e >= 0 && e < g.E);
+    for (int q = 0; q < p && f; ++q) f = (sid[q] != e);
+    first[p] = f;
+  }
+  __syncthreads();
+  if (tid == 0) {  // ordered compaction of first occurrences (P <= 512)
+    int c = 0;
+    for (int p = 0; p < P; ++p) if (first[p]) dlist[c++] = p;
+    ndist = c;
+  }
+  __syncthreads();
+
+  const int lpr = g.lpr;
+  const int rpw = 64 / lpr;
+  const int sub = lane / lpr, li = lane % lpr;
+  const int64_t n0 = (int64_t)blockIdx.x * rpw;  // a workgroup covers one wave-pass of rows
+  const int64_t row = n0 + sub;
+  const bool valid = row < g.N;
+  const int64_t rc = valid ? row : 0;
+
+  for (int di = wave; di < ndist; di += 4) {
+    const int e = sid[dlist[di]];
+    const int64_t Rg = (int64_t)e * g.N + rc;
+    // tokens routed to e, in slot order, GV_MAXT at a time
+    int pos = dlist[di];
+    while (pos < P) {
+      int sl[GV_MAXT];
+      int nt = 0;
+      while (pos < P && nt < GV_MAXT) {
+        if (sid[pos] == e) sl[nt++] = pos;
+        ++pos;
+      }
+      if (nt == 0) break;
+      float r[GV_MAXT];
+#pragma unroll
+      for (int t = 0; t < GV_MAXT; ++t) r[t] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        XChunk xc[GV_MAXT];
+#pragma unroll
+        for (int t = 0; t < GV_MAXT; ++t)
+          if (t < nt) load_x<ACT>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[t]);
+        chunk_dot<FMT, ACT>(g, Rg, li + c * lpr, xc, nt, r, lut_grid, lut_sign);
+      }
+#pragma unroll
+      for (int t = 0; t < GV_MAXT; ++t) {
+        if (t < nt) {
+          const float y = row_reduce(r[t], lpr);
+          if (li == 0) {
+            const int s2 = sl[t];
+            part[wave][s2 / g.topk][sub] += g.topk_w[s2] * y;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int btok = P / g.topk;
+  for (int i = tid; i < btok * rpw; i += 256) {
+    const int b = i / rpw, r = i % rpw;
+    const int64_t n = n0 + r;
+    if (n < g.N) {
+      const float v = ((part[0][b][r] + part[1][b][r]) + part[2][b][r]) + part[3][b][r];
+      store_out(g.out, g.out_dtype, (int64_t)b * g.N + n, v);
+    }
+  }
+}
+
+template <int FMT, int ACT, int CPL>
+static void launch_gemv_fac(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE) {
+    const int rpw = 64 / g.lpr;
+    const dim3 grid((unsigned)((g.N + rpw - 1) / rpw));
+    hipLaunchKernelGGL((gemv_combine_kernel<FMT, ACT, CPL>), grid, dim3(256), 0, s, g);
+  } else {
+    const dim3 grid((unsigned)((units_total + g.units_per_wg - 1) / g.units_per_wg), (unsigned)g.nslots);
+    if (epi == QMOE_EPI_SWIGLU)
+      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_SWIGLU, CPL>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_STORE, CPL>), grid, dim3(256), 0, s, g);
+  }
+}
+
+template <int FMT>
+static void launch_gemv_f(const GemvArgs& g, int act, int cpl, int epi, int64_t units, hipStream_t s) {
+  if (act == QMOE_F16) {
+    if (cpl == 1) launch_gemv_fac<FMT, ACT_F16, 1>(g, epi, units, s);
+    else launch_gemv_fac<FMT, ACT_F16, 2>(g, epi, units, s);
+  } else {
+    if (cpl == 1) launch_gemv_fac<FMT, ACT_BF16, 1>(g, epi, units, s);
+    else launch_gemv_fac<FMT, ACT_BF16, 2>(g, epi, units, s);
+  }
+}
+
+// Host launcher for qmoe_moe_gemv (arguments already validated; K <= 4096).
+void launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const int32_t* ids,
+                 const float* topk_w, int topk, int epi, void* out, int out_dtype, hipStream_t s) {
+  GemvArgs g;
+  g.qs = w->qs; g.aux = w->aux; g.scales = w->scales; g.biases = w->biases;
+  g.d = w->d; g.dmin = w->dmin; g.grid = w->grid; g.signs = w->signs;
+  g.N = w->n; g.K = w->k; g.group = w->group;
+  g.E = w->n_experts; g.topk = topk; g.nslots = (int)(b * topk);
+  g.a = (const uint16_t*)a; g.ids = ids; g.topk_w = topk_w;
+  g.out = out; g.out_dtype = out_dtype;
+  const int64_t chunks = w->k / 32;
+  const int cpl = chunks > 64 ? (int)(chunks / 64) : 1;
+  g.lpr = (int)(chunks / cpl);
+  const int rpw = 64 / g.lpr;
+  const int64_t units = (epi == QMOE_EPI_SWIGLU) ? w->n / 2 : w->n;
+  // Enough workgroups to cover the chip: aim for >= 512 in total.
+  int64_t upw = (units * g.nslots) / 512;
+  if (upw < 4 * rpw) upw = 4 * rpw;
+  upw = (upw + 4 * rpw - 1) / (4 * rpw) * (4 * rpw);
+  if (upw > 64) upw = 64 > 4 * rpw ? 64 : 4 * rpw;
+  g.units_per_wg = (int)upw;
+  switch (w->fmt) {
+    case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
+    case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;
+    case QMOE_IQ2_XXS: launch_gemv_f<QMOE_IQ2_XXS>(g, act, cpl, epi, units, s); break;
+    default: launch_gemv_f<QMOE_INT4>(g, act, cpl, epi, units, s); break;
+  }
+}
+
+}  // namespace qmoe

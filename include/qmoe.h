@@ -1,0 +1,256 @@
+/*
+ * qmoe.h -- C ABI of the block-quantized MoE expert matmul for MI355X (gfx950).
+ *
+ * One shared library, libqmoe.so.  Every compute entry point enqueues HIP
+ * kernels on the caller's stream and returns; nothing synchronises, nothing
+ * allocates, nothing prints, and no C++ exception crosses this boundary.
+ * All buffers are owned by the caller.  Pointers documented as DEVICE must
+ * point to device memory on the current HIP device; pointers documented as
+ * HOST are ordinary host memory.  `stream` is a hipStream_t (NULL = the
+ * default stream).
+ *
+ * Sources (web pages the method is described on):
+ *   [GGUF]  "feat(gguf,dsv4): GGUF block-dequant + DSv4 kernel surface (WIP)":
+ *           PR body, "Design -- CPU-side decomposition", "Kernels" 1-3, "Next"
+ *           item 2, and the commit fixing IQ2_XXS sign reconstruction.
+ *   [DSV4]  "metal: DSV4 M1 Ultra prefill/decode campaign": PR body (map0
+ *           work queue, 64-slot iq2_xxs tile, q2_K SoA down twin, sum-folded
+ *           q2_K down, load-time q2_K SoA repack) and the review-fix commit
+ *           (host-checked launcher contracts: <= 1024 experts, topk <= 8; the
+ *           AoS q2_K codes start at byte 16 of each 84-byte block).
+ *   [BAGEL] "Everything Bagel 2": expert-indexed int4 GEMV (ids read on the
+ *           device, [nExperts, outDim, inDim/8] u32 weights + scales + biases),
+ *           scalar-FMA top-K accumulate, fused swiglu, caller-owned scratch.
+ *   [SHIM]  "WIP: metaltile shim -- Qwen3.6 mt_qmm_mma / mt_moe_gather dispatch
+ *           from VLLMBridge": dense qmm and gathered MoE qmm, commit+wait per
+ *           dispatch capping the win (so nothing here synchronises).
+ *
+ * Status codes: every entry point returns one of the QMOE_* codes below.  All
+ * argument checks run on the host before any launch.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_OK              0
+#define QMOE_ERR_ARG        -1  /* NULL pointer, negative size, bad enum      */
+#define QMOE_ERR_UNSUPPORTED -2 /* format / dtype / epilogue combination      */
+#define QMOE_ERR_BLOCK      -3  /* K (or a count) not a multiple of the block */
+#define QMOE_ERR_LIMIT      -4  /* topk > 8, experts > 1024, size too large   */
+#define QMOE_ERR_WORKSPACE  -5  /* plan / workspace buffer too small          */
+#define QMOE_ERR_ALIGN      -6  /* pointer not aligned as documented          */
+#define QMOE_ERR_ARCH       -7  /* current device is not gfx950               */
+#define QMOE_ERR_LAUNCH     -8  /* HIP reported an error at launch            */
+
+#define QMOE_MAX_EXPERTS 1024
+#define QMOE_MAX_TOPK    8
+#define QMOE_MAX_GEMV_BATCH 64   /* decode tokens per qmoe_moe_gemv call      */
+
+typedef enum { QMOE_F32 = 0, QMOE_F16 = 1, QMOE_BF16 = 2 } qmoe_dtype;
+
+typedef enum {
+  QMOE_Q8_0 = 0,     /* 32-value blocks, one fp16 scale                 [GGUF Kernels 1] */
+  QMOE_Q2_K = 1,     /* 256-value super-blocks, 2-bit codes, 4-bit
+                        scale/min per 16, fp16 d/dmin                    [GGUF Kernels 2] */
+  QMOE_IQ2_XXS = 2,  /* 256-value super-blocks, grid index + 7-bit sign
+                        groups with an even-parity 8th sign, 4-bit scale [GGUF Kernels 3] */
+  QMOE_INT4 = 3      /* MLX-style affine int4: s*q + b per group         [BAGEL]          */
+} qmoe_format;
+
+/* Epilogues of the matmul entry points. */
+enum {
+  QMOE_EPI_STORE = 0,            /* out[row, n] = y                                  */
+  QMOE_EPI_SWIGLU = 1,           /* out[row, j] = silu(y[row, j]) * y[row, N/2 + j]  */
+  QMOE_EPI_WEIGHTED_COMBINE = 2, /* out[t, n] += w[t, j] * y[pair (t, j), n]         */
+  QMOE_EPI_ACCUMULATE = 3        /* out[row, n] += y  (fp32 out only, dense only)    */
+};
+
+/* Where the activation rows of a gathered MoE matmul come from. */
+enum {
+  QMOE_A_GATHER_TOKENS = 0,  /* row for pair p is a[p / topk, :]   (a is [t, K])     */
+  QMOE_A_SORTED_ROWS = 1     /* row for sorted position i is a[i, :] (a is [P, K])  */
+};
+
+/*
+ * A stacked expert weight tensor W[n_experts, n, k] in its GPU-resident split
+ * form, as produced from the on-disk blocks by the qmoe_split_* functions
+ * ([GGUF] "Design -- CPU-side decomposition"; [DSV4] load-time q2_K SoA
+ * repack).  Blocks run along k (the reduction dimension), so y = x . W^T.
+ * All pointers are DEVICE pointers, 16-byte aligned; fields a format does not
+ * use must be NULL.
+ *
+ *   Q8_0     qs     int8  [E, n, k]              codes
+ *            scales fp16  [E, n, k/32]           block scale d
+ *   Q2_K     qs     u32   [E, n, k/256, 16]      the 64 code bytes of a block
+ *            scales u8    [E, n, k/256, 16]      byte s: low nibble scale, high nibble min
+ *            d,dmin fp16  [E, n, k/256]
+ *   IQ2_XXS  qs     u32   [E, n, k/256, 8]       4 grid-index bytes per group of 32
+ *            aux    u32   [E, n, k/256, 8]       4 x 7 sign bits (bits 0..27), scale (28..31)
+ *            d      fp16  [E, n, k/256]
+ *            grid   u8    [256, 8]               magnitude rows
+ *            signs  u8    [128]                  sign masks (qmoe_iq2_signs_table)
+ *   INT4     qs     u32   [E, n, k/8]            GPU nibble order (qmoe_split_int4): word w
+ *                                                holds element 8w+2i in nibble i and element
+ *                                                8w+2i+1 in nibble 4+i (i = 0..3)
+ *            scales fp16  [E, n, k/group]        s
+ *            biases fp16  [E, n, k/group]        b;   value = s*q + b
+ *            group  32, 64, 128 or 256 (bf16 activations in the prefill matmul:
+ *                   64, 128 or 256)
+ */
+typedef struct qmoe_weights {
+  int32_t fmt;          /* qmoe_format                                    */
+  int32_t n_experts;    /* 1 for a dense weight                           */
+  int64_t n;            /* output rows per expert                         */
+  int64_t k;            /* reduction length                               */
+  int32_t group;        /* INT4 group size along k; ignored otherwise     */
+  int32_t reserved;
+  const void* qs;
+  const void* aux;
+  const void* scales;
+  const void* biases;
+  const void* d;
+  const void* dmin;
+  const uint8_t* grid;
+  const uint8_t* signs;
+} qmoe_weights;
+
+/* ------------------------------------------------------------------------
+ * Host-side loader split ([GGUF] "Design -- CPU-side decomposition": each
+ * on-disk block is decomposed once at load into separate GPU-resident
+ * arrays; [DSV4] load-time q2_K SoA repack).  HOST pointers; the caller
+ * uploads the outputs.  `aos` holds n_blocks consecutive on-disk blocks:
+ *   Q8_0     34 B: fp16 d, 32 int8 codes
+ *   Q2_K     84 B: 16 scale|min bytes, 64 code bytes, fp16 d, fp16 dmin
+ *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
+ * Returns QMOE_ERR_ARG on NULL / negative n_blocks.
+ * ------------------------------------------------------------------------ */
+int qmoe_split_q8_0(const void* aos, int64_t n_blocks, int8_t* qs, uint16_t* d);
+int qmoe_split_q2_k(const void* aos, int64_t n_blocks, uint32_t* qs, uint8_t* scales,
+                    uint16_t* d, uint16_t* dmin);
+int qmoe_split_iq2_xxs(const void* aos, int64_t n_blocks, uint32_t* idx, uint32_t* aux,
+                       uint16_t* d);
+/* int4 words from the on-disk (MLX) nibble order, where nibble i of word w is
+ * element 8w+i, to the GPU nibble order above (so that one mask-and-or yields
+ * two consecutive elements in the two halves of a 32-bit register). */
+int qmoe_split_int4(const uint32_t* words, int64_t n_words, uint32_t* out);
+/* The 128-entry IQ2_XXS sign-mask table ([GGUF] sign-fix commit): entry i is
+ * the 7 stored sign bits plus an 8th bit making the count of negated values
+ * even.  HOST pointer to 128 bytes. */
+void qmoe_iq2_signs_table(uint8_t out[128]);
+
+/* ------------------------------------------------------------------------
+ * Standalone dequantisation ([GGUF] "Kernels" 1-3; [BAGEL] int4 slabs).
+ * Decodes every value in fp32 exactly as the format defines it and rounds
+ * once (to nearest even) to out_dtype; results are bit-exact.  DEVICE
+ * pointers, 16-byte aligned; out holds n_blocks * block values (int4:
+ * rows * k) in the block order of the input.
+ * ------------------------------------------------------------------------ */
+int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks,
+                      void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t* d,
+                      const uint16_t* dmin, int64_t n_blocks,
+                      void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
+                         const uint8_t* grid, const uint8_t* signs, int64_t n_blocks,
+                         void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_int4(const uint32_t* qs, const uint16_t* scales, const uint16_t* biases,
+                      int64_t rows, int64_t k, int32_t group,
+                      void* out, int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dense quantised matmul ([SHIM] mt_qmm_mma; [DSV4] wide-tile q8_0 qgemm):
+ * y[m, n] = sum_k x[m, k] * W[0, n, k], fp32 accumulation.
+ *   x      DEVICE [m, k] act_dtype (QMOE_F16 or QMOE_BF16), rows contiguous
+ *   out    DEVICE; STORE: [m, n] out_dtype; SWIGLU: [m, n/2] out_dtype;
+ *          ACCUMULATE: fp32 [m, n], y is added to it
+ * Any n >= 1 is accepted (tails are masked in the kernel); w->n_experts must
+ * be 1.  m = 0 returns QMOE_OK without launching.
+ * ------------------------------------------------------------------------ */
+int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int64_t m,
+                   int32_t epilogue, void* out, int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Routing plan: the expert-sorted token gather with per-expert tiles ([DSV4]
+ * map0 work queue feeding tiles of routed tokens to the MoE GEMM; [BAGEL]
+ * ids stay on the device).
+ *
+ * ids DEVICE int32 [t, topk]; pair p = row * topk + j.  Pairs with an id
+ * outside [0, n_experts) are dropped and counted.  Within an expert, pairs
+ * keep ascending pair order; each expert's run is cut into tiles of at most
+ * `bm` rows (bm in {16, 32, 64, 128}).  The plan is unique.
+ *
+ * Layout of the DEVICE int32 plan buffer (size from qmoe_plan_bytes):
+ *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts  [7] 0
+ *   counts [n_experts] | offsets [n_experts + 1] | sorted pair ids [t * topk]
+ *   | tiles [max_tiles][4] = (expert, row0, nrows, 0) | sorted position of
+ *   each pair, -1 if dropped [t * topk]
+ * ------------------------------------------------------------------------ */
+size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm);
+int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts, int32_t bm,
+                  int32_t* plan, size_t plan_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gathered MoE matmul over a plan ([SHIM] mt_moe_gather_qmm; [DSV4] tiled
+ * MoE prefill GEMM with the iq2_xxs gate/up tile and the q2_K down twin).
+ * For sorted position i holding pair p = plan.sorted[i] with expert e:
+ *   y[i, n] = sum_k A_i[k] * W[e, n, k]
+ * where A_i = a[p / topk] (GATHER_TOKENS, a is [t, K]) or a[i] (SORTED_ROWS,
+ * a is [n_valid, K]).  Epilogues:
+ *   STORE             out [n_valid, N] out_dtype, sorted order
+ *   SWIGLU            out [n_valid, N/2] out_dtype, sorted order; gate = rows
+ *                     0..N/2-1 of W, up = rows N/2..N-1
+ *   WEIGHTED_COMBINE  out fp32 [t, N]: out[p / topk, n] += topk_w[p] * y[i, n]
+ *                     by float atomics (order-dependent rounding); topk_w is
+ *                     DEVICE fp32 [t, topk].  Finish with qmoe_combine_cast.
+ * a, out DEVICE; the plan must come from qmoe_moe_plan with the same t, topk,
+ * bm and n_experts == w->n_experts.  Matmul entry points need k to be a
+ * multiple of 64 and of the format's block.
+ * ------------------------------------------------------------------------ */
+int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
+                        int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
+                        const float* topk_w, int32_t epilogue,
+                        void* out, int32_t out_dtype, void* stream);
+
+/* Deterministic combine ([BAGEL] scalar-FMA top-K accumulate):
+ * out[t, n] = (base ? base[t, n] : 0) + sum_j topk_w[t, j] * y[pos(t, j), n],
+ * j ascending, fp32, one rounding to out_dtype.  y DEVICE [n_valid, N] in
+ * y_dtype (sorted order, e.g. a STORE result); base DEVICE fp32 [t, N] or
+ * NULL; dropped pairs contribute nothing. */
+int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t,
+                     int32_t topk, int32_t n_experts, const float* topk_w, int64_t n, const float* base,
+                     void* out, int32_t out_dtype, void* stream);
+
+/* out = RNE(acc) for n_elems values, then acc = 0 (so the fp32 accumulator
+ * of a WEIGHTED_COMBINE is ready for the next call).  DEVICE pointers. */
+int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode GEMV ([BAGEL] expert-indexed int4 GEMV reading expert ids on the
+ * device; [DSV4] small-batch qgemv and the sum-folded q2_K down projection).
+ * ids DEVICE int32 [b, topk] (entries outside [0, E) contribute nothing);
+ * b <= QMOE_MAX_GEMV_BATCH.  Each expert's weights are read once per call.
+ *   STORE             a = x [b, K];           out [b, topk, N]    = x_b . W[e]^T
+ *   SWIGLU            a = x [b, K];           out [b, topk, N/2]  = silu(g) * u
+ *   WEIGHTED_COMBINE  a = h [b, topk, K];     out [b, N] = sum_j topk_w[b, j] *
+ *                     (h[b, j] . W[ids[b, j]]^T), j ascending, deterministic
+ * a, out, topk_w DEVICE.
+ * ------------------------------------------------------------------------ */
+int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64_t b,
+                  const int32_t* ids, const float* topk_w, int32_t topk, int32_t epilogue,
+                  void* out, int32_t out_dtype, void* stream);
+
+/* QMOE_OK if the current HIP device is gfx950, else QMOE_ERR_ARCH. */
+int qmoe_check_device(void);
+/* Static description of a status code. */
+const char* qmoe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

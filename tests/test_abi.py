@@ -1,0 +1,131 @@
+"""Host-side checks of libqmoe (no GPU): the library loads, exports every
+entry point include/qmoe.h declares, the loader split reproduces the on-disk
+blocks, and argument validation rejects bad calls before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_moe_amd as qm
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qm.lib()
+    names = _declared()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qm.EXPORTS)
+
+
+def test_split_q8_0_round_trip():
+    W = synth.q8_0(np.random.default_rng(0), 2, 3, 64)
+    qs, d = qm.split_q8_0(W.blocks)
+    blocks = W.blocks.reshape(-1, 34)
+    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), blocks[:, :2])
+    assert np.array_equal(qs.view(np.uint8).reshape(-1, 32), blocks[:, 2:])
+
+
+def test_split_q2_k_round_trip():
+    W = synth.q2_k(np.random.default_rng(1), 1, 3, 512)
+    qs, sc, d, dmin = qm.split_q2_k(W.blocks)
+    b = W.blocks.reshape(-1, 84)
+    assert np.array_equal(sc.reshape(-1, 16), b[:, :16])
+    assert np.array_equal(qs.view(np.uint8).reshape(-1, 64), b[:, 16:80])
+    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), b[:, 80:82])
+    assert np.array_equal(dmin.view(np.uint8).reshape(-1, 2), b[:, 82:84])
+
+
+def test_split_iq2_xxs_round_trip():
+    W = synth.iq2_xxs(np.random.default_rng(2), 1, 2, 256)
+    idx, aux, d = qm.split_iq2_xxs(W.blocks)
+    b = W.blocks.reshape(-1, 66)
+    g = b[:, 2:].reshape(-1, 8, 8)
+    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), b[:, :2])
+    assert np.array_equal(idx.view(np.uint8).reshape(-1, 8, 4), g[:, :, :4])
+    assert np.array_equal(aux.view(np.uint8).reshape(-1, 8, 4), g[:, :, 4:])
+
+
+def test_split_int4_nibble_order():
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 2**32, size=257, dtype=np.uint64).astype(np.uint32)
+    out = qm.split_int4(words)
+    for w, o in zip(words[:20], out[:20]):
+        elems = [(int(w) >> (4 * i)) & 15 for i in range(8)]
+        for i in range(4):
+            assert (int(o) >> (4 * i)) & 15 == elems[2 * i]
+            assert (int(o) >> (4 * i + 16)) & 15 == elems[2 * i + 1]
+
+
+def test_signs_table_matches_oracle():
+    assert np.array_equal(qm.iq2_signs_table(), oracle.iq2_signs())
+
+
+def test_plan_bytes_layout():
+    n = qm.plan_bytes(2048, 8, 256, 128)
+    P = 2048 * 8
+    words = 8 + 256 + 257 + P
+    words = (words + 3) & ~3
+    words += 4 * (min(P, 256) + P // 16) + P
+    assert n == 4 * words
+
+
+def test_argument_validation_before_launch():
+    L = qm.lib()
+    E = -1
+    # plan: topk above 8, experts above 1024, bad bm, NULL ids
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 9, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 2000, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 48, ctypes.c_void_p(16), 1 << 20, None) == E
+    assert L.qmoe_moe_plan(None, 4, 2, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == E
+    # plan buffer too small
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(16), 16, None) == -5
+    # misaligned plan
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(20), 1 << 20, None) == -6
+    # dequant: NULL / misaligned / bad dtype
+    assert L.qmoe_dequant_q8_0(None, ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == E
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(8), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == -6
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 7, None) == E
+    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 96, 64,
+                               ctypes.c_void_p(16), 1, None) == -3
+    # matmul: k not a block multiple, too many experts, wrong epilogue / dtype
+    w = qm._Weights(qm.Q2_K, 1, 64, 320, 0, 0, 16, 0, 16, 0, 16, 16, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -3
+    w = qm._Weights(qm.Q8_0, 2000, 64, 256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -4
+    w = qm._Weights(qm.Q8_0, 1, 64, 256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 3, ctypes.c_void_p(16), 1, None) == -2
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 0, 4, 0, ctypes.c_void_p(16), 1, None) == E
+    w = qm._Weights(qm.INT4, 4, 64, 256, 32, 0, 16, 0, 16, 16, 0, 0, 0, 0)
+    assert L.qmoe_moe_gather_qmm(ctypes.byref(w), ctypes.c_void_p(16), 4, 2, 128, ctypes.c_void_p(16), 2, 0,
+                                 None, 0, ctypes.c_void_p(16), 2, None) == -2  # bf16 needs group >= 64
+    # gemv: batch above the limit, combine needs weights
+    w = qm._Weights(qm.INT4, 4, 64, 512, 64, 0, 16, 0, 16, 16, 0, 0, 0, 0)
+    assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 65, ctypes.c_void_p(16), None, 8, 1,
+                           ctypes.c_void_p(16), 2, None) == -4
+    assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 4, ctypes.c_void_p(16), None, 8, 2,
+                           ctypes.c_void_p(16), 2, None) == E
+    # empty inputs return OK without touching the device
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == 0
+    assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 0, ctypes.c_void_p(16), None, 8, 1,
+                           ctypes.c_void_p(16), 2, None) == 0
+    assert qm.lib().qmoe_strerror(-4).decode().startswith("size limit")
+
+
+def test_no_gpu_means_arch_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert qm.lib().qmoe_check_device() == -7

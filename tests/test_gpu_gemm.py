@@ -1,0 +1,216 @@
+"""GPU parity of the prefill matmuls (dense qmm and the gathered MoE GEMM)
+against the fp64 CPU oracle, through the C ABI.
+
+* exact-integer cases (power-of-two scales, small integer activations) must
+  match bit for bit in any summation order;
+* random cases must meet the normwise bound (TOL, net of the output rounding);
+* MoE cases check each stage against the oracle fed the bytes the GPU stage
+  consumed (stage-wise), the deterministic combine for run-to-run identity, and
+  the degenerate routings (empty experts, one hot expert, k = 1, dropped ids).
+"""
+import struct
+
+import numpy as np
+import pytest
+
+import block_quantized_moe_amd as qm
+import oracle
+import synth
+from _helpers import TOL, normwise_err, report, to_f64, torch_act, upload
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4"]
+
+
+def _w(fmt, rng, E, N, K):
+    return synth.int4(rng, E, N, K, 64) if fmt == "int4" else synth.weights(fmt, rng, E, N, K)
+
+
+# ------------------------------------------------------------------ dense
+
+def test_dense_q8_0_smoke_cell():
+    # M=32 N=256 K=2048 fp16, Q8_0 weights, fp16 out.
+    x, W = synth.dense_q8_0()
+    ref = oracle.qmm(oracle.act_to_f64(x, "f16"), W)
+    y = qm.qmm_dense(upload(W), torch_act(x, "f16"), qm.EPI_STORE, qm.F16)
+    torch.cuda.synchronize()
+    err = normwise_err(to_f64(y), ref, "f16")
+    assert err <= TOL, (err, report(to_f64(y), ref))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_dense_random_ragged(fmt, act):
+    rng = np.random.default_rng(hash((fmt, act)) % 2**32)
+    M, N, K = 45, 200, 512
+    W = _w(fmt, rng, 1, N, K)
+    x = synth.activations(rng, M, K, act)
+    ref = oracle.qmm(oracle.act_to_f64(x, act), W)
+    y = qm.qmm_dense(upload(W), torch_act(x, act), qm.EPI_STORE, qm.F32)
+    torch.cuda.synchronize()
+    err = normwise_err(to_f64(y), ref, "f32")
+    assert err <= TOL, (err, report(to_f64(y), ref))
+
+
+def _exact_weights(fmt, rng, E, N, K):
+    """Weights whose decoded values are small integers (exact everywhere)."""
+    W = _w(fmt, rng, E, N, K)
+    h = lambda v: np.frombuffer(struct.pack("<e", v), np.uint8)
+    if fmt == "q8_0":
+        W.blocks[..., 0:2] = h(1.0)
+        q = W.blocks[..., 2:34].view(np.int8)
+        q[...] = np.clip(q, -8, 8)
+    elif fmt == "q2_k":
+        W.blocks[..., 80:82] = h(1.0)
+        W.blocks[..., 82:84] = h(1.0)
+    elif fmt == "iq2_xxs":
+        W.blocks[..., 0:2] = h(8.0)    # group scale 8 * (0.5 + s) / 4 = 1 + 2s
+        W.grid = np.random.default_rng(1).choice(np.array([1, 2, 3], np.uint8), size=(256, 8))
+    else:
+        W.scale[...] = 0x3C00          # 1.0
+        W.bias[...] = 0xC800           # -8.0
+    return W
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_dense_exact_integer_bit_exact(fmt, act):
+    rng = np.random.default_rng(99)
+    M, N, K = 33, 144, 512
+    W = _exact_weights(fmt, rng, 1, N, K)
+    xi = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    x = synth.f16_bits(xi) if act == "f16" else synth.bf16_bits(xi)
+    ref = oracle.qmm(oracle.act_to_f64(x, act), W)
+    assert np.all(np.abs(ref) < 2 ** 24) and np.array_equal(ref, np.rint(ref))
+    y = qm.qmm_dense(upload(W), torch_act(x, act), qm.EPI_STORE, qm.F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(y), ref)
+
+
+def test_dense_swiglu_and_accumulate():
+    rng = np.random.default_rng(4)
+    M, I, K = 70, 96, 256
+    W = _w("q8_0", rng, 1, 2 * I, K)
+    x = synth.activations(rng, M, K, "f16")
+    x64 = oracle.act_to_f64(x, "f16")
+    gu = oracle.qmm(x64, W)
+    href = oracle.silu(gu[:, :I]) * gu[:, I:]
+    dw = upload(W)
+    h = qm.qmm_dense(dw, torch_act(x, "f16"), qm.EPI_SWIGLU, qm.F16)
+    acc = torch.ones((M, 2 * I), dtype=torch.float32, device="cuda")
+    qm.qmm_dense(dw, torch_act(x, "f16"), qm.EPI_ACCUMULATE, qm.F32, out=acc)
+    torch.cuda.synchronize()
+    assert normwise_err(to_f64(h), href, "f16") <= TOL
+    assert normwise_err(to_f64(acc), gu + 1.0, "f32") <= TOL
+
+
+# ------------------------------------------------------------------ MoE
+
+def _moe_case(gu_fmt, d_fmt, act, T=200, E=16, k=4, H=512, I=256, seed=3, routing="softmax"):
+    rng = np.random.default_rng(seed)
+    x = synth.activations(rng, T, H, act)
+    ids, w = (synth.routing_zipf if routing == "zipf" else synth.routing_softmax)(rng, T, E, k)
+    return x, ids, w, _w(gu_fmt, rng, E, 2 * I, H), _w(d_fmt, rng, E, H, I)
+
+
+def _run_moe(x, ids, w, Wgu, Wd, act, bm=128, deterministic=False, out_dtype=None):
+    T, k = ids.shape
+    E = Wgu.E
+    code = qm.F16 if act == "f16" else qm.BF16
+    xd = torch_act(x, act)
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    gu_d, d_d = upload(Wgu), upload(Wd)
+    plan = qm.moe_plan(ids_d, E, bm)
+    n_valid = int(((ids >= 0) & (ids < E)).sum())
+    h = qm.moe_gather_qmm(gu_d, plan, T, k, xd, bm=bm, epilogue=qm.EPI_SWIGLU, out_dtype=code, n_rows=n_valid)
+    oc = code if out_dtype is None else out_dtype
+    if deterministic:
+        y = qm.moe_gather_qmm(d_d, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE,
+                              out_dtype=qm.F32, n_rows=n_valid)
+        out = qm.moe_combine(y, plan, T, k, E, w_d, out_dtype=oc)
+    else:
+        acc = torch.zeros((T, Wd.N), dtype=torch.float32, device="cuda")
+        qm.moe_gather_qmm(d_d, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, topk_w=w_d,
+                          epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+        out = qm.combine_cast(acc, oc)
+        torch.cuda.synchronize()
+        assert float(acc.abs().max()) == 0.0  # the cast clears the accumulator
+    torch.cuda.synchronize()
+    srt = qm.plan_views(plan, T, k, E)["sorted"][:n_valid].cpu().numpy()
+    return h, srt, out
+
+
+def _check_moe(x, ids, w, Wgu, Wd, act, **kw):
+    T, k = ids.shape
+    x64 = oracle.act_to_f64(x, act)
+    h, srt, out = _run_moe(x, ids, w, Wgu, Wd, act, **kw)
+    # stage 1: h in sorted order vs the oracle's per-pair h
+    href = oracle.moe_gate_up(x64, ids, Wgu)[srt]
+    hg = to_f64(h)
+    e1 = normwise_err(hg, href, act)
+    assert e1 <= TOL, ("gate/up", e1, report(hg, href))
+    # stage 2 fed the GPU's h (mapped back to pair order)
+    hp = np.zeros((T * k, Wgu.N // 2))
+    hp[srt] = hg
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < Wgu.E)
+    ids_c = np.where(valid.reshape(ids.shape), ids, 0)
+    w_c = np.where(valid.reshape(ids.shape), w, 0).astype(np.float64)
+    oref = oracle.moe_down_combine(hp, ids_c, w_c, Wd)
+    og = to_f64(out)
+    od = {qm.F16: "f16", qm.BF16: "bf16", qm.F32: "f32"}[kw.get("out_dtype") or (qm.F16 if act == "f16" else qm.BF16)]
+    e2 = normwise_err(og, oref, od)
+    assert e2 <= TOL, ("down+combine", e2, report(og, oref))
+    return h, out
+
+
+@pytest.mark.parametrize("gu,dn,act", [("int4", "int4", "bf16"), ("int4", "int4", "f16"),
+                                       ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
+                                       ("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16")])
+def test_moe_stagewise(gu, dn, act):
+    x, ids, w, Wgu, Wd = _moe_case(gu, dn, act, seed=len(gu) + len(act))
+    _check_moe(x, ids, w, Wgu, Wd, act)
+
+
+def test_moe_deterministic_combine_is_reproducible():
+    x, ids, w, Wgu, Wd = _moe_case("int4", "int4", "bf16", seed=11)
+    _, o1 = _check_moe(x, ids, w, Wgu, Wd, "bf16", deterministic=True)
+    _, o2 = _check_moe(x, ids, w, Wgu, Wd, "bf16", deterministic=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("bm", [16, 64, 128])
+def test_moe_hot_expert_many_tiles_and_empty_experts(bm):
+    # every token picks expert 3 first (300 rows: several tiles), experts 8.. unused
+    x, ids, w, Wgu, Wd = _moe_case("int4", "int4", "bf16", T=300, E=12, k=2, seed=21)
+    ids[:, 0] = 3
+    ids[:, 1] = np.where(ids[:, 1] == 3, 4, ids[:, 1] % 8)
+    _check_moe(x, ids, w, Wgu, Wd, "bf16", bm=bm)
+
+
+def test_moe_top1_dropped_ids_and_single_token():
+    x, ids, w, Wgu, Wd = _moe_case("iq2_xxs", "q2_k", "f16", T=37, E=8, k=1, seed=5)
+    w[:] = 1.0
+    ids[0, 0] = -1
+    ids[5, 0] = 99
+    _check_moe(x, ids, w, Wgu, Wd, "f16")
+    x1, ids1, w1, Wgu1, Wd1 = _moe_case("int4", "int4", "bf16", T=1, E=8, k=8, seed=6)
+    _check_moe(x1, ids1, w1, Wgu1, Wd1, "bf16")
+
+
+def test_moe_single_expert_equals_dense():
+    rng = np.random.default_rng(8)
+    T, H, I = 77, 256, 128
+    W = _w("q8_0", rng, 1, 2 * I, H)
+    x = synth.activations(rng, T, H, "f16")
+    dw = upload(W)
+    xd = torch_act(x, "f16")
+    ids = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+    plan = qm.moe_plan(ids, 1, 128)
+    y_moe = qm.moe_gather_qmm(dw, plan, T, 1, xd, epilogue=qm.EPI_STORE, out_dtype=qm.F32)
+    y_dense = qm.qmm_dense(dw, xd, qm.EPI_STORE, qm.F32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_moe, y_dense)

@@ -1,0 +1,98 @@
+"""GPU parity of the decode GEMV (moe_gemv) against the fp64 oracle through
+the C ABI: the int4 Qwen-shaped decode workload at its real size (hidden 2048,
+intermediate 512, top-8 of 256 experts, B in {1, 4, 8}), the other formats at
+small sizes, run-to-run identity of the sum-folded combine, and agreement with
+the prefill GEMM at T = B."""
+import numpy as np
+import pytest
+
+import block_quantized_moe_amd as qm
+import oracle
+import synth
+from _helpers import TOL, normwise_err, report, to_f64, torch_act, upload
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _gemv(x, ids, w, Wgu, Wd, act):
+    code = qm.F16 if act == "f16" else qm.BF16
+    xd = torch_act(x, act)
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    gu_d, d_d = upload(Wgu), upload(Wd)
+    h = qm.moe_gemv(gu_d, xd, ids_d, epilogue=qm.EPI_SWIGLU, out_dtype=code)
+    out = qm.moe_gemv(d_d, h, ids_d, w_d, epilogue=qm.EPI_WEIGHTED_COMBINE, out_dtype=code)
+    torch.cuda.synchronize()
+    return h, out, (gu_d, d_d, xd, ids_d, w_d)
+
+
+def _check(x, ids, w, Wgu, Wd, act):
+    B, k = ids.shape
+    x64 = oracle.act_to_f64(x, act)
+    h, out, dev = _gemv(x, ids, w, Wgu, Wd, act)
+    href = oracle.moe_gate_up(x64, ids, Wgu)
+    hg = to_f64(h).reshape(B * k, -1)
+    e1 = normwise_err(hg, href, act)
+    assert e1 <= TOL, ("gate/up", e1, report(hg, href))
+    oref = oracle.moe_down_combine(hg, ids, w, Wd)
+    og = to_f64(out)
+    e2 = normwise_err(og, oref, act)
+    assert e2 <= TOL, ("down", e2, report(og, oref))
+    return h, out, dev
+
+
+@pytest.mark.parametrize("B", [1, 4, 8])
+def test_gemv_qwen_decode_int4_full_size(B):
+    inp = synth.qwen_a3b_decode(B)
+    h, out, dev = _check(inp.x, inp.ids, inp.w, inp.w_gate_up, inp.w_down, "bf16")
+    # sum-folded combine is deterministic
+    gu_d, d_d, xd, ids_d, w_d = dev
+    out2 = qm.moe_gemv(d_d, h, ids_d, w_d, epilogue=qm.EPI_WEIGHTED_COMBINE, out_dtype=qm.BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("gu,dn,act", [("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
+                                       ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
+                                       ("int4", "int4", "f16")])
+def test_gemv_formats(gu, dn, act):
+    rng = np.random.default_rng(len(gu) * 7 + len(act))
+    B, E, k, H, I = 4, 16, 4, 1024, 512
+    x = synth.activations(rng, B, H, act)
+    ids, w = synth.routing_softmax(rng, B, E, k)
+    ids[0] = [1, 2, 3, 4]
+    ids[1] = [2, 1, 5, 6]      # shared experts across tokens
+    Wgu = synth.int4(rng, E, 2 * I, H) if gu == "int4" else synth.weights(gu, rng, E, 2 * I, H)
+    Wd = synth.int4(rng, E, H, I) if dn == "int4" else synth.weights(dn, rng, E, H, I)
+    _check(x, ids, w, Wgu, Wd, act)
+
+
+def test_gemv_matches_prefill_gemm_at_t_eq_b():
+    inp = synth.qwen_a3b_decode(4, E=32)
+    B, k = inp.ids.shape
+    h, out, (gu_d, d_d, xd, ids_d, w_d) = _gemv(inp.x, inp.ids, inp.w, inp.w_gate_up, inp.w_down, "bf16")
+    plan = qm.moe_plan(ids_d, inp.E, 16)
+    hp = qm.moe_gather_qmm(gu_d, plan, B, k, xd, bm=16, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F32)
+    torch.cuda.synchronize()
+    srt = qm.plan_views(plan, B, k, inp.E)["sorted"].cpu().numpy()
+    a = to_f64(h).reshape(B * k, -1)[srt]
+    b = to_f64(hp)
+    assert normwise_err(a, b, "bf16") <= TOL
+
+
+def test_gemv_dropped_ids_contribute_nothing():
+    inp = synth.qwen_a3b_decode(2, E=16)
+    ids = inp.ids.copy()
+    ids[0, 3] = -1
+    ids[1, 0] = 16
+    w = inp.w.copy()
+    w[0, 3] = 0.0
+    w[1, 0] = 0.0
+    x64 = oracle.act_to_f64(inp.x, "bf16")
+    h, out, _ = _gemv(inp.x, ids, inp.w, inp.w_gate_up, inp.w_down, "bf16")
+    hg = to_f64(h).reshape(ids.size, -1)
+    valid = (ids.reshape(-1) >= 0) & (ids.reshape(-1) < 16)
+    ids_c = np.where(valid.reshape(ids.shape), ids, 0)
+    oref = oracle.moe_down_combine(np.where(valid[:, None], hg, 0.0), ids_c, w, inp.w_down)
+    assert normwise_err(to_f64(out), oref, "bf16") <= TOL
