@@ -78,7 +78,7 @@ def run_prefill(args, torch, qm):
     gus = [gu0] + [gu0.clone() for _ in range(R - 1)]
     dns = [dn0] + [dn0.clone() for _ in range(R - 1)]
     T, k, E, I = inp.T, inp.k, inp.E, inp.I
-    bm = 128
+    bm = 80
     plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
     acc = torch.zeros((T, inp.H), dtype=torch.float32, device=dev)

@@ -47,12 +47,12 @@ _SIGS = {
     "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 4,
     "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3,
-    "qmoe_split_int4": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p],
+    "qmoe_split_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_iq2_signs_table": [ctypes.c_void_p],
     "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_dequant_q2_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_dequant_iq2_xxs": [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
-    "qmoe_dequant_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_int4": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_qmm_dense": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_plan_bytes": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
     "qmoe_moe_plan": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
@@ -140,11 +140,18 @@ def split_iq2_xxs(aos: np.ndarray):
     return idx, aux, d
 
 
-def split_int4(words: np.ndarray) -> np.ndarray:
-    words = np.ascontiguousarray(words, dtype=np.uint32)
-    out = np.empty_like(words)
-    _check(lib().qmoe_split_int4(_np_ptr(words), words.size, _np_ptr(out)), "split_int4")
-    return out
+def split_int4(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, rows: int, k: int, group: int):
+    """MLX-style int4 rows -> (tiled code words, packed scale|bias<<16 words)."""
+    words = np.ascontiguousarray(words, dtype=np.uint32).reshape(-1)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16).reshape(-1)
+    bias = np.ascontiguousarray(bias, dtype=np.uint16).reshape(-1)
+    if words.size != rows * (k // 8) or scale.size != rows * (k // max(group, 1)) or bias.size != scale.size:
+        raise QmoeError("split_int4: array sizes do not match rows/k/group")
+    qs = np.empty(rows * (k // 8), np.uint32)
+    sb = np.empty(scale.size, np.uint32)
+    _check(lib().qmoe_split_int4(_np_ptr(words), _np_ptr(scale), _np_ptr(bias), rows, k, group,
+                                 _np_ptr(qs), _np_ptr(sb)), "split_int4")
+    return qs, sb
 
 
 def iq2_signs_table() -> np.ndarray:
@@ -212,9 +219,8 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
         t["grid"] = _dev(np.ascontiguousarray(grid, np.uint8).reshape(-1), device)
         t["signs"] = _dev(iq2_signs_table(), device)
     elif fmt == "int4":
-        t["qs"] = _dev(split_int4(qs.reshape(-1)), device)
-        t["scales"] = _dev(np.asarray(scale, np.uint16).reshape(-1), device)
-        t["biases"] = _dev(np.asarray(bias, np.uint16).reshape(-1), device)
+        q, sb = split_int4(qs, scale, bias, E * N, K, group)
+        t["qs"], t["scales"] = _dev(q, device), _dev(sb, device)
     else:
         raise ValueError(fmt)
     return DeviceWeights(fmt, E, N, K, group, t)
@@ -258,7 +264,7 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
         st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["aux"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
                                     w.E * w.N * w.K // 256, _ptr(out), out_dtype, s)
     else:
-        st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["biases"]), w.E * w.N, w.K, w.group,
+        st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, w.group,
                                  _ptr(out), out_dtype, s)
     _check(st, f"dequant_{w.fmt}")
     return out
@@ -280,7 +286,7 @@ def plan_bytes(t: int, topk: int, E: int, bm: int) -> int:
     return int(lib().qmoe_plan_bytes(t, topk, E, bm))
 
 
-def moe_plan(ids, E: int, bm: int = 128, plan=None):
+def moe_plan(ids, E: int, bm: int = 80, plan=None):
     import torch
     T, k = ids.shape
     nbytes = plan_bytes(T, k, E, bm)
@@ -304,7 +310,7 @@ def plan_views(plan, T: int, topk: int, E: int):
                 inv=plan[inv:inv + P])
 
 
-def moe_gather_qmm(w: DeviceWeights, plan, T: int, topk: int, a, *, bm: int = 128,
+def moe_gather_qmm(w: DeviceWeights, plan, T: int, topk: int, a, *, bm: int = 80,
                    a_mode: int = A_GATHER_TOKENS, topk_w=None, epilogue: int = EPI_STORE,
                    out_dtype: int = None, out=None, n_rows: int = None):
     """Gathered MoE matmul.  For STORE / SWIGLU the output has one row per

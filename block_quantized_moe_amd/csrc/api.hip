@@ -15,11 +15,14 @@ void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const
                          void*, int, hipStream_t);
 void launch_dequant_iq2_xxs(const uint32_t*, const uint32_t*, const uint16_t*, const uint8_t*,
                             const uint8_t*, int64_t, void*, int, hipStream_t);
-void launch_dequant_int4(const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t, int,
-                         void*, int, hipStream_t);
+void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
+                         hipStream_t);
 void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
+int64_t plan_scratch_words(int64_t, int);
 void launch_qmm(const qmoe_weights*, const void*, int, int, const int32_t*, int64_t, int, int,
                 int64_t, const float*, int, void*, int, hipStream_t);
+int qmm_int4_bf16_max_groups();
+int qmm_max_rows();
 void launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
                  int, void*, int, hipStream_t);
 void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
@@ -84,9 +87,9 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       break;
     case QMOE_INT4:
       if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
-      if (w->k % w->group) return QMOE_ERR_BLOCK;
-      if (!w->scales || !w->biases) return QMOE_ERR_ARG;
-      if (!al16(w->scales) || !al16(w->biases)) return QMOE_ERR_ALIGN;
+      if (w->k % w->group || w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (!w->scales) return QMOE_ERR_ARG;
+      if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
     default:
       return QMOE_ERR_UNSUPPORTED;
@@ -157,15 +160,15 @@ int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_
   return launched();
 }
 
-int qmoe_dequant_int4(const uint32_t* qs, const uint16_t* scales, const uint16_t* biases,
-                      int64_t rows, int64_t k, int32_t group, void* out, int32_t out_dtype,
-                      void* stream) {
-  if (!qs || !scales || !biases || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k, int32_t group,
+                      void* out, int32_t out_dtype, void* stream) {
+  if (!qs || !sb || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
   if (!(group == 32 || group == 64 || group == 128 || group == 256) || k % group) return QMOE_ERR_BLOCK;
-  if (!al16(qs) || !al16(scales) || !al16(biases) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(sb) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_dequant_int4(qs, scales, biases, rows, k, group, out, out_dtype, (hipStream_t)stream);
+  launch_dequant_int4(qs, sb, rows, k, group, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 
@@ -184,8 +187,10 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
     return QMOE_ERR_UNSUPPORTED;
   }
   if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->group % 64) return QMOE_ERR_UNSUPPORTED;
+  if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->k / w->group > qmm_int4_bf16_max_groups())
+    return QMOE_ERR_LIMIT;
   if (!al16(x) || !al16(out)) return QMOE_ERR_ALIGN;
-  if (m > (1ll << 31) - 1) return QMOE_ERR_LIMIT;
+  if (m * w->k * 2 >= (1ll << 31)) return QMOE_ERR_LIMIT;  // 32-bit activation byte offsets
   if (m == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
   launch_qmm(w, x, act_dtype, 2 /*dense*/, nullptr, 0, 1, 128, m, nullptr, epilogue, out, out_dtype,
@@ -198,10 +203,11 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
 size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm) {
   (void)bm;
   if (t < 0 || topk < 1 || n_experts < 1) return 0;
-  return (size_t)plan_layout(t * topk, n_experts).total * sizeof(int32_t);
+  const int64_t P = t * topk;
+  return (size_t)(plan_layout(P, n_experts).total + plan_scratch_words(P, n_experts)) * sizeof(int32_t);
 }
 
-static bool bm_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+static bool bm_ok(int bm) { return bm >= 16 && bm <= 128 && bm % 16 == 0; }
 
 int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts, int32_t bm,
                   int32_t* plan, size_t plan_bytes, void* stream) {
@@ -240,6 +246,11 @@ int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, i
     return QMOE_ERR_UNSUPPORTED;
   }
   if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->group % 64) return QMOE_ERR_UNSUPPORTED;
+  if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->k / w->group > qmm_int4_bf16_max_groups())
+    return QMOE_ERR_LIMIT;
+  if (bm > qmm_max_rows()) return QMOE_ERR_UNSUPPORTED;
+  // activation rows are addressed with 32-bit byte offsets
+  if ((a_mode == QMOE_A_GATHER_TOKENS ? t : t * topk) * w->k * 2 >= (1ll << 31)) return QMOE_ERR_LIMIT;
   if (!al16(plan) || !al16(a) || !al16(out)) return QMOE_ERR_ALIGN;
   if (t == 0) return QMOE_OK;
   QMOE_TRY(check_arch());

@@ -59,6 +59,16 @@ __device__ __forceinline__ void store_out_t(void* out, int64_t i, float v) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which on gfx9 means waiting for every outstanding vector-memory load
+// (vmcnt(0)) -- including prefetches meant to stay in flight across the
+// barrier.  Here only LDS traffic (lgkmcnt) is drained before s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
 // (selector 0..3 -> lo, 4..7 -> hi, 12 -> 0x00).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {

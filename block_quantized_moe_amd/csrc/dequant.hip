@@ -108,21 +108,23 @@ __global__ __launch_bounds__(256) void dequant_iq2_xxs_kernel(const uint32_t* __
   }
 }
 
-// int4 affine: value = s * q + b per group; GPU nibble order (see qmoe.h).
+// int4 affine: value = s * q + b per group, read from the tiled GPU layout
+// (qmoe.h): unit u is word w = u % (k/8) of row R = u / (k/8).
 template <int OUT>
 __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ qs,
-                                                           const uint16_t* __restrict__ sc,
-                                                           const uint16_t* __restrict__ bi,
+                                                           const uint32_t* __restrict__ sb,
                                                            int64_t n_units, int64_t words_per_row,
                                                            int group, void* __restrict__ out) {
-  const int64_t groups_per_row = words_per_row * 8 / group;
+  const int64_t kt_n = words_per_row / 8, G = words_per_row * 8 / group;
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
-    const int64_t r = u / words_per_row;
-    const int64_t w = u - r * words_per_row;
-    const uint32_t word = qs[u];
-    const int64_t gi = r * groups_per_row + (w * 8) / group;
-    const float s = f16_to_f32(sc[gi]);
-    const float bb = f16_to_f32(bi[gi]);
+    const int64_t R = u / words_per_row;
+    const int64_t w = u - R * words_per_row;
+    const int64_t rb = R >> 4, r = R & 15;
+    const int64_t kt = w >> 3, g = (w >> 1) & 3, h = w & 1;
+    const uint32_t word = qs[((rb * kt_n + kt) * 64 + 16 * g + r) * 2 + h];
+    const uint32_t p = sb[(rb * G + (w * 8) / group) * 16 + r];
+    const float s = f16_to_f32(p & 0xFFFFu);
+    const float bb = f16_to_f32(p >> 16);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -166,11 +168,11 @@ void launch_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint
   QMOE_DISPATCH_OUT(dtype, dequant_iq2_xxs_kernel, dim3(grid_for(units)), dim3(256), 0, s, idx,
                     aux, d, grid, signs, units, out);
 }
-void launch_dequant_int4(const uint32_t* qs, const uint16_t* sc, const uint16_t* bi, int64_t rows,
-                         int64_t k, int group, void* out, int dtype, hipStream_t s) {
+void launch_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k, int group,
+                         void* out, int dtype, hipStream_t s) {
   const int64_t units = rows * (k / 8);
-  QMOE_DISPATCH_OUT(dtype, dequant_int4_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc,
-                    bi, units, k / 8, group, out);
+  QMOE_DISPATCH_OUT(dtype, dequant_int4_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sb,
+                    units, k / 8, group, out);
 }
 
 }  // namespace qmoe

@@ -2,7 +2,7 @@
 // dense qmm share one kernel.
 //
 // What is computed: for each tile of (up to 128) rows routed to one expert
-// and a 128-wide slice of that expert's output rows, y = A . W[e]^T with fp32
+// and a slice of that expert's output rows, y = A . W[e]^T with fp32
 // accumulation, followed by an epilogue (store, SwiGLU, top-k weighted
 // scatter-add, or accumulate).  The DSV4 campaign page's tiled MoE prefill
 // GEMM (map0 work queue, 64-slot iq2_xxs gate/up tile, q2_K SoA down twin)
@@ -10,34 +10,43 @@
 // prior art; the tiling here is built for CDNA4 instead.
 //
 // Layout on gfx950:
-//  * 256 threads = 4 waves.  A workgroup owns one (row tile, column tile).
-//    Wave w owns 32 weight rows as two 16-column MFMA blocks (SwiGLU: 16 gate
-//    rows and the 16 matching up rows, so silu(g)*u is lane-local).
+//  * 256 threads = 4 waves.  A workgroup owns one (row tile, column tile) and
+//    each wave owns 64 weight rows as four 16-column MFMA blocks (SwiGLU: two
+//    blocks of gate rows and the two matching blocks of up rows, so
+//    silu(g)*u is lane-local).  One B fragment feeds every 16-row block of the
+//    tile; one A fragment feeds the wave's four column blocks.
 //  * K advances in 64-wide tiles.  The activation tile (128 x 64) is gathered
 //    by routed row straight into LDS, double buffered, one barrier per tile.
-//  * B fragments are dequantised in registers from the weight bytes each lane
-//    loads itself (one wide load per lane per tile) and fed to
-//    v_mfma_f32_16x16x32_{f16,bf16}; each fragment is reused by every 16-row
-//    block of the tile.
+//    The weight bytes each lane needs are loaded straight into registers two
+//    tiles ahead (ping-pong buffers), so the HBM stream has two tiles of every
+//    wave in flight.
 //  * Within a 64-wide K tile, lane group g (lanes 16g..16g+15) owns the 16
 //    contiguous k-values [16g, 16g+16); MFMA step s consumes values
 //    16g+8s..16g+8s+7 of every lane group (the A fragments are read from LDS
 //    with the same permutation, so the contraction is unchanged).  Formats
-//    whose scale changes every 32 values use the plain k order instead
-//    (MFMA step s = values 32s..32s+31).
+//    whose scale changes every 32 values with bf16 activations use the plain
+//    k order instead (MFMA step s = values 32s..32s+31).
 //  * fp16 activations: weights are dequantised to fp16 in registers (one or
-//    two fp16 roundings per weight).  bf16 activations: the MFMA consumes the
-//    integer codes, which are exact in bf16, and the per-group scale and bias
-//    are applied to the fp32 partial sums, so no weight is ever rounded to
-//    bf16's 8-bit significand.
+//    two fp16 roundings per weight) and fed to v_mfma_f32_16x16x32_f16.
+//  * bf16 activations: the MFMA consumes the integer codes, which are exact in
+//    bf16, and the scales are applied to fp32 partial sums, so no weight is
+//    rounded to bf16's 8-bit significand.  For int4 the per-group term
+//    s*sum(x*(128+q)) is applied per tile, and the bias term
+//    sum_g (b_g - 128 s_g) * X_g (X_g = sum of the activations of group g,
+//    computed by an MFMA against ones) is added at the end by three MFMAs
+//    over the groups with hi/lo bf16 splits of X and of the bias.
 #include "common.h"
 
 namespace qmoe {
 
-constexpr int BM = 128;       // rows per tile
+constexpr int BM = 80;        // rows per tile (at most; plan tiles must not be taller)
 constexpr int BK = 64;        // k per LDS tile
 constexpr int LDA = BK + 8;   // LDS row stride in halves (144 B, conflict-free b128 reads)
 constexpr int MB = BM / 16;   // 16-row MFMA blocks per tile
+constexpr int NB = 4;         // 16-column blocks per wave
+constexpr int BN = 4 * NB * 16;  // weight rows per workgroup (256)
+constexpr int XG_MAX = 64;    // int4 groups per row kept for the bf16 bias term
+constexpr int LDX = XG_MAX + 4;
 
 enum { AM_GATHER = 0, AM_SORTED = 1, AM_DENSE = 2 };
 
@@ -54,6 +63,7 @@ struct GemmArgs {
   int group;
   int amode;
   const uint16_t* a;
+  int64_t a_bytes;  // size of the activation buffer (byte offsets must stay below 2^31)
   const int32_t* plan;
   int E, topk, bm;
   int64_t P;
@@ -90,12 +100,14 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
   Raw r;
   const int64_t K = g.K;
   if constexpr (FMT == QMOE_INT4) {
-    const int64_t kk = k0 + 16 * lg;
-    const u2_t q = *(const u2_t*)((const uint32_t*)g.qs + R * (K / 8) + kk / 8);
-    r.v = u4_t{q[0], q[1], 0u, 0u};
-    const int64_t gi = R * (K / g.group) + kk / g.group;
-    r.x0 = ((const uint16_t*)g.scales)[gi];
-    r.x1 = ((const uint16_t*)g.biases)[gi];
+    // tiled layout: the 16 rows of block R/16 and one 64-wide k tile form one
+    // 512-byte run, lane 16*lg + r holding row r's values 16*lg .. +15
+    const int64_t rb = R >> 4, rr = R & 15;
+    const u2_t q = *(const u2_t*)((const uint32_t*)g.qs + ((rb * (K / 64) + k0 / 64) * 64 + 16 * lg + rr) * 2);
+    r.v[0] = q[0];
+    r.v[1] = q[1];
+    // scale in the low half, bias in the high half (the other fields stay unused)
+    r.x0 = ((const uint32_t*)g.scales)[(rb * (K / g.group) + k0 / g.group) * 16 + rr];
   } else if constexpr (FMT == QMOE_Q8_0) {
     if constexpr (KOrder<FMT, ACT>::chunk) {
       const int64_t kk = k0 + 16 * lg;
@@ -115,6 +127,7 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
     const int byte = 32 * (e0 >> 7) + (e0 & 31);
     r.v = *(const u4_t*)((const uint32_t*)g.qs + B * 16 + byte / 4);
     r.x0 = ((const uint8_t*)g.scales)[B * 16 + (e0 >> 4)];
+    r.x1 = 2u * (uint32_t)((e0 & 127) >> 5);  // bit shift of this lane's codes
     r.x2 = ((const uint16_t*)g.d)[B];
     r.x3 = ((const uint16_t*)g.dmin)[B];
   } else {  // IQ2_XXS
@@ -145,11 +158,10 @@ constexpr uint32_t SEL_B23 = 0x04030402u;  // [b2, m, b3, m]
 // k = 16g + 8s + i).  lg = lane group (only the IQ2_XXS octet choice needs it).
 template <int FMT>
 __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* lut_grid,
-                                         const uint32_t* lut_sign, h8_t& f0, h8_t& f1) {
-  u4_t o0, o1;
+                                         const uint32_t* lut_sign, u4_t& o0, u4_t& o1) {
   if constexpr (FMT == QMOE_INT4) {
     const h2_t s2 = h2_t{__builtin_bit_cast(_Float16, (uint16_t)r.x0), __builtin_bit_cast(_Float16, (uint16_t)r.x0)};
-    const h2_t b2 = h2_t{__builtin_bit_cast(_Float16, (uint16_t)r.x1), __builtin_bit_cast(_Float16, (uint16_t)r.x1)};
+    const h2_t b2 = h2_t{__builtin_bit_cast(_Float16, (uint16_t)(r.x0 >> 16)), __builtin_bit_cast(_Float16, (uint16_t)(r.x0 >> 16))};
     const h2_t off = h2_t{(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -177,7 +189,6 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
       else { o1[2 * (w - 2)] = vl; o1[2 * (w - 2) + 1] = vh; }
     }
   } else if constexpr (FMT == QMOE_Q2_K) {
-    // r.v: 16 code bytes; element shift from the lane's position (baked by caller in x1)
     const uint32_t sc = r.x0;
     const float d = f16_to_f32(r.x2), dm = f16_to_f32(r.x3);
     const _Float16 dl = (_Float16)(d * (float)(sc & 15u));
@@ -216,31 +227,382 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
       }
     }
   }
-  f0 = __builtin_bit_cast(h8_t, o0);
-  f1 = __builtin_bit_cast(h8_t, o1);
+}
+
+// bf16 helpers: round-to-nearest-even fp32 -> bf16 bits, and a hi/lo split.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ void split_hi_lo(float v, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne_bits(v);
+  lo = bf16_rne_bits(v - __builtin_bit_cast(float, hi << 16));
 }
 
 // ------------------------------------------------------------------ kernel
 
+// Per-workgroup context handed from the kernel prologue to the tile body.
+struct TileCtx {
+  uint16_t* As;          // [2][BM * LDA]
+  const int* rows_a;
+  const int* rows_o;
+  const float* wts;
+  float* xg;             // [BM * LDX] (bf16 int4 only)
+  const uint32_t* lut_grid;
+  const uint32_t* lut_sign;
+  int tid, lane, wave, lg, lr;
+  int nrows, mbn;
+  int64_t ncol[NB];
+  bool nvalid[NB];
+  int64_t Rb[NB];
+};
+
+// The K loop and epilogue of a tile of at most MBV 16-row blocks (c.mbn of
+// them hold rows).
+template <int FMT, int ACT, int EPI, int MBV>
+__device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
+  constexpr bool INT4_BF16 = (ACT == ACT_BF16 && FMT == QMOE_INT4);
+  const int tid = c.tid, wave = c.wave, lg = c.lg, lr = c.lr;
+  constexpr int ACHV = (MBV * 16 * 8 + 255) / 256;  // 16-byte activation chunks per thread
+
+  f4_t acc[MBV][NB];
+#pragma unroll
+  for (int m = 0; m < MBV; ++m)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[m][b] = f4_t{0, 0, 0, 0};
+
+  const int KT = (int)(g.K / BK);
+  const uint16_t* __restrict__ A = g.a;
+
+  // ---- activation staging: rows 0 .. 16*MBV-1 of the tile, 8 chunks of 16 B each.
+  // Buffer loads with a byte offset per chunk; rows without data get an
+  // offset past the end of the buffer, which the hardware returns as zeros, so
+  // the staging has no branches (and the vmcnt bookkeeping stays exact).
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A, (short)0, (int)g.a_bytes, 0x00020000);
+  uint32_t aoff[ACHV];
+#pragma unroll
+  for (int i = 0; i < ACHV; ++i) {
+    const int ch = tid + 256 * i;
+    const int r = ch >> 3, part = ch & 7;
+    const int src = (r < 16 * c.mbn) ? c.rows_a[r] : -1;
+    aoff[i] = src >= 0 ? (uint32_t)(src * g.K * 2 + 16 * part) : 0x80000000u;
+  }
+  u4_t astage[ACHV];
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < ACHV; ++i)
+      astage[i] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + (uint32_t)kt * (BK * 2), 0, 0));
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACHV; ++i) {
+      const int ch = tid + 256 * i;
+      const int r = ch >> 3, part = ch & 7;
+      if (r < 16 * MBV) *(u4_t*)(&c.As[buf * BM * LDA + r * LDA + 8 * part]) = astage[i];
+    }
+  };
+
+  // ---- one K tile of MFMA work from LDS buffer `buf` and raw weights `rw`
+  auto compute = [&](int kt, int buf, const Raw (&rw)[NB]) {
+    const uint16_t* Ab = c.As + buf * BM * LDA;
+    if constexpr (ACT == ACT_F16) {
+      u4_t bf[NB][2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) frag_f16<FMT>(rw[b], lg, c.lut_grid, c.lut_sign, bf[b][0], bf[b][1]);
+#pragma unroll
+      for (int m = 0; m < MBV; ++m) {
+        if (m >= c.mbn) break;
+        const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
+        const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)ar);
+        const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(ar + 8));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+          acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+        }
+      }
+    } else if constexpr (FMT == QMOE_INT4) {
+      // codes (128+q) as bf16 pairs; the tile lies inside one group.  The
+      // column blocks are taken two at a time (the A fragments are read from
+      // LDS once per pair) to keep the live registers within two waves/SIMD.
+      const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      const int tiles_per_group = g.group / BK;
+      const int gi = kt / tiles_per_group;
+      const bool first_of_group = (kt % tiles_per_group) == 0;
+#pragma unroll
+      for (int hp = 0; hp < NB; hp += 2) {
+        u4_t c0[2], c1[2];
+        float s[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            c0[j][i] = ((rw[hp + j].v[0] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+            c1[j][i] = ((rw[hp + j].v[1] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+          }
+          s[j] = f16_to_f32(rw[hp + j].x0);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+          const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(ar + 8));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            f4_t t = mfma(a0, __builtin_bit_cast(b8_t, c0[j]), f4_t{0, 0, 0, 0});
+            t = mfma(a1, __builtin_bit_cast(b8_t, c1[j]), t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][hp + j][r] = __builtin_fmaf(s[j], t[r], acc[m][hp + j][r]);
+          }
+          if (hp == 0 && (m & 3) == wave) {  // this wave records the row sums of block m
+            f4_t xs = mfma(a0, ones, f4_t{0, 0, 0, 0});
+            xs = mfma(a1, ones, xs);
+            if (lr < 4) {
+              float* dst = &c.xg[(16 * m + 4 * lg + lr) * LDX + gi];
+              const float val = xs[lr];
+              *dst = first_of_group ? val : *dst + val;
+            }
+          }
+        }
+      }
+    } else if constexpr (FMT == QMOE_Q8_0) {
+      // plain k order: step s = one 32-value block; codes converted exactly
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        u4_t cc[2];
+        const float d0 = f16_to_f32(rw[b].x0), d1 = f16_to_f32(rw[b].x2);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = rw[b].v[2 * st + (i >> 1)];
+            const int sh = 16 * (i & 1);
+            const float lo = (float)(int8_t)((w >> sh) & 0xFFu);
+            const float hi = (float)(int8_t)((w >> (sh + 8)) & 0xFFu);
+            cc[st][i] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
+            const f4_t t = mfma(a, __builtin_bit_cast(b8_t, cc[st]), f4_t{0, 0, 0, 0});
+            const float ds = st ? d1 : d0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(ds, t[r], acc[m][b][r]);
+          }
+        }
+      }
+    } else if constexpr (FMT == QMOE_IQ2_XXS) {
+      // plain k order: step s = one 32-value group, octet lg of it
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        u4_t cc[2];
+        float dsc[2];
+        const float d = f16_to_f32(rw[b].x4);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint32_t idx = st ? rw[b].x2 : rw[b].x0;
+          const uint32_t aux = st ? rw[b].x3 : rw[b].x1;
+          dsc[st] = d * (0.5f + (float)(aux >> 28)) * 0.25f;
+          const uint32_t gi = (idx >> (8 * lg)) & 0xFFu;
+          const uint32_t si = (aux >> (7 * lg)) & 0x7Fu;
+          const u4_t row = *(const u4_t*)(c.lut_grid + 4 * gi);
+          const u4_t msk = *(const u4_t*)(c.lut_sign + 4 * si);
+          cc[st] = row ^ msk;
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
+            const f4_t t = mfma(a, __builtin_bit_cast(b8_t, cc[st]), f4_t{0, 0, 0, 0});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(dsc[st], t[r], acc[m][b][r]);
+          }
+        }
+      }
+    } else {  // Q2_K with bf16: codes a*q and mins m, d and dmin on the partial sums
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        u4_t cq[2], cm;
+        const float a = (float)(rw[b].x0 & 15u);
+        const float mn = (float)(rw[b].x0 >> 4);
+        const float dd = f16_to_f32(rw[b].x2), dm = f16_to_f32(rw[b].x3);
+        const uint32_t mb16 = __builtin_bit_cast(uint32_t, mn) >> 16;
+        cm = u4_t{mb16 | (mb16 << 16), mb16 | (mb16 << 16), mb16 | (mb16 << 16), mb16 | (mb16 << 16)};
+        const uint32_t shift = rw[b].x1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t t = (rw[b].v[w] >> shift) & 0x03030303u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float lo = a * (float)((t >> (16 * h)) & 0xFFu);
+            const float hi = a * (float)((t >> (16 * h + 8)) & 0xFFu);
+            cq[w >> 1][2 * (w & 1) + h] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+          const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(ar + 8));
+          f4_t tq = mfma(a0, __builtin_bit_cast(b8_t, cq[0]), f4_t{0, 0, 0, 0});
+          tq = mfma(a1, __builtin_bit_cast(b8_t, cq[1]), tq);
+          f4_t tm = mfma(a0, __builtin_bit_cast(b8_t, cm), f4_t{0, 0, 0, 0});
+          tm = mfma(a1, __builtin_bit_cast(b8_t, cm), tm);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[m][b][r] = __builtin_fmaf(dd, tq[r], __builtin_fmaf(-dm, tm[r], acc[m][b][r]));
+        }
+      }
+    }
+  };
+
+  // Two tiles per trip: ra holds tile kt, rb tile kt + 1; each is refilled with
+  // the tile two ahead right after it is consumed.  Activation loads run one
+  // tile ahead through registers.  Past the last tile the prefetches re-read
+  // the last tile (an L2 hit), so the loop body has no branches around loads
+  // and the barriers (LDS-only) never wait for the weight stream.
+  const int last = KT - 1;
+  Raw ra[NB], rb[NB];
+  load_a(0);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ra[b] = load_raw<FMT, ACT>(g, c.Rb[b], 0, lg);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rb[b] = load_raw<FMT, ACT>(g, c.Rb[b], (int64_t)min(1, last) * BK, lg);
+  store_a(0);
+  load_a(min(1, last));
+  for (int kt = 0; kt < KT; kt += 2) {
+    lds_barrier();
+    compute(kt, 0, ra);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) ra[b] = load_raw<FMT, ACT>(g, c.Rb[b], (int64_t)min(kt + 2, last) * BK, lg);
+    store_a(1);
+    load_a(min(kt + 2, last));
+    lds_barrier();
+    if (kt + 1 < KT) compute(kt + 1, 1, rb);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rb[b] = load_raw<FMT, ACT>(g, c.Rb[b], (int64_t)min(kt + 3, last) * BK, lg);
+    store_a(0);
+    load_a(min(kt + 3, last));
+  }
+
+  // ---------------------------------------------------------------- bf16 int4 bias term
+  if constexpr (INT4_BF16) {
+    lds_barrier();  // row sums of every block are in xg
+    const int G = (int)(g.K / g.group);
+    for (int c0 = 0; c0 < G; c0 += 32) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        // B operand: (bias - 128 scale) of groups c0 + 8 lg .. + 8 of this lane's row, hi/lo bf16
+        u4_t bh, bl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h2[2], l2[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int gg = c0 + 8 * lg + 2 * i + q;
+            float cb = 0.f;
+            if (gg < G) {
+              const uint32_t sbv = ((const uint32_t*)g.scales)[((c.Rb[b] >> 4) * G + gg) * 16 + (c.Rb[b] & 15)];
+              cb = f16_to_f32(sbv >> 16) - 128.0f * f16_to_f32(sbv & 0xFFFFu);
+            }
+            split_hi_lo(cb, h2[q], l2[q]);
+          }
+          bh[i] = h2[0] | (h2[1] << 16);
+          bl[i] = l2[0] | (l2[1] << 16);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+          const float* xr = &c.xg[(16 * m + lr) * LDX + c0 + 8 * lg];
+          u4_t xh, xl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t h2[2], l2[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int gg = c0 + 8 * lg + 2 * i + q;
+              split_hi_lo(gg < G ? xr[2 * i + q] : 0.f, h2[q], l2[q]);
+            }
+            xh[i] = h2[0] | (h2[1] << 16);
+            xl[i] = l2[0] | (l2[1] << 16);
+          }
+          const b8_t XH = __builtin_bit_cast(b8_t, xh), XL = __builtin_bit_cast(b8_t, xl);
+          acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bh), acc[m][b]);
+          acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bl), acc[m][b]);
+          acc[m][b] = mfma(XL, __builtin_bit_cast(b8_t, bh), acc[m][b]);
+        }
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+#pragma unroll
+  for (int m = 0; m < MBV; ++m) {
+    if (m >= c.mbn) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * m + 4 * lg + r;
+      if (row >= c.nrows) continue;
+      const int64_t orow = c.rows_o[row];
+      if constexpr (EPI == QMOE_EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (c.nvalid[j]) store_out(g.out, g.out_dtype, orow * g.ldo + c.ncol[j], silu_f32(acc[m][j][r]) * acc[m][2 + j][r]);
+      } else if constexpr (EPI == QMOE_EPI_STORE) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (c.nvalid[b]) store_out(g.out, g.out_dtype, orow * g.ldo + c.ncol[b], acc[m][b][r]);
+      } else if constexpr (EPI == QMOE_EPI_WEIGHTED_COMBINE) {
+        const float w = c.wts[row];
+        float* o = (float*)g.out + orow * g.ldo;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (c.nvalid[b]) atomicAdd(o + c.ncol[b], w * acc[m][b][r]);
+      } else {  // ACCUMULATE
+        float* o = (float*)g.out + orow * g.ldo;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (c.nvalid[b]) o[c.ncol[b]] += acc[m][b][r];
+      }
+    }
+  }
+}
+
 template <int FMT, int ACT, int EPI>
 __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
-  typedef typename ActT<ACT>::v8 v8_t;
-  constexpr bool CHUNK = KOrder<FMT, ACT>::chunk;
-  constexpr bool NEED_X = (ACT == ACT_BF16 && FMT == QMOE_INT4);
+  constexpr bool INT4_BF16 = (ACT == ACT_BF16 && FMT == QMOE_INT4);
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * LDA];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
   __shared__ float wts[BM];
-  __shared__ __attribute__((aligned(16))) float xs[2][BM];
+  __shared__ __attribute__((aligned(16))) float xg[INT4_BF16 ? BM * LDX : 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 4, lr = lane & 15;
+  TileCtx c;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.lg = c.lane >> 4;
+  c.lr = c.lane & 15;
+  const int tid = c.tid;
 
-  const int v = xcd_remap(blockIdx.x, g.n_blocks);
+  // The grid is sized for the most tiles a plan can have; only the first
+  // n_tiles * n_ntiles blocks have work, and they are spread over all XCDs.
+  const int active = (g.amode == AM_DENSE) ? g.n_blocks : g.plan[1] * g.n_ntiles;
+  if ((int)blockIdx.x >= active) return;
+  const int v = xcd_remap(blockIdx.x, active);
   const int mt = v / g.n_ntiles, nt = v - mt * g.n_ntiles;
 
   int expert, row0, nrows;
@@ -249,6 +611,11 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
     row0 = mt * BM;
     if (row0 >= g.M) return;
     nrows = (int)min<int64_t>(BM, g.M - row0);
+    if (tid < BM) {
+      rows_a[tid] = tid < nrows ? row0 + tid : -1;
+      rows_o[tid] = row0 + tid;
+      wts[tid] = 0.f;
+    }
   } else {
     if (mt >= g.plan[1]) return;
     const PlanLayout L = plan_layout(g.P, g.E);
@@ -269,11 +636,6 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
       rows_o[tid] = ro;
       wts[tid] = wt;
     }
-  }
-  if (g.amode == AM_DENSE && tid < BM) {
-    rows_a[tid] = tid < nrows ? row0 + tid : -1;
-    rows_o[tid] = row0 + tid;
-    wts[tid] = 0.f;
   }
   if constexpr (IQ2) {
     // grid rows as 8 halves (fp16, or bf16 -- both exact for byte magnitudes)
@@ -299,299 +661,38 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
   }
   __syncthreads();
 
-  const int mbn = (nrows + 15) >> 4;  // valid 16-row blocks
+  c.As = As;
+  c.rows_a = rows_a;
+  c.rows_o = rows_o;
+  c.wts = wts;
+  c.xg = xg;
+  c.lut_grid = lut_grid;
+  c.lut_sign = lut_sign;
+  c.nrows = nrows;
 
-  // Weight rows of this lane for its two column blocks.
-  const bool swiglu = (EPI == QMOE_EPI_SWIGLU);
+  // Weight rows of this lane for its NB column blocks.
+  constexpr bool swiglu = (EPI == QMOE_EPI_SWIGLU);
   const int64_t Nh = g.N / 2;
-  int64_t ncol[2];     // output column (or h column) index of this lane per block
-  int64_t wrow[2];     // weight row (within the expert)
-  bool nvalid[2];
-  if (swiglu) {
-    const int64_t j = (int64_t)nt * 64 + 16 * wave + lr;
-    ncol[0] = ncol[1] = j;
-    nvalid[0] = nvalid[1] = j < Nh;
-    const int64_t jc = j < Nh ? j : Nh - 1;
-    wrow[0] = jc;
-    wrow[1] = Nh + jc;
-  } else {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = (int64_t)nt * 128 + 32 * wave + 16 * b + lr;
-      ncol[b] = n;
-      nvalid[b] = n < g.N;
-      wrow[b] = n < g.N ? n : g.N - 1;
-    }
-  }
-  const int64_t Rb0 = (int64_t)expert * g.N + wrow[0];
-  const int64_t Rb1 = (int64_t)expert * g.N + wrow[1];
-
-  f4_t acc[MB][2];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) { acc[m][0] = f4_t{0, 0, 0, 0}; acc[m][1] = f4_t{0, 0, 0, 0}; }
-
-  const int KT = (int)(g.K / BK);
-  const uint16_t* __restrict__ A = g.a;
-
-  // ---- activation staging (4 x 16 B per thread per tile)
-  u4_t astage[4];
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, part = c & 7;
-      const int src = rows_a[r];
-      if (src >= 0) astage[i] = *(const u4_t*)(A + (int64_t)src * g.K + (int64_t)kt * BK + 8 * part);
-      else astage[i] = u4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, part = c & 7;
-      *(u4_t*)(&As[buf][r * LDA + 8 * part]) = astage[i];
-      if constexpr (NEED_X) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          s += bf16_to_f32(astage[i][q] & 0xFFFFu);
-          s += bf16_to_f32(astage[i][q] >> 16);
-        }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        if (part == 0) xs[buf][r] = s;
-      }
-    }
-  };
-
-  Raw rc0, rc1, rn0, rn1;
-  load_a(0);
-  rc0 = load_raw<FMT, ACT>(g, Rb0, 0, lg);
-  rc1 = load_raw<FMT, ACT>(g, Rb1, 0, lg);
-  store_a(0);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    __syncthreads();
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
-      rn0 = load_raw<FMT, ACT>(g, Rb0, (int64_t)(kt + 1) * BK, lg);
-      rn1 = load_raw<FMT, ACT>(g, Rb1, (int64_t)(kt + 1) * BK, lg);
-    }
-    const uint16_t* Ab = &As[buf][0];
-
-    if constexpr (ACT == ACT_F16) {
-      if constexpr (FMT == QMOE_Q2_K) {
-        const int e0 = (kt * BK & 255) + 16 * lg;
-        rc0.x1 = rc1.x1 = 2u * (uint32_t)((e0 & 127) >> 5);
-      }
-      h8_t b00, b01, b10, b11;
-      frag_f16<FMT>(rc0, lg, lut_grid, lut_sign, b00, b01);
-      frag_f16<FMT>(rc1, lg, lut_grid, lut_sign, b10, b11);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        if (m < mbn) {
-          const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
-          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)ar);
-          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(ar + 8));
-          acc[m][0] = mfma(a0, b00, acc[m][0]);
-          acc[m][1] = mfma(a0, b10, acc[m][1]);
-          acc[m][0] = mfma(a1, b01, acc[m][0]);
-          acc[m][1] = mfma(a1, b11, acc[m][1]);
-        }
-      }
+  for (int b = 0; b < NB; ++b) {
+    int64_t wrow;
+    if (swiglu) {
+      const int64_t j = (int64_t)nt * (BN / 2) + 32 * c.wave + 16 * (b & 1) + c.lr;
+      c.ncol[b] = j;
+      c.nvalid[b] = j < Nh;
+      const int64_t jc = j < Nh ? j : Nh - 1;
+      wrow = (b < 2) ? jc : Nh + jc;
     } else {
-      // ---------------- bf16 activations: integer codes into the MFMA,
-      // scales on the fp32 partial sums.
-      if constexpr (FMT == QMOE_INT4) {
-        u4_t c0a, c0b, c1a, c1b;  // codes (128+q) as bf16 pairs, steps 0/1, blocks 0/1
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c0a[i] = ((rc0.v[0] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-          c0b[i] = ((rc0.v[1] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-          c1a[i] = ((rc1.v[0] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-          c1b[i] = ((rc1.v[1] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-        }
-        const float s0 = f16_to_f32(rc0.x0), s1 = f16_to_f32(rc1.x0);
-        const float cb0 = f16_to_f32(rc0.x1) - 128.0f * s0;
-        const float cb1 = f16_to_f32(rc1.x1) - 128.0f * s1;
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          if (m < mbn) {
-            const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
-            const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
-            const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(ar + 8));
-            f4_t t0 = f4_t{0, 0, 0, 0}, t1 = f4_t{0, 0, 0, 0};
-            t0 = mfma(a0, __builtin_bit_cast(b8_t, c0a), t0);
-            t1 = mfma(a0, __builtin_bit_cast(b8_t, c1a), t1);
-            t0 = mfma(a1, __builtin_bit_cast(b8_t, c0b), t0);
-            t1 = mfma(a1, __builtin_bit_cast(b8_t, c1b), t1);
-            const f4_t X = *(const f4_t*)(&xs[buf][16 * m + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              acc[m][0][r] = __builtin_fmaf(s0, t0[r], __builtin_fmaf(cb0, X[r], acc[m][0][r]));
-              acc[m][1][r] = __builtin_fmaf(s1, t1[r], __builtin_fmaf(cb1, X[r], acc[m][1][r]));
-            }
-          }
-        }
-      } else if constexpr (FMT == QMOE_Q8_0) {
-        // plain k order: step s = one 32-value block; codes converted exactly
-        u4_t c[2][2];  // [block][step]
-        float dsc[2][2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const Raw& r = b ? rc1 : rc0;
-          dsc[b][0] = f16_to_f32(r.x0);
-          dsc[b][1] = f16_to_f32(r.x2);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t w = r.v[2 * s + (i >> 1)];
-              const int sh = 16 * (i & 1);
-              const float lo = (float)(int8_t)((w >> sh) & 0xFFu);
-              const float hi = (float)(int8_t)((w >> (sh + 8)) & 0xFFu);
-              c[b][s][i] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
-            }
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          if (m < mbn) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const uint16_t* ar = Ab + (16 * m + lr) * LDA + 32 * s + 8 * lg;
-              const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
-              const f4_t t0 = mfma(a, __builtin_bit_cast(b8_t, c[0][s]), f4_t{0, 0, 0, 0});
-              const f4_t t1 = mfma(a, __builtin_bit_cast(b8_t, c[1][s]), f4_t{0, 0, 0, 0});
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                acc[m][0][r] = __builtin_fmaf(dsc[0][s], t0[r], acc[m][0][r]);
-                acc[m][1][r] = __builtin_fmaf(dsc[1][s], t1[r], acc[m][1][r]);
-              }
-            }
-          }
-        }
-      } else if constexpr (FMT == QMOE_IQ2_XXS) {
-        // plain k order: step s = one 32-value group, octet lg of it
-        u4_t c[2][2];
-        float dsc[2][2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const Raw& r = b ? rc1 : rc0;
-          const float d = f16_to_f32(r.x4);
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint32_t idx = s ? r.x2 : r.x0;
-            const uint32_t aux = s ? r.x3 : r.x1;
-            dsc[b][s] = d * (0.5f + (float)(aux >> 28)) * 0.25f;
-            const uint32_t gi = (idx >> (8 * lg)) & 0xFFu;
-            const uint32_t si = (aux >> (7 * lg)) & 0x7Fu;
-            const u4_t row = *(const u4_t*)(lut_grid + 4 * gi);
-            const u4_t msk = *(const u4_t*)(lut_sign + 4 * si);
-            c[b][s] = row ^ msk;
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          if (m < mbn) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const uint16_t* ar = Ab + (16 * m + lr) * LDA + 32 * s + 8 * lg;
-              const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
-              const f4_t t0 = mfma(a, __builtin_bit_cast(b8_t, c[0][s]), f4_t{0, 0, 0, 0});
-              const f4_t t1 = mfma(a, __builtin_bit_cast(b8_t, c[1][s]), f4_t{0, 0, 0, 0});
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                acc[m][0][r] = __builtin_fmaf(dsc[0][s], t0[r], acc[m][0][r]);
-                acc[m][1][r] = __builtin_fmaf(dsc[1][s], t1[r], acc[m][1][r]);
-              }
-            }
-          }
-        }
-      } else {  // Q2_K, chunk order: lane chunk = one 16-value sub-block
-        const int e0 = (kt * BK & 255) + 16 * lg;
-        const uint32_t shift = 2u * (uint32_t)((e0 & 127) >> 5);
-        u4_t cq[2][2], cm[2];
-        float dd[2], dm[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const Raw& r = b ? rc1 : rc0;
-          const float a = (float)(r.x0 & 15u);
-          const float mn = (float)(r.x0 >> 4);
-          dd[b] = f16_to_f32(r.x2);
-          dm[b] = f16_to_f32(r.x3);
-          const uint32_t mb16 = __builtin_bit_cast(uint32_t, mn) >> 16;
-          cm[b] = u4_t{mb16 | (mb16 << 16), mb16 | (mb16 << 16), mb16 | (mb16 << 16), mb16 | (mb16 << 16)};
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t t = (r.v[w] >> shift) & 0x03030303u;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float lo = a * (float)((t >> (16 * h)) & 0xFFu);
-              const float hi = a * (float)((t >> (16 * h + 8)) & 0xFFu);
-              cq[b][w >> 1][2 * (w & 1) + h] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
-            }
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          if (m < mbn) {
-            const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
-            const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)ar);
-            const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(ar + 8));
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              f4_t tq = f4_t{0, 0, 0, 0}, tm = f4_t{0, 0, 0, 0};
-              tq = mfma(a0, __builtin_bit_cast(b8_t, cq[b][0]), tq);
-              tq = mfma(a1, __builtin_bit_cast(b8_t, cq[b][1]), tq);
-              tm = mfma(a0, __builtin_bit_cast(b8_t, cm[b]), tm);
-              tm = mfma(a1, __builtin_bit_cast(b8_t, cm[b]), tm);
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[m][b][r] = __builtin_fmaf(dd[b], tq[r], __builtin_fmaf(-dm[b], tm[r], acc[m][b][r]));
-            }
-          }
-        }
-      }
+      const int64_t n = (int64_t)nt * BN + 64 * c.wave + 16 * b + c.lr;
+      c.ncol[b] = n;
+      c.nvalid[b] = n < g.N;
+      wrow = n < g.N ? n : g.N - 1;
     }
-
-    if (more) {
-      store_a(buf ^ 1);
-      rc0 = rn0;
-      rc1 = rn1;
-    }
+    c.Rb[b] = (int64_t)expert * g.N + wrow;
   }
 
-  // ---------------------------------------------------------------- epilogue
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    if (m >= mbn) continue;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * m + 4 * lg + r;
-      if (row >= nrows) continue;
-      const int64_t orow = rows_o[row];
-      if constexpr (EPI == QMOE_EPI_SWIGLU) {
-        if (nvalid[0]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[0], silu_f32(acc[m][0][r]) * acc[m][1][r]);
-      } else if constexpr (EPI == QMOE_EPI_STORE) {
-        if (nvalid[0]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[0], acc[m][0][r]);
-        if (nvalid[1]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[1], acc[m][1][r]);
-      } else if constexpr (EPI == QMOE_EPI_WEIGHTED_COMBINE) {
-        const float w = wts[row];
-        float* o = (float*)g.out + orow * g.ldo;
-        if (nvalid[0]) atomicAdd(o + ncol[0], w * acc[m][0][r]);
-        if (nvalid[1]) atomicAdd(o + ncol[1], w * acc[m][1][r]);
-      } else {  // ACCUMULATE
-        float* o = (float*)g.out + orow * g.ldo;
-        if (nvalid[0]) o[ncol[0]] += acc[m][0][r];
-        if (nvalid[1]) o[ncol[1]] += acc[m][1][r];
-      }
-    }
-  }
+  c.mbn = (nrows + 15) >> 4;  // valid 16-row blocks
+  qmm_body<FMT, ACT, EPI, MB>(g, c);
 }
 
 template <int FMT, int ACT>
@@ -611,6 +712,10 @@ static void launch_f(const GemmArgs& g, int act, int epi, hipStream_t s) {
   else launch_fa<FMT, ACT_BF16>(g, epi, s);
 }
 
+// Groups per row the bf16 int4 path can keep (bias term), and the tallest tile.
+int qmm_int4_bf16_max_groups() { return XG_MAX; }
+int qmm_max_rows() { return BM; }
+
 // Host launcher shared by qmoe_qmm_dense and qmoe_moe_gather_qmm.
 void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const int32_t* plan,
                 int64_t t, int topk, int bm, int64_t M, const float* topk_w, int epi, void* out,
@@ -621,6 +726,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.N = w->n; g.K = w->k; g.group = w->group;
   g.amode = amode;
   g.a = (const uint16_t*)a;
+  g.a_bytes = (amode == AM_DENSE ? M : amode == AM_GATHER ? t : t * topk) * w->k * 2;
   g.plan = plan;
   g.E = w->n_experts;
   g.topk = topk;
@@ -633,8 +739,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.bm = bm;
   if (amode == AM_DENSE) n_mt = (M + BM - 1) / BM;
   else n_mt = plan_max_tiles(g.P, g.E, bm);
-  if (epi == QMOE_EPI_SWIGLU) { g.n_ntiles = (int)((w->n / 2 + 63) / 64); g.ldo = w->n / 2; }
-  else { g.n_ntiles = (int)((w->n + 127) / 128); g.ldo = w->n; }
+  if (epi == QMOE_EPI_SWIGLU) { g.n_ntiles = (int)((w->n / 2 + BN / 2 - 1) / (BN / 2)); g.ldo = w->n / 2; }
+  else { g.n_ntiles = (int)((w->n + BN - 1) / BN); g.ldo = w->n; }
   g.n_blocks = (int)(n_mt * g.n_ntiles);
   if (g.n_blocks == 0) return;
   switch (w->fmt) {

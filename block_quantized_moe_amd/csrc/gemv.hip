@@ -99,10 +99,15 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
                                           const uint32_t* lut_sign) {
   const int64_t K = g.K;
   if constexpr (FMT == QMOE_INT4) {
-    const u4_t q = *(const u4_t*)((const uint32_t*)g.qs + R * (K / 8) + 4 * c);
-    const int64_t gi = R * (K / g.group) + (32 * c) / g.group;
-    const float s = f16_to_f32(((const uint16_t*)g.scales)[gi]);
-    const float b = f16_to_f32(((const uint16_t*)g.biases)[gi]);
+    // Tiled layout: chunk c of row R is lane groups 2(c&1), 2(c&1)+1 of tile (R/16, c/2).
+    const int64_t rb = R >> 4, rr = R & 15;
+    const uint32_t* tile = (const uint32_t*)g.qs + (rb * (K / 64) + (c >> 1)) * 128;
+    const u2_t qa = *(const u2_t*)(tile + (32 * (c & 1) + rr) * 2);
+    const u2_t qb = *(const u2_t*)(tile + (32 * (c & 1) + 16 + rr) * 2);
+    const u4_t q = u4_t{qa[0], qa[1], qb[0], qb[1]};
+    const uint32_t sbv = ((const uint32_t*)g.scales)[(rb * (K / g.group) + (32 * c) / g.group) * 16 + rr];
+    const float s = f16_to_f32(sbv & 0xFFFFu);
+    const float b = f16_to_f32(sbv >> 16);
     uint32_t cp[16];
 #pragma unroll
     for (int w = 0; w < 4; ++w)

@@ -1,114 +1,183 @@
-// Routing plan: expert histogram, offsets and tile list (one workgroup), then
-// a stable expert-sorted scatter of the routed pairs (one workgroup per
-// expert).  The DSV4 campaign page's map0 work queue maps experts to tiles of
-// routed tokens for the tiled MoE prefill GEMM; the Everything Bagel 2 page
-// keeps router ids on the device.  Pairs keep ascending pair order inside an
-// expert, so the plan is unique and identical from run to run.
+// Routing plan: the expert-sorted token gather with per-expert tiles.
+//
+// The DSV4 campaign page's map0 work queue maps experts to tiles of routed
+// tokens for the tiled MoE prefill GEMM; the Everything Bagel 2 page keeps the
+// router ids on the device.  Pairs keep ascending pair order inside an expert,
+// so the plan is unique and identical from run to run.
+//
+// Three short launches over chunks of 1024 pairs (one 1024-thread workgroup
+// per chunk, one pair per thread):
+//   1. chunk histograms: per-expert counts of each chunk;
+//   2. one workgroup turns them into per-chunk bases, expert counts,
+//      offsets, the tile list and the header;
+//   3. each chunk recomputes its in-chunk ranks and scatters its pairs.
+// A wave finds the lanes that share its expert with one ballot per bit of the
+// expert id, so ranks are exact without sorting; waves are combined through
+// per-wave counts in LDS in wave order.  Chunk histograms live in the plan
+// buffer's scratch area after the inverse map.
 #include "common.h"
 
 namespace qmoe {
 
-// One workgroup of 1024 threads: counts, exclusive offsets, tile list, header.
-__global__ __launch_bounds__(1024) void plan_count_kernel(const int32_t* __restrict__ ids, int64_t P,
-                                                          int E, int bm, int64_t t, int topk,
-                                                          int32_t* __restrict__ plan) {
-  __shared__ int hist[QMOE_MAX_EXPERTS];
-  __shared__ int scan_a[QMOE_MAX_EXPERTS];
-  __shared__ int scan_t[QMOE_MAX_EXPERTS];
-  __shared__ int dropped;
-  const int tid = threadIdx.x;
-  if (tid < QMOE_MAX_EXPERTS) hist[tid] = 0;
-  if (tid == 0) dropped = 0;
-  __syncthreads();
-  int my_drop = 0;
-  for (int64_t p = tid; p < P; p += 1024) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    else ++my_drop;
+constexpr int PC = 1024;  // pairs per chunk (per workgroup)
+
+struct PlanArgs {
+  const int32_t* ids;
+  int64_t P;
+  int E, bm, topk;
+  int64_t t;
+  int32_t* plan;
+  int nchunks;
+  int nbits;  // expert ids are below 2^nbits
+};
+
+__device__ __forceinline__ int64_t hist_off(const PlanLayout& L) { return L.total; }
+
+// Lanes of this wave holding the same key: one ballot per key bit (keys are
+// below 2^nbits); lanes with key < 0 get an empty mask.
+__device__ __forceinline__ uint64_t peers_of(int key, int nbits) {
+  uint64_t m = __ballot(key >= 0);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool on = (key >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    m &= on ? bal : ~bal;
   }
-  if (my_drop) atomicAdd(&dropped, my_drop);
+  return key >= 0 ? m : 0ull;
+}
+
+// One pair per thread: the expert of pair p (or -1), its rank among the
+// wave's pairs of that expert, and per-wave counts in wcnt[wave][e].
+__device__ __forceinline__ int wave_rank(const PlanArgs& a, int64_t p, int lane, int* wcnt_w,
+                                         int& key) {
+  int e = -1;
+  if (p < a.P) {
+    const int v = a.ids[p];
+    e = (v >= 0 && v < a.E) ? v : -1;
+  }
+  const uint64_t peers = peers_of(e, a.nbits);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int before = __popcll(peers & lt);
+  if (e >= 0 && before == 0) wcnt_w[e] = __popcll(peers);
+  key = e;
+  return before;
+}
+
+__global__ __launch_bounds__(1024) void plan_hist_kernel(PlanArgs a) {
+  extern __shared__ int wcnt[];  // [16][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 16 * a.E; i += 1024) wcnt[i] = 0;
   __syncthreads();
-  // inclusive scans of counts and of tiles-per-expert (Hillis-Steele over 1024 slots)
-  const int c = (tid < E) ? hist[tid] : 0;
-  const int nt = (c + bm - 1) / bm;
-  scan_a[tid] = c;
-  scan_t[tid] = nt;
+  int key;
+  wave_rank(a, (int64_t)blockIdx.x * PC + tid, lane, wcnt + wave * a.E, key);
+  __syncthreads();
+  const PlanLayout L = plan_layout(a.P, a.E);
+  int32_t* hist = a.plan + hist_off(L) + (int64_t)blockIdx.x * a.E;
+  for (int e = tid; e < a.E; e += 1024) {
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) s += wcnt[w * a.E + e];
+    hist[e] = s;
+  }
+}
+
+// One workgroup of 1024 threads (thread = expert).
+__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
+  __shared__ int sa[QMOE_MAX_EXPERTS], st[QMOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const PlanLayout L = plan_layout(a.P, a.E);
+  int32_t* hist = a.plan + hist_off(L);
+  int c_e = 0;
+  if (tid < a.E) {
+    // running base per chunk (in place: hist[c][e] becomes the chunk's base)
+    int run = 0;
+    for (int c = 0; c < a.nchunks; ++c) {
+      const int v = hist[(int64_t)c * a.E + tid];
+      hist[(int64_t)c * a.E + tid] = run;
+      run += v;
+    }
+    c_e = run;
+  }
+  const int nt = (c_e + a.bm - 1) / a.bm;
+  sa[tid] = c_e;
+  st[tid] = nt;
   __syncthreads();
   for (int off = 1; off < QMOE_MAX_EXPERTS; off <<= 1) {
-    const int va = tid >= off ? scan_a[tid - off] : 0;
-    const int vt = tid >= off ? scan_t[tid - off] : 0;
+    const int va = tid >= off ? sa[tid - off] : 0;
+    const int vt = tid >= off ? st[tid - off] : 0;
     __syncthreads();
-    scan_a[tid] += va;
-    scan_t[tid] += vt;
+    sa[tid] += va;
+    st[tid] += vt;
     __syncthreads();
   }
-  const PlanLayout L = plan_layout(P, E);
-  if (tid < E) {
-    const int row0 = scan_a[tid] - c;     // exclusive offset
-    const int tile0 = scan_t[tid] - nt;
-    plan[L.counts + tid] = c;
-    plan[L.offsets + tid] = row0;
+  if (tid < a.E) {
+    const int row0 = sa[tid] - c_e;
+    const int tile0 = st[tid] - nt;
+    a.plan[L.counts + tid] = c_e;
+    a.plan[L.offsets + tid] = row0;
     for (int i = 0; i < nt; ++i) {
-      int32_t* tl = plan + L.tiles + 4 * (int64_t)(tile0 + i);
+      int32_t* tl = a.plan + L.tiles + 4 * (int64_t)(tile0 + i);
       tl[0] = tid;
-      tl[1] = row0 + i * bm;
-      tl[2] = min(bm, c - i * bm);
+      tl[1] = row0 + i * a.bm;
+      tl[2] = min(a.bm, c_e - i * a.bm);
       tl[3] = 0;
     }
   }
   if (tid == 0) {
-    const int total = scan_a[QMOE_MAX_EXPERTS - 1];
-    plan[0] = dropped;
-    plan[1] = scan_t[QMOE_MAX_EXPERTS - 1];
-    plan[2] = total;
-    plan[3] = bm;
-    plan[4] = (int32_t)t;
-    plan[5] = topk;
-    plan[6] = E;
-    plan[7] = 0;
-    plan[L.offsets + E] = total;
+    const int total = sa[QMOE_MAX_EXPERTS - 1];
+    a.plan[0] = (int32_t)(a.P - total);
+    a.plan[1] = st[QMOE_MAX_EXPERTS - 1];
+    a.plan[2] = total;
+    a.plan[3] = a.bm;
+    a.plan[4] = (int32_t)a.t;
+    a.plan[5] = a.topk;
+    a.plan[6] = a.E;
+    a.plan[7] = 0;
+    a.plan[L.offsets + a.E] = total;
   }
 }
 
-// Workgroup e writes expert e's pairs, in ascending pair order, to
-// sorted[offsets[e] + rank] and records the inverse map.  Workgroup 0 also
-// marks dropped pairs in the inverse map.
-__global__ __launch_bounds__(256) void plan_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
-                                                           int E, int bm, int32_t* __restrict__ plan) {
-  const int e = blockIdx.x;
-  const PlanLayout L = plan_layout(P, E);
-  const int count = plan[L.counts + e];
-  if (count == 0 && e != 0) return;
-  const int base = plan[L.offsets + e];
-  __shared__ int wave_n[4];
+__global__ __launch_bounds__(1024) void plan_scatter_kernel(PlanArgs a) {
+  extern __shared__ int wcnt[];  // [16][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int found = 0;
-  for (int64_t p0 = 0; p0 < P && (found < count || e == 0); p0 += 256) {
-    const int64_t p = p0 + tid;
-    const int id = p < P ? ids[p] : -1;
-    const bool hit = (p < P) && id == e;
-    if (e == 0 && p < P && !(id >= 0 && id < E)) plan[L.inv + p] = -1;
-    const uint64_t bal = __ballot(hit);
-    if (lane == 0) wave_n[wave] = __popcll(bal);
-    __syncthreads();
-    int before = found;
-    for (int w = 0; w < wave; ++w) before += wave_n[w];
-    const int total = wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
-    if (hit) {
-      const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
-      plan[L.sorted + base + rank] = (int32_t)p;
-      plan[L.inv + p] = base + rank;
-    }
-    found += total;
-    __syncthreads();
+  for (int i = tid; i < 16 * a.E; i += 1024) wcnt[i] = 0;
+  __syncthreads();
+  int e;
+  const int64_t p = (int64_t)blockIdx.x * PC + tid;
+  const int rank = wave_rank(a, p, lane, wcnt + wave * a.E, e);
+  __syncthreads();
+  if (p >= a.P) return;
+  const PlanLayout L = plan_layout(a.P, a.E);
+  if (e < 0) {
+    a.plan[L.inv + p] = -1;
+    return;
   }
+  int wb = 0;
+  for (int w = 0; w < wave; ++w) wb += wcnt[w * a.E + e];
+  const int32_t* cbase = a.plan + hist_off(L) + (int64_t)blockIdx.x * a.E;
+  const int pos = a.plan[L.offsets + e] + cbase[e] + wb + rank;
+  a.plan[L.sorted + pos] = (int32_t)p;
+  a.plan[L.inv + p] = pos;
 }
+
+int64_t plan_scratch_words(int64_t P, int E) { return ((P + PC - 1) / PC) * (int64_t)E; }
 
 void launch_plan(const int32_t* ids, int64_t t, int topk, int E, int bm, int32_t* plan,
                  hipStream_t s) {
-  const int64_t P = t * topk;
-  hipLaunchKernelGGL(plan_count_kernel, dim3(1), dim3(1024), 0, s, ids, P, E, bm, t, topk, plan);
-  hipLaunchKernelGGL(plan_scatter_kernel, dim3(E), dim3(256), 0, s, ids, P, E, bm, plan);
+  PlanArgs a;
+  a.ids = ids;
+  a.P = t * topk;
+  a.E = E;
+  a.bm = bm;
+  a.topk = topk;
+  a.t = t;
+  a.plan = plan;
+  a.nchunks = (int)((a.P + PC - 1) / PC);
+  a.nbits = 1;
+  while ((1 << a.nbits) < E) ++a.nbits;
+  const size_t lds = 16 * (size_t)E * sizeof(int);
+  hipLaunchKernelGGL(plan_hist_kernel, dim3(a.nchunks), dim3(1024), lds, s, a);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3(a.nchunks), dim3(1024), lds, s, a);
 }
 
 }  // namespace qmoe

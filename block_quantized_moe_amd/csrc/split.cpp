@@ -51,16 +51,33 @@ int qmoe_split_iq2_xxs(const void* aos, int64_t n_blocks, uint32_t* idx, uint32_
   return QMOE_OK;
 }
 
-int qmoe_split_int4(const uint32_t* words, int64_t n_words, uint32_t* out) {
-  if (!words || !out || n_words < 0) return QMOE_ERR_ARG;
-  for (int64_t w = 0; w < n_words; ++w) {
-    const uint32_t v = words[w];
-    uint32_t r = 0;
-    for (int i = 0; i < 4; ++i) {
-      r |= ((v >> (8 * i)) & 0xFu) << (4 * i);            // element 2i   -> nibble i
-      r |= ((v >> (8 * i + 4)) & 0xFu) << (4 * i + 16);   // element 2i+1 -> nibble 4+i
-    }
-    out[w] = r;
+// Nibble order inside a word: element 2i -> nibble i, element 2i+1 -> nibble 4+i.
+static uint32_t int4_gpu_word(uint32_t v) {
+  uint32_t r = 0;
+  for (int i = 0; i < 4; ++i) {
+    r |= ((v >> (8 * i)) & 0xFu) << (4 * i);
+    r |= ((v >> (8 * i + 4)) & 0xFu) << (4 * i + 16);
+  }
+  return r;
+}
+
+int qmoe_split_int4(const uint32_t* words, const uint16_t* scales, const uint16_t* biases,
+                    int64_t rows, int64_t k, int32_t group, uint32_t* qs_out, uint32_t* sb_out) {
+  if (!words || !scales || !biases || !qs_out || !sb_out || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (!(group == 32 || group == 64 || group == 128 || group == 256)) return QMOE_ERR_BLOCK;
+  if (rows % 16 || k % 64 || k % group) return QMOE_ERR_BLOCK;
+  const int64_t kt_n = k / 64, wpr = k / 8, G = k / group;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t kt = 0; kt < kt_n; ++kt)
+      for (int g = 0; g < 4; ++g)
+        for (int w = 0; w < 2; ++w) {
+          const int64_t src = R * wpr + kt * 8 + g * 2 + w;          // word of k = 64kt + 16g + 8w
+          const int64_t dst = ((rb * kt_n + kt) * 64 + (16 * g + r)) * 2 + w;
+          qs_out[dst] = int4_gpu_word(words[src]);
+        }
+    for (int64_t gi = 0; gi < G; ++gi)
+      sb_out[(rb * G + gi) * 16 + r] = (uint32_t)scales[R * G + gi] | ((uint32_t)biases[R * G + gi] << 16);
   }
   return QMOE_OK;
 }

@@ -95,11 +95,17 @@ enum {
  *            d      fp16  [E, n, k/256]
  *            grid   u8    [256, 8]               magnitude rows
  *            signs  u8    [128]                  sign masks (qmoe_iq2_signs_table)
- *   INT4     qs     u32   [E, n, k/8]            GPU nibble order (qmoe_split_int4): word w
- *                                                holds element 8w+2i in nibble i and element
- *                                                8w+2i+1 in nibble 4+i (i = 0..3)
- *            scales fp16  [E, n, k/group]        s
- *            biases fp16  [E, n, k/group]        b;   value = s*q + b
+ *   INT4     value = s*q + b per group of `group` values along k, tiled by
+ *            qmoe_split_int4 (rows = E*n must be a multiple of 16, k a multiple
+ *            of 64 and of group).  Global row R = e*n + row, block rb = R/16,
+ *            r = R%16, 64-wide k tile kt:
+ *            qs     u32 [R/16][k/64][64 lanes][2]   lane l = 16*g + r holds the 16
+ *                   codes of row 16*rb + r at k = 64*kt + 16*g .. +15 as two words;
+ *                   word w of those holds element 8w+2i in nibble i and 8w+2i+1
+ *                   in nibble 4+i (i = 0..3)
+ *            scales u32 [R/16][k/group][16]         (fp16 s) | (fp16 b) << 16 of
+ *                   row 16*rb + r and each group
+ *            biases NULL
  *            group  32, 64, 128 or 256 (bf16 activations in the prefill matmul:
  *                   64, 128 or 256)
  */
@@ -135,10 +141,14 @@ int qmoe_split_q2_k(const void* aos, int64_t n_blocks, uint32_t* qs, uint8_t* sc
                     uint16_t* d, uint16_t* dmin);
 int qmoe_split_iq2_xxs(const void* aos, int64_t n_blocks, uint32_t* idx, uint32_t* aux,
                        uint16_t* d);
-/* int4 words from the on-disk (MLX) nibble order, where nibble i of word w is
- * element 8w+i, to the GPU nibble order above (so that one mask-and-or yields
- * two consecutive elements in the two halves of a 32-bit register). */
-int qmoe_split_int4(const uint32_t* words, int64_t n_words, uint32_t* out);
+/* int4 slabs from the on-disk (MLX) form -- words [rows][k/8] with element
+ * 8w+i in nibble i of word w, fp16 scales and biases [rows][k/group] -- to the
+ * tiled GPU form above: every wave-wide weight load is one contiguous 512-byte
+ * block, and one mask-and-or yields two consecutive elements in the two halves
+ * of a 32-bit register.  qs_out holds rows*k/8 words, sb_out rows*k/group.
+ * QMOE_ERR_BLOCK unless rows % 16 == 0, k % 64 == 0 and k % group == 0. */
+int qmoe_split_int4(const uint32_t* words, const uint16_t* scales, const uint16_t* biases,
+                    int64_t rows, int64_t k, int32_t group, uint32_t* qs_out, uint32_t* sb_out);
 /* The 128-entry IQ2_XXS sign-mask table ([GGUF] sign-fix commit): entry i is
  * the 7 stored sign bits plus an 8th bit making the count of negated values
  * even.  HOST pointer to 128 bytes. */
@@ -159,9 +169,8 @@ int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t*
 int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
                          const uint8_t* grid, const uint8_t* signs, int64_t n_blocks,
                          void* out, int32_t out_dtype, void* stream);
-int qmoe_dequant_int4(const uint32_t* qs, const uint16_t* scales, const uint16_t* biases,
-                      int64_t rows, int64_t k, int32_t group,
-                      void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k,
+                      int32_t group, void* out, int32_t out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dense quantised matmul ([SHIM] mt_qmm_mma; [DSV4] wide-tile q8_0 qgemm):
@@ -183,13 +192,16 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
  * ids DEVICE int32 [t, topk]; pair p = row * topk + j.  Pairs with an id
  * outside [0, n_experts) are dropped and counted.  Within an expert, pairs
  * keep ascending pair order; each expert's run is cut into tiles of at most
- * `bm` rows (bm in {16, 32, 64, 128}).  The plan is unique.
+ * `bm` rows (bm a multiple of 16, at most 128).  The plan is unique.
  *
  * Layout of the DEVICE int32 plan buffer (size from qmoe_plan_bytes):
  *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts  [7] 0
  *   counts [n_experts] | offsets [n_experts + 1] | sorted pair ids [t * topk]
  *   | tiles [max_tiles][4] = (expert, row0, nrows, 0) | sorted position of
- *   each pair, -1 if dropped [t * topk]
+ *   each pair, -1 if dropped [t * topk] | scratch.  max_tiles is
+ *   min(t*topk, n_experts) + t*topk/16 (the tile array fits any bm); the
+ *   sorted list starts at word 8 + 2*n_experts + 1 and the tile array at the
+ *   next multiple of 4 words after it.
  * ------------------------------------------------------------------------ */
 size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm);
 int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts, int32_t bm,

@@ -58,15 +58,38 @@ def test_split_iq2_xxs_round_trip():
     assert np.array_equal(aux.view(np.uint8).reshape(-1, 8, 4), g[:, :, 4:])
 
 
-def test_split_int4_nibble_order():
+def test_split_int4_tiled_layout():
+    """Every element of the MLX rows lands where the header's tiled layout says."""
     rng = np.random.default_rng(3)
-    words = rng.integers(0, 2**32, size=257, dtype=np.uint64).astype(np.uint32)
-    out = qm.split_int4(words)
-    for w, o in zip(words[:20], out[:20]):
-        elems = [(int(w) >> (4 * i)) & 15 for i in range(8)]
-        for i in range(4):
-            assert (int(o) >> (4 * i)) & 15 == elems[2 * i]
-            assert (int(o) >> (4 * i + 16)) & 15 == elems[2 * i + 1]
+    rows, k, group = 48, 192, 64
+    words = rng.integers(0, 2**32, size=rows * k // 8, dtype=np.uint64).astype(np.uint32)
+    scale = rng.integers(0, 2**16, size=rows * k // group, dtype=np.uint64).astype(np.uint16)
+    bias = rng.integers(0, 2**16, size=rows * k // group, dtype=np.uint64).astype(np.uint16)
+    qs, sb = qm.split_int4(words, scale, bias, rows, k, group)
+    mlx = (words.reshape(rows, k // 8, 1) >> (4 * np.arange(8, dtype=np.uint32))) & 15  # element 8w+j -> nibble j
+    mlx = mlx.reshape(rows, k)
+    for R in range(rows):
+        for kk in range(k):
+            tile = (R // 16) * (k // 64) + kk // 64
+            lane = 16 * ((kk % 64) // 16) + R % 16
+            word = int(qs[(tile * 64 + lane) * 2 + (kk % 16) // 8])
+            j = kk % 8
+            assert (word >> (4 * (j // 2) + 16 * (j % 2))) & 15 == mlx[R, kk]
+    for R in range(rows):
+        for gi in range(k // group):
+            v = int(sb[((R // 16) * (k // group) + gi) * 16 + R % 16])
+            assert v & 0xFFFF == scale[R * (k // group) + gi] and v >> 16 == bias[R * (k // group) + gi]
+
+
+def test_split_int4_rejects_untileable_shapes():
+    z = np.zeros(16 * 96 // 8, np.uint32)
+    s = np.zeros(16 * 96 // 32, np.uint16)
+    with pytest.raises(qm.QmoeError):
+        qm.split_int4(z, s, s, 16, 96, 32)          # k not a multiple of 64
+    z = np.zeros(8 * 64 // 8, np.uint32)
+    s = np.zeros(8, np.uint16)
+    with pytest.raises(qm.QmoeError):
+        qm.split_int4(z, s, s, 8, 64, 64)           # rows not a multiple of 16
 
 
 def test_signs_table_matches_oracle():
@@ -79,6 +102,7 @@ def test_plan_bytes_layout():
     words = 8 + 256 + 257 + P
     words = (words + 3) & ~3
     words += 4 * (min(P, 256) + P // 16) + P
+    words += ((P + 1023) // 1024) * 256  # chunk histogram scratch
     assert n == 4 * words
 
 
@@ -88,7 +112,8 @@ def test_argument_validation_before_launch():
     # plan: topk above 8, experts above 1024, bad bm, NULL ids
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 9, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 2000, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
-    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 48, ctypes.c_void_p(16), 1 << 20, None) == E
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 40, ctypes.c_void_p(16), 1 << 20, None) == E
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 144, ctypes.c_void_p(16), 1 << 20, None) == E
     assert L.qmoe_moe_plan(None, 4, 2, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == E
     # plan buffer too small
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(16), 16, None) == -5
@@ -98,7 +123,9 @@ def test_argument_validation_before_launch():
     assert L.qmoe_dequant_q8_0(None, ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == E
     assert L.qmoe_dequant_q8_0(ctypes.c_void_p(8), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == -6
     assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 7, None) == E
-    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 96, 64,
+    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 96, 32,
+                               ctypes.c_void_p(16), 1, None) == -3
+    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 128, 64,
                                ctypes.c_void_p(16), 1, None) == -3
     # matmul: k not a block multiple, too many experts, wrong epilogue / dtype
     w = qm._Weights(qm.Q2_K, 1, 64, 320, 0, 0, 16, 0, 16, 0, 16, 16, 0, 0)

@@ -39,7 +39,7 @@ def _weights(fmt, rng):
     if fmt in ("q2_k", "iq2_xxs"):
         W = synth.weights(fmt, rng, 2, 37, 512)
     elif fmt == "int4":
-        W = synth.int4(rng, 2, 37, 512, 64)
+        W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
     else:
         W = synth.q8_0(rng, 2, 37, 512)
     return W
