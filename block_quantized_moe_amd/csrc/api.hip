@@ -23,7 +23,7 @@ void launch_qmm(const qmoe_weights*, const void*, int, int, const int32_t*, int6
                 int64_t, const float*, int, void*, int, hipStream_t);
 int qmm_int4_bf16_max_groups();
 int qmm_max_rows();
-void launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
+int launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
                  int, void*, int, hipStream_t);
 void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
 void launch_moe_combine(const void*, int, const int32_t*, int64_t, int, int, const float*, int64_t,
@@ -305,14 +305,13 @@ int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64
     if (!topk_w) return QMOE_ERR_ARG;
     if (!al4(topk_w)) return QMOE_ERR_ALIGN;
     if (w->n > (1ll << 31) / 64) return QMOE_ERR_LIMIT;
-    if (w->k < 512) return QMOE_ERR_UNSUPPORTED;  // at most 4 rows per wave pass
   } else if (epilogue != QMOE_EPI_STORE) {
     return QMOE_ERR_UNSUPPORTED;
   }
   if (!al16(a) || !al4(ids) || !al16(out)) return QMOE_ERR_ALIGN;
   if (b == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_gemv(w, a, act_dtype, b, ids, topk_w, topk, epilogue, out, out_dtype, (hipStream_t)stream);
+  QMOE_TRY(launch_gemv(w, a, act_dtype, b, ids, topk_w, topk, epilogue, out, out_dtype, (hipStream_t)stream));
   return launched();
 }
 

@@ -20,6 +20,8 @@
 // Integer codes are fed to the dot products exactly (as fp16 / bf16 values
 // with a known offset) and the per-block scale and bias are applied to the
 // fp32 partial sums.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qmoe {
@@ -400,6 +402,376 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- int4, tiled
+//
+// On the tiled int4 layout (16 rows x 64 k per contiguous 512-byte run) the
+// product of one expert with the few tokens routed to it runs on the matrix
+// cores: A = activations of up to 16 tokens (token m in lanes m, m+16, m+32,
+// m+48), B = the tile's exact integer codes C + q (C = 128 as bf16, 1024 as
+// fp16) in the tile's own k order, so lane l's 8-byte slice of the run is
+// exactly its B operand.  A second product against ones gives each token's
+// activation sum X over the tile, and per tile
+//     y[m][n] += s[n] * P[m][n] + (b[n] - C * s[n]) * X[m],
+// so scale and bias enter once per group, in fp32 (group >= 64 here).  More
+// than 16 tokens on one expert are taken in further passes; the weights stay
+// in registers between passes.
+
+template <int ACT> struct One;
+template <> struct One<ACT_F16> { static constexpr uint32_t bits = 0x3C003C00u; };
+template <> struct One<ACT_BF16> { static constexpr uint32_t bits = 0x3F803F80u; };
+
+// The eight codes of one word (elements 0..7) as four packed pairs.
+template <int ACT>
+__device__ __forceinline__ u4_t int4_codes(uint32_t q) {
+  u4_t c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = ((q >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
+  return c;
+}
+
+// One tile's contribution for NB row blocks: acc[b] += s * P + cb * X.
+template <int ACT, int NB>
+__device__ __forceinline__ void int4_tile(const u4_t& x0, const u4_t& x1, const u2_t (&w)[NB],
+                                          const uint32_t (&sb)[NB], f4_t (&acc)[NB]) {
+  const u4_t ones = u4_t{One<ACT>::bits, One<ACT>::bits, One<ACT>::bits, One<ACT>::bits};
+  const f4_t z = f4_t{0.f, 0.f, 0.f, 0.f};
+  f4_t X = mfma(as_v8<ACT>(x0), as_v8<ACT>(ones), z);
+  X = mfma(as_v8<ACT>(x1), as_v8<ACT>(ones), X);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    f4_t P = mfma(as_v8<ACT>(x0), as_v8<ACT>(int4_codes<ACT>(w[b][0])), z);
+    P = mfma(as_v8<ACT>(x1), as_v8<ACT>(int4_codes<ACT>(w[b][1])), P);
+    const float s = f16_to_f32(sb[b] & 0xFFFFu);
+    const float cb = __builtin_fmaf(-Magic<ACT>::v, s, f16_to_f32(sb[b] >> 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(cb, X[i], __builtin_fmaf(s, P[i], acc[b][i]));
+  }
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0
+// without touching memory.  base must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset that is always out of range
+
+// Slot ids of a call held in registers: lane l keeps slot 64c + l of chunk c
+// (-1 past the end), so the per-expert token lists below are ballots with no
+// memory traffic.  At most QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK = 512 slots.
+constexpr int GV_CH = (QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK) / 64;
+
+typedef int SlotIds[GV_CH];
+
+// Compile-time loop: f(std::integral_constant<int, c>) for c = C .. N-1, so
+// every register-array index below is a constant from the start.
+template <int C, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (C < N) {
+    f(std::integral_constant<int, C>{});
+    static_for<C + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ void load_slot_ids(const int32_t* ids, int P, SlotIds& s) {
+  const int lane = threadIdx.x & 63;
+  static_for<0, GV_CH>([&](auto ci) {
+    constexpr int c = decltype(ci)::value;
+    const int p = 64 * c + lane;
+    s[c] = ids[p < P ? p : 0];
+    if (p >= P) s[c] = -1;
+  });
+}
+
+// Expert of slot p (p wave-uniform, p < P), as a wave-uniform value.
+__device__ __forceinline__ int slot_expert(const SlotIds& s, int p) {
+  int v = s[0];
+  static_for<1, GV_CH>([&](auto ci) {
+    constexpr int c = decltype(ci)::value;
+    if ((p >> 6) == c) v = s[c];
+  });
+  return __builtin_amdgcn_readlane(v, p & 63);
+}
+
+// Slot of the j-th occurrence (in slot order) of expert e, or -1; *count
+// receives the number of occurrences.  Wave-wide.
+__device__ __forceinline__ int nth_slot(const SlotIds& s, int P, int e, int j, int* count) {
+  int base = 0, res = -1;
+  static_for<0, GV_CH>([&](auto ci) {
+    constexpr int c = decltype(ci)::value;
+    if (64 * c < P) {
+      const uint64_t m = __ballot(s[c] == e);
+      const int cnt = __popcll(m);
+      if (j >= base && j < base + cnt) {
+        uint64_t mm = m;
+        for (int i = base; i < j; ++i) mm &= mm - 1;
+        res = 64 * c + __ffsll((unsigned long long)mm) - 1;
+      }
+      base += cnt;
+    }
+  });
+  *count = base;
+  return res;
+}
+
+// STORE / SWIGLU.  grid = (16-unit blocks, slots), W waves; wave w takes
+// tiles [w*TPW, (w+1)*TPW) of K and the waves' sums meet in LDS.  With SWIGLU
+// a unit block is 16 gate rows and the 16 matching up rows.  A workgroup
+// whose slot repeats an earlier slot's expert exits at once; the first one
+// serves every token routed to that expert.  Four tiles per wave keep the
+// register count low enough for several workgroups per CU, so one
+// workgroup's loads overlap another's arithmetic.
+template <int ACT, int EPI, int W, int TPW>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_int4_rows_kernel(GemvArgs g) {
+  constexpr int NB = (EPI == QMOE_EPI_SWIGLU) ? 2 : 1;
+  __shared__ f4_t red[W - 1][NB][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform, kept in SGPRs
+  const int r = lane & 15, lg = lane >> 4;
+  const int slot = blockIdx.y;
+  const int P = g.nslots;
+  SlotIds sid;
+  load_slot_ids(g.ids, P, sid);
+  const int e = slot_expert(sid, slot);
+  if (e < 0 || e >= g.E) return;
+  int nt;
+  if (nth_slot(sid, P, e, 0, &nt) != slot) return;  // an earlier slot serves e
+
+  // group is a power of two >= 64: tile kt lies in group kt >> gsh
+  const int gsh = __builtin_ctz((unsigned)g.group) - 6;
+  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
+  const int64_t Nunits = (EPI == QMOE_EPI_SWIGLU) ? g.N / 2 : g.N;
+  const int64_t u0 = (int64_t)blockIdx.x * 16;
+  int64_t rb[NB];
+  rb[0] = ((int64_t)e * g.N + u0) >> 4;
+  if constexpr (NB == 2) rb[1] = ((int64_t)e * g.N + Nunits + u0) >> 4;
+  const int kt0 = wave * TPW;
+
+  // Activations first (token sl / topk in this lane, zeros past the list),
+  // then the weights: every load of the first pass is in flight at once.
+  const __amdgpu_buffer_rsrc_t xrs = rsrc(g.a, (uint32_t)((int64_t)(P / g.topk) * K * 2));
+  int cnt;
+  int sl = nth_slot(sid, P, e, r, &cnt);
+  u4_t x[TPW][2];
+  auto load_x = [&]() {
+    const uint32_t xo = sl >= 0 ? (uint32_t)(((int64_t)(sl / g.topk) * K + 16 * lg) * 2) : OOB;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const uint32_t kb = (uint32_t)(min((int64_t)(kt0 + t), T - 1) * 128);
+      x[t][0] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + kb, 0, 0));
+      x[t][1] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + kb + 16, 0, 0));
+    }
+  };
+  load_x();
+  // Weights through buffer resources over the block's tiles: one address
+  // register for all loads, and tiles past K read as zero.
+  u2_t w[TPW][NB];
+  uint32_t sb[TPW][NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const __amdgpu_buffer_rsrc_t wr = rsrc((const uint32_t*)g.qs + rb[b] * T * 128, (uint32_t)(T * 512));
+    const __amdgpu_buffer_rsrc_t sr = rsrc((const uint32_t*)g.scales + rb[b] * G * 16, (uint32_t)(G * 64));
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      w[t][b] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr, (uint32_t)(lane * 8 + (kt0 + t) * 512), 0, 0));
+      sb[t][b] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(r * 4 + ((kt0 + t) >> gsh) * 64), 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+
+  for (int pass = 0; pass < nt; pass += 16) {
+    if (pass > 0) {
+      sl = nth_slot(sid, P, e, pass + r, &cnt);
+      load_x();
+    }
+    f4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      if (kt0 + t < T) int4_tile<ACT, NB>(x[t][0], x[t][1], w[t], sb[t], acc);
+    if (wave > 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave - 1][b][lane] = acc[b];
+    }
+    lds_barrier();
+    if (wave == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < W - 1; ++v) acc[b] += red[v][b][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * lg + i;
+        const int sm = __shfl(sl, m);
+        if (pass + m < nt) {
+          const float v = (EPI == QMOE_EPI_SWIGLU) ? silu_f32(acc[0][i]) * acc[NB - 1][i] : acc[0][i];
+          store_out(g.out, g.out_dtype, (int64_t)sm * Nunits + u0 + r, v);
+        }
+      }
+    }
+    if (pass + 16 < nt) lds_barrier();  // red[] is reused by the next pass
+  }
+}
+
+// WEIGHTED_COMBINE (sum-folded down projection).  grid = 16-row blocks, 8
+// waves.  The per-slot input rows are staged in LDS (dynamic: P * 16 fp32
+// results, then (P + 1) padded input rows, the last one zero).  Wave w takes
+// the experts first seen at slots w, w + 8, ... over the whole K (at most 8
+// tiles), with the next expert's weights loaded while the current one is
+// computed.  The per-slot results land in LDS by slot and the top-k weighted
+// sum per token is then formed in slot order, so the result is
+// bit-reproducible.
+constexpr int GC_WAVES = 8;
+constexpr int GC_LDS = 73728;  // dynamic LDS limit (bytes) for the combine
+
+__host__ __device__ constexpr int64_t gc_lds_bytes(int64_t P, int64_t K) {
+  return P * 64 + (P + 1) * (K + 8) * 2;
+}
+
+template <int ACT>
+__global__ __launch_bounds__(GC_WAVES * 64) void gemv_int4_combine_kernel(GemvArgs g) {
+  constexpr int TPE = 8;
+  extern __shared__ __attribute__((aligned(16))) uint8_t gc_dyn[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, lg = lane >> 4;
+  const int P = g.nslots;
+  const int gsh = __builtin_ctz((unsigned)g.group) - 6;
+  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
+  const int xstride = (int)K + 8;  // padded LDS row: consecutive slots start 4 banks apart
+  float* ybuf = (float*)gc_dyn;                       // [P][16]
+  uint16_t* xs = (uint16_t*)(gc_dyn + (int64_t)P * 64);  // [P + 1][K + 8]
+  const int64_t rblk = blockIdx.x;  // 16-row block within each expert
+  const uint32_t wbytes = (uint32_t)(T * 512), sbytes = (uint32_t)(G * 64);
+
+  SlotIds sid;
+  load_slot_ids(g.ids, P, sid);
+
+  // The next slot p' >= p (p' = p mod 8) where an expert is first seen, or P.
+  auto next_first = [&](int p) {
+    for (; p < P; p += GC_WAVES) {
+      const int e = slot_expert(sid, p);
+      int c;
+      if (e >= 0 && e < g.E && nth_slot(sid, P, e, 0, &c) == p) return p;
+    }
+    return P;
+  };
+  // Two register buffers, selected at compile time (ping-pong over experts).
+  // Slot P loads nothing (empty resource).
+  u2_t wa[TPE][1], wb[TPE][1];
+  uint32_t sa[TPE][1], sbb[TPE][1];
+  auto load_expert = [&](u2_t (&w)[TPE][1], uint32_t (&sb)[TPE][1], int p) {
+    const bool ok = p < P;
+    const int e = ok ? slot_expert(sid, p) : 0;
+    const int64_t rb = ((int64_t)e * g.N >> 4) + rblk;
+    const __amdgpu_buffer_rsrc_t wr = rsrc((const uint32_t*)g.qs + rb * T * 128, ok ? wbytes : 0u);
+    const __amdgpu_buffer_rsrc_t sr = rsrc((const uint32_t*)g.scales + rb * G * 16, ok ? sbytes : 0u);
+#pragma unroll
+    for (int t = 0; t < TPE; ++t) {
+      // offsets in the vector operand only: the range check covers them
+      w[t][0] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr, (uint32_t)(lane * 8 + t * 512), 0, 0));
+      sb[t][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(r * 4 + (t >> gsh) * 64), 0, 0);
+    }
+  };
+  auto run_expert = [&](const u2_t (&w)[TPE][1], const uint32_t (&sb)[TPE][1], int p) {
+    const int e = slot_expert(sid, p);
+    int nt = 1;
+    for (int pass = 0; pass < nt; pass += 16) {
+      const int sl = nth_slot(sid, P, e, pass + r, &nt);
+      const uint16_t* xr = xs + (sl >= 0 ? sl : P) * xstride + 16 * lg;
+      f4_t acc[1] = {f4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int t = 0; t < TPE; ++t) {
+        if (t < T) {
+          const u4_t x0 = *(const u4_t*)(xr + t * 64);
+          const u4_t x1 = *(const u4_t*)(xr + t * 64 + 8);
+          int4_tile<ACT, 1>(x0, x1, w[t], sb[t], acc);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * lg + i;
+        const int sm = __shfl(sl, m);
+        if (pass + m < nt) ybuf[sm * 16 + r] = acc[0][i];
+      }
+    }
+  };
+
+  int pa = next_first(wave);
+  load_expert(wa, sa, pa);
+  // stage every slot's input row (8 values per u4) plus the zero row P
+  const int per_row = (int)(K >> 3);
+  for (int i = tid; i < (P + 1) * per_row; i += GC_WAVES * 64) {
+    const int p = i / per_row, c = i - p * per_row;
+    *(u4_t*)(xs + p * xstride + 8 * c) =
+        p < P ? *(const u4_t*)(g.a + (int64_t)p * K + 8 * c) : u4_t{0, 0, 0, 0};
+  }
+  lds_barrier();
+  while (pa < P) {
+    const int pb = next_first(pa + GC_WAVES);
+    load_expert(wb, sbb, pb);
+    run_expert(wa, sa, pa);
+    if (pb >= P) break;
+    pa = next_first(pb + GC_WAVES);
+    load_expert(wa, sa, pa);
+    run_expert(wb, sbb, pb);
+  }
+  lds_barrier();
+  const int btok = P / g.topk;
+  for (int i = tid; i < btok * 16; i += GC_WAVES * 64) {
+    const int b = i >> 4, n = i & 15;
+    float v = 0.f;
+    for (int j = 0; j < g.topk; ++j) {
+      const int p = b * g.topk + j;
+      const int e = g.ids[p];
+      if (e >= 0 && e < g.E) v = __builtin_fmaf(g.topk_w[p], ybuf[p * 16 + n], v);
+    }
+    store_out(g.out, g.out_dtype, (int64_t)b * g.N + rblk * 16 + n, v);
+  }
+}
+
+// Whether the tiled int4 kernels take this call (else the generic ones do).
+static bool int4_tiled_ok(const GemvArgs& g, int epi) {
+  if (g.group < 64 || g.K > 4096) return false;
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE)
+    return g.N % 16 == 0 && g.K <= 512 && gc_lds_bytes(g.nslots, g.K) <= GC_LDS;
+  return g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16) == 0;
+}
+
+template <int ACT>
+static void launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE) {  // K <= 512: eight tiles per expert
+    static bool attr_set = false;  // raise the dynamic LDS limit once per process
+    if (!attr_set) {
+      hipFuncSetAttribute((const void*)gemv_int4_combine_kernel<ACT>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, GC_LDS);
+      attr_set = true;
+    }
+    const dim3 grid((unsigned)(g.N / 16));
+    hipLaunchKernelGGL((gemv_int4_combine_kernel<ACT>), grid, dim3(GC_WAVES * 64),
+                       (size_t)gc_lds_bytes(g.nslots, g.K), s, g);
+    return;
+  }
+  const int64_t units = epi == QMOE_EPI_SWIGLU ? g.N / 2 : g.N;
+  const dim3 grid((unsigned)(units / 16), (unsigned)g.nslots);
+  const int64_t T = g.K / 64;
+  // four tiles per wave from 16 tiles up; 4, 8 or 16 waves
+#define QMOE_ROWS(EPI_, W_, TPW_) \
+  hipLaunchKernelGGL((gemv_int4_rows_kernel<ACT, EPI_, W_, TPW_>), grid, dim3(W_ * 64), 0, s, g)
+#define QMOE_ROWS_EPI(EPI_)                         \
+  do {                                              \
+    if (T <= 8) QMOE_ROWS(EPI_, 4, 2);              \
+    else if (T <= 16) QMOE_ROWS(EPI_, 4, 4);        \
+    else if (T <= 32) QMOE_ROWS(EPI_, 8, 4);        \
+    else QMOE_ROWS(EPI_, 16, 4);                    \
+  } while (0)
+  if (epi == QMOE_EPI_SWIGLU) QMOE_ROWS_EPI(QMOE_EPI_SWIGLU);
+  else QMOE_ROWS_EPI(QMOE_EPI_STORE);
+#undef QMOE_ROWS_EPI
+#undef QMOE_ROWS
+}
+
 template <int FMT, int ACT, int CPL>
 static void launch_gemv_fac(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
   if (epi == QMOE_EPI_WEIGHTED_COMBINE) {
@@ -427,7 +799,9 @@ static void launch_gemv_f(const GemvArgs& g, int act, int cpl, int epi, int64_t 
 }
 
 // Host launcher for qmoe_moe_gemv (arguments already validated; K <= 4096).
-void launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const int32_t* ids,
+// Returns QMOE_ERR_UNSUPPORTED for a sum-folded call that neither kernel
+// family takes (the generic one needs K >= 512: at most 4 rows per wave pass).
+int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const int32_t* ids,
                  const float* topk_w, int topk, int epi, void* out, int out_dtype, hipStream_t s) {
   GemvArgs g;
   g.qs = w->qs; g.aux = w->aux; g.scales = w->scales; g.biases = w->biases;
@@ -447,12 +821,19 @@ void launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const
   upw = (upw + 4 * rpw - 1) / (4 * rpw) * (4 * rpw);
   if (upw > 64) upw = 64 > 4 * rpw ? 64 : 4 * rpw;
   g.units_per_wg = (int)upw;
+  if (w->fmt == QMOE_INT4 && int4_tiled_ok(g, epi)) {
+    if (act == QMOE_F16) launch_gemv_int4_tiled<ACT_F16>(g, epi, s);
+    else launch_gemv_int4_tiled<ACT_BF16>(g, epi, s);
+    return QMOE_OK;
+  }
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE && w->k < 512) return QMOE_ERR_UNSUPPORTED;
   switch (w->fmt) {
     case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
     case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;
     case QMOE_IQ2_XXS: launch_gemv_f<QMOE_IQ2_XXS>(g, act, cpl, epi, units, s); break;
     default: launch_gemv_f<QMOE_INT4>(g, act, cpl, epi, units, s); break;
   }
+  return QMOE_OK;
 }
 
 }  // namespace qmoe

@@ -96,3 +96,24 @@ def test_gemv_dropped_ids_contribute_nothing():
     ids_c = np.where(valid.reshape(ids.shape), ids, 0)
     oref = oracle.moe_down_combine(np.where(valid[:, None], hg, 0.0), ids_c, w, inp.w_down)
     assert normwise_err(to_f64(out), oref, "bf16") <= TOL
+
+
+def test_gemv_int4_many_tokens_per_expert():
+    # 32 tokens on each of two experts: the int4 kernels take tokens 16 at a time
+    rng = np.random.default_rng(12)
+    B, E, k, H, I = 32, 2, 2, 512, 256
+    x = synth.activations(rng, B, H, "bf16")
+    ids = np.tile(np.array([[0, 1]], np.int32), (B, 1))
+    ids[::3] = ids[::3, ::-1]
+    w = rng.random((B, k)).astype(np.float32)
+    _check(x, ids, w, synth.int4(rng, E, 2 * I, H), synth.int4(rng, E, H, I), "bf16")
+
+
+@pytest.mark.parametrize("group,I", [(32, 512), (64, 1024)])
+def test_gemv_int4_generic_shapes(group, I):
+    # group 32 and a down projection with K = 1024 take the generic kernels
+    rng = np.random.default_rng(group + I)
+    B, E, k, H = 3, 8, 4, 512
+    x = synth.activations(rng, B, H, "bf16")
+    ids, w = synth.routing_softmax(rng, B, E, k)
+    _check(x, ids, w, synth.int4(rng, E, 2 * I, H, group), synth.int4(rng, E, H, I, group), "bf16")
