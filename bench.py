@@ -13,6 +13,10 @@ The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers of weights rotated)
 and the CPU oracle baseline are reported in the same JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+Counter calibration and the traffic record (see profiles/):
+    python bench.py --copy-probe MIB
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR MIB
 """
 from __future__ import annotations
 
@@ -200,17 +204,87 @@ def cpu_baseline(n_tokens):
                        f"fp64 oracle, {dt:.1f} s", tokens_per_s=n_tokens / dt, seconds=dt)
 
 
+def copy_probe(mb, reps=20):
+    """A plain device copy of known size (the runtime's copy kernel), run under
+    rocprofv3 --pmc to calibrate FETCH_SIZE / WRITE_SIZE against true bytes."""
+    import torch
+    a = torch.ones(mb << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} copies of {mb} MiB")
+
+
+def _pmc_median_kib(run_dir, counter, name_part):
+    """Median per-dispatch value (summed over the counter's instances) of one
+    counter for the kernels whose name contains name_part."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} samples for '{name_part}' under {run_dir}")
+    return float(np.median(list(per.values()))), len(per)
+
+
+def _gemm_source_hash():
+    """sha256 of the GEMM kernel source with comments and blank lines removed
+    (the traffic record stays valid across comment-only edits)."""
+    import hashlib
+    import re
+    src = open(os.path.join(ROOT, "block_quantized_moe_amd", "csrc", "gemm.hip")).read()
+    code = [re.sub(r"//.*", "", l).rstrip() for l in src.splitlines()]
+    return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, out):
+    """Turn four rocprofv3 --pmc runs (gate/up FETCH_SIZE, WRITE_SIZE; copy
+    probe FETCH_SIZE, WRITE_SIZE) into HBM bytes per gate/up launch."""
+    kern = "qmm_kernel<3, 1, 1>"
+    f_kib, nf = _pmc_median_kib(fetch_dir, "FETCH_SIZE", kern)
+    w_kib, nw = _pmc_median_kib(write_dir, "WRITE_SIZE", kern)
+    cf_kib, _ = _pmc_median_kib(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw_kib, _ = _pmc_median_kib(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    true = float(copy_mb << 20)
+    k_fetch, k_write = true / (cf_kib * 1024), true / (cw_kib * 1024)
+    inp = prefill_inputs(2048)
+    alg = algorithmic(inp)
+    rec = {
+        "kernel": "qmm_kernel<INT4, bf16, SWIGLU> (gate/up), qwen3.6-a3b-shaped prefill",
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+        "copy_probe_mib": copy_mb, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+        "fetch_scale": k_fetch, "write_scale": k_write,
+        "bytes_per_launch": f_kib * 1024 * k_fetch + w_kib * 1024 * k_write,
+        "algorithmic_bytes_per_launch": alg["bytes_gu"],
+        "gemm_code_sha256": _gemm_source_hash(),
+    }
+    rec["traffic_over_algorithmic"] = rec["bytes_per_launch"] / alg["bytes_gu"]
+    pm = "rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py {a}"
+    prefill = "--steps 3 --warmup 1 --no-decode --no-cpu"
+    rec["commands"] = [pm.format(c="FETCH_SIZE", d=fetch_dir, a=prefill),
+                       pm.format(c="WRITE_SIZE", d=write_dir, a=prefill),
+                       pm.format(c="FETCH_SIZE", d=copy_fetch_dir, a=f"--copy-probe {copy_mb}"),
+                       pm.format(c="WRITE_SIZE", d=copy_write_dir, a=f"--copy-probe {copy_mb}"),
+                       f"python3 bench.py --summarize-traffic {fetch_dir} {write_dir} {copy_fetch_dir} "
+                       f"{copy_write_dir} {copy_mb}"]
+    rec["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch summed over instances, scaled by "
+                   "true bytes / counter bytes of a device copy of known size.")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def traffic_from_profiles():
     """HBM bytes per gate/up launch measured with rocprofv3 counters, if the
-    committed measurement matches the current kernel source."""
-    import hashlib
+    committed measurement was taken on the current kernel code."""
     p = os.path.join(ROOT, "profiles", "gate_up_qwen_prefill_traffic.json")
-    src = os.path.join(ROOT, "block_quantized_moe_amd", "csrc", "gemm.hip")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return rec.get("bytes_per_launch") if rec.get("gemm_sha256") == h else None
+    return rec.get("bytes_per_launch") if rec.get("gemm_code_sha256") == _gemm_source_hash() else None
 
 
 def main():
@@ -221,10 +295,23 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--decode-reps", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="only run a device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-traffic", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "COPY_MIB"),
+                    help="write profiles/gate_up_qwen_prefill_traffic.json from rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        d = args.summarize_traffic
+        summarize_traffic(d[0], d[1], d[2], d[3], int(d[4]),
+                          os.path.join(ROOT, "profiles", "gate_up_qwen_prefill_traffic.json"))
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU layout is described, not built).", file=sys.stderr)

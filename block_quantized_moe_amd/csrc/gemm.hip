@@ -1,7 +1,7 @@
 // Prefill matmul over quantised weights: the gathered MoE tile GEMM and the
 // dense qmm share one kernel.
 //
-// What is computed: for each tile of (up to 128) rows routed to one expert
+// What is computed: for each tile of (up to 80) rows routed to one expert
 // and a slice of that expert's output rows, y = A . W[e]^T with fp32
 // accumulation, followed by an epilogue (store, SwiGLU, top-k weighted
 // scatter-add, or accumulate).  The DSV4 campaign page's tiled MoE prefill
@@ -15,7 +15,7 @@
 //    blocks of gate rows and the two matching blocks of up rows, so
 //    silu(g)*u is lane-local).  One B fragment feeds every 16-row block of the
 //    tile; one A fragment feeds the wave's four column blocks.
-//  * K advances in 64-wide tiles.  The activation tile (128 x 64) is gathered
+//  * K advances in 64-wide tiles.  The activation tile (80 x 64) is gathered
 //    by routed row straight into LDS, double buffered, one barrier per tile.
 //    The weight bytes each lane needs are loaded straight into registers two
 //    tiles ahead (ping-pong buffers), so the HBM stream has two tiles of every

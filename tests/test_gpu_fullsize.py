@@ -1,0 +1,138 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (routing plan with bm = 80, gathered gate/up with SwiGLU,
+gathered down with the top-k weighted scatter-add, cast), checked on sampled
+outputs that the fp64 oracle computes one by one:
+
+  * Qwen3.6-A3B-shaped int4 prefill: T = 2048, H = 2048, E = 256, I = 512, k = 8
+  * DSv4-flash-shaped prefill: T = 2048, H = 4096, E = 256, I = 2048, k = 6,
+    IQ2_XXS gate/up, Q2_K down, fp16 activations
+  * mixed-format FFN block: T = 8192, H = 4096, E = 256, I = 2048, k = 8, Zipf
+    routing, plus a Q8_0 shared expert and four Q8_0 4096 x 4096 projections,
+    bf16 combine output
+
+Stage-wise (each GEMM is fed the bytes the GPU consumed): sampled h entries
+against the oracle's gate/up rows, sampled outputs against the oracle's down
+rows fed the GPU's h.  Tolerance: the normwise 2e-3 bound of tests/_helpers.
+"""
+import numpy as np
+import pytest
+
+import block_quantized_moe_amd as qm
+import oracle
+import synth
+from _helpers import CODES, TOL, normwise_err, report, to_f64, torch_act, upload
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+BM = 80  # the benchmark's tile height
+
+
+def _run_moe(inp):
+    """The benchmark's prefill sequence; returns device tensors and the plan."""
+    T, k, E = inp.T, inp.k, inp.E
+    act = CODES[inp.act]
+    x = torch_act(inp.x, inp.act)
+    ids = torch.from_numpy(inp.ids).cuda()
+    w = torch.from_numpy(inp.w).cuda()
+    gu, dn = upload(inp.w_gate_up), upload(inp.w_down)
+    plan = qm.moe_plan(ids, E, BM)
+    h = qm.moe_gather_qmm(gu, plan, T, k, x, bm=BM, epilogue=qm.EPI_SWIGLU, out_dtype=act)
+    acc = torch.zeros((T, inp.H), dtype=torch.float32, device="cuda")
+    qm.moe_gather_qmm(dn, plan, T, k, h, bm=BM, a_mode=qm.A_SORTED_ROWS, topk_w=w,
+                      epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+    del gu, dn
+    return x, plan, h, acc
+
+
+def _check_gate_up(inp, plan, h, rng, n_pairs=48, n_cols=64):
+    P = inp.T * inp.k
+    pairs = rng.choice(P, n_pairs, replace=False)
+    cols = rng.choice(inp.I, n_cols, replace=False)
+    x64 = oracle.act_to_f64(inp.x, inp.act)
+    ref = oracle.moe_gate_up_rows(x64, inp.ids, inp.w_gate_up, pairs, cols)
+    pos = qm.plan_views(plan, inp.T, inp.k, inp.E)["inv"].cpu().numpy()
+    got = to_f64(h[torch.from_numpy(pos[pairs]).long().cuda()])[:, cols]
+    err = normwise_err(got, ref, inp.act)
+    assert err <= TOL, ("gate/up", err, report(got, ref))
+
+
+def _h_rows(inp, plan, h, tokens):
+    """fp64 h of every pair of the given tokens, as the GPU stored it."""
+    pos = qm.plan_views(plan, inp.T, inp.k, inp.E)["inv"].cpu().numpy()
+    pairs = [t * inp.k + j for t in tokens for j in range(inp.k)]
+    hh = to_f64(h[torch.from_numpy(pos[pairs]).long().cuda()])
+    return {p: hh[i] for i, p in enumerate(pairs)}
+
+
+def test_fullsize_qwen_a3b_int4_prefill():
+    inp = synth.qwen_a3b_prefill(2048)
+    rng = np.random.default_rng(101)
+    x, plan, h, acc = _run_moe(inp)
+    out = qm.combine_cast(acc, CODES[inp.out])
+    torch.cuda.synchronize()
+    _check_gate_up(inp, plan, h, rng)
+    tokens = rng.choice(inp.T, 24, replace=False)
+    cols = rng.choice(inp.H, 64, replace=False)
+    ref = oracle.moe_down_rows(_h_rows(inp, plan, h, tokens), inp.ids, inp.w, inp.w_down, tokens, cols)
+    got = to_f64(out[torch.from_numpy(tokens).long().cuda()])[:, cols]
+    err = normwise_err(got, ref, inp.out)
+    assert err <= TOL, ("down+combine", err, report(got, ref))
+
+
+def test_fullsize_dsv4_flash_prefill():
+    inp = synth.dsv4_flash_prefill(2048)
+    rng = np.random.default_rng(102)
+    x, plan, h, acc = _run_moe(inp)
+    out = qm.combine_cast(acc, CODES[inp.out])
+    torch.cuda.synchronize()
+    _check_gate_up(inp, plan, h, rng)
+    tokens = rng.choice(inp.T, 16, replace=False)
+    cols = rng.choice(inp.H, 64, replace=False)
+    ref = oracle.moe_down_rows(_h_rows(inp, plan, h, tokens), inp.ids, inp.w, inp.w_down, tokens, cols)
+    got = to_f64(out[torch.from_numpy(tokens).long().cuda()])[:, cols]
+    err = normwise_err(got, ref, inp.out)
+    assert err <= TOL, ("down+combine", err, report(got, ref))
+
+
+def test_fullsize_mixed_ffn_block():
+    inp = synth.mixed_ffn(8192)
+    rng = np.random.default_rng(103)
+    x, plan, h, acc = _run_moe(inp)
+    act = CODES[inp.act]
+    # shared expert: silu(g) * u, then added into the fp32 combine buffer
+    sgu, sdn = upload(inp.shared_gate_up), upload(inp.shared_down)
+    hs = qm.qmm_dense(sgu, x, qm.EPI_SWIGLU, act)
+    qm.qmm_dense(sdn, hs, qm.EPI_ACCUMULATE, qm.F32, out=acc)
+    out = qm.combine_cast(acc, CODES[inp.out])
+    proj = [qm.qmm_dense(upload(Wp), x, qm.EPI_STORE, act) for Wp in inp.projections]
+    torch.cuda.synchronize()
+    _check_gate_up(inp, plan, h, rng)
+
+    x64 = oracle.act_to_f64(inp.x, inp.act)
+    tokens = rng.choice(inp.T, 16, replace=False)
+    # shared gate/up on sampled tokens and columns
+    SI = inp.shared_down.K
+    scols = rng.choice(SI, 64, replace=False)
+    Wg = oracle.dequant_rows(inp.shared_gate_up, 0, np.concatenate([scols, scols + SI])).astype(np.float64)
+    gu = x64[tokens] @ Wg.T
+    ref_hs = oracle.silu(gu[:, :64]) * gu[:, 64:]
+    tok_d = torch.from_numpy(tokens).long().cuda()
+    hs64 = to_f64(hs[tok_d])
+    err = normwise_err(hs64[:, scols], ref_hs, inp.act)
+    assert err <= TOL, ("shared gate/up", err)
+    # routed down + combine + shared down (stage-wise: the GPU's h and hs)
+    cols = rng.choice(inp.H, 64, replace=False)
+    ref = oracle.moe_down_rows(_h_rows(inp, plan, h, tokens), inp.ids, inp.w, inp.w_down, tokens, cols)
+    Wsd = oracle.dequant_rows(inp.shared_down, 0, cols).astype(np.float64)
+    ref = ref + hs64 @ Wsd.T
+    got = to_f64(out[tok_d])[:, cols]
+    err = normwise_err(got, ref, inp.out)
+    assert err <= TOL, ("down+combine+shared", err, report(got, ref))
+    # the four projections
+    for j, Wp in enumerate(inp.projections):
+        pc = rng.choice(inp.H, 64, replace=False)
+        refp = x64[tokens] @ oracle.dequant_rows(Wp, 0, pc).astype(np.float64).T
+        gotp = to_f64(proj[j][tok_d])[:, pc]
+        err = normwise_err(gotp, refp, inp.act)
+        assert err <= TOL, (f"projection {j}", err, report(gotp, refp))

@@ -263,3 +263,54 @@ def test_round_bf16_ties_and_specials():
 def test_round_f16_subnormal_and_tie():
     got = oracle.round_f16(np.array([2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 1 + 2 ** -11], np.float32))
     assert list(got) == [0x0001, 0x0000, 0x0002, 0x3C00]
+
+
+# ------------------------------------------------------------ golden layouts
+
+def _golden_layouts():
+    import os
+    rows = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "block_layouts.txt")):
+        if line.strip() and not line.startswith("#"):
+            key, *vals = line.split()
+            rows[key] = [int(v) for v in vals]
+    return rows
+
+
+def test_golden_block_layouts():
+    """tests/golden/block_layouts.txt: block sizes and first code byte as the
+    pages state them; a code planted at that byte decodes into element 0."""
+    g = _golden_layouts()
+    rng = np.random.default_rng(0)
+    # Q8_0: fp16 scale 1.0, code 5 at the first code byte -> element 0 == 5
+    vals, nbytes, first = g["q8_0"]
+    blk = np.zeros((1, nbytes), np.uint8)
+    blk[0, 0:2] = np.frombuffer(struct.pack("<H", h16(1.0)), np.uint8)
+    blk[0, first] = 5
+    v = oracle.dequant_q8_0(blk)
+    assert v.shape[-1] == vals and v.reshape(-1)[0] == 5.0 and np.all(v.reshape(-1)[1:] == 0)
+    assert synth.q8_0(rng, 1, 1, vals).blocks.shape[-1] == nbytes
+    # Q2_K: every sub-block scale 1 / min 0, d = 1, dmin = 0, code 3 in the
+    # low 2 bits of the first code byte -> element 0 == 3, all others 0
+    vals, nbytes, first = g["q2_k"]
+    blk = np.zeros((1, nbytes), np.uint8)
+    blk[0, 0:16] = 0x01
+    blk[0, first] = 0x03
+    blk[0, nbytes - 4:nbytes - 2] = np.frombuffer(struct.pack("<H", h16(1.0)), np.uint8)
+    v = oracle.dequant_q2_k(blk).reshape(-1)
+    assert v.size == vals and v[0] == 3.0 and np.all(v[1:] == 0)
+    assert synth.q2_k(rng, 1, 1, vals).blocks.shape[-1] == nbytes
+    # IQ2_XXS: d = 8 and scale nibble 0 give group scale 1; grid index 1 in
+    # the first code byte, no signs -> elements 0..7 == grid row 1
+    vals, nbytes, first = g["iq2_xxs"]
+    rows, per_row, total = g["grid"]
+    grid = synth.iq2_grid()
+    assert grid.size == total and grid.shape == (rows, per_row)
+    blk = np.zeros((1, nbytes), np.uint8)
+    blk[0, 0:2] = np.frombuffer(struct.pack("<H", h16(8.0)), np.uint8)
+    blk[0, first] = 1
+    v = oracle.dequant_iq2_xxs(blk, grid).reshape(-1)
+    assert v.size == vals
+    assert np.array_equal(v[:8], grid[1].astype(np.float32))
+    assert np.array_equal(v[8:32], np.repeat(grid[0].astype(np.float32)[None], 3, 0).reshape(-1))
+    assert synth.iq2_xxs(rng, 1, 1, vals).blocks.shape[-1] == nbytes

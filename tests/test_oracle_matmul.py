@@ -9,6 +9,8 @@ dense matmul.
 import math
 import struct
 
+import os
+
 import numpy as np
 import pytest
 
@@ -84,12 +86,24 @@ def test_plan_against_sorted_and_invariants():
     assert rows == list(range(len(keep)))
 
 
+def _golden(name):
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    rows = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            key, *vals = line.split()
+            rows[key] = vals
+    return rows
+
+
 def test_router_worked_example():
-    # GPU router top-K test on the "Everything Bagel 2" page: logits (1,5,3,4),
-    # k = 2 picks experts {1, 3}; the weights sum to 1 and the larger logit dominates.
-    ids, w = synth.topk_from_logits(np.array([[1.0, 5.0, 3.0, 4.0]], np.float32), 2)
-    assert set(ids[0].tolist()) == {1, 3}
-    assert abs(float(w.sum()) - 1.0) < 1e-6
+    # tests/golden/router_topk.txt: the router top-K test case of the
+    # "Everything Bagel 2" page; the larger logit also gets the larger weight.
+    g = _golden("router_topk.txt")
+    logits = np.array([[float(v) for v in g["logits"]]], np.float32)
+    ids, w = synth.topk_from_logits(logits, int(g["k"][0]))
+    assert set(ids[0].tolist()) == {int(v) for v in g["experts"]}
+    assert abs(float(w.sum()) - float(g["weight_sum"][0])) < 1e-6
     assert w[0][list(ids[0]).index(1)] > w[0][list(ids[0]).index(3)]
 
 
