@@ -35,6 +35,8 @@
 //    sum_g (b_g - 128 s_g) * X_g (X_g = sum of the activations of group g,
 //    computed by an MFMA against ones) is added at the end by three MFMAs
 //    over the groups with hi/lo bf16 splits of X and of the bias.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qmoe {
@@ -695,6 +697,406 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
   qmm_body<FMT, ACT, EPI, MB>(g, c);
 }
 
+// ------------------------------------------------------------------ int4: LDS ring
+//
+// int4 on the tiled layout streams both operands through a 3-stage LDS ring
+// with direct-to-LDS loads (buffer/global_load ... lds), so two K tiles of
+// weights and gathered activations are in flight while a third is computed,
+// without holding them in registers.  Per K tile and wave: three 16-byte
+// loads of gathered activation chunks (rows past the tile read as zero), two
+// of weight runs (the wave's four 16-row blocks, 512 bytes each) and one of
+// packed scale|bias words.  LDS-DMA completion is tracked by vmcnt, which the
+// compiler does not see for these loads, so the waits are explicit: before
+// tile kt is read, only tile kt+1's loads may still be outstanding.  One
+// LDS-only barrier per tile publishes the activation chunks of all waves and
+// frees the stage the next loads overwrite.
+//
+// Activation rows are stored unpadded with the 16-byte chunks of row r
+// permuted by c ^ ((r ^ (r >> 3)) & 7), so the rows an MFMA fragment read
+// touches land in distinct 16-byte bank groups whether the LDS serves 8 or 16
+// lanes of a 16-byte read per cycle.
+
+constexpr int RS = 3;                      // ring stages
+constexpr int R_ACH = 768;                 // activation chunks per stage (80 rows x 8, padded to 3 loads per wave)
+constexpr int R_A = R_ACH * 16;            // 12288 B
+constexpr int R_B = 4 * 4 * 512;           // 4 waves x 4 blocks x 512 B
+constexpr int R_SB = 4 * 4 * 64;           // 4 waves x 4 blocks x 16 rows x 4 B
+constexpr int R_STAGE = R_A + R_B + R_SB;  // 21504 B
+constexpr int R_NL = 6;                    // ring loads per wave per tile
+constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS-DMA issue.  Written as inline asm so that the compiler, which cannot
+// tell which ring stage a DMA writes, does not drain every outstanding load
+// (vmcnt(0)) before each LDS read; the ring waits for its own transfers
+// explicitly.  Extra loads the compiler does not count can only make its own
+// waits stricter (loads complete in order).  M0 carries the wave's LDS base;
+// lane i writes 16 (or 4) bytes at M0 + i * 16 (or 4).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void_t*)p; }
+__device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ int ring_swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int ring_slot(int r, int c) { return r * 8 + (c ^ ring_swz(r)); }
+
+// (x & mask) | magic in one instruction; magic sits in a register so that the
+// instruction needs a single scalar operand.
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t x, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Workgroup barrier for the ring: drains this wave's LDS instructions
+// (lgkmcnt) but not its vector-memory loads, which include the ring's own
+// LDS-DMA transfers (their completion is waited for explicitly, per tile).  A
+// release fence would wait for every outstanding load.  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int ACT, int EPI>
+__global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
+  constexpr bool BF = (ACT == ACT_BF16);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
+  __shared__ int rows_a[BM];
+  __shared__ int rows_o[BM];
+  __shared__ float wts[BM];
+  __shared__ __attribute__((aligned(16))) float xg[BF ? XG4 * BM : 4];  // [group][row] activation sums
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, lr = lane & 15;
+
+  const int active = (g.amode == AM_DENSE) ? g.n_blocks : g.plan[1] * g.n_ntiles;
+  if ((int)blockIdx.x >= active) return;
+  const int v = xcd_remap(blockIdx.x, active);
+  const int mt = v / g.n_ntiles, nt = v - mt * g.n_ntiles;
+
+  int expert, nrows;
+  if (g.amode == AM_DENSE) {
+    expert = 0;
+    const int64_t row0 = (int64_t)mt * BM;
+    nrows = (int)min<int64_t>(BM, g.M - row0);
+    if (tid < BM) {
+      rows_a[tid] = tid < nrows ? (int)(row0 + tid) : -1;
+      rows_o[tid] = (int)(row0 + tid);
+      wts[tid] = 0.f;
+    }
+  } else {
+    const PlanLayout L = plan_layout(g.P, g.E);
+    const int32_t* tl = g.plan + L.tiles + 4 * (int64_t)mt;
+    expert = tl[0];
+    const int row0 = tl[1];
+    nrows = tl[2];
+    if (tid < BM) {
+      int ra = -1, ro = 0;
+      float wt = 0.f;
+      if (tid < nrows) {
+        const int pair = g.plan[L.sorted + row0 + tid];
+        ra = (g.amode == AM_GATHER) ? pair / g.topk : row0 + tid;
+        ro = (EPI == QMOE_EPI_WEIGHTED_COMBINE) ? pair / g.topk : row0 + tid;
+        if (EPI == QMOE_EPI_WEIGHTED_COMBINE) wt = g.topk_w[pair];
+      }
+      rows_a[tid] = ra;
+      rows_o[tid] = ro;
+      wts[tid] = wt;
+    }
+  }
+  __syncthreads();
+  const int mbn = (nrows + 15) >> 4;
+
+  // The wave's four 16-row weight blocks (all rows of a block are valid or
+  // none are: N is a multiple of 16, and of 32 with SwiGLU).
+  constexpr bool swiglu = (EPI == QMOE_EPI_SWIGLU);
+  const int64_t Nh = g.N / 2;
+  // first weight row of block b (clamped into range; nvalid says whether it holds columns)
+  auto block_base = [&](int b) -> int64_t {
+    if (swiglu) {
+      const int64_t j0 = (int64_t)nt * (BN / 2) + 32 * wave + 16 * (b & 1);
+      const int64_t jc = j0 < Nh ? j0 : Nh - 16;
+      return (b < 2) ? jc : Nh + jc;
+    }
+    const int64_t n0 = (int64_t)nt * BN + 64 * wave + 16 * b;
+    return n0 < g.N ? n0 : g.N - 16;
+  };
+  int64_t ncol[NB];
+  bool nvalid[NB];
+  int64_t rbk[NB];  // run (16-row block) index of each block
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t c0 = swiglu ? (int64_t)nt * (BN / 2) + 32 * wave + 16 * (b & 1) : (int64_t)nt * BN + 64 * wave + 16 * b;
+    ncol[b] = c0 + lr;
+    nvalid[b] = c0 < (swiglu ? Nh : g.N);
+    rbk[b] = ((int64_t)expert * g.N + block_base(b)) >> 4;
+  }
+
+  const int gsh = __builtin_ctz((unsigned)g.group) - 6;  // group >= 64: tile kt lies in group kt >> gsh
+  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
+
+  // ---- per-lane load descriptors
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)g.a_bytes, 0x00020000);
+  uint32_t aoff[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int p = 192 * wave + 64 * i + lane;  // LDS chunk slot this lane fills
+    const int r = p >> 3, c = (p & 7) ^ ring_swz(r);
+    const int src = (r < 16 * mbn) ? rows_a[r] : -1;
+    aoff[i] = src >= 0 ? (uint32_t)((int64_t)src * K * 2 + 16 * c) : 0x80000000u;
+  }
+  // weight runs: load i covers blocks 2i (lanes 0-31) and 2i+1 (lanes 32-63)
+  const uint32_t* qs = (const uint32_t*)g.qs;
+  const uint32_t* wsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t rb = ((int64_t)expert * g.N + block_base(2 * i + (lane >> 5))) >> 4;
+    wsrc[i] = qs + rb * T * 128 + (lane & 31) * 4;
+  }
+  const int64_t rb_s = ((int64_t)expert * g.N + block_base(lg)) >> 4;  // block of this lane's scale word
+  const uint32_t* ssrc = (const uint32_t*)g.scales + rb_s * G * 16 + lr;
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds_addr(ring) + (uint32_t)((kt % RS) * R_STAGE);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma_buf16(arsrc, st + (192 * wave + 64 * i) * 16, aoff[i] + (uint32_t)kt * 128);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_glb16(wsrc[i] + (int64_t)kt * 128, st + R_A + wave * 2048 + i * 1024);
+    dma_glb4(ssrc + (int64_t)(kt >> gsh) * 16, st + R_A + R_B + wave * 256);
+  };
+
+  // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
+  // compile-time count keeps the m loops straight-line, so MFMA results are
+  // consumed late enough to need no pipeline stalls).
+  auto run = [&](auto mbv_c) {
+    constexpr int MBV = decltype(mbv_c)::value;
+    f4_t acc[MBV][NB];
+#pragma unroll
+    for (int m = 0; m < MBV; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[m][b] = f4_t{0, 0, 0, 0};
+
+    auto compute = [&](int kt) {
+      const uint8_t* st = ring + (kt % RS) * R_STAGE;
+      const uint16_t* As = (const uint16_t*)st;
+      const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 2048);
+      const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * 256);
+      u2_t q[NB];
+      uint32_t sbv[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        q[b] = *(const u2_t*)(Bs + b * 128 + lane * 2);
+        sbv[b] = Ss[b * 16 + lr];
+      }
+      if constexpr (!BF) {
+        u4_t bf[NB][2];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          Raw rw;
+          rw.v[0] = q[b][0];
+          rw.v[1] = q[b][1];
+          rw.x0 = sbv[b];
+          frag_f16<QMOE_INT4>(rw, lg, nullptr, nullptr, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const int r = 16 * m + lr;
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+          }
+        }
+      } else {
+        // exact codes (128+q) as bf16; the per-group scale goes on the fp32
+        // partial sums of the tile, the row sums feed the bias term at the end
+        const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+        const uint32_t magic = 0x43004300u;
+        const int gi = kt >> gsh;
+        const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0;
+#pragma unroll
+        for (int hp = 0; hp < NB; hp += 2) {
+          u4_t c0[2], c1[2];
+          float s[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              c0[j][i] = and_or_b32(q[hp + j][0] >> (4 * i), 0x000F000Fu, magic);
+              c1[j][i] = and_or_b32(q[hp + j][1] >> (4 * i), 0x000F000Fu, magic);
+            }
+            s[j] = f16_to_f32(sbv[hp + j]);
+          }
+#pragma unroll
+          for (int m = 0; m < MBV; ++m) {
+              const int r = 16 * m + lr;
+            const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
+            const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              f4_t t = mfma(a0, __builtin_bit_cast(b8_t, c0[j]), f4_t{0, 0, 0, 0});
+              t = mfma(a1, __builtin_bit_cast(b8_t, c1[j]), t);
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) acc[m][hp + j][rr] = __builtin_fmaf(s[j], t[rr], acc[m][hp + j][rr]);
+            }
+          }
+        }
+        // row sums of the tile's activations (for the bias term): wave w
+        // takes block w (and wave 0 also block 4); xg is [group][row]
+        auto row_sums = [&](int m) {
+          const int r = 16 * m + lr;
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+          f4_t xs = mfma(a0, ones, f4_t{0, 0, 0, 0});
+          xs = mfma(a1, ones, xs);
+          if (lr == 0) {  // lane (lg, 0) holds the sums of rows 16m + 4lg .. +3
+            f4_t* dst = (f4_t*)&xg[gi * BM + 16 * m + 4 * lg];
+            *dst = first_of_group ? xs : *dst + xs;
+          }
+        };
+        if (wave < MBV) row_sums(wave);
+        if (MBV == 5 && wave == 0) row_sums(4);
+      }
+    };
+
+    // ---- the K loop: tiles kt+1 and kt+2 stream while kt is computed
+    if (T > 0) issue(0);
+    if (T > 1) issue(1);
+    for (int kt = 0; kt < T; ++kt) {
+      if (kt + 1 < T) wait_vmcnt<R_NL>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      if (kt + 2 < T) issue(kt + 2);
+      compute(kt);
+    }
+
+    // ---- bf16 bias term: sum_g (b - 128 s)[n, g] * X[m, g] by MFMA with hi/lo
+    // splits (G <= 32: one 32-group step; lane group lg holds groups 8lg .. 8lg+7)
+    if constexpr (BF) {
+      uint32_t sv[NB][8];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t* sbrow = (const uint32_t*)g.scales + rbk[b] * G * 16 + lr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[b][i] = sbrow[min((int64_t)(8 * lg + i), G - 1) * 16];
+      }
+      ring_barrier();  // every wave's row sums are in xg
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        u4_t bh, bl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h2[2], l2[2];
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const uint32_t w = sv[b][2 * i + qq];
+            const float cb = (8 * lg + 2 * i + qq < G) ? f16_to_f32(w >> 16) - 128.0f * f16_to_f32(w & 0xFFFFu) : 0.f;
+            split_hi_lo(cb, h2[qq], l2[qq]);
+          }
+          bh[i] = h2[0] | (h2[1] << 16);
+          bl[i] = l2[0] | (l2[1] << 16);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const float* xr = &xg[8 * lg * BM + 16 * m + lr];
+          u4_t xh, xl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t h2[2], l2[2];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+              split_hi_lo(8 * lg + 2 * i + qq < G ? xr[(2 * i + qq) * BM] : 0.f, h2[qq], l2[qq]);
+            xh[i] = h2[0] | (h2[1] << 16);
+            xl[i] = l2[0] | (l2[1] << 16);
+          }
+          const b8_t XH = __builtin_bit_cast(b8_t, xh), XL = __builtin_bit_cast(b8_t, xl);
+          acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bh), acc[m][b]);
+          acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bl), acc[m][b]);
+          acc[m][b] = mfma(XL, __builtin_bit_cast(b8_t, bh), acc[m][b]);
+        }
+      }
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int m = 0; m < MBV; ++m) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * m + 4 * lg + rr;
+        if (row >= nrows) continue;
+        const int64_t orow = rows_o[row];
+        if constexpr (EPI == QMOE_EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (nvalid[j]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[j], silu_f32(acc[m][j][rr]) * acc[m][2 + j][rr]);
+        } else if constexpr (EPI == QMOE_EPI_STORE) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            if (nvalid[b]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[b], acc[m][b][rr]);
+        } else if constexpr (EPI == QMOE_EPI_WEIGHTED_COMBINE) {
+          const float w = wts[row];
+          float* o = (float*)g.out + orow * g.ldo;
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            if (nvalid[b]) atomicAdd(o + ncol[b], w * acc[m][b][rr]);
+        } else {  // ACCUMULATE
+          float* o = (float*)g.out + orow * g.ldo;
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            if (nvalid[b]) o[ncol[b]] += acc[m][b][rr];
+        }
+      }
+    }
+  };
+  switch (mbn) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    default: run(std::integral_constant<int, 5>{}); break;
+  }
+}
+
+// Whether the LDS-ring int4 kernel takes this call.
+static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
+  if (g.group < 64) return false;
+  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
+  if (act == QMOE_BF16 && g.K / g.group > XG4) return false;
+  return true;
+}
+
+template <int ACT>
+static void launch_int4_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(256);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
 template <int FMT, int ACT>
 static void launch_fa(const GemmArgs& g, int epi, hipStream_t s) {
   const dim3 grid(g.n_blocks), block(256);
@@ -743,6 +1145,11 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   else { g.n_ntiles = (int)((w->n + BN - 1) / BN); g.ldo = w->n; }
   g.n_blocks = (int)(n_mt * g.n_ntiles);
   if (g.n_blocks == 0) return;
+  if (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi)) {
+    if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
+    else launch_int4_ring<ACT_BF16>(g, epi, s);
+    return;
+  }
   switch (w->fmt) {
     case QMOE_Q8_0: launch_f<QMOE_Q8_0>(g, act, epi, s); break;
     case QMOE_Q2_K: launch_f<QMOE_Q2_K>(g, act, epi, s); break;
