@@ -702,27 +702,31 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
 // int4 on the tiled layout streams both operands through a 3-stage LDS ring
 // with direct-to-LDS loads (buffer/global_load ... lds), so two K tiles of
 // weights and gathered activations are in flight while a third is computed,
-// without holding them in registers.  Per K tile and wave: three 16-byte
-// loads of gathered activation chunks (rows past the tile read as zero), two
-// of weight runs (the wave's four 16-row blocks, 512 bytes each) and one of
-// packed scale|bias words.  LDS-DMA completion is tracked by vmcnt, which the
-// compiler does not see for these loads, so the waits are explicit: before
-// tile kt is read, only tile kt+1's loads may still be outstanding.  One
-// LDS-only barrier per tile publishes the activation chunks of all waves and
-// frees the stage the next loads overwrite.
+// without holding them in registers.  A workgroup is 8 waves over 80 routed
+// rows x 256 weight rows; each wave owns two 16-row weight blocks (SwiGLU: a
+// gate block and the matching up block) for all 80 rows, which keeps a wave
+// within 128 registers, so two workgroups (four waves per SIMD) share a CU.
+// Per K tile: ten 16-byte loads of gathered activation chunks spread over the
+// waves (rows past the tile read as zero), and per wave one load of its two
+// weight runs (512 bytes each) and one of packed scale|bias words.  LDS-DMA
+// completion is tracked by vmcnt, which the compiler does not see for these
+// loads, so the waits are explicit: before tile kt is read, only tile kt+1's
+// loads may still be outstanding.  One LDS-only barrier per tile publishes the
+// activation chunks of all waves and frees the stage the next loads overwrite.
 //
 // Activation rows are stored unpadded with the 16-byte chunks of row r
 // permuted by c ^ ((r ^ (r >> 3)) & 7), so the rows an MFMA fragment read
 // touches land in distinct 16-byte bank groups whether the LDS serves 8 or 16
 // lanes of a 16-byte read per cycle.
 
+constexpr int RW = 8;                      // waves per workgroup
+constexpr int RNB = 2;                     // 16-row weight blocks per wave
 constexpr int RS = 3;                      // ring stages
-constexpr int R_ACH = 768;                 // activation chunks per stage (80 rows x 8, padded to 3 loads per wave)
-constexpr int R_A = R_ACH * 16;            // 12288 B
-constexpr int R_B = 4 * 4 * 512;           // 4 waves x 4 blocks x 512 B
-constexpr int R_SB = 4 * 4 * 64;           // 4 waves x 4 blocks x 16 rows x 4 B
-constexpr int R_STAGE = R_A + R_B + R_SB;  // 21504 B
-constexpr int R_NL = 6;                    // ring loads per wave per tile
+constexpr int R_ACH = BM * 8;              // activation chunks per stage (640)
+constexpr int R_A = R_ACH * 16;            // 10240 B
+constexpr int R_B = RW * RNB * 512;        // 8192 B
+constexpr int R_SB = RW * 256;             // 2048 B (one 64-lane dword load per wave)
+constexpr int R_STAGE = R_A + R_B + R_SB;  // 20480 B
 constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -776,7 +780,8 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 template <int ACT, int EPI>
-__global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_int4_kernel(GemmArgs g) {
   constexpr bool BF = (ACT == ACT_BF16);
   __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
   __shared__ int rows_a[BM];
@@ -826,62 +831,64 @@ __global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
   __syncthreads();
   const int mbn = (nrows + 15) >> 4;
 
-  // The wave's four 16-row weight blocks (all rows of a block are valid or
-  // none are: N is a multiple of 16, and of 32 with SwiGLU).
+  // The wave's two 16-row weight blocks: all rows of a block are valid or
+  // none are (N is a multiple of 16, and of 32 with SwiGLU); invalid blocks
+  // read a valid block and are not stored.
   constexpr bool swiglu = (EPI == QMOE_EPI_SWIGLU);
   const int64_t Nh = g.N / 2;
-  // first weight row of block b (clamped into range; nvalid says whether it holds columns)
-  auto block_base = [&](int b) -> int64_t {
+  auto col0 = [&](int b) -> int64_t {  // first output column of block b
+    return swiglu ? (int64_t)nt * (BN / 2) + 16 * wave : (int64_t)nt * BN + 32 * wave + 16 * b;
+  };
+  auto block_base = [&](int b) -> int64_t {  // first weight row of block b (clamped)
     if (swiglu) {
-      const int64_t j0 = (int64_t)nt * (BN / 2) + 32 * wave + 16 * (b & 1);
+      const int64_t j0 = col0(b);
       const int64_t jc = j0 < Nh ? j0 : Nh - 16;
-      return (b < 2) ? jc : Nh + jc;
+      return b == 0 ? jc : Nh + jc;
     }
-    const int64_t n0 = (int64_t)nt * BN + 64 * wave + 16 * b;
+    const int64_t n0 = col0(b);
     return n0 < g.N ? n0 : g.N - 16;
   };
-  int64_t ncol[NB];
-  bool nvalid[NB];
-  int64_t rbk[NB];  // run (16-row block) index of each block
+  int64_t ncol[RNB];
+  bool nvalid[RNB];
+  int64_t rbk[RNB];  // run (16-row block) index of each block
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int64_t c0 = swiglu ? (int64_t)nt * (BN / 2) + 32 * wave + 16 * (b & 1) : (int64_t)nt * BN + 64 * wave + 16 * b;
-    ncol[b] = c0 + lr;
-    nvalid[b] = c0 < (swiglu ? Nh : g.N);
+  for (int b = 0; b < RNB; ++b) {
+    ncol[b] = col0(b) + lr;
+    nvalid[b] = col0(b) < (swiglu ? Nh : g.N);
     rbk[b] = ((int64_t)expert * g.N + block_base(b)) >> 4;
   }
 
   const int gsh = __builtin_ctz((unsigned)g.group) - 6;  // group >= 64: tile kt lies in group kt >> gsh
-  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
+  const int64_t K = g.K;
+  const int T = (int)(K >> 6), G = T >> gsh;
 
   // ---- per-lane load descriptors
+  // activation chunks: load j (0..9) fills slots 64j .. 64j+63; wave w issues
+  // loads w and w + 8
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)g.a_bytes, 0x00020000);
-  uint32_t aoff[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int p = 192 * wave + 64 * i + lane;  // LDS chunk slot this lane fills
-    const int r = p >> 3, c = (p & 7) ^ ring_swz(r);
-    const int src = (r < 16 * mbn) ? rows_a[r] : -1;
-    aoff[i] = src >= 0 ? (uint32_t)((int64_t)src * K * 2 + 16 * c) : 0x80000000u;
-  }
-  // weight runs: load i covers blocks 2i (lanes 0-31) and 2i+1 (lanes 32-63)
-  const uint32_t* qs = (const uint32_t*)g.qs;
-  const uint32_t* wsrc[2];
+  const int n_aload = (wave + RW < R_ACH / 64) ? 2 : 1;
+  uint32_t aoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t rb = ((int64_t)expert * g.N + block_base(2 * i + (lane >> 5))) >> 4;
-    wsrc[i] = qs + rb * T * 128 + (lane & 31) * 4;
+    const int p = 64 * (wave + RW * i) + lane;  // LDS chunk slot this lane fills
+    const int r = p >> 3, c = (p & 7) ^ ring_swz(r);
+    const int src = (r < 16 * mbn && p < R_ACH) ? rows_a[min(r, BM - 1)] : -1;
+    aoff[i] = src >= 0 ? (uint32_t)((int64_t)src * K * 2 + 16 * c) : 0x80000000u;
   }
-  const int64_t rb_s = ((int64_t)expert * g.N + block_base(lg)) >> 4;  // block of this lane's scale word
-  const uint32_t* ssrc = (const uint32_t*)g.scales + rb_s * G * 16 + lr;
+  // weight runs: lanes 0-31 block 0, lanes 32-63 block 1
+  const uint32_t* wsrc = (const uint32_t*)g.qs +
+                         (((int64_t)expert * g.N + block_base(lane >> 5)) >> 4) * T * 128 + (lane & 31) * 4;
+  // scale|bias words: lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them)
+  const uint32_t* ssrc = (const uint32_t*)g.scales +
+                         (((int64_t)expert * g.N + block_base((lane >> 4) & 1)) >> 4) * G * 16 + lr;
 
-  auto issue = [&](int kt) {
-    const uint32_t st = lds_addr(ring) + (uint32_t)((kt % RS) * R_STAGE);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) dma_buf16(arsrc, st + (192 * wave + 64 * i) * 16, aoff[i] + (uint32_t)kt * 128);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma_glb16(wsrc[i] + (int64_t)kt * 128, st + R_A + wave * 2048 + i * 1024);
-    dma_glb4(ssrc + (int64_t)(kt >> gsh) * 16, st + R_A + R_B + wave * 256);
+  // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
+  auto issue = [&](int kt, int stage) {
+    const uint32_t st = lds_addr(ring) + (uint32_t)(stage * R_STAGE);
+    dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
+    if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
+    dma_glb16(wsrc + kt * 128, st + R_A + wave * 1024);
+    dma_glb4(ssrc + (kt >> gsh) * 16, st + R_A + R_B + wave * 256);
   };
 
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
@@ -889,28 +896,28 @@ __global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
   // consumed late enough to need no pipeline stalls).
   auto run = [&](auto mbv_c) {
     constexpr int MBV = decltype(mbv_c)::value;
-    f4_t acc[MBV][NB];
+    f4_t acc[MBV][RNB];
 #pragma unroll
     for (int m = 0; m < MBV; ++m)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[m][b] = f4_t{0, 0, 0, 0};
+      for (int b = 0; b < RNB; ++b) acc[m][b] = f4_t{0, 0, 0, 0};
 
-    auto compute = [&](int kt) {
-      const uint8_t* st = ring + (kt % RS) * R_STAGE;
+    auto compute = [&](int kt, int stage) {
+      const uint8_t* st = ring + stage * R_STAGE;
       const uint16_t* As = (const uint16_t*)st;
-      const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 2048);
+      const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 1024);
       const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * 256);
-      u2_t q[NB];
-      uint32_t sbv[NB];
+      u2_t q[RNB];
+      uint32_t sbv[RNB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < RNB; ++b) {
         q[b] = *(const u2_t*)(Bs + b * 128 + lane * 2);
         sbv[b] = Ss[b * 16 + lr];
       }
       if constexpr (!BF) {
-        u4_t bf[NB][2];
+        u4_t bf[RNB][2];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int b = 0; b < RNB; ++b) {
           Raw rw;
           rw.v[0] = q[b][0];
           rw.v[1] = q[b][1];
@@ -923,7 +930,7 @@ __global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
           const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
           const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
+          for (int b = 0; b < RNB; ++b) {
             acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
             acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
           }
@@ -935,75 +942,87 @@ __global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
         const uint32_t magic = 0x43004300u;
         const int gi = kt >> gsh;
         const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0;
+        u4_t c0[RNB], c1[RNB];
+        float sc[RNB];
 #pragma unroll
-        for (int hp = 0; hp < NB; hp += 2) {
-          u4_t c0[2], c1[2];
-          float s[2];
+        for (int b = 0; b < RNB; ++b) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              c0[j][i] = and_or_b32(q[hp + j][0] >> (4 * i), 0x000F000Fu, magic);
-              c1[j][i] = and_or_b32(q[hp + j][1] >> (4 * i), 0x000F000Fu, magic);
-            }
-            s[j] = f16_to_f32(sbv[hp + j]);
+          for (int i = 0; i < 4; ++i) {
+            c0[b][i] = and_or_b32(q[b][0] >> (4 * i), 0x000F000Fu, magic);
+            c1[b][i] = and_or_b32(q[b][1] >> (4 * i), 0x000F000Fu, magic);
           }
+          sc[b] = f16_to_f32(sbv[b]);
+        }
 #pragma unroll
-          for (int m = 0; m < MBV; ++m) {
-              const int r = 16 * m + lr;
-            const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
-            const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+        for (int m = 0; m < MBV; ++m) {
+          const int r = 16 * m + lr;
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              f4_t t = mfma(a0, __builtin_bit_cast(b8_t, c0[j]), f4_t{0, 0, 0, 0});
-              t = mfma(a1, __builtin_bit_cast(b8_t, c1[j]), t);
+          for (int b = 0; b < RNB; ++b) {
+            f4_t t = mfma(a0, __builtin_bit_cast(b8_t, c0[b]), f4_t{0, 0, 0, 0});
+            t = mfma(a1, __builtin_bit_cast(b8_t, c1[b]), t);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) acc[m][hp + j][rr] = __builtin_fmaf(s[j], t[rr], acc[m][hp + j][rr]);
-            }
+            for (int rr = 0; rr < 4; ++rr) acc[m][b][rr] = __builtin_fmaf(sc[b], t[rr], acc[m][b][rr]);
           }
         }
-        // row sums of the tile's activations (for the bias term): wave w
-        // takes block w (and wave 0 also block 4); xg is [group][row]
-        auto row_sums = [&](int m) {
-          const int r = 16 * m + lr;
+        // row sums of the tile's activations (bias term): wave w < MBV takes block w
+        if (wave < MBV) {
+          const int r = 16 * wave + lr;
           const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
           const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
           f4_t xs = mfma(a0, ones, f4_t{0, 0, 0, 0});
           xs = mfma(a1, ones, xs);
-          if (lr == 0) {  // lane (lg, 0) holds the sums of rows 16m + 4lg .. +3
-            f4_t* dst = (f4_t*)&xg[gi * BM + 16 * m + 4 * lg];
+          if (lr == 0) {  // lane (lg, 0) holds the sums of rows 16w + 4lg .. +3
+            f4_t* dst = (f4_t*)&xg[gi * BM + 16 * wave + 4 * lg];
             *dst = first_of_group ? xs : *dst + xs;
           }
-        };
-        if (wave < MBV) row_sums(wave);
-        if (MBV == 5 && wave == 0) row_sums(4);
+        }
       }
     };
 
-    // ---- the K loop: tiles kt+1 and kt+2 stream while kt is computed
-    if (T > 0) issue(0);
-    if (T > 1) issue(1);
-    for (int kt = 0; kt < T; ++kt) {
-      if (kt + 1 < T) wait_vmcnt<R_NL>();
-      else wait_vmcnt<0>();
+    // ---- the K loop: tiles kt+1 and kt+2 stream while kt is computed.  The
+    // last two tiles are peeled off so the steady-state loop has no tests;
+    // `sc` is the ring stage of tile kt.
+    auto wait_next = [&]() {  // only the next tile's loads may be outstanding
+      if (n_aload == 2) wait_vmcnt<4>();
+      else wait_vmcnt<3>();
+    };
+    if (T > 0) issue(0, 0);
+    if (T > 1) issue(1, 1);
+    int sc = 0;
+    for (int kt = 0; kt + 2 < T; ++kt) {
+      wait_next();
       ring_barrier();
-      if (kt + 2 < T) issue(kt + 2);
-      compute(kt);
+      issue(kt + 2, sc == 0 ? 2 : sc - 1);
+      compute(kt, sc);
+      sc = sc == 2 ? 0 : sc + 1;
+    }
+    if (T > 1) {
+      wait_next();
+      ring_barrier();
+      compute(T - 2, sc);
+      sc = sc == 2 ? 0 : sc + 1;
+    }
+    if (T > 0) {
+      wait_vmcnt<0>();
+      ring_barrier();
+      compute(T - 1, sc);
     }
 
     // ---- bf16 bias term: sum_g (b - 128 s)[n, g] * X[m, g] by MFMA with hi/lo
     // splits (G <= 32: one 32-group step; lane group lg holds groups 8lg .. 8lg+7)
     if constexpr (BF) {
-      uint32_t sv[NB][8];
+      uint32_t sv[RNB][8];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < RNB; ++b) {
         const uint32_t* sbrow = (const uint32_t*)g.scales + rbk[b] * G * 16 + lr;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sv[b][i] = sbrow[min((int64_t)(8 * lg + i), G - 1) * 16];
+        for (int i = 0; i < 8; ++i) sv[b][i] = sbrow[min(8 * lg + i, G - 1) * 16];
       }
       ring_barrier();  // every wave's row sums are in xg
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < RNB; ++b) {
         u4_t bh, bl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1047,23 +1066,21 @@ __global__ __launch_bounds__(256, 2) void qmm_int4_kernel(GemmArgs g) {
         if (row >= nrows) continue;
         const int64_t orow = rows_o[row];
         if constexpr (EPI == QMOE_EPI_SWIGLU) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (nvalid[j]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[j], silu_f32(acc[m][j][rr]) * acc[m][2 + j][rr]);
+          if (nvalid[0]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[0], silu_f32(acc[m][0][rr]) * acc[m][1][rr]);
         } else if constexpr (EPI == QMOE_EPI_STORE) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+          for (int b = 0; b < RNB; ++b)
             if (nvalid[b]) store_out(g.out, g.out_dtype, orow * g.ldo + ncol[b], acc[m][b][rr]);
         } else if constexpr (EPI == QMOE_EPI_WEIGHTED_COMBINE) {
           const float w = wts[row];
           float* o = (float*)g.out + orow * g.ldo;
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+          for (int b = 0; b < RNB; ++b)
             if (nvalid[b]) atomicAdd(o + ncol[b], w * acc[m][b][rr]);
         } else {  // ACCUMULATE
           float* o = (float*)g.out + orow * g.ldo;
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+          for (int b = 0; b < RNB; ++b)
             if (nvalid[b]) o[ncol[b]] += acc[m][b][rr];
         }
       }
@@ -1088,7 +1105,7 @@ static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
 
 template <int ACT>
 static void launch_int4_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(256);
+  const dim3 grid(g.n_blocks), block(RW * 64);
   switch (epi) {
     case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_STORE>), grid, block, 0, s, g); break;
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
