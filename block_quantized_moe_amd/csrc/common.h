@@ -69,6 +69,34 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---------------------------------------------------------------- LDS-DMA
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS-DMA issue.  Written as inline asm so that the compiler, which cannot
+// tell which LDS region a DMA writes, does not drain every outstanding load
+// (vmcnt(0)) before each LDS read; the kernels wait for their own transfers
+// explicitly.  Extra loads the compiler does not count can only make its own
+// waits stricter (loads complete in order).  M0 carries the wave's LDS base;
+// lane i writes 16 (or 4) bytes at M0 + i * 16 (or 4).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void_t*)p; }
+__device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
 // (selector 0..3 -> lo, 4..7 -> hi, 12 -> 0x00).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {

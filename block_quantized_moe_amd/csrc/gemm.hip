@@ -729,33 +729,6 @@ constexpr int R_SB = RW * 256;             // 2048 B (one 64-lane dword load per
 constexpr int R_STAGE = R_A + R_B + R_SB;  // 20480 B
 constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// LDS-DMA issue.  Written as inline asm so that the compiler, which cannot
-// tell which ring stage a DMA writes, does not drain every outstanding load
-// (vmcnt(0)) before each LDS read; the ring waits for its own transfers
-// explicitly.  Extra loads the compiler does not count can only make its own
-// waits stricter (loads complete in order).  M0 carries the wave's LDS base;
-// lane i writes 16 (or 4) bytes at M0 + i * 16 (or 4).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void_t*)p; }
-__device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma_glb16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_glb4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) leaving the other counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 __device__ __forceinline__ int ring_swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int ring_slot(int r, int c) { return r * 8 + (c ^ ring_swz(r)); }
 

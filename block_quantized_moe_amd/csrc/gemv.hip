@@ -453,7 +453,6 @@ __device__ __forceinline__ void int4_tile(const u4_t& x0, const u4_t& x1, const 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
-constexpr uint32_t OOB = 0x80000000u;  // a buffer offset that is always out of range
 
 // Slot ids of a call held in registers: lane l keeps slot 64c + l of chunk c
 // (-1 past the end), so the per-expert token lists below are ballots with no
@@ -513,263 +512,210 @@ __device__ __forceinline__ int nth_slot(const SlotIds& s, int P, int e, int j, i
   return res;
 }
 
-// STORE / SWIGLU.  grid = (16-unit blocks, slots), W waves; wave w takes
-// tiles [w*TPW, (w+1)*TPW) of K and the waves' sums meet in LDS.  With SWIGLU
-// a unit block is 16 gate rows and the 16 matching up rows.  A workgroup
-// whose slot repeats an earlier slot's expert exits at once; the first one
-// serves every token routed to that expert.  Four tiles per wave keep the
-// register count low enough for several workgroups per CU, so one
-// workgroup's loads overlap another's arithmetic.
-template <int ACT, int EPI, int W, int TPW>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
-void gemv_int4_rows_kernel(GemvArgs g) {
+// Decode kernels that put a call's whole weight stream in flight at once.  A
+// workgroup owns one item and its waves split K into runs of GS_TPW tiles;
+// each wave issues every load of its run (weight words, scale|bias words and,
+// by LDS-DMA, the activation rows it needs) before computing, so a wave costs
+// about one memory latency and the grid covers the chip.
+//   STORE / SWIGLU: item = (slot p, 16-unit block).  An item whose slot
+//     repeats an earlier slot's expert exits at once; the first one serves
+//     every token routed to that expert, `rows` tokens per pass.
+//   WEIGHTED_COMBINE: item = (token b, 16-row block); wave (j, c) computes the
+//     expert of slot b * topk + j over K run c, and the top-k weighted sum is
+//     formed in slot order (bit-reproducible).
+constexpr int GS_TPW = 8;                     // tiles per wave
+constexpr int GS_ROW = GS_TPW * 64 * 2 + 16;  // bytes per staged activation row (padded)
+constexpr int GS_MAX_ROWS = 8;                // tokens per pass (STORE / SWIGLU)
+
+__host__ __device__ constexpr int64_t gs_lds_bytes(int waves, int rows, int nb, bool cmb) {
+  return (int64_t)waves * rows * GS_ROW + (cmb ? (int64_t)waves * 64 : (int64_t)(waves - 1) * nb * 1024);
+}
+
+template <int ACT, int EPI>
+__global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int rows) {
+  constexpr bool CMB = (EPI == QMOE_EPI_WEIGHTED_COMBINE);
   constexpr int NB = (EPI == QMOE_EPI_SWIGLU) ? 2 : 1;
-  __shared__ f4_t red[W - 1][NB][64];
+  constexpr int NL = GS_TPW * NB * 2;  // vector loads per wave after the activation DMAs
+  extern __shared__ __attribute__((aligned(16))) uint8_t gs_dyn[];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform, kept in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
   const int r = lane & 15, lg = lane >> 4;
-  const int slot = blockIdx.y;
   const int P = g.nslots;
-  SlotIds sid;
-  load_slot_ids(g.ids, P, sid);
-  const int e = slot_expert(sid, slot);
-  if (e < 0 || e >= g.E) return;
-  int nt;
-  if (nth_slot(sid, P, e, 0, &nt) != slot) return;  // an earlier slot serves e
-
-  // group is a power of two >= 64: tile kt lies in group kt >> gsh
   const int gsh = __builtin_ctz((unsigned)g.group) - 6;
-  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
+  const int64_t K = g.K;
+  const int T = (int)(K >> 6), G = T >> gsh;
+  const int CW = (T + GS_TPW - 1) / GS_TPW;  // waves per K
   const int64_t Nunits = (EPI == QMOE_EPI_SWIGLU) ? g.N / 2 : g.N;
-  const int64_t u0 = (int64_t)blockIdx.x * 16;
-  int64_t rb[NB];
-  rb[0] = ((int64_t)e * g.N + u0) >> 4;
-  if constexpr (NB == 2) rb[1] = ((int64_t)e * g.N + Nunits + u0) >> 4;
-  const int kt0 = wave * TPW;
+  const int nub = (int)(Nunits / 16);
+  const uint32_t xw = lds_addr(gs_dyn) + (uint32_t)(wave * rows * GS_ROW);  // this wave's rows
+  uint8_t* const red = gs_dyn + (int64_t)W * rows * GS_ROW;
 
-  // Activations first (token sl / topk in this lane, zeros past the list),
-  // then the weights: every load of the first pass is in flight at once.
-  const __amdgpu_buffer_rsrc_t xrs = rsrc(g.a, (uint32_t)((int64_t)(P / g.topk) * K * 2));
-  int cnt;
-  int sl = nth_slot(sid, P, e, r, &cnt);
-  u4_t x[TPW][2];
-  auto load_x = [&]() {
-    const uint32_t xo = sl >= 0 ? (uint32_t)(((int64_t)(sl / g.topk) * K + 16 * lg) * 2) : OOB;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const uint32_t kb = (uint32_t)(min((int64_t)(kt0 + t), T - 1) * 128);
-      x[t][0] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + kb, 0, 0));
-      x[t][1] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + kb + 16, 0, 0));
+  const int item = blockIdx.x;
+  const int ub = item % nub;
+  int kc, e, slot_c = 0, nt = 1, sl = 0;
+  SlotIds sid;
+  if constexpr (CMB) {
+    const int j = wave / CW;
+    kc = wave - j * CW;
+    slot_c = (item / nub) * g.topk + j;
+    e = __builtin_amdgcn_readfirstlane(g.ids[slot_c]);
+  } else {
+    load_slot_ids(g.ids, P, sid);
+    const int slot = item / nub;
+    e = slot_expert(sid, slot);
+    int c;
+    if (e < 0 || e >= g.E || nth_slot(sid, P, e, 0, &c) != slot) return;  // uniform over the workgroup
+    kc = wave;
+    sl = nth_slot(sid, P, e, r, &nt);
+  }
+  const bool ok = e >= 0 && e < g.E;
+  const int kt0 = kc * GS_TPW;
+  const int64_t arows = CMB ? P : P / g.topk;
+  const __amdgpu_buffer_rsrc_t xrs = rsrc(g.a, (uint32_t)(arows * K * 2));
+
+  // Stage activation rows pass .. pass + n - 1 of this wave's K run.
+  auto stage = [&](int n) {
+    for (int i = 0; i < n; ++i) {
+      const int src = CMB ? slot_c : __builtin_amdgcn_readlane(sl, i) / g.topk;
+      dma_buf16(xrs, xw + (uint32_t)(i * GS_ROW), (uint32_t)(((int64_t)src * K + kt0 * 64) * 2) + lane * 16);
     }
   };
-  load_x();
-  // Weights through buffer resources over the block's tiles: one address
-  // register for all loads, and tiles past K read as zero.
-  u2_t w[TPW][NB];
-  uint32_t sb[TPW][NB];
+  int nrows = CMB ? 1 : min(nt, rows);
+  stage(nrows);
+
+  u2_t w[GS_TPW][NB];
+  uint32_t sb[GS_TPW][NB];
+  __amdgpu_buffer_rsrc_t wr[NB], sr[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const __amdgpu_buffer_rsrc_t wr = rsrc((const uint32_t*)g.qs + rb[b] * T * 128, (uint32_t)(T * 512));
-    const __amdgpu_buffer_rsrc_t sr = rsrc((const uint32_t*)g.scales + rb[b] * G * 16, (uint32_t)(G * 64));
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      w[t][b] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr, (uint32_t)(lane * 8 + (kt0 + t) * 512), 0, 0));
-      sb[t][b] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(r * 4 + ((kt0 + t) >> gsh) * 64), 0, 0);
-    }
+    const int64_t rb = ((int64_t)(ok ? e : 0) * g.N + (b ? Nunits : 0) + ub * 16) >> 4;
+    wr[b] = rsrc((const uint32_t*)g.qs + rb * T * 128, ok ? (uint32_t)(T * 512) : 0u);
+    sr[b] = rsrc((const uint32_t*)g.scales + rb * G * 16, ok ? (uint32_t)(G * 64) : 0u);
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
-
-  for (int pass = 0; pass < nt; pass += 16) {
-    if (pass > 0) {
-      sl = nth_slot(sid, P, e, pass + r, &cnt);
-      load_x();
+  // tile by tile, so that the first tiles can be computed while the rest land
+#pragma unroll
+  for (int t = 0; t < GS_TPW; ++t)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      w[t][b] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr[b], (uint32_t)(lane * 8 + (kt0 + t) * 512), 0, 0));
+      sb[t][b] = __builtin_amdgcn_raw_buffer_load_b32(sr[b], (uint32_t)(r * 4 + ((kt0 + t) >> gsh) * 64), 0, 0);
     }
+  wait_vmcnt<NL>();  // the activation rows have landed
+
+  // One pass: the products of the staged rows, reduced over the waves and
+  // stored (slot rows pass .. pass + nrows - 1 of the expert).
+  auto run_pass = [&]() {
+    const uint8_t* xr = gs_dyn + (int64_t)wave * rows * GS_ROW + (r < nrows ? r : 0) * GS_ROW + 32 * lg;
     f4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-      if (kt0 + t < T) int4_tile<ACT, NB>(x[t][0], x[t][1], w[t], sb[t], acc);
-    if (wave > 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) red[wave - 1][b][lane] = acc[b];
+    for (int t = 0; t < GS_TPW; ++t) {
+      if (kt0 + t < T) {
+        const u4_t x0 = *(const u4_t*)(xr + t * 128);
+        const u4_t x1 = *(const u4_t*)(xr + t * 128 + 16);
+        int4_tile<ACT, NB>(x0, x1, w[t], sb[t], acc);
+      }
     }
-    lds_barrier();
-    if (wave == 0) {
+    // keep the decoding inside each pass (hoisted out of the pass loop below,
+    // it would hold every tile's codes in registers)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int t = 0; t < GS_TPW; ++t)
 #pragma unroll
-        for (int v = 0; v < W - 1; ++v) acc[b] += red[v][b][lane];
+      for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(w[t][b]), "+v"(sb[t][b]));
+    if constexpr (CMB) {
+      // row 0 of the product is the slot's result; lanes 0..15 hold it
+      float* y = (float*)red;  // [W][16]
+      if (lane < 16) y[wave * 16 + lane] = acc[0][0];
+      lds_barrier();
+      if (threadIdx.x < 16) {
+        const int b = item / nub;
+        float v = 0.f;
+        for (int j = 0; j < g.topk; ++j) {
+          const int p = b * g.topk + j;
+          const int ej = g.ids[p];
+          if (ej < 0 || ej >= g.E) continue;
+          float yj = 0.f;
+          for (int c = 0; c < CW; ++c) yj += y[(j * CW + c) * 16 + threadIdx.x];
+          v = __builtin_fmaf(g.topk_w[p], yj, v);
+        }
+        store_out(g.out, g.out_dtype, (int64_t)b * g.N + ub * 16 + threadIdx.x, v);
+      }
+    } else {
+      f4_t* rd = (f4_t*)red;  // [W - 1][NB][64]
+      if (wave > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * lg + i;
-        const int sm = __shfl(sl, m);
-        if (pass + m < nt) {
-          const float v = (EPI == QMOE_EPI_SWIGLU) ? silu_f32(acc[0][i]) * acc[NB - 1][i] : acc[0][i];
-          store_out(g.out, g.out_dtype, (int64_t)sm * Nunits + u0 + r, v);
+        for (int b = 0; b < NB; ++b) rd[((wave - 1) * NB + b) * 64 + lane] = acc[b];
+      }
+      lds_barrier();
+      if (wave == 0) {
+        for (int v = 1; v < W; ++v)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[b] += rd[((v - 1) * NB + b) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * lg + i;
+          const int sm = __shfl(sl, m);
+          if (m < nrows) {
+            const float v = (EPI == QMOE_EPI_SWIGLU) ? silu_f32(acc[0][i]) * acc[NB - 1][i] : acc[0][i];
+            store_out(g.out, g.out_dtype, (int64_t)sm * Nunits + ub * 16 + r, v);
+          }
         }
       }
     }
-    if (pass + 16 < nt) lds_barrier();  // red[] is reused by the next pass
-  }
-}
-
-// WEIGHTED_COMBINE (sum-folded down projection).  grid = 16-row blocks, 8
-// waves.  The per-slot input rows are staged in LDS (dynamic: P * 16 fp32
-// results, then (P + 1) padded input rows, the last one zero).  Wave w takes
-// the experts first seen at slots w, w + 8, ... over the whole K (at most 8
-// tiles), with the next expert's weights loaded while the current one is
-// computed.  The per-slot results land in LDS by slot and the top-k weighted
-// sum per token is then formed in slot order, so the result is
-// bit-reproducible.
-constexpr int GC_WAVES = 8;
-constexpr int GC_LDS = 73728;  // dynamic LDS limit (bytes) for the combine
-
-__host__ __device__ constexpr int64_t gc_lds_bytes(int64_t P, int64_t K) {
-  return P * 64 + (P + 1) * (K + 8) * 2;
-}
-
-template <int ACT>
-__global__ __launch_bounds__(GC_WAVES * 64) void gemv_int4_combine_kernel(GemvArgs g) {
-  constexpr int TPE = 8;
-  extern __shared__ __attribute__((aligned(16))) uint8_t gc_dyn[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15, lg = lane >> 4;
-  const int P = g.nslots;
-  const int gsh = __builtin_ctz((unsigned)g.group) - 6;
-  const int64_t K = g.K, T = K >> 6, G = T >> gsh;
-  const int xstride = (int)K + 8;  // padded LDS row: consecutive slots start 4 banks apart
-  float* ybuf = (float*)gc_dyn;                       // [P][16]
-  uint16_t* xs = (uint16_t*)(gc_dyn + (int64_t)P * 64);  // [P + 1][K + 8]
-  const int64_t rblk = blockIdx.x;  // 16-row block within each expert
-  const uint32_t wbytes = (uint32_t)(T * 512), sbytes = (uint32_t)(G * 64);
-
-  SlotIds sid;
-  load_slot_ids(g.ids, P, sid);
-
-  // The next slot p' >= p (p' = p mod 8) where an expert is first seen, or P.
-  auto next_first = [&](int p) {
-    for (; p < P; p += GC_WAVES) {
-      const int e = slot_expert(sid, p);
+  };
+  run_pass();
+  if constexpr (!CMB) {
+    // more tokens on this expert than one pass holds (rare): restage and rerun
+    for (int pass = rows; pass < nt; pass += rows) {
+      lds_barrier();  // red[] and the staged rows are reused
       int c;
-      if (e >= 0 && e < g.E && nth_slot(sid, P, e, 0, &c) == p) return p;
+      sl = nth_slot(sid, P, e, pass + r, &c);
+      nrows = min(nt - pass, rows);
+      stage(nrows);
+      wait_vmcnt<0>();
+      run_pass();
     }
-    return P;
-  };
-  // Two register buffers, selected at compile time (ping-pong over experts).
-  // Slot P loads nothing (empty resource).
-  u2_t wa[TPE][1], wb[TPE][1];
-  uint32_t sa[TPE][1], sbb[TPE][1];
-  auto load_expert = [&](u2_t (&w)[TPE][1], uint32_t (&sb)[TPE][1], int p) {
-    const bool ok = p < P;
-    const int e = ok ? slot_expert(sid, p) : 0;
-    const int64_t rb = ((int64_t)e * g.N >> 4) + rblk;
-    const __amdgpu_buffer_rsrc_t wr = rsrc((const uint32_t*)g.qs + rb * T * 128, ok ? wbytes : 0u);
-    const __amdgpu_buffer_rsrc_t sr = rsrc((const uint32_t*)g.scales + rb * G * 16, ok ? sbytes : 0u);
-#pragma unroll
-    for (int t = 0; t < TPE; ++t) {
-      // offsets in the vector operand only: the range check covers them
-      w[t][0] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr, (uint32_t)(lane * 8 + t * 512), 0, 0));
-      sb[t][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(r * 4 + (t >> gsh) * 64), 0, 0);
-    }
-  };
-  auto run_expert = [&](const u2_t (&w)[TPE][1], const uint32_t (&sb)[TPE][1], int p) {
-    const int e = slot_expert(sid, p);
-    int nt = 1;
-    for (int pass = 0; pass < nt; pass += 16) {
-      const int sl = nth_slot(sid, P, e, pass + r, &nt);
-      const uint16_t* xr = xs + (sl >= 0 ? sl : P) * xstride + 16 * lg;
-      f4_t acc[1] = {f4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int t = 0; t < TPE; ++t) {
-        if (t < T) {
-          const u4_t x0 = *(const u4_t*)(xr + t * 64);
-          const u4_t x1 = *(const u4_t*)(xr + t * 64 + 8);
-          int4_tile<ACT, 1>(x0, x1, w[t], sb[t], acc);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * lg + i;
-        const int sm = __shfl(sl, m);
-        if (pass + m < nt) ybuf[sm * 16 + r] = acc[0][i];
-      }
-    }
-  };
+  }
+}
 
-  int pa = next_first(wave);
-  load_expert(wa, sa, pa);
-  // stage every slot's input row (8 values per u4) plus the zero row P
-  const int per_row = (int)(K >> 3);
-  for (int i = tid; i < (P + 1) * per_row; i += GC_WAVES * 64) {
-    const int p = i / per_row, c = i - p * per_row;
-    *(u4_t*)(xs + p * xstride + 8 * c) =
-        p < P ? *(const u4_t*)(g.a + (int64_t)p * K + 8 * c) : u4_t{0, 0, 0, 0};
-  }
-  lds_barrier();
-  while (pa < P) {
-    const int pb = next_first(pa + GC_WAVES);
-    load_expert(wb, sbb, pb);
-    run_expert(wa, sa, pa);
-    if (pb >= P) break;
-    pa = next_first(pb + GC_WAVES);
-    load_expert(wa, sa, pa);
-    run_expert(wb, sbb, pb);
-  }
-  lds_barrier();
-  const int btok = P / g.topk;
-  for (int i = tid; i < btok * 16; i += GC_WAVES * 64) {
-    const int b = i >> 4, n = i & 15;
-    float v = 0.f;
-    for (int j = 0; j < g.topk; ++j) {
-      const int p = b * g.topk + j;
-      const int e = g.ids[p];
-      if (e >= 0 && e < g.E) v = __builtin_fmaf(g.topk_w[p], ybuf[p * 16 + n], v);
-    }
-    store_out(g.out, g.out_dtype, (int64_t)b * g.N + rblk * 16 + n, v);
-  }
+// Waves per workgroup of the split kernel (0: it does not take the call).
+static int gs_waves(const GemvArgs& g, int epi) {
+  const int cw = (int)((g.K / 64 + GS_TPW - 1) / GS_TPW);
+  const int w = epi == QMOE_EPI_WEIGHTED_COMBINE ? g.topk * cw : cw;
+  return w <= 16 ? w : 0;
 }
 
 // Whether the tiled int4 kernels take this call (else the generic ones do).
 static bool int4_tiled_ok(const GemvArgs& g, int epi) {
-  if (g.group < 64 || g.K > 4096) return false;
-  if (epi == QMOE_EPI_WEIGHTED_COMBINE)
-    return g.N % 16 == 0 && g.K <= 512 && gc_lds_bytes(g.nslots, g.K) <= GC_LDS;
+  if (g.group < 64 || g.K > 4096 || gs_waves(g, epi) == 0) return false;
   return g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16) == 0;
+}
+
+template <int ACT, int EPI>
+static void launch_gemv_split(const GemvArgs& g, int waves, hipStream_t s) {
+  static bool attr_set = false;  // raise the dynamic LDS limit once per process
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)gemv_int4_split_kernel<ACT, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    attr_set = true;
+  }
+  constexpr bool CMB = EPI == QMOE_EPI_WEIGHTED_COMBINE;
+  const int64_t units = EPI == QMOE_EPI_SWIGLU ? g.N / 2 : g.N;
+  const int64_t tokens = g.nslots / g.topk;
+  const int rows = CMB ? 1 : (int)(tokens < GS_MAX_ROWS ? tokens : GS_MAX_ROWS);
+  const dim3 grid((unsigned)((units / 16) * (CMB ? tokens : g.nslots)));
+  const size_t lds = (size_t)gs_lds_bytes(waves, rows, EPI == QMOE_EPI_SWIGLU ? 2 : 1, CMB);
+  hipLaunchKernelGGL((gemv_int4_split_kernel<ACT, EPI>), grid, dim3(waves * 64), lds, s, g, rows);
 }
 
 template <int ACT>
 static void launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
-  if (epi == QMOE_EPI_WEIGHTED_COMBINE) {  // K <= 512: eight tiles per expert
-    static bool attr_set = false;  // raise the dynamic LDS limit once per process
-    if (!attr_set) {
-      hipFuncSetAttribute((const void*)gemv_int4_combine_kernel<ACT>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, GC_LDS);
-      attr_set = true;
-    }
-    const dim3 grid((unsigned)(g.N / 16));
-    hipLaunchKernelGGL((gemv_int4_combine_kernel<ACT>), grid, dim3(GC_WAVES * 64),
-                       (size_t)gc_lds_bytes(g.nslots, g.K), s, g);
-    return;
-  }
-  const int64_t units = epi == QMOE_EPI_SWIGLU ? g.N / 2 : g.N;
-  const dim3 grid((unsigned)(units / 16), (unsigned)g.nslots);
-  const int64_t T = g.K / 64;
-  // four tiles per wave from 16 tiles up; 4, 8 or 16 waves
-#define QMOE_ROWS(EPI_, W_, TPW_) \
-  hipLaunchKernelGGL((gemv_int4_rows_kernel<ACT, EPI_, W_, TPW_>), grid, dim3(W_ * 64), 0, s, g)
-#define QMOE_ROWS_EPI(EPI_)                         \
-  do {                                              \
-    if (T <= 8) QMOE_ROWS(EPI_, 4, 2);              \
-    else if (T <= 16) QMOE_ROWS(EPI_, 4, 4);        \
-    else if (T <= 32) QMOE_ROWS(EPI_, 8, 4);        \
-    else QMOE_ROWS(EPI_, 16, 4);                    \
-  } while (0)
-  if (epi == QMOE_EPI_SWIGLU) QMOE_ROWS_EPI(QMOE_EPI_SWIGLU);
-  else QMOE_ROWS_EPI(QMOE_EPI_STORE);
-#undef QMOE_ROWS_EPI
-#undef QMOE_ROWS
+  const int w = gs_waves(g, epi);
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE) launch_gemv_split<ACT, QMOE_EPI_WEIGHTED_COMBINE>(g, w, s);
+  else if (epi == QMOE_EPI_SWIGLU) launch_gemv_split<ACT, QMOE_EPI_SWIGLU>(g, w, s);
+  else launch_gemv_split<ACT, QMOE_EPI_STORE>(g, w, s);
 }
 
 template <int FMT, int ACT, int CPL>

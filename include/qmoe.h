@@ -253,9 +253,9 @@ int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype,
  *                     (h[b, j] . W[ids[b, j]]^T), j ascending, deterministic
  * a, out, topk_w DEVICE.  K <= 4096 with K/32 a power of two.  On int4 with
  * group >= 64, N a multiple of 16 (32 for SWIGLU) and, for WEIGHTED_COMBINE,
- * K <= 512 and (b*topk + 1) * (K + 8) <= 34816, the tiled matrix-core kernels
- * run; every other call takes the generic kernels, whose WEIGHTED_COMBINE
- * needs K >= 512 (else QMOE_ERR_UNSUPPORTED, nothing launched).
+ * topk * ceil(K / 512) <= 16, the tiled matrix-core kernels run; every other
+ * call takes the generic kernels, whose WEIGHTED_COMBINE needs K >= 512 (else
+ * QMOE_ERR_UNSUPPORTED, nothing launched).
  * ------------------------------------------------------------------------ */
 int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64_t b,
                   const int32_t* ids, const float* topk_w, int32_t topk, int32_t epilogue,

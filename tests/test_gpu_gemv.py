@@ -99,7 +99,7 @@ def test_gemv_dropped_ids_contribute_nothing():
 
 
 def test_gemv_int4_many_tokens_per_expert():
-    # 32 tokens on each of two experts: the int4 kernels take tokens 16 at a time
+    # 32 tokens on each of two experts: the int4 kernels take tokens 8 at a time
     rng = np.random.default_rng(12)
     B, E, k, H, I = 32, 2, 2, 512, 256
     x = synth.activations(rng, B, H, "bf16")
@@ -109,11 +109,40 @@ def test_gemv_int4_many_tokens_per_expert():
     _check(x, ids, w, synth.int4(rng, E, 2 * I, H), synth.int4(rng, E, H, I), "bf16")
 
 
-@pytest.mark.parametrize("group,I", [(32, 512), (64, 1024)])
+@pytest.mark.parametrize("group,I", [(32, 512), (32, 1024)])
 def test_gemv_int4_generic_shapes(group, I):
-    # group 32 and a down projection with K = 1024 take the generic kernels
+    # group 32 takes the generic kernels
     rng = np.random.default_rng(group + I)
     B, E, k, H = 3, 8, 4, 512
     x = synth.activations(rng, B, H, "bf16")
     ids, w = synth.routing_softmax(rng, B, E, k)
     _check(x, ids, w, synth.int4(rng, E, 2 * I, H, group), synth.int4(rng, E, H, I, group), "bf16")
+
+
+@pytest.mark.parametrize("B,H,I,k,act", [
+    (3, 128, 128, 2, "bf16"),    # K = 128: two tiles, a partial run per wave
+    (2, 4096, 256, 4, "f16"),    # gate/up K = 4096: eight waves split K
+    (5, 512, 1024, 8, "bf16"),   # combine K = 1024, top-8: sixteen waves
+    (4, 256, 2048, 2, "f16"),    # combine K = 2048, top-2: four runs per slot
+    (9, 512, 512, 8, "bf16"),    # nine tokens: a second pass of activation rows
+    (4, 512, 2048, 8, "bf16"),   # combine K = 2048, top-8: generic combine kernel
+])
+def test_gemv_int4_split_shapes(B, H, I, k, act):
+    rng = np.random.default_rng(B * 1000 + H + I + k)
+    E = 12
+    x = synth.activations(rng, B, H, act)
+    ids, w = synth.routing_softmax(rng, B, E, k)
+    if B == 9:
+        ids[:, 0] = 5  # every token on expert 5
+    _check(x, ids, w, synth.int4(rng, E, 2 * I, H), synth.int4(rng, E, H, I), act)
+
+
+def test_gemv_int4_repeated_expert_within_token():
+    # a token may name one expert several times: the expert then has more
+    # slots than there are tokens, served over several passes
+    rng = np.random.default_rng(77)
+    B, E, k, H, I = 2, 4, 4, 256, 128
+    x = synth.activations(rng, B, H, "bf16")
+    ids = np.array([[1, 1, 1, 1], [1, 1, 2, 2]], np.int32)
+    w = rng.random((B, k)).astype(np.float32)
+    _check(x, ids, w, synth.int4(rng, E, 2 * I, H), synth.int4(rng, E, H, I), "bf16")
