@@ -9,8 +9,10 @@ The weights rotate over R copies so no step finds them in the 256 MB
 Infinity Cache.  `value` is algorithmic TFLOP/s of that step (routed pairs
 only; padding is not counted).
 
-The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers of weights rotated)
-and the CPU oracle baseline are reported in the same JSON line.
+The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers, each with its own
+copy of the weights) is timed as a captured HIP graph replay and eagerly; its
+GB/s are weight + activation bytes per layer over graph time per layer.  The
+CPU oracle baseline is reported in the same JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
 
@@ -145,20 +147,45 @@ def run_decode(args, torch, qm, B, layers):
     uniq = np.unique(inp.ids)
     per_expert = (inp.w_gate_up.nbytes + inp.w_down.nbytes) // inp.E
     nbytes = len(uniq) * per_expert + B * inp.H * 2 * 2 + B * inp.k * inp.I * 2 * 2
+    def layer(l):
+        qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
+        qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+
     for _ in range(2):
         for l in range(layers):
-            qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
-            qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+            layer(l)
     torch.cuda.synchronize()
     reps = max(1, args.decode_reps)
-    t0 = time.perf_counter()
+    # eager: every layer launched from the host, events around the whole run
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         for l in range(layers):
-            qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
-            qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+            layer(l)
+    e1.record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / (reps * layers)
-    # kernel durations with events around each launch
+    t_eager = e0.elapsed_time(e1) * 1e-3 / (reps * layers)
+    # graph: the same layers captured once into a HIP graph and replayed
+    # (no launch gaps from the host; the kernels allocate nothing and issue
+    # no memset, so they replay as captured)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for l in range(layers):
+                layer(l)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_graph = e0.elapsed_time(e1) * 1e-3 / (reps * layers)
+    # per-launch durations with events around each launch (upper bounds: an
+    # event pair adds its own gap to a launch this short)
     marks = []
     for l in range(layers):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -171,13 +198,13 @@ def run_decode(args, torch, qm, B, layers):
     torch.cuda.synchronize()
     t_gu = float(np.median([m[0].elapsed_time(m[1]) for m in marks])) * 1e-3
     t_dn = float(np.median([m[1].elapsed_time(m[2]) for m in marks])) * 1e-3
-    del gus, dns
+    del graph, gus, dns
     torch.cuda.empty_cache()
     return dict(B=B, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
-                kernel_s=t_gu + t_dn, gate_up_s=t_gu, down_s=t_dn, wall_s_per_layer=wall,
-                GBps_kernels=nbytes / (t_gu + t_dn) / 1e9,
-                hbm_frac_kernels=nbytes / (t_gu + t_dn) / PEAK_HBM,
-                GBps_wall=nbytes / wall / 1e9, tokens_per_s_per_layer=B / wall)
+                s_per_layer_graph=t_graph, s_per_layer_eager=t_eager,
+                gate_up_s_event=t_gu, down_s_event=t_dn,
+                GBps=nbytes / t_graph / 1e9, hbm_frac=nbytes / t_graph / PEAK_HBM,
+                GBps_eager=nbytes / t_eager / 1e9, tokens_per_s_per_layer=B / t_graph)
 
 
 def cpu_baseline(n_tokens):
@@ -232,19 +259,22 @@ def _pmc_median_kib(run_dir, counter, name_part):
 
 
 def _gemm_source_hash():
-    """sha256 of the GEMM kernel source with comments and blank lines removed
-    (the traffic record stays valid across comment-only edits)."""
+    """sha256 of the GEMM kernel sources (gemm.hip and the shared device
+    helpers) with comments and blank lines removed, so the traffic record
+    stays valid across comment-only edits."""
     import hashlib
     import re
-    src = open(os.path.join(ROOT, "block_quantized_moe_amd", "csrc", "gemm.hip")).read()
-    code = [re.sub(r"//.*", "", l).rstrip() for l in src.splitlines()]
+    code = []
+    for f in ("common.h", "gemm.hip"):
+        src = open(os.path.join(ROOT, "block_quantized_moe_amd", "csrc", f)).read()
+        code += [re.sub(r"//.*", "", l).rstrip() for l in src.splitlines()]
     return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()
 
 
 def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, out):
     """Turn four rocprofv3 --pmc runs (gate/up FETCH_SIZE, WRITE_SIZE; copy
     probe FETCH_SIZE, WRITE_SIZE) into HBM bytes per gate/up launch."""
-    kern = "qmm_kernel<3, 1, 1>"
+    kern = "qmm_int4_kernel<1, 1>"
     f_kib, nf = _pmc_median_kib(fetch_dir, "FETCH_SIZE", kern)
     w_kib, nw = _pmc_median_kib(write_dir, "WRITE_SIZE", kern)
     cf_kib, _ = _pmc_median_kib(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
@@ -254,7 +284,7 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     inp = prefill_inputs(2048)
     alg = algorithmic(inp)
     rec = {
-        "kernel": "qmm_kernel<INT4, bf16, SWIGLU> (gate/up), qwen3.6-a3b-shaped prefill",
+        "kernel": "qmm_int4_kernel<bf16, SWIGLU> (int4 gate/up), qwen3.6-a3b-shaped prefill",
         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
         "copy_probe_mib": copy_mb, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
         "fetch_scale": k_fetch, "write_scale": k_write,
@@ -295,7 +325,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--decode-reps", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
@@ -327,7 +357,7 @@ def main():
     value = alg["flops"] / t_step / 1e12
     t_gu = kern["gate_up"]
     roofline = {
-        "kernel": "qmm_kernel<INT4, bf16, SWIGLU> (gate/up)",
+        "kernel": "qmm_int4_kernel<bf16, SWIGLU> (int4 gate/up)",
         "bound": "hbm",
         "achieved": alg["bytes_gu"] / t_gu / 1e9,
         "peak": PEAK_HBM / 1e9,
@@ -372,10 +402,12 @@ def main():
         "kernels_s": kern,
         "algorithmic": {"flops": alg["flops"], "bytes": alg["bytes"]},
         "roofline": roofline,
-        "decode": [{"B": d["B"], "GBps": d["GBps_kernels"], "hbm_frac": d["hbm_frac_kernels"],
-                    "GBps_wall": d["GBps_wall"], "us_per_layer_kernels": d["kernel_s"] * 1e6,
-                    "us_per_layer_wall": d["wall_s_per_layer"] * 1e6, "unique_experts": d["unique_experts"],
-                    "bytes_per_layer": d["bytes_per_layer"]} for d in decode],
+        "decode": [{"B": d["B"], "GBps": d["GBps"], "hbm_frac": d["hbm_frac"], "GBps_eager": d["GBps_eager"],
+                    "us_per_layer_graph": d["s_per_layer_graph"] * 1e6,
+                    "us_per_layer_eager": d["s_per_layer_eager"] * 1e6,
+                    "us_gate_up_event": d["gate_up_s_event"] * 1e6, "us_down_event": d["down_s_event"] * 1e6,
+                    "unique_experts": d["unique_experts"], "bytes_per_layer": d["bytes_per_layer"]}
+                   for d in decode],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
