@@ -97,6 +97,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// (x & mask) | magic as one v_and_or_b32.  The constants become opaque
+// register values (empty asm, no instruction), so the compiler selects the
+// three-operand instruction itself instead of an AND and an OR with literal
+// operands.  Not written as inline asm: the hazard checks do not see into
+// an asm statement, and a matrix instruction that reads its result too early,
+// or whose operand it overwrites too soon, then computes with wrong values.
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t x, uint32_t mask, uint32_t magic) {
+  asm("" : "+s"(mask));
+  asm("" : "+v"(magic));
+  return (x & mask) | magic;
+}
+
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
 // (selector 0..3 -> lo, 4..7 -> hi, 12 -> 0x00).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {

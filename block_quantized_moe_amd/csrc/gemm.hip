@@ -732,13 +732,6 @@ constexpr int XG4 = 32;                    // int4 groups per row kept for the b
 __device__ __forceinline__ int ring_swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int ring_slot(int r, int c) { return r * 8 + (c ^ ring_swz(r)); }
 
-// (x & mask) | magic in one instruction; magic sits in a register so that the
-// instruction needs a single scalar operand.
-__device__ __forceinline__ uint32_t and_or_b32(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return r;
-}
 
 // Workgroup barrier for the ring: drains this wave's LDS instructions
 // (lgkmcnt) but not its vector-memory loads, which include the ring's own

@@ -423,14 +423,16 @@ template <> struct One<ACT_BF16> { static constexpr uint32_t bits = 0x3F803F80u;
 // The eight codes of one word (elements 0..7) as four packed pairs.
 template <int ACT>
 __device__ __forceinline__ u4_t int4_codes(uint32_t q) {
+  const uint32_t magic = Magic<ACT>::bits;
   u4_t c;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = ((q >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
+  for (int i = 0; i < 4; ++i) c[i] = and_or_b32(q >> (4 * i), 0x000F000Fu, magic);
   return c;
 }
 
-// One tile's contribution for NB row blocks: acc[b] += s * P + cb * X.
-template <int ACT, int NB>
+// One tile's contribution for NB row blocks: acc[b] += s * P + cb * X.  With
+// R1 only row 0 of the product (accumulator element 0 of lanes 0..15) is kept.
+template <int ACT, int NB, bool R1 = false>
 __device__ __forceinline__ void int4_tile(const u4_t& x0, const u4_t& x1, const u2_t (&w)[NB],
                                           const uint32_t (&sb)[NB], f4_t (&acc)[NB]) {
   const u4_t ones = u4_t{One<ACT>::bits, One<ACT>::bits, One<ACT>::bits, One<ACT>::bits};
@@ -444,7 +446,7 @@ __device__ __forceinline__ void int4_tile(const u4_t& x0, const u4_t& x1, const 
     const float s = f16_to_f32(sb[b] & 0xFFFFu);
     const float cb = __builtin_fmaf(-Magic<ACT>::v, s, f16_to_f32(sb[b] >> 16));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(cb, X[i], __builtin_fmaf(s, P[i], acc[b][i]));
+    for (int i = 0; i < (R1 ? 1 : 4); ++i) acc[b][i] = __builtin_fmaf(cb, X[i], __builtin_fmaf(s, P[i], acc[b][i]));
   }
 }
 
@@ -453,6 +455,7 @@ __device__ __forceinline__ void int4_tile(const u4_t& x0, const u4_t& x1, const 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
+constexpr uint32_t OOB = 0x80000000u;  // a buffer offset that is always out of range
 
 // Slot ids of a call held in registers: lane l keeps slot 64c + l of chunk c
 // (-1 past the end), so the per-expert token lists below are ballots with no
@@ -525,7 +528,7 @@ __device__ __forceinline__ int nth_slot(const SlotIds& s, int P, int e, int j, i
 //     formed in slot order (bit-reproducible).
 constexpr int GS_TPW = 8;                     // tiles per wave
 constexpr int GS_ROW = GS_TPW * 64 * 2 + 16;  // bytes per staged activation row (padded)
-constexpr int GS_MAX_ROWS = 8;                // tokens per pass (STORE / SWIGLU)
+constexpr int GS_MAX_ROWS = 4;                // tokens per pass (STORE / SWIGLU)
 
 __host__ __device__ constexpr int64_t gs_lds_bytes(int waves, int rows, int nb, bool cmb) {
   return (int64_t)waves * rows * GS_ROW + (cmb ? (int64_t)waves * 64 : (int64_t)(waves - 1) * nb * 1024);
@@ -535,7 +538,6 @@ template <int ACT, int EPI>
 __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int rows) {
   constexpr bool CMB = (EPI == QMOE_EPI_WEIGHTED_COMBINE);
   constexpr int NB = (EPI == QMOE_EPI_SWIGLU) ? 2 : 1;
-  constexpr int NL = GS_TPW * NB * 2;  // vector loads per wave after the activation DMAs
   extern __shared__ __attribute__((aligned(16))) uint8_t gs_dyn[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -548,7 +550,6 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
   const int CW = (T + GS_TPW - 1) / GS_TPW;  // waves per K
   const int64_t Nunits = (EPI == QMOE_EPI_SWIGLU) ? g.N / 2 : g.N;
   const int nub = (int)(Nunits / 16);
-  const uint32_t xw = lds_addr(gs_dyn) + (uint32_t)(wave * rows * GS_ROW);  // this wave's rows
   uint8_t* const red = gs_dyn + (int64_t)W * rows * GS_ROW;
 
   const int item = blockIdx.x;
@@ -574,15 +575,33 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
   const int64_t arows = CMB ? P : P / g.topk;
   const __amdgpu_buffer_rsrc_t xrs = rsrc(g.a, (uint32_t)(arows * K * 2));
 
-  // Stage activation rows pass .. pass + n - 1 of this wave's K run.
-  auto stage = [&](int n) {
-    for (int i = 0; i < n; ++i) {
-      const int src = CMB ? slot_c : __builtin_amdgcn_readlane(sl, i) / g.topk;
-      dma_buf16(xrs, xw + (uint32_t)(i * GS_ROW), (uint32_t)(((int64_t)src * K + kt0 * 64) * 2) + lane * 16);
+  // Activation rows pass .. pass + n - 1 of this wave's K run: lane i loads
+  // 16 bytes of each row into registers (rows past n load nothing), and
+  // put_rows() writes them to this wave's LDS rows, where the MFMA operand
+  // layout is read back.  Loads into registers, not LDS-DMA: the waits for
+  // them then come from the compiler, in issue order with the weight loads
+  // (an LDS-DMA transfer is not ordered against later register loads by the
+  // vector-memory counter).
+  u4_t xv[GS_MAX_ROWS];
+  auto load_rows = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < GS_MAX_ROWS; ++i) {
+      const int src = CMB ? slot_c : __builtin_amdgcn_readlane(sl, i < n ? i : 0) / g.topk;
+      const uint32_t off = i < n ? (uint32_t)(((int64_t)src * K + kt0 * 64) * 2) + lane * 16 : OOB;
+      xv[i] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+      if (CMB) break;
+    }
+  };
+  auto put_rows = [&](int n) {
+    uint8_t* const base = gs_dyn + (int64_t)wave * rows * GS_ROW + lane * 16;
+#pragma unroll
+    for (int i = 0; i < GS_MAX_ROWS; ++i) {
+      if (i < n) *(u4_t*)(base + i * GS_ROW) = xv[i];
+      if (CMB) break;
     }
   };
   int nrows = CMB ? 1 : min(nt, rows);
-  stage(nrows);
+  load_rows(nrows);
 
   u2_t w[GS_TPW][NB];
   uint32_t sb[GS_TPW][NB];
@@ -593,15 +612,19 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
     wr[b] = rsrc((const uint32_t*)g.qs + rb * T * 128, ok ? (uint32_t)(T * 512) : 0u);
     sr[b] = rsrc((const uint32_t*)g.scales + rb * G * 16, ok ? (uint32_t)(G * 64) : 0u);
   }
-  // tile by tile, so that the first tiles can be computed while the rest land
+  // Tile by tile, so that the first tiles are computed while the rest land.
+  // The empty asm statements keep this order (the scheduler would otherwise
+  // group the loads by kind, and the first tile would wait for the last load).
 #pragma unroll
-  for (int t = 0; t < GS_TPW; ++t)
+  for (int t = 0; t < GS_TPW; ++t) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       w[t][b] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(wr[b], (uint32_t)(lane * 8 + (kt0 + t) * 512), 0, 0));
       sb[t][b] = __builtin_amdgcn_raw_buffer_load_b32(sr[b], (uint32_t)(r * 4 + ((kt0 + t) >> gsh) * 64), 0, 0);
     }
-  wait_vmcnt<NL>();  // the activation rows have landed
+    asm volatile("" ::: "memory");
+  }
+  put_rows(nrows);
 
   // One pass: the products of the staged rows, reduced over the waves and
   // stored (slot rows pass .. pass + nrows - 1 of the expert).
@@ -610,14 +633,19 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
     f4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+    auto tiles = [&](auto r1) {
 #pragma unroll
-    for (int t = 0; t < GS_TPW; ++t) {
-      if (kt0 + t < T) {
-        const u4_t x0 = *(const u4_t*)(xr + t * 128);
-        const u4_t x1 = *(const u4_t*)(xr + t * 128 + 16);
-        int4_tile<ACT, NB>(x0, x1, w[t], sb[t], acc);
+      for (int t = 0; t < GS_TPW; ++t) {
+        if (kt0 + t < T) {
+          const u4_t x0 = *(const u4_t*)(xr + t * 128);
+          const u4_t x1 = *(const u4_t*)(xr + t * 128 + 16);
+          int4_tile<ACT, NB, decltype(r1)::value>(x0, x1, w[t], sb[t], acc);
+        }
       }
-    }
+    };
+    // one token (always, for the combine): only row 0 of each product is used
+    if (CMB || nrows == 1) tiles(std::true_type{});
+    else tiles(std::false_type{});
     // keep the decoding inside each pass (hoisted out of the pass loop below,
     // it would hold every tile's codes in registers)
 #pragma unroll
@@ -673,8 +701,8 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
       int c;
       sl = nth_slot(sid, P, e, pass + r, &c);
       nrows = min(nt - pass, rows);
-      stage(nrows);
-      wait_vmcnt<0>();
+      load_rows(nrows);
+      put_rows(nrows);
       run_pass();
     }
   }
