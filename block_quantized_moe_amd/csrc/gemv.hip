@@ -578,10 +578,8 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
   // Activation rows pass .. pass + n - 1 of this wave's K run: lane i loads
   // 16 bytes of each row into registers (rows past n load nothing), and
   // put_rows() writes them to this wave's LDS rows, where the MFMA operand
-  // layout is read back.  Loads into registers, not LDS-DMA: the waits for
-  // them then come from the compiler, in issue order with the weight loads
-  // (an LDS-DMA transfer is not ordered against later register loads by the
-  // vector-memory counter).
+  // layout is read back.  Loads into registers, not LDS-DMA, so that every
+  // wait is the compiler's own, in issue order with the weight loads.
   u4_t xv[GS_MAX_ROWS];
   auto load_rows = [&](int n) {
 #pragma unroll
