@@ -149,12 +149,16 @@ __device__ __forceinline__ float dot2t(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
 }
 
-// Blocks of a launch are dealt to the 8 XCDs round-robin.  Renumber them so
-// that consecutive virtual ids run on the same XCD (and share its L2).
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int xcd = bid & 7, slot = bid >> 3;
-  return xcd * q + (xcd < r ? xcd : r) + slot;
+// Work item of block b in a tiled launch.  Blocks are dealt to the 8 XCDs
+// round-robin; tile t goes to XCD t % 8, and each XCD runs its tiles'
+// n_nt column tiles back to back, so a tile's activation rows stay in one L2
+// and every XCD walks the tiles in list order (a plan lists its partial
+// tiles last, so a launch ends on its smallest tiles).  False: no work.
+__device__ __forceinline__ bool tile_of_block(int b, int n_tiles, int n_nt, int& mt, int& nt) {
+  const int x = b & 7, j = b >> 3, q = j / n_nt;
+  mt = x + 8 * q;
+  nt = j - q * n_nt;
+  return mt < n_tiles;
 }
 
 // Plan buffer layout (int32 words), see qmoe_moe_plan in qmoe.h.  The tile

@@ -600,12 +600,11 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
   c.lr = c.lane & 15;
   const int tid = c.tid;
 
-  // The grid is sized for the most tiles a plan can have; only the first
-  // n_tiles * n_ntiles blocks have work, and they are spread over all XCDs.
-  const int active = (g.amode == AM_DENSE) ? g.n_blocks : g.plan[1] * g.n_ntiles;
-  if ((int)blockIdx.x >= active) return;
-  const int v = xcd_remap(blockIdx.x, active);
-  const int mt = v / g.n_ntiles, nt = v - mt * g.n_ntiles;
+  // The grid is sized for the most tiles a plan can have; blocks past the
+  // plan's tiles have no work.
+  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM) : g.plan[1];
+  int mt, nt;
+  if (!tile_of_block(blockIdx.x, n_tiles, g.n_ntiles, mt, nt)) return;
 
   int expert, row0, nrows;
   if (g.amode == AM_DENSE) {
@@ -759,10 +758,11 @@ void qmm_int4_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
 
-  const int active = (g.amode == AM_DENSE) ? g.n_blocks : g.plan[1] * g.n_ntiles;
-  if ((int)blockIdx.x >= active) return;
-  const int v = xcd_remap(blockIdx.x, active);
-  const int mt = v / g.n_ntiles, nt = v - mt * g.n_ntiles;
+  // The grid is sized for the most tiles a plan can have; blocks past the
+  // plan's tiles have no work.
+  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM) : g.plan[1];
+  int mt, nt;
+  if (!tile_of_block(blockIdx.x, n_tiles, g.n_ntiles, mt, nt)) return;
 
   int expert, nrows;
   if (g.amode == AM_DENSE) {
@@ -1126,7 +1126,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   else n_mt = plan_max_tiles(g.P, g.E, bm);
   if (epi == QMOE_EPI_SWIGLU) { g.n_ntiles = (int)((w->n / 2 + BN / 2 - 1) / (BN / 2)); g.ldo = w->n / 2; }
   else { g.n_ntiles = (int)((w->n + BN - 1) / BN); g.ldo = w->n; }
-  g.n_blocks = (int)(n_mt * g.n_ntiles);
+  g.n_blocks = (int)((n_mt + 7) / 8 * 8 * g.n_ntiles);  // whole rounds of the 8 XCDs
   if (g.n_blocks == 0) return;
   if (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi)) {
     if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);

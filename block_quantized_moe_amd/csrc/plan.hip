@@ -82,7 +82,7 @@ __global__ __launch_bounds__(1024) void plan_hist_kernel(PlanArgs a) {
 
 // One workgroup of 1024 threads (thread = expert).
 __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
-  __shared__ int sa[QMOE_MAX_EXPERTS], st[QMOE_MAX_EXPERTS];
+  __shared__ int sa[QMOE_MAX_EXPERTS], st[QMOE_MAX_EXPERTS], sp[QMOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const PlanLayout L = plan_layout(a.P, a.E);
   int32_t* hist = a.plan + hist_off(L);
@@ -97,35 +97,42 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
     }
     c_e = run;
   }
-  const int nt = (c_e + a.bm - 1) / a.bm;
+  // Tile order: every expert's full tiles (bm rows) first, in expert order,
+  // then the experts' last partial tiles.  Workgroups take tiles in this
+  // order, so a launch ends on its smallest tiles.
+  const int nfull = c_e / a.bm, part = (c_e % a.bm) != 0;
   sa[tid] = c_e;
-  st[tid] = nt;
+  st[tid] = nfull;
+  sp[tid] = part;
   __syncthreads();
   for (int off = 1; off < QMOE_MAX_EXPERTS; off <<= 1) {
     const int va = tid >= off ? sa[tid - off] : 0;
     const int vt = tid >= off ? st[tid - off] : 0;
+    const int vp = tid >= off ? sp[tid - off] : 0;
     __syncthreads();
     sa[tid] += va;
     st[tid] += vt;
+    sp[tid] += vp;
     __syncthreads();
   }
   if (tid < a.E) {
     const int row0 = sa[tid] - c_e;
-    const int tile0 = st[tid] - nt;
     a.plan[L.counts + tid] = c_e;
     a.plan[L.offsets + tid] = row0;
-    for (int i = 0; i < nt; ++i) {
-      int32_t* tl = a.plan + L.tiles + 4 * (int64_t)(tile0 + i);
+    auto put = [&](int t, int i, int n) {
+      int32_t* tl = a.plan + L.tiles + 4 * (int64_t)t;
       tl[0] = tid;
       tl[1] = row0 + i * a.bm;
-      tl[2] = min(a.bm, c_e - i * a.bm);
+      tl[2] = n;
       tl[3] = 0;
-    }
+    };
+    for (int i = 0; i < nfull; ++i) put(st[tid] - nfull + i, i, a.bm);
+    if (part) put(st[QMOE_MAX_EXPERTS - 1] + sp[tid] - 1, nfull, c_e - nfull * a.bm);
   }
   if (tid == 0) {
     const int total = sa[QMOE_MAX_EXPERTS - 1];
     a.plan[0] = (int32_t)(a.P - total);
-    a.plan[1] = st[QMOE_MAX_EXPERTS - 1];
+    a.plan[1] = st[QMOE_MAX_EXPERTS - 1] + sp[QMOE_MAX_EXPERTS - 1];
     a.plan[2] = total;
     a.plan[3] = a.bm;
     a.plan[4] = (int32_t)a.t;

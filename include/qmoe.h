@@ -197,8 +197,10 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
  * Layout of the DEVICE int32 plan buffer (size from qmoe_plan_bytes):
  *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts  [7] 0
  *   counts [n_experts] | offsets [n_experts + 1] | sorted pair ids [t * topk]
- *   | tiles [max_tiles][4] = (expert, row0, nrows, 0) | sorted position of
- *   each pair, -1 if dropped [t * topk] | scratch.  max_tiles is
+ *   | tiles [max_tiles][4] = (expert, row0, nrows, 0), the full tiles (bm
+ *   rows) in expert order, then the experts' partial last tiles in expert
+ *   order | sorted position of each pair, -1 if dropped [t * topk] |
+ *   scratch.  max_tiles is
  *   min(t*topk, n_experts) + t*topk/16 (the tile array fits any bm); the
  *   sorted list starts at word 8 + 2*n_experts + 1 and the tile array at the
  *   next multiple of 4 words after it.

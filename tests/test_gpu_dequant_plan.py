@@ -126,7 +126,15 @@ def test_plan_exact(T, k, E, bm, skew):
     assert np.array_equal(v["counts"], ref["counts"])
     assert np.array_equal(v["offsets"], ref["offsets"])
     assert np.array_equal(v["sorted"][:len(ref["sorted"])], ref["sorted"])
-    assert np.array_equal(v["tiles"][:nt, :3], ref["tiles"])
+    # the tile set is unique; its order is the kernel's schedule: full tiles
+    # first (expert order), then the partial ones (expert order)
+    got = v["tiles"][:nt, :3]
+    key = lambda t: np.lexsort((t[:, 1], t[:, 0]))
+    assert np.array_equal(got[key(got)], ref["tiles"][key(ref["tiles"])])
+    full = got[:, 2] == bm
+    assert not np.any(full[np.argmin(full):]) if not full.all() else True
+    for part in (got[full], got[~full]):
+        assert np.all(np.diff(part[:, 0] * (T * k + 1) + part[:, 1]) > 0)
     inv = np.full(T * k, -1)
     inv[ref["sorted"]] = np.arange(len(ref["sorted"]))
     assert np.array_equal(v["inv"], inv)
