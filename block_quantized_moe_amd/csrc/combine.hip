@@ -67,6 +67,76 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict
   store_out(out, out_dtype, t * N + n, acc);
 }
 
+// The same sum, eight consecutive outputs per thread: a token's expert rows
+// are read with 16-byte loads, all issued before the first FMA (buffer loads:
+// a dropped pair reads zeros at no cost and is then skipped).  Requires N % 8
+// == 0 and y under 4 GiB.  Sum order as above, so results are identical.
+template <int YT>
+__global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __restrict__ y,
+                                                              const int32_t* __restrict__ plan, int64_t P,
+                                                              int E, int topk, const float* __restrict__ w,
+                                                              int64_t N, const float* __restrict__ base,
+                                                              void* __restrict__ out, int out_dtype) {
+  const int64_t nb = (N + 2047) / 2048;
+  const int64_t t = blockIdx.x / nb;
+  const int64_t n0 = ((blockIdx.x - t * nb) * 256 + threadIdx.x) * 8;
+  if (n0 >= N) return;
+  const PlanLayout L = plan_layout(P, E);
+  constexpr int ES = YT == QMOE_F32 ? 4 : 2;  // bytes per y element
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)y, (short)0, (int)(uint32_t)(P * N * ES), 0x00020000);
+  int pos[QMOE_MAX_TOPK];
+  float wt[QMOE_MAX_TOPK];
+  u4_t v[QMOE_MAX_TOPK][ES / 2];
+#pragma unroll
+  for (int j = 0; j < QMOE_MAX_TOPK; ++j) {
+    pos[j] = j < topk ? plan[L.inv + t * topk + j] : -1;
+    wt[j] = j < topk ? w[t * topk + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < QMOE_MAX_TOPK; ++j) {
+    const uint32_t off = pos[j] >= 0 ? (uint32_t)(((int64_t)pos[j] * N + n0) * ES) : 0x80000000u;
+#pragma unroll
+    for (int h = 0; h < ES / 2; ++h)
+      v[j][h] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(yr, off + 16 * h, 0, 0));
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = base ? base[t * N + n0 + i] : 0.f;
+#pragma unroll
+  for (int j = 0; j < QMOE_MAX_TOPK; ++j) {
+    if (pos[j] < 0) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x;
+      if constexpr (YT == QMOE_F32) {
+        // through a scalar: a bit_cast applied to the vector element itself
+        // reads element 0 with this compiler
+        const uint32_t b = v[j][i / 4][i % 4];
+        x = __builtin_bit_cast(float, b);
+      } else {
+        const uint32_t b = (v[j][0][i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        x = YT == QMOE_F16 ? f16_to_f32(b) : bf16_to_f32(b);
+      }
+      acc[i] = __builtin_fmaf(wt[j], x, acc[i]);
+    }
+  }
+  const int64_t o = t * N + n0;
+  if (out_dtype == QMOE_F32) {
+    ((f4_t*)out)[o / 4] = f4_t{acc[0], acc[1], acc[2], acc[3]};
+    ((f4_t*)out)[o / 4 + 1] = f4_t{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    u4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = out_dtype == QMOE_F16 ? f32_to_f16(acc[2 * i]) : f32_to_bf16(acc[2 * i]);
+      const uint32_t hi = out_dtype == QMOE_F16 ? f32_to_f16(acc[2 * i + 1]) : f32_to_bf16(acc[2 * i + 1]);
+      r[i] = lo | (hi << 16);
+    }
+    ((u4_t*)out)[o / 8] = r;
+  }
+}
+
 void launch_combine_cast(float* acc, int64_t n, void* out, int out_dtype, hipStream_t s) {
   const int64_t n4 = n / 4;
   if (n4 > 0) {
@@ -83,6 +153,20 @@ void launch_combine_cast(float* acc, int64_t n, void* out, int out_dtype, hipStr
 void launch_moe_combine(const void* y, int y_dtype, const int32_t* plan, int64_t t, int topk, int E,
                         const float* w, int64_t N, const float* base, void* out, int out_dtype,
                         hipStream_t s) {
+  const int64_t ybytes = t * topk * N * (y_dtype == QMOE_F32 ? 4 : 2);
+  if (N % 8 == 0 && ybytes < (1ll << 32)) {
+    const dim3 grid((unsigned)(((N + 2047) / 2048) * t));
+    if (y_dtype == QMOE_F32)
+      hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_F32>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
+                         base, out, out_dtype);
+    else if (y_dtype == QMOE_F16)
+      hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_F16>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
+                         base, out, out_dtype);
+    else
+      hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_BF16>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
+                         base, out, out_dtype);
+    return;
+  }
   const dim3 grid((unsigned)(((N + 255) / 256) * t));
   hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, y, y_dtype, plan, t * topk, E, topk,
                      w, N, base, out, out_dtype);

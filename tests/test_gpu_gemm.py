@@ -214,3 +214,33 @@ def test_moe_single_expert_equals_dense():
     y_dense = qm.qmm_dense(dw, xd, qm.EPI_STORE, qm.F32)
     torch.cuda.synchronize()
     assert torch.equal(y_moe, y_dense)
+
+
+@pytest.mark.parametrize("N,ydt", [(2048, "bf16"), (2048, "f32"), (1004, "bf16")])
+def test_moe_combine_paths(N, ydt):
+    # the deterministic top-k combine over sorted rows, with a base, dropped
+    # pairs, 16-byte row loads (N % 8 == 0) and the element-wise path
+    rng = np.random.default_rng(N + len(ydt))
+    T, k, E = 300, 8, 32
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    ids[5, 2] = -1
+    ids[7, 0] = E
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    plan = qm.moe_plan(ids_d, E, 80)
+    y64 = rng.standard_normal((T * k, N))
+    y = torch.from_numpy(y64.astype(np.float32)).cuda()
+    if ydt == "bf16":
+        y = y.to(torch.bfloat16)
+    base = torch.from_numpy(rng.standard_normal((T, N)).astype(np.float32)).cuda()
+    out = qm.moe_combine(y, plan, T, k, E, w_d, base=base, out_dtype=qm.F32)
+    out2 = qm.moe_combine(y, plan, T, k, E, w_d, base=base, out_dtype=qm.F32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    yv = to_f64(y)
+    inv = qm.plan_views(plan, T, k, E)["inv"].cpu().numpy().reshape(T, k)
+    ref = base.cpu().numpy().astype(np.float64)
+    for j in range(k):
+        ok = inv[:, j] >= 0
+        ref[ok] += w[ok, j, None].astype(np.float64) * yv[inv[ok, j]]
+    assert normwise_err(to_f64(out), ref, "f32") <= 1e-6
