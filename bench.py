@@ -12,9 +12,12 @@ only; padding is not counted).
 The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers, each with its own
 copy of the weights) is timed as a captured HIP graph replay and eagerly; its
 GB/s are weight + activation bytes per layer over graph time per layer.  The
+DSv4-flash-shaped prefill (IQ2_XXS gate/up, Q2_K down, fp16, T = 2048) and the
+mixed-format FFN block (T = 8192, plus a Q8_0 shared expert; its four Q8_0
+projections timed apart) are reported under other_prefill_workloads.  The
 CPU oracle baseline is reported in the same JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-extra]
 
 Counter calibration and the traffic record (see profiles/):
     python bench.py --copy-probe MIB
@@ -130,6 +133,102 @@ def run_prefill(args, torch, qm):
             ev[name].append(m[j].elapsed_time(m[j + 1]) * 1e-3)
     kern = {n: float(np.median(v)) for n, v in ev.items()}
     return inp, alg, wall, kern
+
+
+def run_prefill_other(args, torch, qm, inp, R, steps):
+    """Another prefill workload, the same step as run_prefill (plan, gate/up
+    with SwiGLU, down with the weighted scatter-add, cast), plus the shared
+    expert (added into the same accumulator) when the workload has one; its
+    dense projections are timed separately."""
+    dev = "cuda"
+    codes = {"f16": qm.F16, "bf16": qm.BF16}
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    x = act_tensor(torch, inp.x) if inp.act == "bf16" else \
+        torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.float16)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
+    gus = [gu0] + [gu0.clone() for _ in range(R - 1)]
+    dns = [dn0] + [dn0.clone() for _ in range(R - 1)]
+    T, k, E, H, I = inp.T, inp.k, inp.E, inp.H, inp.I
+    bm = 80
+    plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
+    h = torch.empty((T * k, I), dtype=tdt[inp.act], device=dev)
+    acc = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=tdt[inp.out], device=dev)
+    shared = inp.shared_gate_up is not None
+    if shared:
+        sgu, sdn = upload(qm, inp.shared_gate_up), upload(qm, inp.shared_down)
+        hs = torch.empty((T, inp.shared_down.K), dtype=tdt[inp.act], device=dev)
+    names = ["plan", "gate_up", "down"] + (["shared"] if shared else []) + ["cast"]
+
+    def step(i, timed):
+        marks = []
+
+        def mark():
+            if timed:
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record()
+
+        mark()
+        qm.moe_plan(ids, E, bm, plan=plan)
+        mark()
+        qm.moe_gather_qmm(gus[i % R], plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
+        mark()
+        qm.moe_gather_qmm(dns[i % R], plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, topk_w=w,
+                          epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+        mark()
+        if shared:
+            qm.qmm_dense(sgu, x, qm.EPI_SWIGLU, codes[inp.act], out=hs)
+            qm.qmm_dense(sdn, hs, qm.EPI_ACCUMULATE, qm.F32, out=acc)
+            mark()
+        qm.combine_cast(acc, codes[inp.out], out=out)
+        mark()
+        return marks
+
+    for i in range(2):
+        step(i, False)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i, False)
+    e1.record()
+    torch.cuda.synchronize()
+    t_step = e0.elapsed_time(e1) * 1e-3 / steps
+    all_marks = [step(i, True) for i in range(steps)]
+    torch.cuda.synchronize()
+    kern = {n: float(np.median([m[j].elapsed_time(m[j + 1]) for m in all_marks])) * 1e-3
+            for j, n in enumerate(names)}
+    P = int(inp.ids.size)
+    flops = 2.0 * P * 3 * I * H
+    if shared:
+        SI = inp.shared_down.K
+        flops += 2.0 * T * 3 * SI * H
+    res = dict(workload=inp.name, tokens=T, hidden=H, intermediate=I, experts=E, top_k=k,
+               weights=f"gate/up {inp.w_gate_up.fmt}, down {inp.w_down.fmt}" + (", shared expert q8_0" if shared else ""),
+               activations=inp.act, weight_copies_rotated=R, ms_per_step=t_step * 1e3,
+               tflops=flops / t_step / 1e12, mfma_frac=flops / t_step / PEAK_MFMA_BF16,
+               kernels_us={n: v * 1e6 for n, v in kern.items()})
+    if inp.projections:
+        ps = [upload(qm, Wp) for Wp in inp.projections]
+        y = torch.empty((T, H), dtype=tdt[inp.act], device=dev)
+        for Wp in ps:
+            qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=y)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            for Wp in ps:
+                qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        tp = e0.elapsed_time(e1) * 1e-3 / steps
+        pf = 2.0 * T * H * H * len(ps)
+        res["projections"] = dict(count=len(ps), ms=tp * 1e3, tflops=pf / tp / 1e12, mfma_frac=pf / tp / PEAK_MFMA_BF16)
+        del ps
+    del gus, dns
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_decode(args, torch, qm, B, layers):
@@ -328,6 +427,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the DSv4-shaped and mixed-format prefill lines")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a device copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--summarize-traffic", nargs=5,
@@ -370,6 +470,14 @@ def main():
         "mfma_frac": alg["flops_gu"] / t_gu / PEAK_MFMA_BF16,
     }
     log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; kernels {json.dumps(kern)}")
+    others = []
+    if not args.no_extra:
+        import synth
+        for name, make, R in (("dsv4", lambda: synth.dsv4_flash_prefill(2048), 2),
+                              ("mixed", lambda: synth.mixed_ffn(8192), 2)):
+            log(f"prefill ({name}): building inputs")
+            others.append(run_prefill_other(args, torch, qm, make(), R, max(3, args.steps // 4)))
+            log(json.dumps(others[-1]))
     decode = []
     if not args.no_decode:
         for B in (1, 4, 8):
@@ -408,6 +516,7 @@ def main():
                     "us_gate_up_event": d["gate_up_s_event"] * 1e6, "us_down_event": d["down_s_event"] * 1e6,
                     "unique_experts": d["unique_experts"], "bytes_per_layer": d["bytes_per_layer"]}
                    for d in decode],
+        "other_prefill_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
