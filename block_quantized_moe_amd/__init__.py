@@ -45,13 +45,15 @@ _lib = None
 
 _SIGS = {
     "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
-    "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 4,
-    "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3,
+    "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
+    "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
     "qmoe_split_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_iq2_signs_table": [ctypes.c_void_p],
     "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
-    "qmoe_dequant_q2_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
-    "qmoe_dequant_iq2_xxs": [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_q2_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                  ctypes.c_void_p],
+    "qmoe_dequant_iq2_xxs": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                     ctypes.c_void_p],
     "qmoe_dequant_int4": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_qmm_dense": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_plan_bytes": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
@@ -119,25 +121,31 @@ def split_q8_0(aos: np.ndarray):
     return qs, d
 
 
-def split_q2_k(aos: np.ndarray):
-    aos = np.ascontiguousarray(aos, dtype=np.uint8)
-    nb = aos.size // 84
+def split_q2_k(aos: np.ndarray, rows: int, k: int):
+    """Q2_K blocks [rows, k/256, 84] -> tiled (qs bytes, scales, d, dmin)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 256) * 84:
+        raise QmoeError("split_q2_k: block count does not match rows/k")
+    nb = rows * (k // 256)
     qs = np.empty(nb * 16, np.uint32)
     sc = np.empty(nb * 16, np.uint8)
     d = np.empty(nb, np.uint16)
     dmin = np.empty(nb, np.uint16)
-    _check(lib().qmoe_split_q2_k(_np_ptr(aos), nb, _np_ptr(qs), _np_ptr(sc), _np_ptr(d), _np_ptr(dmin)), "split_q2_k")
+    _check(lib().qmoe_split_q2_k(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(sc), _np_ptr(d), _np_ptr(dmin)),
+           "split_q2_k")
     return qs, sc, d, dmin
 
 
-def split_iq2_xxs(aos: np.ndarray):
-    aos = np.ascontiguousarray(aos, dtype=np.uint8)
-    nb = aos.size // 66
-    idx = np.empty(nb * 8, np.uint32)
-    aux = np.empty(nb * 8, np.uint32)
+def split_iq2_xxs(aos: np.ndarray, rows: int, k: int):
+    """IQ2_XXS blocks [rows, k/256, 66] -> tiled ((index, aux) word pairs, d)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 256) * 66:
+        raise QmoeError("split_iq2_xxs: block count does not match rows/k")
+    nb = rows * (k // 256)
+    ia = np.empty(nb * 16, np.uint32)
     d = np.empty(nb, np.uint16)
-    _check(lib().qmoe_split_iq2_xxs(_np_ptr(aos), nb, _np_ptr(idx), _np_ptr(aux), _np_ptr(d)), "split_iq2_xxs")
-    return idx, aux, d
+    _check(lib().qmoe_split_iq2_xxs(_np_ptr(aos), rows, k, _np_ptr(ia), _np_ptr(d)), "split_iq2_xxs")
+    return ia, d
 
 
 def split_int4(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, rows: int, k: int, group: int):
@@ -211,11 +219,11 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
         q, d = split_q8_0(blocks)
         t["qs"], t["scales"] = _dev(q, device), _dev(d, device)
     elif fmt == "q2_k":
-        q, sc, d, dmin = split_q2_k(blocks)
+        q, sc, d, dmin = split_q2_k(blocks, E * N, K)
         t["qs"], t["scales"], t["d"], t["dmin"] = (_dev(q, device), _dev(sc, device), _dev(d, device), _dev(dmin, device))
     elif fmt == "iq2_xxs":
-        idx, aux, d = split_iq2_xxs(blocks)
-        t["qs"], t["aux"], t["d"] = _dev(idx, device), _dev(aux, device), _dev(d, device)
+        ia, d = split_iq2_xxs(blocks, E * N, K)
+        t["qs"], t["d"] = _dev(ia, device), _dev(d, device)
         t["grid"] = _dev(np.ascontiguousarray(grid, np.uint8).reshape(-1), device)
         t["signs"] = _dev(iq2_signs_table(), device)
     elif fmt == "int4":
@@ -259,10 +267,10 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
         st = L.qmoe_dequant_q8_0(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N * w.K // 32, _ptr(out), out_dtype, s)
     elif w.fmt == "q2_k":
         st = L.qmoe_dequant_q2_k(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["d"]), _ptr(t["dmin"]),
-                                 w.E * w.N * w.K // 256, _ptr(out), out_dtype, s)
+                                 w.E * w.N, w.K, _ptr(out), out_dtype, s)
     elif w.fmt == "iq2_xxs":
-        st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["aux"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
-                                    w.E * w.N * w.K // 256, _ptr(out), out_dtype, s)
+        st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
+                                    w.E * w.N, w.K, _ptr(out), out_dtype, s)
     else:
         st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, w.group,
                                  _ptr(out), out_dtype, s)

@@ -11,10 +11,10 @@
 
 namespace qmoe {
 void launch_dequant_q8_0(const int8_t*, const uint16_t*, int64_t, void*, int, hipStream_t);
-void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const uint16_t*, int64_t,
+void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
                          void*, int, hipStream_t);
-void launch_dequant_iq2_xxs(const uint32_t*, const uint32_t*, const uint16_t*, const uint8_t*,
-                            const uint8_t*, int64_t, void*, int, hipStream_t);
+void launch_dequant_iq2_xxs(const uint32_t*, const uint16_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
+                            void*, int, hipStream_t);
 void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
                          hipStream_t);
 void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
@@ -76,14 +76,14 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_Q2_K:
-      if (w->k % 256) return QMOE_ERR_BLOCK;
+      if (w->k % 256 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
       if (!w->scales || !w->d || !w->dmin) return QMOE_ERR_ARG;
       if (!al16(w->scales) || !al16(w->d) || !al16(w->dmin)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_IQ2_XXS:
-      if (w->k % 256) return QMOE_ERR_BLOCK;
-      if (!w->aux || !w->d || !w->grid || !w->signs) return QMOE_ERR_ARG;
-      if (!al16(w->aux) || !al16(w->d) || !al16(w->grid) || !al16(w->signs)) return QMOE_ERR_ALIGN;
+      if (w->k % 256 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (!w->d || !w->grid || !w->signs) return QMOE_ERR_ARG;
+      if (!al16(w->d) || !al16(w->grid) || !al16(w->signs)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_INT4:
       if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
@@ -137,26 +137,24 @@ int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, voi
 }
 
 int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t* d,
-                      const uint16_t* dmin, int64_t n_blocks, void* out, int32_t out_dtype,
+                      const uint16_t* dmin, int64_t rows, int64_t k, void* out, int32_t out_dtype,
                       void* stream) {
-  if (!qs || !scales || !d || !dmin || !out || n_blocks < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (!qs || !scales || !d || !dmin || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(scales) || !al16(d) || !al16(dmin) || !al16(out)) return QMOE_ERR_ALIGN;
-  if (n_blocks == 0) return QMOE_OK;
+  if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_dequant_q2_k(qs, scales, d, dmin, n_blocks, out, out_dtype, (hipStream_t)stream);
+  launch_dequant_q2_k(qs, scales, d, dmin, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
-
-int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
-                         const uint8_t* grid, const uint8_t* signs, int64_t n_blocks, void* out,
-                         int32_t out_dtype, void* stream) {
-  if (!idx || !aux || !d || !grid || !signs || !out || n_blocks < 0 || !dtype_ok(out_dtype))
-    return QMOE_ERR_ARG;
-  if (!al16(idx) || !al16(aux) || !al16(d) || !al16(grid) || !al16(signs) || !al16(out))
-    return QMOE_ERR_ALIGN;
-  if (n_blocks == 0) return QMOE_OK;
+int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid, const uint8_t* signs,
+                         int64_t rows, int64_t k, void* out, int32_t out_dtype, void* stream) {
+  if (!qs || !d || !grid || !signs || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(d) || !al16(grid) || !al16(signs) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_dequant_iq2_xxs(idx, aux, d, grid, signs, n_blocks, out, out_dtype, (hipStream_t)stream);
+  launch_dequant_iq2_xxs(qs, d, grid, signs, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 

@@ -50,22 +50,24 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
 
 // Q2_K: value = (d * a) * q - dmin * m with the sub-block's scale a (low
 // nibble) and min m (high nibble); element e's 2-bit code is in code byte
-// 32*(e/128) + e%32 at bit 2*((e%128)/32).
+// 32*(e/128) + e%32 at bit 2*((e%128)/32).  Tiled layout (qmoe.h): unit u
+// is 8-value unit p of super-block sb of row R.
 template <int OUT>
-__global__ __launch_bounds__(256) void dequant_q2_k_kernel(const uint32_t* __restrict__ qs,
+__global__ __launch_bounds__(256) void dequant_q2_k_kernel(const uint8_t* __restrict__ qs,
                                                            const uint8_t* __restrict__ sc,
                                                            const uint16_t* __restrict__ d,
                                                            const uint16_t* __restrict__ dmin,
-                                                           int64_t n_units, void* __restrict__ out) {
+                                                           int64_t n_units, int64_t SB, void* __restrict__ out) {
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
-    const int64_t b = u >> 5;
-    const int p = (int)(u & 31);            // elements 8p .. 8p+7 of the block
-    const int byte0 = 32 * (p >> 4) + 8 * (p & 3);
+    const int64_t R = u / (SB * 32), ur = u - R * SB * 32;
+    const int64_t sb = ur >> 5, t = (R >> 4) * SB + sb, r = R & 15;
+    const int p = (int)(ur & 31);            // elements 8p .. 8p+7 of the block
+    const int h = p >> 4, cb = 8 * (p & 3);  // code bytes 32h + cb .. +7
     const int shift = 2 * ((p & 15) >> 2);
-    const u2_t q = *(const u2_t*)(qs + b * 16 + (byte0 >> 2));
-    const uint32_t s = sc[b * 16 + (p >> 1)];
-    const float dl = f16_to_f32(d[b]) * (float)(s & 15u);
-    const float ml = f16_to_f32(dmin[b]) * (float)(s >> 4);
+    const u2_t q = *(const u2_t*)(qs + ((t * 2 + h) * 16 + r) * 32 + cb);
+    const uint32_t s = sc[(t * 16 + r) * 16 + (p >> 1)];
+    const float dl = f16_to_f32(d[t * 16 + r]) * (float)(s & 15u);
+    const float ml = f16_to_f32(dmin[t * 16 + r]) * (float)(s >> 4);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -78,26 +80,28 @@ __global__ __launch_bounds__(256) void dequant_q2_k_kernel(const uint32_t* __res
 
 // IQ2_XXS: octet j of group g takes magnitudes grid[idx_j][0..7], signs from
 // signs[(aux >> 7j) & 127] (bit l negates element l), scale d*(0.5+aux>>28)/4.
+// Tiled layout (qmoe.h): (index word, aux word) pairs by group and row.
 template <int OUT>
-__global__ __launch_bounds__(256) void dequant_iq2_xxs_kernel(const uint32_t* __restrict__ idx,
-                                                              const uint32_t* __restrict__ aux,
+__global__ __launch_bounds__(256) void dequant_iq2_xxs_kernel(const uint32_t* __restrict__ qs,
                                                               const uint16_t* __restrict__ d,
                                                               const uint8_t* __restrict__ grid,
                                                               const uint8_t* __restrict__ signs,
-                                                              int64_t n_units, void* __restrict__ out) {
+                                                              int64_t n_units, int64_t SB, void* __restrict__ out) {
   __shared__ uint8_t lgrid[2048];
   __shared__ uint8_t lsign[128];
   for (int i = threadIdx.x; i < 512; i += 256) ((uint32_t*)lgrid)[i] = ((const uint32_t*)grid)[i];
   if (threadIdx.x < 32) ((uint32_t*)lsign)[threadIdx.x] = ((const uint32_t*)signs)[threadIdx.x];
   __syncthreads();
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
-    const int64_t b = u >> 5;
-    const int p = (int)(u & 31);
+    const int64_t R = u / (SB * 32), ur = u - R * SB * 32;
+    const int64_t sb = ur >> 5, t = (R >> 4) * SB + sb, r = R & 15;
+    const int p = (int)(ur & 31);
     const int g = p >> 2, j = p & 3;
-    const uint32_t ix = (idx[b * 8 + g] >> (8 * j)) & 0xFFu;
-    const uint32_t a = aux[b * 8 + g];
+    const u2_t ia = *(const u2_t*)(qs + ((t * 8 + g) * 16 + r) * 2);
+    const uint32_t ix = (ia[0] >> (8 * j)) & 0xFFu;
+    const uint32_t a = ia[1];
     const uint32_t mask = lsign[(a >> (7 * j)) & 127u];
-    const float db = f16_to_f32(d[b]) * (0.5f + (float)(a >> 28)) * 0.25f;
+    const float db = f16_to_f32(d[t * 16 + r]) * (0.5f + (float)(a >> 28)) * 0.25f;
     float v[8];
 #pragma unroll
     for (int l = 0; l < 8; ++l) {
@@ -155,18 +159,17 @@ void launch_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, 
                     units, out);
 }
 void launch_dequant_q2_k(const uint32_t* qs, const uint8_t* sc, const uint16_t* d,
-                         const uint16_t* dmin, int64_t n_blocks, void* out, int dtype,
+                         const uint16_t* dmin, int64_t rows, int64_t k, void* out, int dtype,
                          hipStream_t s) {
-  const int64_t units = n_blocks * 32;
-  QMOE_DISPATCH_OUT(dtype, dequant_q2_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc,
-                    d, dmin, units, out);
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_q2_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, (const uint8_t*)qs, sc,
+                    d, dmin, units, k / 256, out);
 }
-void launch_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
-                            const uint8_t* grid, const uint8_t* signs, int64_t n_blocks,
-                            void* out, int dtype, hipStream_t s) {
-  const int64_t units = n_blocks * 32;
-  QMOE_DISPATCH_OUT(dtype, dequant_iq2_xxs_kernel, dim3(grid_for(units)), dim3(256), 0, s, idx,
-                    aux, d, grid, signs, units, out);
+void launch_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid, const uint8_t* signs,
+                            int64_t rows, int64_t k, void* out, int dtype, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_iq2_xxs_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, d, grid, signs,
+                    units, k / 256, out);
 }
 void launch_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k, int group,
                          void* out, int dtype, hipStream_t s) {

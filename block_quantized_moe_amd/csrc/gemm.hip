@@ -124,28 +124,34 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
       r.x2 = ((const uint16_t*)g.scales)[R * (K / 32) + k0 / 32 + 1];
     }
   } else if constexpr (FMT == QMOE_Q2_K) {
-    const int64_t B = R * (K / 256) + k0 / 256;
+    // tiled layout: t = 16-row block * K/256 + super-block; a wave's loads of
+    // one 16-row block read contiguous runs
+    const int64_t t = (R >> 4) * (K / 256) + k0 / 256, rr = R & 15;
     const int e0 = (int)(k0 & 255) + 16 * lg;
-    const int byte = 32 * (e0 >> 7) + (e0 & 31);
-    r.v = *(const u4_t*)((const uint32_t*)g.qs + B * 16 + byte / 4);
-    r.x0 = ((const uint8_t*)g.scales)[B * 16 + (e0 >> 4)];
+    const int h = e0 >> 7, cb = e0 & 31;  // code bytes 32h + cb .. +15
+    r.v = *(const u4_t*)((const uint8_t*)g.qs + ((t * 2 + h) * 16 + rr) * 32 + cb);
+    r.x0 = ((const uint8_t*)g.scales)[(t * 16 + rr) * 16 + (e0 >> 4)];
     r.x1 = 2u * (uint32_t)((e0 & 127) >> 5);  // bit shift of this lane's codes
-    r.x2 = ((const uint16_t*)g.d)[B];
-    r.x3 = ((const uint16_t*)g.dmin)[B];
-  } else {  // IQ2_XXS
-    const int64_t B = R * (K / 256) + k0 / 256;
+    r.x2 = ((const uint16_t*)g.d)[t * 16 + rr];
+    r.x3 = ((const uint16_t*)g.dmin)[t * 16 + rr];
+  } else {  // IQ2_XXS, tiled: (index word, aux word) pairs by group and row
+    const int64_t t = (R >> 4) * (K / 256) + k0 / 256, rr = R & 15;
+    const uint32_t* ia = (const uint32_t*)g.qs + (t * 8 * 16 + rr) * 2;
     if constexpr (KOrder<FMT, ACT>::chunk) {
       const int G = ((int)(k0 & 255) + 16 * lg) >> 5;
-      r.x0 = ((const uint32_t*)g.qs)[B * 8 + G];
-      r.x1 = ((const uint32_t*)g.aux)[B * 8 + G];
+      const u2_t p = *(const u2_t*)(ia + G * 32);
+      r.x0 = p[0];
+      r.x1 = p[1];
     } else {
       const int G = (int)(k0 & 255) >> 5;
-      r.x0 = ((const uint32_t*)g.qs)[B * 8 + G];
-      r.x1 = ((const uint32_t*)g.aux)[B * 8 + G];
-      r.x2 = ((const uint32_t*)g.qs)[B * 8 + G + 1];
-      r.x3 = ((const uint32_t*)g.aux)[B * 8 + G + 1];
+      const u2_t p0 = *(const u2_t*)(ia + G * 32);
+      const u2_t p1 = *(const u2_t*)(ia + (G + 1) * 32);
+      r.x0 = p0[0];
+      r.x1 = p0[1];
+      r.x2 = p1[0];
+      r.x3 = p1[1];
     }
-    r.x4 = ((const uint16_t*)g.d)[B];
+    r.x4 = ((const uint16_t*)g.d)[t * 16 + rr];
   }
   return r;
 }

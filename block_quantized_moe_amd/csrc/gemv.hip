@@ -146,16 +146,17 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       }
     }
   } else if constexpr (FMT == QMOE_Q2_K) {
-    const int64_t B = R * (K / 256) + c / 8;
+    // tiled layout: t = (R/16) * (K/256) + super-block, row r = R % 16
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
     const int cc = (int)(c & 7);
-    const uint32_t* qb = (const uint32_t*)g.qs + B * 16 + 8 * (cc >> 2);
+    const uint8_t* qb = (const uint8_t*)g.qs + ((t * 2 + (cc >> 2)) * 16 + r) * 32;
     const u4_t q0 = *(const u4_t*)qb;
-    const u4_t q1 = *(const u4_t*)(qb + 4);
+    const u4_t q1 = *(const u4_t*)(qb + 16);
     const uint32_t shift = 2u * (uint32_t)(cc & 3);
-    const uint32_t sc0 = ((const uint8_t*)g.scales)[B * 16 + 2 * cc];
-    const uint32_t sc1 = ((const uint8_t*)g.scales)[B * 16 + 2 * cc + 1];
-    const float d = f16_to_f32(((const uint16_t*)g.d)[B]);
-    const float dm = f16_to_f32(((const uint16_t*)g.dmin)[B]);
+    const uint32_t sc0 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc];
+    const uint32_t sc1 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc + 1];
+    const float d = f16_to_f32(((const uint16_t*)g.d)[t * 16 + r]);
+    const float dm = f16_to_f32(((const uint16_t*)g.dmin)[t * 16 + r]);
     const float dl0 = d * (float)(sc0 & 15u), ml0 = dm * (float)(sc0 >> 4);
     const float dl1 = d * (float)(sc1 & 15u), ml1 = dm * (float)(sc1 >> 4);
     uint32_t cp[16];
@@ -181,12 +182,13 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
                   dl1 * (p1 - Magic<ACT>::v * x[t].s1) - ml1 * x[t].s1;
       }
     }
-  } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8
-    const int64_t B = R * (K / 256) + c / 8;
+  } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8 (tiled layout)
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
     const int G = (int)(c & 7);
-    const uint32_t idx = ((const uint32_t*)g.qs)[B * 8 + G];
-    const uint32_t aux = ((const uint32_t*)g.aux)[B * 8 + G];
-    const float db = f16_to_f32(((const uint16_t*)g.d)[B]) * (0.5f + (float)(aux >> 28)) * 0.25f;
+    const u2_t ia = *(const u2_t*)((const uint32_t*)g.qs + ((t * 8 + G) * 16 + r) * 2);
+    const uint32_t idx = ia[0];
+    const uint32_t aux = ia[1];
+    const float db = f16_to_f32(((const uint16_t*)g.d)[t * 16 + r]) * (0.5f + (float)(aux >> 28)) * 0.25f;
     uint32_t cp[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -6,7 +6,8 @@
 // codes, scales, lookup tables) so the hot kernels do no per-call byte
 // surgery; the DSV4 campaign page repacks q2_K blocks to SoA at load because
 // the AoS code bytes sit at 84*blk+16 and are only 4-byte aligned.  Here every
-// output array is naturally aligned and contiguous per block.
+// output array is naturally aligned, and the matmul formats are tiled by
+// 16-row blocks for coalesced wave-wide loads.
 #include <stdint.h>
 #include <string.h>
 
@@ -24,28 +25,45 @@ int qmoe_split_q8_0(const void* aos, int64_t n_blocks, int8_t* qs, uint16_t* d) 
   return QMOE_OK;
 }
 
-int qmoe_split_q2_k(const void* aos, int64_t n_blocks, uint32_t* qs, uint8_t* scales,
+// Q2_K and IQ2_XXS are tiled by 16-row blocks (global row R = 16 rb + r),
+// super-block sb = k / 256 inner, so that every 64-wide k tile of a 16-row
+// block reads its codes and per-row metadata as a few contiguous runs (the
+// layouts are spelled out in qmoe.h).  aos holds rows * k/256 blocks, row
+// after row.
+int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin) {
-  if (!aos || !qs || !scales || !d || !dmin || n_blocks < 0) return QMOE_ERR_ARG;
-  const uint8_t* p = (const uint8_t*)aos;
-  for (int64_t b = 0; b < n_blocks; ++b, p += 84) {
-    memcpy(&scales[b * 16], p, 16);
-    memcpy(&qs[b * 16], p + 16, 64);  // 16 little-endian u32 words
-    memcpy(&d[b], p + 80, 2);
-    memcpy(&dmin[b], p + 82, 2);
+  if (!aos || !qs || !scales || !d || !dmin || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  const int64_t SB = k / 256;
+  uint8_t* qb = (uint8_t*)qs;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t sb = 0; sb < SB; ++sb) {
+      const uint8_t* p = (const uint8_t*)aos + (R * SB + sb) * 84;
+      const int64_t base = rb * SB + sb;
+      memcpy(&scales[(base * 16 + r) * 16], p, 16);
+      for (int h = 0; h < 2; ++h) memcpy(&qb[((base * 2 + h) * 16 + r) * 32], p + 16 + 32 * h, 32);
+      memcpy(&d[base * 16 + r], p + 80, 2);
+      memcpy(&dmin[base * 16 + r], p + 82, 2);
+    }
   }
   return QMOE_OK;
 }
 
-int qmoe_split_iq2_xxs(const void* aos, int64_t n_blocks, uint32_t* idx, uint32_t* aux,
-                       uint16_t* d) {
-  if (!aos || !idx || !aux || !d || n_blocks < 0) return QMOE_ERR_ARG;
-  const uint8_t* p = (const uint8_t*)aos;
-  for (int64_t b = 0; b < n_blocks; ++b, p += 66) {
-    memcpy(&d[b], p, 2);
-    for (int g = 0; g < 8; ++g) {
-      memcpy(&idx[b * 8 + g], p + 2 + 8 * g, 4);
-      memcpy(&aux[b * 8 + g], p + 2 + 8 * g + 4, 4);
+int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* ia, uint16_t* d) {
+  if (!aos || !ia || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  const int64_t SB = k / 256;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t sb = 0; sb < SB; ++sb) {
+      const uint8_t* p = (const uint8_t*)aos + (R * SB + sb) * 66;
+      const int64_t base = rb * SB + sb;
+      memcpy(&d[base * 16 + r], p, 2);
+      for (int g = 0; g < 8; ++g) {
+        memcpy(&ia[((base * 8 + g) * 16 + r) * 2], p + 2 + 8 * g, 4);      // grid indices
+        memcpy(&ia[((base * 8 + g) * 16 + r) * 2 + 1], p + 6 + 8 * g, 4);  // signs | scale
+      }
     }
   }
   return QMOE_OK;

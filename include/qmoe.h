@@ -87,12 +87,20 @@ enum {
  *
  *   Q8_0     qs     int8  [E, n, k]              codes
  *            scales fp16  [E, n, k/32]           block scale d
- *   Q2_K     qs     u32   [E, n, k/256, 16]      the 64 code bytes of a block
- *            scales u8    [E, n, k/256, 16]      byte s: low nibble scale, high nibble min
- *            d,dmin fp16  [E, n, k/256]
- *   IQ2_XXS  qs     u32   [E, n, k/256, 8]       4 grid-index bytes per group of 32
- *            aux    u32   [E, n, k/256, 8]       4 x 7 sign bits (bits 0..27), scale (28..31)
- *            d      fp16  [E, n, k/256]
+ *   Q2_K and IQ2_XXS are tiled by qmoe_split_q2_k / qmoe_split_iq2_xxs
+ *   (rows = E*n a multiple of 16, k a multiple of 256).  Global row
+ *   R = e*n + row, block rb = R/16, r = R%16, super-block sb (256 values
+ *   along k), SB = k/256, t = rb*SB + sb:
+ *   Q2_K     qs     u8    [t][2][16][32]         half h of row r's 64 code bytes
+ *                                                (bytes 32h .. 32h+31)
+ *            scales u8    [t][16][16]            row r's 16 bytes s: low nibble
+ *                                                scale, high nibble min
+ *            d,dmin fp16  [t][16]
+ *   IQ2_XXS  qs     u32   [t][8][16][2]          group g (32 values) of row r:
+ *                                                (4 grid-index bytes, aux word =
+ *                                                4 x 7 sign bits (0..27) | scale (28..31))
+ *            aux    NULL
+ *            d      fp16  [t][16]
  *            grid   u8    [256, 8]               magnitude rows
  *            signs  u8    [128]                  sign masks (qmoe_iq2_signs_table)
  *   INT4     value = s*q + b per group of `group` values along k, tiled by
@@ -130,17 +138,21 @@ typedef struct qmoe_weights {
  * Host-side loader split ([GGUF] "Design -- CPU-side decomposition": each
  * on-disk block is decomposed once at load into separate GPU-resident
  * arrays; [DSV4] load-time q2_K SoA repack).  HOST pointers; the caller
- * uploads the outputs.  `aos` holds n_blocks consecutive on-disk blocks:
+ * uploads the outputs.  `aos` holds consecutive on-disk blocks (Q8_0:
+ * n_blocks of them; Q2_K, IQ2_XXS: rows * k/256 of them, row after row):
  *   Q8_0     34 B: fp16 d, 32 int8 codes
  *   Q2_K     84 B: 16 scale|min bytes, 64 code bytes, fp16 d, fp16 dmin
  *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
- * Returns QMOE_ERR_ARG on NULL / negative n_blocks.
+ * Q2_K and IQ2_XXS come out in the tiled form above (so that each wave-wide
+ * metadata load of the matmul kernels reads contiguous bytes): qs holds
+ * rows*k/16 bytes (Q2_K) or rows*k/16 u32 (IQ2_XXS), scales rows*k/16 bytes,
+ * d and dmin rows*k/256 values.  Returns QMOE_ERR_ARG on NULL / negative
+ * sizes, QMOE_ERR_BLOCK unless rows % 16 == 0 and k % 256 == 0.
  * ------------------------------------------------------------------------ */
 int qmoe_split_q8_0(const void* aos, int64_t n_blocks, int8_t* qs, uint16_t* d);
-int qmoe_split_q2_k(const void* aos, int64_t n_blocks, uint32_t* qs, uint8_t* scales,
+int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin);
-int qmoe_split_iq2_xxs(const void* aos, int64_t n_blocks, uint32_t* idx, uint32_t* aux,
-                       uint16_t* d);
+int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint16_t* d);
 /* int4 slabs from the on-disk (MLX) form -- words [rows][k/8] with element
  * 8w+i in nibble i of word w, fp16 scales and biases [rows][k/group] -- to the
  * tiled GPU form above: every wave-wide weight load is one contiguous 512-byte
@@ -158,16 +170,18 @@ void qmoe_iq2_signs_table(uint8_t out[128]);
  * Standalone dequantisation ([GGUF] "Kernels" 1-3; [BAGEL] int4 slabs).
  * Decodes every value in fp32 exactly as the format defines it and rounds
  * once (to nearest even) to out_dtype; results are bit-exact.  DEVICE
- * pointers, 16-byte aligned; out holds n_blocks * block values (int4:
- * rows * k) in the block order of the input.
+ * pointers, 16-byte aligned; out holds n_blocks * 32 values (Q8_0) or the
+ * rows x k matrix (the tiled formats), row-major.  Tiled formats return
+ * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 256 (int4: 64
+ * and group).
  * ------------------------------------------------------------------------ */
 int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks,
                       void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t* d,
-                      const uint16_t* dmin, int64_t n_blocks,
+                      const uint16_t* dmin, int64_t rows, int64_t k,
                       void* out, int32_t out_dtype, void* stream);
-int qmoe_dequant_iq2_xxs(const uint32_t* idx, const uint32_t* aux, const uint16_t* d,
-                         const uint8_t* grid, const uint8_t* signs, int64_t n_blocks,
+int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid,
+                         const uint8_t* signs, int64_t rows, int64_t k,
                          void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k,
                       int32_t group, void* out, int32_t out_dtype, void* stream);

@@ -38,24 +38,43 @@ def test_split_q8_0_round_trip():
     assert np.array_equal(qs.view(np.uint8).reshape(-1, 32), blocks[:, 2:])
 
 
-def test_split_q2_k_round_trip():
-    W = synth.q2_k(np.random.default_rng(1), 1, 3, 512)
-    qs, sc, d, dmin = qm.split_q2_k(W.blocks)
-    b = W.blocks.reshape(-1, 84)
-    assert np.array_equal(sc.reshape(-1, 16), b[:, :16])
-    assert np.array_equal(qs.view(np.uint8).reshape(-1, 64), b[:, 16:80])
-    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), b[:, 80:82])
-    assert np.array_equal(dmin.view(np.uint8).reshape(-1, 2), b[:, 82:84])
+def test_split_q2_k_tiled_layout():
+    """Every byte of each block lands where the header's tiled layout says."""
+    rows, k = 32, 512
+    W = synth.q2_k(np.random.default_rng(1), 2, rows // 2, k)
+    qs, sc, d, dmin = qm.split_q2_k(W.blocks, rows, k)
+    b = W.blocks.reshape(rows, k // 256, 84)
+    SB = k // 256
+    q8 = qs.view(np.uint8).reshape(rows // 16, SB, 2, 16, 32)
+    sc = sc.reshape(rows // 16, SB, 16, 16)
+    d = d.view(np.uint8).reshape(rows // 16, SB, 16, 2)
+    dmin = dmin.view(np.uint8).reshape(rows // 16, SB, 16, 2)
+    for R in range(rows):
+        for s_ in range(SB):
+            blk = b[R, s_]
+            assert np.array_equal(sc[R // 16, s_, R % 16], blk[:16])
+            for h in range(2):
+                assert np.array_equal(q8[R // 16, s_, h, R % 16], blk[16 + 32 * h:48 + 32 * h])
+            assert np.array_equal(d[R // 16, s_, R % 16], blk[80:82])
+            assert np.array_equal(dmin[R // 16, s_, R % 16], blk[82:84])
+    with pytest.raises(qm.QmoeError):
+        qm.split_q2_k(W.blocks[:1], 8, k)   # 8 rows: not a multiple of 16
 
 
-def test_split_iq2_xxs_round_trip():
-    W = synth.iq2_xxs(np.random.default_rng(2), 1, 2, 256)
-    idx, aux, d = qm.split_iq2_xxs(W.blocks)
-    b = W.blocks.reshape(-1, 66)
-    g = b[:, 2:].reshape(-1, 8, 8)
-    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), b[:, :2])
-    assert np.array_equal(idx.view(np.uint8).reshape(-1, 8, 4), g[:, :, :4])
-    assert np.array_equal(aux.view(np.uint8).reshape(-1, 8, 4), g[:, :, 4:])
+def test_split_iq2_xxs_tiled_layout():
+    rows, k = 16, 768
+    W = synth.iq2_xxs(np.random.default_rng(2), 1, rows, k)
+    ia, d = qm.split_iq2_xxs(W.blocks, rows, k)
+    SB = k // 256
+    b = W.blocks.reshape(rows, SB, 66)
+    ia = ia.view(np.uint8).reshape(rows // 16, SB, 8, 16, 8)
+    d = d.view(np.uint8).reshape(rows // 16, SB, 16, 2)
+    for R in range(rows):
+        for s_ in range(SB):
+            blk = b[R, s_]
+            assert np.array_equal(d[R // 16, s_, R % 16], blk[:2])
+            for g in range(8):
+                assert np.array_equal(ia[R // 16, s_, g, R % 16], blk[2 + 8 * g:10 + 8 * g])
 
 
 def test_split_int4_tiled_layout():
@@ -127,6 +146,10 @@ def test_argument_validation_before_launch():
                                ctypes.c_void_p(16), 1, None) == -3
     assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 128, 64,
                                ctypes.c_void_p(16), 1, None) == -3
+    # tiled formats: rows not a multiple of 16, k not a multiple of 256
+    P16 = ctypes.c_void_p(16)
+    assert L.qmoe_dequant_q2_k(P16, P16, P16, P16, 8, 256, P16, 1, None) == -3
+    assert L.qmoe_dequant_iq2_xxs(P16, P16, P16, P16, 16, 128, P16, 1, None) == -3
     # matmul: k not a block multiple, too many experts, wrong epilogue / dtype
     w = qm._Weights(qm.Q2_K, 1, 64, 320, 0, 0, 16, 0, 16, 0, 16, 16, 0, 0)
     assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -3

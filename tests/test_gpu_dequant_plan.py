@@ -37,7 +37,7 @@ def _bits_equal(gpu, ref, dtype):
 
 def _weights(fmt, rng):
     if fmt in ("q2_k", "iq2_xxs"):
-        W = synth.weights(fmt, rng, 2, 37, 512)
+        W = synth.weights(fmt, rng, 2, 40, 512)   # E*N a multiple of 16 (tiled layout)
     elif fmt == "int4":
         W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
     else:
