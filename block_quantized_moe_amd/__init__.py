@@ -44,12 +44,13 @@ class _Weights(ctypes.Structure):
 _lib = None
 
 _SIGS = {
-    "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
+    "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
     "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
     "qmoe_split_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_iq2_signs_table": [ctypes.c_void_p],
-    "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                          ctypes.c_int32, ctypes.c_void_p],
     "qmoe_dequant_q2_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                                                   ctypes.c_void_p],
     "qmoe_dequant_iq2_xxs": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
@@ -112,12 +113,14 @@ def _np_ptr(a: np.ndarray):
 # host-side split (C functions of the library)
 # ---------------------------------------------------------------------------
 
-def split_q8_0(aos: np.ndarray):
-    aos = np.ascontiguousarray(aos, dtype=np.uint8)
-    nb = aos.size // 34
-    qs = np.empty(nb * 32, np.int8)
-    d = np.empty(nb, np.uint16)
-    _check(lib().qmoe_split_q8_0(_np_ptr(aos), nb, _np_ptr(qs), _np_ptr(d)), "split_q8_0")
+def split_q8_0(aos: np.ndarray, rows: int, k: int):
+    """Q8_0 blocks [rows, k/32, 34] -> tiled (codes, scales)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 32) * 34:
+        raise QmoeError("split_q8_0: block count does not match rows/k")
+    qs = np.empty(rows * k, np.int8)
+    d = np.empty(rows * (k // 32), np.uint16)
+    _check(lib().qmoe_split_q8_0(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(d)), "split_q8_0")
     return qs, d
 
 
@@ -216,7 +219,7 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
     qs, scale, bias: MLX-style int4 arrays for int4.  grid: uint8 [256, 8] (iq2_xxs)."""
     t = {}
     if fmt == "q8_0":
-        q, d = split_q8_0(blocks)
+        q, d = split_q8_0(blocks, E * N, K)
         t["qs"], t["scales"] = _dev(q, device), _dev(d, device)
     elif fmt == "q2_k":
         q, sc, d, dmin = split_q2_k(blocks, E * N, K)
@@ -264,7 +267,7 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
     L = lib()
     s = _stream()
     if w.fmt == "q8_0":
-        st = L.qmoe_dequant_q8_0(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N * w.K // 32, _ptr(out), out_dtype, s)
+        st = L.qmoe_dequant_q8_0(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
     elif w.fmt == "q2_k":
         st = L.qmoe_dequant_q2_k(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["d"]), _ptr(t["dmin"]),
                                  w.E * w.N, w.K, _ptr(out), out_dtype, s)

@@ -10,7 +10,7 @@
 #include "common.h"
 
 namespace qmoe {
-void launch_dequant_q8_0(const int8_t*, const uint16_t*, int64_t, void*, int, hipStream_t);
+void launch_dequant_q8_0(const int8_t*, const uint16_t*, int64_t, int64_t, void*, int, hipStream_t);
 void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
                          void*, int, hipStream_t);
 void launch_dequant_iq2_xxs(const uint32_t*, const uint16_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
@@ -71,7 +71,7 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
   if (!w->qs || !al16(w->qs)) return w->qs ? QMOE_ERR_ALIGN : QMOE_ERR_ARG;
   switch (w->fmt) {
     case QMOE_Q8_0:
-      if (w->k % 32) return QMOE_ERR_BLOCK;
+      if (w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
       if (!w->scales) return QMOE_ERR_ARG;
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
@@ -126,13 +126,14 @@ const char* qmoe_strerror(int status) {
 
 // ------------------------------------------------------------------ dequant
 
-int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, void* out,
-                      int32_t out_dtype, void* stream) {
-  if (!qs || !d || !out || n_blocks < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k, void* out, int32_t out_dtype,
+                      void* stream) {
+  if (!qs || !d || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(d) || !al16(out)) return QMOE_ERR_ALIGN;
-  if (n_blocks == 0) return QMOE_OK;
+  if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_dequant_q8_0(qs, d, n_blocks, out, out_dtype, (hipStream_t)stream);
+  launch_dequant_q8_0(qs, d, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 

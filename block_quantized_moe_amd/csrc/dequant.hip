@@ -30,19 +30,23 @@ __device__ __forceinline__ void store8(void* out, int64_t u, const float (&v)[8]
   }
 }
 
-// Q8_0: value = code * d over 32-value blocks.
+// Q8_0: value = code * d over 32-value blocks.  Tiled layout (qmoe.h): unit
+// u is values 8(u % (k/8)) .. +7 of row R = u / (k/8).
 template <int OUT>
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restrict__ qs,
                                                            const uint16_t* __restrict__ d,
-                                                           int64_t n_units, void* __restrict__ out) {
+                                                           int64_t n_units, int64_t k, void* __restrict__ out) {
+  const int64_t upr = k / 8, KT = k / 64;
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
-    const u2_t q = ((const u2_t*)qs)[u];
-    const float s = f16_to_f32(d[u >> 2]);
+    const int64_t R = u / upr, kk = 8 * (u - R * upr);
+    const int64_t rb = R >> 4, r = R & 15, kt = kk >> 6, c = (kk & 63) >> 4;
+    const u2_t q = *(const u2_t*)(qs + (((rb * KT + kt) * 4 + c) * 16 + r) * 16 + (kk & 15));
+    const float s = f16_to_f32(d[(rb * (k / 32) + (kk >> 5)) * 16 + r]);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int8_t c = (int8_t)((q[i >> 2] >> (8 * (i & 3))) & 0xFF);
-      v[i] = (float)c * s;
+      const int8_t cd = (int8_t)((q[i >> 2] >> (8 * (i & 3))) & 0xFF);
+      v[i] = (float)cd * s;
     }
     store8<OUT>(out, u, v);
   }
@@ -152,11 +156,11 @@ static inline unsigned grid_for(int64_t units) {
     else hipLaunchKernelGGL(KERNEL<QMOE_BF16>, __VA_ARGS__);                          \
   } while (0)
 
-void launch_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks, void* out,
+void launch_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k, void* out,
                          int dtype, hipStream_t s) {
-  const int64_t units = n_blocks * 4;
+  const int64_t units = rows * (k / 8);
   QMOE_DISPATCH_OUT(dtype, dequant_q8_0_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, d,
-                    units, out);
+                    units, k, out);
 }
 void launch_dequant_q2_k(const uint32_t* qs, const uint8_t* sc, const uint16_t* d,
                          const uint16_t* dmin, int64_t rows, int64_t k, void* out, int dtype,

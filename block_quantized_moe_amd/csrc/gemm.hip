@@ -111,17 +111,21 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
     // scale in the low half, bias in the high half (the other fields stay unused)
     r.x0 = ((const uint32_t*)g.scales)[(rb * (K / g.group) + k0 / g.group) * 16 + rr];
   } else if constexpr (FMT == QMOE_Q8_0) {
+    // tiled layout: the 16 rows x 64 k of one tile are one 1 KB run, chunk c
+    // (16 values) of row r at byte 256c + 16r
+    const int64_t rb = R >> 4, rr = R & 15;
+    const int8_t* tile = (const int8_t*)g.qs + (rb * (K / 64) + k0 / 64) * 1024 + 16 * rr;
+    const uint16_t* sc = (const uint16_t*)g.scales + (rb * (K / 32) + k0 / 32) * 16 + rr;
     if constexpr (KOrder<FMT, ACT>::chunk) {
-      const int64_t kk = k0 + 16 * lg;
-      r.v = *(const u4_t*)((const int8_t*)g.qs + R * K + kk);
-      r.x0 = ((const uint16_t*)g.scales)[R * (K / 32) + kk / 32];
+      r.v = *(const u4_t*)(tile + 256 * lg);
+      r.x0 = sc[16 * (lg >> 1)];
     } else {
-      const int8_t* base = (const int8_t*)g.qs + R * K + k0 + 8 * lg;
-      const u2_t q0 = *(const u2_t*)base;
-      const u2_t q1 = *(const u2_t*)(base + 32);
+      // values 8lg .. 8lg+7 and 32+8lg .. 32+8lg+7 of the tile
+      const u2_t q0 = *(const u2_t*)(tile + 256 * (lg >> 1) + 8 * (lg & 1));
+      const u2_t q1 = *(const u2_t*)(tile + 256 * (2 + (lg >> 1)) + 8 * (lg & 1));
       r.v = u4_t{q0[0], q0[1], q1[0], q1[1]};
-      r.x0 = ((const uint16_t*)g.scales)[R * (K / 32) + k0 / 32];
-      r.x2 = ((const uint16_t*)g.scales)[R * (K / 32) + k0 / 32 + 1];
+      r.x0 = sc[0];
+      r.x2 = sc[16];
     }
   } else if constexpr (FMT == QMOE_Q2_K) {
     // tiled layout: t = 16-row block * K/256 + super-block; a wave's loads of

@@ -126,10 +126,12 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       }
     }
   } else if constexpr (FMT == QMOE_Q8_0) {
-    const int8_t* base = (const int8_t*)g.qs + R * K + 32 * c;
+    // tiled layout: chunks 2(c&1), 2(c&1)+1 of k tile c/2, 16 bytes each per row
+    const int64_t rb = R >> 4, rr = R & 15;
+    const int8_t* base = (const int8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
     const u4_t q0 = *(const u4_t*)base;
-    const u4_t q1 = *(const u4_t*)(base + 16);
-    const float dd = f16_to_f32(((const uint16_t*)g.scales)[R * (K / 32) + c]);
+    const u4_t q1 = *(const u4_t*)(base + 256);
+    const float dd = f16_to_f32(((const uint16_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr]);
     uint32_t cp[16];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {

@@ -15,12 +15,22 @@
 
 extern "C" {
 
-int qmoe_split_q8_0(const void* aos, int64_t n_blocks, int8_t* qs, uint16_t* d) {
-  if (!aos || !qs || !d || n_blocks < 0) return QMOE_ERR_ARG;
-  const uint8_t* p = (const uint8_t*)aos;
-  for (int64_t b = 0; b < n_blocks; ++b, p += 34) {
-    memcpy(&d[b], p, 2);
-    memcpy(&qs[b * 32], p + 2, 32);
+// Q8_0: codes tiled as [R/16][k/64][4][16][16] (chunk c of 16 values of row
+// 16 rb + r in k tile kt), block scales as [R/16][k/32][16].
+int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16_t* d) {
+  if (!aos || !qs || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  const int64_t KT = k / 64, NB = k / 32;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t b = 0; b < NB; ++b) {
+      const uint8_t* p = (const uint8_t*)aos + (R * NB + b) * 34;
+      memcpy(&d[(rb * NB + b) * 16 + r], p, 2);
+      for (int h = 0; h < 2; ++h) {  // the block's two 16-value chunks
+        const int64_t kk = 32 * b + 16 * h, kt = kk / 64, c = (kk % 64) / 16;
+        memcpy(&qs[(((rb * KT + kt) * 4 + c) * 16 + r) * 16], p + 2 + 16 * h, 16);
+      }
+    }
   }
   return QMOE_OK;
 }

@@ -85,8 +85,11 @@ enum {
  * All pointers are DEVICE pointers, 16-byte aligned; fields a format does not
  * use must be NULL.
  *
- *   Q8_0     qs     int8  [E, n, k]              codes
- *            scales fp16  [E, n, k/32]           block scale d
+ *   Q8_0     tiled by qmoe_split_q8_0 (rows = E*n a multiple of 16, k of 64);
+ *            R, rb, r as below, 64-wide k tile kt:
+ *            qs     int8  [R/16][k/64][4][16][16]  chunk c (16 values at
+ *                                                64kt + 16c) of row 16rb + r
+ *            scales fp16  [R/16][k/32][16]       block scale d of row 16rb + r
  *   Q2_K and IQ2_XXS are tiled by qmoe_split_q2_k / qmoe_split_iq2_xxs
  *   (rows = E*n a multiple of 16, k a multiple of 256).  Global row
  *   R = e*n + row, block rb = R/16, r = R%16, super-block sb (256 values
@@ -138,18 +141,20 @@ typedef struct qmoe_weights {
  * Host-side loader split ([GGUF] "Design -- CPU-side decomposition": each
  * on-disk block is decomposed once at load into separate GPU-resident
  * arrays; [DSV4] load-time q2_K SoA repack).  HOST pointers; the caller
- * uploads the outputs.  `aos` holds consecutive on-disk blocks (Q8_0:
- * n_blocks of them; Q2_K, IQ2_XXS: rows * k/256 of them, row after row):
+ * uploads the outputs.  `aos` holds the on-disk blocks of a rows x k
+ * matrix, row after row (rows * k/32 blocks for Q8_0, rows * k/256 for Q2_K
+ * and IQ2_XXS):
  *   Q8_0     34 B: fp16 d, 32 int8 codes
  *   Q2_K     84 B: 16 scale|min bytes, 64 code bytes, fp16 d, fp16 dmin
  *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
- * Q2_K and IQ2_XXS come out in the tiled form above (so that each wave-wide
- * metadata load of the matmul kernels reads contiguous bytes): qs holds
- * rows*k/16 bytes (Q2_K) or rows*k/16 u32 (IQ2_XXS), scales rows*k/16 bytes,
- * d and dmin rows*k/256 values.  Returns QMOE_ERR_ARG on NULL / negative
- * sizes, QMOE_ERR_BLOCK unless rows % 16 == 0 and k % 256 == 0.
+ * They come out in the tiled forms above (so that each wave-wide load of
+ * the matmul kernels reads contiguous bytes): Q8_0 qs rows*k bytes, scales
+ * rows*k/32; Q2_K qs rows*k/4 bytes, scales rows*k/16 bytes, d and dmin
+ * rows*k/256; IQ2_XXS qs rows*k/16 u32, d rows*k/256.  Returns QMOE_ERR_ARG
+ * on NULL / negative sizes, QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a
+ * multiple of 64 (Q8_0) or 256.
  * ------------------------------------------------------------------------ */
-int qmoe_split_q8_0(const void* aos, int64_t n_blocks, int8_t* qs, uint16_t* d);
+int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16_t* d);
 int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin);
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint16_t* d);
@@ -170,12 +175,11 @@ void qmoe_iq2_signs_table(uint8_t out[128]);
  * Standalone dequantisation ([GGUF] "Kernels" 1-3; [BAGEL] int4 slabs).
  * Decodes every value in fp32 exactly as the format defines it and rounds
  * once (to nearest even) to out_dtype; results are bit-exact.  DEVICE
- * pointers, 16-byte aligned; out holds n_blocks * 32 values (Q8_0) or the
- * rows x k matrix (the tiled formats), row-major.  Tiled formats return
- * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 256 (int4: 64
- * and group).
+ * pointers, 16-byte aligned; out holds the rows x k matrix, row-major.
+ * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0), 256
+ * (Q2_K, IQ2_XXS) or 64 and group (int4).
  * ------------------------------------------------------------------------ */
-int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t n_blocks,
+int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k,
                       void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t* d,
                       const uint16_t* dmin, int64_t rows, int64_t k,

@@ -30,12 +30,20 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(qm.EXPORTS)
 
 
-def test_split_q8_0_round_trip():
-    W = synth.q8_0(np.random.default_rng(0), 2, 3, 64)
-    qs, d = qm.split_q8_0(W.blocks)
-    blocks = W.blocks.reshape(-1, 34)
-    assert np.array_equal(d.view(np.uint8).reshape(-1, 2), blocks[:, :2])
-    assert np.array_equal(qs.view(np.uint8).reshape(-1, 32), blocks[:, 2:])
+def test_split_q8_0_tiled_layout():
+    """Every code and scale lands where the header's tiled layout says."""
+    rows, k = 32, 192
+    W = synth.q8_0(np.random.default_rng(0), 2, rows // 2, k)
+    qs, d = qm.split_q8_0(W.blocks, rows, k)
+    b = W.blocks.reshape(rows, k // 32, 34)
+    q = qs.view(np.uint8).reshape(rows // 16, k // 64, 4, 16, 16)
+    d = d.view(np.uint8).reshape(rows // 16, k // 32, 16, 2)
+    for R in range(rows):
+        for j in range(k // 32):
+            assert np.array_equal(d[R // 16, j, R % 16], b[R, j, :2])
+            for h in range(2):
+                kk = 32 * j + 16 * h
+                assert np.array_equal(q[R // 16, kk // 64, (kk % 64) // 16, R % 16], b[R, j, 2 + 16 * h:18 + 16 * h])
 
 
 def test_split_q2_k_tiled_layout():
@@ -139,9 +147,10 @@ def test_argument_validation_before_launch():
     # misaligned plan
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(20), 1 << 20, None) == -6
     # dequant: NULL / misaligned / bad dtype
-    assert L.qmoe_dequant_q8_0(None, ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == E
-    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(8), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 1, None) == -6
-    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.c_void_p(16), 7, None) == E
+    assert L.qmoe_dequant_q8_0(None, ctypes.c_void_p(16), 16, 64, ctypes.c_void_p(16), 1, None) == E
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(8), ctypes.c_void_p(16), 16, 64, ctypes.c_void_p(16), 1, None) == -6
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 64, ctypes.c_void_p(16), 7, None) == E
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 96, ctypes.c_void_p(16), 1, None) == -3
     assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 96, 32,
                                ctypes.c_void_p(16), 1, None) == -3
     assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 128, 64,
@@ -168,7 +177,7 @@ def test_argument_validation_before_launch():
     assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 4, ctypes.c_void_p(16), None, 8, 2,
                            ctypes.c_void_p(16), 2, None) == E
     # empty inputs return OK without touching the device
-    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, ctypes.c_void_p(16), 1, None) == 0
+    assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 64, ctypes.c_void_p(16), 1, None) == 0
     assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 0, ctypes.c_void_p(16), None, 8, 1,
                            ctypes.c_void_p(16), 2, None) == 0
     assert qm.lib().qmoe_strerror(-4).decode().startswith("size limit")

@@ -41,7 +41,7 @@ def _weights(fmt, rng):
     elif fmt == "int4":
         W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
     else:
-        W = synth.q8_0(rng, 2, 37, 512)
+        W = synth.q8_0(rng, 2, 40, 512)
     return W
 
 
