@@ -2,8 +2,8 @@
 
 Step (the timed unit): one pass of the whole prefill MoE hot path over the
 Qwen3.6-A3B-shaped int4 workload -- routing plan, gathered gate/up GEMM with
-the SwiGLU epilogue, gathered down GEMM with the top-k weighted scatter-add,
-and the final cast -- for T = 2048 tokens, hidden 2048, 256 experts, top-8,
+the SwiGLU epilogue, gathered down GEMM into per-pair rows, and the
+deterministic top-k weighted combine -- for T = 2048 tokens, hidden 2048, 256 experts, top-8,
 expert intermediate 512, bf16 activations, int4 affine weights (group 64).
 The weights rotate over R copies so no step finds them in the 256 MB
 Infinity Cache.  `value` is algorithmic TFLOP/s of that step (routed pairs
@@ -90,11 +90,10 @@ def run_prefill(args, torch, qm):
     bm = 80
     plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    acc = torch.zeros((T, inp.H), dtype=torch.float32, device=dev)
+    y = torch.empty((T * k, inp.H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, inp.H), dtype=torch.bfloat16, device=dev)
-    n_valid = T * k
 
-    ev = {name: [] for name in ("plan", "gate_up", "down", "cast")}
+    ev = {name: [] for name in ("plan", "gate_up", "down", "combine")}
 
     def step(i, timed):
         gu, dn = gus[i % R], dns[i % R]
@@ -107,11 +106,10 @@ def run_prefill(args, torch, qm):
         qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
         if timed:
             marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.moe_gather_qmm(dn, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, topk_w=w,
-                          epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+        qm.moe_gather_qmm(dn, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE, out=y)
         if timed:
             marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.combine_cast(acc, qm.BF16, out=out)
+        qm.moe_combine(y, plan, T, k, E, w, out=out)
         if timed:
             marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
         return marks
@@ -129,7 +127,7 @@ def run_prefill(args, torch, qm):
     all_marks = [step(i, True) for i in range(args.steps)]
     torch.cuda.synchronize()
     for m in all_marks:
-        for j, name in enumerate(("plan", "gate_up", "down", "cast")):
+        for j, name in enumerate(("plan", "gate_up", "down", "combine")):
             ev[name].append(m[j].elapsed_time(m[j + 1]) * 1e-3)
     kern = {n: float(np.median(v)) for n, v in ev.items()}
     return inp, alg, wall, kern
@@ -154,13 +152,15 @@ def run_prefill_other(args, torch, qm, inp, R, steps):
     bm = 80
     plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
     h = torch.empty((T * k, I), dtype=tdt[inp.act], device=dev)
-    acc = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    y = torch.empty((T * k, H), dtype=tdt[inp.act], device=dev)
     out = torch.empty((T, H), dtype=tdt[inp.out], device=dev)
     shared = inp.shared_gate_up is not None
+    base = None
     if shared:
         sgu, sdn = upload(qm, inp.shared_gate_up), upload(qm, inp.shared_down)
         hs = torch.empty((T, inp.shared_down.K), dtype=tdt[inp.act], device=dev)
-    names = ["plan", "gate_up", "down"] + (["shared"] if shared else []) + ["cast"]
+        base = torch.empty((T, H), dtype=torch.float32, device=dev)
+    names = ["plan", "gate_up", "down"] + (["shared"] if shared else []) + ["combine"]
 
     def step(i, timed):
         marks = []
@@ -175,14 +175,13 @@ def run_prefill_other(args, torch, qm, inp, R, steps):
         mark()
         qm.moe_gather_qmm(gus[i % R], plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
         mark()
-        qm.moe_gather_qmm(dns[i % R], plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, topk_w=w,
-                          epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+        qm.moe_gather_qmm(dns[i % R], plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE, out=y)
         mark()
         if shared:
             qm.qmm_dense(sgu, x, qm.EPI_SWIGLU, codes[inp.act], out=hs)
-            qm.qmm_dense(sdn, hs, qm.EPI_ACCUMULATE, qm.F32, out=acc)
+            qm.qmm_dense(sdn, hs, qm.EPI_STORE, qm.F32, out=base)
             mark()
-        qm.combine_cast(acc, codes[inp.out], out=out)
+        qm.moe_combine(y, plan, T, k, E, w, base=base, out=out)
         mark()
         return marks
 

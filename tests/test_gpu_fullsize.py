@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark uses (routing plan with bm = 80, gathered gate/up with SwiGLU,
-gathered down with the top-k weighted scatter-add, cast), checked on sampled
-outputs that the fp64 oracle computes one by one:
+gathered down into per-pair rows, the deterministic top-k combine), checked
+on sampled outputs that the fp64 oracle computes one by one:
 
   * Qwen3.6-A3B-shaped int4 prefill: T = 2048, H = 2048, E = 256, I = 512, k = 8
   * DSv4-flash-shaped prefill: T = 2048, H = 4096, E = 256, I = 2048, k = 6,
@@ -28,8 +28,10 @@ torch = pytest.importorskip("torch")
 BM = 80  # the benchmark's tile height
 
 
-def _run_moe(inp):
-    """The benchmark's prefill sequence; returns device tensors and the plan."""
+def _run_moe(inp, base=None):
+    """The benchmark's prefill sequence: plan, gate/up with SwiGLU, down into
+    per-pair rows (sorted order, activation dtype), the deterministic top-k
+    combine (plus an fp32 base) rounded to the output dtype."""
     T, k, E = inp.T, inp.k, inp.E
     act = CODES[inp.act]
     x = torch_act(inp.x, inp.act)
@@ -38,11 +40,10 @@ def _run_moe(inp):
     gu, dn = upload(inp.w_gate_up), upload(inp.w_down)
     plan = qm.moe_plan(ids, E, BM)
     h = qm.moe_gather_qmm(gu, plan, T, k, x, bm=BM, epilogue=qm.EPI_SWIGLU, out_dtype=act)
-    acc = torch.zeros((T, inp.H), dtype=torch.float32, device="cuda")
-    qm.moe_gather_qmm(dn, plan, T, k, h, bm=BM, a_mode=qm.A_SORTED_ROWS, topk_w=w,
-                      epilogue=qm.EPI_WEIGHTED_COMBINE, out=acc)
+    y = qm.moe_gather_qmm(dn, plan, T, k, h, bm=BM, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE, out_dtype=act)
+    out = qm.moe_combine(y, plan, T, k, E, w, base=base, out_dtype=CODES[inp.out])
     del gu, dn
-    return x, plan, h, acc
+    return x, plan, h, out
 
 
 def _check_gate_up(inp, plan, h, rng, n_pairs=48, n_cols=64):
@@ -68,8 +69,7 @@ def _h_rows(inp, plan, h, tokens):
 def test_fullsize_qwen_a3b_int4_prefill():
     inp = synth.qwen_a3b_prefill(2048)
     rng = np.random.default_rng(101)
-    x, plan, h, acc = _run_moe(inp)
-    out = qm.combine_cast(acc, CODES[inp.out])
+    x, plan, h, out = _run_moe(inp)
     torch.cuda.synchronize()
     _check_gate_up(inp, plan, h, rng)
     tokens = rng.choice(inp.T, 24, replace=False)
@@ -83,8 +83,7 @@ def test_fullsize_qwen_a3b_int4_prefill():
 def test_fullsize_dsv4_flash_prefill():
     inp = synth.dsv4_flash_prefill(2048)
     rng = np.random.default_rng(102)
-    x, plan, h, acc = _run_moe(inp)
-    out = qm.combine_cast(acc, CODES[inp.out])
+    x, plan, h, out = _run_moe(inp)
     torch.cuda.synchronize()
     _check_gate_up(inp, plan, h, rng)
     tokens = rng.choice(inp.T, 16, replace=False)
@@ -98,13 +97,13 @@ def test_fullsize_dsv4_flash_prefill():
 def test_fullsize_mixed_ffn_block():
     inp = synth.mixed_ffn(8192)
     rng = np.random.default_rng(103)
-    x, plan, h, acc = _run_moe(inp)
     act = CODES[inp.act]
-    # shared expert: silu(g) * u, then added into the fp32 combine buffer
+    # shared expert: silu(g) * u, its down projection in fp32 is the combine's base
     sgu, sdn = upload(inp.shared_gate_up), upload(inp.shared_down)
-    hs = qm.qmm_dense(sgu, x, qm.EPI_SWIGLU, act)
-    qm.qmm_dense(sdn, hs, qm.EPI_ACCUMULATE, qm.F32, out=acc)
-    out = qm.combine_cast(acc, CODES[inp.out])
+    x0 = torch_act(inp.x, inp.act)
+    hs = qm.qmm_dense(sgu, x0, qm.EPI_SWIGLU, act)
+    base = qm.qmm_dense(sdn, hs, qm.EPI_STORE, qm.F32)
+    x, plan, h, out = _run_moe(inp, base=base)
     proj = [qm.qmm_dense(upload(Wp), x, qm.EPI_STORE, act) for Wp in inp.projections]
     torch.cuda.synchronize()
     _check_gate_up(inp, plan, h, rng)
