@@ -5,12 +5,12 @@
 // router ids on the device.  Pairs keep ascending pair order inside an expert,
 // so the plan is unique and identical from run to run.
 //
-// Three short launches over chunks of 1024 pairs (one 1024-thread workgroup
+// Two short launches over chunks of 1024 pairs (one 1024-thread workgroup
 // per chunk, one pair per thread):
 //   1. chunk histograms: per-expert counts of each chunk;
-//   2. one workgroup turns them into per-chunk bases, expert counts,
-//      offsets, the tile list and the header;
-//   3. each chunk recomputes its in-chunk ranks and scatters its pairs.
+//   2. each chunk sums the histograms into expert counts, its own bases and
+//      the offsets (chunk 0 also writes the counts, offsets, tile list and
+//      header), recomputes its in-chunk ranks and scatters its pairs.
 // A wave finds the lanes that share its expert with one ballot per bit of the
 // expert id, so ranks are exact without sorting; waves are combined through
 // per-wave counts in LDS in wave order.  Chunk histograms live in the plan
@@ -80,30 +80,37 @@ __global__ __launch_bounds__(1024) void plan_hist_kernel(PlanArgs a) {
   }
 }
 
-// One workgroup of 1024 threads (thread = expert).
-__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
+// Scan and scatter in one launch, one workgroup per chunk (thread = expert
+// for the scan).  Every workgroup reads all chunk histograms: an expert's
+// count is their sum, and this chunk's base within the expert is the sum
+// over the chunks before it.  Offsets and tile counts come from a prefix sum
+// over the experts in LDS; workgroup 0 also writes the counts, offsets, tile
+// list and header.  Then each pair is placed at offset + chunk base + the
+// ranks of earlier waves + its rank in its wave.
+__global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
+  extern __shared__ int wcnt[];  // [16][E], then base[E]
   __shared__ int sa[QMOE_MAX_EXPERTS], st[QMOE_MAX_EXPERTS], sp[QMOE_MAX_EXPERTS];
-  const int tid = threadIdx.x;
+  int* base = wcnt + 16 * a.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const PlanLayout L = plan_layout(a.P, a.E);
-  int32_t* hist = a.plan + hist_off(L);
-  int c_e = 0;
+  const int32_t* hist = a.plan + hist_off(L);
+  const int chunk = blockIdx.x;
+
+  int c_e = 0, cb = 0;
   if (tid < a.E) {
-    // running base per chunk (in place: hist[c][e] becomes the chunk's base)
-    int run = 0;
     for (int c = 0; c < a.nchunks; ++c) {
-      const int v = hist[(int64_t)c * a.E + tid];
-      hist[(int64_t)c * a.E + tid] = run;
-      run += v;
+      if (c == chunk) cb = c_e;
+      c_e += hist[(int64_t)c * a.E + tid];
     }
-    c_e = run;
   }
   // Tile order: every expert's full tiles (bm rows) first, in expert order,
-  // then the experts' last partial tiles.  Workgroups take tiles in this
-  // order, so a launch ends on its smallest tiles.
+  // then the experts' last partial tiles.  Workgroups of the matmul take
+  // tiles in this order, so a launch ends on its smallest tiles.
   const int nfull = c_e / a.bm, part = (c_e % a.bm) != 0;
   sa[tid] = c_e;
   st[tid] = nfull;
   sp[tid] = part;
+  for (int i = tid; i < 16 * a.E; i += 1024) wcnt[i] = 0;
   __syncthreads();
   for (int off = 1; off < QMOE_MAX_EXPERTS; off <<= 1) {
     const int va = tid >= off ? sa[tid - off] : 0;
@@ -117,19 +124,22 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
   }
   if (tid < a.E) {
     const int row0 = sa[tid] - c_e;
-    a.plan[L.counts + tid] = c_e;
-    a.plan[L.offsets + tid] = row0;
-    auto put = [&](int t, int i, int n) {
-      int32_t* tl = a.plan + L.tiles + 4 * (int64_t)t;
-      tl[0] = tid;
-      tl[1] = row0 + i * a.bm;
-      tl[2] = n;
-      tl[3] = 0;
-    };
-    for (int i = 0; i < nfull; ++i) put(st[tid] - nfull + i, i, a.bm);
-    if (part) put(st[QMOE_MAX_EXPERTS - 1] + sp[tid] - 1, nfull, c_e - nfull * a.bm);
+    base[tid] = row0 + cb;
+    if (chunk == 0) {
+      a.plan[L.counts + tid] = c_e;
+      a.plan[L.offsets + tid] = row0;
+      auto put = [&](int t, int i, int n) {
+        int32_t* tl = a.plan + L.tiles + 4 * (int64_t)t;
+        tl[0] = tid;
+        tl[1] = row0 + i * a.bm;
+        tl[2] = n;
+        tl[3] = 0;
+      };
+      for (int i = 0; i < nfull; ++i) put(st[tid] - nfull + i, i, a.bm);
+      if (part) put(st[QMOE_MAX_EXPERTS - 1] + sp[tid] - 1, nfull, c_e - nfull * a.bm);
+    }
   }
-  if (tid == 0) {
+  if (chunk == 0 && tid == 0) {
     const int total = sa[QMOE_MAX_EXPERTS - 1];
     a.plan[0] = (int32_t)(a.P - total);
     a.plan[1] = st[QMOE_MAX_EXPERTS - 1] + sp[QMOE_MAX_EXPERTS - 1];
@@ -141,27 +151,20 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a) {
     a.plan[7] = 0;
     a.plan[L.offsets + a.E] = total;
   }
-}
+  __syncthreads();  // base[] and the cleared counts
 
-__global__ __launch_bounds__(1024) void plan_scatter_kernel(PlanArgs a) {
-  extern __shared__ int wcnt[];  // [16][E]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < 16 * a.E; i += 1024) wcnt[i] = 0;
-  __syncthreads();
   int e;
-  const int64_t p = (int64_t)blockIdx.x * PC + tid;
+  const int64_t p = (int64_t)chunk * PC + tid;
   const int rank = wave_rank(a, p, lane, wcnt + wave * a.E, e);
   __syncthreads();
   if (p >= a.P) return;
-  const PlanLayout L = plan_layout(a.P, a.E);
   if (e < 0) {
     a.plan[L.inv + p] = -1;
     return;
   }
   int wb = 0;
   for (int w = 0; w < wave; ++w) wb += wcnt[w * a.E + e];
-  const int32_t* cbase = a.plan + hist_off(L) + (int64_t)blockIdx.x * a.E;
-  const int pos = a.plan[L.offsets + e] + cbase[e] + wb + rank;
+  const int pos = base[e] + wb + rank;
   a.plan[L.sorted + pos] = (int32_t)p;
   a.plan[L.inv + p] = pos;
 }
@@ -183,8 +186,7 @@ void launch_plan(const int32_t* ids, int64_t t, int topk, int E, int bm, int32_t
   while ((1 << a.nbits) < E) ++a.nbits;
   const size_t lds = 16 * (size_t)E * sizeof(int);
   hipLaunchKernelGGL(plan_hist_kernel, dim3(a.nchunks), dim3(1024), lds, s, a);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(plan_scatter_kernel, dim3(a.nchunks), dim3(1024), lds, s, a);
+  hipLaunchKernelGGL(plan_scan_scatter_kernel, dim3(a.nchunks), dim3(1024), lds + E * sizeof(int), s, a);
 }
 
 }  // namespace qmoe
