@@ -738,7 +738,11 @@ constexpr int R_SB = RW * 256;             // 2048 B (one 64-lane dword load per
 constexpr int R_STAGE = R_A + R_B + R_SB;  // 20480 B
 constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
 
-__device__ __forceinline__ int ring_swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Chunk swizzle of the activation rows in a ring stage (rows 128 bytes
+// apart share banks every 8 rows).  It depends on r % 16 only, so the rows
+// of MFMA sub-tile m sit at a constant offset (2048 m bytes) from those of
+// sub-tile 0 and the reads use immediate offsets.
+__device__ __forceinline__ int ring_swz(int r) { return ((r & 15) ^ ((r >> 3) & 1)) & 7; }
 __device__ __forceinline__ int ring_slot(int r, int c) { return r * 8 + (c ^ ring_swz(r)); }
 
 
@@ -878,6 +882,9 @@ void qmm_int4_kernel(GemmArgs g) {
 #pragma unroll
       for (int b = 0; b < RNB; ++b) acc[m][b] = f4_t{0, 0, 0, 0};
 
+    // chunk slots of this lane's activation reads in MFMA sub-tile 0 (sub-tile
+    // m adds 128 m: the swizzle depends on the row mod 16 only)
+    const int slot_a0 = ring_slot(lr, 2 * lg), slot_a1 = ring_slot(lr, 2 * lg + 1);
     auto compute = [&](int kt, int stage) {
       const uint8_t* st = ring + stage * R_STAGE;
       const uint16_t* As = (const uint16_t*)st;
@@ -902,9 +909,8 @@ void qmm_int4_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
-          const int r = 16 * m + lr;
-          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
-          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
 #pragma unroll
           for (int b = 0; b < RNB; ++b) {
             acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
@@ -931,9 +937,8 @@ void qmm_int4_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
-          const int r = 16 * m + lr;
-          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
-          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
 #pragma unroll
           for (int b = 0; b < RNB; ++b) {
             f4_t t = mfma(a0, __builtin_bit_cast(b8_t, c0[b]), f4_t{0, 0, 0, 0});
@@ -944,9 +949,8 @@ void qmm_int4_kernel(GemmArgs g) {
         }
         // row sums of the tile's activations (bias term): wave w < MBV takes block w
         if (wave < MBV) {
-          const int r = 16 * wave + lr;
-          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg)));
-          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * ring_slot(r, 2 * lg + 1)));
+          const b8_t a0 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * wave)));
+          const b8_t a1 = __builtin_bit_cast(b8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * wave)));
           f4_t xs = mfma(a0, ones, f4_t{0, 0, 0, 0});
           xs = mfma(a1, ones, xs);
           if (lr == 0) {  // lane (lg, 0) holds the sums of rows 16w + 4lg .. +3
