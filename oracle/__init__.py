@@ -34,6 +34,9 @@ Readings where the pages are silent (each repeated at the function):
   * Sign table: entry i is i with bit 7 set iff i has an odd number of set
     bits (the "even-parity 8th sign").
   * int4: nibble i of word w is element 8*w + i (low nibble first).
+  * Routers: equal scores select the lower expert index first; the DSv4
+    sqrtsoftplus gather weight is the unbiased score times the routed scaling
+    factor, with no renormalisation (none is stated).
 Parity pins for every function live in tests/test_oracle_*.py.
 """
 from __future__ import annotations
@@ -45,6 +48,7 @@ __all__ = [
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
+    "router_topk_softmax", "router_sqrtsoftplus",
 ]
 
 # ---------------------------------------------------------------------------
@@ -340,3 +344,49 @@ def moe_down_rows(h64_pairs: dict, ids, w, Wd, tokens, cols) -> np.ndarray:
             W = dequant_rows(Wd, e, cols).astype(np.float64)
             out[i] += np.float64(w[t, j]) * (W @ h64_pairs[t * k + j])
     return out
+
+
+# ---------------------------------------------------------------------------
+# routers (the step before the path: logits -> expert ids and top-k weights)
+# ---------------------------------------------------------------------------
+
+def router_topk_softmax(logits: np.ndarray, k: int):
+    """Softmax top-k router [BAGEL, the commit moving the MoE router top-K to
+    the GPU: per row the k largest logits, weights from a softmax over the
+    selected logits, summing to 1; it replaces a CPU top-K + softmax].
+
+    Selection compares the logits themselves (no arithmetic), equal logits
+    going to the lower expert index.  Weights in fp64.
+    Returns ids int32 [T, k] (best first), w float64 [T, k]."""
+    L = np.asarray(logits, dtype=np.float64)
+    order = np.argsort(-L, axis=1, kind="stable")[:, :k]   # stable: ties keep index order
+    sel = np.take_along_axis(L, order, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return order.astype(np.int32), z / z.sum(axis=1, keepdims=True)
+
+
+def _softplus_f32(x: np.ndarray) -> np.ndarray:
+    """softplus(x) = max(x, 0) + log(1 + exp(-|x|)) evaluated in fp32 [GGUF,
+    the DeepSeek V4 routing scoring commit: the stable form, since
+    log(1 + exp(x)) overflows for large x]."""
+    x = np.asarray(x, dtype=np.float32)
+    return (np.maximum(x, np.float32(0)) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def router_sqrtsoftplus(logits: np.ndarray, bias: np.ndarray, k: int, scale: float):
+    """DSv4 router [GGUF, the DeepSeek V4 routing scoring commit]:
+    unbiased score s_e = sqrt(softplus(l_e)); the k largest biased scores
+    s_e + bias_e are selected (aux-loss-free load balancing); the gather
+    weight of a selected expert is s_e * routed_scaling_factor.
+
+    The selection is an argmax decided in the kernel's precision: s and
+    s + bias are formed in fp32 from fp32 logits (equal biased scores go to
+    the lower expert index).  Weights use the fp64 score.
+    Returns ids int32 [T, k], w float64 [T, k], biased fp32 scores [T, E]."""
+    L32 = np.asarray(logits, dtype=np.float32)
+    s32 = np.sqrt(_softplus_f32(L32)).astype(np.float32)
+    biased = (s32 + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    order = np.argsort(-biased.astype(np.float64), axis=1, kind="stable")[:, :k]
+    L64 = np.take_along_axis(L32.astype(np.float64), order, axis=1)
+    sp64 = np.maximum(L64, 0.0) + np.log1p(np.exp(-np.abs(L64)))
+    return order.astype(np.int32), np.sqrt(sp64) * float(scale), biased
