@@ -230,6 +230,55 @@ def run_prefill_other(args, torch, qm, inp, R, steps):
     return res
 
 
+def run_router(args, torch, qm):
+    """Device router top-k ahead of the plan: per-launch time from a replayed
+    graph of launches (events on the replay stream), and the HBM rate of its
+    algorithmic bytes (logits and bias read, ids and weights written)."""
+    import synth
+    rows = []
+    for name, T, E, k, dt, scoring in (("qwen3.6-a3b-shaped softmax top-8", 2048, 256, 8, "bf16", qm.ROUTER_SOFTMAX),
+                                       ("qwen3.6-a3b-shaped softmax top-8, decode batch", 8, 256, 8, "bf16",
+                                        qm.ROUTER_SOFTMAX),
+                                       ("dsv4-flash-shaped sqrtsoftplus top-6", 2048, 288, 6, "f32",
+                                        qm.ROUTER_SQRTSOFTPLUS)):
+        rng = np.random.default_rng(E)
+        x = synth.router_logits(rng, T, E, dt, 2.0)
+        L = torch.from_numpy(x).cuda() if dt == "f32" else act_tensor(torch, x)
+        bias = torch.from_numpy((0.1 * rng.standard_normal(E)).astype(np.float32)).cuda() \
+            if scoring == qm.ROUTER_SQRTSOFTPLUS else None
+        scale = 1.5 if bias is not None else 1.0
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        # launches captured in a graph and replayed, so host launch cost does
+        # not hide the kernel's own time
+        n = 100
+        for _ in range(3):
+            qm.router_topk(L, k, scoring, bias, scale, ids, w)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(n):
+                    qm.router_topk(L, k, scoring, bias, scale, ids, w)
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / (5 * n)
+        nbytes = L.numel() * L.element_size() + T * k * 8 + (E * 4 if bias is not None else 0)
+        rows.append({"workload": name, "tokens": T, "experts": E, "top_k": k, "logits": dt,
+                     "us_per_launch": t * 1e6, "GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / PEAK_HBM,
+                     "bytes_per_launch": nbytes})
+    return rows
+
+
 def run_decode(args, torch, qm, B, layers):
     import synth
     inp = synth.qwen_a3b_decode(B)
@@ -477,6 +526,9 @@ def main():
             log(f"prefill ({name}): building inputs")
             others.append(run_prefill_other(args, torch, qm, make(), R, max(3, args.steps // 4)))
             log(json.dumps(others[-1]))
+    log("router top-k")
+    router = run_router(args, torch, qm)
+    log(json.dumps(router))
     decode = []
     if not args.no_decode:
         for B in (1, 4, 8):
@@ -516,6 +568,7 @@ def main():
                     "unique_experts": d["unique_experts"], "bytes_per_layer": d["bytes_per_layer"]}
                    for d in decode],
         "other_prefill_workloads": others,
+        "router": router,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -21,6 +21,7 @@ F32, F16, BF16 = 0, 1, 2
 Q8_0, Q2_K, IQ2_XXS, INT4 = 0, 1, 2, 3
 EPI_STORE, EPI_SWIGLU, EPI_WEIGHTED_COMBINE, EPI_ACCUMULATE = 0, 1, 2, 3
 A_GATHER_TOKENS, A_SORTED_ROWS = 0, 1
+ROUTER_SOFTMAX, ROUTER_SQRTSOFTPLUS = 0, 1
 FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4}
 MAX_TOPK, MAX_EXPERTS, MAX_GEMV_BATCH = 8, 1024, 64
 
@@ -67,6 +68,9 @@ _SIGS = {
     "qmoe_combine_cast": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_moe_gemv": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_router_topk": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_void_p],
     "qmoe_check_device": [],
     "qmoe_strerror": [ctypes.c_int],
 }
@@ -305,6 +309,23 @@ def moe_plan(ids, E: int, bm: int = 80, plan=None):
         plan = torch.empty(nbytes // 4, dtype=torch.int32, device=ids.device)
     _check(lib().qmoe_moe_plan(_ptr(ids), T, k, E, bm, _ptr(plan), plan.numel() * 4, _stream()), "moe_plan")
     return plan
+
+
+def router_topk(logits, k: int, scoring: int = ROUTER_SOFTMAX, bias=None, scale: float = 1.0,
+                ids=None, weights=None):
+    """Router top-k on the device: logits [T, E] (f32 / f16 / bf16) ->
+    (ids int32 [T, k], weights f32 [T, k]), best first (include/qmoe.h)."""
+    import torch
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    if T == 0:
+        return ids, weights
+    _check(lib().qmoe_router_topk(_ptr(logits), _code(logits), T, E, k, scoring, _ptr(bias), scale,
+                                  _ptr(ids), _ptr(weights), _stream()), "router_topk")
+    return ids, weights
 
 
 def plan_views(plan, T: int, topk: int, E: int):

@@ -16,7 +16,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["dequant.hip", "plan.hip", "gemm.hip", "gemv.hip", "combine.hip", "api.hip"]
+HIP_SOURCES = ["dequant.hip", "plan.hip", "gemm.hip", "gemv.hip", "combine.hip", "router.hip", "api.hip"]
 HOST_SOURCES = ["split.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]

@@ -26,6 +26,8 @@ int qmm_max_rows();
 int launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
                  int, void*, int, hipStream_t);
 void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
+void launch_router_topk(const void*, int, int64_t, int, int, int, const float*, float, int32_t*,
+                        float*, hipStream_t);
 void launch_moe_combine(const void*, int, const int32_t*, int64_t, int, int, const float*, int64_t,
                         const float*, void*, int, hipStream_t);
 }  // namespace qmoe
@@ -279,6 +281,27 @@ int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype,
   if (n_elems == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
   launch_combine_cast(acc, n_elems, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+// ------------------------------------------------------------------ router top-k
+
+int qmoe_router_topk(const void* logits, int32_t logits_dtype, int64_t t, int32_t n_experts,
+                     int32_t topk, int32_t scoring, const float* bias, float scale,
+                     int32_t* ids, float* weights, void* stream) {
+  if (!logits || !ids || !weights || t < 0 || topk < 1 || n_experts < 1 || !dtype_ok(logits_dtype))
+    return QMOE_ERR_ARG;
+  if (scoring != QMOE_ROUTER_SOFTMAX && scoring != QMOE_ROUTER_SQRTSOFTPLUS) return QMOE_ERR_ARG;
+  if (scoring == QMOE_ROUTER_SOFTMAX && (bias || scale != 1.0f)) return QMOE_ERR_ARG;
+  if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS || t > (1ll << 31)) return QMOE_ERR_LIMIT;
+  if (topk > n_experts) return QMOE_ERR_ARG;
+  const uintptr_t esz = logits_dtype == QMOE_F32 ? 4 : 2;
+  if ((uintptr_t)logits % esz || !al4(ids) || !al4(weights) || (bias && !al4(bias)))
+    return QMOE_ERR_ALIGN;
+  if (t == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_router_topk(logits, logits_dtype, t, n_experts, topk, scoring, bias, scale, ids, weights,
+                     (hipStream_t)stream);
   return launched();
 }
 

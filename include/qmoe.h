@@ -71,6 +71,13 @@ enum {
   QMOE_EPI_ACCUMULATE = 3        /* out[row, n] += y  (fp32 out only, dense only)    */
 };
 
+/* Router scorings of qmoe_router_topk. */
+enum {
+  QMOE_ROUTER_SOFTMAX = 0,      /* top-k logits, softmax over the selected        [BAGEL] */
+  QMOE_ROUTER_SQRTSOFTPLUS = 1  /* top-k of sqrt(softplus(l)) + bias, weight
+                                   sqrt(softplus(l)) * scale (DeepSeek V4)        [GGUF]  */
+};
+
 /* Where the activation rows of a gathered MoE matmul come from. */
 enum {
   QMOE_A_GATHER_TOKENS = 0,  /* row for pair p is a[p / topk, :]   (a is [t, K])     */
@@ -280,6 +287,32 @@ int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype,
 int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64_t b,
                   const int32_t* ids, const float* topk_w, int32_t topk, int32_t epilogue,
                   void* out, int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Router top-k: expert ids and gather weights from router logits, on the
+ * device, so the ids feed qmoe_moe_plan / qmoe_moe_gemv with no host
+ * round trip ([BAGEL] the commit moving the MoE router top-K to the GPU;
+ * [GGUF] the DeepSeek V4 sqrtsoftplus routing scoring commit).
+ *   logits DEVICE [t, n_experts] row-major, logits_dtype F32 / F16 / BF16
+ *          (aligned to its element size).
+ *   SOFTMAX        selects the topk largest logits; weights[t, j] =
+ *                  exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected
+ *                  (they sum to 1).  bias must be NULL and scale 1.
+ *   SQRTSOFTPLUS   s_e = sqrt(max(l, 0) + log1p(exp(-|l|))) in fp32; selects
+ *                  the topk largest s_e + bias[e] (bias DEVICE f32
+ *                  [n_experts], or NULL for zero); weights = s_e * scale
+ *                  (no renormalisation).
+ *   ids DEVICE int32 [t, topk], weights DEVICE f32 [t, topk], written in
+ *   selection order (best first).  Equal selection scores go to the lower
+ *   expert index; NaN scores rank below every number, -0 equals +0.
+ * Errors: QMOE_ERR_ARG (NULL pointer, t < 0, topk < 1 or > n_experts, bad
+ * dtype / scoring, SOFTMAX with a bias or scale != 1), QMOE_ERR_LIMIT
+ * (topk > QMOE_MAX_TOPK, n_experts > QMOE_MAX_EXPERTS, t > 2^31),
+ * QMOE_ERR_ALIGN; nothing is launched on error.  t == 0 launches nothing.
+ * ------------------------------------------------------------------------ */
+int qmoe_router_topk(const void* logits, int32_t logits_dtype, int64_t t, int32_t n_experts,
+                     int32_t topk, int32_t scoring, const float* bias, float scale,
+                     int32_t* ids, float* weights, void* stream);
 
 /* QMOE_OK if the current HIP device is gfx950, else QMOE_ERR_ARCH. */
 int qmoe_check_device(void);

@@ -187,32 +187,42 @@ def activations(rng: np.random.Generator, T: int, K: int, dtype: str) -> np.ndar
     return f16_bits(x) if dtype == "f16" else bf16_bits(x)
 
 
-def topk_from_logits(logits: np.ndarray, k: int):
-    """Top-k experts per row (ties to the lower expert index) and their weights,
-    a softmax over the selected logits (so each row's weights sum to 1)."""
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
-    sel = np.take_along_axis(logits, order, axis=1).astype(np.float64)
-    z = np.exp(sel - sel.max(axis=1, keepdims=True))
-    w = z / z.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), w.astype(np.float32)
+def _pairs_from_keys(rng: np.random.Generator, keys: np.ndarray, k: int):
+    """k distinct experts per row, the k largest of the random keys (a sampling
+    step: continuous keys, so no ties in practice), and random positive pair
+    weights, decreasing along the row and summing to 1.  A stand-in for a
+    router's output, not a router."""
+    ids = np.argsort(-keys, axis=1, kind="stable")[:, :k]
+    u = -np.sort(-rng.uniform(0.05, 1.0, size=ids.shape), axis=1)
+    w = u / u.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w.astype(np.float32)
 
 
 def routing_softmax(rng: np.random.Generator, T: int, E: int, k: int):
-    """Router of the Qwen-shaped workloads: top-k of softmax(N(0,1) logits)."""
-    logits = rng.standard_normal((T, E), dtype=np.float32)
-    return topk_from_logits(logits, k)
+    """Uniform routing of the Qwen-shaped workloads: k distinct experts drawn
+    uniformly per token (N(0,1) keys)."""
+    return _pairs_from_keys(rng, rng.standard_normal((T, E), dtype=np.float32), k)
 
 
 def routing_zipf(rng: np.random.Generator, T: int, E: int, k: int, alpha: float = 1.1):
-    """Skewed router: expert popularity p ~ rank^-alpha over a seeded permutation;
-    per-token logits log p + Gumbel(0,1), so top-k samples experts without
-    replacement in proportion to p."""
+    """Skewed routing: expert popularity p ~ rank^-alpha over a seeded
+    permutation; keys log p + Gumbel(0,1), so the top k of a row samples
+    experts without replacement in proportion to p."""
     perm = rng.permutation(E)
     p = np.empty(E)
     p[perm] = np.arange(1, E + 1, dtype=np.float64) ** (-alpha)
     p /= p.sum()
-    logits = (np.log(p)[None, :] + rng.gumbel(size=(T, E))).astype(np.float32)
-    return topk_from_logits(logits, k)
+    keys = (np.log(p)[None, :] + rng.gumbel(size=(T, E))).astype(np.float32)
+    return _pairs_from_keys(rng, keys, k)
+
+
+def router_logits(rng: np.random.Generator, T: int, E: int, dtype: str, sigma: float = 1.0) -> np.ndarray:
+    """Router logits N(0, sigma^2) [T, E]: float32, or uint16 bit patterns of
+    fp16 / bf16."""
+    x = (sigma * rng.standard_normal((T, E))).astype(np.float32)
+    if dtype == "f32":
+        return x
+    return f16_bits(x) if dtype == "f16" else bf16_bits(x)
 
 
 # ---------------------------------------------------------------------------

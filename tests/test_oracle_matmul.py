@@ -9,7 +9,6 @@ dense matmul.
 import math
 import struct
 
-import os
 
 import numpy as np
 import pytest
@@ -84,27 +83,6 @@ def test_plan_against_sorted_and_invariants():
         assert np.all(flat[seg] == e)
         rows.extend(range(r0, r0 + n))
     assert rows == list(range(len(keep)))
-
-
-def _golden(name):
-    path = os.path.join(os.path.dirname(__file__), "golden", name)
-    rows = {}
-    for line in open(path):
-        if line.strip() and not line.startswith("#"):
-            key, *vals = line.split()
-            rows[key] = vals
-    return rows
-
-
-def test_router_worked_example():
-    # tests/golden/router_topk.txt: the router top-K test case of the
-    # "Everything Bagel 2" page; the larger logit also gets the larger weight.
-    g = _golden("router_topk.txt")
-    logits = np.array([[float(v) for v in g["logits"]]], np.float32)
-    ids, w = synth.topk_from_logits(logits, int(g["k"][0]))
-    assert set(ids[0].tolist()) == {int(v) for v in g["experts"]}
-    assert abs(float(w.sum()) - float(g["weight_sum"][0])) < 1e-6
-    assert w[0][list(ids[0]).index(1)] > w[0][list(ids[0]).index(3)]
 
 
 def _tiny_moe(E=3, T=5, k=2, H=64, I=64, fmt="int4", act="bf16", seed=4):
