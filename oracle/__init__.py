@@ -48,7 +48,7 @@ __all__ = [
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
-    "router_topk_softmax", "router_sqrtsoftplus",
+    "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual",
 ]
 
 # ---------------------------------------------------------------------------
@@ -299,10 +299,13 @@ def moe_down_combine(h64: np.ndarray, ids: np.ndarray, w: np.ndarray, Wd) -> np.
     return out
 
 
-def moe_ffn(x64, ids, w, Wgu, Wd, h_dtype: str | None = None, shared=None):
+def moe_ffn(x64, ids, w, Wgu, Wd, h_dtype: str | None = None, shared=None, shared_gate=None,
+            residual=None):
     """Whole MoE FFN.  If h_dtype is given, h is rounded to that storage dtype
     between the two GEMMs (the storage point of the GPU path).  `shared` is an
-    optional (gate_up, down) pair of dense weights added with weight 1."""
+    optional (gate_up, down) pair of dense weights, added with weight 1 or,
+    with per-token gate logits `shared_gate`, with weight sigmoid(logit);
+    `residual` is added last (see gated_shared_residual)."""
     h = moe_gate_up(x64, ids, Wgu)
     if h_dtype is not None:
         h = out_to_f64(round_out(h, h_dtype), h_dtype)
@@ -314,7 +317,24 @@ def moe_ffn(x64, ids, w, Wgu, Wd, h_dtype: str | None = None, shared=None):
         hs = silu(gu[:, :I]) * gu[:, I:]
         if h_dtype is not None:
             hs = out_to_f64(round_out(hs, h_dtype), h_dtype)
-        out = out + qmm(hs, sd)
+        return gated_shared_residual(out, qmm(hs, sd), shared_gate, residual)
+    return gated_shared_residual(out, None, None, residual)
+
+
+def gated_shared_residual(moe_out, shared_out=None, gate_logits=None, residual=None):
+    """Post-MoE epilogue [BAGEL, the commit adding the scalar-FMA wrappers:
+    the sigmoid-gated FMA with the residual add folded in]:
+        out = residual + sigmoid(g_t) * shared + moe_out
+    per token t, every term optional (a missing gate means weight 1).  fp64."""
+    out = np.array(moe_out, dtype=np.float64)
+    if shared_out is not None:
+        g = 1.0
+        if gate_logits is not None:
+            with np.errstate(over="ignore"):  # exp(-g) = inf for g << 0 gives the exact limit 0
+                g = (1.0 / (1.0 + np.exp(-np.asarray(gate_logits, np.float64))))[:, None]
+        out = out + g * np.asarray(shared_out, np.float64)
+    if residual is not None:
+        out = out + np.asarray(residual, np.float64)
     return out
 
 

@@ -120,3 +120,20 @@ def test_sqrtsoftplus_bias_selects_but_does_not_weight():
     score = [math.sqrt(math.log1p(math.exp(L[0, e]))) + float(bias[e]) for e in range(6)]
     best = max(itertools.combinations(range(6), 2), key=lambda c: score[c[0]] + score[c[1]])
     assert sorted(ids[0].tolist()) == sorted(best)
+
+
+def test_gated_shared_residual_closed_forms():
+    # sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4; a missing
+    # gate is weight 1; a very negative logit switches the shared expert off.
+    moe = np.array([[1.0, -2.0], [0.5, 0.0], [3.0, 1.0], [0.0, 0.0]])
+    shared = np.array([[4.0, 8.0], [-4.0, 2.0], [1.0, 1.0], [10.0, -10.0]])
+    res = np.array([[0.25, 0.5], [1.0, 1.0], [-1.0, 2.0], [7.0, 7.0]])
+    g = np.array([0.0, math.log(3), -math.log(3), -800.0])
+    out = oracle.gated_shared_residual(moe, shared, g, res)
+    expect = np.array([[0.25 + 2.0 + 1.0, 0.5 + 4.0 - 2.0],
+                       [1.0 - 3.0 + 0.5, 1.0 + 1.5 + 0.0],
+                       [-1.0 + 0.25 + 3.0, 2.0 + 0.25 + 1.0],
+                       [7.0, 7.0]])
+    assert np.allclose(out, expect, rtol=0, atol=1e-12)
+    assert np.array_equal(oracle.gated_shared_residual(moe, shared), moe + shared)
+    assert np.array_equal(oracle.gated_shared_residual(moe, None, None, res), moe + res)
