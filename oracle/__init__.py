@@ -48,7 +48,7 @@ __all__ = [
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
-    "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual",
+    "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual", "combine_pairs",
 ]
 
 # ---------------------------------------------------------------------------
@@ -292,10 +292,19 @@ def moe_down_combine(h64: np.ndarray, ids: np.ndarray, w: np.ndarray, Wd) -> np.
     for e, pairs in _by_expert(ids, Wd.E):
         W = dequant_rows(Wd, e, np.arange(Wd.N)).astype(np.float64)
         y[pairs] = h64[pairs] @ W.T
-    y = y.reshape(T, k, Wd.N)
-    out = np.zeros((T, Wd.N))
+    return combine_pairs(y, ids, w, Wd.E)
+
+
+def combine_pairs(y_pairs: np.ndarray, ids: np.ndarray, w: np.ndarray, n_experts: int) -> np.ndarray:
+    """Top-k combine of per-pair expert outputs [BAGEL scalar-FMA top-K
+    accumulator]: out_t = sum_j w[t,j] * y[t*k + j] over the pairs whose
+    expert id is in [0, E); j ascending.  y fp64 [T*k, N] in pair order."""
+    T, k = ids.shape
+    y = np.asarray(y_pairs, np.float64).reshape(T, k, -1)
+    ok = (ids >= 0) & (ids < n_experts)
+    out = np.zeros((T, y.shape[2]))
     for j in range(k):
-        out += np.asarray(w, np.float64)[:, j, None] * y[:, j]
+        out += np.where(ok[:, j, None], np.asarray(w, np.float64)[:, j, None] * y[:, j], 0.0)
     return out
 
 

@@ -137,3 +137,16 @@ def test_gated_shared_residual_closed_forms():
     assert np.allclose(out, expect, rtol=0, atol=1e-12)
     assert np.array_equal(oracle.gated_shared_residual(moe, shared), moe + shared)
     assert np.array_equal(oracle.gated_shared_residual(moe, None, None, res), moe + res)
+
+
+def test_combine_pairs_closed_forms():
+    # two tokens, k = 2: token 0 mixes rows 0 and 1; token 1's second pair is
+    # dropped (expert id out of range), so only row 2 counts, weighted.
+    y = np.array([[1.0, 2.0], [10.0, 20.0], [3.0, -3.0], [1e9, 1e9]])
+    ids = np.array([[0, 1], [1, 4]])
+    w = np.array([[0.25, 0.75], [0.5, 0.5]])
+    out = oracle.combine_pairs(y, ids, w, 4)
+    assert np.array_equal(out, np.array([[7.75, 15.5], [1.5, -1.5]]))
+    # k = 1 with unit weights is the identity on the rows
+    y1 = np.arange(12.0).reshape(3, 4)
+    assert np.array_equal(oracle.combine_pairs(y1, np.zeros((3, 1), int), np.ones((3, 1)), 1), y1)
