@@ -36,7 +36,8 @@ Readings where the pages are silent (each repeated at the function):
   * int4: nibble i of word w is element 8*w + i (low nibble first).
   * Routers: equal scores select the lower expert index first; the DSv4
     sqrtsoftplus gather weight is the unbiased score times the routed scaling
-    factor, with no renormalisation (none is stated).
+    factor, with no renormalisation (none is stated); the softmax-then-bias
+    router selects on p + bias and weights the selected p renormalised.
 Parity pins for every function live in tests/test_oracle_*.py.
 """
 from __future__ import annotations
@@ -379,19 +380,36 @@ def moe_down_rows(h64_pairs: dict, ids, w, Wd, tokens, cols) -> np.ndarray:
 # routers (the step before the path: logits -> expert ids and top-k weights)
 # ---------------------------------------------------------------------------
 
-def router_topk_softmax(logits: np.ndarray, k: int):
+def router_topk_softmax(logits: np.ndarray, k: int, bias: np.ndarray | None = None):
     """Softmax top-k router [BAGEL, the commit moving the MoE router top-K to
     the GPU: per row the k largest logits, weights from a softmax over the
     selected logits, summing to 1; it replaces a CPU top-K + softmax].
 
-    Selection compares the logits themselves (no arithmetic), equal logits
-    going to the lower expert index.  Weights in fp64.
+    Without a bias the selection compares the logits themselves (no
+    arithmetic), equal logits going to the lower expert index.
+
+    With a per-expert bias [BAGEL, the LFM2-MoE softmax-then-bias routing and
+    the fix that makes the router apply it]: p = softmax over all experts, the
+    k largest p_e + bias_e are selected, and the weights are the selected
+    p renormalised to sum 1 (reading: the same weights as the unbiased router
+    gives for the same selection).  The selection is decided in fp32 (p and
+    p + bias formed in fp32); the weights use fp64 p.
+
     Returns ids int32 [T, k] (best first), w float64 [T, k]."""
     L = np.asarray(logits, dtype=np.float64)
-    order = np.argsort(-L, axis=1, kind="stable")[:, :k]   # stable: ties keep index order
-    sel = np.take_along_axis(L, order, axis=1)
-    z = np.exp(sel - sel.max(axis=1, keepdims=True))
-    return order.astype(np.int32), z / z.sum(axis=1, keepdims=True)
+    if bias is None:
+        order = np.argsort(-L, axis=1, kind="stable")[:, :k]   # stable: ties keep index order
+        sel = np.take_along_axis(L, order, axis=1)
+        z = np.exp(sel - sel.max(axis=1, keepdims=True))
+        return order.astype(np.int32), z / z.sum(axis=1, keepdims=True)
+    L32 = L.astype(np.float32)
+    e32 = np.exp(L32 - L32.max(axis=1, keepdims=True))
+    p32 = (e32 / e32.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    biased = (p32 + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
+    order = np.argsort(-biased.astype(np.float64), axis=1, kind="stable")[:, :k]
+    p64 = np.exp(L - L.max(axis=1, keepdims=True))
+    sel = np.take_along_axis(p64, order, axis=1)
+    return order.astype(np.int32), sel / sel.sum(axis=1, keepdims=True)
 
 
 def _softplus_f32(x: np.ndarray) -> np.ndarray:

@@ -150,3 +150,23 @@ def test_combine_pairs_closed_forms():
     # k = 1 with unit weights is the identity on the rows
     y1 = np.arange(12.0).reshape(3, 4)
     assert np.array_equal(oracle.combine_pairs(y1, np.zeros((3, 1), int), np.ones((3, 1)), 1), y1)
+
+
+def test_softmax_bias_router():
+    # logits (2, 1, 0), bias (0, 0, 1): p = softmax = (e^2, e, 1) / (e^2 + e + 1);
+    # p_2 + 1 beats p_0, so k = 1 picks expert 2 with weight 1, and k = 2 picks
+    # 2 then 0 with the renormalised p: 1 / (1 + e^2) and e^2 / (1 + e^2).
+    L = np.array([[2.0, 1.0, 0.0]])
+    b = np.array([0.0, 0.0, 1.0], np.float32)
+    ids, w = oracle.router_topk_softmax(L, 1, b)
+    assert ids.tolist() == [[2]] and abs(w[0, 0] - 1.0) < 1e-15
+    ids, w = oracle.router_topk_softmax(L, 2, b)
+    assert ids.tolist() == [[2, 0]]
+    e2 = math.exp(2.0)
+    assert np.allclose(w[0], [1 / (1 + e2), e2 / (1 + e2)], rtol=1e-14, atol=0)
+    # a zero bias gives the unbiased router's choice and weights (distinct logits)
+    rng = np.random.default_rng(9)
+    L = np.stack([rng.permutation(64) * 0.05 for _ in range(5)])
+    ids0, w0 = oracle.router_topk_softmax(L, 8)
+    ids1, w1 = oracle.router_topk_softmax(L, 8, np.zeros(64, np.float32))
+    assert np.array_equal(ids0, ids1) and np.allclose(w0, w1, rtol=1e-13, atol=0)
