@@ -50,6 +50,7 @@ __all__ = [
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
     "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual", "combine_pairs",
+    "router_softmax_bias_scores",
 ]
 
 # ---------------------------------------------------------------------------
@@ -402,14 +403,20 @@ def router_topk_softmax(logits: np.ndarray, k: int, bias: np.ndarray | None = No
         sel = np.take_along_axis(L, order, axis=1)
         z = np.exp(sel - sel.max(axis=1, keepdims=True))
         return order.astype(np.int32), z / z.sum(axis=1, keepdims=True)
-    L32 = L.astype(np.float32)
-    e32 = np.exp(L32 - L32.max(axis=1, keepdims=True))
-    p32 = (e32 / e32.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
-    biased = (p32 + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
+    biased = router_softmax_bias_scores(L, bias)
     order = np.argsort(-biased.astype(np.float64), axis=1, kind="stable")[:, :k]
     p64 = np.exp(L - L.max(axis=1, keepdims=True))
     sel = np.take_along_axis(p64, order, axis=1)
     return order.astype(np.int32), sel / sel.sum(axis=1, keepdims=True)
+
+
+def router_softmax_bias_scores(logits: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """Selection scores of the softmax-then-bias router in fp32: p + bias with
+    p = exp(l - max l) / sum exp(l - max l) over the row.  fp32 [T, E]."""
+    L32 = np.asarray(logits, dtype=np.float32)
+    e32 = np.exp(L32 - L32.max(axis=1, keepdims=True))
+    p32 = (e32 / e32.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    return (p32 + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
 
 
 def _softplus_f32(x: np.ndarray) -> np.ndarray:
