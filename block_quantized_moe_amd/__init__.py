@@ -65,6 +65,9 @@ _SIGS = {
                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_moe_combine": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_moe_combine_shared": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_combine_cast": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
     "qmoe_moe_gemv": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
@@ -368,6 +371,21 @@ def moe_combine(y, plan, T: int, topk: int, E: int, topk_w, base=None, out_dtype
         out = torch.empty((T, N), dtype=_dt(out_dtype), device=y.device)
     _check(lib().qmoe_moe_combine(_ptr(y), _code(y), _ptr(plan), T, topk, E, _ptr(topk_w), N, _ptr(base),
                                   _ptr(out), _code(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_combine_shared(y, plan, T: int, topk: int, E: int, topk_w, shared=None, shared_gate=None,
+                       residual=None, out_dtype: int = BF16, out=None):
+    """Combine plus a sigmoid-gated shared expert and the residual add
+    (include/qmoe.h); out may be the residual tensor itself."""
+    import torch
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=_dt(out_dtype), device=y.device)
+    rcode = _code(residual) if residual is not None else F32
+    _check(lib().qmoe_moe_combine_shared(_ptr(y), _code(y), _ptr(plan), T, topk, E, _ptr(topk_w), N, _ptr(shared),
+                                         _ptr(shared_gate), _ptr(residual), rcode, _ptr(out), _code(out),
+                                         _stream()), "moe_combine_shared")
     return out
 
 

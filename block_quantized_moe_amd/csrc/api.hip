@@ -29,7 +29,7 @@ void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
 void launch_router_topk(const void*, int, int64_t, int, int, int, const float*, float, int32_t*,
                         float*, hipStream_t);
 void launch_moe_combine(const void*, int, const int32_t*, int64_t, int, int, const float*, int64_t,
-                        const float*, void*, int, hipStream_t);
+                        const float*, const float*, const void*, int, void*, int, hipStream_t);
 }  // namespace qmoe
 
 using namespace qmoe;
@@ -260,18 +260,48 @@ int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, i
   return launched();
 }
 
-int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t, int32_t topk,
-                     int32_t n_experts, const float* topk_w, int64_t n, const float* base, void* out,
-                     int32_t out_dtype, void* stream) {
+static int combine_checks(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t, int32_t topk,
+                          int32_t n_experts, const float* topk_w, int64_t n, const float* base,
+                          const void* out, int32_t out_dtype) {
   if (!y || !plan || !topk_w || !out || t < 0 || n < 0 || topk < 1 || n_experts < 1) return QMOE_ERR_ARG;
   if (!dtype_ok(y_dtype) || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
   if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS) return QMOE_ERR_LIMIT;
   if (t * topk > (1ll << 30) || ((n + 255) / 256) * t > (1ll << 31) - 1) return QMOE_ERR_LIMIT;
   if (!al16(y) || !al16(plan) || !al4(topk_w) || !al16(out) || (base && !al4(base))) return QMOE_ERR_ALIGN;
+  return QMOE_OK;
+}
+
+int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t, int32_t topk,
+                     int32_t n_experts, const float* topk_w, int64_t n, const float* base, void* out,
+                     int32_t out_dtype, void* stream) {
+  QMOE_TRY(combine_checks(y, y_dtype, plan, t, topk, n_experts, topk_w, n, base, out, out_dtype));
   if (t == 0 || n == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
-  launch_moe_combine(y, y_dtype, plan, t, topk, n_experts, topk_w, n, base, out, out_dtype,
-                     (hipStream_t)stream);
+  launch_moe_combine(y, y_dtype, plan, t, topk, n_experts, topk_w, n, base, nullptr, nullptr, QMOE_F32, out,
+                     out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_moe_combine_shared(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t, int32_t topk,
+                            int32_t n_experts, const float* topk_w, int64_t n, const float* shared,
+                            const float* shared_gate, const void* residual, int32_t residual_dtype,
+                            void* out, int32_t out_dtype, void* stream) {
+  QMOE_TRY(combine_checks(y, y_dtype, plan, t, topk, n_experts, topk_w, n, shared, out, out_dtype));
+  if (shared_gate && !shared) return QMOE_ERR_ARG;
+  if (residual && !dtype_ok(residual_dtype)) return QMOE_ERR_ARG;
+  if ((shared_gate && !al4(shared_gate)) || (residual && !al16(residual))) return QMOE_ERR_ALIGN;
+  // out may be the residual buffer itself (same dtype), any other overlap is an error
+  if (residual && residual != out) {
+    const int64_t rb = t * n * (residual_dtype == QMOE_F32 ? 4 : 2);
+    const int64_t ob = t * n * (out_dtype == QMOE_F32 ? 4 : 2);
+    const uintptr_t r0 = (uintptr_t)residual, o0 = (uintptr_t)out;
+    if (r0 < o0 + ob && o0 < r0 + rb) return QMOE_ERR_ARG;
+  }
+  if (residual && residual == out && residual_dtype != out_dtype) return QMOE_ERR_ARG;
+  if (t == 0 || n == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_moe_combine(y, y_dtype, plan, t, topk, n_experts, topk_w, n, shared, shared_gate, residual,
+                     residual ? residual_dtype : QMOE_F32, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 
@@ -292,7 +322,7 @@ int qmoe_router_topk(const void* logits, int32_t logits_dtype, int64_t t, int32_
   if (!logits || !ids || !weights || t < 0 || topk < 1 || n_experts < 1 || !dtype_ok(logits_dtype))
     return QMOE_ERR_ARG;
   if (scoring != QMOE_ROUTER_SOFTMAX && scoring != QMOE_ROUTER_SQRTSOFTPLUS) return QMOE_ERR_ARG;
-  if (scoring == QMOE_ROUTER_SOFTMAX && (bias || scale != 1.0f)) return QMOE_ERR_ARG;
+  if (scoring == QMOE_ROUTER_SOFTMAX && scale != 1.0f) return QMOE_ERR_ARG;
   if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS || t > (1ll << 31)) return QMOE_ERR_LIMIT;
   if (topk > n_experts) return QMOE_ERR_ARG;
   const uintptr_t esz = logits_dtype == QMOE_F32 ? 4 : 2;

@@ -9,7 +9,10 @@
 //    accumulator is cleared for the next call (no separate memset launch);
 //  * moe_combine_kernel is the deterministic alternative: for each token it
 //    adds its k expert outputs (gathered through the plan's inverse map) in
-//    ascending j, in fp32, then rounds once.
+//    ascending j, in fp32, then rounds once.  Optionally the sum starts from
+//    a shared expert's output, scaled by the sigmoid of a per-token gate
+//    logit, and the residual stream is added before the rounding (the page's
+//    sigmoid-gated scalar FMA with the post-MoE residual folded in).
 #include "common.h"
 
 namespace qmoe {
@@ -47,23 +50,22 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict
                                                           const int32_t* __restrict__ plan, int64_t P,
                                                           int E, int topk, const float* __restrict__ w,
                                                           int64_t N, const float* __restrict__ base,
-                                                          void* __restrict__ out, int out_dtype) {
+                                                          const float* __restrict__ gate, const void* res,
+                                                          int res_dtype, void* out, int out_dtype) {
   const int64_t nb = (N + 255) / 256;
   const int64_t t = blockIdx.x / nb;
   const int64_t n = (blockIdx.x - t * nb) * 256 + threadIdx.x;
   if (n >= N) return;
   const PlanLayout L = plan_layout(P, E);
-  float acc = base ? base[t * N + n] : 0.f;
+  float acc = base ? base[t * N + n] * (gate ? sigmoid_f32(gate[t]) : 1.0f) : 0.f;
   for (int j = 0; j < topk; ++j) {
     const int pos = plan[L.inv + t * topk + j];
     if (pos < 0) continue;
     const int64_t i = (int64_t)pos * N + n;
-    float v;
-    if (y_dtype == QMOE_F32) v = ((const float*)y)[i];
-    else if (y_dtype == QMOE_F16) v = f16_to_f32(((const uint16_t*)y)[i]);
-    else v = bf16_to_f32(((const uint16_t*)y)[i]);
+    const float v = load_act(y, y_dtype, i);
     acc = __builtin_fmaf(w[t * topk + j], v, acc);
   }
+  if (res) acc += load_act(res, res_dtype, t * N + n);
   store_out(out, out_dtype, t * N + n, acc);
 }
 
@@ -76,7 +78,8 @@ __global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __rest
                                                               const int32_t* __restrict__ plan, int64_t P,
                                                               int E, int topk, const float* __restrict__ w,
                                                               int64_t N, const float* __restrict__ base,
-                                                              void* __restrict__ out, int out_dtype) {
+                                                              const float* __restrict__ gate, const void* res,
+                                                              int res_dtype, void* out, int out_dtype) {
   const int64_t nb = (N + 2047) / 2048;
   const int64_t t = blockIdx.x / nb;
   const int64_t n0 = ((blockIdx.x - t * nb) * 256 + threadIdx.x) * 8;
@@ -101,8 +104,9 @@ __global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __rest
       v[j][h] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(yr, off + 16 * h, 0, 0));
   }
   float acc[8];
+  const float gs = gate ? sigmoid_f32(gate[t]) : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = base ? base[t * N + n0 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = base ? base[t * N + n0 + i] * gs : 0.f;
 #pragma unroll
   for (int j = 0; j < QMOE_MAX_TOPK; ++j) {
     if (pos[j] < 0) continue;
@@ -122,6 +126,24 @@ __global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __rest
     }
   }
   const int64_t o = t * N + n0;
+  if (res) {
+    // read before the store below: out may be the residual buffer itself
+    if (res_dtype == QMOE_F32) {
+      const f4_t r0 = ((const f4_t*)res)[o / 4], r1 = ((const f4_t*)res)[o / 4 + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += r0[i];
+        acc[4 + i] += r1[i];
+      }
+    } else {
+      const u4_t r = ((const u4_t*)res)[o / 8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = (r[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+        acc[i] += res_dtype == QMOE_F16 ? f16_to_f32(b) : bf16_to_f32(b);
+      }
+    }
+  }
   if (out_dtype == QMOE_F32) {
     ((f4_t*)out)[o / 4] = f4_t{acc[0], acc[1], acc[2], acc[3]};
     ((f4_t*)out)[o / 4 + 1] = f4_t{acc[4], acc[5], acc[6], acc[7]};
@@ -151,25 +173,25 @@ void launch_combine_cast(float* acc, int64_t n, void* out, int out_dtype, hipStr
 }
 
 void launch_moe_combine(const void* y, int y_dtype, const int32_t* plan, int64_t t, int topk, int E,
-                        const float* w, int64_t N, const float* base, void* out, int out_dtype,
-                        hipStream_t s) {
+                        const float* w, int64_t N, const float* base, const float* gate, const void* res,
+                        int res_dtype, void* out, int out_dtype, hipStream_t s) {
   const int64_t ybytes = t * topk * N * (y_dtype == QMOE_F32 ? 4 : 2);
   if (N % 8 == 0 && ybytes < (1ll << 32)) {
     const dim3 grid((unsigned)(((N + 2047) / 2048) * t));
     if (y_dtype == QMOE_F32)
       hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_F32>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
-                         base, out, out_dtype);
+                         base, gate, res, res_dtype, out, out_dtype);
     else if (y_dtype == QMOE_F16)
       hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_F16>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
-                         base, out, out_dtype);
+                         base, gate, res, res_dtype, out, out_dtype);
     else
       hipLaunchKernelGGL(moe_combine_vec_kernel<QMOE_BF16>, grid, dim3(256), 0, s, y, plan, t * topk, E, topk, w, N,
-                         base, out, out_dtype);
+                         base, gate, res, res_dtype, out, out_dtype);
     return;
   }
   const dim3 grid((unsigned)(((N + 255) / 256) * t));
   hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, s, y, y_dtype, plan, t * topk, E, topk,
-                     w, N, base, out, out_dtype);
+                     w, N, base, gate, res, res_dtype, out, out_dtype);
 }
 
 }  // namespace qmoe

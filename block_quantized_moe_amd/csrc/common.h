@@ -58,6 +58,13 @@ __device__ __forceinline__ void store_out_t(void* out, int64_t i, float v) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+// Element i of an f32 / f16 / bf16 array.
+__device__ __forceinline__ float load_act(const void* p, int dtype, int64_t i) {
+  if (dtype == QMOE_F32) return ((const float*)p)[i];
+  if (dtype == QMOE_F16) return f16_to_f32(((const uint16_t*)p)[i]);
+  return bf16_to_f32(((const uint16_t*)p)[i]);
+}
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also orders global
 // memory, which on gfx9 means waiting for every outstanding vector-memory load

@@ -4,7 +4,10 @@
 // Two scorings:
 //   * softmax top-k [Everything Bagel 2, the commit moving the MoE router
 //     top-K to the GPU]: the k largest logits; weights are a softmax over the
-//     selected logits (they sum to 1);
+//     selected logits (they sum to 1).  With a per-expert bias (the LFM2-MoE
+//     softmax-then-bias routing on the same page): p = softmax over all
+//     experts, the k largest p + bias are selected, weights are the selected
+//     p renormalised;
 //   * DeepSeek V4 sqrtsoftplus [GGUF block-dequant + DSv4 kernel surface, the
 //     routing scoring commit]: score s = sqrt(softplus(logit)) with the stable
 //     softplus max(x, 0) + log(1 + exp(-|x|)); the k largest s + bias are
@@ -21,11 +24,14 @@
 // lane agree on the winner, and the order of equal scores is fixed.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace qmoe {
 
 constexpr int RT_WAVES = 4;  // tokens per 256-thread workgroup
+constexpr int ROUTER_SOFTMAX_BIAS = 2;  // softmax scoring with a bias given
 
 struct RouterArgs {
   const void* logits;
@@ -79,6 +85,25 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
+// Wave sum of a float with the same partner pattern; every lane gets the same
+// bits (each step adds the same two values on both partners).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  auto step = [](float x, auto ctrl) {
+    const uint32_t o = __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, x), decltype(ctrl)::value,
+                                                   0xf, 0xf, false);
+    return x + __builtin_bit_cast(float, o);
+  };
+  v = step(v, std::integral_constant<int, 0xB1>{});
+  v = step(v, std::integral_constant<int, 0x4E>{});
+  v = step(v, std::integral_constant<int, 0x141>{});
+  v = step(v, std::integral_constant<int, 0x140>{});
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 template <int DT>
 __device__ __forceinline__ float load_logit(const void* p, int64_t i) {
   if constexpr (DT == QMOE_F32) return ((const float*)p)[i];
@@ -93,8 +118,9 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_topk_kernel(RouterArgs a
   if (tok >= a.t) return;  // whole wave leaves; no barrier follows
 
   // Softmax selects on the logit itself, which the winning key gives back;
-  // sqrtsoftplus keeps the unbiased score beside the key.
-  constexpr int NV = SCORING == QMOE_ROUTER_SQRTSOFTPLUS ? NS : 1;
+  // the other scorings keep the weight's value (unbiased score or
+  // probability) beside the key.
+  constexpr int NV = SCORING == QMOE_ROUTER_SOFTMAX ? 1 : NS;
   uint64_t key[NS];  // 0: no expert (past E) or already selected
   float val[NV];
 #pragma unroll
@@ -110,8 +136,33 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_topk_kernel(RouterArgs a
         const float sc = sqrtf(sp);
         sel = a.bias ? sc + a.bias[e] : sc;
         val[s] = sc;
+      } else if constexpr (SCORING == ROUTER_SOFTMAX_BIAS) {
+        val[s] = x;  // the logit, until the softmax below
       }
       key[s] = ((uint64_t)score_key(sel) << 32) | (uint32_t)~(uint32_t)e;
+    }
+  }
+  if constexpr (SCORING == ROUTER_SOFTMAX_BIAS) {
+    // p = softmax over all experts in fp32, then the selection key p + bias
+    uint64_t kmax = key[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) kmax = key[s] > kmax ? key[s] : kmax;
+    const float m = key_score((uint32_t)(wave_max_u64(kmax) >> 32));
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float ex = key[s] ? expf(val[s] - m) : 0.0f;
+      val[s] = ex;
+      part += ex;
+    }
+    const float inv = 1.0f / wave_sum_f32(part);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int e = lane + 64 * s;
+      if (key[s]) {
+        val[s] *= inv;
+        key[s] = ((uint64_t)score_key(val[s] + a.bias[e]) << 32) | (uint32_t)~(uint32_t)e;
+      }
     }
   }
 
@@ -133,18 +184,20 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_topk_kernel(RouterArgs a
     for (int s = 0; s < NS; ++s) key[s] = key[s] == win ? 0ull : key[s];  // keys are unique
     const int e = (int)~(uint32_t)win;
     float v;
-    if constexpr (SCORING == QMOE_ROUTER_SQRTSOFTPLUS)
-      v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, bv), e & 63));
-    else v = key_score((uint32_t)(win >> 32));
+    if constexpr (SCORING == QMOE_ROUTER_SOFTMAX) v = key_score((uint32_t)(win >> 32));
+    else v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, bv), e & 63));
     if constexpr (SCORING == QMOE_ROUTER_SOFTMAX) {
       if (j == 0) m = v;  // the first selection is the largest logit
       sum += expf(v - m);
+    } else if constexpr (SCORING == ROUTER_SOFTMAX_BIAS) {
+      sum += v;
     }
     if (j == lane) { idj = e; vj = v; }
   }
 
   float wj;
   if constexpr (SCORING == QMOE_ROUTER_SQRTSOFTPLUS) wj = vj * a.scale;
+  else if constexpr (SCORING == ROUTER_SOFTMAX_BIAS) wj = vj / sum;
   else wj = expf(vj - m) / sum;
   if (lane < a.k) {
     a.ids[tok * a.k + lane] = idj;
@@ -164,6 +217,7 @@ static void launch_ns(const RouterArgs& a, int ns, dim3 g, hipStream_t s) {
 template <int DT>
 static void launch_dt(const RouterArgs& a, int ns, dim3 g, hipStream_t s) {
   if (a.scoring == QMOE_ROUTER_SQRTSOFTPLUS) launch_ns<DT, QMOE_ROUTER_SQRTSOFTPLUS>(a, ns, g, s);
+  else if (a.bias) launch_ns<DT, ROUTER_SOFTMAX_BIAS>(a, ns, g, s);
   else launch_ns<DT, QMOE_ROUTER_SOFTMAX>(a, ns, g, s);
 }
 

@@ -73,7 +73,8 @@ enum {
 
 /* Router scorings of qmoe_router_topk. */
 enum {
-  QMOE_ROUTER_SOFTMAX = 0,      /* top-k logits, softmax over the selected        [BAGEL] */
+  QMOE_ROUTER_SOFTMAX = 0,      /* top-k logits, softmax over the selected; with
+                                   a bias: top-k of softmax + bias (LFM2-MoE)     [BAGEL] */
   QMOE_ROUTER_SQRTSOFTPLUS = 1  /* top-k of sqrt(softplus(l)) + bias, weight
                                    sqrt(softplus(l)) * scale (DeepSeek V4)        [GGUF]  */
 };
@@ -265,6 +266,24 @@ int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_
                      int32_t topk, int32_t n_experts, const float* topk_w, int64_t n, const float* base,
                      void* out, int32_t out_dtype, void* stream);
 
+/* Combine with a gated shared expert and the residual add ([BAGEL] the
+ * sigmoid-gated scalar FMA with the post-MoE residual add folded in, used to
+ * accumulate the top-K expert outputs):
+ *   out[t, n] = residual[t, n] + g_t * shared[t, n]
+ *               + sum_j topk_w[t, j] * y[pos(t, j), n],
+ *   g_t = 1 / (1 + exp(-shared_gate[t]))  (g_t = 1 when shared_gate is NULL).
+ * fp32: the shared term first, then the pairs in ascending j, then the
+ * residual; one rounding to out_dtype.  shared DEVICE fp32 [t, N] or NULL (no
+ * shared term; shared_gate must then be NULL); shared_gate DEVICE fp32 [t]
+ * logits or NULL; residual DEVICE [t, N] in residual_dtype or NULL, 16-byte
+ * aligned.  out may be the residual buffer itself when the dtypes agree (the
+ * update is then in place); any other overlap of out and residual is
+ * QMOE_ERR_ARG.  Other arguments and errors as qmoe_moe_combine. */
+int qmoe_moe_combine_shared(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t,
+                            int32_t topk, int32_t n_experts, const float* topk_w, int64_t n,
+                            const float* shared, const float* shared_gate, const void* residual,
+                            int32_t residual_dtype, void* out, int32_t out_dtype, void* stream);
+
 /* out = RNE(acc) for n_elems values, then acc = 0 (so the fp32 accumulator
  * of a WEIGHTED_COMBINE is ready for the next call).  DEVICE pointers. */
 int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype, void* stream);
@@ -295,9 +314,13 @@ int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64
  * [GGUF] the DeepSeek V4 sqrtsoftplus routing scoring commit).
  *   logits DEVICE [t, n_experts] row-major, logits_dtype F32 / F16 / BF16
  *          (aligned to its element size).
- *   SOFTMAX        selects the topk largest logits; weights[t, j] =
- *                  exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected
- *                  (they sum to 1).  bias must be NULL and scale 1.
+ *   SOFTMAX        bias NULL: selects the topk largest logits; weights[t, j]
+ *                  = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected
+ *                  (they sum to 1).  With a bias (DEVICE f32 [n_experts],
+ *                  the LFM2-MoE softmax-then-bias routing): p = softmax of
+ *                  the row over all experts in fp32, selects the topk largest
+ *                  p_e + bias[e], weights = the selected p / their sum.  scale
+ *                  must be 1.
  *   SQRTSOFTPLUS   s_e = sqrt(max(l, 0) + log1p(exp(-|l|))) in fp32; selects
  *                  the topk largest s_e + bias[e] (bias DEVICE f32
  *                  [n_experts], or NULL for zero); weights = s_e * scale
@@ -305,8 +328,10 @@ int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64
  *   ids DEVICE int32 [t, topk], weights DEVICE f32 [t, topk], written in
  *   selection order (best first).  Equal selection scores go to the lower
  *   expert index; NaN scores rank below every number, -0 equals +0.
+ * A NaN logit in a row makes that row's softmax weights NaN when it is
+ * selected (no bias) or always (bias).
  * Errors: QMOE_ERR_ARG (NULL pointer, t < 0, topk < 1 or > n_experts, bad
- * dtype / scoring, SOFTMAX with a bias or scale != 1), QMOE_ERR_LIMIT
+ * dtype / scoring, SOFTMAX with scale != 1), QMOE_ERR_LIMIT
  * (topk > QMOE_MAX_TOPK, n_experts > QMOE_MAX_EXPERTS, t > 2^31),
  * QMOE_ERR_ALIGN; nothing is launched on error.  t == 0 launches nothing.
  * ------------------------------------------------------------------------ */

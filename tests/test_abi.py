@@ -180,10 +180,9 @@ def test_argument_validation_before_launch():
     assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 64, ctypes.c_void_p(16), 1, None) == 0
     assert L.qmoe_moe_gemv(ctypes.byref(w), ctypes.c_void_p(16), 2, 0, ctypes.c_void_p(16), None, 8, 1,
                            ctypes.c_void_p(16), 2, None) == 0
-    # router top-k: softmax takes no bias or scale; topk within [1, min(8, E)]
+    # router top-k: softmax takes no scale; topk within [1, min(8, E)]
     P = ctypes.c_void_p(16)
     r = L.qmoe_router_topk
-    assert r(P, 2, 4, 128, 8, 0, P, 1.0, P, P, None) == E
     assert r(P, 2, 4, 128, 8, 0, None, 2.0, P, P, None) == E
     assert r(P, 2, 4, 128, 9, 1, None, 1.0, P, P, None) == -4
     assert r(P, 2, 4, 2048, 8, 1, None, 1.0, P, P, None) == -4

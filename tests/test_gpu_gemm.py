@@ -244,3 +244,43 @@ def test_moe_combine_paths(N, ydt):
         ok = inv[:, j] >= 0
         ref[ok] += w[ok, j, None].astype(np.float64) * yv[inv[ok, j]]
     assert normwise_err(to_f64(out), ref, "f32") <= 1e-6
+
+
+@pytest.mark.parametrize("N,ydt,rdt,odt,gated,inplace", [
+    (2048, "bf16", "bf16", "bf16", True, True),   # 16-byte path, residual updated in place
+    (2048, "f32", "f32", "f32", True, False),
+    (1004, "bf16", "bf16", "bf16", True, False),  # element-wise path
+    (2048, "bf16", None, "f32", False, False),    # ungated shared expert, no residual
+    (2048, "bf16", "f16", "bf16", True, False),   # residual in another dtype
+    (1000, "f32", None, "bf16", True, False),
+])
+def test_moe_combine_shared(N, ydt, rdt, odt, gated, inplace):
+    # combine + sigmoid-gated shared expert + residual against the oracle's
+    # pair combine and post-MoE epilogue
+    rng = np.random.default_rng(N + 3 * len(ydt) + (rdt is None))
+    T, k, E = 300, 8, 32
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    ids[5, 2] = -1
+    ids[9, 7] = E
+    pl = oracle.plan(ids, E, 80)
+    ys = rng.standard_normal((len(pl["sorted"]), N)).astype(np.float32)   # rows in expert-sorted order
+    shared = rng.standard_normal((T, N)).astype(np.float32)
+    glog = (3.0 * rng.standard_normal(T)).astype(np.float32)
+    glog[:4] = [0.0, 40.0, -40.0, -200.0]
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    y = torch.from_numpy(ys).cuda().to(dt[ydt])
+    res = None if rdt is None else torch.from_numpy(rng.standard_normal((T, N)).astype(np.float32)).cuda().to(dt[rdt])
+    plan = qm.moe_plan(torch.from_numpy(ids).cuda(), E, 80)
+    args = dict(shared=torch.from_numpy(shared).cuda(), shared_gate=torch.from_numpy(glog).cuda() if gated else None,
+                residual=res, out_dtype={"bf16": qm.BF16, "f32": qm.F32}[odt])
+    res64 = None if res is None else to_f64(res)
+    if inplace:
+        args["out"] = res
+    out = qm.moe_combine_shared(y, plan, T, k, E, torch.from_numpy(w).cuda(), **args)
+    torch.cuda.synchronize()
+    yp = np.zeros((T * k, N))
+    yp[pl["sorted"]] = to_f64(y)
+    ref = oracle.gated_shared_residual(oracle.combine_pairs(yp, ids, w, E), shared, glog if gated else None, res64)
+    assert normwise_err(to_f64(out), ref, odt) <= (1e-6 if odt == "f32" else TOL)
+    if inplace:
+        assert out.data_ptr() == res.data_ptr()

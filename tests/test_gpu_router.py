@@ -131,6 +131,41 @@ def test_sqrtsoftplus_large_logits_and_no_bias():
     assert np.array_equal(np.sort(ids.cpu().numpy(), 1), np.sort(ref_ids, 1))
 
 
+def _check_validity(b64, ids, k):
+    """GPU ids against fp32 oracle selection scores b64 [T, E]: distinct, in
+    range, best first and no unselected expert clearly better (a few ulp);
+    equal to the oracle's set where the boundary gap is clear."""
+    tol = 4 * np.spacing(np.abs(b64).max(axis=1, keepdims=True).astype(np.float32)).astype(np.float64)
+    sel = np.take_along_axis(b64, ids.astype(np.int64), 1)
+    mask = np.ones_like(b64, bool)
+    np.put_along_axis(mask, ids.astype(np.int64), False, 1)
+    rest = np.where(mask, b64, -np.inf).max(1)
+    assert all(len(set(r.tolist())) == k for r in ids)
+    assert (sel.min(1) >= rest - tol[:, 0]).all()
+    assert (np.diff(sel, axis=1) <= tol).all()
+    srt = -np.sort(-b64, axis=1)
+    return (srt[:, k - 1] - srt[:, k] > tol[:, 0]) if k < b64.shape[1] else np.ones(len(b64), bool)
+
+
+@pytest.mark.parametrize("T,E,k,dt", [(1024, 32, 4, "bf16"), (300, 256, 8, "f32"), (77, 1000, 8, "f16")])
+def test_softmax_bias_matches_oracle(T, E, k, dt):
+    # softmax-then-bias: p = softmax over all experts, select on p + bias,
+    # weights the selected p renormalised
+    rng = np.random.default_rng(T + E)
+    L, L64 = _logits(rng, T, E, dt, sigma=2.0)
+    bias = (0.05 * rng.standard_normal(E)).astype(np.float32)
+    ids, w = qm.router_topk(L, k, bias=torch.from_numpy(bias).cuda())
+    ids = ids.cpu().numpy()
+    ref_ids, _ = oracle.router_topk_softmax(L64, k, bias)
+    b64 = oracle.router_softmax_bias_scores(L64, bias).astype(np.float64)
+    clear = _check_validity(b64, ids, k)
+    assert clear.mean() > 0.95
+    assert np.array_equal(np.sort(ids[clear], 1), np.sort(ref_ids[clear], 1))
+    p64 = np.exp(L64 - L64.max(1, keepdims=True))
+    sel = np.take_along_axis(p64, ids.astype(np.int64), 1)
+    assert np.allclose(w.cpu().numpy(), sel / sel.sum(1, keepdims=True), rtol=0, atol=2e-6)
+
+
 def test_bias_decides_but_does_not_weight():
     L = torch.tensor([[3.0, 0.0, 1.0, -2.0]], device="cuda")
     bias = torch.tensor([0.0, 5.0, 0.0, 0.0], device="cuda")
