@@ -22,6 +22,7 @@ Sources (web pages the method is described on):
           the GPU MoE router top-K and the expert-indexed int4 GEMV
           ([nExperts, outDim, inDim/8] u32 weights with scales and biases),
           and the fused swiglu commit (silu(g) * u).
+          Also the MXFP4 dequant commit (OCP MX v1.0 blocks).
   [SHIM]  "WIP: metaltile shim -- Qwen3.6 mt_qmm_mma / mt_moe_gather dispatch
           from VLLMBridge", PR body (dense qmm smoke cell M=32 N=256 K=2048).
 
@@ -34,6 +35,8 @@ Readings where the pages are silent (each repeated at the function):
   * Sign table: entry i is i with bit 7 set iff i has an odd number of set
     bits (the "even-parity 8th sign").
   * int4: nibble i of word w is element 8*w + i (low nibble first).
+  * MXFP4: "low nibble first" read as element 2i in the low nibble of code
+    byte i (adjacent elements share a byte).
   * Routers: equal scores select the lower expert index first; the DSv4
     sqrtsoftplus gather weight is the unbiased score times the routed scaling
     factor, with no renormalisation (none is stated); the softmax-then-bias
@@ -47,6 +50,7 @@ import numpy as np
 __all__ = [
     "f16_to_f64", "bf16_to_f64", "act_to_f64", "round_f16", "round_bf16",
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
+    "e2m1_value", "e8m0_scale", "dequant_mxfp4",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
     "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual", "combine_pairs",
@@ -199,6 +203,40 @@ def dequant_int4(qs: np.ndarray, scale: np.ndarray, bias: np.ndarray, group: int
     return s * q + b
 
 
+def e2m1_value(code) -> np.ndarray:
+    """The FP4 E2M1 element of the OCP MX format [GGUF, the MXFP4 dequant
+    commit, "Format"]: bit 3 sign, bits 2-1 exponent E, bit 0 mantissa m;
+    E = 0 is subnormal, m/2; E > 0 is 2^(E-1) * (1 + m/2).  No NaN or inf.
+    int [...] -> fp64 [...]."""
+    c = np.asarray(code, dtype=np.int64)
+    E = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(E == 0, m / 2.0, np.exp2(E - 1.0) * (1.0 + m / 2.0))
+    return np.where(c & 8, -mag, mag)
+
+
+def e8m0_scale(e) -> np.ndarray:
+    """E8M0 block scale [GGUF, the MXFP4 dequant commit]: 2^(e - 127), and
+    e = 0xFF is NaN.  uint8 [...] -> fp64 [...]."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def dequant_mxfp4(blocks: np.ndarray) -> np.ndarray:
+    """MXFP4 [GGUF, the MXFP4 dequant commit]: 17-byte blocks of 32 values,
+    the E8M0 exponent byte then 16 bytes of 4-bit codes, low nibble first
+    (element 2i is the low nibble of code byte i, element 2i+1 its high
+    nibble); value = e2m1(code) * 2^(e - 127).  Every product is exact in fp32
+    (a 2-bit significand times a power of two, subnormals included) unless it
+    exceeds fp32's range (e = 254 with |value| >= 2), where the fp32 result is
+    +-inf.  blocks: uint8 [..., 17] -> fp32 [..., 32]."""
+    e = blocks[..., 0]
+    b = blocks[..., 1:17].astype(np.int64)
+    codes = np.stack([b & 15, b >> 4], axis=-1).reshape(b.shape[:-1] + (32,))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return (e2m1_value(codes) * e8m0_scale(e)[..., None]).astype(np.float32)
+
+
 def dequant(W) -> np.ndarray:
     """Whole weight tensor (a synth.QWeights) -> fp32 [E, N, K]."""
     if W.fmt == "int4":
@@ -209,6 +247,8 @@ def dequant(W) -> np.ndarray:
         v = dequant_q2_k(W.blocks)
     elif W.fmt == "iq2_xxs":
         v = dequant_iq2_xxs(W.blocks, W.grid)
+    elif W.fmt == "mxfp4":
+        v = dequant_mxfp4(W.blocks)
     else:
         raise ValueError(W.fmt)
     return v.reshape(W.E, W.N, W.K)

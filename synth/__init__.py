@@ -36,6 +36,8 @@ QK_K = 256
 Q2_K_BYTES = 84
 IQ2_XXS_BYTES = 66
 INT4_GROUP = 64
+MXFP4_BLOCK = 32
+MXFP4_BYTES = 17
 
 # Child-stream order for one configuration's SeedSequence.
 STREAMS = ("activations", "router", "w_gate_up", "w_down", "shared")
@@ -76,7 +78,7 @@ def bf16_bits(a) -> np.ndarray:
 class QWeights:
     """A stacked expert weight tensor W[E, N, K] in its on-disk form.
 
-    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "int4".
+    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "mxfp4" | "int4".
     blocks: uint8 [E, N, K/block, block_bytes] for the GGUF-style formats.
     qs/scale/bias: int4 arrays (uint32 [E,N,K/8], uint16 fp16 bits [E,N,K/group]).
     grid: uint8 [256, 8] magnitude table (IQ2_XXS only).
@@ -173,8 +175,20 @@ def int4(rng: np.random.Generator, E: int, N: int, K: int, group: int = INT4_GRO
     return QWeights("int4", E, N, K, group, qs=qs, scale=s, bias=b)
 
 
+def mxfp4(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
+    """MXFP4 blocks: the E8M0 exponent byte (2^-9 .. 2^-5 scales, so the
+    largest code, 6, gives weights up to about 0.19) and 16 bytes of uniform
+    random 4-bit codes."""
+    assert K % MXFP4_BLOCK == 0
+    nb = K // MXFP4_BLOCK
+    blocks = np.empty((E, N, nb, MXFP4_BYTES), dtype=np.uint8)
+    blocks[..., 0] = rng.integers(118, 123, size=(E, N, nb), dtype=np.uint8)
+    blocks[..., 1:] = rng.integers(0, 256, size=(E, N, nb, 16), dtype=np.uint8)
+    return QWeights("mxfp4", E, N, K, MXFP4_BLOCK, blocks=blocks)
+
+
 def weights(fmt: str, rng, E, N, K, **kw) -> QWeights:
-    return {"q8_0": q8_0, "q2_k": q2_k, "iq2_xxs": iq2_xxs, "int4": int4}[fmt](rng, E, N, K, **kw)
+    return {"q8_0": q8_0, "q2_k": q2_k, "iq2_xxs": iq2_xxs, "mxfp4": mxfp4, "int4": int4}[fmt](rng, E, N, K, **kw)
 
 
 # ---------------------------------------------------------------------------
