@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
 # enums mirrored from include/qmoe.h
 F32, F16, BF16 = 0, 1, 2
-Q8_0, Q2_K, IQ2_XXS, INT4 = 0, 1, 2, 3
+Q8_0, Q2_K, IQ2_XXS, INT4, MXFP4 = 0, 1, 2, 3, 4
 EPI_STORE, EPI_SWIGLU, EPI_WEIGHTED_COMBINE, EPI_ACCUMULATE = 0, 1, 2, 3
 A_GATHER_TOKENS, A_SORTED_ROWS = 0, 1
 ROUTER_SOFTMAX, ROUTER_SQRTSOFTPLUS = 0, 1
-FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4}
+FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4, "mxfp4": MXFP4}
 MAX_TOPK, MAX_EXPERTS, MAX_GEMV_BATCH = 8, 1024, 64
 
 
@@ -48,6 +48,9 @@ _SIGS = {
     "qmoe_split_q8_0": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
     "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
+    "qmoe_split_mxfp4": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
+    "qmoe_dequant_mxfp4": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                    ctypes.c_void_p],
     "qmoe_split_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_iq2_signs_table": [ctypes.c_void_p],
     "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -158,6 +161,17 @@ def split_iq2_xxs(aos: np.ndarray, rows: int, k: int):
     return ia, d
 
 
+def split_mxfp4(aos: np.ndarray, rows: int, k: int):
+    """MXFP4 blocks [rows, k/32, 17] -> tiled (code words, E8M0 exponents)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 32) * 17:
+        raise QmoeError("split_mxfp4: block count does not match rows/k")
+    qs = np.empty(rows * k // 8, np.uint32)
+    e = np.empty(rows * (k // 32), np.uint8)
+    _check(lib().qmoe_split_mxfp4(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(e)), "split_mxfp4")
+    return qs, e
+
+
 def split_int4(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, rows: int, k: int, group: int):
     """MLX-style int4 rows -> (tiled code words, packed scale|bias<<16 words)."""
     words = np.ascontiguousarray(words, dtype=np.uint32).reshape(-1)
@@ -222,7 +236,7 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
            bias=None, group: int = 0, grid=None) -> DeviceWeights:
     """Split on-disk weights on the host (library splitter) and copy them to the device.
 
-    blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs.
+    blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs / mxfp4.
     qs, scale, bias: MLX-style int4 arrays for int4.  grid: uint8 [256, 8] (iq2_xxs)."""
     t = {}
     if fmt == "q8_0":
@@ -236,6 +250,9 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
         t["qs"], t["d"] = _dev(ia, device), _dev(d, device)
         t["grid"] = _dev(np.ascontiguousarray(grid, np.uint8).reshape(-1), device)
         t["signs"] = _dev(iq2_signs_table(), device)
+    elif fmt == "mxfp4":
+        q, e = split_mxfp4(blocks, E * N, K)
+        t["qs"], t["scales"] = _dev(q, device), _dev(e, device)
     elif fmt == "int4":
         q, sb = split_int4(qs, scale, bias, E * N, K, group)
         t["qs"], t["scales"] = _dev(q, device), _dev(sb, device)
@@ -281,6 +298,8 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
     elif w.fmt == "iq2_xxs":
         st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
                                     w.E * w.N, w.K, _ptr(out), out_dtype, s)
+    elif w.fmt == "mxfp4":
+        st = L.qmoe_dequant_mxfp4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
     else:
         st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, w.group,
                                  _ptr(out), out_dtype, s)

@@ -15,6 +15,7 @@ void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const
                          void*, int, hipStream_t);
 void launch_dequant_iq2_xxs(const uint32_t*, const uint16_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
                             void*, int, hipStream_t);
+void launch_dequant_mxfp4(const uint32_t*, const uint8_t*, int64_t, int64_t, void*, int, hipStream_t);
 void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
                          hipStream_t);
 void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
@@ -87,6 +88,11 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       if (!w->d || !w->grid || !w->signs) return QMOE_ERR_ARG;
       if (!al16(w->d) || !al16(w->grid) || !al16(w->signs)) return QMOE_ERR_ALIGN;
       break;
+    case QMOE_MXFP4:
+      if (w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (!w->scales) return QMOE_ERR_ARG;
+      if (!al16(w->scales)) return QMOE_ERR_ALIGN;
+      break;
     case QMOE_INT4:
       if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
       if (w->k % w->group || w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
@@ -136,6 +142,17 @@ int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
   launch_dequant_q8_0(qs, d, rows, k, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k, void* out,
+                       int32_t out_dtype, void* stream) {
+  if (!qs || !e || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(e) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_mxfp4(qs, e, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 

@@ -149,6 +149,29 @@ static inline unsigned grid_for(int64_t units) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
+// MXFP4: value = e2m1(code) * 2^(e - 127) over 32-value blocks (OCP MX, the
+// GGUF page's MXFP4 dequant commit).  The E2M1 values are exact in fp16, the
+// product with the power-of-two scale is exact in fp32 unless it leaves fp32's
+// range.  Tiled layout (qmoe.h): unit u is tiled word w (elements 8w .. 8w+7)
+// of block j of row R.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint32_t* __restrict__ qs,
+                                                            const uint8_t* __restrict__ e,
+                                                            int64_t n_units, int64_t k, void* __restrict__ out) {
+  const int64_t upr = k / 8, KT = k / 64;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t R = u / upr, kk = 8 * (u - R * upr);
+    const int64_t rb = R >> 4, r = R & 15, kt = kk >> 6, j = (kk & 63) >> 5, w = (kk & 31) >> 3;
+    const uint32_t q = qs[(((rb * KT + kt) * 2 + j) * 16 + r) * 4 + w];
+    const float s = e8m0_to_f32(e[(rb * (k / 32) + (kk >> 5)) * 16 + r]);
+    const u4_t p = fp4x8_pairs<ACT_F16>(q);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = f16_to_f32((p[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) * s;
+    store8<OUT>(out, u, v);
+  }
+}
+
 #define QMOE_DISPATCH_OUT(dtype, KERNEL, ...)                                         \
   do {                                                                                \
     if ((dtype) == QMOE_F32) hipLaunchKernelGGL(KERNEL<QMOE_F32>, __VA_ARGS__);       \
@@ -174,6 +197,11 @@ void launch_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t
   const int64_t units = rows * (k / 8);
   QMOE_DISPATCH_OUT(dtype, dequant_iq2_xxs_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, d, grid, signs,
                     units, k / 256, out);
+}
+void launch_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k, void* out,
+                          int dtype, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_mxfp4_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, e, units, k, out);
 }
 void launch_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k, int group,
                          void* out, int dtype, hipStream_t s) {

@@ -82,7 +82,8 @@ struct GemmArgs {
 template <int FMT, int ACT>
 struct KOrder {
   // true: lane group g owns k in [16g, 16g+16); false: MFMA step s covers [32s, 32s+32)
-  static constexpr bool chunk = !(ACT == ACT_BF16 && (FMT == QMOE_Q8_0 || FMT == QMOE_IQ2_XXS));
+  static constexpr bool chunk =
+      !(FMT == QMOE_MXFP4 || (ACT == ACT_BF16 && (FMT == QMOE_Q8_0 || FMT == QMOE_IQ2_XXS)));
 };
 
 // Raw weight bytes one lane needs for one 64-wide K tile of one output row.
@@ -127,6 +128,17 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
       r.x0 = sc[0];
       r.x2 = sc[16];
     }
+  } else if constexpr (FMT == QMOE_MXFP4) {
+    // tiled layout: block j of the tile is 16 rows x 16 B; lane group lg
+    // takes word lg (elements 8lg .. 8lg+7) of both blocks, a wave reading
+    // 256 contiguous bytes per block
+    const int64_t rb = R >> 4, rr = R & 15;
+    const uint32_t* tile = (const uint32_t*)g.qs + (rb * (K / 64) + k0 / 64) * 128 + 4 * rr + lg;
+    r.v[0] = tile[0];
+    r.v[1] = tile[64];
+    const uint8_t* e = (const uint8_t*)g.scales + (rb * (K / 32) + k0 / 32) * 16 + rr;
+    r.x0 = e[0];
+    r.x2 = e[16];
   } else if constexpr (FMT == QMOE_Q2_K) {
     // tiled layout: t = 16-row block * K/256 + super-block; a wave's loads of
     // one 16-row block read contiguous runs
@@ -318,7 +330,29 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
   // ---- one K tile of MFMA work from LDS buffer `buf` and raw weights `rw`
   auto compute = [&](int kt, int buf, const Raw (&rw)[NB]) {
     const uint16_t* Ab = c.As + buf * BM * LDA;
-    if constexpr (ACT == ACT_F16) {
+    if constexpr (FMT == QMOE_MXFP4) {
+      // plain k order, either activation type: step s = one 32-value block;
+      // the E2M1 code values enter the MFMA exactly and the block's
+      // power-of-two scale multiplies the partial sum
+      typedef typename ActT<ACT>::v8 V8;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u4_t cc[2] = {fp4x8_pairs<ACT>(rw[b].v[0]), fp4x8_pairs<ACT>(rw[b].v[1])};
+        const float d0 = e8m0_to_f32(rw[b].x0), d1 = e8m0_to_f32(rw[b].x2);
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const V8 a = __builtin_bit_cast(V8, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
+            const f4_t t = mfma(a, __builtin_bit_cast(V8, cc[st]), f4_t{0, 0, 0, 0});
+            const float ds = st ? d1 : d0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(ds, t[r], acc[m][b][r]);
+          }
+        }
+      }
+    } else if constexpr (ACT == ACT_F16) {
       u4_t bf[NB][2];
 #pragma unroll
       for (int b = 0; b < NB; ++b) frag_f16<FMT>(rw[b], lg, c.lut_grid, c.lut_sign, bf[b][0], bf[b][1]);
@@ -1151,6 +1185,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     case QMOE_Q8_0: launch_f<QMOE_Q8_0>(g, act, epi, s); break;
     case QMOE_Q2_K: launch_f<QMOE_Q2_K>(g, act, epi, s); break;
     case QMOE_IQ2_XXS: launch_f<QMOE_IQ2_XXS>(g, act, epi, s); break;
+    case QMOE_MXFP4: launch_f<QMOE_MXFP4>(g, act, epi, s); break;
     default: launch_f<QMOE_INT4>(g, act, epi, s); break;
   }
 }

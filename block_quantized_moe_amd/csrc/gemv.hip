@@ -147,6 +147,27 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
         res[t] += dd * p;
       }
     }
+  } else if constexpr (FMT == QMOE_MXFP4) {
+    // tiled layout: chunk c is block c&1 of k tile c/2, 16 bytes per row
+    const int64_t rb = R >> 4, rr = R & 15;
+    const u4_t q = *(const u4_t*)((const uint32_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 2 + (c & 1)) * 16 + rr) * 4);
+    const float dd = e8m0_to_f32(((const uint8_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr]);
+    uint32_t cp[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u4_t p = fp4x8_pairs<ACT>(q[w]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cp[4 * w + i] = p[i];
+    }
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        res[t] += dd * p;
+      }
+    }
   } else if constexpr (FMT == QMOE_Q2_K) {
     // tiled layout: t = (R/16) * (K/256) + super-block, row r = R % 16
     const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
@@ -807,6 +828,7 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
     case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
     case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;
     case QMOE_IQ2_XXS: launch_gemv_f<QMOE_IQ2_XXS>(g, act, cpl, epi, units, s); break;
+    case QMOE_MXFP4: launch_gemv_f<QMOE_MXFP4>(g, act, cpl, epi, units, s); break;
     default: launch_gemv_f<QMOE_INT4>(g, act, cpl, epi, units, s); break;
   }
   return QMOE_OK;

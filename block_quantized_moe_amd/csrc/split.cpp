@@ -35,6 +35,37 @@ int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16
   return QMOE_OK;
 }
 
+// MXFP4: 17-byte blocks (E8M0 exponent, 16 code bytes with element 2i in the
+// low nibble of byte i).  Codes tiled as u32 [R/16][k/64][2][16][4]: word w
+// of block j of row 16 rb + r holds elements 8w .. 8w+7 with element 8w+i in
+// the low nibble of byte i and 8w+4+i in its high nibble (a byte-wise table
+// lookup then yields elements in k order); exponents as [R/16][k/32][16].
+int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e) {
+  if (!aos || !qs || !e || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  const int64_t KT = k / 64, NB = k / 32;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t b = 0; b < NB; ++b) {
+      const uint8_t* p = (const uint8_t*)aos + (R * NB + b) * 17;
+      e[(rb * NB + b) * 16 + r] = p[0];
+      uint8_t code[32];
+      for (int i = 0; i < 16; ++i) {
+        code[2 * i] = p[1 + i] & 15;
+        code[2 * i + 1] = p[1 + i] >> 4;
+      }
+      uint32_t* dst = qs + (((rb * KT + b / 2) * 2 + (b % 2)) * 16 + r) * 4;
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+        for (int i = 0; i < 4; ++i)
+          word |= (uint32_t)(code[8 * w + i] | (code[8 * w + 4 + i] << 4)) << (8 * i);
+        dst[w] = word;
+      }
+    }
+  }
+  return QMOE_OK;
+}
+
 // Q2_K and IQ2_XXS are tiled by 16-row blocks (global row R = 16 rb + r),
 // super-block sb = k / 256 inner, so that every 64-wide k tile of a 16-row
 // block reads its codes and per-row metadata as a few contiguous runs (the

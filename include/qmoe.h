@@ -60,7 +60,8 @@ typedef enum {
                         scale/min per 16, fp16 d/dmin                    [GGUF Kernels 2] */
   QMOE_IQ2_XXS = 2,  /* 256-value super-blocks, grid index + 7-bit sign
                         groups with an even-parity 8th sign, 4-bit scale [GGUF Kernels 3] */
-  QMOE_INT4 = 3      /* MLX-style affine int4: s*q + b per group         [BAGEL]          */
+  QMOE_INT4 = 3,     /* MLX-style affine int4: s*q + b per group         [BAGEL]          */
+  QMOE_MXFP4 = 4     /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 values [GGUF MXFP4]     */
 } qmoe_format;
 
 /* Epilogues of the matmul entry points. */
@@ -127,6 +128,15 @@ enum {
  *            biases NULL
  *            group  32, 64, 128 or 256 (bf16 activations in the prefill matmul:
  *                   64, 128 or 256)
+ *   MXFP4    value = e2m1(code) * 2^(e - 127) over 32-value blocks (e = 0xFF:
+ *            NaN), tiled by qmoe_split_mxfp4 (rows = E*n a multiple of 16, k
+ *            of 64).  R, rb, r as above, 64-wide k tile kt:
+ *            qs     u32 [R/16][k/64][2][16][4]      word w of block j (32 values
+ *                   at 64kt + 32j) of row 16rb + r holds the codes of elements
+ *                   8w .. 8w+7 of the block: element 8w+i (i < 4) in the low
+ *                   nibble of byte i, element 8w+4+i in its high nibble
+ *            scales u8  [R/16][k/32][16]        E8M0 exponent e of each block
+ *            group  ignored (32)
  */
 typedef struct qmoe_weights {
   int32_t fmt;          /* qmoe_format                                    */
@@ -155,17 +165,21 @@ typedef struct qmoe_weights {
  *   Q8_0     34 B: fp16 d, 32 int8 codes
  *   Q2_K     84 B: 16 scale|min bytes, 64 code bytes, fp16 d, fp16 dmin
  *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
+ *   MXFP4    17 B: E8M0 exponent, 16 code bytes (element 2i in the low
+ *            nibble of byte i, 2i+1 in its high nibble)  [GGUF MXFP4 "Format"]
  * They come out in the tiled forms above (so that each wave-wide load of
  * the matmul kernels reads contiguous bytes): Q8_0 qs rows*k bytes, scales
  * rows*k/32; Q2_K qs rows*k/4 bytes, scales rows*k/16 bytes, d and dmin
- * rows*k/256; IQ2_XXS qs rows*k/16 u32, d rows*k/256.  Returns QMOE_ERR_ARG
- * on NULL / negative sizes, QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a
- * multiple of 64 (Q8_0) or 256.
+ * rows*k/256; IQ2_XXS qs rows*k/16 u32, d rows*k/256; MXFP4 qs rows*k/8 u32,
+ * e rows*k/32 bytes.  Returns QMOE_ERR_ARG on NULL / negative sizes,
+ * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0,
+ * MXFP4) or 256.
  * ------------------------------------------------------------------------ */
 int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16_t* d);
 int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin);
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint16_t* d);
+int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e);
 /* int4 slabs from the on-disk (MLX) form -- words [rows][k/8] with element
  * 8w+i in nibble i of word w, fp16 scales and biases [rows][k/group] -- to the
  * tiled GPU form above: every wave-wide weight load is one contiguous 512-byte
@@ -180,12 +194,14 @@ int qmoe_split_int4(const uint32_t* words, const uint16_t* scales, const uint16_
 void qmoe_iq2_signs_table(uint8_t out[128]);
 
 /* ------------------------------------------------------------------------
- * Standalone dequantisation ([GGUF] "Kernels" 1-3; [BAGEL] int4 slabs).
+ * Standalone dequantisation ([GGUF] "Kernels" 1-3 and the MXFP4 dequant
+ * commit; [BAGEL] int4 slabs).
  * Decodes every value in fp32 exactly as the format defines it and rounds
  * once (to nearest even) to out_dtype; results are bit-exact.  DEVICE
  * pointers, 16-byte aligned; out holds the rows x k matrix, row-major.
- * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0), 256
- * (Q2_K, IQ2_XXS) or 64 and group (int4).
+ * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0,
+ * MXFP4), 256 (Q2_K, IQ2_XXS) or 64 and group (int4).  MXFP4 values past the
+ * fp32 range (e = 254, |code value| >= 2) come out as +-inf, e = 0xFF as NaN.
  * ------------------------------------------------------------------------ */
 int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k,
                       void* out, int32_t out_dtype, void* stream);
@@ -197,6 +213,8 @@ int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* g
                          void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k,
                       int32_t group, void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k,
+                       void* out, int32_t out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dense quantised matmul ([SHIM] mt_qmm_mma; [DSV4] wide-tile q8_0 qgemm):

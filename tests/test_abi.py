@@ -85,6 +85,27 @@ def test_split_iq2_xxs_tiled_layout():
                 assert np.array_equal(ia[R // 16, s_, g, R % 16], blk[2 + 8 * g:10 + 8 * g])
 
 
+def test_split_mxfp4_tiled_layout():
+    """Every code and exponent lands where the header's tiled layout says."""
+    rows, k = 32, 192
+    W = synth.mxfp4(np.random.default_rng(2), 2, rows // 2, k)
+    qs, e = qm.split_mxfp4(W.blocks, rows, k)
+    b = W.blocks.reshape(rows, k // 32, 17)
+    q = qs.reshape(rows // 16, k // 64, 2, 16, 4)
+    e = e.reshape(rows // 16, k // 32, 16)
+    for R in range(rows):
+        for j in range(k // 32):
+            assert e[R // 16, j, R % 16] == b[R, j, 0]
+            codes = np.stack([b[R, j, 1:] & 15, b[R, j, 1:] >> 4], 1).reshape(32)  # element order
+            for w in range(4):
+                word = int(q[R // 16, j // 2, j % 2, R % 16, w])
+                for i in range(4):
+                    byte = (word >> (8 * i)) & 0xFF
+                    assert byte & 15 == codes[8 * w + i] and byte >> 4 == codes[8 * w + 4 + i]
+    with pytest.raises(qm.QmoeError):
+        qm.split_mxfp4(W.blocks[:, :8], 8 * 2 // 2, k)
+
+
 def test_split_int4_tiled_layout():
     """Every element of the MLX rows lands where the header's tiled layout says."""
     rng = np.random.default_rng(3)

@@ -40,6 +40,8 @@ def _weights(fmt, rng):
         W = synth.weights(fmt, rng, 2, 40, 512)   # E*N a multiple of 16 (tiled layout)
     elif fmt == "int4":
         W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
+    elif fmt == "mxfp4":
+        W = synth.mxfp4(rng, 2, 40, 512)
     else:
         W = synth.q8_0(rng, 2, 40, 512)
     return W
@@ -57,6 +59,10 @@ def _plant_specials(W):
         W.blocks[0, 1, 0, 82:84] = h(0x0001)
         W.blocks[0, 2, 0, 80:82] = h(0x0003)
         W.blocks[0, 3, 0, 80:84] = 0
+    elif W.fmt == "mxfp4":
+        for i, e in enumerate([255, 0, 254, 1, 253, 127]):  # NaN, 2^-127, past fp32 for |v| >= 2, ...
+            W.blocks[0, i, 0, 0] = e
+        W.blocks[0, 7, 2, 1:] = 0x88   # -0 codes
     elif W.fmt == "iq2_xxs":
         W.blocks[0, 0, 0, 0:2] = h(0x7E00)
         W.blocks[0, 1, 0, 0:2] = h(0x0001)
@@ -69,17 +75,34 @@ def _plant_specials(W):
     return W
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_dequant_bit_exact(fmt, dtype):
     W = _plant_specials(_weights(fmt, np.random.default_rng(17)))
     dw = upload(W)
     code = {"f32": qm.F32, "f16": qm.F16, "bf16": qm.BF16}[dtype]
-    with np.errstate(invalid="ignore", over="ignore"):
+    with np.errstate(invalid="ignore", over="ignore"):  # planted NaN / inf / out-of-range scales
         ref32 = oracle.dequant(W)
+        ref = oracle.round_out(ref32, dtype) if dtype != "f32" else ref32
     out = qm.dequant(dw, code)
     torch.cuda.synchronize()
-    _bits_equal(out.reshape(-1), oracle.round_out(ref32, dtype).reshape(-1) if dtype != "f32" else ref32.reshape(-1), dtype)
+    _bits_equal(out.reshape(-1), ref.reshape(-1), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dequant_mxfp4_every_code_and_exponent(dtype):
+    # all 256 exponent bytes x all 16 codes, each exponent in its own block
+    W = synth.mxfp4(np.random.default_rng(6), 1, 256, 64)
+    W.blocks[0, :, :, 0] = np.arange(256, dtype=np.uint8)[:, None]
+    codes = np.arange(32) % 16
+    W.blocks[0, :, :, 1:] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    code = {"f32": qm.F32, "f16": qm.F16, "bf16": qm.BF16}[dtype]
+    out = qm.dequant(upload(W), code)
+    torch.cuda.synchronize()
+    ref32 = oracle.dequant(W)
+    with np.errstate(over="ignore"):
+        ref = oracle.round_out(ref32, dtype) if dtype != "f32" else ref32
+    _bits_equal(out.reshape(-1), ref.reshape(-1), dtype)
 
 
 def test_dequant_iq2_xxs_every_index_and_sign():

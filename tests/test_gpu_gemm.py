@@ -21,7 +21,7 @@ from _helpers import TOL, normwise_err, report, to_f64, torch_act, upload
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4"]
+FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4"]
 
 
 def _w(fmt, rng, E, N, K):
@@ -65,6 +65,8 @@ def _exact_weights(fmt, rng, E, N, K):
     elif fmt == "q2_k":
         W.blocks[..., 80:82] = h(1.0)
         W.blocks[..., 82:84] = h(1.0)
+    elif fmt == "mxfp4":
+        W.blocks[..., 0] = 128         # scale 2: values 0, +-1, +-2, +-3, +-4, +-6, +-8, +-12
     elif fmt == "iq2_xxs":
         W.blocks[..., 0:2] = h(8.0)    # group scale 8 * (0.5 + s) / 4 = 1 + 2s
         W.grid = np.random.default_rng(1).choice(np.array([1, 2, 3], np.uint8), size=(256, 8))
@@ -169,7 +171,8 @@ def _check_moe(x, ids, w, Wgu, Wd, act, **kw):
 
 @pytest.mark.parametrize("gu,dn,act", [("int4", "int4", "bf16"), ("int4", "int4", "f16"),
                                        ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
-                                       ("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16")])
+                                       ("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
+                                       ("mxfp4", "mxfp4", "bf16"), ("mxfp4", "mxfp4", "f16")])
 def test_moe_stagewise(gu, dn, act):
     x, ids, w, Wgu, Wd = _moe_case(gu, dn, act, seed=len(gu) + len(act))
     _check_moe(x, ids, w, Wgu, Wd, act)
