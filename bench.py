@@ -117,12 +117,34 @@ def run_prefill(args, torch, qm):
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
-    # untimed-overhead-free pass: wall clock over K steps
+    # eager: K steps launched from the host, wall clock
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, False)
     torch.cuda.synchronize()
+    wall_eager = (time.perf_counter() - t0) / args.steps
+    # the same step captured once per weight copy into a HIP graph (its
+    # kernels allocate nothing and issue no memset), then K steps replayed:
+    # the launches go out without host gaps.  Wall clock, synchronised.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(i, False)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(R):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    del graphs
     # per-kernel durations (events on the launch stream) over another K steps
     all_marks = [step(i, True) for i in range(args.steps)]
     torch.cuda.synchronize()
@@ -130,7 +152,7 @@ def run_prefill(args, torch, qm):
         for j, name in enumerate(("plan", "gate_up", "down", "combine")):
             ev[name].append(m[j].elapsed_time(m[j + 1]) * 1e-3)
     kern = {n: float(np.median(v)) for n, v in ev.items()}
-    return inp, alg, wall, kern
+    return inp, alg, wall, kern, wall_eager
 
 
 def run_prefill_other(args, torch, qm, inp, R, steps):
@@ -279,18 +301,19 @@ def run_router(args, torch, qm):
     return rows
 
 
-def run_decode(args, torch, qm, B, layers):
+def run_decode(args, torch, qm, B, layers, inp=None):
     import synth
-    inp = synth.qwen_a3b_decode(B)
+    inp = synth.qwen_a3b_decode(B) if inp is None else inp
     dev = "cuda"
-    x = act_tensor(torch, inp.x)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[inp.act]
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).to(dev).view(tdt)
     ids = torch.from_numpy(inp.ids).to(dev)
     w = torch.from_numpy(inp.w).to(dev)
     gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
     gus = [gu0] + [gu0.clone() for _ in range(layers - 1)]
     dns = [dn0] + [dn0.clone() for _ in range(layers - 1)]
-    h = torch.empty((B, inp.k, inp.I), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((B, inp.H), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((B, inp.k, inp.I), dtype=tdt, device=dev)
+    out = torch.empty((B, inp.H), dtype=tdt, device=dev)
     uniq = np.unique(inp.ids)
     per_expert = (inp.w_gate_up.nbytes + inp.w_down.nbytes) // inp.E
     nbytes = len(uniq) * per_expert + B * inp.H * 2 * 2 + B * inp.k * inp.I * 2 * 2
@@ -347,7 +370,7 @@ def run_decode(args, torch, qm, B, layers):
     t_dn = float(np.median([m[1].elapsed_time(m[2]) for m in marks])) * 1e-3
     del graph, gus, dns
     torch.cuda.empty_cache()
-    return dict(B=B, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
+    return dict(workload=inp.name, B=B, layers=layers, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
                 s_per_layer_graph=t_graph, s_per_layer_eager=t_eager,
                 gate_up_s_event=t_gu, down_s_event=t_dn,
                 GBps=nbytes / t_graph / 1e9, hbm_frac=nbytes / t_graph / PEAK_HBM,
@@ -500,7 +523,7 @@ def main():
 
     qm.check_device()
     log("prefill: building inputs")
-    inp, alg, wall, kern = run_prefill(args, torch, qm)
+    inp, alg, wall, kern, wall_eager = run_prefill(args, torch, qm)
     t_step = wall
     value = alg["flops"] / t_step / 1e12
     t_gu = kern["gate_up"]
@@ -519,13 +542,20 @@ def main():
     }
     log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; kernels {json.dumps(kern)}")
     others = []
+    mx = None
     if not args.no_extra:
         import synth
+        mx = None
         for name, make, R in (("dsv4", lambda: synth.dsv4_flash_prefill(2048), 2),
+                              ("dsv4 mxfp4", lambda: synth.dsv4_flash_mxfp4_prefill(2048), 2),
                               ("mixed", lambda: synth.mixed_ffn(8192), 2)):
             log(f"prefill ({name}): building inputs")
-            others.append(run_prefill_other(args, torch, qm, make(), R, max(3, args.steps // 4)))
+            inp_o = make()
+            others.append(run_prefill_other(args, torch, qm, inp_o, R, max(3, args.steps // 4)))
             log(json.dumps(others[-1]))
+            if name == "dsv4 mxfp4":
+                mx = inp_o  # its weights also serve the MXFP4 decode lines
+            del inp_o
     log("router top-k")
     router = run_router(args, torch, qm)
     log(json.dumps(router))
@@ -535,6 +565,14 @@ def main():
             log(f"decode: B={B}")
             decode.append(run_decode(args, torch, qm, B, args.decode_layers))
             log(json.dumps(decode[-1]))
+        if not args.no_extra and mx is not None:
+            import dataclasses
+            for B in (1, 4):
+                log(f"decode (dsv4 mxfp4): B={B}")
+                dec = dataclasses.replace(mx, name=f"dsv4-flash-mxfp4-decode-b{B}", T=B, x=mx.x[:B],
+                                          ids=mx.ids[:B], w=mx.w[:B])
+                decode.append(run_decode(args, torch, qm, B, max(2, args.decode_layers // 5), dec))
+                log(json.dumps(decode[-1]))
     cpu = None
     if not args.no_cpu:
         log("cpu baseline: oracle sample")
@@ -547,6 +585,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": t_step * 1e3,
+        "ms_per_step_eager": wall_eager * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -561,7 +600,7 @@ def main():
         "kernels_s": kern,
         "algorithmic": {"flops": alg["flops"], "bytes": alg["bytes"]},
         "roofline": roofline,
-        "decode": [{"B": d["B"], "GBps": d["GBps"], "hbm_frac": d["hbm_frac"], "GBps_eager": d["GBps_eager"],
+        "decode": [{"workload": d["workload"], "B": d["B"], "layers": d["layers"], "GBps": d["GBps"], "hbm_frac": d["hbm_frac"], "GBps_eager": d["GBps_eager"],
                     "us_per_layer_graph": d["s_per_layer_graph"] * 1e6,
                     "us_per_layer_eager": d["s_per_layer_eager"] * 1e6,
                     "us_gate_up_event": d["gate_up_s_event"] * 1e6, "us_down_event": d["down_s_event"] * 1e6,

@@ -95,7 +95,7 @@ __device__ __forceinline__ void i8x4_pairs(uint32_t w, uint32_t& p0, uint32_t& p
 
 // Dot products of one 32-value weight chunk (global row R, chunk c) with the
 // activations of nt tokens; results added to res[].
-template <int FMT, int ACT>
+template <int FMT, int ACT, int MT>
 __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t c, const XChunk* x,
                                           int nt, float* res, const uint32_t* lut_grid,
                                           const uint32_t* lut_sign) {
@@ -117,7 +117,7 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       for (int i = 0; i < 4; ++i) cp[4 * w + i] = ((q[w] >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
     const float cb = b - Magic<ACT>::v * s;
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         float p = 0.f;
 #pragma unroll
@@ -139,7 +139,7 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       i8x4_pairs<ACT>(q1[w], cp[8 + 2 * w], cp[8 + 2 * w + 1]);
     }
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         float p = 0.f;
 #pragma unroll
@@ -160,7 +160,7 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       for (int i = 0; i < 4; ++i) cp[4 * w + i] = p[i];
     }
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         float p = 0.f;
 #pragma unroll
@@ -193,7 +193,7 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       cp[8 + 2 * w + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u) & 0xFF03FF03u;
     }
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
@@ -221,7 +221,7 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       for (int i = 0; i < 4; ++i) cp[4 * j + i] = row[i] ^ msk[i];
     }
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         float p = 0.f;
 #pragma unroll
@@ -263,7 +263,7 @@ __device__ __forceinline__ float row_reduce(float v, int lpr) {
 }
 
 // STORE / SWIGLU.  grid = (row blocks, slots).
-template <int FMT, int ACT, int EPI, int CPL>
+template <int FMT, int ACT, int EPI, int CPL, int MT>
 __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
@@ -295,11 +295,11 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
   const int64_t Nunits = swiglu ? g.N / 2 : g.N;
   const int64_t u0 = (int64_t)blockIdx.x * g.units_per_wg;
 
-  for (int tb = 0; tb < n; tb += GV_MAXT) {
-    const int nt = min(GV_MAXT, n - tb);
-    XChunk x[GV_MAXT][CPL];
+  for (int tb = 0; tb < n; tb += MT) {
+    const int nt = min(MT, n - tb);
+    XChunk x[MT][CPL];
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t < nt) {
         const int s2 = list[tb + t];
         const uint16_t* xr = g.a + (int64_t)(s2 / g.topk) * g.K;
@@ -311,20 +311,20 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
       const int64_t unit = u0 + ub + sub;
       const bool valid = (ub + sub < g.units_per_wg) && unit < Nunits;
       const int64_t uc = valid ? unit : 0;
-      float r0[GV_MAXT], r1[GV_MAXT];
+      float r0[MT], r1[MT];
 #pragma unroll
-      for (int t = 0; t < GV_MAXT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
+      for (int t = 0; t < MT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
       const int64_t Rg = (int64_t)e * g.N + uc;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        XChunk xc[GV_MAXT];
+        XChunk xc[MT];
 #pragma unroll
-        for (int t = 0; t < GV_MAXT; ++t) xc[t] = x[t][c];
-        chunk_dot<FMT, ACT>(g, Rg, li + c * lpr, xc, nt, r0, lut_grid, lut_sign);
-        if (swiglu) chunk_dot<FMT, ACT>(g, Rg + g.N / 2, li + c * lpr, xc, nt, r1, lut_grid, lut_sign);
+        for (int t = 0; t < MT; ++t) xc[t] = x[t][c];
+        chunk_dot<FMT, ACT, MT>(g, Rg, li + c * lpr, xc, nt, r0, lut_grid, lut_sign);
+        if (swiglu) chunk_dot<FMT, ACT, MT>(g, Rg + g.N / 2, li + c * lpr, xc, nt, r1, lut_grid, lut_sign);
       }
 #pragma unroll
-      for (int t = 0; t < GV_MAXT; ++t) {
+      for (int t = 0; t < MT; ++t) {
         if (t < nt) {
           const float y0 = row_reduce(r0[t], lpr);
           const float y1 = swiglu ? row_reduce(r1[t], lpr) : 0.f;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
 }
 
 // WEIGHTED_COMBINE (sum-folded down projection).  grid = row blocks.
-template <int FMT, int ACT, int CPL>
+template <int FMT, int ACT, int CPL, int MT>
 __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
@@ -382,29 +382,29 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   for (int di = wave; di < ndist; di += 4) {
     const int e = sid[dlist[di]];
     const int64_t Rg = (int64_t)e * g.N + rc;
-    // tokens routed to e, in slot order, GV_MAXT at a time
+    // tokens routed to e, in slot order, MT at a time
     int pos = dlist[di];
     while (pos < P) {
-      int sl[GV_MAXT];
+      int sl[MT];
       int nt = 0;
-      while (pos < P && nt < GV_MAXT) {
+      while (pos < P && nt < MT) {
         if (sid[pos] == e) sl[nt++] = pos;
         ++pos;
       }
       if (nt == 0) break;
-      float r[GV_MAXT];
+      float r[MT];
 #pragma unroll
-      for (int t = 0; t < GV_MAXT; ++t) r[t] = 0.f;
+      for (int t = 0; t < MT; ++t) r[t] = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        XChunk xc[GV_MAXT];
+        XChunk xc[MT];
 #pragma unroll
-        for (int t = 0; t < GV_MAXT; ++t)
+        for (int t = 0; t < MT; ++t)
           if (t < nt) load_x<ACT>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[t]);
-        chunk_dot<FMT, ACT>(g, Rg, li + c * lpr, xc, nt, r, lut_grid, lut_sign);
+        chunk_dot<FMT, ACT, MT>(g, Rg, li + c * lpr, xc, nt, r, lut_grid, lut_sign);
       }
 #pragma unroll
-      for (int t = 0; t < GV_MAXT; ++t) {
+      for (int t = 0; t < MT; ++t) {
         if (t < nt) {
           const float y = row_reduce(r[t], lpr);
           if (li == 0) {
@@ -769,19 +769,28 @@ static void launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
   else launch_gemv_split<ACT, QMOE_EPI_STORE>(g, w, s);
 }
 
-template <int FMT, int ACT, int CPL>
-static void launch_gemv_fac(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
+template <int FMT, int ACT, int CPL, int MT>
+static void launch_gemv_facm(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
   if (epi == QMOE_EPI_WEIGHTED_COMBINE) {
     const int rpw = 64 / g.lpr;
     const dim3 grid((unsigned)((g.N + rpw - 1) / rpw));
-    hipLaunchKernelGGL((gemv_combine_kernel<FMT, ACT, CPL>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemv_combine_kernel<FMT, ACT, CPL, MT>), grid, dim3(256), 0, s, g);
   } else {
     const dim3 grid((unsigned)((units_total + g.units_per_wg - 1) / g.units_per_wg), (unsigned)g.nslots);
     if (epi == QMOE_EPI_SWIGLU)
-      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_SWIGLU, CPL>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_SWIGLU, CPL, MT>), grid, dim3(256), 0, s, g);
     else
-      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_STORE, CPL>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemv_rows_kernel<FMT, ACT, QMOE_EPI_STORE, CPL, MT>), grid, dim3(256), 0, s, g);
   }
+}
+
+// One token per call (b = 1): the kernels hold one token's activations per
+// pass instead of GV_MAXT, which frees registers for more waves per SIMD.  A
+// token that names one expert twice still works, in two passes.
+template <int FMT, int ACT, int CPL>
+static void launch_gemv_fac(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
+  if (g.nslots == g.topk) launch_gemv_facm<FMT, ACT, CPL, 1>(g, epi, units_total, s);
+  else launch_gemv_facm<FMT, ACT, CPL, GV_MAXT>(g, epi, units_total, s);
 }
 
 template <int FMT>
@@ -812,8 +821,9 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
   g.lpr = (int)(chunks / cpl);
   const int rpw = 64 / g.lpr;
   const int64_t units = (epi == QMOE_EPI_SWIGLU) ? w->n / 2 : w->n;
-  // Enough workgroups to cover the chip: aim for >= 512 in total.
-  int64_t upw = (units * g.nslots) / 512;
+  // Enough workgroups to keep several waves per SIMD waiting on memory: aim
+  // for about 4096 in total (measured: 512 left the MXFP4 decode 15-20% slower).
+  int64_t upw = (units * g.nslots) / 4096;
   if (upw < 4 * rpw) upw = 4 * rpw;
   upw = (upw + 4 * rpw - 1) / (4 * rpw) * (4 * rpw);
   if (upw > 64) upw = 64 > 4 * rpw ? 64 : 4 * rpw;

@@ -313,5 +313,11 @@ def dsv4_flash_prefill(T: int = 2048, **over) -> MoEInputs:
     return moe(3, T=T, name="dsv4-flash-iq2xxs-q2k-prefill", **{**DSV4_FLASH, **over})
 
 
+def dsv4_flash_mxfp4_prefill(T: int = 2048, **over) -> MoEInputs:
+    """The DSv4-Flash expert shapes with its native MXFP4 expert weights."""
+    fmt = dict(gate_up_fmt="mxfp4", down_fmt="mxfp4")
+    return moe(5, T=T, name="dsv4-flash-mxfp4-prefill", **{**DSV4_FLASH, **fmt, **over})
+
+
 def mixed_ffn(T: int = 8192, **over) -> MoEInputs:
     return moe(4, T=T, name="mixed-format-moe-ffn", **{**MIXED_FFN, **over})

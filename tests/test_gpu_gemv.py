@@ -147,3 +147,18 @@ def test_gemv_int4_repeated_expert_within_token():
     ids = np.array([[1, 1, 1, 1], [1, 1, 2, 2]], np.int32)
     w = rng.random((B, k)).astype(np.float32)
     _check(x, ids, w, synth.int4(rng, E, 2 * I, H), synth.int4(rng, E, H, I), "bf16")
+
+
+@pytest.mark.parametrize("fmt,act,H,I", [("mxfp4", "f16", 4096, 2048), ("q8_0", "bf16", 1024, 512),
+                                         ("iq2_xxs", "f16", 1024, 512)])
+def test_gemv_generic_single_token(fmt, act, H, I):
+    # one token per call takes the one-token-per-pass kernels; the token names
+    # expert 3 twice (two passes over its weights)
+    rng = np.random.default_rng(len(fmt) + H)
+    E, k = 8, 6
+    x = synth.activations(rng, 1, H, act)
+    ids = np.array([[3, 5, 3, 0, 1, 7]], np.int32)
+    w = rng.random((1, k)).astype(np.float32)
+    Wgu = synth.weights(fmt, rng, E, 2 * I, H)
+    Wd = synth.weights(fmt if fmt != "iq2_xxs" else "q2_k", rng, E, H, I)
+    _check(x, ids, w, Wgu, Wd, act)

@@ -98,3 +98,38 @@ def test_graph_prefill_sequence_replays():
         # other eager work between replays
         qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU)
         torch.cuda.synchronize()
+
+
+def test_graph_prefill_store_combine_replays():
+    # the bench's prefill step: plan, gate/up SwiGLU, down STORE per pair,
+    # deterministic combine -- every replay bit-identical to the eager run
+    inp = synth.qwen_a3b_prefill(256, E=32)
+    T, k, E, H, I = inp.T, inp.k, inp.E, inp.H, inp.I
+    bm = 80
+    x = torch_act(inp.x, "bf16")
+    ids = torch.from_numpy(inp.ids).cuda()
+    w = torch.from_numpy(inp.w).cuda()
+    gu, dn = upload(inp.w_gate_up), upload(inp.w_down)
+    plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device="cuda")
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        qm.moe_plan(ids, E, bm, plan=plan)
+        qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
+        qm.moe_gather_qmm(dn, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE, out=y)
+        qm.moe_combine(y, plan, T, k, E, w, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = _capture(step)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        plan.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU)
+        torch.cuda.synchronize()
