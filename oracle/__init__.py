@@ -22,7 +22,8 @@ Sources (web pages the method is described on):
           the GPU MoE router top-K and the expert-indexed int4 GEMV
           ([nExperts, outDim, inDim/8] u32 weights with scales and biases),
           and the fused swiglu commit (silu(g) * u).
-          Also the MXFP4 dequant commit (OCP MX v1.0 blocks).
+          Also the MXFP4 dequant commit (OCP MX v1.0 blocks) and the FP8
+          block dequant commit (E4M3 bytes, fp32 scale per 128 x 128).
   [SHIM]  "WIP: metaltile shim -- Qwen3.6 mt_qmm_mma / mt_moe_gather dispatch
           from VLLMBridge", PR body (dense qmm smoke cell M=32 N=256 K=2048).
 
@@ -50,7 +51,7 @@ import numpy as np
 __all__ = [
     "f16_to_f64", "bf16_to_f64", "act_to_f64", "round_f16", "round_bf16",
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
-    "e2m1_value", "e8m0_scale", "dequant_mxfp4",
+    "e2m1_value", "e8m0_scale", "dequant_mxfp4", "e4m3_value", "dequant_fp8_block",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
     "router_topk_softmax", "router_sqrtsoftplus", "gated_shared_residual", "combine_pairs",
@@ -237,10 +238,38 @@ def dequant_mxfp4(blocks: np.ndarray) -> np.ndarray:
         return (e2m1_value(codes) * e8m0_scale(e)[..., None]).astype(np.float32)
 
 
+def e4m3_value(byte) -> np.ndarray:
+    """FP8 E4M3 [GGUF, the DSv4 FP8 block dequant commit]: bit 7 sign, bits
+    6-3 exponent with bias 7, bits 2-0 mantissa; exponent 0 is subnormal
+    (m/8 * 2^-6); 0x7F and 0xFF are NaN; the largest magnitude is 448.
+    uint8 [...] -> fp64 [...]."""
+    b = np.asarray(byte, dtype=np.int64)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, np.exp2(e - 7.0) * (1.0 + m / 8.0))
+    v = np.where(b & 0x80, -mag, mag)
+    return np.where((b & 0x7F) == 0x7F, np.nan, v)
+
+
+def dequant_fp8_block(w: np.ndarray, scales: np.ndarray, row_block: int = 128) -> np.ndarray:
+    """FP8 block weights [GGUF, the DSv4 FP8 block dequant commit]: one E4M3
+    byte per weight and one fp32 scale per 128 x 128 block;
+    out[i, j] = e4m3(w[i, j]) * scales[i/128, j/128], the product rounded once
+    in fp32.  w uint8 [..., N, K], scales fp32 [..., N/row_block, K/128]
+    (row_block 1: one scale row per weight row, for a selection of rows)
+    -> fp32 [..., N, K]."""
+    v = e4m3_value(w).astype(np.float32)        # exact: 4 significant bits
+    s = np.repeat(np.repeat(np.asarray(scales, np.float32), row_block, axis=-2), 128, axis=-1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return (v * s).astype(np.float32)
+
+
 def dequant(W) -> np.ndarray:
     """Whole weight tensor (a synth.QWeights) -> fp32 [E, N, K]."""
     if W.fmt == "int4":
         return dequant_int4(W.qs, W.scale, W.bias, W.group)
+    if W.fmt == "fp8":
+        return dequant_fp8_block(W.qs, W.scale, W.group)
     if W.fmt == "q8_0":
         v = dequant_q8_0(W.blocks)
     elif W.fmt == "q2_k":

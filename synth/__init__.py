@@ -78,9 +78,10 @@ def bf16_bits(a) -> np.ndarray:
 class QWeights:
     """A stacked expert weight tensor W[E, N, K] in its on-disk form.
 
-    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "mxfp4" | "int4".
+    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "mxfp4" | "int4" | "fp8".
     blocks: uint8 [E, N, K/block, block_bytes] for the GGUF-style formats.
-    qs/scale/bias: int4 arrays (uint32 [E,N,K/8], uint16 fp16 bits [E,N,K/group]).
+    qs/scale/bias: int4 arrays (uint32 [E,N,K/8], uint16 fp16 bits [E,N,K/group]);
+    for fp8, qs uint8 E4M3 bytes [E,N,K] and scale fp32 [E,N/128,K/128].
     grid: uint8 [256, 8] magnitude table (IQ2_XXS only).
     """
     fmt: str
@@ -98,6 +99,10 @@ class QWeights:
     def expert_rows(self, e: int, rows) -> "QWeights":
         """A view restricted to expert e and the given output rows (E=1)."""
         rows = np.asarray(rows)
+        if self.fmt == "fp8":
+            # group = weight rows per scale row: 1 here (one scale row per selected row)
+            return QWeights("fp8", 1, len(rows), self.K, 1, qs=self.qs[e, rows][None],
+                            scale=self.scale[e, rows // 128][None])
         if self.fmt == "int4":
             return QWeights("int4", 1, len(rows), self.K, self.group,
                             qs=self.qs[e, rows][None], scale=self.scale[e, rows][None],
@@ -107,6 +112,8 @@ class QWeights:
 
     @property
     def nbytes(self) -> int:
+        if self.fmt == "fp8":
+            return int(self.qs.nbytes + self.scale.nbytes)
         if self.fmt == "int4":
             return int(self.qs.nbytes + self.scale.nbytes + self.bias.nbytes)
         return int(self.blocks.nbytes)
@@ -187,8 +194,22 @@ def mxfp4(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
     return QWeights("mxfp4", E, N, K, MXFP4_BLOCK, blocks=blocks)
 
 
+def fp8(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
+    """FP8 E4M3 block weights: bytes with exponent fields 4..10 (magnitudes
+    1/8 .. 15) and random signs and mantissas (no NaN codes), and fp32 scales
+    |N(0, 0.02)| / 8 per 128 x 128 block."""
+    assert N % 128 == 0 and K % 128 == 0
+    e = rng.integers(4, 11, size=(E, N, K), dtype=np.uint8)
+    m = rng.integers(0, 8, size=(E, N, K), dtype=np.uint8)
+    s = rng.integers(0, 2, size=(E, N, K), dtype=np.uint8)
+    qs = (s << 7) | (e << 3) | m
+    scale = (_absn(rng, (E, N // 128, K // 128), 0.02) / np.float32(8.0)).astype(np.float32)
+    return QWeights("fp8", E, N, K, 128, qs=qs, scale=scale)  # group: weight rows per scale row
+
+
 def weights(fmt: str, rng, E, N, K, **kw) -> QWeights:
-    return {"q8_0": q8_0, "q2_k": q2_k, "iq2_xxs": iq2_xxs, "mxfp4": mxfp4, "int4": int4}[fmt](rng, E, N, K, **kw)
+    return {"q8_0": q8_0, "q2_k": q2_k, "iq2_xxs": iq2_xxs, "mxfp4": mxfp4, "int4": int4,
+            "fp8": fp8}[fmt](rng, E, N, K, **kw)
 
 
 # ---------------------------------------------------------------------------
