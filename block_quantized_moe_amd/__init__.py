@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
 # enums mirrored from include/qmoe.h
 F32, F16, BF16 = 0, 1, 2
-Q8_0, Q2_K, IQ2_XXS, INT4, MXFP4 = 0, 1, 2, 3, 4
+Q8_0, Q2_K, IQ2_XXS, INT4, MXFP4, FP8 = 0, 1, 2, 3, 4, 5
 EPI_STORE, EPI_SWIGLU, EPI_WEIGHTED_COMBINE, EPI_ACCUMULATE = 0, 1, 2, 3
 A_GATHER_TOKENS, A_SORTED_ROWS = 0, 1
 ROUTER_SOFTMAX, ROUTER_SQRTSOFTPLUS = 0, 1
-FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4, "mxfp4": MXFP4}
+FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4, "mxfp4": MXFP4, "fp8": FP8}
 MAX_TOPK, MAX_EXPERTS, MAX_GEMV_BATCH = 8, 1024, 64
 
 
@@ -51,6 +51,9 @@ _SIGS = {
     "qmoe_split_mxfp4": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
     "qmoe_dequant_mxfp4": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                                                     ctypes.c_void_p],
+    "qmoe_split_fp8": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p],
+    "qmoe_dequant_fp8": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                  ctypes.c_void_p],
     "qmoe_split_int4": [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "qmoe_iq2_signs_table": [ctypes.c_void_p],
     "qmoe_dequant_q8_0": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -172,6 +175,16 @@ def split_mxfp4(aos: np.ndarray, rows: int, k: int):
     return qs, e
 
 
+def split_fp8(w: np.ndarray, rows: int, k: int):
+    """FP8 E4M3 codes [rows, k] -> tiled codes (the fp32 block scales need no split)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    if w.size != rows * k:
+        raise QmoeError("split_fp8: code count does not match rows/k")
+    qs = np.empty(rows * k, np.uint8)
+    _check(lib().qmoe_split_fp8(_np_ptr(w), rows, k, _np_ptr(qs)), "split_fp8")
+    return qs
+
+
 def split_int4(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, rows: int, k: int, group: int):
     """MLX-style int4 rows -> (tiled code words, packed scale|bias<<16 words)."""
     words = np.ascontiguousarray(words, dtype=np.uint32).reshape(-1)
@@ -237,7 +250,8 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
     """Split on-disk weights on the host (library splitter) and copy them to the device.
 
     blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs / mxfp4.
-    qs, scale, bias: MLX-style int4 arrays for int4.  grid: uint8 [256, 8] (iq2_xxs)."""
+    qs, scale, bias: MLX-style int4 arrays for int4; for fp8, qs uint8 E4M3 codes
+    [E, N, K] and scale fp32 [E, N/128, K/128].  grid: uint8 [256, 8] (iq2_xxs)."""
     t = {}
     if fmt == "q8_0":
         q, d = split_q8_0(blocks, E * N, K)
@@ -253,6 +267,9 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
     elif fmt == "mxfp4":
         q, e = split_mxfp4(blocks, E * N, K)
         t["qs"], t["scales"] = _dev(q, device), _dev(e, device)
+    elif fmt == "fp8":
+        t["qs"] = _dev(split_fp8(qs, E * N, K), device)
+        t["scales"] = _dev(np.ascontiguousarray(scale, np.float32).reshape(-1), device)
     elif fmt == "int4":
         q, sb = split_int4(qs, scale, bias, E * N, K, group)
         t["qs"], t["scales"] = _dev(q, device), _dev(sb, device)
@@ -298,6 +315,8 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
     elif w.fmt == "iq2_xxs":
         st = L.qmoe_dequant_iq2_xxs(_ptr(t["qs"]), _ptr(t["d"]), _ptr(t["grid"]), _ptr(t["signs"]),
                                     w.E * w.N, w.K, _ptr(out), out_dtype, s)
+    elif w.fmt == "fp8":
+        st = L.qmoe_dequant_fp8(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
     elif w.fmt == "mxfp4":
         st = L.qmoe_dequant_mxfp4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
     else:

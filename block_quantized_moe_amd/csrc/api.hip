@@ -16,6 +16,7 @@ void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const
 void launch_dequant_iq2_xxs(const uint32_t*, const uint16_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
                             void*, int, hipStream_t);
 void launch_dequant_mxfp4(const uint32_t*, const uint8_t*, int64_t, int64_t, void*, int, hipStream_t);
+void launch_dequant_fp8(const uint8_t*, const float*, int64_t, int64_t, void*, int, hipStream_t);
 void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
                          hipStream_t);
 void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
@@ -93,6 +94,12 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       if (!w->scales) return QMOE_ERR_ARG;
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
+    case QMOE_FP8:
+      // one scale per 128 x 128 block: scale rows follow expert * n / 128 + row / 128
+      if (w->k % 128 || w->n % 128) return QMOE_ERR_BLOCK;
+      if (!w->scales) return QMOE_ERR_ARG;
+      if (!al16(w->scales)) return QMOE_ERR_ALIGN;
+      break;
     case QMOE_INT4:
       if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
       if (w->k % w->group || w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
@@ -153,6 +160,17 @@ int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
   launch_dequant_mxfp4(qs, e, rows, k, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_fp8(const uint8_t* qs, const float* scales, int64_t rows, int64_t k, void* out,
+                     int32_t out_dtype, void* stream) {
+  if (!qs || !scales || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (rows % 128 || k % 128) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(scales) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_fp8(qs, scales, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
 

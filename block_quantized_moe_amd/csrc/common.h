@@ -12,6 +12,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
@@ -150,6 +151,22 @@ __device__ __forceinline__ u4_t fp4x8_pairs(uint32_t q) {
   // pair (2j, 2j+1) = [lo(2j), hi(2j), lo(2j+1), hi(2j+1)]
   return u4_t{perm_b32(h0, l0, 0x05010400u), perm_b32(h0, l0, 0x07030602u),
               perm_b32(h1, l1, 0x05010400u), perm_b32(h1, l1, 0x07030602u)};
+}
+
+// ---------------------------------------------------------------- FP8 E4M3
+
+// Four E4M3 codes (byte i = element i) -> two packed pairs of fp16 (ACT_F16)
+// or bf16 values, elements (0, 1) and (2, 3), with the hardware conversion
+// at scale 1.  Exact: an E4M3 value has 4 significant bits and its exponent
+// range (2^-9 .. 448) lies inside both formats'; 0x7F / 0xFF give NaN.
+template <int ACT>
+__device__ __forceinline__ u2_t fp8x4_pairs(uint32_t q) {
+  if constexpr (ACT == ACT_F16)
+    return u2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, true))};
+  else
+    return u2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, true))};
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -172,6 +172,35 @@ __global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint32_t* __re
   }
 }
 
+// FP8 block weights: value = e4m3(code) * scale of the 128 x 128 block (the
+// GGUF page's FP8 block dequant commit).  The code converts exactly to fp32
+// (v_cvt_pk_f32_fp8, OCP E4M3 on gfx950, 0x7F / 0xFF NaN) and the product
+// rounds once.  Codes tiled like Q8_0's; unit u is values 8(u % (k/8)) .. +7
+// of row R = u / (k/8).
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t* __restrict__ qs,
+                                                          const float* __restrict__ scales,
+                                                          int64_t n_units, int64_t k, void* __restrict__ out) {
+  const int64_t upr = k / 8, KT = k / 64;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t R = u / upr, kk = 8 * (u - R * upr);
+    const int64_t rb = R >> 4, r = R & 15, kt = kk >> 6, c = (kk & 63) >> 4;
+    const u2_t q = *(const u2_t*)(qs + (((rb * KT + kt) * 4 + c) * 16 + r) * 16 + (kk & 15));
+    const float s = scales[(R >> 7) * (k >> 7) + (kk >> 7)];
+    float v[8];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], false);
+      const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], true);
+      v[4 * w + 0] = lo[0] * s;
+      v[4 * w + 1] = lo[1] * s;
+      v[4 * w + 2] = hi[0] * s;
+      v[4 * w + 3] = hi[1] * s;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
 #define QMOE_DISPATCH_OUT(dtype, KERNEL, ...)                                         \
   do {                                                                                \
     if ((dtype) == QMOE_F32) hipLaunchKernelGGL(KERNEL<QMOE_F32>, __VA_ARGS__);       \
@@ -202,6 +231,11 @@ void launch_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, in
                           int dtype, hipStream_t s) {
   const int64_t units = rows * (k / 8);
   QMOE_DISPATCH_OUT(dtype, dequant_mxfp4_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, e, units, k, out);
+}
+void launch_dequant_fp8(const uint8_t* qs, const float* sc, int64_t rows, int64_t k, void* out, int dtype,
+                        hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_fp8_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc, units, k, out);
 }
 void launch_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k, int group,
                          void* out, int dtype, hipStream_t s) {

@@ -139,6 +139,12 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
     const uint8_t* e = (const uint8_t*)g.scales + (rb * (K / 32) + k0 / 32) * 16 + rr;
     r.x0 = e[0];
     r.x2 = e[16];
+  } else if constexpr (FMT == QMOE_FP8) {
+    // codes tiled like Q8_0 (chunk c of row r at byte 256c + 16r of the 1 KB
+    // tile); the tile lies inside one 128 x 128 scale block
+    const int64_t rb = R >> 4, rr = R & 15;
+    r.v = *(const u4_t*)((const uint8_t*)g.qs + (rb * (K / 64) + k0 / 64) * 1024 + 16 * rr + 256 * lg);
+    r.x0 = __builtin_bit_cast(uint32_t, ((const float*)g.scales)[(R >> 7) * (K >> 7) + (k0 >> 7)]);
   } else if constexpr (FMT == QMOE_Q2_K) {
     // tiled layout: t = 16-row block * K/256 + super-block; a wave's loads of
     // one 16-row block read contiguous runs
@@ -349,6 +355,41 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
             const float ds = st ? d1 : d0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(ds, t[r], acc[m][b][r]);
+          }
+        }
+      }
+    } else if constexpr (FMT == QMOE_FP8) {
+      // chunk order, either activation type: the E4M3 values enter the MFMA
+      // exactly and the block scale multiplies the tile's fp32 partial sum.
+      // Column blocks two at a time (A fragments read from LDS once per
+      // pair), which keeps the converted operands within the register budget.
+      typedef typename ActT<ACT>::v8 V8;
+#pragma unroll
+      for (int hp = 0; hp < NB; hp += 2) {
+        u4_t cc[2][2];
+        float sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const u2_t p0 = fp8x4_pairs<ACT>(rw[hp + j].v[2 * st]);
+            const u2_t p1 = fp8x4_pairs<ACT>(rw[hp + j].v[2 * st + 1]);
+            cc[j][st] = u4_t{p0[0], p0[1], p1[0], p1[1]};
+          }
+          sc[j] = __builtin_bit_cast(float, rw[hp + j].x0);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          if (m >= c.mbn) break;
+          const uint16_t* ar = Ab + (16 * m + lr) * LDA + 16 * lg;
+          const V8 a0 = __builtin_bit_cast(V8, *(const u4_t*)ar);
+          const V8 a1 = __builtin_bit_cast(V8, *(const u4_t*)(ar + 8));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            f4_t t = mfma(a0, __builtin_bit_cast(V8, cc[j][0]), f4_t{0, 0, 0, 0});
+            t = mfma(a1, __builtin_bit_cast(V8, cc[j][1]), t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][hp + j][r] = __builtin_fmaf(sc[j], t[r], acc[m][hp + j][r]);
           }
         }
       }
@@ -1186,6 +1227,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     case QMOE_Q2_K: launch_f<QMOE_Q2_K>(g, act, epi, s); break;
     case QMOE_IQ2_XXS: launch_f<QMOE_IQ2_XXS>(g, act, epi, s); break;
     case QMOE_MXFP4: launch_f<QMOE_MXFP4>(g, act, epi, s); break;
+    case QMOE_FP8: launch_f<QMOE_FP8>(g, act, epi, s); break;
     default: launch_f<QMOE_INT4>(g, act, epi, s); break;
   }
 }

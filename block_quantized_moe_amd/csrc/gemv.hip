@@ -168,6 +168,32 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
         res[t] += dd * p;
       }
     }
+  } else if constexpr (FMT == QMOE_FP8) {
+    // codes tiled like Q8_0: chunks 2(c&1), 2(c&1)+1 of k tile c/2; one
+    // fp32 scale per 128 x 128 block
+    const int64_t rb = R >> 4, rr = R & 15;
+    const uint8_t* base = (const uint8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
+    const u4_t q0 = *(const u4_t*)base;
+    const u4_t q1 = *(const u4_t*)(base + 256);
+    const float dd = ((const float*)g.scales)[(R >> 7) * (K >> 7) + (c >> 2)];
+    uint32_t cp[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u2_t p0 = fp8x4_pairs<ACT>(q0[w]), p1 = fp8x4_pairs<ACT>(q1[w]);
+      cp[2 * w] = p0[0];
+      cp[2 * w + 1] = p0[1];
+      cp[8 + 2 * w] = p1[0];
+      cp[8 + 2 * w + 1] = p1[1];
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        res[t] += dd * p;
+      }
+    }
   } else if constexpr (FMT == QMOE_Q2_K) {
     // tiled layout: t = (R/16) * (K/256) + super-block, row r = R % 16
     const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
@@ -839,6 +865,7 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
     case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;
     case QMOE_IQ2_XXS: launch_gemv_f<QMOE_IQ2_XXS>(g, act, cpl, epi, units, s); break;
     case QMOE_MXFP4: launch_gemv_f<QMOE_MXFP4>(g, act, cpl, epi, units, s); break;
+    case QMOE_FP8: launch_gemv_f<QMOE_FP8>(g, act, cpl, epi, units, s); break;
     default: launch_gemv_f<QMOE_INT4>(g, act, cpl, epi, units, s); break;
   }
   return QMOE_OK;

@@ -35,6 +35,23 @@ int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16
   return QMOE_OK;
 }
 
+// FP8 block weights: E4M3 codes [rows][k], one byte per weight, tiled like
+// the Q8_0 codes ([R/16][k/64][4][16][16]: chunk c of 16 values of row
+// 16 rb + r in k tile kt).  The fp32 block scales [rows/128][k/128] are used
+// as they are.
+int qmoe_split_fp8(const uint8_t* w, int64_t rows, int64_t k, uint8_t* qs) {
+  if (!w || !qs || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (rows % 128 || k % 128) return QMOE_ERR_BLOCK;
+  const int64_t KT = k / 64;
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t kt = 0; kt < KT; ++kt)
+      for (int c = 0; c < 4; ++c)
+        memcpy(&qs[(((rb * KT + kt) * 4 + c) * 16 + r) * 16], w + R * k + 64 * kt + 16 * c, 16);
+  }
+  return QMOE_OK;
+}
+
 // MXFP4: 17-byte blocks (E8M0 exponent, 16 code bytes with element 2i in the
 // low nibble of byte i).  Codes tiled as u32 [R/16][k/64][2][16][4]: word w
 // of block j of row 16 rb + r holds elements 8w .. 8w+7 with element 8w+i in

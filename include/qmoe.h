@@ -12,7 +12,10 @@
  * Sources (web pages the method is described on):
  *   [GGUF]  "feat(gguf,dsv4): GGUF block-dequant + DSv4 kernel surface (WIP)":
  *           PR body, "Design -- CPU-side decomposition", "Kernels" 1-3, "Next"
- *           item 2, and the commit fixing IQ2_XXS sign reconstruction.
+ *           item 2, the commit fixing IQ2_XXS sign reconstruction, the
+ *           MXFP4 dequant commit ("Format") and the FP8 block dequant
+ *           commit (E4M3 bytes, fp32 scale per 128 x 128 block; the fused
+ *           FP8 block GEMV named there as the follow-up).
  *   [DSV4]  "metal: DSV4 M1 Ultra prefill/decode campaign": PR body (map0
  *           work queue, 64-slot iq2_xxs tile, q2_K SoA down twin, sum-folded
  *           q2_K down, load-time q2_K SoA repack) and the review-fix commit
@@ -61,7 +64,8 @@ typedef enum {
   QMOE_IQ2_XXS = 2,  /* 256-value super-blocks, grid index + 7-bit sign
                         groups with an even-parity 8th sign, 4-bit scale [GGUF Kernels 3] */
   QMOE_INT4 = 3,     /* MLX-style affine int4: s*q + b per group         [BAGEL]          */
-  QMOE_MXFP4 = 4     /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 values [GGUF MXFP4]     */
+  QMOE_MXFP4 = 4,    /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 values [GGUF MXFP4]     */
+  QMOE_FP8 = 5       /* FP8 E4M3 bytes, fp32 scale per 128 x 128 block   [GGUF FP8 block] */
 } qmoe_format;
 
 /* Epilogues of the matmul entry points. */
@@ -137,6 +141,15 @@ enum {
  *                   nibble of byte i, element 8w+4+i in its high nibble
  *            scales u8  [R/16][k/32][16]        E8M0 exponent e of each block
  *            group  ignored (32)
+ *   FP8      value = e4m3(code) * scale of its 128 x 128 block (E4M3: sign,
+ *            4 exponent bits with bias 7, 3 mantissa bits, 0x7F / 0xFF NaN,
+ *            largest magnitude 448), the product rounded once in fp32.  n
+ *            and k multiples of 128; codes tiled by qmoe_split_fp8:
+ *            qs     u8  [R/16][k/64][4][16][16]     chunk c (16 values at
+ *                   64kt + 16c) of row 16rb + r (the Q8_0 code tiling)
+ *            scales f32 [R/128][k/128]          block scales, the on-disk
+ *                   [E][n/128][k/128] array unchanged
+ *            group  ignored (128)
  */
 typedef struct qmoe_weights {
   int32_t fmt;          /* qmoe_format                                    */
@@ -180,6 +193,11 @@ int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint
                     uint16_t* d, uint16_t* dmin);
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint16_t* d);
 int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e);
+/* FP8 block weights ([GGUF] FP8 block dequant commit: one E4M3 byte per
+ * weight, row-major [rows][k], and one fp32 scale per 128 x 128 block) ->
+ * the tiled code array above (rows*k bytes); the scales need no split.
+ * QMOE_ERR_BLOCK unless rows and k are multiples of 128. */
+int qmoe_split_fp8(const uint8_t* w, int64_t rows, int64_t k, uint8_t* qs);
 /* int4 slabs from the on-disk (MLX) form -- words [rows][k/8] with element
  * 8w+i in nibble i of word w, fp16 scales and biases [rows][k/group] -- to the
  * tiled GPU form above: every wave-wide weight load is one contiguous 512-byte
@@ -215,6 +233,11 @@ int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int6
                       int32_t group, void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k,
                        void* out, int32_t out_dtype, void* stream);
+/* FP8 block weights ([GGUF] FP8 block dequant commit): qs tiled as in
+ * qmoe_weights, scales fp32 [rows/128][k/128]; rows and k multiples of 128
+ * (else QMOE_ERR_BLOCK).  0x7F / 0xFF decode to NaN. */
+int qmoe_dequant_fp8(const uint8_t* qs, const float* scales, int64_t rows, int64_t k,
+                     void* out, int32_t out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dense quantised matmul ([SHIM] mt_qmm_mma; [DSV4] wide-tile q8_0 qgemm):

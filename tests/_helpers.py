@@ -35,6 +35,8 @@ def to_f64(t, dtype: str | None = None) -> np.ndarray:
 def upload(W, device="cuda") -> "qm.DeviceWeights":
     if W.fmt == "int4":
         return qm.upload("int4", W.E, W.N, W.K, device=device, qs=W.qs, scale=W.scale, bias=W.bias, group=W.group)
+    if W.fmt == "fp8":
+        return qm.upload("fp8", W.E, W.N, W.K, device=device, qs=W.qs, scale=W.scale)
     return qm.upload(W.fmt, W.E, W.N, W.K, device=device, blocks=W.blocks, grid=W.grid)
 
 

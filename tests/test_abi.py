@@ -106,6 +106,21 @@ def test_split_mxfp4_tiled_layout():
         qm.split_mxfp4(W.blocks[:, :8], 8 * 2 // 2, k)
 
 
+def test_split_fp8_tiled_layout():
+    """Every code lands where the header's tiled layout says (the Q8_0 code tiling)."""
+    rows, k = 256, 384
+    W = synth.fp8(np.random.default_rng(4), 2, rows // 2, k)
+    qs = qm.split_fp8(W.qs, rows, k).reshape(rows // 16, k // 64, 4, 16, 16)
+    w = W.qs.reshape(rows, k)
+    for R in range(0, rows, 7):
+        for kk in range(k):
+            assert qs[R // 16, kk // 64, (kk % 64) // 16, R % 16, kk % 16] == w[R, kk]
+    with pytest.raises(qm.QmoeError):
+        qm.split_fp8(W.qs[:1, :64], 64, k)             # rows not a multiple of 128
+    with pytest.raises(qm.QmoeError):
+        qm.split_fp8(W.qs[..., :192], rows, 192)      # k not a multiple of 128
+
+
 def test_split_int4_tiled_layout():
     """Every element of the MLX rows lands where the header's tiled layout says."""
     rng = np.random.default_rng(3)
@@ -180,6 +195,14 @@ def test_argument_validation_before_launch():
     P16 = ctypes.c_void_p(16)
     assert L.qmoe_dequant_q2_k(P16, P16, P16, P16, 8, 256, P16, 1, None) == -3
     assert L.qmoe_dequant_iq2_xxs(P16, P16, P16, P16, 16, 128, P16, 1, None) == -3
+    # FP8: rows and k multiples of the 128 x 128 scale block; scales required
+    assert L.qmoe_dequant_fp8(P16, P16, 64, 128, P16, 1, None) == -3
+    assert L.qmoe_dequant_fp8(P16, P16, 128, 192, P16, 1, None) == -3
+    assert L.qmoe_dequant_fp8(P16, None, 128, 128, P16, 1, None) == E
+    w = qm._Weights(qm.FP8, 2, 64, 256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)   # n not a multiple of 128
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -3
+    w = qm._Weights(qm.FP8, 1, 128, 256, 0, 0, 16, 0, 0, 0, 0, 0, 0, 0)   # no scales
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == E
     # matmul: k not a block multiple, too many experts, wrong epilogue / dtype
     w = qm._Weights(qm.Q2_K, 1, 64, 320, 0, 0, 16, 0, 16, 0, 16, 16, 0, 0)
     assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -3

@@ -42,6 +42,8 @@ def _weights(fmt, rng):
         W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
     elif fmt == "mxfp4":
         W = synth.mxfp4(rng, 2, 40, 512)
+    elif fmt == "fp8":
+        W = synth.fp8(rng, 2, 128, 512)   # N and K multiples of the 128 x 128 scale block
     else:
         W = synth.q8_0(rng, 2, 40, 512)
     return W
@@ -63,6 +65,13 @@ def _plant_specials(W):
         for i, e in enumerate([255, 0, 254, 1, 253, 127]):  # NaN, 2^-127, past fp32 for |v| >= 2, ...
             W.blocks[0, i, 0, 0] = e
         W.blocks[0, 7, 2, 1:] = 0x88   # -0 codes
+    elif W.fmt == "fp8":
+        f = np.float32
+        for j, v in enumerate([f(np.nan), f(np.inf), f(1e-45), f(-0.0)]):
+            W.scale[0, 0, j] = v
+        W.scale[1, 0, 0] = f(3e38)                            # 3e38 * 448 overflows fp32
+        W.qs[0, 0, 0:4] = [0x7F, 0xFF, 0x80, 0x01]          # NaN, NaN, -0, smallest subnormal
+        W.qs[0, 1, 128:136] = [0x00, 0x07, 0x08, 0x7E, 0xFE, 0x87, 0x88, 0xF7]
     elif W.fmt == "iq2_xxs":
         W.blocks[0, 0, 0, 0:2] = h(0x7E00)
         W.blocks[0, 1, 0, 0:2] = h(0x0001)
@@ -75,7 +84,7 @@ def _plant_specials(W):
     return W
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_dequant_bit_exact(fmt, dtype):
     W = _plant_specials(_weights(fmt, np.random.default_rng(17)))
@@ -101,6 +110,24 @@ def test_dequant_mxfp4_every_code_and_exponent(dtype):
     torch.cuda.synchronize()
     ref32 = oracle.dequant(W)
     with np.errstate(over="ignore"):
+        ref = oracle.round_out(ref32, dtype) if dtype != "f32" else ref32
+    _bits_equal(out.reshape(-1), ref.reshape(-1), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dequant_fp8_every_code(dtype):
+    # all 256 E4M3 bytes in every row, under scales of 1, powers of two and random values
+    rng = np.random.default_rng(8)
+    W = synth.fp8(rng, 1, 256, 512)
+    W.qs[0] = (np.arange(512)[None, :] + 37 * np.arange(256)[:, None]) % 256
+    W.scale[0, 0, 0] = 1.0
+    W.scale[0, 0, 1] = 2.0 ** -20
+    W.scale[0, 1, 2] = 2.0 ** 10
+    code = {"f32": qm.F32, "f16": qm.F16, "bf16": qm.BF16}[dtype]
+    out = qm.dequant(upload(W), code)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref32 = oracle.dequant(W)
         ref = oracle.round_out(ref32, dtype) if dtype != "f32" else ref32
     _bits_equal(out.reshape(-1), ref.reshape(-1), dtype)
 

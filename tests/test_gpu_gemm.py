@@ -21,7 +21,7 @@ from _helpers import TOL, normwise_err, report, to_f64, torch_act, upload
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4"]
+FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8"]
 
 
 def _w(fmt, rng, E, N, K):
@@ -45,6 +45,8 @@ def test_dense_q8_0_smoke_cell():
 def test_dense_random_ragged(fmt, act):
     rng = np.random.default_rng(hash((fmt, act)) % 2**32)
     M, N, K = 45, 208, 512    # N: 13 blocks of 16 rows (the tiled layouts), not a multiple of the 256-row tile
+    if fmt == "fp8":
+        N = 384               # 3 rows of 128 x 128 scale blocks, still not a multiple of the 256-row tile
     W = _w(fmt, rng, 1, N, K)
     x = synth.activations(rng, M, K, act)
     ref = oracle.qmm(oracle.act_to_f64(x, act), W)
@@ -67,6 +69,11 @@ def _exact_weights(fmt, rng, E, N, K):
         W.blocks[..., 82:84] = h(1.0)
     elif fmt == "mxfp4":
         W.blocks[..., 0] = 128         # scale 2: values 0, +-1, +-2, +-3, +-4, +-6, +-8, +-12
+    elif fmt == "fp8":
+        # integer-valued E4M3 codes (+-1, 2, 3, 4, 6, 8) under power-of-two block scales
+        ints = np.array([0x38, 0x40, 0x44, 0x48, 0x4C, 0x50], np.uint8)
+        W.qs[...] = ints[rng.integers(0, 6, size=W.qs.shape)] | (rng.integers(0, 2, size=W.qs.shape) << 7).astype(np.uint8)
+        W.scale[...] = np.where(rng.random(W.scale.shape) < 0.5, 1.0, 2.0).astype(np.float32)
     elif fmt == "iq2_xxs":
         W.blocks[..., 0:2] = h(8.0)    # group scale 8 * (0.5 + s) / 4 = 1 + 2s
         W.grid = np.random.default_rng(1).choice(np.array([1, 2, 3], np.uint8), size=(256, 8))
@@ -80,7 +87,7 @@ def _exact_weights(fmt, rng, E, N, K):
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_dense_exact_integer_bit_exact(fmt, act):
     rng = np.random.default_rng(99)
-    M, N, K = 33, 144, 512
+    M, N, K = 33, (384 if fmt == "fp8" else 144), 512
     W = _exact_weights(fmt, rng, 1, N, K)
     xi = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
     x = synth.f16_bits(xi) if act == "f16" else synth.bf16_bits(xi)
@@ -89,6 +96,25 @@ def test_dense_exact_integer_bit_exact(fmt, act):
     y = qm.qmm_dense(upload(W), torch_act(x, act), qm.EPI_STORE, qm.F32)
     torch.cuda.synchronize()
     assert np.array_equal(to_f64(y), ref)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_dense_fp8_every_code_through_the_matmul(act):
+    # one-hot activation rows pick single weight columns: y[m, n] = e4m3(w[n, m]) * scale
+    # exactly, for every non-NaN E4M3 byte under several block scales
+    rng = np.random.default_rng(12)
+    N, K = 256, 256
+    W = synth.fp8(rng, 1, N, K)
+    codes = np.array([b for b in range(256) if b & 0x7F != 0x7F], np.uint8)
+    W.qs[0] = codes[(np.arange(K)[None, :] + 5 * np.arange(N)[:, None]) % codes.size]
+    W.scale[0] = np.array([[1.0, 2.0 ** -12], [2.0 ** 7, 0.0371]], np.float32)
+    one = 0x3C00 if act == "f16" else 0x3F80
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = one
+    y = qm.qmm_dense(upload(W), torch_act(x, act), qm.EPI_STORE, qm.F32)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(W)[0].T             # [K, N]: y[m, n] = w[n, m]
+    assert np.array_equal(to_f64(y), ref.astype(np.float64))
 
 
 def test_dense_swiglu_and_accumulate():
@@ -172,7 +198,8 @@ def _check_moe(x, ids, w, Wgu, Wd, act, **kw):
 @pytest.mark.parametrize("gu,dn,act", [("int4", "int4", "bf16"), ("int4", "int4", "f16"),
                                        ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
                                        ("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
-                                       ("mxfp4", "mxfp4", "bf16"), ("mxfp4", "mxfp4", "f16")])
+                                       ("mxfp4", "mxfp4", "bf16"), ("mxfp4", "mxfp4", "f16"),
+                                       ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16")])
 def test_moe_stagewise(gu, dn, act):
     x, ids, w, Wgu, Wd = _moe_case(gu, dn, act, seed=len(gu) + len(act))
     _check_moe(x, ids, w, Wgu, Wd, act)

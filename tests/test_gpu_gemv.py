@@ -56,7 +56,7 @@ def test_gemv_qwen_decode_int4_full_size(B):
 @pytest.mark.parametrize("gu,dn,act", [("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
                                        ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
                                        ("int4", "int4", "f16"), ("mxfp4", "mxfp4", "bf16"),
-                                       ("mxfp4", "mxfp4", "f16")])
+                                       ("mxfp4", "mxfp4", "f16"), ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16")])
 def test_gemv_formats(gu, dn, act):
     rng = np.random.default_rng(len(gu) * 7 + len(act))
     B, E, k, H, I = 4, 16, 4, 1024, 512
@@ -150,7 +150,7 @@ def test_gemv_int4_repeated_expert_within_token():
 
 
 @pytest.mark.parametrize("fmt,act,H,I", [("mxfp4", "f16", 4096, 2048), ("q8_0", "bf16", 1024, 512),
-                                         ("iq2_xxs", "f16", 1024, 512)])
+                                         ("iq2_xxs", "f16", 1024, 512), ("fp8", "bf16", 4096, 2048)])
 def test_gemv_generic_single_token(fmt, act, H, I):
     # one token per call takes the one-token-per-pass kernels; the token names
     # expert 3 twice (two passes over its weights)
