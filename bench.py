@@ -52,6 +52,8 @@ def act_tensor(torch, bits):
 def upload(qm, W):
     if W.fmt == "int4":
         return qm.upload("int4", W.E, W.N, W.K, qs=W.qs, scale=W.scale, bias=W.bias, group=W.group)
+    if W.fmt == "fp8":
+        return qm.upload("fp8", W.E, W.N, W.K, qs=W.qs, scale=W.scale)
     return qm.upload(W.fmt, W.E, W.N, W.K, blocks=W.blocks, grid=W.grid)
 
 
@@ -522,19 +524,19 @@ def main():
     }
     log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; kernels {json.dumps(kern)}")
     others = []
-    mx = None
+    decode_inputs = {}
     if not args.no_extra:
         import synth
-        mx = None
         for name, make, R in (("dsv4", lambda: synth.dsv4_flash_prefill(2048), 2),
                               ("dsv4 mxfp4", lambda: synth.dsv4_flash_mxfp4_prefill(2048), 2),
+                              ("dsv4 fp8", lambda: synth.dsv4_flash_fp8_prefill(2048), 2),
                               ("mixed", lambda: synth.mixed_ffn(8192), 2)):
             log(f"prefill ({name}): building inputs")
             inp_o = make()
             others.append(run_prefill_other(args, torch, qm, inp_o, R, max(3, args.steps // 4)))
             log(json.dumps(others[-1]))
-            if name == "dsv4 mxfp4":
-                mx = inp_o  # its weights also serve the MXFP4 decode lines
+            if name in ("dsv4 mxfp4", "dsv4 fp8"):
+                decode_inputs[name] = inp_o  # its weights also serve the decode lines of the format
             del inp_o
     log("router top-k")
     router = run_router(args, torch, qm)
@@ -545,14 +547,16 @@ def main():
             log(f"decode: B={B}")
             decode.append(run_decode(args, torch, qm, B, args.decode_layers))
             log(json.dumps(decode[-1]))
-        if not args.no_extra and mx is not None:
+        if not args.no_extra:
             import dataclasses
-            for B in (1, 4):
-                log(f"decode (dsv4 mxfp4): B={B}")
-                dec = dataclasses.replace(mx, name=f"dsv4-flash-mxfp4-decode-b{B}", T=B, x=mx.x[:B],
-                                          ids=mx.ids[:B], w=mx.w[:B])
-                decode.append(run_decode(args, torch, qm, B, max(2, args.decode_layers // 5), dec))
-                log(json.dumps(decode[-1]))
+            for name, src in decode_inputs.items():
+                fmt = name.split()[1]
+                for B in (1, 4):
+                    log(f"decode ({name}): B={B}")
+                    dec = dataclasses.replace(src, name=f"dsv4-flash-{fmt}-decode-b{B}", T=B, x=src.x[:B],
+                                              ids=src.ids[:B], w=src.w[:B])
+                    decode.append(run_decode(args, torch, qm, B, max(2, args.decode_layers // 5), dec))
+                    log(json.dumps(decode[-1]))
     cpu = None
     if not args.no_cpu:
         log("cpu baseline: oracle sample")

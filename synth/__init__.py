@@ -196,13 +196,16 @@ def mxfp4(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
 
 def fp8(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
     """FP8 E4M3 block weights: bytes with exponent fields 4..10 (magnitudes
-    1/8 .. 15) and random signs and mantissas (no NaN codes), and fp32 scales
-    |N(0, 0.02)| / 8 per 128 x 128 block."""
+    1/8 .. 15; field 4 + (r mod 7) of a uniform byte r, so nearly uniform) and
+    uniform signs and mantissas (no NaN codes), and fp32 scales |N(0, 0.02)| / 8
+    per 128 x 128 block.  Drawn one expert at a time (two uniform bytes per
+    weight) so full-size expert stacks stay quick to generate."""
     assert N % 128 == 0 and K % 128 == 0
-    e = rng.integers(4, 11, size=(E, N, K), dtype=np.uint8)
-    m = rng.integers(0, 8, size=(E, N, K), dtype=np.uint8)
-    s = rng.integers(0, 2, size=(E, N, K), dtype=np.uint8)
-    qs = (s << 7) | (e << 3) | m
+    qs = np.empty((E, N, K), np.uint8)
+    ex = ((4 + np.arange(256) % 7) << 3).astype(np.uint8)       # exponent field of byte r
+    for e in range(E):
+        r = np.frombuffer(rng.bytes(2 * N * K), np.uint8).reshape(2, N, K)
+        qs[e] = (r[0] & np.uint8(0x87)) | ex[r[1]]                 # sign and mantissa | exponent
     scale = (_absn(rng, (E, N // 128, K // 128), 0.02) / np.float32(8.0)).astype(np.float32)
     return QWeights("fp8", E, N, K, 128, qs=qs, scale=scale)  # group: weight rows per scale row
 
@@ -338,6 +341,13 @@ def dsv4_flash_mxfp4_prefill(T: int = 2048, **over) -> MoEInputs:
     """The DSv4-Flash expert shapes with its native MXFP4 expert weights."""
     fmt = dict(gate_up_fmt="mxfp4", down_fmt="mxfp4")
     return moe(5, T=T, name="dsv4-flash-mxfp4-prefill", **{**DSV4_FLASH, **fmt, **over})
+
+
+def dsv4_flash_fp8_prefill(T: int = 2048, **over) -> MoEInputs:
+    """The DSv4-Flash expert shapes with FP8 E4M3 block expert weights (the
+    DeepSeek V3 storage that V4 inherits: fp32 scale per 128 x 128 block)."""
+    fmt = dict(gate_up_fmt="fp8", down_fmt="fp8")
+    return moe(6, T=T, name="dsv4-flash-fp8-prefill", **{**DSV4_FLASH, **fmt, **over})
 
 
 def mixed_ffn(T: int = 8192, **over) -> MoEInputs:
