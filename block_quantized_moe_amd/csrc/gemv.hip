@@ -14,9 +14,10 @@
 //    dot2 instructions accumulate in fp32; a butterfly over the lanes of a row
 //    finishes each dot product.
 //  * gemv_combine_kernel (WEIGHTED_COMBINE): one workgroup per block of output
-//    rows; its four waves share out the distinct experts, each wave keeps
-//    per-token partial sums in LDS, and the waves' sums are added in a fixed
-//    order, so the result is bit-reproducible.
+//    rows; its four waves share out the distinct experts, each wave loads its
+//    tokens' activations once and walks the block's rows, keeps per-token
+//    partial sums in LDS, and the waves' sums are added in a fixed order, so
+//    the result is bit-reproducible.
 // Integer codes are fed to the dot products exactly (as fp16 / bf16 values
 // with a known offset) and the per-block scale and bias are applied to the
 // fp32 partial sums.
@@ -93,28 +94,83 @@ __device__ __forceinline__ void i8x4_pairs(uint32_t w, uint32_t& p0, uint32_t& p
   p1 = o[1];
 }
 
-// Dot products of one 32-value weight chunk (global row R, chunk c) with the
-// activations of nt tokens; results added to res[].
-template <int FMT, int ACT, int MT>
-__device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t c, const XChunk* x,
-                                          int nt, float* res, const uint32_t* lut_grid,
-                                          const uint32_t* lut_sign) {
+// The weight bytes of one 32-value chunk (global row R, chunk c), as loaded:
+// codes and the per-block metadata, unpacked later by chunk_math.  Loading
+// and arithmetic are separate so a kernel can put the loads of several rows
+// in flight before the first dot product.
+struct ChunkRaw {
+  u4_t q0, q1;
+  uint32_t m0, m1, m2, m3;
+};
+
+template <int FMT>
+__device__ __forceinline__ ChunkRaw chunk_load(const GemvArgs& g, int64_t R, int64_t c) {
   const int64_t K = g.K;
+  ChunkRaw w;
   if constexpr (FMT == QMOE_INT4) {
     // Tiled layout: chunk c of row R is lane groups 2(c&1), 2(c&1)+1 of tile (R/16, c/2).
     const int64_t rb = R >> 4, rr = R & 15;
     const uint32_t* tile = (const uint32_t*)g.qs + (rb * (K / 64) + (c >> 1)) * 128;
     const u2_t qa = *(const u2_t*)(tile + (32 * (c & 1) + rr) * 2);
     const u2_t qb = *(const u2_t*)(tile + (32 * (c & 1) + 16 + rr) * 2);
-    const u4_t q = u4_t{qa[0], qa[1], qb[0], qb[1]};
-    const uint32_t sbv = ((const uint32_t*)g.scales)[(rb * (K / g.group) + (32 * c) / g.group) * 16 + rr];
-    const float s = f16_to_f32(sbv & 0xFFFFu);
-    const float b = f16_to_f32(sbv >> 16);
+    w.q0 = u4_t{qa[0], qa[1], qb[0], qb[1]};
+    w.m0 = ((const uint32_t*)g.scales)[(rb * (K / g.group) + (32 * c) / g.group) * 16 + rr];
+  } else if constexpr (FMT == QMOE_Q8_0) {
+    // tiled layout: chunks 2(c&1), 2(c&1)+1 of k tile c/2, 16 bytes each per row
+    const int64_t rb = R >> 4, rr = R & 15;
+    const int8_t* base = (const int8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
+    w.q0 = *(const u4_t*)base;
+    w.q1 = *(const u4_t*)(base + 256);
+    w.m0 = ((const uint16_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr];
+  } else if constexpr (FMT == QMOE_FP8) {
+    // codes tiled like Q8_0: chunks 2(c&1), 2(c&1)+1 of k tile c/2; one
+    // fp32 scale per 128 x 128 block
+    const int64_t rb = R >> 4, rr = R & 15;
+    const uint8_t* base = (const uint8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
+    w.q0 = *(const u4_t*)base;
+    w.q1 = *(const u4_t*)(base + 256);
+    w.m0 = __builtin_bit_cast(uint32_t, ((const float*)g.scales)[(R >> 7) * (K >> 7) + (c >> 2)]);
+  } else if constexpr (FMT == QMOE_MXFP4) {
+    // tiled layout: chunk c is block c&1 of k tile c/2, 16 bytes per row
+    const int64_t rb = R >> 4, rr = R & 15;
+    w.q0 = *(const u4_t*)((const uint32_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 2 + (c & 1)) * 16 + rr) * 4);
+    w.m0 = ((const uint8_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr];
+  } else if constexpr (FMT == QMOE_Q2_K) {
+    // tiled layout: t = (R/16) * (K/256) + super-block, row r = R % 16
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
+    const int cc = (int)(c & 7);
+    const uint8_t* qb = (const uint8_t*)g.qs + ((t * 2 + (cc >> 2)) * 16 + r) * 32;
+    w.q0 = *(const u4_t*)qb;
+    w.q1 = *(const u4_t*)(qb + 16);
+    w.m0 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc];
+    w.m1 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc + 1];
+    w.m2 = ((const uint16_t*)g.d)[t * 16 + r];
+    w.m3 = ((const uint16_t*)g.dmin)[t * 16 + r];
+  } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8 (tiled layout)
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
+    const int G = (int)(c & 7);
+    const u2_t ia = *(const u2_t*)((const uint32_t*)g.qs + ((t * 8 + G) * 16 + r) * 2);
+    w.m0 = ia[0];
+    w.m1 = ia[1];
+    w.m2 = ((const uint16_t*)g.d)[t * 16 + r];
+  }
+  return w;
+}
+
+// Dot products of one loaded chunk (chunk c) with the activations of nt
+// tokens; results added to res[].
+template <int FMT, int ACT, int MT>
+__device__ __forceinline__ void chunk_math(const GemvArgs& g, const ChunkRaw& w, int64_t c, const XChunk* x,
+                                           int nt, float* res, const uint32_t* lut_grid,
+                                           const uint32_t* lut_sign) {
+  if constexpr (FMT == QMOE_INT4) {
+    const float s = f16_to_f32(w.m0 & 0xFFFFu);
+    const float b = f16_to_f32(w.m0 >> 16);
     uint32_t cp[16];
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cp[4 * w + i] = ((q[w] >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
+      for (int i = 0; i < 4; ++i) cp[4 * q + i] = ((w.q0[q] >> (4 * i)) & 0x000F000Fu) | Magic<ACT>::bits;
     const float cb = b - Magic<ACT>::v * s;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -125,65 +181,34 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
         res[t] += s * p + cb * (x[t].s0 + x[t].s1);
       }
     }
-  } else if constexpr (FMT == QMOE_Q8_0) {
-    // tiled layout: chunks 2(c&1), 2(c&1)+1 of k tile c/2, 16 bytes each per row
-    const int64_t rb = R >> 4, rr = R & 15;
-    const int8_t* base = (const int8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
-    const u4_t q0 = *(const u4_t*)base;
-    const u4_t q1 = *(const u4_t*)(base + 256);
-    const float dd = f16_to_f32(((const uint16_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr]);
+  } else if constexpr (FMT == QMOE_Q8_0 || FMT == QMOE_FP8 || FMT == QMOE_MXFP4) {
     uint32_t cp[16];
+    float dd;
+    if constexpr (FMT == QMOE_Q8_0) {
+      dd = f16_to_f32(w.m0);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      i8x4_pairs<ACT>(q0[w], cp[2 * w], cp[2 * w + 1]);
-      i8x4_pairs<ACT>(q1[w], cp[8 + 2 * w], cp[8 + 2 * w + 1]);
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (t < nt) {
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
-        res[t] += dd * p;
+      for (int q = 0; q < 4; ++q) {
+        i8x4_pairs<ACT>(w.q0[q], cp[2 * q], cp[2 * q + 1]);
+        i8x4_pairs<ACT>(w.q1[q], cp[8 + 2 * q], cp[8 + 2 * q + 1]);
       }
-    }
-  } else if constexpr (FMT == QMOE_MXFP4) {
-    // tiled layout: chunk c is block c&1 of k tile c/2, 16 bytes per row
-    const int64_t rb = R >> 4, rr = R & 15;
-    const u4_t q = *(const u4_t*)((const uint32_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 2 + (c & 1)) * 16 + rr) * 4);
-    const float dd = e8m0_to_f32(((const uint8_t*)g.scales)[(rb * (K / 32) + c) * 16 + rr]);
-    uint32_t cp[16];
+    } else if constexpr (FMT == QMOE_FP8) {
+      dd = __builtin_bit_cast(float, w.m0);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u4_t p = fp4x8_pairs<ACT>(q[w]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cp[4 * w + i] = p[i];
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (t < nt) {
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
-        res[t] += dd * p;
+      for (int q = 0; q < 4; ++q) {
+        const u2_t p0 = fp8x4_pairs<ACT>(w.q0[q]), p1 = fp8x4_pairs<ACT>(w.q1[q]);
+        cp[2 * q] = p0[0];
+        cp[2 * q + 1] = p0[1];
+        cp[8 + 2 * q] = p1[0];
+        cp[8 + 2 * q + 1] = p1[1];
       }
-    }
-  } else if constexpr (FMT == QMOE_FP8) {
-    // codes tiled like Q8_0: chunks 2(c&1), 2(c&1)+1 of k tile c/2; one
-    // fp32 scale per 128 x 128 block
-    const int64_t rb = R >> 4, rr = R & 15;
-    const uint8_t* base = (const uint8_t*)g.qs + (((rb * (K / 64) + (c >> 1)) * 4 + 2 * (c & 1)) * 16 + rr) * 16;
-    const u4_t q0 = *(const u4_t*)base;
-    const u4_t q1 = *(const u4_t*)(base + 256);
-    const float dd = ((const float*)g.scales)[(R >> 7) * (K >> 7) + (c >> 2)];
-    uint32_t cp[16];
+    } else {
+      dd = e8m0_to_f32(w.m0);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u2_t p0 = fp8x4_pairs<ACT>(q0[w]), p1 = fp8x4_pairs<ACT>(q1[w]);
-      cp[2 * w] = p0[0];
-      cp[2 * w + 1] = p0[1];
-      cp[8 + 2 * w] = p1[0];
-      cp[8 + 2 * w + 1] = p1[1];
+      for (int q = 0; q < 4; ++q) {
+        const u4_t p = fp4x8_pairs<ACT>(w.q0[q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cp[4 * q + i] = p[i];
+      }
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -195,28 +220,22 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       }
     }
   } else if constexpr (FMT == QMOE_Q2_K) {
-    // tiled layout: t = (R/16) * (K/256) + super-block, row r = R % 16
-    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
     const int cc = (int)(c & 7);
-    const uint8_t* qb = (const uint8_t*)g.qs + ((t * 2 + (cc >> 2)) * 16 + r) * 32;
-    const u4_t q0 = *(const u4_t*)qb;
-    const u4_t q1 = *(const u4_t*)(qb + 16);
     const uint32_t shift = 2u * (uint32_t)(cc & 3);
-    const uint32_t sc0 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc];
-    const uint32_t sc1 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc + 1];
-    const float d = f16_to_f32(((const uint16_t*)g.d)[t * 16 + r]);
-    const float dm = f16_to_f32(((const uint16_t*)g.dmin)[t * 16 + r]);
+    const uint32_t sc0 = w.m0, sc1 = w.m1;
+    const float d = f16_to_f32(w.m2);
+    const float dm = f16_to_f32(w.m3);
     const float dl0 = d * (float)(sc0 & 15u), ml0 = dm * (float)(sc0 >> 4);
     const float dl1 = d * (float)(sc1 & 15u), ml1 = dm * (float)(sc1 >> 4);
     uint32_t cp[16];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t t0 = (q0[w] >> shift) & 0x03030303u;
-      const uint32_t t1 = (q1[w] >> shift) & 0x03030303u;
-      cp[2 * w] = perm_b32(Magic<ACT>::byte, t0, 0x04010400u) & 0xFF03FF03u;
-      cp[2 * w + 1] = perm_b32(Magic<ACT>::byte, t0, 0x04030402u) & 0xFF03FF03u;
-      cp[8 + 2 * w] = perm_b32(Magic<ACT>::byte, t1, 0x04010400u) & 0xFF03FF03u;
-      cp[8 + 2 * w + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u) & 0xFF03FF03u;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t t0 = (w.q0[q] >> shift) & 0x03030303u;
+      const uint32_t t1 = (w.q1[q] >> shift) & 0x03030303u;
+      cp[2 * q] = perm_b32(Magic<ACT>::byte, t0, 0x04010400u) & 0xFF03FF03u;
+      cp[2 * q + 1] = perm_b32(Magic<ACT>::byte, t0, 0x04030402u) & 0xFF03FF03u;
+      cp[8 + 2 * q] = perm_b32(Magic<ACT>::byte, t1, 0x04010400u) & 0xFF03FF03u;
+      cp[8 + 2 * q + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u) & 0xFF03FF03u;
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -231,13 +250,10 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
                   dl1 * (p1 - Magic<ACT>::v * x[t].s1) - ml1 * x[t].s1;
       }
     }
-  } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8 (tiled layout)
-    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
-    const int G = (int)(c & 7);
-    const u2_t ia = *(const u2_t*)((const uint32_t*)g.qs + ((t * 8 + G) * 16 + r) * 2);
-    const uint32_t idx = ia[0];
-    const uint32_t aux = ia[1];
-    const float db = f16_to_f32(((const uint16_t*)g.d)[t * 16 + r]) * (0.5f + (float)(aux >> 28)) * 0.25f;
+  } else {  // IQ2_XXS
+    const uint32_t idx = w.m0;
+    const uint32_t aux = w.m1;
+    const float db = f16_to_f32(w.m2) * (0.5f + (float)(aux >> 28)) * 0.25f;
     uint32_t cp[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -256,6 +272,13 @@ __device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t 
       }
     }
   }
+}
+
+template <int FMT, int ACT, int MT>
+__device__ __forceinline__ void chunk_dot(const GemvArgs& g, int64_t R, int64_t c, const XChunk* x,
+                                          int nt, float* res, const uint32_t* lut_grid,
+                                          const uint32_t* lut_sign) {
+  chunk_math<FMT, ACT, MT>(g, chunk_load<FMT>(g, R, c), c, x, nt, res, lut_grid, lut_sign);
 }
 
 template <int ACT>
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
   const int lpr = g.lpr;
   const int rpw = 64 / lpr;                 // row units per wave pass
   const int sub = lane / lpr, li = lane % lpr;
-  const bool swiglu = (EPI == QMOE_EPI_SWIGLU);
+  constexpr bool swiglu = (EPI == QMOE_EPI_SWIGLU);
   const int64_t Nunits = swiglu ? g.N / 2 : g.N;
   const int64_t u0 = (int64_t)blockIdx.x * g.units_per_wg;
 
@@ -365,7 +388,17 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
   }
 }
 
-// WEIGHTED_COMBINE (sum-folded down projection).  grid = row blocks.
+// WEIGHTED_COMBINE (sum-folded down projection).  grid = row blocks of
+// GC_ITERS wave passes (GC_ITERS * 64 / lpr rows).  A wave takes distinct
+// experts; for each it loads the activation chunks of up to MT of the tokens
+// routed there once and then walks the block's rows with them (the row loop
+// is unrolled, so the weight loads of several rows are in flight together).
+// Per-token partial sums sit in LDS per wave and are added in wave order, so
+// the result is bit-reproducible.
+constexpr int GC_ITERS = 8;
+constexpr int GC_LOAD = 4;             // row passes whose weight loads are issued together
+constexpr int GC_ROWS = GC_ITERS * 4;  // rows per block at most (lpr >= 16)
+
 template <int FMT, int ACT, int CPL, int MT>
 __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
@@ -375,13 +408,13 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   __shared__ int first[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
   __shared__ int dlist[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
   __shared__ int ndist;
-  __shared__ float part[4][QMOE_MAX_GEMV_BATCH][4];  // [wave][token][row in block]
+  __shared__ float part[4][QMOE_MAX_GEMV_BATCH][GC_ROWS];  // [wave][token][row in block]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = g.nslots;
   if constexpr (IQ2) build_iq2_luts<ACT>(g.grid, g.signs, lut_grid, lut_sign);
   for (int p = tid; p < P; p += 256) sid[p] = g.ids[p];
-  for (int i = tid; i < 4 * QMOE_MAX_GEMV_BATCH * 4; i += 256) (&part[0][0][0])[i] = 0.f;
+  for (int i = tid; i < 4 * QMOE_MAX_GEMV_BATCH * GC_ROWS; i += 256) (&part[0][0][0])[i] = 0.f;
   __syncthreads();
   for (int p = tid; p < P; p += 256) {
     const int e = sid[p];
@@ -400,14 +433,11 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   const int lpr = g.lpr;
   const int rpw = 64 / lpr;
   const int sub = lane / lpr, li = lane % lpr;
-  const int64_t n0 = (int64_t)blockIdx.x * rpw;  // a workgroup covers one wave-pass of rows
-  const int64_t row = n0 + sub;
-  const bool valid = row < g.N;
-  const int64_t rc = valid ? row : 0;
+  const int rows_blk = GC_ITERS * rpw;
+  const int64_t n0 = (int64_t)blockIdx.x * rows_blk;
 
   for (int di = wave; di < ndist; di += 4) {
     const int e = sid[dlist[di]];
-    const int64_t Rg = (int64_t)e * g.N + rc;
     // tokens routed to e, in slot order, MT at a time
     int pos = dlist[di];
     while (pos < P) {
@@ -418,24 +448,40 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
         ++pos;
       }
       if (nt == 0) break;
-      float r[MT];
+      XChunk xc[CPL][MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) r[t] = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        XChunk xc[MT];
+      for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          if (t < nt) load_x<ACT>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[t]);
-        chunk_dot<FMT, ACT, MT>(g, Rg, li + c * lpr, xc, nt, r, lut_grid, lut_sign);
-      }
+          if (t < nt) load_x<ACT>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[c][t]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        if (t < nt) {
-          const float y = row_reduce(r[t], lpr);
-          if (li == 0) {
-            const int s2 = sl[t];
-            part[wave][s2 / g.topk][sub] += g.topk_w[s2] * y;
+      for (int i0 = 0; i0 < GC_ITERS; i0 += GC_LOAD) {
+        // the weight chunks of GC_LOAD row passes, all loads issued first
+        ChunkRaw wr[GC_LOAD][CPL];
+#pragma unroll
+        for (int i = 0; i < GC_LOAD; ++i) {
+          const int64_t row = n0 + (i0 + i) * rpw + sub;
+          const int64_t Rg = (int64_t)e * g.N + (row < g.N ? row : g.N - 1);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) wr[i][c] = chunk_load<FMT>(g, Rg, li + c * lpr);
+        }
+#pragma unroll
+        for (int i = 0; i < GC_LOAD; ++i) {
+          float r[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) r[t] = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            chunk_math<FMT, ACT, MT>(g, wr[i][c], li + c * lpr, xc[c], nt, r, lut_grid, lut_sign);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            if (t < nt) {
+              const float y = row_reduce(r[t], lpr);
+              if (li == 0) {
+                const int s2 = sl[t];
+                part[wave][s2 / g.topk][(i0 + i) * rpw + sub] += g.topk_w[s2] * y;
+              }
+            }
           }
         }
       }
@@ -443,8 +489,8 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   }
   __syncthreads();
   const int btok = P / g.topk;
-  for (int i = tid; i < btok * rpw; i += 256) {
-    const int b = i / rpw, r = i % rpw;
+  for (int i = tid; i < btok * rows_blk; i += 256) {
+    const int b = i / rows_blk, r = i % rows_blk;
     const int64_t n = n0 + r;
     if (n < g.N) {
       const float v = ((part[0][b][r] + part[1][b][r]) + part[2][b][r]) + part[3][b][r];
@@ -798,8 +844,8 @@ static void launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
 template <int FMT, int ACT, int CPL, int MT>
 static void launch_gemv_facm(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
   if (epi == QMOE_EPI_WEIGHTED_COMBINE) {
-    const int rpw = 64 / g.lpr;
-    const dim3 grid((unsigned)((g.N + rpw - 1) / rpw));
+    const int rows_blk = GC_ITERS * (64 / g.lpr);
+    const dim3 grid((unsigned)((g.N + rows_blk - 1) / rows_blk));
     hipLaunchKernelGGL((gemv_combine_kernel<FMT, ACT, CPL, MT>), grid, dim3(256), 0, s, g);
   } else {
     const dim3 grid((unsigned)((units_total + g.units_per_wg - 1) / g.units_per_wg), (unsigned)g.nslots);
