@@ -98,9 +98,12 @@ __global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
 
   int c_e = 0, cb = 0;
   if (tid < a.E) {
+    // unrolled so that eight histogram loads are in flight at a time
+#pragma unroll 8
     for (int c = 0; c < a.nchunks; ++c) {
+      const int v = hist[(int64_t)c * a.E + tid];
       if (c == chunk) cb = c_e;
-      c_e += hist[(int64_t)c * a.E + tid];
+      c_e += v;
     }
   }
   // Tile order: every expert's full tiles (bm rows) first, in expert order,
@@ -112,7 +115,9 @@ __global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
   sp[tid] = part;
   for (int i = tid; i < 16 * a.E; i += 1024) wcnt[i] = 0;
   __syncthreads();
-  for (int off = 1; off < QMOE_MAX_EXPERTS; off <<= 1) {
+  // inclusive scan over the first E entries (offsets up to the largest power
+  // of two below E reach every earlier entry)
+  for (int off = 1; off < a.E; off <<= 1) {
     const int va = tid >= off ? sa[tid - off] : 0;
     const int vt = tid >= off ? st[tid - off] : 0;
     const int vp = tid >= off ? sp[tid - off] : 0;
@@ -136,13 +141,13 @@ __global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
         tl[3] = 0;
       };
       for (int i = 0; i < nfull; ++i) put(st[tid] - nfull + i, i, a.bm);
-      if (part) put(st[QMOE_MAX_EXPERTS - 1] + sp[tid] - 1, nfull, c_e - nfull * a.bm);
+      if (part) put(st[a.E - 1] + sp[tid] - 1, nfull, c_e - nfull * a.bm);
     }
   }
   if (chunk == 0 && tid == 0) {
-    const int total = sa[QMOE_MAX_EXPERTS - 1];
+    const int total = sa[a.E - 1];
     a.plan[0] = (int32_t)(a.P - total);
-    a.plan[1] = st[QMOE_MAX_EXPERTS - 1] + sp[QMOE_MAX_EXPERTS - 1];
+    a.plan[1] = st[a.E - 1] + sp[a.E - 1];
     a.plan[2] = total;
     a.plan[3] = a.bm;
     a.plan[4] = (int32_t)a.t;
