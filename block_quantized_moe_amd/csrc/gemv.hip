@@ -28,6 +28,12 @@
 namespace qmoe {
 
 constexpr int GV_MAXT = 4;  // tokens per pass over the weights
+// Unit passes of gemv_rows_kernel whose weight loads are issued together: two
+// when the batch still leaves room for several waves per SIMD (one token per
+// pass, or formats with at most 16 code bytes per chunk), else one.
+__host__ __device__ constexpr int gr_load(int fmt, int mt) {
+  return (mt == 1 || fmt == QMOE_MXFP4 || fmt == QMOE_IQ2_XXS || fmt == QMOE_INT4) ? 2 : 1;
+}
 
 struct GemvArgs {
   const void* qs;
@@ -356,31 +362,47 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
         for (int c = 0; c < CPL; ++c) load_x<ACT>(xr + 32 * (int64_t)(li + c * lpr), x[t][c]);
       }
     }
-    for (int ub = 4 * rpw * 0 + wave * rpw; ub < g.units_per_wg; ub += 4 * rpw) {
-      const int64_t unit = u0 + ub + sub;
-      const bool valid = (ub + sub < g.units_per_wg) && unit < Nunits;
-      const int64_t uc = valid ? unit : 0;
-      float r0[MT], r1[MT];
+    // GR_LOAD unit passes at a time (units_per_wg is a multiple of
+    // GR_LOAD * 4 * rpw): every weight load of the batch is issued before the
+    // first dot product
+    constexpr int NR = swiglu ? 2 : 1;  // weight rows per unit (gate, up)
+    constexpr int GR_LOAD = gr_load(FMT, MT);
+    for (int ub0 = wave * rpw; ub0 < g.units_per_wg; ub0 += GR_LOAD * 4 * rpw) {
+      ChunkRaw wr[GR_LOAD][NR][CPL];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
-      const int64_t Rg = (int64_t)e * g.N + uc;
+      for (int i = 0; i < GR_LOAD; ++i) {
+        const int64_t unit = u0 + ub0 + i * 4 * rpw + sub;
+        const int64_t Rg = (int64_t)e * g.N + (unit < Nunits ? unit : 0);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        XChunk xc[MT];
+        for (int h = 0; h < NR; ++h)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xc[t] = x[t][c];
-        chunk_dot<FMT, ACT, MT>(g, Rg, li + c * lpr, xc, nt, r0, lut_grid, lut_sign);
-        if (swiglu) chunk_dot<FMT, ACT, MT>(g, Rg + g.N / 2, li + c * lpr, xc, nt, r1, lut_grid, lut_sign);
+          for (int c = 0; c < CPL; ++c) wr[i][h][c] = chunk_load<FMT>(g, Rg + h * (g.N / 2), li + c * lpr);
       }
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        if (t < nt) {
-          const float y0 = row_reduce(r0[t], lpr);
-          const float y1 = swiglu ? row_reduce(r1[t], lpr) : 0.f;
-          if (valid && li == 0) {
-            const int s2 = list[tb + t];
-            if (swiglu) store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, silu_f32(y0) * y1);
-            else store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, y0);
+      for (int i = 0; i < GR_LOAD; ++i) {
+        const int64_t unit = u0 + ub0 + i * 4 * rpw + sub;
+        const bool valid = unit < Nunits;
+        float r0[MT], r1[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          XChunk xc[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) xc[t] = x[t][c];
+          chunk_math<FMT, ACT, MT>(g, wr[i][0][c], li + c * lpr, xc, nt, r0, lut_grid, lut_sign);
+          if constexpr (swiglu) chunk_math<FMT, ACT, MT>(g, wr[i][NR - 1][c], li + c * lpr, xc, nt, r1, lut_grid, lut_sign);
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          if (t < nt) {
+            const float y0 = row_reduce(r0[t], lpr);
+            const float y1 = swiglu ? row_reduce(r1[t], lpr) : 0.f;
+            if (valid && li == 0) {
+              const int s2 = list[tb + t];
+              if (swiglu) store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, silu_f32(y0) * y1);
+              else store_out(g.out, g.out_dtype, (int64_t)s2 * Nunits + unit, y0);
+            }
           }
         }
       }
@@ -895,10 +917,12 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
   const int64_t units = (epi == QMOE_EPI_SWIGLU) ? w->n / 2 : w->n;
   // Enough workgroups to keep several waves per SIMD waiting on memory: aim
   // for about 4096 in total (measured: 512 left the MXFP4 decode 15-20% slower).
+  // The rows kernel takes gr_load passes of 4 * rpw units at a time.
+  const int64_t step = gr_load(w->fmt, g.nslots == topk ? 1 : GV_MAXT) * 4 * rpw;
   int64_t upw = (units * g.nslots) / 4096;
-  if (upw < 4 * rpw) upw = 4 * rpw;
-  upw = (upw + 4 * rpw - 1) / (4 * rpw) * (4 * rpw);
-  if (upw > 64) upw = 64 > 4 * rpw ? 64 : 4 * rpw;
+  if (upw < step) upw = step;
+  upw = (upw + step - 1) / step * step;
+  if (upw > 64) upw = 64 > step ? 64 : step;
   g.units_per_wg = (int)upw;
   if (w->fmt == QMOE_INT4 && int4_tiled_ok(g, epi)) {
     if (act == QMOE_F16) launch_gemv_int4_tiled<ACT_F16>(g, epi, s);
