@@ -339,8 +339,19 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
     if constexpr (FMT == QMOE_MXFP4) {
       // plain k order, either activation type: step s = one 32-value block;
       // the E2M1 code values enter the MFMA exactly and the block's
-      // power-of-two scale multiplies the partial sum
+      // power-of-two scale multiplies the partial sum.  The tile's A
+      // fragments are read from LDS once into registers and serve all four
+      // column blocks (reading them once per block made the kernel
+      // LDS-bound).
       typedef typename ActT<ACT>::v8 V8;
+      V8 af[MBV][2];
+#pragma unroll
+      for (int m = 0; m < MBV; ++m) {
+        if (m >= c.mbn) break;
+        const uint16_t* ar = Ab + (16 * m + lr) * LDA + 8 * lg;
+        af[m][0] = __builtin_bit_cast(V8, *(const u4_t*)ar);
+        af[m][1] = __builtin_bit_cast(V8, *(const u4_t*)(ar + 32));
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const u4_t cc[2] = {fp4x8_pairs<ACT>(rw[b].v[0]), fp4x8_pairs<ACT>(rw[b].v[1])};
@@ -348,14 +359,10 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
           if (m >= c.mbn) break;
+          const f4_t t0 = mfma(af[m][0], __builtin_bit_cast(V8, cc[0]), f4_t{0, 0, 0, 0});
+          const f4_t t1 = mfma(af[m][1], __builtin_bit_cast(V8, cc[1]), f4_t{0, 0, 0, 0});
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const V8 a = __builtin_bit_cast(V8, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
-            const f4_t t = mfma(a, __builtin_bit_cast(V8, cc[st]), f4_t{0, 0, 0, 0});
-            const float ds = st ? d1 : d0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(ds, t[r], acc[m][b][r]);
-          }
+          for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(d1, t1[r], __builtin_fmaf(d0, t0[r], acc[m][b][r]));
         }
       }
     } else if constexpr (FMT == QMOE_FP8) {
