@@ -314,3 +314,29 @@ def test_moe_combine_shared(N, ydt, rdt, odt, gated, inplace):
     assert normwise_err(to_f64(out), ref, odt) <= (1e-6 if odt == "f32" else TOL)
     if inplace:
         assert out.data_ptr() == res.data_ptr()
+
+
+def test_empty_inputs_launch_nothing():
+    # T = 0 / M = 0 through the C ABI: every entry point returns QMOE_OK
+    # without launching and leaves its output untouched
+    import ctypes
+    L = qm.lib()
+    rng = np.random.default_rng(7)
+    dw = upload(_w("int4", rng, 4, 64, 256))
+    ws = dw.struct()
+    buf = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")      # plan / ids / weights
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((1, 64), dtype=torch.float32, device="cuda")
+    out = torch.full((4, 64), 7.0, dtype=torch.float32, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = qm._stream()
+    assert L.qmoe_moe_plan(P(buf), 0, 2, 4, 80, P(buf), buf.numel() * 4, s) == 0
+    assert L.qmoe_moe_gather_qmm(ctypes.byref(ws), P(buf), 0, 2, 80, P(x), qm.BF16, qm.A_GATHER_TOKENS,
+                                 None, qm.EPI_STORE, P(out), qm.F32, s) == 0
+    wd = upload(_w("int4", rng, 1, 64, 256)).struct()    # dense: one expert
+    assert L.qmoe_qmm_dense(ctypes.byref(wd), P(x), qm.BF16, 0, qm.EPI_STORE, P(out), qm.F32, s) == 0
+    assert L.qmoe_moe_combine(P(y), qm.F32, P(buf), 0, 2, 4, P(buf), 64, None, P(out), qm.F32, s) == 0
+    assert L.qmoe_moe_gemv(ctypes.byref(ws), P(x), qm.BF16, 0, P(buf), None, 2, qm.EPI_STORE, P(out), qm.F32, s) == 0
+    assert L.qmoe_router_topk(P(y), qm.F32, 0, 64, 2, qm.ROUTER_SOFTMAX, None, 1.0, P(buf), P(buf), s) == 0
+    torch.cuda.synchronize()
+    assert float(out.min()) == 7.0 and float(out.max()) == 7.0

@@ -162,3 +162,17 @@ def test_gemv_generic_single_token(fmt, act, H, I):
     Wgu = synth.weights(fmt, rng, E, 2 * I, H)
     Wd = synth.weights(fmt if fmt != "iq2_xxs" else "q2_k", rng, E, H, I)
     _check(x, ids, w, Wgu, Wd, act)
+
+
+@pytest.mark.parametrize("fmt,act,H,I", [("int4", "bf16", 2048, 512), ("fp8", "f16", 1024, 512),
+                                         ("mxfp4", "bf16", 1024, 512)])
+def test_gemv_largest_batch(fmt, act, H, I):
+    # the largest decode batch a call takes (64 tokens x top-8 = 512 slots),
+    # with skewed routing so some experts serve many tokens (several passes)
+    rng = np.random.default_rng(64 + len(fmt))
+    B, E, k = qm.MAX_GEMV_BATCH, 24, qm.MAX_TOPK
+    x = synth.activations(rng, B, H, act)
+    ids, w = synth.routing_zipf(rng, B, E, k, 1.1)
+    Wgu = synth.int4(rng, E, 2 * I, H) if fmt == "int4" else synth.weights(fmt, rng, E, 2 * I, H)
+    Wd = synth.int4(rng, E, H, I) if fmt == "int4" else synth.weights(fmt, rng, E, H, I)
+    _check(x, ids, w, Wgu, Wd, act)
