@@ -288,8 +288,9 @@ struct TileCtx {
 };
 
 // The K loop and epilogue of a tile of at most MBV 16-row blocks (c.mbn of
-// them hold rows).
-template <int FMT, int ACT, int EPI, int MBV>
+// them hold rows).  FOLD (MXFP4 with fp16 activations only): every block
+// scale of the workgroup's weight rows is known to lie in 2^-13 .. 2^13.
+template <int FMT, int ACT, int EPI, int MBV, bool FOLD = false>
 __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
   constexpr bool INT4_BF16 = (ACT == ACT_BF16 && FMT == QMOE_INT4);
   const int tid = c.tid, wave = c.wave, lg = c.lg, lr = c.lr;
@@ -352,17 +353,38 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
         af[m][0] = __builtin_bit_cast(V8, *(const u4_t*)ar);
         af[m][1] = __builtin_bit_cast(V8, *(const u4_t*)(ar + 32));
       }
+      if constexpr (FOLD) {
+        // each E2M1 value times its block scale is an exact fp16 normal
+        // number (0.5 * 2^-13 .. 6 * 2^13): the scale goes into the B operand
+        // with one packed fp16 multiply per pair and the MFMAs accumulate
+        // directly, with no fp32 scaling per block
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const u4_t cc[2] = {fp4x8_pairs<ACT>(rw[b].v[0]), fp4x8_pairs<ACT>(rw[b].v[1])};
-        const float d0 = e8m0_to_f32(rw[b].x0), d1 = e8m0_to_f32(rw[b].x2);
+        for (int b = 0; b < NB; ++b) {
+          // fp16 bits of 2^(e - 127) for the two blocks
+          const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)((rw[b].x0 - 112u) << 10));
+          const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)((rw[b].x2 - 112u) << 10));
+          const h8_t b0 = __builtin_bit_cast(h8_t, fp4x8_pairs<ACT>(rw[b].v[0])) * s0;
+          const h8_t b1 = __builtin_bit_cast(h8_t, fp4x8_pairs<ACT>(rw[b].v[1])) * s1;
 #pragma unroll
-        for (int m = 0; m < MBV; ++m) {
-          if (m >= c.mbn) break;
-          const f4_t t0 = mfma(af[m][0], __builtin_bit_cast(V8, cc[0]), f4_t{0, 0, 0, 0});
-          const f4_t t1 = mfma(af[m][1], __builtin_bit_cast(V8, cc[1]), f4_t{0, 0, 0, 0});
+          for (int m = 0; m < MBV; ++m) {
+            if (m >= c.mbn) break;
+            acc[m][b] = mfma(af[m][0], b0, acc[m][b]);
+            acc[m][b] = mfma(af[m][1], b1, acc[m][b]);
+          }
+        }
+      } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(d1, t1[r], __builtin_fmaf(d0, t0[r], acc[m][b][r]));
+        for (int b = 0; b < NB; ++b) {
+          const u4_t cc[2] = {fp4x8_pairs<ACT>(rw[b].v[0]), fp4x8_pairs<ACT>(rw[b].v[1])};
+          const float d0 = e8m0_to_f32(rw[b].x0), d1 = e8m0_to_f32(rw[b].x2);
+#pragma unroll
+          for (int m = 0; m < MBV; ++m) {
+            if (m >= c.mbn) break;
+            const f4_t t0 = mfma(af[m][0], __builtin_bit_cast(V8, cc[0]), f4_t{0, 0, 0, 0});
+            const f4_t t1 = mfma(af[m][1], __builtin_bit_cast(V8, cc[1]), f4_t{0, 0, 0, 0});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(d1, t1[r], __builtin_fmaf(d0, t0[r], acc[m][b][r]));
+          }
         }
       }
     } else if constexpr (FMT == QMOE_FP8) {
@@ -671,6 +693,33 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
   }
 }
 
+// MXFP4: whether every E8M0 exponent of this lane's weight rows, over all of
+// K, lies in 114 .. 140 (scales 2^-13 .. 2^13), read from the 16-byte scale
+// vectors of the lane's 16-row blocks (lane l checks vectors l, l + 64, ...).
+// A block whose rows do not start on a 16-row boundary (clamped tail rows)
+// answers false.
+__device__ __forceinline__ bool mxfp4_foldable(const GemmArgs& g, const TileCtx& c) {
+  const int64_t KB = g.K / 32;  // scale vectors per 16-row block
+  bool ok = true;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t base = c.Rb[b] - c.lr;
+    if (base & 15) {
+      ok = false;
+      continue;
+    }
+    const u4_t* run = (const u4_t*)((const uint8_t*)g.scales + (base >> 4) * KB * 16);
+    for (int64_t i = c.lane; i < KB; i += 64) {
+      const u4_t v = run[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ok = ok && ((v[q] >> (8 * j)) & 0xFFu) - 114u <= 26u;
+    }
+  }
+  return ok;
+}
+
 template <int FMT, int ACT, int EPI>
 __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
   constexpr bool INT4_BF16 = (ACT == ACT_BF16 && FMT == QMOE_INT4);
@@ -785,6 +834,12 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
   }
 
   c.mbn = (nrows + 15) >> 4;  // valid 16-row blocks
+  if constexpr (FMT == QMOE_MXFP4 && ACT == ACT_F16) {
+    if (__syncthreads_and(mxfp4_foldable(g, c))) {
+      qmm_body<FMT, ACT, EPI, MB, true>(g, c);
+      return;
+    }
+  }
   qmm_body<FMT, ACT, EPI, MB>(g, c);
 }
 

@@ -340,3 +340,27 @@ def test_empty_inputs_launch_nothing():
     assert L.qmoe_router_topk(P(y), qm.F32, 0, 64, 2, qm.ROUTER_SOFTMAX, None, 1.0, P(buf), P(buf), s) == 0
     torch.cuda.synchronize()
     assert float(out.min()) == 7.0 and float(out.max()) == 7.0
+
+
+@pytest.mark.parametrize("planted", [None, 141, 113, 255])
+def test_dense_mxfp4_f16_scale_ranges(planted):
+    # fp16 activations: a workgroup whose block scales all lie in 2^-13 .. 2^13
+    # folds them into the fp16 operands; one exponent outside that range (or
+    # NaN, 0xFF) in the first 256 rows sends that workgroup down the fp32-scale
+    # path while the second keeps folding
+    rng = np.random.default_rng(33)
+    M, N, K = 40, 512, 512
+    W = synth.mxfp4(rng, 1, N, K)
+    if planted is not None:
+        W.blocks[0, 3, 5, 0] = planted
+    x = synth.activations(rng, M, K, "f16")
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.qmm(oracle.act_to_f64(x, "f16"), W)
+    y = qm.qmm_dense(upload(W), torch_act(x, "f16"), qm.EPI_STORE, qm.F32)
+    torch.cuda.synchronize()
+    got = to_f64(y)
+    if planted == 255:   # a NaN scale poisons exactly the outputs of row 3
+        assert np.isnan(got[:, 3]).all() and np.isfinite(np.delete(got, 3, axis=1)).all()
+        got, ref = np.delete(got, 3, axis=1), np.delete(ref, 3, axis=1)
+    err = normwise_err(got, ref, "f32")
+    assert err <= TOL, (err, report(got, ref))
