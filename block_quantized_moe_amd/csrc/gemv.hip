@@ -63,7 +63,13 @@ struct XChunk {
   float s0, s1;
 };
 
-template <int ACT>
+// The half sums are formed only for the formats whose arithmetic uses them
+// (int4 bias, Q2_K mins): forming them makes the kernel wait for the
+// activations before it issues its weight loads.
+template <int FMT>
+__host__ __device__ constexpr bool needs_x_sums() { return FMT == QMOE_INT4 || FMT == QMOE_Q2_K; }
+
+template <int ACT, bool SUMS>
 __device__ __forceinline__ void load_x(const uint16_t* src, XChunk& x) {
   const u4_t* v = (const u4_t*)src;
   float s0 = 0.f, s1 = 0.f;
@@ -73,8 +79,10 @@ __device__ __forceinline__ void load_x(const uint16_t* src, XChunk& x) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x.p[4 * i + j] = q[j];
-      const float a = act_to_f32<ACT>(q[j] & 0xFFFFu) + act_to_f32<ACT>(q[j] >> 16);
-      if (i < 2) s0 += a; else s1 += a;
+      if constexpr (SUMS) {
+        const float a = act_to_f32<ACT>(q[j] & 0xFFFFu) + act_to_f32<ACT>(q[j] >> 16);
+        if (i < 2) s0 += a; else s1 += a;
+      }
     }
   }
   x.s0 = s0;
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
         const int s2 = list[tb + t];
         const uint16_t* xr = g.a + (int64_t)(s2 / g.topk) * g.K;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) load_x<ACT>(xr + 32 * (int64_t)(li + c * lpr), x[t][c]);
+        for (int c = 0; c < CPL; ++c) load_x<ACT, needs_x_sums<FMT>()>(xr + 32 * (int64_t)(li + c * lpr), x[t][c]);
       }
     }
     // GR_LOAD unit passes at a time (units_per_wg is a multiple of
@@ -427,7 +435,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
   __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
   __shared__ int sid[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
-  __shared__ int first[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
+  __shared__ int minslot[QMOE_MAX_EXPERTS];
   __shared__ int dlist[QMOE_MAX_GEMV_BATCH * QMOE_MAX_TOPK];
   __shared__ int ndist;
   __shared__ float part[4][QMOE_MAX_GEMV_BATCH][GC_ROWS];  // [wave][token][row in block]
@@ -437,18 +445,25 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
   if constexpr (IQ2) build_iq2_luts<ACT>(g.grid, g.signs, lut_grid, lut_sign);
   for (int p = tid; p < P; p += 256) sid[p] = g.ids[p];
   for (int i = tid; i < 4 * QMOE_MAX_GEMV_BATCH * GC_ROWS; i += 256) (&part[0][0][0])[i] = 0.f;
+  for (int i = tid; i < g.E; i += 256) minslot[i] = P;
   __syncthreads();
+  // the first slot of each expert: the smallest slot index naming it
   for (int p = tid; p < P; p += 256) {
     const int e = sid[p];
-    int f = (e >= 0 && e < g.E);
-    for (int q = 0; q < p && f; ++q) f = (sid[q] != e);
-    first[p] = f;
+    if (e >= 0 && e < g.E) atomicMin(&minslot[e], p);
   }
   __syncthreads();
-  if (tid == 0) {  // ordered compaction of first occurrences (P <= 512)
-    int c = 0;
-    for (int p = 0; p < P; ++p) if (first[p]) dlist[c++] = p;
-    ndist = c;
+  if (wave == 0) {  // ordered compaction of first occurrences, 64 slots per ballot (P <= 512)
+    int base = 0;
+    for (int p0 = 0; p0 < P; p0 += 64) {
+      const int p = p0 + lane;
+      const int e = p < P ? sid[p] : -1;
+      const bool f = e >= 0 && e < g.E && minslot[e] == p;
+      const uint64_t m = __ballot(f);
+      if (f) dlist[base + __popcll(m & ((1ull << lane) - 1ull))] = p;
+      base += __popcll(m);
+    }
+    if (lane == 0) ndist = base;
   }
   __syncthreads();
 
@@ -475,7 +490,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          if (t < nt) load_x<ACT>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[c][t]);
+          if (t < nt) load_x<ACT, needs_x_sums<FMT>()>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[c][t]);
 #pragma unroll
       for (int i0 = 0; i0 < GC_ITERS; i0 += GC_LOAD) {
         // the weight chunks of GC_LOAD row passes, all loads issued first
