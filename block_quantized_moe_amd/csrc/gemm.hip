@@ -76,6 +76,7 @@ struct GemmArgs {
   int64_t ldo;
   int n_ntiles;
   int n_blocks;
+  int stage_out;  // int4 ring kernel: 2-byte output through LDS in whole rows (16-byte aligned rows)
 };
 
 // Which k order a (format, activation) path uses inside a 64-wide tile.
@@ -1175,6 +1176,47 @@ void qmm_int4_kernel(GemmArgs g) {
     }
 
     // ---- epilogue
+    if constexpr (EPI == QMOE_EPI_STORE || EPI == QMOE_EPI_SWIGLU) {
+      // 2-byte outputs: the tile's values go to the (now idle) ring as rows
+      // of the workgroup's W output columns, then every thread writes
+      // 16-byte pieces, so each output row is written whole and contiguous
+      // instead of 32 bytes per row per store instruction.
+      if (g.stage_out) {
+        constexpr int W = swiglu ? BN / 2 : BN;  // output columns per workgroup
+        constexpr int CPR = W / 8;               // 16-byte pieces per row
+        constexpr int LROW = 2 * W + 16;         // LDS row stride in bytes
+        static_assert(BM * LROW <= RS * R_STAGE, "output tile fits in the ring");
+        const bool half = (g.out_dtype == QMOE_F16);
+        ring_barrier();  // every wave is done with the ring
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = 16 * m + 4 * lg + rr;
+            uint16_t* dst = (uint16_t*)(ring + row * LROW);
+            if constexpr (swiglu) {
+              const float v = silu_f32(acc[m][0][rr]) * acc[m][1][rr];
+              dst[16 * wave + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
+            } else {
+#pragma unroll
+              for (int b = 0; b < RNB; ++b) {
+                const float v = acc[m][b][rr];
+                dst[32 * wave + 16 * b + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
+              }
+            }
+          }
+        }
+        ring_barrier();
+        const int64_t nlim = swiglu ? Nh : g.N;
+        for (int i = tid; i < nrows * CPR; i += RW * 64) {
+          const int r = i / CPR, c = i - r * CPR;
+          const int64_t col = (int64_t)nt * W + 8 * c;
+          if (col < nlim)
+            *(u4_t*)((uint16_t*)g.out + (int64_t)rows_o[r] * g.ldo + col) = *(const u4_t*)(ring + r * LROW + 16 * c);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int m = 0; m < MBV; ++m) {
 #pragma unroll
@@ -1278,6 +1320,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   if (epi == QMOE_EPI_SWIGLU) { g.n_ntiles = (int)((w->n / 2 + BN / 2 - 1) / (BN / 2)); g.ldo = w->n / 2; }
   else { g.n_ntiles = (int)((w->n + BN - 1) / BN); g.ldo = w->n; }
   g.n_blocks = (int)((n_mt + 7) / 8 * 8 * g.n_ntiles);  // whole rounds of the 8 XCDs
+  g.stage_out = (out_dtype == QMOE_F16 || out_dtype == QMOE_BF16) && g.ldo % 8 == 0 && (uintptr_t)out % 16 == 0;
   if (g.n_blocks == 0) return;
   if (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi)) {
     if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);

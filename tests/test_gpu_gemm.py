@@ -364,3 +364,28 @@ def test_dense_mxfp4_f16_scale_ranges(planted):
         got, ref = np.delete(got, 3, axis=1), np.delete(ref, 3, axis=1)
     err = normwise_err(got, ref, "f32")
     assert err <= TOL, (err, report(got, ref))
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("epi", ["store", "swiglu"])
+def test_int4_two_byte_outputs_whole_rows(act, epi):
+    # 2-byte outputs of the int4 prefill kernel leave through LDS as whole
+    # rows: ragged rows and a partial column tile against the oracle, and
+    # bit for bit the kernel's own fp32 output rounded to nearest even
+    rng = np.random.default_rng(17 + len(act) + len(epi))
+    M, K = 173, 512
+    N = 800 if epi == "store" else 704  # 3 full 256-column tiles + 32 / 2 full 128-column tiles + 96
+    W = synth.int4(rng, 1, N, K, 64)
+    x = synth.activations(rng, M, K, act)
+    code = qm.F16 if act == "f16" else qm.BF16
+    ep = qm.EPI_STORE if epi == "store" else qm.EPI_SWIGLU
+    z = oracle.qmm(oracle.act_to_f64(x, act), W)
+    ref = z if epi == "store" else oracle.silu(z[:, :N // 2]) * z[:, N // 2:]
+    Wd, xd = upload(W), torch_act(x, act)
+    y = qm.qmm_dense(Wd, xd, ep, code)
+    y32 = qm.qmm_dense(Wd, xd, ep, qm.F32)
+    torch.cuda.synchronize()
+    err = normwise_err(to_f64(y), ref, act)
+    assert err <= TOL, (err, report(to_f64(y), ref))
+    bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits, oracle.round_out(y32.cpu().numpy(), act))
