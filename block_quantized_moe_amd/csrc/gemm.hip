@@ -662,6 +662,55 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
   }
 
   // ---------------------------------------------------------------- epilogue
+  if constexpr (EPI == QMOE_EPI_STORE || EPI == QMOE_EPI_SWIGLU) {
+    // 2-byte outputs leave through the (now idle) activation tile as rows of
+    // 128 output columns, then 16-byte pieces per thread, so each output row
+    // is written whole and contiguous.  SwiGLU's 128 columns take one pass;
+    // STORE's 256 take two (waves 0-1, then waves 2-3).
+    if (g.stage_out) {
+      constexpr bool swiglu = (EPI == QMOE_EPI_SWIGLU);
+      constexpr int HW = 128;            // output columns per pass
+      constexpr int LROW = 2 * HW + 16;  // LDS row stride in bytes
+      static_assert(BM * LROW <= 2 * BM * LDA * 2, "a pass fits in the activation tile");
+      const bool half = (g.out_dtype == QMOE_F16);
+      uint8_t* stg = (uint8_t*)c.As;
+      const int64_t nlim = swiglu ? g.N / 2 : g.N;
+      const int64_t col0 = swiglu ? c.ncol[0] - 32 * wave - lr : c.ncol[0] - 64 * wave - lr;  // first column of the workgroup
+#pragma unroll
+      for (int h = 0; h < (swiglu ? 1 : 2); ++h) {
+        __syncthreads();  // the K loop (or the previous pass) is done with the tile
+        if (swiglu || (wave >> 1) == h) {
+#pragma unroll
+          for (int m = 0; m < MBV; ++m) {
+            if (m >= c.mbn) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              uint16_t* dst = (uint16_t*)(stg + (16 * m + 4 * lg + r) * LROW);
+              if constexpr (swiglu) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                  const float v = silu_f32(acc[m][j][r]) * acc[m][2 + j][r];
+                  dst[32 * wave + 16 * j + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
+                }
+              } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                  dst[64 * (wave & 1) + 16 * b + lr] = half ? f32_to_f16(acc[m][b][r]) : f32_to_bf16(acc[m][b][r]);
+              }
+            }
+          }
+        }
+        __syncthreads();
+        for (int i = tid; i < c.nrows * (HW / 8); i += 256) {
+          const int r = i / (HW / 8), cc = i - r * (HW / 8);
+          const int64_t col = col0 + HW * h + 8 * cc;
+          if (col < nlim)
+            *(u4_t*)((uint16_t*)g.out + (int64_t)c.rows_o[r] * g.ldo + col) = *(const u4_t*)(stg + r * LROW + 16 * cc);
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int m = 0; m < MBV; ++m) {
     if (m >= c.mbn) break;

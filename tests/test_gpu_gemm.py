@@ -366,16 +366,19 @@ def test_dense_mxfp4_f16_scale_ranges(planted):
     assert err <= TOL, (err, report(got, ref))
 
 
+@pytest.mark.parametrize("fmt", ["int4", "q8_0", "mxfp4", "fp8"])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("epi", ["store", "swiglu"])
-def test_int4_two_byte_outputs_whole_rows(act, epi):
-    # 2-byte outputs of the int4 prefill kernel leave through LDS as whole
-    # rows: ragged rows and a partial column tile against the oracle, and
-    # bit for bit the kernel's own fp32 output rounded to nearest even
-    rng = np.random.default_rng(17 + len(act) + len(epi))
+def test_two_byte_outputs_whole_rows(fmt, act, epi):
+    # 2-byte outputs of the prefill kernels leave through LDS as whole rows:
+    # ragged rows and a partial column tile against the oracle, and bit for
+    # bit the kernel's own fp32 output rounded to nearest even
+    rng = np.random.default_rng(17 + len(act) + len(epi) + len(fmt))
     M, K = 173, 512
     N = 800 if epi == "store" else 704  # 3 full 256-column tiles + 32 / 2 full 128-column tiles + 96
-    W = synth.int4(rng, 1, N, K, 64)
+    if fmt == "fp8":
+        N = 896 if epi == "store" else 640  # multiples of the 128-row scale blocks
+    W = _w(fmt, rng, 1, N, K)
     x = synth.activations(rng, M, K, act)
     code = qm.F16 if act == "f16" else qm.BF16
     ep = qm.EPI_STORE if epi == "store" else qm.EPI_SWIGLU
