@@ -225,33 +225,37 @@ def activations(rng: np.random.Generator, T: int, K: int, dtype: str) -> np.ndar
     return f16_bits(x) if dtype == "f16" else bf16_bits(x)
 
 
-def _pairs_from_keys(rng: np.random.Generator, keys: np.ndarray, k: int):
-    """k distinct experts per row, the k largest of the random keys (a sampling
-    step: continuous keys, so no ties in practice), and random positive pair
-    weights, decreasing along the row and summing to 1.  A stand-in for a
-    router's output, not a router."""
+def _pairs_from_keys(keys: np.ndarray, k: int):
+    """k distinct experts per row, the k largest keys (continuous keys, so no
+    ties in practice), and the pair weights the workload text names: a
+    softmax over the k selected keys, exp(l_j - l_0) / sum_i exp(l_i - l_0)
+    in fp64 (l_0 the largest), stored as fp32.  An input recipe drawn on the
+    host, not the device router."""
     ids = np.argsort(-keys, axis=1, kind="stable")[:, :k]
-    u = -np.sort(-rng.uniform(0.05, 1.0, size=ids.shape), axis=1)
-    w = u / u.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(keys.astype(np.float64), ids, axis=1)
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
     return ids.astype(np.int32), w.astype(np.float32)
 
 
 def routing_softmax(rng: np.random.Generator, T: int, E: int, k: int):
-    """Uniform routing of the Qwen-shaped workloads: k distinct experts drawn
-    uniformly per token (N(0,1) keys)."""
-    return _pairs_from_keys(rng, rng.standard_normal((T, E), dtype=np.float32), k)
+    """Uniform routing of the Qwen-shaped workloads: N(0,1) router logits per
+    token and expert, the top k of each row, weights the softmax over the
+    selected logits."""
+    return _pairs_from_keys(rng.standard_normal((T, E), dtype=np.float32), k)
 
 
 def routing_zipf(rng: np.random.Generator, T: int, E: int, k: int, alpha: float = 1.1):
     """Skewed routing: expert popularity p ~ rank^-alpha over a seeded
-    permutation; keys log p + Gumbel(0,1), so the top k of a row samples
-    experts without replacement in proportion to p."""
+    permutation; keys log p + Gumbel(0,1) act as the router logits, so the
+    top k of a row samples experts without replacement in proportion to p;
+    weights the softmax over the selected keys."""
     perm = rng.permutation(E)
     p = np.empty(E)
     p[perm] = np.arange(1, E + 1, dtype=np.float64) ** (-alpha)
     p /= p.sum()
     keys = (np.log(p)[None, :] + rng.gumbel(size=(T, E))).astype(np.float32)
-    return _pairs_from_keys(rng, keys, k)
+    return _pairs_from_keys(keys, k)
 
 
 def router_logits(rng: np.random.Generator, T: int, E: int, dtype: str, sigma: float = 1.0) -> np.ndarray:

@@ -278,8 +278,10 @@ def _golden_layouts():
 
 
 def test_golden_block_layouts():
-    """tests/golden/block_layouts.txt: block sizes and first code byte as the
-    pages state them; a code planted at that byte decodes into element 0."""
+    """tests/golden/block_layouts.txt: block sizes and first code byte (the
+    Q2_K row and the grid size as the pages state them, the Q8_0 and IQ2_XXS
+    byte positions as readings c1 / c3); a code planted at that byte decodes
+    into element 0."""
     g = _golden_layouts()
     rng = np.random.default_rng(0)
     # Q8_0: fp16 scale 1.0, code 5 at the first code byte -> element 0 == 5

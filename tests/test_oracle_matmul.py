@@ -163,3 +163,75 @@ def test_moe_exact_integer_case():
     y = oracle.qmm(oracle.act_to_f64(xb, "f16"), W, e=1)
     codes = W.blocks[1, :, :, 2:].view(np.int8).reshape(N, H).astype(np.int64)
     assert np.array_equal(y, (xi @ codes.T).astype(np.float64))
+
+
+def _expert0_as_dense(W):
+    """Routed expert 0 of a stacked int4 weight, as a dense [1, N, K] weight."""
+    return synth.QWeights("int4", 1, W.N, W.K, W.group, qs=W.qs[:1].copy(), scale=W.scale[:1].copy(),
+                          bias=W.bias[:1].copy())
+
+
+@pytest.mark.parametrize("h_dtype", [None, "bf16"])
+def test_moe_ffn_shared_expert_equal_to_routed(h_dtype):
+    """The shared-expert branch of moe_ffn (gate/up, SwiGLU, the h storage
+    rounding, down, then the gated add): with the shared weights equal to
+    routed expert 0 and every token routed top-1 to expert 0 with weight 1,
+    the shared term equals the routed output, so the result is exactly twice
+    it, 1 + sigmoid(0) = 1.5 times it with gate logits 0, and 1 + 3/4 with
+    gate logits ln 3 -- a swapped gate/up half, a dropped rounding or a
+    misplaced gate in the shared branch breaks the equality."""
+    x, _, _, wgu, wd = _tiny_moe(E=3, T=6, k=2)
+    T = x.shape[0]
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    x64 = oracle.act_to_f64(x, "bf16")
+    routed = oracle.moe_ffn(x64, ids, w, wgu, wd, h_dtype=h_dtype)
+    shared = (_expert0_as_dense(wgu), _expert0_as_dense(wd))
+    assert np.abs(routed).max() > 0
+    both = oracle.moe_ffn(x64, ids, w, wgu, wd, h_dtype=h_dtype, shared=shared)
+    assert np.array_equal(both, 2.0 * routed)
+    half = oracle.moe_ffn(x64, ids, w, wgu, wd, h_dtype=h_dtype, shared=shared, shared_gate=np.zeros(T))
+    assert np.array_equal(half, 1.5 * routed)
+    g3 = oracle.moe_ffn(x64, ids, w, wgu, wd, h_dtype=h_dtype, shared=shared, shared_gate=np.full(T, math.log(3.0)))
+    assert np.allclose(g3, 1.75 * routed, rtol=1e-15, atol=0)
+    res = np.arange(T * wd.N, dtype=np.float64).reshape(T, wd.N) / 7.0
+    with_res = oracle.moe_ffn(x64, ids, w, wgu, wd, h_dtype=h_dtype, shared=shared, residual=res)
+    assert np.array_equal(with_res, 2.0 * routed + res)
+
+
+def test_moe_ffn_shared_expert_brute_force():
+    """The shared branch against scalar loops over the blocks (a shared
+    expert unlike any routed one): out_t = routed_t + silu(g_t) * u_t . Wsd^T."""
+    x, ids, w, wgu, wd = _tiny_moe(E=2, T=3, k=1, H=64, I=64, seed=9)
+    rng = np.random.default_rng(10)
+    H, I = wd.N, wd.K
+    sgu = synth.int4(rng, 1, 2 * I, H)
+    sd = synth.int4(rng, 1, H, I)
+    x64 = oracle.act_to_f64(x, "bf16")
+    routed = oracle.moe_ffn(x64, ids, w, wgu, wd)
+    got = oracle.moe_ffn(x64, ids, w, wgu, wd, shared=(sgu, sd))
+    for t in range(x.shape[0]):
+        hs = np.zeros(I)
+        for i in range(I):
+            g = sum(x64[t, c] * _scalar_int4(sgu, 0, i, c) for c in range(H))
+            u = sum(x64[t, c] * _scalar_int4(sgu, 0, I + i, c) for c in range(H))
+            hs[i] = g / (1 + math.exp(-g)) * u
+        ref = routed[t] + np.array([sum(hs[i] * _scalar_int4(sd, 0, n, i) for i in range(I)) for n in range(H)])
+        assert np.allclose(got[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_synth_pair_weights_are_softmax_of_selected_logits():
+    """The routing recipe of the inputs: ids are the k largest logits of the
+    row, weights exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected ones
+    (they sum to 1 and fall along the row)."""
+    logits = np.array([[1.0, 5.0, 3.0, 4.0], [0.5, -1.0, 2.0, 2.5]], np.float32)
+    ids, w = synth._pairs_from_keys(logits, 2)
+    assert ids.tolist() == [[1, 3], [3, 2]]
+    e1 = 1.0 / (1.0 + math.exp(-1.0))  # softmax of (a, a - 1): sigmoid(1), sigmoid(-1)
+    assert np.allclose(w[0], [e1, 1 - e1], rtol=1e-7)
+    e2 = 1.0 / (1.0 + math.exp(-0.5))
+    assert np.allclose(w[1], [e2, 1 - e2], rtol=1e-7)
+    rng = np.random.default_rng(3)
+    ids, w = synth.routing_softmax(rng, 50, 16, 4)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6) and np.all(np.diff(w, axis=1) <= 0)
+    assert all(len(set(r)) == 4 for r in ids.tolist())
