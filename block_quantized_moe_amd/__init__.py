@@ -82,6 +82,8 @@ _SIGS = {
                          ctypes.c_void_p],
     "qmoe_check_device": [],
     "qmoe_strerror": [ctypes.c_int],
+    "qmoe_split_rows": [ctypes.c_int64],
+    "qmoe_workspace_bytes": [ctypes.c_int32, ctypes.POINTER(_Weights), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32],
 }
 EXPORTS = tuple(_SIGS)
 
@@ -98,6 +100,8 @@ def lib():
             f.argtypes = args
             f.restype = ctypes.c_int
         L.qmoe_plan_bytes.restype = ctypes.c_size_t
+        L.qmoe_workspace_bytes.restype = ctypes.c_size_t
+        L.qmoe_split_rows.restype = ctypes.c_int64
         L.qmoe_strerror.restype = ctypes.c_char_p
         L.qmoe_iq2_signs_table.restype = None
         _lib = L
@@ -126,13 +130,19 @@ def _np_ptr(a: np.ndarray):
 # host-side split (C functions of the library)
 # ---------------------------------------------------------------------------
 
+def split_rows(rows: int) -> int:
+    """Rows of every tiled split array: rows rounded up to a multiple of 16."""
+    return int(lib().qmoe_split_rows(rows))
+
+
 def split_q8_0(aos: np.ndarray, rows: int, k: int):
-    """Q8_0 blocks [rows, k/32, 34] -> tiled (codes, scales)."""
+    """Q8_0 blocks [rows, k/32, 34] -> tiled (codes, scales), sized for split_rows(rows)."""
     aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
     if aos.size != rows * (k // 32) * 34:
         raise QmoeError("split_q8_0: block count does not match rows/k")
-    qs = np.empty(rows * k, np.int8)
-    d = np.empty(rows * (k // 32), np.uint16)
+    R = split_rows(rows)
+    qs = np.empty(R * k, np.int8)
+    d = np.empty(R * (k // 32), np.uint16)
     _check(lib().qmoe_split_q8_0(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(d)), "split_q8_0")
     return qs, d
 
@@ -142,7 +152,7 @@ def split_q2_k(aos: np.ndarray, rows: int, k: int):
     aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
     if aos.size != rows * (k // 256) * 84:
         raise QmoeError("split_q2_k: block count does not match rows/k")
-    nb = rows * (k // 256)
+    nb = split_rows(rows) * (k // 256)
     qs = np.empty(nb * 16, np.uint32)
     sc = np.empty(nb * 16, np.uint8)
     d = np.empty(nb, np.uint16)
@@ -157,7 +167,7 @@ def split_iq2_xxs(aos: np.ndarray, rows: int, k: int):
     aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
     if aos.size != rows * (k // 256) * 66:
         raise QmoeError("split_iq2_xxs: block count does not match rows/k")
-    nb = rows * (k // 256)
+    nb = split_rows(rows) * (k // 256)
     ia = np.empty(nb * 16, np.uint32)
     d = np.empty(nb, np.uint16)
     _check(lib().qmoe_split_iq2_xxs(_np_ptr(aos), rows, k, _np_ptr(ia), _np_ptr(d)), "split_iq2_xxs")
@@ -169,8 +179,9 @@ def split_mxfp4(aos: np.ndarray, rows: int, k: int):
     aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
     if aos.size != rows * (k // 32) * 17:
         raise QmoeError("split_mxfp4: block count does not match rows/k")
-    qs = np.empty(rows * k // 8, np.uint32)
-    e = np.empty(rows * (k // 32), np.uint8)
+    R = split_rows(rows)
+    qs = np.empty(R * k // 8, np.uint32)
+    e = np.empty(R * (k // 32), np.uint8)
     _check(lib().qmoe_split_mxfp4(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(e)), "split_mxfp4")
     return qs, e
 
@@ -192,8 +203,9 @@ def split_int4(words: np.ndarray, scale: np.ndarray, bias: np.ndarray, rows: int
     bias = np.ascontiguousarray(bias, dtype=np.uint16).reshape(-1)
     if words.size != rows * (k // 8) or scale.size != rows * (k // max(group, 1)) or bias.size != scale.size:
         raise QmoeError("split_int4: array sizes do not match rows/k/group")
-    qs = np.empty(rows * (k // 8), np.uint32)
-    sb = np.empty(scale.size, np.uint32)
+    R = split_rows(rows)
+    qs = np.empty(R * (k // 8), np.uint32)
+    sb = np.empty(R * (k // max(group, 1)), np.uint32)
     _check(lib().qmoe_split_int4(_np_ptr(words), _np_ptr(scale), _np_ptr(bias), rows, k, group,
                                  _np_ptr(qs), _np_ptr(sb)), "split_int4")
     return qs, sb
@@ -295,6 +307,40 @@ def _code(t):
     return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}[t.dtype]
 
 
+def _need(t, name, *, shape=None, cols=None, min_rows=None, dtypes=None, dim=None):
+    """Check a caller-supplied tensor before its pointer reaches the library:
+    contiguity, rank, shape (None entries match anything), dtype, and that it
+    is on a GPU.  Raises ValueError."""
+    import torch
+    if t is None:
+        raise ValueError(f"{name}: a tensor is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name}: expected {dim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and (t.dim() != len(shape) or any(w is not None and int(v) != int(w)
+                                                           for v, w in zip(t.shape, shape))):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if cols is not None and (t.dim() < 1 or int(t.shape[-1]) != int(cols)):
+        raise ValueError(f"{name}: expected {cols} columns, got shape {tuple(t.shape)}")
+    if min_rows is not None and (t.dim() < 1 or int(t.shape[0]) < int(min_rows)):
+        raise ValueError(f"{name}: expected at least {min_rows} rows, got shape {tuple(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
+def _acts():
+    import torch
+    return (torch.float16, torch.bfloat16)
+
+
+def _outs():
+    import torch
+    return (torch.float32, torch.float16, torch.bfloat16)
+
+
 def check_device():
     _check(lib().qmoe_check_device(), "check_device")
 
@@ -304,6 +350,9 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
     import torch
     if out is None:
         out = torch.empty((w.E, w.N, w.K), dtype=_dt(out_dtype), device=w.tensors["qs"].device)
+    _need(out, "out", shape=(w.E, w.N, w.K), dtypes=_outs())
+    if _code(out) != out_dtype:
+        raise ValueError(f"out: dtype {out.dtype} does not match out_dtype {out_dtype}")
     t = w.tensors
     L = lib()
     s = _stream()
@@ -328,10 +377,12 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
 
 def qmm_dense(w: DeviceWeights, x, epilogue: int = EPI_STORE, out_dtype: int = F16, out=None):
     import torch
+    _need(x, "x", dim=2, cols=w.K, dtypes=_acts())
     M = x.shape[0]
+    n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
     if out is None:
-        n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
         out = torch.empty((M, n), dtype=_dt(out_dtype), device=x.device)
+    _need(out, "out", shape=(M, n), dtypes=(torch.float32,) if epilogue == EPI_ACCUMULATE else _outs())
     ws = w.struct()
     _check(lib().qmoe_qmm_dense(ctypes.byref(ws), _ptr(x), _code(x), M, epilogue, _ptr(out), _code(out), _stream()),
            "qmm_dense")
@@ -344,10 +395,14 @@ def plan_bytes(t: int, topk: int, E: int, bm: int) -> int:
 
 def moe_plan(ids, E: int, bm: int = 80, plan=None):
     import torch
+    _need(ids, "ids", dim=2, dtypes=(torch.int32,))
     T, k = ids.shape
     nbytes = plan_bytes(T, k, E, bm)
     if plan is None:
         plan = torch.empty(nbytes // 4, dtype=torch.int32, device=ids.device)
+    _need(plan, "plan", dtypes=(torch.int32,))
+    if plan.numel() * 4 < nbytes:
+        raise ValueError(f"plan: {plan.numel() * 4} bytes, the call needs {nbytes}")
     _check(lib().qmoe_moe_plan(_ptr(ids), T, k, E, bm, _ptr(plan), plan.numel() * 4, _stream()), "moe_plan")
     return plan
 
@@ -357,11 +412,16 @@ def router_topk(logits, k: int, scoring: int = ROUTER_SOFTMAX, bias=None, scale:
     """Router top-k on the device: logits [T, E] (f32 / f16 / bf16) ->
     (ids int32 [T, k], weights f32 [T, k]), best first (include/qmoe.h)."""
     import torch
+    _need(logits, "logits", dim=2, dtypes=_outs())
     T, E = logits.shape
     if ids is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if weights is None:
         weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need(ids, "ids", shape=(T, k), dtypes=(torch.int32,))
+    _need(weights, "weights", shape=(T, k), dtypes=(torch.float32,))
+    if bias is not None:
+        _need(bias, "bias", shape=(E,), dtypes=(torch.float32,))
     if T == 0:
         return ids, weights
     _check(lib().qmoe_router_topk(_ptr(logits), _code(logits), T, E, k, scoring, _ptr(bias), scale,
@@ -387,19 +447,46 @@ def moe_gather_qmm(w: DeviceWeights, plan, T: int, topk: int, a, *, bm: int = 80
                    a_mode: int = A_GATHER_TOKENS, topk_w=None, epilogue: int = EPI_STORE,
                    out_dtype: int = None, out=None, n_rows: int = None):
     """Gathered MoE matmul.  For STORE / SWIGLU the output has one row per
-    sorted position (n_rows = number of valid pairs, default T * topk)."""
+    sorted position (n_rows = number of valid pairs, default T * topk); with
+    SORTED_ROWS the activations hold one row per sorted position.  Rows past
+    the given tensors cannot be checked on the host (the plan's valid-pair
+    count lives on the device): out and SORTED_ROWS activations must hold at
+    least the plan's valid pairs."""
     import torch
+    _need(a, "a", dim=2, cols=w.K, dtypes=_acts())
+    if a_mode == A_GATHER_TOKENS and a.shape[0] != T:
+        raise ValueError(f"a: GATHER_TOKENS takes [T={T}, K] activations, got {tuple(a.shape)}")
+    if a_mode == A_SORTED_ROWS and n_rows is not None and a.shape[0] < n_rows:
+        raise ValueError(f"a: {a.shape[0]} rows for {n_rows} valid pairs")
+    _need(plan, "plan", dtypes=(torch.int32,))
+    if plan.numel() * 4 < plan_bytes(T, topk, w.E, bm):
+        raise ValueError("plan: smaller than a plan for this call")
+    n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    rows = T * topk if n_rows is None else n_rows
     if out is None:
         if epilogue == EPI_WEIGHTED_COMBINE:
             out = torch.zeros((T, w.N), dtype=torch.float32, device=a.device)
         else:
-            rows = T * topk if n_rows is None else n_rows
-            n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
             out = torch.empty((rows, n), dtype=_dt(out_dtype if out_dtype is not None else _code(a)), device=a.device)
+    if epilogue == EPI_WEIGHTED_COMBINE:
+        _need(out, "out", shape=(T, w.N), dtypes=(torch.float32,))
+        _need(topk_w, "topk_w", shape=(T, topk), dtypes=(torch.float32,))
+    else:
+        _need(out, "out", dim=2, cols=n, min_rows=rows if n_rows is not None else 1, dtypes=_outs())
     ws = w.struct()
     _check(lib().qmoe_moe_gather_qmm(ctypes.byref(ws), _ptr(plan), T, topk, bm, _ptr(a), _code(a), a_mode,
                                      _ptr(topk_w), epilogue, _ptr(out), _code(out), _stream()), "moe_gather_qmm")
     return out
+
+
+def _combine_checks(y, plan, T, topk, E, topk_w, out):
+    import torch
+    _need(y, "y", dim=2, dtypes=_outs())
+    _need(plan, "plan", dtypes=(torch.int32,))
+    if plan.numel() * 4 < plan_bytes(T, topk, E, 16):
+        raise ValueError("plan: smaller than a plan for this call")
+    _need(topk_w, "topk_w", shape=(T, topk), dtypes=(torch.float32,))
+    _need(out, "out", shape=(T, y.shape[1]), dtypes=_outs())
 
 
 def moe_combine(y, plan, T: int, topk: int, E: int, topk_w, base=None, out_dtype: int = BF16, out=None):
@@ -407,6 +494,9 @@ def moe_combine(y, plan, T: int, topk: int, E: int, topk_w, base=None, out_dtype
     N = y.shape[1]
     if out is None:
         out = torch.empty((T, N), dtype=_dt(out_dtype), device=y.device)
+    _combine_checks(y, plan, T, topk, E, topk_w, out)
+    if base is not None:
+        _need(base, "base", shape=(T, N), dtypes=(torch.float32,))
     _check(lib().qmoe_moe_combine(_ptr(y), _code(y), _ptr(plan), T, topk, E, _ptr(topk_w), N, _ptr(base),
                                   _ptr(out), _code(out), _stream()), "moe_combine")
     return out
@@ -420,6 +510,13 @@ def moe_combine_shared(y, plan, T: int, topk: int, E: int, topk_w, shared=None, 
     N = y.shape[1]
     if out is None:
         out = torch.empty((T, N), dtype=_dt(out_dtype), device=y.device)
+    _combine_checks(y, plan, T, topk, E, topk_w, out)
+    if shared is not None:
+        _need(shared, "shared", shape=(T, N), dtypes=(torch.float32,))
+    if shared_gate is not None:
+        _need(shared_gate, "shared_gate", shape=(T,), dtypes=(torch.float32,))
+    if residual is not None:
+        _need(residual, "residual", shape=(T, N), dtypes=_outs())
     rcode = _code(residual) if residual is not None else F32
     _check(lib().qmoe_moe_combine_shared(_ptr(y), _code(y), _ptr(plan), T, topk, E, _ptr(topk_w), N, _ptr(shared),
                                          _ptr(shared_gate), _ptr(residual), rcode, _ptr(out), _code(out),
@@ -429,8 +526,10 @@ def moe_combine_shared(y, plan, T: int, topk: int, E: int, topk_w, shared=None, 
 
 def combine_cast(acc, out_dtype: int = BF16, out=None):
     import torch
+    _need(acc, "acc", dtypes=(torch.float32,))
     if out is None:
         out = torch.empty(acc.shape, dtype=_dt(out_dtype), device=acc.device)
+    _need(out, "out", shape=tuple(acc.shape), dtypes=_outs())
     _check(lib().qmoe_combine_cast(_ptr(acc), acc.numel(), _ptr(out), _code(out), _stream()), "combine_cast")
     return out
 
@@ -440,14 +539,19 @@ def moe_gemv(w: DeviceWeights, a, ids, topk_w=None, *, epilogue: int = EPI_SWIGL
     """Decode GEMV.  STORE/SWIGLU: a = x [B, K] -> [B, topk, N or N/2];
     WEIGHTED_COMBINE: a = h [B, topk, K] -> [B, N]."""
     import torch
+    _need(ids, "ids", dim=2, dtypes=(torch.int32,))
     B, topk = ids.shape
+    if epilogue == EPI_WEIGHTED_COMBINE:
+        _need(a, "a", shape=(B, topk, w.K), dtypes=_acts())
+        _need(topk_w, "topk_w", shape=(B, topk), dtypes=(torch.float32,))
+    else:
+        _need(a, "a", shape=(B, w.K), dtypes=_acts())
     od = out_dtype if out_dtype is not None else _code(a)
+    n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    oshape = (B, w.N) if epilogue == EPI_WEIGHTED_COMBINE else (B, topk, n)
     if out is None:
-        if epilogue == EPI_WEIGHTED_COMBINE:
-            out = torch.empty((B, w.N), dtype=_dt(od), device=a.device)
-        else:
-            n = w.N // 2 if epilogue == EPI_SWIGLU else w.N
-            out = torch.empty((B, topk, n), dtype=_dt(od), device=a.device)
+        out = torch.empty(oshape, dtype=_dt(od), device=a.device)
+    _need(out, "out", shape=oshape, dtypes=_outs())
     ws = w.struct()
     _check(lib().qmoe_moe_gemv(ctypes.byref(ws), _ptr(a), _code(a), B, _ptr(ids), _ptr(topk_w), topk, epilogue,
                                _ptr(out), _code(out), _stream()), "moe_gemv")

@@ -27,6 +27,7 @@ int qmm_int4_bf16_max_groups();
 int qmm_max_rows();
 int launch_gemv(const qmoe_weights*, const void*, int, int64_t, const int32_t*, const float*, int,
                  int, void*, int, hipStream_t);
+int64_t gemv_max_k();
 void launch_combine_cast(float*, int64_t, void*, int, hipStream_t);
 void launch_router_topk(const void*, int, int64_t, int, int, int, const float*, float, int32_t*,
                         float*, hipStream_t);
@@ -65,7 +66,9 @@ int launched() {
 }
 
 // Shared validation of a weight descriptor.  need_k64: matmul entry points
-// stage k in 64-wide tiles.
+// stage k in 64-wide tiles.  Any row count n is accepted: the splitter pads
+// the stacked rows to a multiple of 16 and the kernels mask the tail rows
+// (FP8 keeps its 128-row scale blocks).
 int check_weights(const qmoe_weights* w, bool need_k64) {
   if (!w) return QMOE_ERR_ARG;
   if (w->n_experts < 1 || w->n < 1 || w->k < 1) return QMOE_ERR_ARG;
@@ -75,22 +78,22 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
   if (!w->qs || !al16(w->qs)) return w->qs ? QMOE_ERR_ALIGN : QMOE_ERR_ARG;
   switch (w->fmt) {
     case QMOE_Q8_0:
-      if (w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (w->k % 64) return QMOE_ERR_BLOCK;
       if (!w->scales) return QMOE_ERR_ARG;
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_Q2_K:
-      if (w->k % 256 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (w->k % 256) return QMOE_ERR_BLOCK;
       if (!w->scales || !w->d || !w->dmin) return QMOE_ERR_ARG;
       if (!al16(w->scales) || !al16(w->d) || !al16(w->dmin)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_IQ2_XXS:
-      if (w->k % 256 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (w->k % 256) return QMOE_ERR_BLOCK;
       if (!w->d || !w->grid || !w->signs) return QMOE_ERR_ARG;
       if (!al16(w->d) || !al16(w->grid) || !al16(w->signs)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_MXFP4:
-      if (w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (w->k % 64) return QMOE_ERR_BLOCK;
       if (!w->scales) return QMOE_ERR_ARG;
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
@@ -102,7 +105,7 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       break;
     case QMOE_INT4:
       if (!(w->group == 32 || w->group == 64 || w->group == 128 || w->group == 256)) return QMOE_ERR_BLOCK;
-      if (w->k % w->group || w->k % 64 || (w->n_experts * w->n) % 16) return QMOE_ERR_BLOCK;
+      if (w->k % w->group || w->k % 64) return QMOE_ERR_BLOCK;
       if (!w->scales) return QMOE_ERR_ARG;
       if (!al16(w->scales)) return QMOE_ERR_ALIGN;
       break;
@@ -144,7 +147,7 @@ const char* qmoe_strerror(int status) {
 int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k, void* out, int32_t out_dtype,
                       void* stream) {
   if (!qs || !d || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (k % 64) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(d) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
@@ -155,7 +158,7 @@ int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t
 int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k, void* out,
                        int32_t out_dtype, void* stream) {
   if (!qs || !e || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (k % 64) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(e) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
@@ -178,7 +181,7 @@ int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t*
                       const uint16_t* dmin, int64_t rows, int64_t k, void* out, int32_t out_dtype,
                       void* stream) {
   if (!qs || !scales || !d || !dmin || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  if (k % 256) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(scales) || !al16(d) || !al16(dmin) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
@@ -188,7 +191,7 @@ int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t*
 int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid, const uint8_t* signs,
                          int64_t rows, int64_t k, void* out, int32_t out_dtype, void* stream) {
   if (!qs || !d || !grid || !signs || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  if (k % 256) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(d) || !al16(grid) || !al16(signs) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
@@ -200,7 +203,7 @@ int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int6
                       void* out, int32_t out_dtype, void* stream) {
   if (!qs || !sb || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
   if (!(group == 32 || group == 64 || group == 128 || group == 256) || k % group) return QMOE_ERR_BLOCK;
-  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (k % 64) return QMOE_ERR_BLOCK;
   if (!al16(qs) || !al16(sb) || !al16(out)) return QMOE_ERR_ALIGN;
   if (rows == 0 || k == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
@@ -234,6 +237,15 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
   return launched();
 }
 
+// ------------------------------------------------------------------ workspace
+
+size_t qmoe_workspace_bytes(int32_t what, const qmoe_weights* w, int64_t t, int32_t topk, int32_t bm) {
+  if (!w || t < 0 || topk < 1 || w->n_experts < 1 || w->n < 1) return 0;
+  if (what == QMOE_WS_PLAN) return qmoe_plan_bytes(t, topk, w->n_experts, bm);
+  if (what == QMOE_WS_COMBINE_ACC) return (size_t)t * (size_t)w->n * sizeof(float);
+  return 0;
+}
+
 // ------------------------------------------------------------------ plan
 
 size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm) {
@@ -243,7 +255,10 @@ size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm) {
   return (size_t)(plan_layout(P, n_experts).total + plan_scratch_words(P, n_experts)) * sizeof(int32_t);
 }
 
+// Tile heights the plan and the gathered matmul accept: a multiple of 16 up
+// to the matmul's register tile (80 rows).
 static bool bm_ok(int bm) { return bm >= 16 && bm <= 128 && bm % 16 == 0; }
+static bool bm_fits(int bm) { return bm <= qmm_max_rows(); }
 
 int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts, int32_t bm,
                   int32_t* plan, size_t plan_bytes, void* stream) {
@@ -251,6 +266,7 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
   if (topk > QMOE_MAX_TOPK || n_experts > QMOE_MAX_EXPERTS) return QMOE_ERR_LIMIT;
   if (t * topk > (1ll << 30)) return QMOE_ERR_LIMIT;
   if (!bm_ok(bm)) return QMOE_ERR_ARG;
+  if (!bm_fits(bm)) return QMOE_ERR_UNSUPPORTED;
   if (!al4(ids) || !al16(plan)) return QMOE_ERR_ALIGN;
   if (plan_bytes < qmoe_plan_bytes(t, topk, n_experts, bm)) return QMOE_ERR_WORKSPACE;
   QMOE_TRY(check_arch());
@@ -284,7 +300,7 @@ int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, i
   if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->group % 64) return QMOE_ERR_UNSUPPORTED;
   if (act_dtype == QMOE_BF16 && w->fmt == QMOE_INT4 && w->k / w->group > qmm_int4_bf16_max_groups())
     return QMOE_ERR_LIMIT;
-  if (bm > qmm_max_rows()) return QMOE_ERR_UNSUPPORTED;
+  if (!bm_fits(bm)) return QMOE_ERR_UNSUPPORTED;
   // activation rows are addressed with 32-bit byte offsets
   if ((a_mode == QMOE_A_GATHER_TOKENS ? t : t * topk) * w->k * 2 >= (1ll << 31)) return QMOE_ERR_LIMIT;
   if (!al16(plan) || !al16(a) || !al16(out)) return QMOE_ERR_ALIGN;
@@ -380,12 +396,7 @@ int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64
     return QMOE_ERR_ARG;
   if (topk > QMOE_MAX_TOPK || b > QMOE_MAX_GEMV_BATCH) return QMOE_ERR_LIMIT;
   if (w->k % 32) return QMOE_ERR_BLOCK;
-  if (w->k > 4096) return QMOE_ERR_LIMIT;
-  {
-    // lanes per row must be a power of two: k/32 in {1, 2, 4, ..., 64} or 128 (two chunks per lane)
-    const int64_t c = w->k / 32;
-    if (c & (c - 1)) return QMOE_ERR_BLOCK;
-  }
+  if (w->k > gemv_max_k()) return QMOE_ERR_LIMIT;
   if (epilogue == QMOE_EPI_SWIGLU) {
     if (w->n % 2) return QMOE_ERR_ARG;
   } else if (epilogue == QMOE_EPI_WEIGHTED_COMBINE) {

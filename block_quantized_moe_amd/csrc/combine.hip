@@ -17,6 +17,12 @@
 
 namespace qmoe {
 
+// The plan must name this call's tokens, top-k and experts (its tile height
+// does not matter here); otherwise its inverse map has another layout.
+__device__ __forceinline__ bool plan_header_ok(const int32_t* plan, int64_t P, int E, int topk) {
+  return plan[4] == (int32_t)(P / topk) && plan[5] == topk && plan[6] == E;
+}
+
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_cast_kernel(float* __restrict__ acc, int64_t n4,
                                                            void* __restrict__ out) {
@@ -56,6 +62,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict
   const int64_t t = blockIdx.x / nb;
   const int64_t n = (blockIdx.x - t * nb) * 256 + threadIdx.x;
   if (n >= N) return;
+  if (!plan_header_ok(plan, P, E, topk)) return;
   const PlanLayout L = plan_layout(P, E);
   float acc = base ? base[t * N + n] * (gate ? sigmoid_f32(gate[t]) : 1.0f) : 0.f;
   for (int j = 0; j < topk; ++j) {
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __rest
   const int64_t t = blockIdx.x / nb;
   const int64_t n0 = ((blockIdx.x - t * nb) * 256 + threadIdx.x) * 8;
   if (n0 >= N) return;
+  if (!plan_header_ok(plan, P, E, topk)) return;
   const PlanLayout L = plan_layout(P, E);
   constexpr int ES = YT == QMOE_F32 ? 4 : 2;  // bytes per y element
   const __amdgpu_buffer_rsrc_t yr =

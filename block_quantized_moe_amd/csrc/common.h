@@ -235,4 +235,12 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t P, int E) {
   return L;
 }
 
+// Whether a plan buffer's header names the call it is used with (tile
+// height, tokens, top-k, experts: words 3..6).  A plan built for another
+// call has other offsets and tile heights; kernels given one do no work
+// rather than read past their arrays.
+__device__ __forceinline__ bool plan_matches(const int32_t* plan, int bm, int64_t t, int topk, int E) {
+  return plan[3] == bm && plan[4] == (int32_t)t && plan[5] == topk && plan[6] == E;
+}
+
 }  // namespace qmoe

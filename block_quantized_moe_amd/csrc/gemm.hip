@@ -68,7 +68,7 @@ struct GemmArgs {
   int64_t a_bytes;  // size of the activation buffer (byte offsets must stay below 2^31)
   const int32_t* plan;
   int E, topk, bm;
-  int64_t P;
+  int64_t P, t;
   int64_t M;  // dense rows
   const float* topk_w;
   void* out;
@@ -793,7 +793,9 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
 
   // The grid is sized for the most tiles a plan can have; blocks past the
   // plan's tiles have no work.
-  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM) : g.plan[1];
+  // A plan whose header names another call gives no tiles.
+  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM)
+                      : plan_matches(g.plan, g.bm, g.t, g.topk, g.E) ? g.plan[1] : 0;
   int mt, nt;
   if (!tile_of_block(blockIdx.x, n_tiles, g.n_ntiles, mt, nt)) return;
 
@@ -809,12 +811,12 @@ __global__ __launch_bounds__(256, 2) void qmm_kernel(GemmArgs g) {
       wts[tid] = 0.f;
     }
   } else {
-    if (mt >= g.plan[1]) return;
     const PlanLayout L = plan_layout(g.P, g.E);
     const int32_t* tl = g.plan + L.tiles + 4 * (int64_t)mt;
     expert = tl[0];
     row0 = tl[1];
-    nrows = tl[2];
+    nrows = min(tl[2], BM);
+    if (expert < 0 || expert >= g.E) return;
     if (tid < BM) {
       int ra = -1, ro = 0;
       float wt = 0.f;
@@ -961,7 +963,9 @@ void qmm_int4_kernel(GemmArgs g) {
 
   // The grid is sized for the most tiles a plan can have; blocks past the
   // plan's tiles have no work.
-  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM) : g.plan[1];
+  // A plan whose header names another call gives no tiles.
+  const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM)
+                      : plan_matches(g.plan, g.bm, g.t, g.topk, g.E) ? g.plan[1] : 0;
   int mt, nt;
   if (!tile_of_block(blockIdx.x, n_tiles, g.n_ntiles, mt, nt)) return;
 
@@ -980,7 +984,8 @@ void qmm_int4_kernel(GemmArgs g) {
     const int32_t* tl = g.plan + L.tiles + 4 * (int64_t)mt;
     expert = tl[0];
     const int row0 = tl[1];
-    nrows = tl[2];
+    nrows = min(tl[2], BM);
+    if (expert < 0 || expert >= g.E) return;
     if (tid < BM) {
       int ra = -1, ro = 0;
       float wt = 0.f;
@@ -1358,6 +1363,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.E = w->n_experts;
   g.topk = topk;
   g.P = t * topk;
+  g.t = t;
   g.M = M;
   g.topk_w = topk_w;
   g.out = out;

@@ -28,11 +28,13 @@
 namespace qmoe {
 
 constexpr int GV_MAXT = 4;  // tokens per pass over the weights
+constexpr int GV_MAX_K = 8192;  // longest reduction: 4 chunks of 32 per lane
 // Unit passes of gemv_rows_kernel whose weight loads are issued together: two
 // when the batch still leaves room for several waves per SIMD (one token per
-// pass, or formats with at most 16 code bytes per chunk), else one.
-__host__ __device__ constexpr int gr_load(int fmt, int mt) {
-  return (mt == 1 || fmt == QMOE_MXFP4 || fmt == QMOE_IQ2_XXS || fmt == QMOE_INT4) ? 2 : 1;
+// pass, or formats with at most 16 code bytes per chunk), else one (always
+// one with four chunks per lane).
+__host__ __device__ constexpr int gr_load(int fmt, int mt, int cpl) {
+  return cpl > 2 ? 1 : (mt == 1 || fmt == QMOE_MXFP4 || fmt == QMOE_IQ2_XXS || fmt == QMOE_INT4) ? 2 : 1;
 }
 
 struct GemvArgs {
@@ -52,7 +54,8 @@ struct GemvArgs {
   const float* topk_w;
   void* out;
   int out_dtype;
-  int lpr;        // lanes per row (K / 32 / CPL, at most 64)
+  int lpr;        // lanes per row (a power of two, at most 64)
+  int chunks;     // 32-value chunks per row (K / 32); lane li takes li, li + lpr, ... below it
   int units_per_wg;
 };
 
@@ -367,14 +370,15 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
         const int s2 = list[tb + t];
         const uint16_t* xr = g.a + (int64_t)(s2 / g.topk) * g.K;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) load_x<ACT, needs_x_sums<FMT>()>(xr + 32 * (int64_t)(li + c * lpr), x[t][c]);
+        for (int c = 0; c < CPL; ++c)
+          load_x<ACT, needs_x_sums<FMT>()>(xr + 32 * (int64_t)min(li + c * lpr, g.chunks - 1), x[t][c]);
       }
     }
     // GR_LOAD unit passes at a time (units_per_wg is a multiple of
     // GR_LOAD * 4 * rpw): every weight load of the batch is issued before the
     // first dot product
     constexpr int NR = swiglu ? 2 : 1;  // weight rows per unit (gate, up)
-    constexpr int GR_LOAD = gr_load(FMT, MT);
+    constexpr int GR_LOAD = gr_load(FMT, MT, CPL);
     for (int ub0 = wave * rpw; ub0 < g.units_per_wg; ub0 += GR_LOAD * 4 * rpw) {
       ChunkRaw wr[GR_LOAD][NR][CPL];
 #pragma unroll
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
 #pragma unroll
         for (int h = 0; h < NR; ++h)
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) wr[i][h][c] = chunk_load<FMT>(g, Rg + h * (g.N / 2), li + c * lpr);
+          for (int c = 0; c < CPL; ++c) wr[i][h][c] = chunk_load<FMT>(g, Rg + h * (g.N / 2), min(li + c * lpr, g.chunks - 1));
       }
 #pragma unroll
       for (int i = 0; i < GR_LOAD; ++i) {
@@ -395,6 +399,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
         for (int t = 0; t < MT; ++t) { r0[t] = 0.f; r1[t] = 0.f; }
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
+          if (li + c * lpr >= g.chunks) continue;  // lanes past the row's last chunk
           XChunk xc[MT];
 #pragma unroll
           for (int t = 0; t < MT; ++t) xc[t] = x[t][c];
@@ -426,7 +431,8 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs g) {
 // Per-token partial sums sit in LDS per wave and are added in wave order, so
 // the result is bit-reproducible.
 constexpr int GC_ITERS = 8;
-constexpr int GC_LOAD = 4;             // row passes whose weight loads are issued together
+// row passes whose weight loads are issued together (one with four chunks per lane)
+__host__ __device__ constexpr int gc_load(int cpl) { return cpl > 2 ? 1 : 4; }
 constexpr int GC_ROWS = GC_ITERS * 4;  // rows per block at most (lpr >= 16)
 
 template <int FMT, int ACT, int CPL, int MT>
@@ -490,7 +496,10 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          if (t < nt) load_x<ACT, needs_x_sums<FMT>()>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)(li + c * lpr), xc[c][t]);
+          if (t < nt)
+            load_x<ACT, needs_x_sums<FMT>()>(g.a + (int64_t)sl[t] * g.K + 32 * (int64_t)min(li + c * lpr, g.chunks - 1),
+                                             xc[c][t]);
+      constexpr int GC_LOAD = gc_load(CPL);
 #pragma unroll
       for (int i0 = 0; i0 < GC_ITERS; i0 += GC_LOAD) {
         // the weight chunks of GC_LOAD row passes, all loads issued first
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
           const int64_t row = n0 + (i0 + i) * rpw + sub;
           const int64_t Rg = (int64_t)e * g.N + (row < g.N ? row : g.N - 1);
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) wr[i][c] = chunk_load<FMT>(g, Rg, li + c * lpr);
+          for (int c = 0; c < CPL; ++c) wr[i][c] = chunk_load<FMT>(g, Rg, min(li + c * lpr, g.chunks - 1));
         }
 #pragma unroll
         for (int i = 0; i < GC_LOAD; ++i) {
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvArgs g) {
           for (int t = 0; t < MT; ++t) r[t] = 0.f;
 #pragma unroll
           for (int c = 0; c < CPL; ++c)
-            chunk_math<FMT, ACT, MT>(g, wr[i][c], li + c * lpr, xc[c], nt, r, lut_grid, lut_sign);
+            if (li + c * lpr < g.chunks) chunk_math<FMT, ACT, MT>(g, wr[i][c], li + c * lpr, xc[c], nt, r, lut_grid, lut_sign);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             if (t < nt) {
@@ -895,10 +904,11 @@ static void launch_gemv_facm(const GemvArgs& g, int epi, int64_t units_total, hi
 
 // One token per call (b = 1): the kernels hold one token's activations per
 // pass instead of GV_MAXT, which frees registers for more waves per SIMD.  A
-// token that names one expert twice still works, in two passes.
+// token that names one expert twice still works, in two passes.  Four chunks
+// per lane (K above 4096) always take one token per pass.
 template <int FMT, int ACT, int CPL>
 static void launch_gemv_fac(const GemvArgs& g, int epi, int64_t units_total, hipStream_t s) {
-  if (g.nslots == g.topk) launch_gemv_facm<FMT, ACT, CPL, 1>(g, epi, units_total, s);
+  if (g.nslots == g.topk || CPL > 2) launch_gemv_facm<FMT, ACT, CPL, 1>(g, epi, units_total, s);
   else launch_gemv_facm<FMT, ACT, CPL, GV_MAXT>(g, epi, units_total, s);
 }
 
@@ -906,16 +916,21 @@ template <int FMT>
 static void launch_gemv_f(const GemvArgs& g, int act, int cpl, int epi, int64_t units, hipStream_t s) {
   if (act == QMOE_F16) {
     if (cpl == 1) launch_gemv_fac<FMT, ACT_F16, 1>(g, epi, units, s);
-    else launch_gemv_fac<FMT, ACT_F16, 2>(g, epi, units, s);
+    else if (cpl == 2) launch_gemv_fac<FMT, ACT_F16, 2>(g, epi, units, s);
+    else launch_gemv_fac<FMT, ACT_F16, 4>(g, epi, units, s);
   } else {
     if (cpl == 1) launch_gemv_fac<FMT, ACT_BF16, 1>(g, epi, units, s);
-    else launch_gemv_fac<FMT, ACT_BF16, 2>(g, epi, units, s);
+    else if (cpl == 2) launch_gemv_fac<FMT, ACT_BF16, 2>(g, epi, units, s);
+    else launch_gemv_fac<FMT, ACT_BF16, 4>(g, epi, units, s);
   }
 }
 
-// Host launcher for qmoe_moe_gemv (arguments already validated; K <= 4096).
-// Returns QMOE_ERR_UNSUPPORTED for a sum-folded call that neither kernel
-// family takes (the generic one needs K >= 512: at most 4 rows per wave pass).
+int64_t gemv_max_k() { return GV_MAX_K; }
+
+// Host launcher for qmoe_moe_gemv (arguments already validated: K a multiple
+// of 32, at most GV_MAX_K).  A row's K / 32 chunks are spread over lpr lanes
+// (a power of two), CPL chunks per lane; lanes whose chunk index lies past
+// the row's last chunk load a valid chunk and skip its arithmetic.
 int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const int32_t* ids,
                  const float* topk_w, int topk, int epi, void* out, int out_dtype, hipStream_t s) {
   GemvArgs g;
@@ -926,25 +941,31 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
   g.a = (const uint16_t*)a; g.ids = ids; g.topk_w = topk_w;
   g.out = out; g.out_dtype = out_dtype;
   const int64_t chunks = w->k / 32;
-  const int cpl = chunks > 64 ? (int)(chunks / 64) : 1;
-  g.lpr = (int)(chunks / cpl);
+  g.chunks = (int)chunks;
+  const int cpl = chunks <= 64 ? 1 : chunks <= 128 ? 2 : 4;
+  int lpr = 64;
+  if (cpl == 1)
+    for (lpr = 1; lpr < chunks; lpr <<= 1) {}
+  // the sum-folded kernel keeps at most 4 rows per wave pass
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE && lpr < 16) lpr = 16;
+  g.lpr = lpr;
   const int rpw = 64 / g.lpr;
   const int64_t units = (epi == QMOE_EPI_SWIGLU) ? w->n / 2 : w->n;
   // Enough workgroups to keep several waves per SIMD waiting on memory: aim
   // for about 4096 in total (measured: 512 left the MXFP4 decode 15-20% slower).
   // The rows kernel takes gr_load passes of 4 * rpw units at a time.
-  const int64_t step = gr_load(w->fmt, g.nslots == topk ? 1 : GV_MAXT) * 4 * rpw;
+  const int mt = (g.nslots == topk || cpl > 2) ? 1 : GV_MAXT;
+  const int64_t step = gr_load(w->fmt, mt, cpl) * 4 * rpw;
   int64_t upw = (units * g.nslots) / 4096;
   if (upw < step) upw = step;
   upw = (upw + step - 1) / step * step;
   if (upw > 64) upw = 64 > step ? 64 : step;
   g.units_per_wg = (int)upw;
-  if (w->fmt == QMOE_INT4 && int4_tiled_ok(g, epi)) {
+  if (w->fmt == QMOE_INT4 && (chunks & (chunks - 1)) == 0 && int4_tiled_ok(g, epi)) {
     if (act == QMOE_F16) launch_gemv_int4_tiled<ACT_F16>(g, epi, s);
     else launch_gemv_int4_tiled<ACT_BF16>(g, epi, s);
     return QMOE_OK;
   }
-  if (epi == QMOE_EPI_WEIGHTED_COMBINE && w->k < 512) return QMOE_ERR_UNSUPPORTED;
   switch (w->fmt) {
     case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
     case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;

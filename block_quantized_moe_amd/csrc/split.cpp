@@ -7,20 +7,29 @@
 // surgery; the DSV4 campaign page repacks q2_K blocks to SoA at load because
 // the AoS code bytes sit at 84*blk+16 and are only 4-byte aligned.  Here every
 // output array is naturally aligned, and the matmul formats are tiled by
-// 16-row blocks for coalesced wave-wide loads.
+// 16-row blocks for coalesced wave-wide loads.  Any row count is accepted:
+// the tiled arrays are sized for rows rounded up to a multiple of 16
+// (qmoe_split_rows), and the rows past the end are written as zeros, so the
+// kernels may read a whole 16-row block even where its tail holds no row.
 #include <stdint.h>
 #include <string.h>
 
 #include "../../include/qmoe.h"
 
+static inline int64_t pad16(int64_t rows) { return (rows + 15) / 16 * 16; }
+
 extern "C" {
+
+int64_t qmoe_split_rows(int64_t rows) { return rows < 0 ? -1 : pad16(rows); }
 
 // Q8_0: codes tiled as [R/16][k/64][4][16][16] (chunk c of 16 values of row
 // 16 rb + r in k tile kt), block scales as [R/16][k/32][16].
 int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16_t* d) {
   if (!aos || !qs || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (k % 64) return QMOE_ERR_BLOCK;
   const int64_t KT = k / 64, NB = k / 32;
+  memset(qs + rows / 16 * 16 * k, 0, (size_t)((pad16(rows) - rows / 16 * 16) * k));
+  memset(d + rows / 16 * 16 * NB, 0, (size_t)((pad16(rows) - rows / 16 * 16) * NB) * 2);
   for (int64_t R = 0; R < rows; ++R) {
     const int64_t rb = R / 16, r = R % 16;
     for (int64_t b = 0; b < NB; ++b) {
@@ -59,8 +68,10 @@ int qmoe_split_fp8(const uint8_t* w, int64_t rows, int64_t k, uint8_t* qs) {
 // lookup then yields elements in k order); exponents as [R/16][k/32][16].
 int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e) {
   if (!aos || !qs || !e || rows < 0 || k < 0) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 64) return QMOE_ERR_BLOCK;
+  if (k % 64) return QMOE_ERR_BLOCK;
   const int64_t KT = k / 64, NB = k / 32;
+  memset(qs + rows / 16 * 16 * k / 8, 0, (size_t)((pad16(rows) - rows / 16 * 16) * k / 8) * 4);
+  memset(e + rows / 16 * 16 * NB, 0, (size_t)((pad16(rows) - rows / 16 * 16) * NB));
   for (int64_t R = 0; R < rows; ++R) {
     const int64_t rb = R / 16, r = R % 16;
     for (int64_t b = 0; b < NB; ++b) {
@@ -91,9 +102,16 @@ int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uin
 int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin) {
   if (!aos || !qs || !scales || !d || !dmin || rows < 0 || k < 0) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  if (k % 256) return QMOE_ERR_BLOCK;
   const int64_t SB = k / 256;
   uint8_t* qb = (uint8_t*)qs;
+  {
+    const int64_t r0 = rows / 16 * 16, np = pad16(rows) - r0;  // rows of the last, partial block
+    memset(qb + r0 * SB * 64, 0, (size_t)(np * SB * 64));
+    memset(scales + r0 * SB * 16, 0, (size_t)(np * SB * 16));
+    memset(d + r0 * SB, 0, (size_t)(np * SB) * 2);
+    memset(dmin + r0 * SB, 0, (size_t)(np * SB) * 2);
+  }
   for (int64_t R = 0; R < rows; ++R) {
     const int64_t rb = R / 16, r = R % 16;
     for (int64_t sb = 0; sb < SB; ++sb) {
@@ -110,8 +128,13 @@ int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint
 
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* ia, uint16_t* d) {
   if (!aos || !ia || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
-  if (rows % 16 || k % 256) return QMOE_ERR_BLOCK;
+  if (k % 256) return QMOE_ERR_BLOCK;
   const int64_t SB = k / 256;
+  {
+    const int64_t r0 = rows / 16 * 16, np = pad16(rows) - r0;
+    memset(ia + r0 * SB * 16, 0, (size_t)(np * SB * 16) * 4);
+    memset(d + r0 * SB, 0, (size_t)(np * SB) * 2);
+  }
   for (int64_t R = 0; R < rows; ++R) {
     const int64_t rb = R / 16, r = R % 16;
     for (int64_t sb = 0; sb < SB; ++sb) {
@@ -141,8 +164,13 @@ int qmoe_split_int4(const uint32_t* words, const uint16_t* scales, const uint16_
                     int64_t rows, int64_t k, int32_t group, uint32_t* qs_out, uint32_t* sb_out) {
   if (!words || !scales || !biases || !qs_out || !sb_out || rows < 0 || k < 0) return QMOE_ERR_ARG;
   if (!(group == 32 || group == 64 || group == 128 || group == 256)) return QMOE_ERR_BLOCK;
-  if (rows % 16 || k % 64 || k % group) return QMOE_ERR_BLOCK;
+  if (k % 64 || k % group) return QMOE_ERR_BLOCK;
   const int64_t kt_n = k / 64, wpr = k / 8, G = k / group;
+  {
+    const int64_t r0 = rows / 16 * 16, np = pad16(rows) - r0;
+    memset(qs_out + r0 * wpr, 0, (size_t)(np * wpr) * 4);
+    memset(sb_out + r0 * G, 0, (size_t)(np * G) * 4);
+  }
   for (int64_t R = 0; R < rows; ++R) {
     const int64_t rb = R / 16, r = R % 16;
     for (int64_t kt = 0; kt < kt_n; ++kt)

@@ -90,21 +90,28 @@ enum {
   QMOE_A_SORTED_ROWS = 1     /* row for sorted position i is a[i, :] (a is [P, K])  */
 };
 
+/* Which caller-owned buffer qmoe_workspace_bytes sizes. */
+enum {
+  QMOE_WS_PLAN = 0,        /* the plan buffer of qmoe_moe_plan                   */
+  QMOE_WS_COMBINE_ACC = 1  /* the fp32 accumulator [t, n] of a WEIGHTED_COMBINE  */
+};
+
 /*
  * A stacked expert weight tensor W[n_experts, n, k] in its GPU-resident split
  * form, as produced from the on-disk blocks by the qmoe_split_* functions
  * ([GGUF] "Design -- CPU-side decomposition"; [DSV4] load-time q2_K SoA
  * repack).  Blocks run along k (the reduction dimension), so y = x . W^T.
  * All pointers are DEVICE pointers, 16-byte aligned; fields a format does not
- * use must be NULL.
+ * use must be NULL.  Every tiled array covers the stacked rows E*n rounded
+ * up to a multiple of 16 (qmoe_split_rows), as the splitters write them.
  *
- *   Q8_0     tiled by qmoe_split_q8_0 (rows = E*n a multiple of 16, k of 64);
+ *   Q8_0     tiled by qmoe_split_q8_0 (k a multiple of 64);
  *            R, rb, r as below, 64-wide k tile kt:
  *            qs     int8  [R/16][k/64][4][16][16]  chunk c (16 values at
  *                                                64kt + 16c) of row 16rb + r
  *            scales fp16  [R/16][k/32][16]       block scale d of row 16rb + r
  *   Q2_K and IQ2_XXS are tiled by qmoe_split_q2_k / qmoe_split_iq2_xxs
- *   (rows = E*n a multiple of 16, k a multiple of 256).  Global row
+ *   (k a multiple of 256).  Global row
  *   R = e*n + row, block rb = R/16, r = R%16, super-block sb (256 values
  *   along k), SB = k/256, t = rb*SB + sb:
  *   Q2_K     qs     u8    [t][2][16][32]         half h of row r's 64 code bytes
@@ -120,8 +127,7 @@ enum {
  *            grid   u8    [256, 8]               magnitude rows
  *            signs  u8    [128]                  sign masks (qmoe_iq2_signs_table)
  *   INT4     value = s*q + b per group of `group` values along k, tiled by
- *            qmoe_split_int4 (rows = E*n must be a multiple of 16, k a multiple
- *            of 64 and of group).  Global row R = e*n + row, block rb = R/16,
+ *            qmoe_split_int4 (k a multiple of 64 and of group).  Global row R = e*n + row, block rb = R/16,
  *            r = R%16, 64-wide k tile kt:
  *            qs     u32 [R/16][k/64][64 lanes][2]   lane l = 16*g + r holds the 16
  *                   codes of row 16*rb + r at k = 64*kt + 16*g .. +15 as two words;
@@ -133,8 +139,7 @@ enum {
  *            group  32, 64, 128 or 256 (bf16 activations in the prefill matmul:
  *                   64, 128 or 256)
  *   MXFP4    value = e2m1(code) * 2^(e - 127) over 32-value blocks (e = 0xFF:
- *            NaN), tiled by qmoe_split_mxfp4 (rows = E*n a multiple of 16, k
- *            of 64).  R, rb, r as above, 64-wide k tile kt:
+ *            NaN), tiled by qmoe_split_mxfp4 (k a multiple of 64).  R, rb, r as above, 64-wide k tile kt:
  *            qs     u32 [R/16][k/64][2][16][4]      word w of block j (32 values
  *                   at 64kt + 32j) of row 16rb + r holds the codes of elements
  *                   8w .. 8w+7 of the block: element 8w+i (i < 4) in the low
@@ -174,20 +179,24 @@ typedef struct qmoe_weights {
  * arrays; [DSV4] load-time q2_K SoA repack).  HOST pointers; the caller
  * uploads the outputs.  `aos` holds the on-disk blocks of a rows x k
  * matrix, row after row (rows * k/32 blocks for Q8_0, rows * k/256 for Q2_K
- * and IQ2_XXS):
+ * and IQ2_XXS).  For a stack of experts, rows = n_experts * n.  Any row count
+ * is accepted; the rows of the tiled outputs past `rows` (up to
+ * qmoe_split_rows(rows)) are written as zeros and never used:
  *   Q8_0     34 B: fp16 d, 32 int8 codes
  *   Q2_K     84 B: 16 scale|min bytes, 64 code bytes, fp16 d, fp16 dmin
  *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
  *   MXFP4    17 B: E8M0 exponent, 16 code bytes (element 2i in the low
  *            nibble of byte i, 2i+1 in its high nibble)  [GGUF MXFP4 "Format"]
  * They come out in the tiled forms above (so that each wave-wide load of
- * the matmul kernels reads contiguous bytes): Q8_0 qs rows*k bytes, scales
- * rows*k/32; Q2_K qs rows*k/4 bytes, scales rows*k/16 bytes, d and dmin
- * rows*k/256; IQ2_XXS qs rows*k/16 u32, d rows*k/256; MXFP4 qs rows*k/8 u32,
- * e rows*k/32 bytes.  Returns QMOE_ERR_ARG on NULL / negative sizes,
- * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0,
- * MXFP4) or 256.
+ * the matmul kernels reads contiguous bytes), with R = qmoe_split_rows(rows):
+ * Q8_0 qs R*k bytes, scales R*k/32; Q2_K qs R*k/4 bytes, scales R*k/16
+ * bytes, d and dmin R*k/256; IQ2_XXS qs R*k/16 u32, d R*k/256; MXFP4 qs
+ * R*k/8 u32, e R*k/32 bytes.  Returns QMOE_ERR_ARG on NULL / negative sizes,
+ * QMOE_ERR_BLOCK unless k is a multiple of 64 (Q8_0, MXFP4) or 256.
  * ------------------------------------------------------------------------ */
+/* rows rounded up to a multiple of 16: the row count every tiled array of
+ * the splitters is sized for (-1 for a negative count). */
+int64_t qmoe_split_rows(int64_t rows);
 int qmoe_split_q8_0(const void* aos, int64_t rows, int64_t k, int8_t* qs, uint16_t* d);
 int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* scales,
                     uint16_t* d, uint16_t* dmin);
@@ -202,8 +211,9 @@ int qmoe_split_fp8(const uint8_t* w, int64_t rows, int64_t k, uint8_t* qs);
  * 8w+i in nibble i of word w, fp16 scales and biases [rows][k/group] -- to the
  * tiled GPU form above: every wave-wide weight load is one contiguous 512-byte
  * block, and one mask-and-or yields two consecutive elements in the two halves
- * of a 32-bit register.  qs_out holds rows*k/8 words, sb_out rows*k/group.
- * QMOE_ERR_BLOCK unless rows % 16 == 0, k % 64 == 0 and k % group == 0. */
+ * of a 32-bit register.  qs_out holds R*k/8 words, sb_out R*k/group (R =
+ * qmoe_split_rows(rows), zero rows past `rows`).  QMOE_ERR_BLOCK unless
+ * k % 64 == 0 and k % group == 0. */
 int qmoe_split_int4(const uint32_t* words, const uint16_t* scales, const uint16_t* biases,
                     int64_t rows, int64_t k, int32_t group, uint32_t* qs_out, uint32_t* sb_out);
 /* The 128-entry IQ2_XXS sign-mask table ([GGUF] sign-fix commit): entry i is
@@ -216,10 +226,11 @@ void qmoe_iq2_signs_table(uint8_t out[128]);
  * commit; [BAGEL] int4 slabs).
  * Decodes every value in fp32 exactly as the format defines it and rounds
  * once (to nearest even) to out_dtype; results are bit-exact.  DEVICE
- * pointers, 16-byte aligned; out holds the rows x k matrix, row-major.
- * QMOE_ERR_BLOCK unless rows % 16 == 0 and k is a multiple of 64 (Q8_0,
- * MXFP4), 256 (Q2_K, IQ2_XXS) or 64 and group (int4).  MXFP4 values past the
- * fp32 range (e = 254, |code value| >= 2) come out as +-inf, e = 0xFF as NaN.
+ * pointers, 16-byte aligned; the inputs are the splitters' tiled arrays for
+ * `rows` rows (any count), out holds the rows x k matrix, row-major.
+ * QMOE_ERR_BLOCK unless k is a multiple of 64 (Q8_0, MXFP4), 256 (Q2_K,
+ * IQ2_XXS) or 64 and group (int4).  MXFP4 values past the fp32 range
+ * (e = 254, |code value| >= 2) come out as +-inf, e = 0xFF as NaN.
  * ------------------------------------------------------------------------ */
 int qmoe_dequant_q8_0(const int8_t* qs, const uint16_t* d, int64_t rows, int64_t k,
                       void* out, int32_t out_dtype, void* stream);
@@ -245,8 +256,12 @@ int qmoe_dequant_fp8(const uint8_t* qs, const float* scales, int64_t rows, int64
  *   x      DEVICE [m, k] act_dtype (QMOE_F16 or QMOE_BF16), rows contiguous
  *   out    DEVICE; STORE: [m, n] out_dtype; SWIGLU: [m, n/2] out_dtype;
  *          ACCUMULATE: fp32 [m, n], y is added to it
- * Any n >= 1 is accepted (tails are masked in the kernel); w->n_experts must
- * be 1.  m = 0 returns QMOE_OK without launching.
+ * Any n >= 1 is accepted (the split arrays are padded to whole 16-row
+ * blocks; tail columns are masked in the kernel), except FP8, whose n is a
+ * multiple of its 128-row scale block (else QMOE_ERR_BLOCK), and SWIGLU,
+ * which needs an even n (QMOE_ERR_ARG).  k is a multiple of 64 and of the
+ * format's block (QMOE_ERR_BLOCK).  w->n_experts must be 1.  m = 0 returns
+ * QMOE_OK without launching.
  * ------------------------------------------------------------------------ */
 int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int64_t m,
                    int32_t epilogue, void* out, int32_t out_dtype, void* stream);
@@ -259,7 +274,10 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
  * ids DEVICE int32 [t, topk]; pair p = row * topk + j.  Pairs with an id
  * outside [0, n_experts) are dropped and counted.  Within an expert, pairs
  * keep ascending pair order; each expert's run is cut into tiles of at most
- * `bm` rows (bm a multiple of 16, at most 128).  The plan is unique.
+ * `bm` rows (bm a multiple of 16 from 16 to 128, else QMOE_ERR_ARG; above
+ * the matmul's 80-row register tile QMOE_ERR_UNSUPPORTED).  The plan is
+ * unique.  The buffer is the call's only scratch: qmoe_plan_bytes (or
+ * qmoe_workspace_bytes(QMOE_WS_PLAN, ...)) gives its size.
  *
  * Layout of the DEVICE int32 plan buffer (size from qmoe_plan_bytes):
  *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts  [7] 0
@@ -290,8 +308,12 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
  *                     by float atomics (order-dependent rounding); topk_w is
  *                     DEVICE fp32 [t, topk].  Finish with qmoe_combine_cast.
  * a, out DEVICE; the plan must come from qmoe_moe_plan with the same t, topk,
- * bm and n_experts == w->n_experts.  Matmul entry points need k to be a
- * multiple of 64 and of the format's block.
+ * bm and n_experts == w->n_experts: the kernels read its header (words 3..6)
+ * and a plan that names another call gives no tiles (out is left as it
+ * was).  Matmul entry points need k to be a multiple of 64 and of the
+ * format's block; any n (as qmoe_qmm_dense).  Determinism is chosen by entry
+ * point rather than a flag: STORE + qmoe_moe_combine is bit-reproducible,
+ * WEIGHTED_COMBINE (atomics) is not.
  * ------------------------------------------------------------------------ */
 int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
                         int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
@@ -302,7 +324,8 @@ int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, i
  * out[t, n] = (base ? base[t, n] : 0) + sum_j topk_w[t, j] * y[pos(t, j), n],
  * j ascending, fp32, one rounding to out_dtype.  y DEVICE [n_valid, N] in
  * y_dtype (sorted order, e.g. a STORE result); base DEVICE fp32 [t, N] or
- * NULL; dropped pairs contribute nothing. */
+ * NULL; dropped pairs contribute nothing.  A plan whose header names other
+ * (t, topk, n_experts) makes the kernel write nothing. */
 int qmoe_moe_combine(const void* y, int32_t y_dtype, const int32_t* plan, int64_t t,
                      int32_t topk, int32_t n_experts, const float* topk_w, int64_t n, const float* base,
                      void* out, int32_t out_dtype, void* stream);
@@ -338,11 +361,11 @@ int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype,
  *   SWIGLU            a = x [b, K];           out [b, topk, N/2]  = silu(g) * u
  *   WEIGHTED_COMBINE  a = h [b, topk, K];     out [b, N] = sum_j topk_w[b, j] *
  *                     (h[b, j] . W[ids[b, j]]^T), j ascending, deterministic
- * a, out, topk_w DEVICE.  K <= 4096 with K/32 a power of two.  On int4 with
- * group >= 64, N a multiple of 16 (32 for SWIGLU) and, for WEIGHTED_COMBINE,
- * topk * ceil(K / 512) <= 16, the tiled matrix-core kernels run; every other
- * call takes the generic kernels, whose WEIGHTED_COMBINE needs K >= 512 (else
- * QMOE_ERR_UNSUPPORTED, nothing launched).
+ * a, out, topk_w DEVICE.  K a multiple of 32 (QMOE_ERR_BLOCK) and at most
+ * 8192 (QMOE_ERR_LIMIT); any N.  On int4 with group >= 64, K <= 4096 with
+ * K/32 a power of two, N a multiple of 16 (32 for SWIGLU) and, for
+ * WEIGHTED_COMBINE, topk * ceil(K / 512) <= 16, the tiled matrix-core
+ * kernels run; every other call takes the generic kernels.
  * ------------------------------------------------------------------------ */
 int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64_t b,
                   const int32_t* ids, const float* topk_w, int32_t topk, int32_t epilogue,
@@ -379,6 +402,16 @@ int qmoe_moe_gemv(const qmoe_weights* w, const void* a, int32_t act_dtype, int64
 int qmoe_router_topk(const void* logits, int32_t logits_dtype, int64_t t, int32_t n_experts,
                      int32_t topk, int32_t scoring, const float* bias, float scale,
                      int32_t* ids, float* weights, void* stream);
+
+/* Bytes of the caller-owned buffer `what` names (QMOE_WS_*), or 0 on a bad
+ * argument:
+ *   QMOE_WS_PLAN         the plan buffer of qmoe_moe_plan for t tokens, topk
+ *                        and w->n_experts experts (= qmoe_plan_bytes);
+ *   QMOE_WS_COMBINE_ACC  the fp32 [t, w->n] accumulator a WEIGHTED_COMBINE
+ *                        gathered matmul adds into.
+ * No other entry point needs scratch: dense qmm, STORE / SWIGLU matmuls,
+ * the combines, the GEMV and the router use only their inputs and outputs. */
+size_t qmoe_workspace_bytes(int32_t what, const qmoe_weights* w, int64_t t, int32_t topk, int32_t bm);
 
 /* QMOE_OK if the current HIP device is gfx950, else QMOE_ERR_ARCH. */
 int qmoe_check_device(void);

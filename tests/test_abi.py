@@ -149,10 +149,10 @@ def test_split_int4_rejects_untileable_shapes():
     s = np.zeros(16 * 96 // 32, np.uint16)
     with pytest.raises(qm.QmoeError):
         qm.split_int4(z, s, s, 16, 96, 32)          # k not a multiple of 64
-    z = np.zeros(8 * 64 // 8, np.uint32)
-    s = np.zeros(8, np.uint16)
+    z = np.zeros(16 * 64 // 8, np.uint32)
+    s = np.zeros(16 * 64 // 48, np.uint16)
     with pytest.raises(qm.QmoeError):
-        qm.split_int4(z, s, s, 8, 64, 64)           # rows not a multiple of 16
+        qm.split_int4(z, s, s, 16, 64, 48)          # group not 32 / 64 / 128 / 256
 
 
 def test_signs_table_matches_oracle():
@@ -173,15 +173,19 @@ def test_argument_validation_before_launch():
     L = qm.lib()
     E = -1
     # plan: topk above 8, experts above 1024, bad bm, NULL ids
-    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 9, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
-    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 2000, 128, ctypes.c_void_p(16), 1 << 20, None) == -4
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 9, 8, 80, ctypes.c_void_p(16), 1 << 20, None) == -4
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 2000, 80, ctypes.c_void_p(16), 1 << 20, None) == -4
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 40, ctypes.c_void_p(16), 1 << 20, None) == E
     assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 144, ctypes.c_void_p(16), 1 << 20, None) == E
-    assert L.qmoe_moe_plan(None, 4, 2, 8, 128, ctypes.c_void_p(16), 1 << 20, None) == E
+    assert L.qmoe_moe_plan(None, 4, 2, 8, 80, ctypes.c_void_p(16), 1 << 20, None) == E
+    # plan tiles taller than the matmul's 80-row register tile are refused,
+    # so a plan and the matmul always accept the same tile heights
+    for bm in (96, 112, 128):
+        assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, bm, ctypes.c_void_p(16), 1 << 20, None) == -2
     # plan buffer too small
-    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(16), 16, None) == -5
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 80, ctypes.c_void_p(16), 16, None) == -5
     # misaligned plan
-    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 128, ctypes.c_void_p(20), 1 << 20, None) == -6
+    assert L.qmoe_moe_plan(ctypes.c_void_p(16), 4, 2, 8, 80, ctypes.c_void_p(20), 1 << 20, None) == -6
     # dequant: NULL / misaligned / bad dtype
     assert L.qmoe_dequant_q8_0(None, ctypes.c_void_p(16), 16, 64, ctypes.c_void_p(16), 1, None) == E
     assert L.qmoe_dequant_q8_0(ctypes.c_void_p(8), ctypes.c_void_p(16), 16, 64, ctypes.c_void_p(16), 1, None) == -6
@@ -189,11 +193,11 @@ def test_argument_validation_before_launch():
     assert L.qmoe_dequant_q8_0(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 96, ctypes.c_void_p(16), 1, None) == -3
     assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 96, 32,
                                ctypes.c_void_p(16), 1, None) == -3
-    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 8, 128, 64,
+    assert L.qmoe_dequant_int4(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 128, 48,
                                ctypes.c_void_p(16), 1, None) == -3
-    # tiled formats: rows not a multiple of 16, k not a multiple of 256
+    # tiled formats: k not a multiple of 256 (any row count is accepted)
     P16 = ctypes.c_void_p(16)
-    assert L.qmoe_dequant_q2_k(P16, P16, P16, P16, 8, 256, P16, 1, None) == -3
+    assert L.qmoe_dequant_q2_k(P16, P16, P16, P16, 8, 320, P16, 1, None) == -3
     assert L.qmoe_dequant_iq2_xxs(P16, P16, P16, P16, 16, 128, P16, 1, None) == -3
     # FP8: rows and k multiples of the 128 x 128 scale block; scales required
     assert L.qmoe_dequant_fp8(P16, P16, 64, 128, P16, 1, None) == -3
@@ -245,3 +249,101 @@ def test_no_gpu_means_arch_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert qm.lib().qmoe_check_device() == -7
+
+
+def _with_zero_rows(aos, rows, k, block_vals, block_bytes, pad):
+    """On-disk blocks of `rows` rows followed by `pad` rows of zero blocks."""
+    a = np.asarray(aos, np.uint8).reshape(rows, k // block_vals, block_bytes)
+    return np.concatenate([a, np.zeros((pad, k // block_vals, block_bytes), np.uint8)])
+
+
+@pytest.mark.parametrize("rows", [1, 5, 20, 33])
+def test_split_any_row_count_pads_with_zero_rows(rows):
+    """Any row count splits: the tiled arrays are sized for split_rows(rows)
+    rows and equal the split of the same matrix with zero rows appended up to
+    the next multiple of 16 (so the kernels may read whole 16-row blocks)."""
+    R = qm.split_rows(rows)
+    assert R % 16 == 0 and rows <= R < rows + 16
+    rng = np.random.default_rng(rows)
+    k = 512
+    for fmt, bv, bb, split in (("q8_0", 32, 34, qm.split_q8_0), ("q2_k", 256, 84, qm.split_q2_k),
+                               ("iq2_xxs", 256, 66, qm.split_iq2_xxs), ("mxfp4", 32, 17, qm.split_mxfp4)):
+        W = synth.weights(fmt, rng, 1, rows, k)
+        got = split(W.blocks, rows, k)
+        ref = split(_with_zero_rows(W.blocks, rows, k, bv, bb, R - rows), R, k)
+        for g, r in zip(got, ref):
+            assert g.size == r.size and np.array_equal(g, r), fmt
+    W = synth.int4(rng, 1, rows, k)
+
+    def pad(a):
+        a = a.reshape(rows, -1)
+        return np.concatenate([a, np.zeros((R - rows, a.shape[1]), a.dtype)])
+
+    got = qm.split_int4(W.qs, W.scale, W.bias, rows, k, 64)
+    ref = qm.split_int4(pad(W.qs), pad(W.scale), pad(W.bias), R, k, 64)
+    for g, r in zip(got, ref):
+        assert g.size == r.size and np.array_equal(g, r)
+
+
+def test_split_rows_and_workspace_bytes():
+    L = qm.lib()
+    assert [qm.split_rows(r) for r in (0, 1, 16, 17, 255)] == [0, 16, 16, 32, 256]
+    assert L.qmoe_split_rows(-3) == -1
+    w = qm._Weights(qm.INT4, 256, 2048, 512, 64, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_workspace_bytes(0, ctypes.byref(w), 2048, 8, 80) == qm.plan_bytes(2048, 8, 256, 80)
+    assert L.qmoe_workspace_bytes(1, ctypes.byref(w), 2048, 8, 80) == 2048 * 2048 * 4
+    assert L.qmoe_workspace_bytes(7, ctypes.byref(w), 2048, 8, 80) == 0
+    assert L.qmoe_workspace_bytes(0, None, 2048, 8, 80) == 0
+
+
+def test_boundary_accepts_any_n_and_long_k():
+    """The argument checks pass (the call then stops at the device check: -7
+    without a GPU) for any output row count n and any decode K that is a
+    multiple of 32 up to 8192; FP8 keeps its 128-row scale blocks."""
+    L = qm.lib()
+    if L.qmoe_check_device() == 0:
+        pytest.skip("a GPU is present: the calls would launch")
+    P = ctypes.c_void_p(16)
+    for n in (1, 40, 200, 1000):
+        w = qm._Weights(qm.Q8_0, 1, n, 256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+        assert L.qmoe_qmm_dense(ctypes.byref(w), P, 1, 4, 0, P, 1, None) == -7
+        w = qm._Weights(qm.INT4, 3, n, 256, 64, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+        assert L.qmoe_moe_gather_qmm(ctypes.byref(w), P, 4, 2, 80, P, 2, 0, None, 0, P, 2, None) == -7
+    for k in (1408, 3072, 7168, 8192):
+        w = qm._Weights(qm.Q8_0, 8, 24, k, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+        assert L.qmoe_moe_gemv(ctypes.byref(w), P, 1, 2, P, P, 4, 2, P, 1, None) == -7
+    w = qm._Weights(qm.Q8_0, 8, 24, 8256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_moe_gemv(ctypes.byref(w), P, 1, 2, P, P, 4, 2, P, 1, None) == -4
+    w = qm._Weights(qm.MXFP4, 8, 24, 96, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_moe_gemv(ctypes.byref(w), P, 1, 2, P, P, 4, 1, P, 1, None) == -3  # k % 64
+    w = qm._Weights(qm.FP8, 1, 200, 256, 0, 0, 16, 0, 16, 0, 0, 0, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), P, 1, 4, 0, P, 1, None) == -3
+
+
+def test_binding_rejects_mis_shaped_tensors():
+    """The binding checks every caller-supplied tensor (shape, dtype,
+    contiguity) before a pointer reaches the library."""
+    torch = pytest.importorskip("torch")
+    w = qm.DeviceWeights("int4", 4, 64, 128, 64, {})
+    with pytest.raises(ValueError):                           # K mismatch
+        qm.qmm_dense(w, torch.zeros((8, 96), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):                           # activations must be f16 / bf16
+        qm.qmm_dense(w, torch.zeros((8, 128), dtype=torch.float32))
+    with pytest.raises(ValueError):                           # not contiguous
+        qm.qmm_dense(w, torch.zeros((128, 8), dtype=torch.bfloat16).t())
+    with pytest.raises(ValueError):                           # ids must be int32
+        qm.moe_plan(torch.zeros((4, 2), dtype=torch.int64), 4)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):                           # plan buffer too small
+        qm.moe_plan(ids, 4, plan=torch.zeros(8, dtype=torch.int32))
+    with pytest.raises(ValueError):                           # GATHER_TOKENS needs [T, K]
+        qm.moe_gather_qmm(w, torch.zeros(4096, dtype=torch.int32), 4, 2, torch.zeros((5, 128), dtype=torch.bfloat16))
+    wd = qm.DeviceWeights("int4", 4, 128, 128, 64, {})
+    with pytest.raises(ValueError):                           # combine GEMV takes [B, topk, K]
+        qm.moe_gemv(wd, torch.zeros((4, 2, 64), dtype=torch.bfloat16), ids, torch.zeros((4, 2)),
+                    epilogue=qm.EPI_WEIGHTED_COMBINE)
+    with pytest.raises(ValueError):                           # topk_w shape
+        qm.moe_combine(torch.zeros((8, 64), dtype=torch.bfloat16), torch.zeros(4096, dtype=torch.int32), 4, 2, 4,
+                       torch.zeros((4, 3)))
+    with pytest.raises(ValueError):                           # out shape
+        qm.combine_cast(torch.zeros((4, 64)), out=torch.zeros((4, 32), dtype=torch.bfloat16))

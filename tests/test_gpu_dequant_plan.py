@@ -160,8 +160,8 @@ def _plan_case(T, k, E, bm, seed, bad=True, skew=False):
     return ids
 
 
-@pytest.mark.parametrize("T,k,E,bm,skew", [(300, 8, 64, 128, False), (1, 1, 4, 16, False),
-                                           (2048, 8, 256, 64, False), (4096, 8, 256, 128, True),
+@pytest.mark.parametrize("T,k,E,bm,skew", [(300, 8, 64, 80, False), (1, 1, 4, 16, False),
+                                           (2048, 8, 256, 64, False), (4096, 8, 256, 48, True),
                                            (513, 6, 1024, 32, False)])
 def test_plan_exact(T, k, E, bm, skew):
     ids = _plan_case(T, k, E, bm, 7 + T, skew=skew)

@@ -13,7 +13,10 @@ on sampled outputs that the fp64 oracle computes one by one:
 
 Stage-wise (each GEMM is fed the bytes the GPU consumed): sampled h entries
 against the oracle's gate/up rows, sampled outputs against the oracle's down
-rows fed the GPU's h.  Tolerance: the normwise 2e-3 bound of tests/_helpers.
+rows fed the GPU's h.  End to end: sampled outputs against the oracle's whole
+FFN for those tokens, with h rounded to the activation dtype where the GPU
+stores it (reading c9) and nothing else taken from the GPU.  Tolerance: the
+normwise 2e-3 bound of tests/_helpers.
 """
 import numpy as np
 import pytest
@@ -67,6 +70,25 @@ def _h_rows(inp, plan, h, tokens):
     return {p: hh[i] for i, p in enumerate(pairs)}
 
 
+def _check_end_to_end(inp, out, rng, n_tokens, n_cols=64, base_rows=None):
+    """Sampled outputs against the oracle's FFN for n_tokens tokens: h of every
+    pair of those tokens over all I columns, rounded to the activation dtype,
+    then down + weighted combine on n_cols sampled columns (plus the shared
+    expert's rows, formed the same way, when base_rows is given)."""
+    tokens = rng.choice(inp.T, n_tokens, replace=False)
+    cols = rng.choice(inp.H, n_cols, replace=False)
+    x64 = oracle.act_to_f64(inp.x, inp.act)
+    pairs = [int(t) * inp.k + j for t in tokens for j in range(inp.k)]
+    h = oracle.moe_gate_up_rows(x64, inp.ids, inp.w_gate_up, pairs, np.arange(inp.I))
+    h = oracle.out_to_f64(oracle.round_out(h, inp.act), inp.act)
+    ref = oracle.moe_down_rows({p: h[i] for i, p in enumerate(pairs)}, inp.ids, inp.w, inp.w_down, tokens, cols)
+    if base_rows is not None:
+        ref = ref + base_rows(tokens, cols)
+    got = to_f64(out[torch.from_numpy(tokens).long().cuda()])[:, cols]
+    err = normwise_err(got, ref, inp.out)
+    assert err <= TOL, ("end to end", err, report(got, ref))
+
+
 def test_fullsize_qwen_a3b_int4_prefill():
     inp = synth.qwen_a3b_prefill(2048)
     rng = np.random.default_rng(101)
@@ -79,6 +101,7 @@ def test_fullsize_qwen_a3b_int4_prefill():
     got = to_f64(out[torch.from_numpy(tokens).long().cuda()])[:, cols]
     err = normwise_err(got, ref, inp.out)
     assert err <= TOL, ("down+combine", err, report(got, ref))
+    _check_end_to_end(inp, out, rng, 16)
 
 
 @pytest.mark.parametrize("experts", ["iq2_xxs/q2_k", "mxfp4", "fp8"])
@@ -96,6 +119,7 @@ def test_fullsize_dsv4_flash_prefill(experts):
     got = to_f64(out[torch.from_numpy(tokens).long().cuda()])[:, cols]
     err = normwise_err(got, ref, inp.out)
     assert err <= TOL, ("down+combine", err, report(got, ref))
+    _check_end_to_end(inp, out, rng, 8)
 
 
 def test_fullsize_mixed_ffn_block():
@@ -132,6 +156,17 @@ def test_fullsize_mixed_ffn_block():
     got = to_f64(out[tok_d])[:, cols]
     err = normwise_err(got, ref, inp.out)
     assert err <= TOL, ("down+combine+shared", err, report(got, ref))
+    # end to end: routed FFN plus the shared expert, every h rounded to the
+    # activation dtype where the GPU stores it
+
+    def shared_rows(tok, c):
+        Wsg = oracle.dequant_rows(inp.shared_gate_up, 0, np.arange(2 * SI)).astype(np.float64)
+        g = x64[tok] @ Wsg.T
+        hs_ref = oracle.silu(g[:, :SI]) * g[:, SI:]
+        hs_ref = oracle.out_to_f64(oracle.round_out(hs_ref, inp.act), inp.act)
+        return hs_ref @ oracle.dequant_rows(inp.shared_down, 0, c).astype(np.float64).T
+
+    _check_end_to_end(inp, out, rng, 8, base_rows=shared_rows)
     # the four projections
     for j, Wp in enumerate(inp.projections):
         pc = rng.choice(inp.H, 64, replace=False)
