@@ -83,6 +83,10 @@ _SIGS = {
     "qmoe_check_device": [],
     "qmoe_strerror": [ctypes.c_int],
     "qmoe_split_rows": [ctypes.c_int64],
+    "qmoe_moe_gather_qmm_combine_static": [ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "qmoe_static_acc_bytes": [],
     "qmoe_workspace_bytes": [ctypes.c_int32, ctypes.POINTER(_Weights), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32],
 }
 EXPORTS = tuple(_SIGS)
@@ -102,6 +106,7 @@ def lib():
         L.qmoe_plan_bytes.restype = ctypes.c_size_t
         L.qmoe_workspace_bytes.restype = ctypes.c_size_t
         L.qmoe_split_rows.restype = ctypes.c_int64
+        L.qmoe_static_acc_bytes.restype = ctypes.c_size_t
         L.qmoe_strerror.restype = ctypes.c_char_p
         L.qmoe_iq2_signs_table.restype = None
         _lib = L
@@ -487,6 +492,28 @@ def _combine_checks(y, plan, T, topk, E, topk_w, out):
         raise ValueError("plan: smaller than a plan for this call")
     _need(topk_w, "topk_w", shape=(T, topk), dtypes=(torch.float32,))
     _need(out, "out", shape=(T, y.shape[1]), dtypes=_outs())
+
+
+def moe_gather_qmm_combine_static(w: DeviceWeights, plan, T: int, topk: int, a, topk_w, *, bm: int = 80,
+                                  a_mode: int = A_SORTED_ROWS, out_dtype: int = BF16, out=None):
+    """WEIGHTED_COMBINE gathered matmul plus the cast, with the fp32
+    accumulator inside the library (no allocation in the call; include/qmoe.h)."""
+    import torch
+    _need(a, "a", dim=2, cols=w.K, dtypes=_acts())
+    if a_mode == A_GATHER_TOKENS and a.shape[0] != T:
+        raise ValueError(f"a: GATHER_TOKENS takes [T={T}, K] activations, got {tuple(a.shape)}")
+    _need(plan, "plan", dtypes=(torch.int32,))
+    if plan.numel() * 4 < plan_bytes(T, topk, w.E, bm):
+        raise ValueError("plan: smaller than a plan for this call")
+    _need(topk_w, "topk_w", shape=(T, topk), dtypes=(torch.float32,))
+    if out is None:
+        out = torch.empty((T, w.N), dtype=_dt(out_dtype), device=a.device)
+    _need(out, "out", shape=(T, w.N), dtypes=_outs())
+    ws = w.struct()
+    _check(lib().qmoe_moe_gather_qmm_combine_static(ctypes.byref(ws), _ptr(plan), T, topk, bm, _ptr(a), _code(a),
+                                                    a_mode, _ptr(topk_w), _ptr(out), _code(out), _stream()),
+           "moe_gather_qmm_combine_static")
+    return out
 
 
 def moe_combine(y, plan, T: int, topk: int, E: int, topk_w, base=None, out_dtype: int = BF16, out=None):

@@ -277,10 +277,10 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
 
 // ------------------------------------------------------------------ gathered MoE qmm
 
-int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
-                        int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
-                        const float* topk_w, int32_t epilogue, void* out, int32_t out_dtype,
-                        void* stream) {
+// Argument checks of the gathered matmul (shared by the no-allocation variant).
+static int gather_checks(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk, int32_t bm,
+                         const void* a, int32_t act_dtype, int32_t a_mode, const float* topk_w,
+                         int32_t epilogue, const void* out, int32_t out_dtype) {
   QMOE_TRY(check_weights(w, true));
   if (!plan || !a || !out || t < 0 || topk < 1 || !act_ok(act_dtype) || !dtype_ok(out_dtype))
     return QMOE_ERR_ARG;
@@ -304,6 +304,14 @@ int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, i
   // activation rows are addressed with 32-bit byte offsets
   if ((a_mode == QMOE_A_GATHER_TOKENS ? t : t * topk) * w->k * 2 >= (1ll << 31)) return QMOE_ERR_LIMIT;
   if (!al16(plan) || !al16(a) || !al16(out)) return QMOE_ERR_ALIGN;
+  return QMOE_OK;
+}
+
+int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
+                        int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
+                        const float* topk_w, int32_t epilogue, void* out, int32_t out_dtype,
+                        void* stream) {
+  QMOE_TRY(gather_checks(w, plan, t, topk, bm, a, act_dtype, a_mode, topk_w, epilogue, out, out_dtype));
   if (t == 0) return QMOE_OK;
   QMOE_TRY(check_arch());
   launch_qmm(w, a, act_dtype, a_mode == QMOE_A_GATHER_TOKENS ? 0 : 1, plan, t, topk, bm, 0, topk_w,
@@ -364,6 +372,77 @@ int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype,
   launch_combine_cast(acc, n_elems, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
+
+// ------------------------------------------------------------------ no-allocation variant
+//
+// The WEIGHTED_COMBINE gathered matmul plus the cast, with its fp32
+// accumulator in a fixed device array instead of a caller buffer, for
+// callers that cannot allocate (code under graph capture, tight serving
+// loops).  Every call on a device shares that device's copy of the array.
+
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kStaticAccBytes = size_t(32) << 20;  // 32 MiB: t * n <= 8M fp32 values
+
+static __device__ __align__(256) float scratch[kStaticAccBytes / sizeof(float)];
+
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current (each GPU holds its own copy at its own address).  The
+// array's name is only a host stand-in and is never passed to a kernel.
+int scratch_ptr(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMOE_ERR_ARCH;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return QMOE_ERR_LAUNCH;
+    p = (float*)q;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return QMOE_OK;
+}
+
+// Zero n floats (a kernel rather than a memset, so the call can be captured).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    ((f4_t*)p)[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t tail = n4 * 4 + blockIdx.x * 256ll + threadIdx.x;
+  if (blockIdx.x == 0 && tail < n) p[tail] = 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmoe_moe_gather_qmm_combine_static(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
+                                       int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
+                                       const float* topk_w, void* out, int32_t out_dtype, void* stream) {
+  QMOE_TRY(gather_checks(w, plan, t, topk, bm, a, act_dtype, a_mode, topk_w, QMOE_EPI_WEIGHTED_COMBINE, out,
+                         QMOE_F32));
+  if (!dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if ((size_t)t * (size_t)w->n * sizeof(float) > kStaticAccBytes) return QMOE_ERR_WORKSPACE;
+  if (t == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  float* acc = nullptr;
+  QMOE_TRY(scratch_ptr(&acc));
+  const int64_t n = t * w->n;
+  const hipStream_t s = (hipStream_t)stream;
+  int64_t grid = (n / 4 + 255) / 256;
+  grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, acc, n);
+  launch_qmm(w, a, act_dtype, a_mode == QMOE_A_GATHER_TOKENS ? 0 : 1, plan, t, topk, bm, 0, topk_w,
+             QMOE_EPI_WEIGHTED_COMBINE, acc, QMOE_F32, s);
+  launch_combine_cast(acc, n, out, out_dtype, s);
+  return launched();
+}
+
+size_t qmoe_static_acc_bytes(void) { return kStaticAccBytes; }
 
 // ------------------------------------------------------------------ router top-k
 

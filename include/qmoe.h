@@ -352,6 +352,26 @@ int qmoe_moe_combine_shared(const void* y, int32_t y_dtype, const int32_t* plan,
  * of a WEIGHTED_COMBINE is ready for the next call).  DEVICE pointers. */
 int qmoe_combine_cast(float* acc, int64_t n_elems, void* out, int32_t out_dtype, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the
+ * WEIGHTED_COMBINE gathered matmul followed by the cast, as
+ *   qmoe_moe_gather_qmm(..., QMOE_EPI_WEIGHTED_COMBINE, acc, QMOE_F32) then
+ *   qmoe_combine_cast(acc, t * w->n, out, out_dtype),
+ * but with the fp32 accumulator acc in a fixed array inside the library
+ * (qmoe_static_acc_bytes() bytes, 32 MiB, held on each GPU the library runs
+ * on until the process ends) instead of a caller buffer.  Arguments as
+ * qmoe_moe_gather_qmm; out DEVICE [t, w->n] in out_dtype (F32 / F16 / BF16),
+ * 16-byte aligned.  The call clears the accumulator first (a kernel, no
+ * memset), so no earlier call's contents matter; it allocates nothing.
+ * QMOE_ERR_WORKSPACE when t * w->n * 4 exceeds qmoe_static_acc_bytes().  All
+ * calls on one GPU share its array: calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results. */
+int qmoe_moe_gather_qmm_combine_static(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
+                                       int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,
+                                       const float* topk_w, void* out, int32_t out_dtype, void* stream);
+/* Size in bytes of the fixed accumulator of qmoe_moe_gather_qmm_combine_static. */
+size_t qmoe_static_acc_bytes(void);
+
 /* ------------------------------------------------------------------------
  * Decode GEMV ([BAGEL] expert-indexed int4 GEMV reading expert ids on the
  * device; [DSV4] small-batch qgemv and the sum-folded q2_K down projection).
