@@ -1,27 +1,37 @@
 """Benchmark of the block-quantized MoE expert matmul on one MI355X.
 
-Step (the timed unit): one pass of the whole prefill MoE hot path over the
-Qwen3.6-A3B-shaped int4 workload -- routing plan, gathered gate/up GEMM with
-the SwiGLU epilogue, gathered down GEMM into per-pair rows, and the
-deterministic top-k weighted combine -- for T = 2048 tokens, hidden 2048, 256 experts, top-8,
-expert intermediate 512, bf16 activations, int4 affine weights (group 64).
-The weights rotate over R copies so no step finds them in the 256 MB
-Infinity Cache.  `value` is algorithmic TFLOP/s of that step (routed pairs
-only; padding is not counted).
+Step (the timed unit of `value`): one pass of the whole prefill MoE hot path
+over the Qwen3.6-A3B-shaped int4 workload -- routing plan, gathered gate/up
+GEMM with the SwiGLU epilogue, gathered down GEMM into per-pair rows, and the
+deterministic top-k weighted combine -- for T = 2048 tokens, hidden 2048, 256
+experts, top-8, expert intermediate 512, bf16 activations, int4 affine
+weights (group 64).  The weights rotate over R copies so no step finds them
+in the 256 MB Infinity Cache.  `value` is algorithmic TFLOP/s of that step
+(routed pairs only; padding is not counted), from the wall clock over K
+steps; per-step and per-kernel times (HIP events on the launch stream) are
+reported as p10 / p50 / p90.
 
-The decode GEMV leg (same model, B in {1, 4, 8}, 40 layers, each with its own
-copy of the weights) is timed as a captured HIP graph replay and eagerly; its
-GB/s are weight + activation bytes per layer over graph time per layer.  The
-DSv4-flash-shaped prefill (IQ2_XXS gate/up, Q2_K down, fp16, T = 2048) and the
-mixed-format FFN block (T = 8192, plus a Q8_0 shared expert; its four Q8_0
-projections timed apart) are reported under other_prefill_workloads.  The
-CPU oracle baseline is reported in the same JSON line.
+Also in the same JSON line:
+  * roofline       the headline workload's dominant kernel (int4 gate/up);
+  * rooflines      every workload's kernels against their own bound: the
+                   Qwen-shaped down GEMM and combine, the DSv4-flash-shaped
+                   prefill (IQ2_XXS gate/up, Q2_K down, fp16; also with MXFP4
+                   and FP8 block experts), the mixed-format FFN block
+                   (T = 8192, Zipf routing, Q8_0 shared expert and four Q8_0
+                   4096 x 4096 projections) and the decode kernels;
+  * dense_q8_0     the M=32 N=256 K=2048 dense Q8_0 cell (launch-bound);
+  * decode         the Qwen-shaped decode GEMV (B in {1, 4, 8}, 40 layers
+                   with their own weight copies) as graph replays;
+  * imbalance      per-expert row statistics of the Zipf-routed block;
+  * cpu_baseline   the oracle on the headline workload, and cpu_oracle on
+                   bounded samples of the others (1-core and all-core C1).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-extra]
+                    [--only {qwen,dense,decode,dsv4,dsv4-mxfp4,dsv4-fp8,mixed,router}]
 
-Counter calibration and the traffic record (see profiles/):
+Counter calibration and traffic records (see profiles/):
     python bench.py --copy-probe MIB
-    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR MIB
+    python bench.py --summarize-traffic NAME KERNEL ALG_BYTES FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR MIB
 """
 from __future__ import annotations
 
@@ -38,15 +48,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_BF16 = 2.5166e15   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 PEAK_HBM = 8.0e12            # bytes/s
+N_CU = 256
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def act_tensor(torch, bits):
-    """uint16 bf16 bit patterns -> a bf16 tensor on the GPU."""
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+def pct(values, scale=1.0):
+    v = np.asarray(values, dtype=np.float64) * scale
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.median(v)), "p90": float(np.percentile(v, 90))}
+
+
+def act_tensor(torch, bits, dtype="bf16"):
+    """uint16 bit patterns -> an fp16 / bf16 tensor on the GPU."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to("cuda")
 
 
 def upload(qm, W):
@@ -57,103 +74,70 @@ def upload(qm, W):
     return qm.upload(W.fmt, W.E, W.N, W.K, blocks=W.blocks, grid=W.grid)
 
 
+def roof(kernel, workload, flops, nbytes, t, traffic=None, note=None):
+    """A kernel against its own roofline: algorithmic bytes and flops per
+    launch over the launch's duration; the bound is whichever peak the work
+    needs longer on."""
+    hbm = nbytes / t / PEAK_HBM
+    mfma = flops / t / PEAK_MFMA_BF16
+    bound = "hbm" if nbytes / PEAK_HBM >= flops / PEAK_MFMA_BF16 else "mfma"
+    r = {"kernel": kernel, "workload": workload, "bound": bound,
+         "achieved": nbytes / t / 1e9 if bound == "hbm" else flops / t / 1e12,
+         "peak": PEAK_HBM / 1e9 if bound == "hbm" else PEAK_MFMA_BF16 / 1e12,
+         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+         "frac": hbm if bound == "hbm" else mfma, "traffic": traffic,
+         "algorithmic_bytes_per_launch": int(nbytes), "algorithmic_flops_per_launch": float(flops),
+         "launch_us": t * 1e6, "hbm_frac": hbm, "mfma_frac": mfma}
+    if note:
+        r["note"] = note
+    return r
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
 def prefill_inputs(T):
     import synth
     return synth.qwen_a3b_prefill(T)
 
 
-def algorithmic(inp):
-    """Flops and bytes of one prefill step (routed pairs only)."""
-    P = int(inp.ids.size)
-    H, I = inp.H, inp.I
+def algorithmic(inp, wbytes_gu=None, wbytes_dn=None):
+    """Flops and bytes of one prefill step (routed pairs only), and of each
+    kernel as launched (the down GEMM writes per-pair rows that the combine
+    reads back)."""
+    P = int(((inp.ids >= 0) & (inp.ids < inp.E)).sum())
+    H, I, T = inp.H, inp.I, inp.T
+    act = 2
+    wgu = inp.w_gate_up.nbytes if wbytes_gu is None else wbytes_gu
+    wdn = inp.w_down.nbytes if wbytes_dn is None else wbytes_dn
     flops_gu = 2.0 * P * (2 * I) * H
     flops_dn = 2.0 * P * H * I
-    wbytes_gu = inp.w_gate_up.nbytes
-    wbytes_dn = inp.w_down.nbytes
-    act = 2  # bf16
-    bytes_gu = wbytes_gu + inp.T * H * act + P * I * act    # weights + x read + h write
-    bytes_dn = wbytes_dn + P * I * act + inp.T * H * act    # weights + h read + out write
+    ob = 2 if inp.out in ("f16", "bf16") else 4
     return dict(P=P, flops=flops_gu + flops_dn, flops_gu=flops_gu, flops_dn=flops_dn,
-                bytes=bytes_gu + bytes_dn, bytes_gu=bytes_gu, bytes_dn=bytes_dn)
+                # the method's bytes: weights, x, h written and read once, out
+                bytes=wgu + wdn + T * H * act + 2 * P * I * act + T * H * ob,
+                bytes_gu=wgu + T * H * act + P * I * act,                 # weights + x read + h write
+                bytes_dn=wdn + P * I * act + P * H * act,                 # weights + h read + y rows write
+                bytes_cb=P * H * act + T * inp.k * 8 + T * H * ob)        # y rows read + plan/w + out write
 
 
-def run_prefill(args, torch, qm):
-    inp = prefill_inputs(2048)
-    alg = algorithmic(inp)
-    dev = "cuda"
-    x = act_tensor(torch, inp.x)
-    ids = torch.from_numpy(inp.ids).to(dev)
-    w = torch.from_numpy(inp.w).to(dev)
-    gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
-    R = args.rotate
-    gus = [gu0] + [gu0.clone() for _ in range(R - 1)]
-    dns = [dn0] + [dn0.clone() for _ in range(R - 1)]
-    T, k, E, I = inp.T, inp.k, inp.E, inp.I
-    bm = 80
-    plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
-    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((T * k, inp.H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, inp.H), dtype=torch.bfloat16, device=dev)
-
-    ev = {name: [] for name in ("plan", "gate_up", "down", "combine")}
-
-    def step(i, timed):
-        gu, dn = gus[i % R], dns[i % R]
-        marks = []
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.moe_plan(ids, E, bm, plan=plan)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.moe_gather_qmm(gu, plan, T, k, x, bm=bm, epilogue=qm.EPI_SWIGLU, out=h)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.moe_gather_qmm(dn, plan, T, k, h, bm=bm, a_mode=qm.A_SORTED_ROWS, epilogue=qm.EPI_STORE, out=y)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        qm.moe_combine(y, plan, T, k, E, w, out=out)
-        if timed:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record()
-        return marks
-
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    # K steps launched from the host, wall clock.  (A HIP graph of the step
-    # measured slower here: 320 against 294 us, the graph launch costing more
-    # than the four host launches it replaces.)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, False)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
-    # per-kernel durations (events on the launch stream) over another K steps
-    all_marks = [step(i, True) for i in range(args.steps)]
-    torch.cuda.synchronize()
-    for m in all_marks:
-        for j, name in enumerate(("plan", "gate_up", "down", "combine")):
-            ev[name].append(m[j].elapsed_time(m[j + 1]) * 1e-3)
-    kern = {n: float(np.median(v)) for n, v in ev.items()}
-    return inp, alg, wall, kern
-
-
-def run_prefill_other(args, torch, qm, inp, R, steps):
-    """Another prefill workload, the same step as run_prefill (plan, gate/up
-    with SwiGLU, down with the weighted scatter-add, cast), plus the shared
-    expert (added into the same accumulator) when the workload has one; its
-    dense projections are timed separately."""
+def run_prefill(args, torch, qm, inp, R, steps, warmup, bm=80):
+    """The prefill step of a workload: plan, gate/up with SwiGLU, down into
+    per-pair rows, the deterministic combine (plus the shared expert into the
+    combine's fp32 base when the workload has one).  Returns the wall time per
+    step over `steps` launched back to back and event timings per step and
+    per kernel over another `steps`."""
     dev = "cuda"
     codes = {"f16": qm.F16, "bf16": qm.BF16}
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
-    x = act_tensor(torch, inp.x) if inp.act == "bf16" else \
-        torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.float16)
+    x = act_tensor(torch, inp.x, inp.act)
     ids = torch.from_numpy(inp.ids).to(dev)
     w = torch.from_numpy(inp.w).to(dev)
     gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
     gus = [gu0] + [gu0.clone() for _ in range(R - 1)]
     dns = [dn0] + [dn0.clone() for _ in range(R - 1)]
     T, k, E, H, I = inp.T, inp.k, inp.E, inp.H, inp.I
-    bm = 80
     plan = torch.empty(qm.plan_bytes(T, k, E, bm) // 4, dtype=torch.int32, device=dev)
     h = torch.empty((T * k, I), dtype=tdt[inp.act], device=dev)
     y = torch.empty((T * k, H), dtype=tdt[inp.act], device=dev)
@@ -189,55 +173,158 @@ def run_prefill_other(args, torch, qm, inp, R, steps):
         mark()
         return marks
 
-    for i in range(2):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    # K steps launched from the host back to back, wall clock (a HIP graph of
+    # the step measured slower here than the four host launches it replaces)
+    t0 = time.perf_counter()
     for i in range(steps):
         step(i, False)
-    e1.record()
     torch.cuda.synchronize()
-    t_step = e0.elapsed_time(e1) * 1e-3 / steps
+    wall = (time.perf_counter() - t0) / steps
     all_marks = [step(i, True) for i in range(steps)]
     torch.cuda.synchronize()
-    kern = {n: float(np.median([m[j].elapsed_time(m[j + 1]) for m in all_marks])) * 1e-3
-            for j, n in enumerate(names)}
-    P = int(inp.ids.size)
-    flops = 2.0 * P * 3 * I * H
-    if shared:
-        SI = inp.shared_down.K
-        flops += 2.0 * T * 3 * SI * H
-    res = dict(workload=inp.name, tokens=T, hidden=H, intermediate=I, experts=E, top_k=k,
-               weights=f"gate/up {inp.w_gate_up.fmt}, down {inp.w_down.fmt}" + (", shared expert q8_0" if shared else ""),
-               activations=inp.act, weight_copies_rotated=R, ms_per_step=t_step * 1e3,
-               tflops=flops / t_step / 1e12, mfma_frac=flops / t_step / PEAK_MFMA_BF16,
-               kernels_us={n: v * 1e6 for n, v in kern.items()})
+    kern = {n: [m[j].elapsed_time(m[j + 1]) * 1e-3 for m in all_marks] for j, n in enumerate(names)}
+    step_t = [m[0].elapsed_time(m[-1]) * 1e-3 for m in all_marks]
+    res = dict(wall=wall, kern=kern, step=step_t, wbytes_gu=gu0.nbytes, wbytes_dn=dn0.nbytes)
     if inp.projections:
         ps = [upload(qm, Wp) for Wp in inp.projections]
-        y = torch.empty((T, H), dtype=tdt[inp.act], device=dev)
+        yp = torch.empty((T, H), dtype=tdt[inp.act], device=dev)
         for Wp in ps:
-            qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=y)
+            qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=yp)
         torch.cuda.synchronize()
-        e0.record()
+        per = []
         for _ in range(steps):
-            for Wp in ps:
-                qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=y)
-        e1.record()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(ps) + 1)]
+            e[0].record()
+            for j, Wp in enumerate(ps):
+                qm.qmm_dense(Wp, x, qm.EPI_STORE, codes[inp.act], out=yp)
+                e[j + 1].record()
+            per.append(e)
         torch.cuda.synchronize()
-        tp = e0.elapsed_time(e1) * 1e-3 / steps
-        pf = 2.0 * T * H * H * len(ps)
-        res["projections"] = dict(count=len(ps), ms=tp * 1e3, tflops=pf / tp / 1e12, mfma_frac=pf / tp / PEAK_MFMA_BF16)
+        res["projection"] = [p[j].elapsed_time(p[j + 1]) * 1e-3 for p in per for j in range(len(ps))]
+        res["projection_bytes"] = ps[0].nbytes
         del ps
     del gus, dns
     torch.cuda.empty_cache()
     return res
 
 
-def run_router(args, torch, qm):
+def imbalance(inp, bm=80, bn_gu=128, bn_dn=256):
+    """Per-expert row statistics of a routing, and what they do to the
+    gathered matmuls' launches (tiles of at most bm rows; gate/up workgroups
+    cover bn_gu output columns, down workgroups bn_dn)."""
+    flat = inp.ids.reshape(-1)
+    c = np.bincount(flat[(flat >= 0) & (flat < inp.E)], minlength=inp.E)
+    tiles = int(np.sum((c + bm - 1) // bm))
+    rows16 = int(np.sum((c + 15) // 16 * 16))
+    wg_gu = tiles * -(-inp.I // bn_gu)
+    wg_dn = tiles * -(-inp.H // bn_dn)
+    return {"rows_per_expert": {"max": int(c.max()), "median": float(np.median(c)), "min": int(c.min()),
+                                "mean": float(c.mean()), "empty_experts": int((c == 0).sum())},
+            "hottest_expert_share": float(c.max() / c.sum()),
+            "tiles_bm80": tiles, "hottest_expert_tiles": int(-(-c.max() // bm)),
+            "rows_padded_to_16_over_routed": rows16 / float(c.sum()),
+            "gate_up_workgroups": wg_gu, "gate_up_workgroups_per_cu": wg_gu / N_CU,
+            "down_workgroups": wg_dn, "down_workgroups_per_cu": wg_dn / N_CU}
+
+
+def prefill_line(name, inp, res, R):
+    alg = algorithmic(inp, res["wbytes_gu"], res["wbytes_dn"])
+    kern = res["kern"]
+    t_step = float(np.median(res["step"]))
+    flops = alg["flops"]
+    if inp.shared_gate_up is not None:
+        flops += 2.0 * inp.T * 3 * inp.shared_down.K * inp.H
+    out = dict(workload=inp.name, tokens=inp.T, hidden=inp.H, intermediate=inp.I, experts=inp.E, top_k=inp.k,
+               weights=f"gate/up {inp.w_gate_up.fmt}, down {inp.w_down.fmt}"
+                       + (", shared expert q8_0" if inp.shared_gate_up is not None else ""),
+               activations=inp.act, weight_copies_rotated=R, ms_per_step=t_step * 1e3,
+               step_us=pct(res["step"], 1e6), tflops=flops / t_step / 1e12, mfma_frac=flops / t_step / PEAK_MFMA_BF16,
+               tokens_per_s=inp.T / t_step,
+               kernels_us={n: pct(v, 1e6) for n, v in kern.items()})
+    rl = [roof(f"gate/up {inp.w_gate_up.fmt} SWIGLU", name, alg["flops_gu"], alg["bytes_gu"],
+               float(np.median(kern["gate_up"])), traffic_from_profiles(f"gate_up_{name}")),
+          roof(f"down {inp.w_down.fmt} STORE (per-pair rows)", name, alg["flops_dn"], alg["bytes_dn"],
+               float(np.median(kern["down"])), traffic_from_profiles(f"down_{name}")),
+          roof("combine (deterministic, fp32)", name, 2.0 * alg["P"] * inp.H, alg["bytes_cb"],
+               float(np.median(kern["combine"])))]
+    if "projection" in res:
+        pf = 2.0 * inp.T * inp.H * inp.H
+        pb = res["projection_bytes"] + 2 * inp.T * inp.H * 2
+        tp = float(np.median(res["projection"]))
+        out["projections"] = dict(count=len(inp.projections), us_each=pct(res["projection"], 1e6),
+                                  tflops=pf / tp / 1e12, mfma_frac=pf / tp / PEAK_MFMA_BF16)
+        rl.append(roof("dense q8_0 projection 4096x4096", name, pf, pb, tp))
+    return out, rl
+
+
+# ---------------------------------------------------------------------------
+# dense Q8_0 cell, router, decode
+# ---------------------------------------------------------------------------
+
+def graph_time(torch, fn, n, reps=5):
+    """Seconds per call of fn, from a captured graph of n calls replayed reps
+    times (no host launch gaps); events on the replay stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (reps * n)
+    del g
+    return t
+
+
+def run_dense_cell(torch, qm):
+    """Dense Q8_0 qmm M=32 N=256 K=2048, fp16 in / out: a launch-bound
+    correctness cell, timed as graph-replayed launches and as single event-
+    timed launches."""
+    import synth
+    x, W = synth.dense_q8_0()
+    dw = upload(qm, W)
+    xd = act_tensor(torch, x, "f16")
+    y = torch.empty((32, 256), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        qm.qmm_dense(dw, xd, qm.EPI_STORE, qm.F16, out=y)
+    torch.cuda.synchronize()
+    t = graph_time(torch, lambda i: qm.qmm_dense(dw, xd, qm.EPI_STORE, qm.F16, out=y), 200)
+    ev = []
+    for _ in range(20):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        qm.qmm_dense(dw, xd, qm.EPI_STORE, qm.F16, out=y)
+        e[1].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    flops = 2.0 * 32 * 256 * 2048
+    nbytes = dw.nbytes + 32 * 2048 * 2 + 32 * 256 * 2
+    te = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
+    return {"workload": "dense q8_0 qmm M=32 N=256 K=2048 fp16", "bound": "launch",
+            "us_per_launch_graph": t * 1e6, "us_per_launch_event": pct(te, 1e6),
+            "tflops": flops / t / 1e12, "GBps": nbytes / t / 1e9,
+            "mfma_frac": flops / t / PEAK_MFMA_BF16, "hbm_frac": nbytes / t / PEAK_HBM,
+            "algorithmic_flops": flops, "algorithmic_bytes": int(nbytes),
+            "note": "33.6 MFLOP and 0.7 MB take 13 ns on the matrix cores and 88 ns of HBM at peak; "
+                    "the launch and the kernel's fixed latency set its time"}
+
+
+def run_router(torch, qm):
     """Device router top-k ahead of the plan: per-launch time from a replayed
-    graph of launches (events on the replay stream), and the HBM rate of its
-    algorithmic bytes (logits and bias read, ids and weights written)."""
+    graph of launches, and the HBM rate of its algorithmic bytes (logits and
+    bias read, ids and weights written)."""
     import synth
     rows = []
     for name, T, E, k, dt, scoring in (("qwen3.6-a3b-shaped softmax top-8", 2048, 256, 8, "bf16", qm.ROUTER_SOFTMAX),
@@ -253,29 +340,10 @@ def run_router(args, torch, qm):
         scale = 1.5 if bias is not None else 1.0
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-        # launches captured in a graph and replayed, so host launch cost does
-        # not hide the kernel's own time
-        n = 100
         for _ in range(3):
             qm.router_topk(L, k, scoring, bias, scale, ids, w)
         torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for _ in range(n):
-                    qm.router_topk(L, k, scoring, bias, scale, ids, w)
-        torch.cuda.current_stream().wait_stream(side)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / (5 * n)
+        t = graph_time(torch, lambda i: qm.router_topk(L, k, scoring, bias, scale, ids, w), 100)
         nbytes = L.numel() * L.element_size() + T * k * 8 + (E * 4 if bias is not None else 0)
         rows.append({"workload": name, "tokens": T, "experts": E, "top_k": k, "logits": dt,
                      "us_per_launch": t * 1e6, "GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / PEAK_HBM,
@@ -284,11 +352,15 @@ def run_router(args, torch, qm):
 
 
 def run_decode(args, torch, qm, B, layers, inp=None):
+    """One decode layer step (gate/up SwiGLU GEMV, then the sum-folded down
+    GEMV) over `layers` copies of the weights, each read cold: the layer time
+    from a graph replay of all layers, each kernel alone from graphs of its
+    launches only, plus eager and event-timed figures."""
     import synth
     inp = synth.qwen_a3b_decode(B) if inp is None else inp
     dev = "cuda"
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[inp.act]
-    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).to(dev).view(tdt)
+    x = act_tensor(torch, inp.x, inp.act)
     ids = torch.from_numpy(inp.ids).to(dev)
     w = torch.from_numpy(inp.w).to(dev)
     gu0, dn0 = upload(qm, inp.w_gate_up), upload(qm, inp.w_down)
@@ -297,18 +369,26 @@ def run_decode(args, torch, qm, B, layers, inp=None):
     h = torch.empty((B, inp.k, inp.I), dtype=tdt, device=dev)
     out = torch.empty((B, inp.H), dtype=tdt, device=dev)
     uniq = np.unique(inp.ids)
-    per_expert = (inp.w_gate_up.nbytes + inp.w_down.nbytes) // inp.E
-    nbytes = len(uniq) * per_expert + B * inp.H * 2 * 2 + B * inp.k * inp.I * 2 * 2
-    def layer(l):
+    pe_gu, pe_dn = gu0.nbytes // inp.E, dn0.nbytes // inp.E
+    bytes_gu = len(uniq) * pe_gu + B * inp.H * 2 + B * inp.k * inp.I * 2
+    bytes_dn = len(uniq) * pe_dn + B * inp.k * inp.I * 2 + B * inp.H * 2
+    nbytes = bytes_gu + bytes_dn   # the layer: weights, x, h written and read, out
+
+    def gate_up(l):
         qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
+
+    def down(l):
         qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
+
+    def layer(l):
+        gate_up(l)
+        down(l)
 
     for _ in range(2):
         for l in range(layers):
             layer(l)
     torch.cuda.synchronize()
     reps = max(1, args.decode_reps)
-    # eager: every layer launched from the host, events around the whole run
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -317,71 +397,124 @@ def run_decode(args, torch, qm, B, layers, inp=None):
     e1.record()
     torch.cuda.synchronize()
     t_eager = e0.elapsed_time(e1) * 1e-3 / (reps * layers)
-    # graph: the same layers captured once into a HIP graph and replayed
-    # (no launch gaps from the host; the kernels allocate nothing and issue
-    # no memset, so they replay as captured)
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for l in range(layers):
-                layer(l)
-    torch.cuda.current_stream().wait_stream(stream)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t_graph = e0.elapsed_time(e1) * 1e-3 / (reps * layers)
-    # per-launch durations with events around each launch (upper bounds: an
-    # event pair adds its own gap to a launch this short)
-    marks = []
-    for l in range(layers):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        qm.moe_gemv(gus[l], x, ids, epilogue=qm.EPI_SWIGLU, out=h)
-        e[1].record()
-        qm.moe_gemv(dns[l], h, ids, w, epilogue=qm.EPI_WEIGHTED_COMBINE, out=out)
-        e[2].record()
-        marks.append(e)
-    torch.cuda.synchronize()
-    t_gu = float(np.median([m[0].elapsed_time(m[1]) for m in marks])) * 1e-3
-    t_dn = float(np.median([m[1].elapsed_time(m[2]) for m in marks])) * 1e-3
-    del graph, gus, dns
+    t_graph = graph_time(torch, layer, layers, reps)
+    t_gu = graph_time(torch, gate_up, layers, reps)
+    t_dn = graph_time(torch, down, layers, reps)
+    del gus, dns
     torch.cuda.empty_cache()
+    f_gu = 2.0 * B * inp.k * 2 * inp.I * inp.H
+    f_dn = 2.0 * B * inp.k * inp.I * inp.H
+    rl = [roof("decode gate/up SWIGLU GEMV", inp.name, f_gu, bytes_gu, t_gu,
+               traffic_from_profiles(f"decode_gate_up_b{B}"), note="graph of the layers' gate/up launches only"),
+          roof("decode down sum-folded GEMV", inp.name, f_dn, bytes_dn, t_dn,
+               traffic_from_profiles(f"decode_down_b{B}"), note="graph of the layers' down launches only")]
     return dict(workload=inp.name, B=B, layers=layers, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
-                s_per_layer_graph=t_graph, s_per_layer_eager=t_eager,
-                gate_up_s_event=t_gu, down_s_event=t_dn,
+                us_per_layer_graph=t_graph * 1e6, us_per_layer_eager=t_eager * 1e6,
+                us_gate_up_graph=t_gu * 1e6, us_down_graph=t_dn * 1e6,
                 GBps=nbytes / t_graph / 1e9, hbm_frac=nbytes / t_graph / PEAK_HBM,
-                GBps_eager=nbytes / t_eager / 1e9, tokens_per_s_per_layer=B / t_graph)
+                GBps_eager=nbytes / t_eager / 1e9, tokens_per_s_per_layer=B / t_graph), rl
 
 
-def cpu_baseline(n_tokens):
-    """The oracle, as it stands, on a bounded sample of the prefill workload:
+# ---------------------------------------------------------------------------
+# CPU oracle baselines
+# ---------------------------------------------------------------------------
+
+def host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": aff}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, n_tokens):
+    """The oracle, as it stands, on a bounded sample of the headline workload:
     the full MoE FFN (gate/up + SwiGLU, down, weighted combine) for the first
     n_tokens tokens, in fp64."""
     import oracle
-    inp = prefill_inputs(2048)
-    ids = inp.ids[:n_tokens]
-    w = inp.w[:n_tokens]
-    x64 = oracle.act_to_f64(inp.x[:n_tokens], "bf16")
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    ids, w = inp.ids[:n_tokens], inp.w[:n_tokens]
+    x64 = oracle.act_to_f64(inp.x[:n_tokens], inp.act)
     t0 = time.perf_counter()
-    oracle.moe_ffn(x64, ids, w, inp.w_gate_up, inp.w_down, h_dtype="bf16")
+    oracle.moe_ffn(x64, ids, w, inp.w_gate_up, inp.w_down, h_dtype=inp.act)
     dt = time.perf_counter() - t0
     P = ids.size
     flops = 2.0 * P * (3 * inp.I * inp.H)
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"first {n_tokens} of 2048 tokens ({P} routed pairs) of the prefill workload, "
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(_blas_threads()), kind="oracle",
+                sample=f"first {n_tokens} of {inp.T} tokens ({P} routed pairs) of the prefill workload, "
                        f"fp64 oracle, {dt:.1f} s", tokens_per_s=n_tokens / dt, seconds=dt)
 
+
+def cpu_sample_experts(inp, experts):
+    """The oracle's MoE FFN on the routed pairs of a few experts only (every
+    token with such a pair, its other pairs dropped): the oracle's cost is
+    per expert decoded plus the pairs' fp64 products, so a handful of experts
+    bounds the run."""
+    import oracle
+    keep = np.isin(inp.ids, experts)
+    rows = np.nonzero(keep.any(axis=1))[0]
+    ids = np.where(keep, inp.ids, -1)[rows]
+    x64 = oracle.act_to_f64(inp.x[rows], inp.act)
+    t0 = time.perf_counter()
+    oracle.moe_ffn(x64, ids, inp.w[rows], inp.w_gate_up, inp.w_down, h_dtype=inp.act)
+    dt = time.perf_counter() - t0
+    P = int(keep.sum())
+    flops = 2.0 * P * 3 * inp.I * inp.H
+    return dict(workload=inp.name, kind="oracle", gflops=flops / dt / 1e9, seconds=dt, routed_pairs=P,
+                cores=int(_blas_threads()),
+                sample=f"the {P} routed pairs of experts {list(map(int, experts))} ({len(rows)} tokens), fp64 oracle")
+
+
+def cpu_dense_cell():
+    """The oracle's dense Q8_0 qmm M=32 N=256 K=2048 on all cores and on one."""
+    import oracle
+    import synth
+    x, W = synth.dense_q8_0()
+    x64 = oracle.act_to_f64(x, "f16")
+    flops = 2.0 * 32 * 256 * 2048
+
+    def timed():
+        oracle.qmm(x64, W)
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            oracle.qmm(x64, W)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    res = []
+    t = timed()
+    res.append(dict(workload="dense q8_0 qmm M=32 N=256 K=2048", kind="oracle", cores=int(_blas_threads()),
+                    seconds=t, gflops=flops / t / 1e9, sample="whole cell, median of 5 after one warm-up"))
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t = timed()
+        res.append(dict(workload="dense q8_0 qmm M=32 N=256 K=2048", kind="oracle", cores=1, seconds=t,
+                        gflops=flops / t / 1e9, sample="whole cell, median of 5 after one warm-up"))
+    except Exception as e:  # threadpoolctl missing: report what ran
+        res.append(dict(kind="oracle", cores=1, error=str(e)))
+    return res
+
+
+# ---------------------------------------------------------------------------
+# counter records
+# ---------------------------------------------------------------------------
 
 def copy_probe(mb, reps=20):
     """A plain device copy of known size (the runtime's copy kernel), run under
@@ -410,64 +543,57 @@ def _pmc_median_kib(run_dir, counter, name_part):
     return float(np.median(list(per.values()))), len(per)
 
 
-def _gemm_source_hash():
-    """sha256 of the GEMM kernel sources (gemm.hip and the shared device
-    helpers) with comments and blank lines removed, so the traffic record
-    stays valid across comment-only edits."""
+KERNEL_SOURCES = {"gemm": ("common.h", "gemm.hip"), "gemv": ("common.h", "gemv.hip")}
+
+
+def _source_hash(kind):
+    """sha256 of a kernel family's sources with comments and blank lines
+    removed, so a traffic record stays valid across comment-only edits."""
     import hashlib
     import re
     code = []
-    for f in ("common.h", "gemm.hip"):
+    for f in KERNEL_SOURCES[kind]:
         src = open(os.path.join(ROOT, "block_quantized_moe_amd", "csrc", f)).read()
         code += [re.sub(r"//.*", "", l).rstrip() for l in src.splitlines()]
     return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()
 
 
-def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, out):
-    """Turn four rocprofv3 --pmc runs (gate/up FETCH_SIZE, WRITE_SIZE; copy
-    probe FETCH_SIZE, WRITE_SIZE) into HBM bytes per gate/up launch."""
-    kern = "qmm_int4_kernel<1, 1>"
-    f_kib, nf = _pmc_median_kib(fetch_dir, "FETCH_SIZE", kern)
-    w_kib, nw = _pmc_median_kib(write_dir, "WRITE_SIZE", kern)
+def summarize_traffic(name, kernel, alg_bytes, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb):
+    """Turn four rocprofv3 --pmc runs (the kernel's FETCH_SIZE and WRITE_SIZE;
+    the copy probe's FETCH_SIZE and WRITE_SIZE) into HBM bytes per launch,
+    written to profiles/<name>_traffic.json."""
+    f_kib, nf = _pmc_median_kib(fetch_dir, "FETCH_SIZE", kernel)
+    w_kib, nw = _pmc_median_kib(write_dir, "WRITE_SIZE", kernel)
     cf_kib, _ = _pmc_median_kib(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     cw_kib, _ = _pmc_median_kib(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     true = float(copy_mb << 20)
     k_fetch, k_write = true / (cf_kib * 1024), true / (cw_kib * 1024)
-    inp = prefill_inputs(2048)
-    alg = algorithmic(inp)
-    rec = {
-        "kernel": "qmm_int4_kernel<bf16, SWIGLU> (int4 gate/up), qwen3.6-a3b-shaped prefill",
-        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
-        "copy_probe_mib": copy_mb, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
-        "fetch_scale": k_fetch, "write_scale": k_write,
-        "bytes_per_launch": f_kib * 1024 * k_fetch + w_kib * 1024 * k_write,
-        "algorithmic_bytes_per_launch": alg["bytes_gu"],
-        "gemm_code_sha256": _gemm_source_hash(),
-    }
-    rec["traffic_over_algorithmic"] = rec["bytes_per_launch"] / alg["bytes_gu"]
-    pm = "rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py {a}"
-    prefill = "--steps 3 --warmup 1 --no-decode --no-cpu --no-extra"
-    rec["commands"] = [pm.format(c="FETCH_SIZE", d=fetch_dir, a=prefill),
-                       pm.format(c="WRITE_SIZE", d=write_dir, a=prefill),
-                       pm.format(c="FETCH_SIZE", d=copy_fetch_dir, a=f"--copy-probe {copy_mb}"),
-                       pm.format(c="WRITE_SIZE", d=copy_write_dir, a=f"--copy-probe {copy_mb}"),
-                       f"python3 bench.py --summarize-traffic {fetch_dir} {write_dir} {copy_fetch_dir} "
-                       f"{copy_write_dir} {copy_mb}"]
+    kind = "gemv" if "gemv" in kernel else "gemm"
+    rec = {"name": name, "kernel": kernel,
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_probe_mib": copy_mb, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": k_fetch, "write_scale": k_write,
+           "bytes_per_launch": f_kib * 1024 * k_fetch + w_kib * 1024 * k_write,
+           "algorithmic_bytes_per_launch": alg_bytes, "code_sha256": _source_hash(kind), "code": kind}
+    rec["traffic_over_algorithmic"] = rec["bytes_per_launch"] / alg_bytes
     rec["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch summed over instances, scaled by "
                    "true bytes / counter bytes of a device copy of known size.")
+    out = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec, indent=1))
 
 
-def traffic_from_profiles():
-    """HBM bytes per gate/up launch measured with rocprofv3 counters, if the
-    committed measurement was taken on the current kernel code."""
-    p = os.path.join(ROOT, "profiles", "gate_up_qwen_prefill_traffic.json")
+def traffic_from_profiles(name):
+    """HBM bytes per launch measured with rocprofv3 counters, if a record
+    exists and was taken on the current kernel code."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    return rec.get("bytes_per_launch") if rec.get("gemm_code_sha256") == _gemm_source_hash() else None
+    return rec.get("bytes_per_launch") if rec.get("code_sha256") == _source_hash(rec.get("code", "gemm")) else None
 
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -481,16 +607,18 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the DSv4-shaped and mixed-format prefill lines")
+    ap.add_argument("--only", choices=["qwen", "dense", "decode", "dsv4", "dsv4-mxfp4", "dsv4-fp8", "mixed", "router"],
+                    help="run one workload (for per-workload profiles); prints its own JSON, not the bench line")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a device copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--summarize-traffic", nargs=5,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "COPY_MIB"),
-                    help="write profiles/gate_up_qwen_prefill_traffic.json from rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-traffic", nargs=8,
+                    metavar=("NAME", "KERNEL", "ALG_BYTES", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                             "COPY_WRITE_DIR", "COPY_MIB"),
+                    help="write profiles/NAME_traffic.json from rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.summarize_traffic:
         d = args.summarize_traffic
-        summarize_traffic(d[0], d[1], d[2], d[3], int(d[4]),
-                          os.path.join(ROOT, "profiles", "gate_up_qwen_prefill_traffic.json"))
+        summarize_traffic(d[0], d[1], int(d[2]), d[3], d[4], d[5], d[6], int(d[7]))
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -501,66 +629,97 @@ def main():
         sys.exit(2)
 
     import torch
+
     import block_quantized_moe_amd as qm
+    import synth
 
     qm.check_device()
-    log("prefill: building inputs")
-    inp, alg, wall, kern = run_prefill(args, torch, qm)
-    t_step = wall
-    value = alg["flops"] / t_step / 1e12
-    t_gu = kern["gate_up"]
-    roofline = {
-        "kernel": "qmm_int4_kernel<bf16, SWIGLU> (int4 gate/up)",
-        "bound": "hbm",
-        "achieved": alg["bytes_gu"] / t_gu / 1e9,
-        "peak": PEAK_HBM / 1e9,
-        "unit": "GB/s",
-        "frac": alg["bytes_gu"] / t_gu / PEAK_HBM,
-        "traffic": traffic_from_profiles(),
-        "algorithmic_bytes_per_launch": alg["bytes_gu"],
-        "launch_s": t_gu,
-        "mfma_tflops": alg["flops_gu"] / t_gu / 1e12,
-        "mfma_frac": alg["flops_gu"] / t_gu / PEAK_MFMA_BF16,
-    }
-    log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; kernels {json.dumps(kern)}")
-    others = []
+    only = args.only
+    want = lambda w: only is None or only == w
+    others, rooflines, cpu_other, decode = [], [], [], []
+    dense = router = imb = None
     decode_inputs = {}
-    if not args.no_extra:
-        import synth
+    extra = not args.no_extra and only != "qwen"
+
+    if want("qwen"):
+        log("prefill (qwen): building inputs")
+        inp = prefill_inputs(2048)
+        res = run_prefill(args, torch, qm, inp, args.rotate, args.steps, args.warmup)
+        alg = algorithmic(inp, res["wbytes_gu"], res["wbytes_dn"])
+        t_step = res["wall"]
+        value = alg["flops"] / t_step / 1e12
+        t_gu = float(np.median(res["kern"]["gate_up"]))
+        roofline = roof("qmm_int4_kernel<bf16, SWIGLU> (int4 gate/up)", "qwen3.6-a3b-int4-prefill",
+                        alg["flops_gu"], alg["bytes_gu"], t_gu, traffic_from_profiles("gate_up_qwen"))
+        roofline["bound"], roofline["unit"] = "hbm", "GB/s"   # HBM-bound by its own work (41 vs 27 us at peak)
+        roofline["achieved"], roofline["peak"] = alg["bytes_gu"] / t_gu / 1e9, PEAK_HBM / 1e9
+        roofline["frac"] = alg["bytes_gu"] / t_gu / PEAK_HBM
+        qline, qrl = prefill_line("qwen", inp, res, args.rotate)
+        rooflines += qrl
+        log(f"prefill: step {t_step*1e6:.1f} us, {value:.1f} TFLOP/s; {json.dumps(qline['kernels_us'])}")
+        cpu = None
+        if not args.no_cpu and only is None:
+            log("cpu baseline: oracle sample")
+            cpu = cpu_baseline(inp, args.cpu_tokens)
+        del inp
+    if (extra or only == "dense") and want("dense"):
+        log("dense q8_0 cell")
+        dense = run_dense_cell(torch, qm)
+        log(json.dumps(dense))
+        if not args.no_cpu and only is None:
+            cpu_other += cpu_dense_cell()
+    if extra:
         for name, make, R in (("dsv4", lambda: synth.dsv4_flash_prefill(2048), 2),
-                              ("dsv4 mxfp4", lambda: synth.dsv4_flash_mxfp4_prefill(2048), 2),
-                              ("dsv4 fp8", lambda: synth.dsv4_flash_fp8_prefill(2048), 2),
+                              ("dsv4-mxfp4", lambda: synth.dsv4_flash_mxfp4_prefill(2048), 2),
+                              ("dsv4-fp8", lambda: synth.dsv4_flash_fp8_prefill(2048), 2),
                               ("mixed", lambda: synth.mixed_ffn(8192), 2)):
+            if not want(name):
+                continue
             log(f"prefill ({name}): building inputs")
             inp_o = make()
-            others.append(run_prefill_other(args, torch, qm, inp_o, R, max(3, args.steps // 4)))
-            log(json.dumps(others[-1]))
-            if name in ("dsv4 mxfp4", "dsv4 fp8"):
+            res = run_prefill(args, torch, qm, inp_o, R, max(3, args.steps // 4), 2)
+            line_o, rl = prefill_line(name, inp_o, res, R)
+            if name == "mixed":
+                imb = imbalance(inp_o)
+                line_o["imbalance"] = imb
+            others.append(line_o)
+            rooflines += rl
+            log(json.dumps(line_o))
+            if not args.no_cpu and only is None and name in ("dsv4", "mixed"):
+                log(f"cpu oracle sample ({name})")
+                cpu_other.append(cpu_sample_experts(inp_o, np.arange(8)))
+            if name in ("dsv4-mxfp4", "dsv4-fp8"):
                 decode_inputs[name] = inp_o  # its weights also serve the decode lines of the format
-            del inp_o
-    log("router top-k")
-    router = run_router(args, torch, qm)
-    log(json.dumps(router))
-    decode = []
-    if not args.no_decode:
+            else:
+                del inp_o
+    if (extra or only == "router") and want("router"):
+        log("router top-k")
+        router = run_router(torch, qm)
+        log(json.dumps(router))
+    if not args.no_decode and want("decode"):
         for B in (1, 4, 8):
             log(f"decode: B={B}")
-            decode.append(run_decode(args, torch, qm, B, args.decode_layers))
-            log(json.dumps(decode[-1]))
-        if not args.no_extra:
-            import dataclasses
-            for name, src in decode_inputs.items():
-                fmt = name.split()[1]
-                for B in (1, 4):
-                    log(f"decode ({name}): B={B}")
-                    dec = dataclasses.replace(src, name=f"dsv4-flash-{fmt}-decode-b{B}", T=B, x=src.x[:B],
-                                              ids=src.ids[:B], w=src.w[:B])
-                    decode.append(run_decode(args, torch, qm, B, max(2, args.decode_layers // 5), dec))
-                    log(json.dumps(decode[-1]))
-    cpu = None
-    if not args.no_cpu:
-        log("cpu baseline: oracle sample")
-        cpu = cpu_baseline(args.cpu_tokens)
+            d, rl = run_decode(args, torch, qm, B, args.decode_layers)
+            decode.append(d)
+            rooflines += rl
+            log(json.dumps(d))
+    if not args.no_decode and extra and only is None:
+        import dataclasses
+        for name, src in decode_inputs.items():
+            fmt = name.split("-")[1]
+            for B in (1, 4):
+                log(f"decode ({name}): B={B}")
+                dec = dataclasses.replace(src, name=f"dsv4-flash-{fmt}-decode-b{B}", T=B, x=src.x[:B],
+                                          ids=src.ids[:B], w=src.w[:B])
+                d, rl = run_decode(args, torch, qm, B, max(2, args.decode_layers // 5), dec)
+                decode.append(d)
+                rooflines += rl
+                log(json.dumps(d))
+
+    if only is not None and only != "qwen":
+        print(json.dumps({"only": only, "other_prefill_workloads": others, "decode": decode, "dense_q8_0": dense,
+                          "router": router, "rooflines": rooflines}), flush=True)
+        return
     line = {
         "metric": "MoE qGEMM prefill TFLOP/s (% MFMA peak) + decode GEMV GB/s (% HBM peak)",
         "value": value,
@@ -574,24 +733,25 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3.6-a3b-shaped int4 MoE prefill", "tokens": inp.T, "hidden": inp.H,
-                   "experts": inp.E, "top_k": inp.k, "intermediate": inp.I,
+        "config": {"workload": "qwen3.6-a3b-shaped int4 MoE prefill", "tokens": 2048, "hidden": 2048,
+                   "experts": 256, "top_k": 8, "intermediate": 512,
                    "weights": "int4 affine, group 64, fp16 scale+bias", "activations": "bf16",
                    "weight_copies_rotated": args.rotate},
         "mfma_frac": value * 1e12 / PEAK_MFMA_BF16,
-        "tokens_per_s": inp.T / t_step,
-        "kernels_s": kern,
+        "tokens_per_s": 2048 / t_step,
+        "step_us": qline["step_us"],
+        "kernels_us": qline["kernels_us"],
         "algorithmic": {"flops": alg["flops"], "bytes": alg["bytes"]},
         "roofline": roofline,
-        "decode": [{"workload": d["workload"], "B": d["B"], "layers": d["layers"], "GBps": d["GBps"], "hbm_frac": d["hbm_frac"], "GBps_eager": d["GBps_eager"],
-                    "us_per_layer_graph": d["s_per_layer_graph"] * 1e6,
-                    "us_per_layer_eager": d["s_per_layer_eager"] * 1e6,
-                    "us_gate_up_event": d["gate_up_s_event"] * 1e6, "us_down_event": d["down_s_event"] * 1e6,
-                    "unique_experts": d["unique_experts"], "bytes_per_layer": d["bytes_per_layer"]}
-                   for d in decode],
+        "rooflines": rooflines,
+        "dense_q8_0": dense,
+        "decode": decode,
         "other_prefill_workloads": others,
+        "imbalance": imb,
         "router": router,
         "cpu_baseline": cpu,
+        "cpu_oracle": cpu_other,
+        "host": host_info(),
     }
     print(json.dumps(line), flush=True)
 
