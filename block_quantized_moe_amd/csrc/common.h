@@ -97,6 +97,16 @@ __device__ __forceinline__ void dma_glb16(const void* src, uint32_t lds) {
 __device__ __forceinline__ void dma_glb4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(lds), "v"(src) : "memory", "m0");
 }
+// The same with a wave-uniform base address in SGPRs and a 32-bit per-lane
+// byte offset (one VGPR instead of a 64-bit address per lane).
+__device__ __forceinline__ void dma_glb16_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_glb4_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" :: "s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
 
 // s_waitcnt vmcnt(N) leaving the other counters alone.
 template <int N>

@@ -1047,20 +1047,24 @@ void qmm_int4_kernel(GemmArgs g) {
     const int src = (r < 16 * mbn && p < R_ACH) ? rows_a[min(r, BM - 1)] : -1;
     aoff[i] = src >= 0 ? (uint32_t)((int64_t)src * K * 2 + 16 * c) : 0x80000000u;
   }
-  // weight runs: lanes 0-31 block 0, lanes 32-63 block 1
-  const uint32_t* wsrc = (const uint32_t*)g.qs +
-                         (((int64_t)expert * g.N + block_base(lane >> 5)) >> 4) * T * 128 + (lane & 31) * 4;
-  // scale|bias words: lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them)
-  const uint32_t* ssrc = (const uint32_t*)g.scales +
-                         (((int64_t)expert * g.N + block_base((lane >> 4) & 1)) >> 4) * G * 16 + lr;
+  // weight runs: lanes 0-31 block 0, lanes 32-63 block 1; scale|bias words:
+  // lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them).  The base
+  // (block 0's run) is wave-uniform and lives in SGPRs; each lane adds a
+  // 32-bit byte offset (block 1's run lies at most one expert's codes further)
+  const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
+  const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
+  const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * 512;
+  const uint32_t woff = (uint32_t)((lane >> 5) * (rb1 - rb0) * T * 512 + (lane & 31) * 16);
+  const uint8_t* sbase = (const uint8_t*)g.scales + rb0 * G * 64;
+  const uint32_t soff = (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * G * 64 + lr * 4);
 
   // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
   auto issue = [&](int kt, int stage) {
     const uint32_t st = lds_addr(ring) + (uint32_t)(stage * R_STAGE);
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
-    dma_glb16(wsrc + kt * 128, st + R_A + wave * 1024);
-    dma_glb4(ssrc + (kt >> gsh) * 16, st + R_A + R_B + wave * 256);
+    dma_glb16_s(wbase + (int64_t)kt * 512, woff, st + R_A + wave * 1024);
+    dma_glb4_s(sbase + (int64_t)(kt >> gsh) * 64, soff, st + R_A + R_B + wave * 256);
   };
 
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
@@ -1183,7 +1187,11 @@ void qmm_int4_kernel(GemmArgs g) {
     }
 
     // ---- bf16 bias term: sum_g (b - 128 s)[n, g] * X[m, g] by MFMA with hi/lo
-    // splits (G <= 32: one 32-group step; lane group lg holds groups 8lg .. 8lg+7)
+    // bf16 splits of both factors (G <= 32: one 32-group step; lane group lg
+    // holds groups 8lg .. 8lg+7).  The activation sums are split once per
+    // workgroup into the idle ring ([row][hi: 32 groups][lo: 32 groups] bf16,
+    // rows padded to 144 bytes so the 16-byte operand reads do not share
+    // banks); each wave splits only its own rows' coefficients.
     if constexpr (BF) {
       uint32_t sv[RNB][8];
 #pragma unroll
@@ -1192,36 +1200,46 @@ void qmm_int4_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) sv[b][i] = sbrow[min(8 * lg + i, G - 1) * 16];
       }
-      ring_barrier();  // every wave's row sums are in xg
+      constexpr int XROW = 72;  // bf16 per staged row (64 + 8 of padding)
+      uint16_t* xsp = (uint16_t*)ring;
+      ring_barrier();  // every wave's row sums are in xg and the ring is idle
+      for (int i = tid; i < 16 * MBV * 4; i += RW * 64) {  // (row, 8-group chunk)
+        const int r = i >> 2, c = i & 3;
+        u4_t hh, ll;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int g0 = 8 * c + 2 * j;
+          const f2_t v = {g0 < G ? xg[g0 * BM + r] : 0.f, g0 + 1 < G ? xg[(g0 + 1) * BM + r] : 0.f};
+          const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2_t));
+          const f2_t hv = {__builtin_bit_cast(float, h << 16), __builtin_bit_cast(float, h & 0xFFFF0000u)};
+          hh[j] = h;
+          ll[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hv, b2_t));
+        }
+        *(u4_t*)(xsp + r * XROW + 8 * c) = hh;
+        *(u4_t*)(xsp + r * XROW + 32 + 8 * c) = ll;
+      }
+      ring_barrier();
 #pragma unroll
       for (int b = 0; b < RNB; ++b) {
         u4_t bh, bl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t h2[2], l2[2];
+          f2_t cb;
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
             const uint32_t w = sv[b][2 * i + qq];
-            const float cb = (8 * lg + 2 * i + qq < G) ? f16_to_f32(w >> 16) - 128.0f * f16_to_f32(w & 0xFFFFu) : 0.f;
-            split_hi_lo(cb, h2[qq], l2[qq]);
+            cb[qq] = (8 * lg + 2 * i + qq < G) ? f16_to_f32(w >> 16) - 128.0f * f16_to_f32(w & 0xFFFFu) : 0.f;
           }
-          bh[i] = h2[0] | (h2[1] << 16);
-          bl[i] = l2[0] | (l2[1] << 16);
+          const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(cb, b2_t));
+          const f2_t hv = {__builtin_bit_cast(float, h << 16), __builtin_bit_cast(float, h & 0xFFFF0000u)};
+          bh[i] = h;
+          bl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(cb - hv, b2_t));
         }
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
-          const float* xr = &xg[8 * lg * BM + 16 * m + lr];
-          u4_t xh, xl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t h2[2], l2[2];
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq)
-              split_hi_lo(8 * lg + 2 * i + qq < G ? xr[(2 * i + qq) * BM] : 0.f, h2[qq], l2[qq]);
-            xh[i] = h2[0] | (h2[1] << 16);
-            xl[i] = l2[0] | (l2[1] << 16);
-          }
-          const b8_t XH = __builtin_bit_cast(b8_t, xh), XL = __builtin_bit_cast(b8_t, xl);
+          const uint16_t* xr = xsp + (16 * m + lr) * XROW + 8 * lg;
+          const b8_t XH = __builtin_bit_cast(b8_t, *(const u4_t*)xr);
+          const b8_t XL = __builtin_bit_cast(b8_t, *(const u4_t*)(xr + 32));
           acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bh), acc[m][b]);
           acc[m][b] = mfma(XH, __builtin_bit_cast(b8_t, bl), acc[m][b]);
           acc[m][b] = mfma(XL, __builtin_bit_cast(b8_t, bh), acc[m][b]);
@@ -1311,6 +1329,7 @@ void qmm_int4_kernel(GemmArgs g) {
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
+  if (g.N * g.K / 2 >= (1ll << 31)) return false;  // per-lane byte offsets within one expert's codes
   if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
   if (act == QMOE_BF16 && g.K / g.group > XG4) return false;
   return true;
