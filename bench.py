@@ -583,6 +583,103 @@ def summarize_traffic(name, kernel, alg_bytes, fetch_dir, write_dir, copy_fetch_
     print(json.dumps(rec, indent=1))
 
 
+PMC_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU2 SQ_WAIT_INST_LDS SQ_ACTIVE_INST_SCA "
+    "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_MISC SQ_INSTS_MFMA GRBM_GUI_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_INSTS_LDS SQ_INST_LEVEL_LDS "
+    "SQ_INSTS_VALU SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+)
+
+
+def _csv_rows(run_dir, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(run_dir, "**", "*" + suffix), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_stats(run_dir, name, command, note, out_dir):
+    """profiles/<name>.md from a rocprofv3 --kernel-trace run: per kernel the
+    launch count and the median / mean / min / max duration (from the kernel
+    trace), and the share of GPU time."""
+    per = {}
+    for r in _csv_rows(run_dir, "kernel_trace.csv"):
+        per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    if not per:
+        raise SystemExit(f"no kernel trace under {run_dir}")
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# Kernel durations: {name}", "", "Command (MI355X, one GPU, from the repository root):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd -", command, "```", "", note, "",
+             "| kernel | calls | median us | mean us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        short = k if len(k) < 90 else k[:87] + "..."
+        lines.append(f"| `{short}` | {len(v)} | {v[len(v) // 2]:.1f} | {sum(v) / len(v):.1f} | {v[0]:.1f} | "
+                     f"{v[-1]:.1f} | {100 * sum(v) / total:.2f} |")
+    lines += ["", "Template arguments: `qmm_int4_kernel<act, epilogue>`, `qmm_kernel<format, act, epilogue>`, "
+              "`gemv_int4_split_kernel<act, epilogue>`: act 0 = fp16, 1 = bf16; epilogue 0 = STORE, 1 = SWIGLU, "
+              "2 = WEIGHTED_COMBINE, 3 = ACCUMULATE; format 0 = Q8_0, 1 = Q2_K, 2 = IQ2_XXS, 3 = int4, 4 = MXFP4, "
+              "5 = FP8 E4M3 block."]
+    open(os.path.join(out_dir, f"{name}.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(run_dirs, name, kernel, command, note, out_dir):
+    """profiles/<name>_counters.md from rocprofv3 --pmc passes (one directory
+    per pass, the PMC_PASSES sets): totals over the kernel's dispatches and
+    the ratios that say what bounds it.  Per-SIMD counters are summed over
+    the chip's 1024 SIMDs, per-SE ones over its CUs; GRBM_GUI_ACTIVE over
+    its 8 XCDs."""
+    tot, disp = {}, {}
+    for d in run_dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            c = r["Counter_Name"]
+            tot[(d, c)] = tot.get((d, c), 0.0) + float(r["Counter_Value"])
+            disp.setdefault(d, set()).add(r["Dispatch_Id"])
+    if not tot:
+        raise SystemExit(f"no counters for '{kernel}'")
+    v = {}
+    for (d, c), x in tot.items():   # per dispatch, averaged over the passes that have the counter
+        v.setdefault(c, []).append(x / len(disp[d]))
+    v = {c: float(np.mean(x)) for c, x in v.items()}
+    n_simd, n_cu, n_xcd = 1024, 256, 8
+    cyc = v["GRBM_GUI_ACTIVE"] / n_xcd           # cycles per dispatch
+    ratios = {
+        "kernel cycles per dispatch (GRBM_GUI_ACTIVE / 8 XCDs)": cyc,
+        "MFMA busy, % of cycles per SIMD": 100 * v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / n_simd / cyc,
+        "VALU instructions per MFMA (SQ_INSTS_VALU - MFMA) / MFMA": (v.get("SQ_INSTS_VALU", 0) - v.get("SQ_INSTS_MFMA", 0))
+        / max(v.get("SQ_INSTS_MFMA", 1), 1),
+        "VALU busy, % of cycles per SIMD (4 cycles per wave64 VALU instruction)":
+            100 * 4 * (v.get("SQ_INSTS_VALU", 0) - v.get("SQ_INSTS_MFMA", 0)) / n_simd / cyc,
+        "MFMA and VALU co-executing, % of MFMA busy cycles": 100 * v.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0)
+        / max(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 1), 1),
+        "LDS active, % of cycles per CU (SQ_LDS_IDX_ACTIVE)": 100 * v.get("SQ_LDS_IDX_ACTIVE", 0) / n_cu / cyc,
+        "LDS bank-conflict cycles, % of LDS active": 100 * v.get("SQ_LDS_BANK_CONFLICT", 0)
+        / max(v.get("SQ_LDS_IDX_ACTIVE", 1), 1),
+        "wave time waiting on anything (s_waitcnt etc.), %": 100 * v.get("SQ_WAIT_ANY", 0) / v["SQ_WAVE_CYCLES"],
+        "wave time ready but not issued, %": 100 * v.get("SQ_WAIT_INST_ANY", 0) / v["SQ_WAVE_CYCLES"],
+        "wave time issuing, %": 100 * v.get("SQ_ACTIVE_INST_ANY", 0) / v["SQ_WAVE_CYCLES"],
+    }
+    lines = [f"# Counters: {name}", "", f"Kernel: `{kernel}` (dispatches whose name contains it).", "",
+             "Commands (MI355X, one GPU, from the repository root; one rocprofv3 run per counter set):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd -"]
+    lines += [command.format(counters=c, i=i + 1) for i, c in enumerate(PMC_PASSES)]
+    lines += [f"python3 bench.py --summarize-counters {name} '{kernel}' " + " ".join(run_dirs), "```", "", note, "",
+              "| ratio | value |", "|---|---:|"]
+    lines += [f"| {k} | {x:.3g} |" for k, x in ratios.items()]
+    lines += ["", "Raw counters, per dispatch:", "", "| counter | value |", "|---|---:|"]
+    lines += [f"| {c} | {x:.4g} |" for c, x in sorted(v.items())]
+    open(os.path.join(out_dir, f"{name}_counters.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_from_profiles(name):
     """HBM bytes per launch measured with rocprofv3 counters, if a record
     exists and was taken on the current kernel code."""
@@ -611,11 +708,23 @@ def main():
                     help="run one workload (for per-workload profiles); prints its own JSON, not the bench line")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-stats", nargs=4, metavar=("RUN_DIR", "NAME", "COMMAND", "NOTE"),
+                    help="write profiles/NAME.md from a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="NAME KERNEL COMMAND NOTE DIR...: write profiles/NAME_counters.md from --pmc passes")
     ap.add_argument("--summarize-traffic", nargs=8,
                     metavar=("NAME", "KERNEL", "ALG_BYTES", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                              "COPY_WRITE_DIR", "COPY_MIB"),
                     help="write profiles/NAME_traffic.json from rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_stats:
+        d = args.summarize_stats
+        summarize_stats(d[0], d[1], d[2], d[3], os.path.join(ROOT, "profiles"))
+        return
+    if args.summarize_counters:
+        d = args.summarize_counters
+        summarize_counters(d[4:], d[0], d[1], d[2], d[3], os.path.join(ROOT, "profiles"))
+        return
     if args.summarize_traffic:
         d = args.summarize_traffic
         summarize_traffic(d[0], d[1], int(d[2]), d[3], d[4], d[5], d[6], int(d[7]))
