@@ -288,6 +288,25 @@ def graph_time(torch, fn, n, reps=5):
     return t
 
 
+def run_launch_floor(torch, layers):
+    """The floor a decode layer's two dependent launches sit on: per-launch
+    time of a graph of 2 x layers trivial fills (16 floats), and of a graph of
+    2 x layers gathers of 8 rows (32 KB) from a different cold 8 MB matrix
+    each time, the smallest kernel that, like a decode GEMV, waits on HBM."""
+    n = 2 * layers
+    small = torch.zeros(16, device="cuda")
+    big = [torch.randn(256, 8192, device="cuda") for _ in range(n)]
+    ids = torch.randint(0, 256, (8,), device="cuda")
+    out = torch.empty(8, 8192, device="cuda")
+    t_fill = graph_time(torch, lambda i: small.fill_(1.0), n, reps=10)
+    t_gather = graph_time(torch, lambda i: torch.index_select(big[i], 0, ids, out=out), n, reps=10)
+    del big
+    return {"us_per_launch_fill": t_fill * 1e6, "us_per_launch_cold_gather_8_rows": t_gather * 1e6,
+            "us_per_layer_two_dependent_launches": 2 * t_gather * 1e6,
+            "note": "graph replays on one stream; a decode layer (gate/up GEMV, then down GEMV) cannot go below "
+                    "two dependent launches that each wait on HBM"}
+
+
 def run_dense_cell(torch, qm):
     """Dense Q8_0 qmm M=32 N=256 K=2048, fp16 in / out: a launch-bound
     correctness cell, timed as graph-replayed launches and as single event-
@@ -530,13 +549,15 @@ def copy_probe(mb, reps=20):
 
 def _pmc_median_kib(run_dir, counter, name_part):
     """Median per-dispatch value (summed over the counter's instances) of one
-    counter for the kernels whose name contains name_part."""
+    counter for the kernels whose name contains name_part (``name@grid``:
+    only dispatches of that grid size, e.g. one decode batch size)."""
     import csv
     import glob
+    name_part, _, grid = name_part.partition("@")
     per = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"] and (not grid or r["Grid_Size"] == grid):
                 per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not per:
         raise SystemExit(f"no {counter} samples for '{name_part}' under {run_dir}")
@@ -558,7 +579,8 @@ def _source_hash(kind):
     return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()
 
 
-def summarize_traffic(name, kernel, alg_bytes, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb):
+def summarize_traffic(name, kernel, alg_bytes, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb,
+                      bench_args=None):
     """Turn four rocprofv3 --pmc runs (the kernel's FETCH_SIZE and WRITE_SIZE;
     the copy probe's FETCH_SIZE and WRITE_SIZE) into HBM bytes per launch,
     written to profiles/<name>_traffic.json."""
@@ -578,6 +600,14 @@ def summarize_traffic(name, kernel, alg_bytes, fetch_dir, write_dir, copy_fetch_
     rec["traffic_over_algorithmic"] = rec["bytes_per_launch"] / alg_bytes
     rec["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch summed over instances, scaled by "
                    "true bytes / counter bytes of a device copy of known size.")
+    if bench_args:
+        pmc = "cd /tmp && export TMPDIR=/tmp && cd - && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py {a}"
+        rec["commands"] = [pmc.format(c="FETCH_SIZE", d=fetch_dir, a=bench_args),
+                           pmc.format(c="WRITE_SIZE", d=write_dir, a=bench_args),
+                           pmc.format(c="FETCH_SIZE", d=copy_fetch_dir, a=f"--copy-probe {copy_mb}"),
+                           pmc.format(c="WRITE_SIZE", d=copy_write_dir, a=f"--copy-probe {copy_mb}"),
+                           f"python3 bench.py --summarize-traffic {name} '{kernel}' {alg_bytes} {fetch_dir} {write_dir} "
+                           f"{copy_fetch_dir} {copy_write_dir} {copy_mb} '{bench_args}'"]
     out = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec, indent=1))
@@ -625,6 +655,7 @@ def summarize_stats(run_dir, name, command, note, out_dir):
               "`gemv_int4_split_kernel<act, epilogue>`: act 0 = fp16, 1 = bf16; epilogue 0 = STORE, 1 = SWIGLU, "
               "2 = WEIGHTED_COMBINE, 3 = ACCUMULATE; format 0 = Q8_0, 1 = Q2_K, 2 = IQ2_XXS, 3 = int4, 4 = MXFP4, "
               "5 = FP8 E4M3 block."]
+    os.makedirs(out_dir, exist_ok=True)
     open(os.path.join(out_dir, f"{name}.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -676,6 +707,7 @@ def summarize_counters(run_dirs, name, kernel, command, note, out_dir):
     lines += [f"| {k} | {x:.3g} |" for k, x in ratios.items()]
     lines += ["", "Raw counters, per dispatch:", "", "| counter | value |", "|---|---:|"]
     lines += [f"| {c} | {x:.4g} |" for c, x in sorted(v.items())]
+    os.makedirs(out_dir, exist_ok=True)
     open(os.path.join(out_dir, f"{name}_counters.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -712,10 +744,9 @@ def main():
                     help="write profiles/NAME.md from a rocprofv3 --kernel-trace run")
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="NAME KERNEL COMMAND NOTE DIR...: write profiles/NAME_counters.md from --pmc passes")
-    ap.add_argument("--summarize-traffic", nargs=8,
-                    metavar=("NAME", "KERNEL", "ALG_BYTES", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
-                             "COPY_WRITE_DIR", "COPY_MIB"),
-                    help="write profiles/NAME_traffic.json from rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-traffic", nargs="+", metavar="ARG",
+                    help="NAME KERNEL ALG_BYTES FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR COPY_MIB [BENCH_ARGS]: "
+                         "write profiles/NAME_traffic.json")
     args = ap.parse_args()
     if args.summarize_stats:
         d = args.summarize_stats
@@ -727,7 +758,7 @@ def main():
         return
     if args.summarize_traffic:
         d = args.summarize_traffic
-        summarize_traffic(d[0], d[1], int(d[2]), d[3], d[4], d[5], d[6], int(d[7]))
+        summarize_traffic(d[0], d[1], int(d[2]), d[3], d[4], d[5], d[6], int(d[7]), d[8] if len(d) > 8 else None)
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -805,7 +836,10 @@ def main():
         log("router top-k")
         router = run_router(torch, qm)
         log(json.dumps(router))
+    decode_floor = None
     if not args.no_decode and want("decode"):
+        decode_floor = run_launch_floor(torch, args.decode_layers)
+        log(f"decode launch floor: {json.dumps(decode_floor)}")
         for B in (1, 4, 8):
             log(f"decode: B={B}")
             d, rl = run_decode(args, torch, qm, B, args.decode_layers)
@@ -826,7 +860,8 @@ def main():
                 log(json.dumps(d))
 
     if only is not None and only != "qwen":
-        print(json.dumps({"only": only, "other_prefill_workloads": others, "decode": decode, "dense_q8_0": dense,
+        print(json.dumps({"only": only, "other_prefill_workloads": others, "decode": decode,
+                          "decode_launch_floor": decode_floor, "dense_q8_0": dense,
                           "router": router, "rooflines": rooflines}), flush=True)
         return
     line = {
@@ -855,6 +890,7 @@ def main():
         "rooflines": rooflines,
         "dense_q8_0": dense,
         "decode": decode,
+        "decode_launch_floor": decode_floor,
         "other_prefill_workloads": others,
         "imbalance": imb,
         "router": router,
