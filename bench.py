@@ -423,10 +423,12 @@ def run_decode(args, torch, qm, B, layers, inp=None):
     torch.cuda.empty_cache()
     f_gu = 2.0 * B * inp.k * 2 * inp.I * inp.H
     f_dn = 2.0 * B * inp.k * inp.I * inp.H
+    # traffic records: decode_gate_up_b{B} for the int4 Qwen-shaped layer, decode_gate_up_<fmt>_b{B} for others
+    tkey = "" if inp.w_gate_up.fmt == "int4" else "_" + inp.w_gate_up.fmt
     rl = [roof("decode gate/up SWIGLU GEMV", inp.name, f_gu, bytes_gu, t_gu,
-               traffic_from_profiles(f"decode_gate_up_b{B}"), note="graph of the layers' gate/up launches only"),
+               traffic_from_profiles(f"decode_gate_up{tkey}_b{B}"), note="graph of the layers' gate/up launches only"),
           roof("decode down sum-folded GEMV", inp.name, f_dn, bytes_dn, t_dn,
-               traffic_from_profiles(f"decode_down_b{B}"), note="graph of the layers' down launches only")]
+               traffic_from_profiles(f"decode_down{tkey}_b{B}"), note="graph of the layers' down launches only")]
     return dict(workload=inp.name, B=B, layers=layers, unique_experts=int(len(uniq)), bytes_per_layer=int(nbytes),
                 us_per_layer_graph=t_graph * 1e6, us_per_layer_eager=t_eager * 1e6,
                 us_gate_up_graph=t_gu * 1e6, us_down_graph=t_dn * 1e6,
