@@ -716,6 +716,18 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
   const bool ok = e >= 0 && e < g.E;
   const int kt0 = kc * GS_TPW;
   const int64_t arows = CMB ? P : P / g.topk;
+  // Combine: the token's k expert ids and weights, read by wave 0's lanes
+  // now (in flight with the weights) rather than one dependent load pair
+  // per slot after the reduction.
+  int cmb_id = -1;
+  float cmb_w = 0.f;
+  if constexpr (CMB) {
+    if (wave == 0 && lane < g.topk) {
+      const int p = (item / nub) * g.topk + lane;
+      cmb_id = g.ids[p];
+      cmb_w = g.topk_w[p];
+    }
+  }
   const __amdgpu_buffer_rsrc_t xrs = rsrc(g.a, (uint32_t)(arows * K * 2));
 
   // Activation rows pass .. pass + n - 1 of this wave's K run: lane i loads
@@ -802,12 +814,11 @@ __global__ __launch_bounds__(1024) void gemv_int4_split_kernel(GemvArgs g, int r
         const int b = item / nub;
         float v = 0.f;
         for (int j = 0; j < g.topk; ++j) {
-          const int p = b * g.topk + j;
-          const int ej = g.ids[p];
+          const int ej = __builtin_amdgcn_readlane(cmb_id, j);
           if (ej < 0 || ej >= g.E) continue;
           float yj = 0.f;
           for (int c = 0; c < CW; ++c) yj += y[(j * CW + c) * 16 + threadIdx.x];
-          v = __builtin_fmaf(g.topk_w[p], yj, v);
+          v = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cmb_w), j)), yj, v);
         }
         store_out(g.out, g.out_dtype, (int64_t)b * g.N + ub * 16 + threadIdx.x, v);
       }
