@@ -20,7 +20,6 @@ void launch_dequant_fp8(const uint8_t*, const float*, int64_t, int64_t, void*, i
 void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
                          hipStream_t);
 void launch_plan(const int32_t*, int64_t, int, int, int, int32_t*, hipStream_t);
-int64_t plan_scratch_words(int64_t, int);
 void launch_qmm(const qmoe_weights*, const void*, int, int, const int32_t*, int64_t, int, int,
                 int64_t, const float*, int, void*, int, hipStream_t);
 int qmm_int4_bf16_max_groups();
@@ -252,7 +251,7 @@ size_t qmoe_plan_bytes(int64_t t, int32_t topk, int32_t n_experts, int32_t bm) {
   (void)bm;
   if (t < 0 || topk < 1 || n_experts < 1) return 0;
   const int64_t P = t * topk;
-  return (size_t)(plan_layout(P, n_experts).total + plan_scratch_words(P, n_experts)) * sizeof(int32_t);
+  return (size_t)plan_words(P, n_experts) * sizeof(int32_t);
 }
 
 // Tile heights the plan and the gathered matmul accept: a multiple of 16 up

@@ -108,6 +108,15 @@ __device__ __forceinline__ void dma_glb4_s(const void* base, uint32_t voff, uint
                : "memory", "m0");
 }
 
+// A wave-uniform pointer as one SGPR pair (for operands that must be scalar).
+template <typename T>
+__device__ __forceinline__ T* sgpr_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters alone.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -243,6 +252,28 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t P, int E) {
   L.inv = L.tiles + 4 * plan_max_tiles(P, E, 16);
   L.total = L.inv + P;
   return L;
+}
+
+// Chunk histograms of the plan build follow the layout (pairs per chunk).
+constexpr int PLAN_CHUNK = 1024;
+__host__ __device__ inline int64_t plan_scratch_words(int64_t P, int E) {
+  return ((P + PLAN_CHUNK - 1) / PLAN_CHUNK) * (int64_t)E;
+}
+
+// Work-balancing area of a plan for the int4 gathered matmul (plans of at
+// least SK_MIN_PAIRS pairs): SK_SLOTS tickets, then SK_SLOTS fp32 partial
+// tiles of 80 x 256 accumulators, one per K part of a unit that the matmul
+// splits across workgroups.  The plan build zeroes the tickets, header word
+// 7 records SK_SLOTS, and every split unit leaves its ticket at zero.
+constexpr int SK_SLOTS = 512;
+constexpr int SK_PART_FLOATS = 80 * 256;
+constexpr int64_t SK_MIN_PAIRS = 2048;
+__host__ __device__ inline int64_t plan_sk_offset(int64_t P, int E) {
+  return (plan_layout(P, E).total + plan_scratch_words(P, E) + 63) & ~(int64_t)63;
+}
+__host__ __device__ inline int64_t plan_words(int64_t P, int E) {
+  if (P < SK_MIN_PAIRS) return plan_layout(P, E).total + plan_scratch_words(P, E);
+  return plan_sk_offset(P, E) + SK_SLOTS + (int64_t)SK_SLOTS * SK_PART_FLOATS;
 }
 
 // Whether a plan buffer's header names the call it is used with (tile

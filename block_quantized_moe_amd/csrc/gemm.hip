@@ -35,6 +35,7 @@
 //    sum_g (b_g - 128 s_g) * X_g (X_g = sum of the activations of group g,
 //    computed by an MFMA against ones) is added at the end by three MFMAs
 //    over the groups with hi/lo bf16 splits of X and of the bias.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -77,6 +78,9 @@ struct GemmArgs {
   int n_ntiles;
   int n_blocks;
   int stage_out;  // int4 ring kernel: 2-byte output through LDS in whole rows (16-byte aligned rows)
+  int sk_slots_xcd;      // int4 ring kernel: resident workgroups per XCD (0: no split units)
+  int32_t* sk_tickets;   // the plan's work-balancing area
+  float* sk_part;
 };
 
 // Which k order a (format, activation) path uses inside a 64-wide tile.
@@ -947,6 +951,54 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The work of workgroup b of the int4 ring kernel.  Workgroup b runs on XCD
+// x = b & 7 as the j-th of that XCD (b = 8j + x) and XCD x owns tiles x,
+// x + 8, ...: its units are (tile, column block) pairs u = q * n_nt + nt of
+// tile x + 8q.  With sx workgroups resident per XCD, the units past the
+// XCD's last whole round (at most a quarter round of them) would take one
+// more round by themselves; each is split instead into SK_PARTS parts along
+// K (when every part keeps at least 4 K tiles), dealt after the whole units
+// so they go to the workgroup slots that free first.  Returns false when b
+// has no work.
+constexpr int SK_PARTS = 4;
+struct Work {
+  int mt, nt, kb, ke;
+  int part;   // K part of a split unit (-1: a whole unit)
+  int pslot;  // the part's partial-tile slot (the unit's parts are pslot - part .. + SK_PARTS - 1)
+  int tslot;  // the unit's ticket
+};
+__device__ __forceinline__ bool work_of_block(int b, int n_tiles, int n_nt, int KT, int sx, Work& w) {
+  const int x = b & 7, j = b >> 3;
+  const int nq = n_tiles > x ? (n_tiles - x + 7) >> 3 : 0;
+  const int ux = nq * n_nt;
+  int R = 0;
+  if (sx > 0 && sx <= 64 && ux > sx && KT >= 4 * SK_PARTS) {
+    R = ux % sx;
+    if (R * SK_PARTS > sx) R = 0;
+  }
+  int u;
+  w.kb = 0;
+  w.ke = KT;
+  w.part = -1;
+  w.pslot = w.tslot = 0;
+  if (j < ux - R) {
+    u = j;
+  } else {
+    const int i = j - (ux - R);  // part i % SK_PARTS of split unit i / SK_PARTS
+    if (i >= R * SK_PARTS) return false;
+    u = ux - R + i / SK_PARTS;
+    w.part = i % SK_PARTS;
+    w.kb = w.part * KT / SK_PARTS;
+    w.ke = (w.part + 1) * KT / SK_PARTS;
+    w.pslot = 64 * x + i;
+    w.tslot = 16 * x + i / SK_PARTS;
+  }
+  const int q = u / n_nt;
+  w.mt = x + 8 * q;
+  w.nt = u - q * n_nt;
+  return true;
+}
+
 template <int ACT, int EPI>
 __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void qmm_int4_kernel(GemmArgs g) {
@@ -956,6 +1008,7 @@ void qmm_int4_kernel(GemmArgs g) {
   __shared__ int rows_o[BM];
   __shared__ float wts[BM];
   __shared__ __attribute__((aligned(16))) float xg[BF ? XG4 * BM : 4];  // [group][row] activation sums
+  __shared__ int sk_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -966,8 +1019,11 @@ void qmm_int4_kernel(GemmArgs g) {
   // A plan whose header names another call gives no tiles.
   const int n_tiles = (g.amode == AM_DENSE) ? (int)((g.M + BM - 1) / BM)
                       : plan_matches(g.plan, g.bm, g.t, g.topk, g.E) ? g.plan[1] : 0;
-  int mt, nt;
-  if (!tile_of_block(blockIdx.x, n_tiles, g.n_ntiles, mt, nt)) return;
+  const int KT = (int)(g.K >> 6);
+  const bool split_ok = g.amode != AM_DENSE && g.sk_tickets != nullptr && g.plan[7] == SK_SLOTS;
+  Work wk;
+  if (!work_of_block(blockIdx.x, n_tiles, g.n_ntiles, KT, split_ok ? g.sk_slots_xcd : 0, wk)) return;
+  const int mt = wk.mt, nt = wk.nt, kb = wk.kb, ke = wk.ke;
 
   int expert, nrows;
   if (g.amode == AM_DENSE) {
@@ -1032,7 +1088,7 @@ void qmm_int4_kernel(GemmArgs g) {
 
   const int gsh = __builtin_ctz((unsigned)g.group) - 6;  // group >= 64: tile kt lies in group kt >> gsh
   const int64_t K = g.K;
-  const int T = (int)(K >> 6), G = T >> gsh;
+  const int T = KT, G = T >> gsh;
 
   // ---- per-lane load descriptors
   // activation chunks: load j (0..9) fills slots 64j .. 64j+63; wave w issues
@@ -1119,7 +1175,7 @@ void qmm_int4_kernel(GemmArgs g) {
         const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
         const uint32_t magic = 0x43004300u;
         const int gi = kt >> gsh;
-        const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0;
+        const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0 || kt == kb;
         u4_t c0[RNB], c1[RNB];
         float sc[RNB];
 #pragma unroll
@@ -1164,26 +1220,31 @@ void qmm_int4_kernel(GemmArgs g) {
       if (n_aload == 2) wait_vmcnt<4>();
       else wait_vmcnt<3>();
     };
-    if (T > 0) issue(0, 0);
-    if (T > 1) issue(1, 1);
+    if constexpr (BF) {  // a K part sums only its own groups: the others stay zero
+      if (kb > 0 || ke < T)
+        for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
+    }
+    const int nk = ke - kb;
+    if (nk > 0) issue(kb, 0);
+    if (nk > 1) issue(kb + 1, 1);
     int sc = 0;
-    for (int kt = 0; kt + 2 < T; ++kt) {
+    for (int kt = kb; kt + 2 < ke; ++kt) {
       wait_next();
       ring_barrier();
       issue(kt + 2, sc == 0 ? 2 : sc - 1);
       compute(kt, sc);
       sc = sc == 2 ? 0 : sc + 1;
     }
-    if (T > 1) {
+    if (nk > 1) {
       wait_next();
       ring_barrier();
-      compute(T - 2, sc);
+      compute(ke - 2, sc);
       sc = sc == 2 ? 0 : sc + 1;
     }
-    if (T > 0) {
+    if (nk > 0) {
       wait_vmcnt<0>();
       ring_barrier();
-      compute(T - 1, sc);
+      compute(ke - 1, sc);
     }
 
     // ---- bf16 bias term: sum_g (b - 128 s)[n, g] * X[m, g] by MFMA with hi/lo
@@ -1245,6 +1306,47 @@ void qmm_int4_kernel(GemmArgs g) {
           acc[m][b] = mfma(XL, __builtin_bit_cast(b8_t, bh), acc[m][b]);
         }
       }
+    }
+
+    // ---- a unit split into K parts: every part parks its fp32 sums in its
+    // slot and takes a ticket; the last to arrive adds the parts in part
+    // order (so the result does not depend on which finished first) and
+    // writes the unit.  Nobody waits.  The sums and the ticket travel as
+    // device-scope relaxed atomics (coherent across the XCDs' L2s without
+    // flushing or invalidating them); a part's stores are complete
+    // (vmcnt(0)) before its ticket is taken.
+    if (wk.part >= 0) {
+      // 16-byte buffer accesses with the sc1 cache policy (device-scope
+      // coherent), offsets in bytes within the unit's SK_PARTS slots
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)sgpr_ptr(g.sk_part + (int64_t)(wk.pslot - wk.part) * SK_PART_FLOATS), (short)0,
+          (int)(SK_PARTS * SK_PART_FLOATS * sizeof(float)), 0x00020000);
+      constexpr int SC1 = 16;
+      int* tk = g.sk_tickets + wk.tslot;
+#pragma unroll
+      for (int m = 0; m < MBV; ++m)
+#pragma unroll
+        for (int b = 0; b < RNB; ++b)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u4_t, acc[m][b]), prs,
+              (uint32_t)((wk.part * SK_PART_FLOATS + 4 * ((m * RNB + b) * (RW * 64) + tid)) * 4), 0, SC1);
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __syncthreads();
+      if (tid == 0) sk_arrival = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (sk_arrival != SK_PARTS - 1) return;
+      if (tid == 0) __hip_atomic_store(tk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int m = 0; m < MBV; ++m)
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          acc[m][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int pp = 0; pp < SK_PARTS; ++pp)
+            acc[m][b] += __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                prs, (uint32_t)((pp * SK_PART_FLOATS + 4 * ((m * RNB + b) * (RW * 64) + tid)) * 4), 0, SC1));
+        }
     }
 
     // ---- epilogue
@@ -1363,6 +1465,24 @@ static void launch_f(const GemmArgs& g, int act, int epi, hipStream_t s) {
   else launch_fa<FMT, ACT_BF16>(g, epi, s);
 }
 
+// Workgroups of the int4 ring kernel resident at once on the current device
+// (two per CU), a multiple of the 8 XCDs and at most 512 (the plan's
+// balancing slots); 0 when the device cannot be queried.
+static int resident_ring_blocks() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static std::atomic<int> cache[64];
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    v = min(64, 2 * cus / 8) * 8;
+    if (v <= 0) v = -1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
 // Groups per row the bf16 int4 path can keep (bias term), and the tallest tile.
 int qmm_int4_bf16_max_groups() { return XG_MAX; }
 int qmm_max_rows() { return BM; }
@@ -1395,8 +1515,22 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   else { g.n_ntiles = (int)((w->n + BN - 1) / BN); g.ldo = w->n; }
   g.n_blocks = (int)((n_mt + 7) / 8 * 8 * g.n_ntiles);  // whole rounds of the 8 XCDs
   g.stage_out = (out_dtype == QMOE_F16 || out_dtype == QMOE_BF16) && g.ldo % 8 == 0 && (uintptr_t)out % 16 == 0;
+  g.sk_slots_xcd = 0;
+  g.sk_tickets = nullptr;
+  g.sk_part = nullptr;
   if (g.n_blocks == 0) return;
   if (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi)) {
+    // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
+    // of a short last round are split along K (work_of_block), which needs
+    // up to 3 * sx / 4 more workgroups per XCD.
+    const int npb = amode != AM_DENSE && g.P >= SK_MIN_PAIRS ? resident_ring_blocks() : 0;
+    if (npb > 0) {
+      int32_t* sk = const_cast<int32_t*>(plan) + plan_sk_offset(g.P, g.E);
+      g.sk_slots_xcd = npb / 8;
+      g.sk_tickets = sk;
+      g.sk_part = (float*)(sk + SK_SLOTS);
+      g.n_blocks += 8 * (3 * g.sk_slots_xcd / 4);
+    }
     if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;

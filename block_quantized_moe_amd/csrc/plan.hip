@@ -19,7 +19,7 @@
 
 namespace qmoe {
 
-constexpr int PC = 1024;  // pairs per chunk (per workgroup)
+constexpr int PC = PLAN_CHUNK;  // pairs per chunk (per workgroup)
 
 struct PlanArgs {
   const int32_t* ids;
@@ -153,8 +153,12 @@ __global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
     a.plan[4] = (int32_t)a.t;
     a.plan[5] = a.topk;
     a.plan[6] = a.E;
-    a.plan[7] = 0;
+    a.plan[7] = a.P >= SK_MIN_PAIRS ? SK_SLOTS : 0;
     a.plan[L.offsets + a.E] = total;
+  }
+  if (chunk == 0 && a.P >= SK_MIN_PAIRS) {  // work-balancing tickets start at zero
+    int32_t* tk = a.plan + plan_sk_offset(a.P, a.E);
+    for (int i = tid; i < SK_SLOTS; i += 1024) tk[i] = 0;
   }
   __syncthreads();  // base[] and the cleared counts
 
@@ -173,8 +177,6 @@ __global__ __launch_bounds__(1024) void plan_scan_scatter_kernel(PlanArgs a) {
   a.plan[L.sorted + pos] = (int32_t)p;
   a.plan[L.inv + p] = pos;
 }
-
-int64_t plan_scratch_words(int64_t P, int E) { return ((P + PC - 1) / PC) * (int64_t)E; }
 
 void launch_plan(const int32_t* ids, int64_t t, int topk, int E, int bm, int32_t* plan,
                  hipStream_t s) {

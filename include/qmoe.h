@@ -280,12 +280,17 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
  * qmoe_workspace_bytes(QMOE_WS_PLAN, ...)) gives its size.
  *
  * Layout of the DEVICE int32 plan buffer (size from qmoe_plan_bytes):
- *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts  [7] 0
+ *   [0] dropped  [1] n_tiles  [2] n_valid  [3] bm  [4] t  [5] topk  [6] n_experts
+ *   [7] 512 when the buffer carries a work-balancing area, else 0
  *   counts [n_experts] | offsets [n_experts + 1] | sorted pair ids [t * topk]
  *   | tiles [max_tiles][4] = (expert, row0, nrows, 0), the full tiles (bm
  *   rows) in expert order, then the experts' partial last tiles in expert
  *   order | sorted position of each pair, -1 if dropped [t * topk] |
- *   scratch.  max_tiles is
+ *   scratch | (plans of t * topk >= 2048 pairs, from the next multiple of
+ *   64 words) the work-balancing area of the int4 gathered matmul: 512
+ *   int32 tickets (zeroed by the plan build, left at zero by every matmul
+ *   call) and 512 fp32 partial tiles of 80 x 256 values (about 40 MiB).
+ *   max_tiles is
  *   min(t*topk, n_experts) + t*topk/16 (the tile array fits any bm); the
  *   sorted list starts at word 8 + 2*n_experts + 1 and the tile array at the
  *   next multiple of 4 words after it.
@@ -314,6 +319,13 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
  * format's block; any n (as qmoe_qmm_dense).  Determinism is chosen by entry
  * point rather than a flag: STORE + qmoe_moe_combine is bit-reproducible,
  * WEIGHTED_COMBINE (atomics) is not.
+ * int4 weights on a plan with a work-balancing area: when an XCD's (tile,
+ * column block) units fill its resident workgroups' rounds plus a short last
+ * round, those last units are split into 4 parts along K that meet through
+ * the plan's area (fp32 partial sums added in part order, so the result is
+ * the same on every run on the same device; it can differ in the last bits
+ * from an unsplit evaluation).  The call writes the plan's area: two
+ * gathered int4 matmuls that share one plan must not run at the same time.
  * ------------------------------------------------------------------------ */
 int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
                         int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,

@@ -159,14 +159,23 @@ def test_signs_table_matches_oracle():
     assert np.array_equal(qm.iq2_signs_table(), oracle.iq2_signs())
 
 
-def test_plan_bytes_layout():
-    n = qm.plan_bytes(2048, 8, 256, 128)
-    P = 2048 * 8
-    words = 8 + 256 + 257 + P
+def _plan_words(T, k, E):
+    P = T * k
+    words = 8 + E + E + 1 + P
     words = (words + 3) & ~3
-    words += 4 * (min(P, 256) + P // 16) + P
-    words += ((P + 1023) // 1024) * 256  # chunk histogram scratch
-    assert n == 4 * words
+    words += 4 * (min(P, E) + P // 16) + P
+    words += ((P + 1023) // 1024) * E  # chunk histogram scratch
+    if P >= 2048:  # work-balancing area: 512 tickets and 512 partial tiles of 80 x 256 fp32
+        words = (words + 63) & ~63
+        words += 512 + 512 * 80 * 256
+    return words
+
+
+def test_plan_bytes_layout():
+    assert qm.plan_bytes(2048, 8, 256, 128) == 4 * _plan_words(2048, 8, 256)
+    assert qm.plan_bytes(255, 8, 64, 80) == 4 * _plan_words(255, 8, 64)      # P = 2040: no balancing area
+    assert qm.plan_bytes(256, 8, 64, 80) == 4 * _plan_words(256, 8, 64)      # P = 2048: with it
+    assert qm.plan_bytes(256, 8, 64, 80) - qm.plan_bytes(255, 8, 64, 80) > 40 << 20
 
 
 def test_argument_validation_before_launch():
