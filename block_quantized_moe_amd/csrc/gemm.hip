@@ -1023,7 +1023,7 @@ void qmm_int4_kernel(GemmArgs g) {
   const bool split_ok = g.amode != AM_DENSE && g.sk_tickets != nullptr && g.plan[7] == SK_SLOTS;
   Work wk;
   if (!work_of_block(blockIdx.x, n_tiles, g.n_ntiles, KT, split_ok ? g.sk_slots_xcd : 0, wk)) return;
-  const int mt = wk.mt, nt = wk.nt, kb = wk.kb, ke = wk.ke;
+  const int mt = wk.mt, nt = wk.nt;
 
   int expert, nrows;
   if (g.amode == AM_DENSE) {
@@ -1126,8 +1126,10 @@ void qmm_int4_kernel(GemmArgs g) {
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
   // compile-time count keeps the m loops straight-line, so MFMA results are
   // consumed late enough to need no pipeline stalls).
-  auto run = [&](auto mbv_c) {
+  auto run = [&](auto mbv_c, auto part_c) {
     constexpr int MBV = decltype(mbv_c)::value;
+    constexpr bool PART = decltype(part_c)::value;  // a K part of a split unit (whole units keep the plain loop)
+    const int kb = PART ? wk.kb : 0, ke = PART ? wk.ke : KT;
     f4_t acc[MBV][RNB];
 #pragma unroll
     for (int m = 0; m < MBV; ++m)
@@ -1175,7 +1177,7 @@ void qmm_int4_kernel(GemmArgs g) {
         const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
         const uint32_t magic = 0x43004300u;
         const int gi = kt >> gsh;
-        const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0 || kt == kb;
+        const bool first_of_group = (kt & ((1 << gsh) - 1)) == 0 || (PART && kt == kb);
         u4_t c0[RNB], c1[RNB];
         float sc[RNB];
 #pragma unroll
@@ -1220,9 +1222,8 @@ void qmm_int4_kernel(GemmArgs g) {
       if (n_aload == 2) wait_vmcnt<4>();
       else wait_vmcnt<3>();
     };
-    if constexpr (BF) {  // a K part sums only its own groups: the others stay zero
-      if (kb > 0 || ke < T)
-        for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
+    if constexpr (BF && PART) {  // a K part sums only its own groups: the others stay zero
+      for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
     }
     const int nk = ke - kb;
     if (nk > 0) issue(kb, 0);
@@ -1315,7 +1316,7 @@ void qmm_int4_kernel(GemmArgs g) {
     // device-scope relaxed atomics (coherent across the XCDs' L2s without
     // flushing or invalidating them); a part's stores are complete
     // (vmcnt(0)) before its ticket is taken.
-    if (wk.part >= 0) {
+    if (PART) {
       // 16-byte buffer accesses with the sc1 cache policy (device-scope
       // coherent), offsets in bytes within the unit's SK_PARTS slots
       const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1419,13 +1420,17 @@ void qmm_int4_kernel(GemmArgs g) {
       }
     }
   };
-  switch (mbn) {
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    case 2: run(std::integral_constant<int, 2>{}); break;
-    case 3: run(std::integral_constant<int, 3>{}); break;
-    case 4: run(std::integral_constant<int, 4>{}); break;
-    default: run(std::integral_constant<int, 5>{}); break;
-  }
+  auto dispatch = [&](auto part_c) {
+    switch (mbn) {
+      case 1: run(std::integral_constant<int, 1>{}, part_c); break;
+      case 2: run(std::integral_constant<int, 2>{}, part_c); break;
+      case 3: run(std::integral_constant<int, 3>{}, part_c); break;
+      case 4: run(std::integral_constant<int, 4>{}, part_c); break;
+      default: run(std::integral_constant<int, 5>{}, part_c); break;
+    }
+  };
+  if (wk.part >= 0) dispatch(std::true_type{});
+  else dispatch(std::false_type{});
 }
 
 // Whether the LDS-ring int4 kernel takes this call.
