@@ -999,15 +999,24 @@ __device__ __forceinline__ bool work_of_block(int b, int n_tiles, int n_nt, int 
   return true;
 }
 
-template <int ACT, int EPI>
-__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
-void qmm_int4_kernel(GemmArgs g) {
+// The ring kernel's body for int4 (either activation type) and for IQ2_XXS
+// with fp16 activations.  IQ2_XXS on the tiled layout has one contiguous
+// 256-byte run per 16-row block and K tile (two 32-value groups of
+// (index word, aux word) pairs) and one fp16 d per row and 256-value
+// super-block; the magnitudes and sign masks are expanded into LDS tables
+// once per workgroup, as in the generic kernel.
+template <int FMT, int ACT, int EPI>
+__device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool BF = (ACT == ACT_BF16);
+  constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
+  static_assert(FMT == QMOE_INT4 || (IQ2 && !BF), "ring formats: int4, IQ2_XXS with fp16 activations");
   __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
   __shared__ float wts[BM];
   __shared__ __attribute__((aligned(16))) float xg[BF ? XG4 * BM : 4];  // [group][row] activation sums
+  __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
   __shared__ int sk_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1056,6 +1065,22 @@ void qmm_int4_kernel(GemmArgs g) {
       wts[tid] = wt;
     }
   }
+  if constexpr (IQ2) {
+    if (tid < 256) {  // grid row tid as 8 fp16 magnitudes
+      const u2_t b = *(const u2_t*)(g.grid + 8 * tid);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = b[i >> 1] >> (16 * (i & 1));
+        lut_grid[4 * tid + i] = (uint32_t)f32_to_f16((float)(w & 0xFFu)) | ((uint32_t)f32_to_f16((float)((w >> 8) & 0xFFu)) << 16);
+      }
+    } else if (tid < 384) {  // sign mask tid - 256 as fp16 sign bits
+      const int si = tid - 256;
+      const uint32_t m = g.signs[si];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lut_sign[4 * si + i] = (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+    }
+  }
   __syncthreads();
   const int mbn = (nrows + 15) >> 4;
 
@@ -1086,7 +1111,9 @@ void qmm_int4_kernel(GemmArgs g) {
     rbk[b] = ((int64_t)expert * g.N + block_base(b)) >> 4;
   }
 
-  const int gsh = __builtin_ctz((unsigned)g.group) - 6;  // group >= 64: tile kt lies in group kt >> gsh
+  // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS: in
+  // super-block kt >> 2
+  const int gsh = IQ2 ? 2 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1103,24 +1130,31 @@ void qmm_int4_kernel(GemmArgs g) {
     const int src = (r < 16 * mbn && p < R_ACH) ? rows_a[min(r, BM - 1)] : -1;
     aoff[i] = src >= 0 ? (uint32_t)((int64_t)src * K * 2 + 16 * c) : 0x80000000u;
   }
-  // weight runs: lanes 0-31 block 0, lanes 32-63 block 1; scale|bias words:
-  // lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them).  The base
-  // (block 0's run) is wave-uniform and lives in SGPRs; each lane adds a
-  // 32-bit byte offset (block 1's run lies at most one expert's codes further)
+  // int4 weight runs (512 bytes per block and K tile): lanes 0-31 block 0,
+  // lanes 32-63 block 1; scale|bias words (64 bytes per block and group):
+  // lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them).  IQ2_XXS
+  // runs (256 bytes): lanes 0-15 block 0, 16-31 block 1; d halves (32 bytes
+  // per block and super-block): lanes 0-7 block 0, 8-15 block 1 (the other
+  // lanes repeat them into unused LDS).  The base (block 0's run) is
+  // wave-uniform and lives in SGPRs; each lane adds a 32-bit byte offset
+  // (block 1's run lies at most one expert's codes further)
+  constexpr int WRUN = IQ2 ? 256 : 512, SRUN = IQ2 ? 32 : 64;
   const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
   const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
-  const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * 512;
-  const uint32_t woff = (uint32_t)((lane >> 5) * (rb1 - rb0) * T * 512 + (lane & 31) * 16);
-  const uint8_t* sbase = (const uint8_t*)g.scales + rb0 * G * 64;
-  const uint32_t soff = (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * G * 64 + lr * 4);
+  const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * WRUN;
+  const uint32_t woff = IQ2 ? (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * T * WRUN + (lane & 15) * 16)
+                            : (uint32_t)((lane >> 5) * (rb1 - rb0) * T * WRUN + (lane & 31) * 16);
+  const uint8_t* sbase = (const uint8_t*)(IQ2 ? g.d : g.scales) + rb0 * G * SRUN;
+  const uint32_t soff = IQ2 ? (uint32_t)(((lane >> 3) & 1) * (rb1 - rb0) * G * SRUN + (lane & 7) * 4)
+                            : (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * G * SRUN + lr * 4);
 
   // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
   auto issue = [&](int kt, int stage) {
     const uint32_t st = lds_addr(ring) + (uint32_t)(stage * R_STAGE);
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
-    dma_glb16_s(wbase + (int64_t)kt * 512, woff, st + R_A + wave * 1024);
-    dma_glb4_s(sbase + (int64_t)(kt >> gsh) * 64, soff, st + R_A + R_B + wave * 256);
+    dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
+    dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * 256);
   };
 
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
@@ -1144,6 +1178,31 @@ void qmm_int4_kernel(GemmArgs g) {
       const uint16_t* As = (const uint16_t*)st;
       const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 1024);
       const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * 256);
+      if constexpr (IQ2) {
+        // lane group lg takes group lg >> 1 of the tile (its octets 2(lg & 1), +1)
+        const uint16_t* Ds = (const uint16_t*)Ss;
+        u4_t bf[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          Raw rw;
+          const u2_t p = *(const u2_t*)(Bs + b * 64 + (lg >> 1) * 32 + lr * 2);
+          rw.x0 = p[0];
+          rw.x1 = p[1];
+          rw.x4 = Ds[b * 16 + lr];
+          frag_f16<QMOE_IQ2_XXS>(rw, lg, lut_grid, lut_sign, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+          }
+        }
+        return;
+      }
       u2_t q[RNB];
       uint32_t sbv[RNB];
 #pragma unroll
@@ -1433,6 +1492,18 @@ void qmm_int4_kernel(GemmArgs g) {
   else dispatch(std::false_type{});
 }
 
+template <int ACT, int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_int4_kernel(GemmArgs g) {
+  ring_body<QMOE_INT4, ACT, EPI>(g);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_iq2_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_IQ2_XXS, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -1440,6 +1511,24 @@ static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
   if (act == QMOE_BF16 && g.K / g.group > XG4) return false;
   return true;
+}
+
+// Whether the LDS-ring IQ2_XXS kernel takes this call (fp16 activations).
+static bool iq2_ring_ok(const GemmArgs& g, int act, int epi) {
+  if (act != QMOE_F16) return false;
+  if (g.N * g.K / 4 >= (1ll << 31)) return false;  // per-lane byte offsets within one expert's codes
+  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
+  return true;
+}
+
+static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
 }
 
 template <int ACT>
@@ -1524,7 +1613,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.sk_tickets = nullptr;
   g.sk_part = nullptr;
   if (g.n_blocks == 0) return;
-  if (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi)) {
+  const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && iq2_ring_ok(g, act, epi);
+  if (iq2_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -1536,7 +1626,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
       g.sk_part = (float*)(sk + SK_SLOTS);
       g.n_blocks += 8 * (3 * g.sk_slots_xcd / 4);
     }
-    if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
+    if (iq2_ring) launch_iq2_ring(g, epi, s);
+    else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;
   }

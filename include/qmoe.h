@@ -287,7 +287,7 @@ int qmoe_qmm_dense(const qmoe_weights* w, const void* x, int32_t act_dtype, int6
  *   rows) in expert order, then the experts' partial last tiles in expert
  *   order | sorted position of each pair, -1 if dropped [t * topk] |
  *   scratch | (plans of t * topk >= 2048 pairs, from the next multiple of
- *   64 words) the work-balancing area of the int4 gathered matmul: 512
+ *   64 words) the work-balancing area of the ring gathered matmul: 512
  *   int32 tickets (zeroed by the plan build, left at zero by every matmul
  *   call) and 512 fp32 partial tiles of 80 x 256 values (about 40 MiB).
  *   max_tiles is
@@ -319,13 +319,14 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
  * format's block; any n (as qmoe_qmm_dense).  Determinism is chosen by entry
  * point rather than a flag: STORE + qmoe_moe_combine is bit-reproducible,
  * WEIGHTED_COMBINE (atomics) is not.
- * int4 weights on a plan with a work-balancing area: when an XCD's (tile,
+ * int4 weights, and IQ2_XXS weights with fp16 activations, on a plan with a
+ * work-balancing area: when an XCD's (tile,
  * column block) units fill its resident workgroups' rounds plus a short last
  * round, those last units are split into 4 parts along K that meet through
  * the plan's area (fp32 partial sums added in part order, so the result is
  * the same on every run on the same device; it can differ in the last bits
- * from an unsplit evaluation).  The call writes the plan's area: two
- * gathered int4 matmuls that share one plan must not run at the same time.
+ * from an unsplit evaluation).  The call writes the plan's area: two such
+ * gathered matmuls that share one plan must not run at the same time.
  * ------------------------------------------------------------------------ */
 int qmoe_moe_gather_qmm(const qmoe_weights* w, const int32_t* plan, int64_t t, int32_t topk,
                         int32_t bm, const void* a, int32_t act_dtype, int32_t a_mode,

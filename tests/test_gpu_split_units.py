@@ -1,7 +1,8 @@
-"""GPU checks of the int4 gathered matmul's split units.
+"""GPU checks of the split units of the LDS-ring gathered matmul (int4, and
+IQ2_XXS with fp16 activations).
 
 With a routing plan of at least 2048 pairs (which carries a work-balancing
-area), the LDS-ring int4 kernel looks at each XCD's units (tiles x, x + 8,
+area), the ring kernel looks at each XCD's units (tiles x, x + 8,
 ... of XCD x, times the column blocks): when they fill whole rounds of the
 XCD's resident workgroups plus a short last round (at most a quarter of
 one), those last units are split into 4 parts along K when each part keeps
@@ -17,6 +18,8 @@ units are split:
     64, STORE with fp16 activations and group 128 (K = 1280: 20 K tiles, so
     parts start at tiles 5, 10, 15, in the middle of a group), the weighted
     combine into fp32 with bf16, group 128;
+  * the IQ2_XXS ring kernel (fp16 activations, SwiGLU, K = 1280: parts start
+    inside a 256-value super-block) against the fp64 oracle;
   * two calls give bit-identical outputs (the parts are summed in a fixed
     order whichever finishes last);
   * the plan's tickets are zero after every call.
@@ -151,6 +154,26 @@ def test_split_units_weighted_combine_bf16_group128():
     oref = oracle.moe_down_combine(x64[np.arange(T * k) // k], ids, w, W)
     err = normwise_err(to_f64(out), oref, "f32")
     assert err <= TOL, (err, report(to_f64(out), oref))
+
+
+def test_split_units_iq2_xxs_swiglu_f16():
+    N, K, T, E, k = 4096, 1280, 512, 64, 8
+    rng = np.random.default_rng(16)
+    x = synth.activations(rng, T, K, "f16")
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    W = synth.iq2_xxs(rng, E, N, K)
+    plan, v = _plan(ids, T, k, E, n_nt=N // 2 // 128, KT=K // 64)
+    gu = upload(W)
+    xd = torch_act(x, "f16")
+    h1 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    h2 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    torch.cuda.synchronize()
+    _tickets_zero(plan, T, k, E)
+    assert torch.equal(h1, h2)
+    srt = v["sorted"].cpu().numpy()
+    href = oracle.moe_gate_up(oracle.act_to_f64(x, "f16"), ids, W)[srt]
+    err = normwise_err(to_f64(h1), href, "f16")
+    assert err <= TOL, (err, report(to_f64(h1), href))
 
 
 def test_model_of_the_split_rule():
