@@ -151,25 +151,28 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return __builtin_bit_cast(float, bits);
 }
 
-// Eight E2M1 codes of one tiled word (element i < 4 in the low nibble of byte
-// i, element 4 + i in its high nibble) -> four packed pairs in k order, fp16
-// (ACT_F16) or bf16.  The 3-bit magnitude selects the value's bytes from
-// 8-entry tables with byte permutes; the sign bit moves to bit 15.  Exact:
-// every E2M1 value is representable in both formats.
+// Eight E2M1 codes of one tiled word (element i in nibble i, the on-disk byte
+// order) -> four packed pairs (2j, 2j+1) in k order, fp16 (ACT_F16) or bf16,
+// each value times s: the hardware conversion turns byte j into elements 2j
+// (low nibble) and 2j+1.  Exact when every code times s is zero or a normal
+// number of the format: always for s = 1 (every E2M1 value is representable
+// in both), and for fp16 when s = 2^-13 .. 2^13.
+template <int ACT>
+__device__ __forceinline__ u4_t fp4x8_pairs_scaled(uint32_t q, float s) {
+  if constexpr (ACT == ACT_F16)
+    return u4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, s, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, s, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, s, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, s, 3))};
+  else
+    return u4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3))};
+}
 template <int ACT>
 __device__ __forceinline__ u4_t fp4x8_pairs(uint32_t q) {
-  // high / low bytes of 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  constexpr uint32_t HB0 = ACT == ACT_F16 ? 0x3E3C3800u : 0x3F3F3F00u;
-  constexpr uint32_t HB1 = ACT == ACT_F16 ? 0x46444240u : 0x40404040u;
-  constexpr uint32_t LB0 = ACT == ACT_F16 ? 0u : 0xC0800000u;
-  constexpr uint32_t LB1 = ACT == ACT_F16 ? 0u : 0xC0804000u;
-  const uint32_t m0 = q & 0x07070707u, m1 = (q >> 4) & 0x07070707u;  // elements 0-3, 4-7
-  const uint32_t h0 = perm_b32(HB1, HB0, m0) | ((q << 4) & 0x80808080u);
-  const uint32_t h1 = perm_b32(HB1, HB0, m1) | (q & 0x80808080u);
-  const uint32_t l0 = perm_b32(LB1, LB0, m0), l1 = perm_b32(LB1, LB0, m1);
-  // pair (2j, 2j+1) = [lo(2j), hi(2j), lo(2j+1), hi(2j+1)]
-  return u4_t{perm_b32(h0, l0, 0x05010400u), perm_b32(h0, l0, 0x07030602u),
-              perm_b32(h1, l1, 0x05010400u), perm_b32(h1, l1, 0x07030602u)};
+  return fp4x8_pairs_scaled<ACT>(q, 1.0f);
 }
 
 // ---------------------------------------------------------------- FP8 E4M3

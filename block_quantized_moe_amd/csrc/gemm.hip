@@ -361,15 +361,12 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
       if constexpr (FOLD) {
         // each E2M1 value times its block scale is an exact fp16 normal
         // number (0.5 * 2^-13 .. 6 * 2^13): the scale goes into the B operand
-        // with one packed fp16 multiply per pair and the MFMAs accumulate
-        // directly, with no fp32 scaling per block
+        // through the conversion and the MFMAs accumulate directly, with no
+        // fp32 scaling per block
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          // fp16 bits of 2^(e - 127) for the two blocks
-          const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)((rw[b].x0 - 112u) << 10));
-          const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)((rw[b].x2 - 112u) << 10));
-          const h8_t b0 = __builtin_bit_cast(h8_t, fp4x8_pairs<ACT>(rw[b].v[0])) * s0;
-          const h8_t b1 = __builtin_bit_cast(h8_t, fp4x8_pairs<ACT>(rw[b].v[1])) * s1;
+          const h8_t b0 = __builtin_bit_cast(h8_t, fp4x8_pairs_scaled<ACT>(rw[b].v[0], e8m0_to_f32(rw[b].x0)));
+          const h8_t b1 = __builtin_bit_cast(h8_t, fp4x8_pairs_scaled<ACT>(rw[b].v[1], e8m0_to_f32(rw[b].x2)));
 #pragma unroll
           for (int m = 0; m < MBV; ++m) {
             if (m >= c.mbn) break;

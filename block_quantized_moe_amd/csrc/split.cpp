@@ -64,8 +64,8 @@ int qmoe_split_fp8(const uint8_t* w, int64_t rows, int64_t k, uint8_t* qs) {
 // MXFP4: 17-byte blocks (E8M0 exponent, 16 code bytes with element 2i in the
 // low nibble of byte i).  Codes tiled as u32 [R/16][k/64][2][16][4]: word w
 // of block j of row 16 rb + r holds elements 8w .. 8w+7 with element 8w+i in
-// the low nibble of byte i and 8w+4+i in its high nibble (a byte-wise table
-// lookup then yields elements in k order); exponents as [R/16][k/32][16].
+// nibble i (code bytes 4w .. 4w+3 as they are on disk, so a per-byte
+// conversion yields pairs in k order); exponents as [R/16][k/32][16].
 int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e) {
   if (!aos || !qs || !e || rows < 0 || k < 0) return QMOE_ERR_ARG;
   if (k % 64) return QMOE_ERR_BLOCK;
@@ -86,7 +86,7 @@ int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uin
       for (int w = 0; w < 4; ++w) {
         uint32_t word = 0;
         for (int i = 0; i < 4; ++i)
-          word |= (uint32_t)(code[8 * w + i] | (code[8 * w + 4 + i] << 4)) << (8 * i);
+          word |= (uint32_t)(code[8 * w + 2 * i] | (code[8 * w + 2 * i + 1] << 4)) << (8 * i);
         dst[w] = word;
       }
     }

@@ -142,8 +142,8 @@ enum {
  *            NaN), tiled by qmoe_split_mxfp4 (k a multiple of 64).  R, rb, r as above, 64-wide k tile kt:
  *            qs     u32 [R/16][k/64][2][16][4]      word w of block j (32 values
  *                   at 64kt + 32j) of row 16rb + r holds the codes of elements
- *                   8w .. 8w+7 of the block: element 8w+i (i < 4) in the low
- *                   nibble of byte i, element 8w+4+i in its high nibble
+ *                   8w .. 8w+7 of the block: element 8w+i in nibble i (bits
+ *                   4i .. 4i+3; the block's code bytes 4w .. 4w+3 as on disk)
  *            scales u8  [R/16][k/32][16]        E8M0 exponent e of each block
  *            group  ignored (32)
  *   FP8      value = e4m3(code) * scale of its 128 x 128 block (E4M3: sign,

@@ -101,7 +101,7 @@ def test_split_mxfp4_tiled_layout():
                 word = int(q[R // 16, j // 2, j % 2, R % 16, w])
                 for i in range(4):
                     byte = (word >> (8 * i)) & 0xFF
-                    assert byte & 15 == codes[8 * w + i] and byte >> 4 == codes[8 * w + 4 + i]
+                    assert byte & 15 == codes[8 * w + 2 * i] and byte >> 4 == codes[8 * w + 2 * i + 1]
     with pytest.raises(qm.QmoeError):
         qm.split_mxfp4(W.blocks[:, :8], 8 * 2 // 2, k)
 
