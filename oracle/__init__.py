@@ -38,6 +38,11 @@ Readings where the pages are silent (each repeated at the function):
   * int4: nibble i of word w is element 8*w + i (low nibble first).
   * MXFP4: "low nibble first" read as element 2i in the low nibble of code
     byte i (adjacent elements share a byte).
+  * Q4_K and Q6_K: the pages only name these formats; the oracle reads them
+    as the GGUF k-quant blocks (layouts at dequant_q4_k / dequant_q6_k).
+    PARITY UNPINNED: nothing on the pages fixes these layouts, so the pins in
+    tests/test_oracle_kquants.py check only the decoders' arithmetic and bit
+    bookkeeping against that reading.
   * Routers: equal scores select the lower expert index first; the DSv4
     sqrtsoftplus gather weight is the unbiased score times the routed scaling
     factor, with no renormalisation (none is stated); the softmax-then-bias
@@ -51,6 +56,7 @@ import numpy as np
 __all__ = [
     "f16_to_f64", "bf16_to_f64", "act_to_f64", "round_f16", "round_bf16",
     "iq2_signs", "dequant", "dequant_q8_0", "dequant_q2_k", "dequant_iq2_xxs",
+    "q4_k_scales_mins", "dequant_q4_k", "dequant_q6_k",
     "e2m1_value", "e8m0_scale", "dequant_mxfp4", "e4m3_value", "dequant_fp8_block",
     "dequant_int4", "dequant_rows", "qmm", "silu", "plan", "moe_gate_up",
     "moe_down_combine", "moe_ffn", "moe_gate_up_rows", "moe_down_rows",
@@ -147,6 +153,69 @@ def dequant_q2_k(blocks: np.ndarray) -> np.ndarray:
     dl = d[..., None] * a
     ml = dmin[..., None] * m
     return dl * q - ml
+
+
+def q4_k_scales_mins(packed: np.ndarray):
+    """The 8 six-bit (scale, min) pairs of a Q4_K super-block from its 12
+    packed bytes (reading of the GGUF k-quant layout; parity unpinned).
+    Sub-blocks 0-3: scale = low 6 bits of byte j, min = low 6 bits of byte
+    j + 4.  Sub-blocks 4-7: the low 4 bits come from byte j + 4 (scale: its
+    low nibble, min: its high nibble) and the top 2 bits from the spare top
+    bits of bytes j - 4 (scale) and j (min).
+    packed: uint8 [..., 12] -> (scale, min) uint8 [..., 8] each."""
+    b = packed.astype(np.uint8)
+    sc = np.empty(b.shape[:-1] + (8,), np.uint8)
+    mn = np.empty(b.shape[:-1] + (8,), np.uint8)
+    for j in range(4):
+        sc[..., j] = b[..., j] & 63
+        mn[..., j] = b[..., j + 4] & 63
+        sc[..., j + 4] = (b[..., j + 8] & 15) | ((b[..., j] >> 6) << 4)
+        mn[..., j + 4] = (b[..., j + 8] >> 4) | ((b[..., j + 4] >> 6) << 4)
+    return sc, mn
+
+
+def dequant_q4_k(blocks: np.ndarray) -> np.ndarray:
+    """Q4_K (named by the pages; layout read as the GGUF k-quant block,
+    parity unpinned): a 256-value super-block of 8 sub-blocks of 32 values,
+    144 bytes = fp16 d, fp16 dmin, 12 bytes of packed six-bit scales and
+    mins (q4_k_scales_mins), 128 code bytes.  Element e sits in code byte
+    32*(e//64) + e%32, low nibble when e%64 < 32, else high nibble.
+    value = (d*sc_j)*q - dmin*m_j for sub-block j = e//32; d*sc*q (11 + 6 + 4
+    bits) and dmin*m are exact in fp32, so only the subtraction rounds.
+    blocks: uint8 [..., 144] -> fp32 [..., 256]."""
+    d = _f16_field(blocks, 0)
+    dmin = _f16_field(blocks, 2)
+    sc, mn = q4_k_scales_mins(blocks[..., 4:16])
+    codes = blocks[..., 16:144]
+    e = np.arange(256)
+    byte = codes[..., 32 * (e // 64) + (e % 32)]
+    q = np.where(e % 64 < 32, byte & 15, byte >> 4).astype(np.float32)
+    j = e // 32
+    return (d[..., None] * sc[..., j].astype(np.float32)) * q - dmin[..., None] * mn[..., j].astype(np.float32)
+
+
+def dequant_q6_k(blocks: np.ndarray) -> np.ndarray:
+    """Q6_K (named by the pages; layout read as the GGUF k-quant block,
+    parity unpinned): a 256-value super-block of 16 sub-blocks of 16 values,
+    210 bytes = 128 bytes of low nibbles, 64 bytes of high bit pairs, 16
+    signed scale bytes, fp16 d.  Element e = 128*n + 32*p + l (n < 2, p < 4,
+    l < 32): low 4 bits from byte 64*n + 32*(p % 2) + l of the first array
+    (low nibble for p < 2, high for p >= 2), top 2 bits from byte 32*n + l of
+    the second array at bits 2p, 2p+1; code q in 0..63.
+    value = (d*sc_s)*(q - 32) for sub-block s = e//16; d*sc is exact in fp32,
+    the product with q - 32 rounds once.
+    blocks: uint8 [..., 210] -> fp32 [..., 256]."""
+    ql = blocks[..., 0:128]
+    qh = blocks[..., 128:192]
+    sc = np.ascontiguousarray(blocks[..., 192:208]).view(np.int8).astype(np.float32)
+    d = _f16_field(blocks, 208)
+    e = np.arange(256)
+    n, p, l = e // 128, (e % 128) // 32, e % 32
+    lo = ql[..., 64 * n + 32 * (p % 2) + l]
+    lo = np.where(p < 2, lo & 15, lo >> 4)
+    hi = (qh[..., 32 * n + l] >> (2 * p).astype(np.uint8)) & 3
+    q = (lo | (hi << 4)).astype(np.float32) - np.float32(32.0)
+    return (d[..., None] * sc[..., e // 16]) * q
 
 
 def iq2_signs() -> np.ndarray:
@@ -278,6 +347,10 @@ def dequant(W) -> np.ndarray:
         v = dequant_iq2_xxs(W.blocks, W.grid)
     elif W.fmt == "mxfp4":
         v = dequant_mxfp4(W.blocks)
+    elif W.fmt == "q4_k":
+        v = dequant_q4_k(W.blocks)
+    elif W.fmt == "q6_k":
+        v = dequant_q6_k(W.blocks)
     else:
         raise ValueError(W.fmt)
     return v.reshape(W.E, W.N, W.K)

@@ -11,6 +11,8 @@ On-disk layouts produced here (one block per row-chunk of K, little endian):
 * Q8_0      34 B / 32 values : [fp16 d][32 x int8 q]
 * Q2_K      84 B / 256 values: [16 B scale|min nibbles][64 B 2-bit codes][fp16 d][fp16 dmin]
 * IQ2_XXS   66 B / 256 values: [fp16 d] then 8 groups of [4 grid-index bytes][u32 aux]
+* Q4_K     144 B / 256 values: [fp16 d][fp16 dmin][12 B packed 6-bit scales/mins][128 B 4-bit codes]
+* Q6_K     210 B / 256 values: [128 B low nibbles][64 B high bit pairs][16 x int8 scale][fp16 d]
 * int4      MLX-style, already split: qs u32 [E, N, K/8] (8 nibbles per word),
             scale / bias fp16 [E, N, K/group]
 
@@ -35,6 +37,8 @@ Q8_0_BYTES = 34
 QK_K = 256
 Q2_K_BYTES = 84
 IQ2_XXS_BYTES = 66
+Q4_K_BYTES = 144
+Q6_K_BYTES = 210
 INT4_GROUP = 64
 MXFP4_BLOCK = 32
 MXFP4_BYTES = 17
@@ -78,7 +82,7 @@ def bf16_bits(a) -> np.ndarray:
 class QWeights:
     """A stacked expert weight tensor W[E, N, K] in its on-disk form.
 
-    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "mxfp4" | "int4" | "fp8".
+    fmt: "q8_0" | "q2_k" | "iq2_xxs" | "mxfp4" | "int4" | "fp8" | "q4_k" | "q6_k".
     blocks: uint8 [E, N, K/block, block_bytes] for the GGUF-style formats.
     qs/scale/bias: int4 arrays (uint32 [E,N,K/8], uint16 fp16 bits [E,N,K/group]);
     for fp8, qs uint8 E4M3 bytes [E,N,K] and scale fp32 [E,N/128,K/128].
@@ -152,6 +156,29 @@ def q2_k(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
     return QWeights("q2_k", E, N, K, QK_K, blocks=blocks)
 
 
+def q4_k(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
+    assert K % QK_K == 0
+    nb = K // QK_K
+    blocks = np.empty((E, N, nb, Q4_K_BYTES), dtype=np.uint8)
+    d = f16_bits(_absn(rng, (E, N, nb), 0.02) / np.float32(240.0))
+    dmin = f16_bits(_absn(rng, (E, N, nb), 0.02) / np.float32(32.0))
+    blocks[..., 0:2] = d[..., None].view(np.uint8).reshape(E, N, nb, 2)
+    blocks[..., 2:4] = dmin[..., None].view(np.uint8).reshape(E, N, nb, 2)
+    blocks[..., 4:144] = rng.integers(0, 256, size=(E, N, nb, 140), dtype=np.uint8)
+    return QWeights("q4_k", E, N, K, QK_K, blocks=blocks)
+
+
+def q6_k(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
+    assert K % QK_K == 0
+    nb = K // QK_K
+    blocks = np.empty((E, N, nb, Q6_K_BYTES), dtype=np.uint8)
+    blocks[..., 0:192] = rng.integers(0, 256, size=(E, N, nb, 192), dtype=np.uint8)
+    blocks[..., 192:208] = rng.integers(-64, 64, size=(E, N, nb, 16), dtype=np.int16).astype(np.int8).view(np.uint8)
+    d = f16_bits(_absn(rng, (E, N, nb), 0.02) / np.float32(512.0))
+    blocks[..., 208:210] = d[..., None].view(np.uint8).reshape(E, N, nb, 2)
+    return QWeights("q6_k", E, N, K, QK_K, blocks=blocks)
+
+
 def iq2_xxs(rng: np.random.Generator, E: int, N: int, K: int,
             grid: np.ndarray | None = None) -> QWeights:
     assert K % QK_K == 0
@@ -212,7 +239,7 @@ def fp8(rng: np.random.Generator, E: int, N: int, K: int) -> QWeights:
 
 def weights(fmt: str, rng, E, N, K, **kw) -> QWeights:
     return {"q8_0": q8_0, "q2_k": q2_k, "iq2_xxs": iq2_xxs, "mxfp4": mxfp4, "int4": int4,
-            "fp8": fp8}[fmt](rng, E, N, K, **kw)
+            "fp8": fp8, "q4_k": q4_k, "q6_k": q6_k}[fmt](rng, E, N, K, **kw)
 
 
 # ---------------------------------------------------------------------------
