@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(HERE, "libqmoe.so")
 
 # enums mirrored from include/qmoe.h
 F32, F16, BF16 = 0, 1, 2
-Q8_0, Q2_K, IQ2_XXS, INT4, MXFP4, FP8 = 0, 1, 2, 3, 4, 5
+Q8_0, Q2_K, IQ2_XXS, INT4, MXFP4, FP8, Q4_K, Q6_K = 0, 1, 2, 3, 4, 5, 6, 7
 EPI_STORE, EPI_SWIGLU, EPI_WEIGHTED_COMBINE, EPI_ACCUMULATE = 0, 1, 2, 3
 A_GATHER_TOKENS, A_SORTED_ROWS = 0, 1
 ROUTER_SOFTMAX, ROUTER_SQRTSOFTPLUS = 0, 1
-FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4, "mxfp4": MXFP4, "fp8": FP8}
+FORMATS = {"q8_0": Q8_0, "q2_k": Q2_K, "iq2_xxs": IQ2_XXS, "int4": INT4, "mxfp4": MXFP4, "fp8": FP8,
+           "q4_k": Q4_K, "q6_k": Q6_K}
 MAX_TOPK, MAX_EXPERTS, MAX_GEMV_BATCH = 8, 1024, 64
 
 
@@ -49,6 +50,12 @@ _SIGS = {
     "qmoe_split_q2_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
     "qmoe_split_iq2_xxs": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
     "qmoe_split_mxfp4": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 2,
+    "qmoe_split_q4_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
+    "qmoe_split_q6_k": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4,
+    "qmoe_dequant_q4_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                  ctypes.c_void_p],
+    "qmoe_dequant_q6_k": [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                  ctypes.c_void_p],
     "qmoe_dequant_mxfp4": [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                                                     ctypes.c_void_p],
     "qmoe_split_fp8": [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p],
@@ -167,6 +174,36 @@ def split_q2_k(aos: np.ndarray, rows: int, k: int):
     return qs, sc, d, dmin
 
 
+def split_q4_k(aos: np.ndarray, rows: int, k: int):
+    """Q4_K blocks [rows, k/256, 144] -> tiled (qs bytes, scales|mins bytes, d, dmin)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 256) * 144:
+        raise QmoeError("split_q4_k: block count does not match rows/k")
+    nb = split_rows(rows) * (k // 256)
+    qs = np.empty(nb * 128, np.uint8)
+    sc = np.empty(nb * 16, np.uint8)
+    d = np.empty(nb, np.uint16)
+    dmin = np.empty(nb, np.uint16)
+    _check(lib().qmoe_split_q4_k(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(sc), _np_ptr(d), _np_ptr(dmin)),
+           "split_q4_k")
+    return qs, sc, d, dmin
+
+
+def split_q6_k(aos: np.ndarray, rows: int, k: int):
+    """Q6_K blocks [rows, k/256, 210] -> tiled (low-nibble bytes, top-bit-pair bytes, int8 scales, d)."""
+    aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
+    if aos.size != rows * (k // 256) * 210:
+        raise QmoeError("split_q6_k: block count does not match rows/k")
+    nb = split_rows(rows) * (k // 256)
+    qs = np.empty(nb * 128, np.uint8)
+    qh = np.empty(nb * 64, np.uint8)
+    sc = np.empty(nb * 16, np.int8)
+    d = np.empty(nb, np.uint16)
+    _check(lib().qmoe_split_q6_k(_np_ptr(aos), rows, k, _np_ptr(qs), _np_ptr(qh), _np_ptr(sc), _np_ptr(d)),
+           "split_q6_k")
+    return qs, qh, sc, d
+
+
 def split_iq2_xxs(aos: np.ndarray, rows: int, k: int):
     """IQ2_XXS blocks [rows, k/256, 66] -> tiled ((index, aux) word pairs, d)."""
     aos = np.ascontiguousarray(aos, dtype=np.uint8).reshape(-1)
@@ -266,7 +303,7 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
            bias=None, group: int = 0, grid=None) -> DeviceWeights:
     """Split on-disk weights on the host (library splitter) and copy them to the device.
 
-    blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs / mxfp4.
+    blocks: uint8 on-disk blocks [E, N, K/block, bytes] for q8_0 / q2_k / iq2_xxs / mxfp4 / q4_k / q6_k.
     qs, scale, bias: MLX-style int4 arrays for int4; for fp8, qs uint8 E4M3 codes
     [E, N, K] and scale fp32 [E, N/128, K/128].  grid: uint8 [256, 8] (iq2_xxs)."""
     t = {}
@@ -284,6 +321,12 @@ def upload(fmt: str, E: int, N: int, K: int, *, device="cuda", blocks=None, qs=N
     elif fmt == "mxfp4":
         q, e = split_mxfp4(blocks, E * N, K)
         t["qs"], t["scales"] = _dev(q, device), _dev(e, device)
+    elif fmt == "q4_k":
+        q, sc, d, dmin = split_q4_k(blocks, E * N, K)
+        t["qs"], t["scales"], t["d"], t["dmin"] = (_dev(q, device), _dev(sc, device), _dev(d, device), _dev(dmin, device))
+    elif fmt == "q6_k":
+        q, qh, sc, d = split_q6_k(blocks, E * N, K)
+        t["qs"], t["aux"], t["scales"], t["d"] = (_dev(q, device), _dev(qh, device), _dev(sc, device), _dev(d, device))
     elif fmt == "fp8":
         t["qs"] = _dev(split_fp8(qs, E * N, K), device)
         t["scales"] = _dev(np.ascontiguousarray(scale, np.float32).reshape(-1), device)
@@ -373,6 +416,12 @@ def dequant(w: DeviceWeights, out_dtype: int = F32, out=None):
         st = L.qmoe_dequant_fp8(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
     elif w.fmt == "mxfp4":
         st = L.qmoe_dequant_mxfp4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, _ptr(out), out_dtype, s)
+    elif w.fmt == "q4_k":
+        st = L.qmoe_dequant_q4_k(_ptr(t["qs"]), _ptr(t["scales"]), _ptr(t["d"]), _ptr(t["dmin"]),
+                                 w.E * w.N, w.K, _ptr(out), out_dtype, s)
+    elif w.fmt == "q6_k":
+        st = L.qmoe_dequant_q6_k(_ptr(t["qs"]), _ptr(t["aux"]), _ptr(t["scales"]), _ptr(t["d"]),
+                                 w.E * w.N, w.K, _ptr(out), out_dtype, s)
     else:
         st = L.qmoe_dequant_int4(_ptr(t["qs"]), _ptr(t["scales"]), w.E * w.N, w.K, w.group,
                                  _ptr(out), out_dtype, s)

@@ -15,6 +15,10 @@ void launch_dequant_q2_k(const uint32_t*, const uint8_t*, const uint16_t*, const
                          void*, int, hipStream_t);
 void launch_dequant_iq2_xxs(const uint32_t*, const uint16_t*, const uint8_t*, const uint8_t*, int64_t, int64_t,
                             void*, int, hipStream_t);
+void launch_dequant_q4_k(const uint8_t*, const uint8_t*, const uint16_t*, const uint16_t*, int64_t, int64_t, void*,
+                         int, hipStream_t);
+void launch_dequant_q6_k(const uint8_t*, const uint8_t*, const int8_t*, const uint16_t*, int64_t, int64_t, void*,
+                         int, hipStream_t);
 void launch_dequant_mxfp4(const uint32_t*, const uint8_t*, int64_t, int64_t, void*, int, hipStream_t);
 void launch_dequant_fp8(const uint8_t*, const float*, int64_t, int64_t, void*, int, hipStream_t);
 void launch_dequant_int4(const uint32_t*, const uint32_t*, int64_t, int64_t, int, void*, int,
@@ -85,6 +89,16 @@ int check_weights(const qmoe_weights* w, bool need_k64) {
       if (w->k % 256) return QMOE_ERR_BLOCK;
       if (!w->scales || !w->d || !w->dmin) return QMOE_ERR_ARG;
       if (!al16(w->scales) || !al16(w->d) || !al16(w->dmin)) return QMOE_ERR_ALIGN;
+      break;
+    case QMOE_Q4_K:
+      if (w->k % 256) return QMOE_ERR_BLOCK;
+      if (!w->scales || !w->d || !w->dmin) return QMOE_ERR_ARG;
+      if (!al16(w->scales) || !al16(w->d) || !al16(w->dmin)) return QMOE_ERR_ALIGN;
+      break;
+    case QMOE_Q6_K:
+      if (w->k % 256) return QMOE_ERR_BLOCK;
+      if (!w->aux || !w->scales || !w->d) return QMOE_ERR_ARG;
+      if (!al16(w->aux) || !al16(w->scales) || !al16(w->d)) return QMOE_ERR_ALIGN;
       break;
     case QMOE_IQ2_XXS:
       if (w->k % 256) return QMOE_ERR_BLOCK;
@@ -187,6 +201,28 @@ int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t*
   launch_dequant_q2_k(qs, scales, d, dmin, rows, k, out, out_dtype, (hipStream_t)stream);
   return launched();
 }
+int qmoe_dequant_q4_k(const uint8_t* qs, const uint8_t* scales, const uint16_t* d, const uint16_t* dmin,
+                      int64_t rows, int64_t k, void* out, int32_t out_dtype, void* stream) {
+  if (!qs || !scales || !d || !dmin || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (k % 256) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(scales) || !al16(d) || !al16(dmin) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_q4_k(qs, scales, d, dmin, rows, k, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
+int qmoe_dequant_q6_k(const uint8_t* qs, const uint8_t* qh, const int8_t* scales, const uint16_t* d,
+                      int64_t rows, int64_t k, void* out, int32_t out_dtype, void* stream) {
+  if (!qs || !qh || !scales || !d || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;
+  if (k % 256) return QMOE_ERR_BLOCK;
+  if (!al16(qs) || !al16(qh) || !al16(scales) || !al16(d) || !al16(out)) return QMOE_ERR_ALIGN;
+  if (rows == 0 || k == 0) return QMOE_OK;
+  QMOE_TRY(check_arch());
+  launch_dequant_q6_k(qs, qh, scales, d, rows, k, out, out_dtype, (hipStream_t)stream);
+  return launched();
+}
+
 int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid, const uint8_t* signs,
                          int64_t rows, int64_t k, void* out, int32_t out_dtype, void* stream) {
   if (!qs || !d || !grid || !signs || !out || rows < 0 || k < 0 || !dtype_ok(out_dtype)) return QMOE_ERR_ARG;

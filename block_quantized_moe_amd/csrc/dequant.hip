@@ -52,6 +52,65 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
   }
 }
 
+// Q4_K (tiled layout, qmoe.h): value = (d * sc_j) * q - dmin * m_j for
+// sub-block j = e / 32; both products are exact in fp32 (11 + 6 + 4 and 11 + 6
+// bits), so only the subtraction rounds.  Unit u is elements 8p .. 8p+7 of a
+// super-block of row R: the low (p % 8 < 4) or high nibbles of code bytes
+// 8 (p % 4) .. +7 of quarter p / 8.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_q4_k_kernel(const uint8_t* __restrict__ qs,
+                                                           const uint8_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ d,
+                                                           const uint16_t* __restrict__ dmin,
+                                                           int64_t n_units, int64_t SB, void* __restrict__ out) {
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t R = u / (SB * 32), ur = u - R * SB * 32;
+    const int64_t sb = ur >> 5, t = (R >> 4) * SB + sb, r = R & 15;
+    const int p = (int)(ur & 31);
+    const int h = p >> 3, cb = 8 * (p & 3), shift = 4 * ((p >> 2) & 1), j = p >> 2;
+    const u2_t q = *(const u2_t*)(qs + ((t * 4 + h) * 16 + r) * 32 + cb);
+    const float dl = f16_to_f32(d[t * 16 + r]) * (float)sc[(t * 16 + r) * 16 + j];
+    const float ml = f16_to_f32(dmin[t * 16 + r]) * (float)sc[(t * 16 + r) * 16 + 8 + j];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (q[i >> 2] >> (8 * (i & 3) + shift)) & 15u;
+      v[i] = dl * (float)c - ml;
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
+// Q6_K (tiled layout, qmoe.h): value = (d * sc_s) * (q - 32) for sub-block
+// s = e / 16; d * sc is exact in fp32, the product with q - 32 rounds once.
+// Unit u is elements 8p .. 8p+7 of a super-block of row R: low nibbles from
+// quarter p / 8 of qs (high nibbles when p % 8 >= 4), top bit pairs from half
+// p / 16 of qh at bits 2 ((p % 16) / 4).
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_q6_k_kernel(const uint8_t* __restrict__ qs,
+                                                           const uint8_t* __restrict__ qh,
+                                                           const int8_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ d,
+                                                           int64_t n_units, int64_t SB, void* __restrict__ out) {
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < n_units; u += (int64_t)gridDim.x * 256) {
+    const int64_t R = u / (SB * 32), ur = u - R * SB * 32;
+    const int64_t sb = ur >> 5, t = (R >> 4) * SB + sb, r = R & 15;
+    const int p = (int)(ur & 31);
+    const int cb = 8 * (p & 3);
+    const int sn = 4 * ((p >> 2) & 1), sh = 2 * ((p & 15) >> 2);
+    const u2_t lo = *(const u2_t*)(qs + ((t * 4 + (p >> 3)) * 16 + r) * 32 + cb);
+    const u2_t hi = *(const u2_t*)(qh + ((t * 2 + (p >> 4)) * 16 + r) * 32 + cb);
+    const float ds = f16_to_f32(d[t * 16 + r]) * (float)sc[(t * 16 + r) * 16 + (p >> 1)];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = ((lo[i >> 2] >> (8 * (i & 3) + sn)) & 15u) | (((hi[i >> 2] >> (8 * (i & 3) + sh)) & 3u) << 4);
+      v[i] = ds * (float)((int)c - 32);
+    }
+    store8<OUT>(out, u, v);
+  }
+}
+
 // Q2_K: value = (d * a) * q - dmin * m with the sub-block's scale a (low
 // nibble) and min m (high nibble); element e's 2-bit code is in code byte
 // 32*(e/128) + e%32 at bit 2*((e%128)/32).  Tiled layout (qmoe.h): unit u
@@ -220,6 +279,18 @@ void launch_dequant_q2_k(const uint32_t* qs, const uint8_t* sc, const uint16_t* 
   const int64_t units = rows * (k / 8);
   QMOE_DISPATCH_OUT(dtype, dequant_q2_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, (const uint8_t*)qs, sc,
                     d, dmin, units, k / 256, out);
+}
+void launch_dequant_q4_k(const uint8_t* qs, const uint8_t* sc, const uint16_t* d, const uint16_t* dmin,
+                         int64_t rows, int64_t k, void* out, int dtype, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_q4_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, sc, d, dmin, units,
+                    k / 256, out);
+}
+void launch_dequant_q6_k(const uint8_t* qs, const uint8_t* qh, const int8_t* sc, const uint16_t* d, int64_t rows,
+                         int64_t k, void* out, int dtype, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  QMOE_DISPATCH_OUT(dtype, dequant_q6_k_kernel, dim3(grid_for(units)), dim3(256), 0, s, qs, qh, sc, d, units,
+                    k / 256, out);
 }
 void launch_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid, const uint8_t* signs,
                             int64_t rows, int64_t k, void* out, int dtype, hipStream_t s) {

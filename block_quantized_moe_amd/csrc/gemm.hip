@@ -88,12 +88,14 @@ template <int FMT, int ACT>
 struct KOrder {
   // true: lane group g owns k in [16g, 16g+16); false: MFMA step s covers [32s, 32s+32)
   static constexpr bool chunk =
-      !(FMT == QMOE_MXFP4 || (ACT == ACT_BF16 && (FMT == QMOE_Q8_0 || FMT == QMOE_IQ2_XXS)));
+      !(FMT == QMOE_MXFP4 ||
+        (ACT == ACT_BF16 && (FMT == QMOE_Q8_0 || FMT == QMOE_IQ2_XXS || FMT == QMOE_Q4_K || FMT == QMOE_Q6_K)));
 };
 
 // Raw weight bytes one lane needs for one 64-wide K tile of one output row.
 struct Raw {
   u4_t v;        // codes
+  u4_t v2;       // Q6_K: the codes' top bit pairs
   uint32_t x0;   // scale / idx word
   uint32_t x1;   // bias / aux word
   uint32_t x2;   // d / second idx word
@@ -161,6 +163,56 @@ __device__ __forceinline__ Raw load_raw(const GemmArgs& g, int64_t R, int64_t k0
     r.x1 = 2u * (uint32_t)((e0 & 127) >> 5);  // bit shift of this lane's codes
     r.x2 = ((const uint16_t*)g.d)[t * 16 + rr];
     r.x3 = ((const uint16_t*)g.dmin)[t * 16 + rr];
+  } else if constexpr (FMT == QMOE_Q4_K) {
+    // tiled layout: the 64-wide tile is quarter h of the super-block, 32 code
+    // bytes per row (element 64h + i in the low nibble of byte i, 64h + 32 + i
+    // in the high); scales then mins of the 8 sub-blocks as bytes
+    const int64_t t = (R >> 4) * (K / 256) + k0 / 256, rr = R & 15;
+    const int h = (int)(k0 & 255) >> 6;
+    const uint8_t* cq = (const uint8_t*)g.qs + ((t * 4 + h) * 16 + rr) * 32;
+    const uint8_t* sm = (const uint8_t*)g.scales + (t * 16 + rr) * 16;
+    if constexpr (KOrder<FMT, ACT>::chunk) {
+      // values 16 lg .. +15: bytes 16 (lg & 1) .. +15, high nibbles for lg >= 2
+      r.v = *(const u4_t*)(cq + 16 * (lg & 1));
+      r.x1 = 4u * (uint32_t)(lg >> 1);
+      const int j = 2 * h + (lg >> 1);
+      r.x0 = (uint32_t)sm[j] | ((uint32_t)sm[8 + j] << 8);
+    } else {
+      // MFMA step s: values 32 s + 8 lg .. +7 = low (s = 0) or high (s = 1)
+      // nibbles of bytes 8 lg .. +7; sub-blocks 2h and 2h + 1
+      const u2_t q = *(const u2_t*)(cq + 8 * lg);
+      r.v[0] = q[0];
+      r.v[1] = q[1];
+      r.x0 = (uint32_t)sm[2 * h] | ((uint32_t)sm[2 * h + 1] << 8) | ((uint32_t)sm[8 + 2 * h] << 16) |
+             ((uint32_t)sm[9 + 2 * h] << 24);
+    }
+    r.x2 = ((const uint16_t*)g.d)[t * 16 + rr];
+    r.x3 = ((const uint16_t*)g.dmin)[t * 16 + rr];
+  } else if constexpr (FMT == QMOE_Q6_K) {
+    // tiled layout: low 4 bits as Q4_K's codes; top bit pairs of element
+    // 128 n + 32 p + i at byte i of half n, bits 2p (the tile is quarter h, so
+    // n = h / 2 and p = 2 (h % 2) + (0 or 1)); int8 scales of 16-value sub-blocks
+    const int64_t t = (R >> 4) * (K / 256) + k0 / 256, rr = R & 15;
+    const int h = (int)(k0 & 255) >> 6;
+    const uint8_t* cq = (const uint8_t*)g.qs + ((t * 4 + h) * 16 + rr) * 32;
+    const uint8_t* ch = (const uint8_t*)g.aux + ((t * 2 + (h >> 1)) * 16 + rr) * 32;
+    const int8_t* sc = (const int8_t*)g.scales + (t * 16 + rr) * 16;
+    if constexpr (KOrder<FMT, ACT>::chunk) {
+      r.v = *(const u4_t*)(cq + 16 * (lg & 1));
+      r.v2 = *(const u4_t*)(ch + 16 * (lg & 1));
+      r.x1 = (4u * (uint32_t)(lg >> 1)) | ((2u * (uint32_t)(2 * (h & 1) + (lg >> 1))) << 8);
+      r.x0 = (uint32_t)(uint8_t)sc[4 * h + lg];  // sub-block of values 16 lg .. +15
+    } else {
+      // step s: values 32 s + 8 lg .. +7: nibbles of bytes 8 lg .. +7 (high
+      // for s = 1), top bits of bytes 8 lg .. +7 at bits 4 (h % 2) + 2 s;
+      // the four scales of sub-blocks 4h .. 4h + 3
+      const u2_t q = *(const u2_t*)(cq + 8 * lg);
+      const u2_t p = *(const u2_t*)(ch + 8 * lg);
+      r.v = u4_t{q[0], q[1], p[0], p[1]};
+      r.x1 = 4u * (uint32_t)(h & 1);
+      r.x0 = *(const uint32_t*)(sc + 4 * h);
+    }
+    r.x2 = ((const uint16_t*)g.d)[t * 16 + rr];
   } else {  // IQ2_XXS, tiled: (index word, aux word) pairs by group and row
     const int64_t t = (R >> 4) * (K / 256) + k0 / 256, rr = R & 15;
     const uint32_t* ia = (const uint32_t*)g.qs + (t * 8 * 16 + rr) * 2;
@@ -238,6 +290,37 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
       const h2_t hi = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B23)) - off;
       const uint32_t vl = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, dl2, ml2));
       const uint32_t vh = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(hi, dl2, ml2));
+      if (w < 2) { o0[2 * w] = vl; o0[2 * w + 1] = vh; }
+      else { o1[2 * (w - 2)] = vl; o1[2 * (w - 2) + 1] = vh; }
+    }
+  } else if constexpr (FMT == QMOE_Q4_K) {
+    const float d = f16_to_f32(r.x2), dm = f16_to_f32(r.x3);
+    const _Float16 dl = (_Float16)(d * (float)(r.x0 & 255u));
+    const _Float16 ml = (_Float16)(-(dm * (float)((r.x0 >> 8) & 255u)));
+    const h2_t dl2 = h2_t{dl, dl}, ml2 = h2_t{ml, ml};
+    const h2_t off = h2_t{(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t t = (r.v[w] >> r.x1) & 0x0F0F0F0Fu;
+      const h2_t lo = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B01)) - off;
+      const h2_t hi = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B23)) - off;
+      const uint32_t vl = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, dl2, ml2));
+      const uint32_t vh = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(hi, dl2, ml2));
+      if (w < 2) { o0[2 * w] = vl; o0[2 * w + 1] = vh; }
+      else { o1[2 * (w - 2)] = vl; o1[2 * (w - 2) + 1] = vh; }
+    }
+  } else if constexpr (FMT == QMOE_Q6_K) {
+    const _Float16 dl = (_Float16)(f16_to_f32(r.x2) * (float)(int8_t)(r.x0 & 255u));
+    const h2_t dl2 = h2_t{dl, dl};
+    const h2_t off = h2_t{(_Float16)1056.0f, (_Float16)1056.0f};  // 1024 + 32
+    const uint32_t sn = r.x1 & 255u, sh = (r.x1 >> 8) & 255u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t t = ((r.v[w] >> sn) & 0x0F0F0F0Fu) | (((r.v2[w] >> sh) & 0x03030303u) << 4);
+      const h2_t lo = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B01)) - off;
+      const h2_t hi = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B23)) - off;
+      const uint32_t vl = __builtin_bit_cast(uint32_t, lo * dl2);
+      const uint32_t vh = __builtin_bit_cast(uint32_t, hi * dl2);
       if (w < 2) { o0[2 * w] = vl; o0[2 * w + 1] = vh; }
       else { o1[2 * (w - 2)] = vl; o1[2 * (w - 2) + 1] = vh; }
     }
@@ -542,6 +625,87 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
             const f4_t t = mfma(a, __builtin_bit_cast(b8_t, cc[st]), f4_t{0, 0, 0, 0});
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[m][b][r] = __builtin_fmaf(dsc[st], t[r], acc[m][b][r]);
+          }
+        }
+      }
+    } else if constexpr (FMT == QMOE_Q4_K) {
+      // plain k order: step s = sub-block 2h + s of the tile's quarter h.  The
+      // codes enter as exact bf16 (128 + q); sum a*(d sc q - dmin m) over the
+      // step is d sc * T - (128 d sc + dmin m) * X with T the MFMA of the
+      // codes and X the step's activation sums (an MFMA with ones)
+      const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      u4_t cc[NB][2];
+      float dsc[NB][2], cx[NB][2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float d = f16_to_f32(rw[b].x2), dm = f16_to_f32(rw[b].x3);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint32_t t0 = (rw[b].v[0] >> (4 * st)) & 0x0F0F0F0Fu, t1 = (rw[b].v[1] >> (4 * st)) & 0x0F0F0F0Fu;
+          cc[b][st] = u4_t{perm_b32(0x43434343u, t0, SEL_B01), perm_b32(0x43434343u, t0, SEL_B23),
+                           perm_b32(0x43434343u, t1, SEL_B01), perm_b32(0x43434343u, t1, SEL_B23)};
+          dsc[b][st] = d * (float)((rw[b].x0 >> (8 * st)) & 255u);
+          cx[b][st] = 128.0f * dsc[b][st] + dm * (float)((rw[b].x0 >> (16 + 8 * st)) & 255u);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MBV; ++m) {
+        if (m >= c.mbn) break;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
+          const f4_t tx = mfma(a, ones, f4_t{0, 0, 0, 0});
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f4_t tq = mfma(a, __builtin_bit_cast(b8_t, cc[b][st]), f4_t{0, 0, 0, 0});
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[m][b][r] = __builtin_fmaf(dsc[b][st], tq[r], __builtin_fmaf(-cx[b][st], tx[r], acc[m][b][r]));
+          }
+        }
+      }
+    } else if constexpr (FMT == QMOE_Q6_K) {
+      // plain k order: step s covers sub-blocks 4h + 2s (lane groups 0-1) and
+      // 4h + 2s + 1 (lane groups 2-3), each with its own scale, so each half
+      // goes through its own MFMA (the other lanes' operands zero).  Codes
+      // (128 + q) are exact in bf16 (q < 64); sum a*d sc (q - 32) over a half
+      // is d sc * (T - 160 X).
+      const b8_t ones = __builtin_bit_cast(b8_t, u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      const b8_t zero8 = __builtin_bit_cast(b8_t, u4_t{0u, 0u, 0u, 0u});
+      const bool first_half = lg < 2;
+      u4_t cc[NB][2];
+      float ds[NB][4];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float d = f16_to_f32(rw[b].x2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ds[b][j] = d * (float)(int8_t)((rw[b].x0 >> (8 * j)) & 255u);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint32_t sh = rw[b].x1 + 2u * (uint32_t)st;
+          const uint32_t t0 = ((rw[b].v[0] >> (4 * st)) & 0x0F0F0F0Fu) | (((rw[b].v[2] >> sh) & 0x03030303u) << 4);
+          const uint32_t t1 = ((rw[b].v[1] >> (4 * st)) & 0x0F0F0F0Fu) | (((rw[b].v[3] >> sh) & 0x03030303u) << 4);
+          cc[b][st] = u4_t{perm_b32(0x43434343u, t0, SEL_B01), perm_b32(0x43434343u, t0, SEL_B23),
+                           perm_b32(0x43434343u, t1, SEL_B01), perm_b32(0x43434343u, t1, SEL_B23)};
+        }
+      }
+      const b8_t ones_a = first_half ? ones : zero8, ones_b = first_half ? zero8 : ones;
+#pragma unroll
+      for (int m = 0; m < MBV; ++m) {
+        if (m >= c.mbn) break;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const b8_t a = __builtin_bit_cast(b8_t, *(const u4_t*)(Ab + (16 * m + lr) * LDA + 32 * st + 8 * lg));
+          const f4_t xa = mfma(a, ones_a, f4_t{0, 0, 0, 0});
+          const f4_t xb = mfma(a, ones_b, f4_t{0, 0, 0, 0});
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const b8_t cv = __builtin_bit_cast(b8_t, cc[b][st]);
+            const f4_t ta = mfma(a, first_half ? cv : zero8, f4_t{0, 0, 0, 0});
+            const f4_t tb = mfma(a, first_half ? zero8 : cv, f4_t{0, 0, 0, 0});
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[m][b][r] += ds[b][2 * st] * (ta[r] - 160.0f * xa[r]) + ds[b][2 * st + 1] * (tb[r] - 160.0f * xb[r]);
           }
         }
       }
@@ -1631,6 +1795,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   switch (w->fmt) {
     case QMOE_Q8_0: launch_f<QMOE_Q8_0>(g, act, epi, s); break;
     case QMOE_Q2_K: launch_f<QMOE_Q2_K>(g, act, epi, s); break;
+    case QMOE_Q4_K: launch_f<QMOE_Q4_K>(g, act, epi, s); break;
+    case QMOE_Q6_K: launch_f<QMOE_Q6_K>(g, act, epi, s); break;
     case QMOE_IQ2_XXS: launch_f<QMOE_IQ2_XXS>(g, act, epi, s); break;
     case QMOE_MXFP4: launch_f<QMOE_MXFP4>(g, act, epi, s); break;
     case QMOE_FP8: launch_f<QMOE_FP8>(g, act, epi, s); break;

@@ -70,7 +70,9 @@ struct XChunk {
 // (int4 bias, Q2_K mins): forming them makes the kernel wait for the
 // activations before it issues its weight loads.
 template <int FMT>
-__host__ __device__ constexpr bool needs_x_sums() { return FMT == QMOE_INT4 || FMT == QMOE_Q2_K; }
+__host__ __device__ constexpr bool needs_x_sums() {
+  return FMT == QMOE_INT4 || FMT == QMOE_Q2_K || FMT == QMOE_Q4_K || FMT == QMOE_Q6_K;
+}
 
 template <int ACT, bool SUMS>
 __device__ __forceinline__ void load_x(const uint16_t* src, XChunk& x) {
@@ -117,6 +119,7 @@ __device__ __forceinline__ void i8x4_pairs(uint32_t w, uint32_t& p0, uint32_t& p
 // in flight before the first dot product.
 struct ChunkRaw {
   u4_t q0, q1;
+  u4_t q2, q3;  // Q6_K: the codes' top bit pairs
   uint32_t m0, m1, m2, m3;
 };
 
@@ -163,6 +166,34 @@ __device__ __forceinline__ ChunkRaw chunk_load(const GemvArgs& g, int64_t R, int
     w.m1 = ((const uint8_t*)g.scales)[(t * 16 + r) * 16 + 2 * cc + 1];
     w.m2 = ((const uint16_t*)g.d)[t * 16 + r];
     w.m3 = ((const uint16_t*)g.dmin)[t * 16 + r];
+  } else if constexpr (FMT == QMOE_Q4_K) {
+    // chunk c = sub-block j = c%8 of super-block c/8: bytes 0..31 of quarter
+    // j/2 of row r, low nibbles for even j, high for odd
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
+    const int j = (int)(c & 7);
+    const uint8_t* qb = (const uint8_t*)g.qs + ((t * 4 + (j >> 1)) * 16 + r) * 32;
+    w.q0 = *(const u4_t*)qb;
+    w.q1 = *(const u4_t*)(qb + 16);
+    const uint8_t* sm = (const uint8_t*)g.scales + (t * 16 + r) * 16;
+    w.m0 = sm[j];
+    w.m1 = sm[8 + j];
+    w.m2 = ((const uint16_t*)g.d)[t * 16 + r];
+    w.m3 = ((const uint16_t*)g.dmin)[t * 16 + r];
+  } else if constexpr (FMT == QMOE_Q6_K) {
+    // chunk c = sub-blocks 2j, 2j+1 (j = c%8) of super-block c/8: low bits as
+    // Q4_K's codes, top bit pairs from bytes 0..31 of half j/4 at bits 2 (j%4)
+    const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
+    const int j = (int)(c & 7);
+    const uint8_t* qb = (const uint8_t*)g.qs + ((t * 4 + (j >> 1)) * 16 + r) * 32;
+    const uint8_t* hb = (const uint8_t*)g.aux + ((t * 2 + (j >> 2)) * 16 + r) * 32;
+    w.q0 = *(const u4_t*)qb;
+    w.q1 = *(const u4_t*)(qb + 16);
+    w.q2 = *(const u4_t*)hb;
+    w.q3 = *(const u4_t*)(hb + 16);
+    const uint8_t* sc = (const uint8_t*)g.scales + (t * 16 + r) * 16;
+    w.m0 = sc[2 * j];
+    w.m1 = sc[2 * j + 1];
+    w.m2 = ((const uint16_t*)g.d)[t * 16 + r];
   } else {  // IQ2_XXS: chunk c is group c%8 of super-block c/8 (tiled layout)
     const int64_t t = (R >> 4) * (K / 256) + c / 8, r = R & 15;
     const int G = (int)(c & 7);
@@ -265,6 +296,59 @@ __device__ __forceinline__ void chunk_math(const GemvArgs& g, const ChunkRaw& w,
         }
         res[t] += dl0 * (p0 - Magic<ACT>::v * x[t].s0) - ml0 * x[t].s0 +
                   dl1 * (p1 - Magic<ACT>::v * x[t].s1) - ml1 * x[t].s1;
+      }
+    }
+  } else if constexpr (FMT == QMOE_Q4_K) {
+    // value = d sc q - dmin m over the whole chunk (one sub-block)
+    const uint32_t shift = 4u * (uint32_t)(c & 1);
+    const float dl = f16_to_f32(w.m2) * (float)w.m0;
+    const float ml = f16_to_f32(w.m3) * (float)w.m1;
+    uint32_t cp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t t0 = (w.q0[q] >> shift) & 0x0F0F0F0Fu;
+      const uint32_t t1 = (w.q1[q] >> shift) & 0x0F0F0F0Fu;
+      cp[2 * q] = perm_b32(Magic<ACT>::byte, t0, 0x04010400u);
+      cp[2 * q + 1] = perm_b32(Magic<ACT>::byte, t0, 0x04030402u);
+      cp[8 + 2 * q] = perm_b32(Magic<ACT>::byte, t1, 0x04010400u);
+      cp[8 + 2 * q + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t < nt) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2t<ACT>(x[t].p[i], cp[i], p);
+        const float xs = x[t].s0 + x[t].s1;
+        res[t] += dl * (p - Magic<ACT>::v * xs) - ml * xs;
+      }
+    }
+  } else if constexpr (FMT == QMOE_Q6_K) {
+    // value = d sc (q - 32) per 16-value half, each half with its own scale
+    const uint32_t sn = 4u * (uint32_t)(c & 1), sh = 2u * (uint32_t)(c & 3);
+    const float d = f16_to_f32(w.m2);
+    const float d0 = d * (float)(int8_t)w.m0, d1 = d * (float)(int8_t)w.m1;
+    uint32_t cp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t t0 = ((w.q0[q] >> sn) & 0x0F0F0F0Fu) | (((w.q2[q] >> sh) & 0x03030303u) << 4);
+      const uint32_t t1 = ((w.q1[q] >> sn) & 0x0F0F0F0Fu) | (((w.q3[q] >> sh) & 0x03030303u) << 4);
+      cp[2 * q] = perm_b32(Magic<ACT>::byte, t0, 0x04010400u);
+      cp[2 * q + 1] = perm_b32(Magic<ACT>::byte, t0, 0x04030402u);
+      cp[8 + 2 * q] = perm_b32(Magic<ACT>::byte, t1, 0x04010400u);
+      cp[8 + 2 * q + 1] = perm_b32(Magic<ACT>::byte, t1, 0x04030402u);
+    }
+    constexpr float off = Magic<ACT>::v + 32.0f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t < nt) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0 = dot2t<ACT>(x[t].p[i], cp[i], p0);
+          p1 = dot2t<ACT>(x[t].p[8 + i], cp[8 + i], p1);
+        }
+        res[t] += d0 * (p0 - off * x[t].s0) + d1 * (p1 - off * x[t].s1);
       }
     }
   } else {  // IQ2_XXS
@@ -980,6 +1064,8 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
   switch (w->fmt) {
     case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
     case QMOE_Q2_K: launch_gemv_f<QMOE_Q2_K>(g, act, cpl, epi, units, s); break;
+    case QMOE_Q4_K: launch_gemv_f<QMOE_Q4_K>(g, act, cpl, epi, units, s); break;
+    case QMOE_Q6_K: launch_gemv_f<QMOE_Q6_K>(g, act, cpl, epi, units, s); break;
     case QMOE_IQ2_XXS: launch_gemv_f<QMOE_IQ2_XXS>(g, act, cpl, epi, units, s); break;
     case QMOE_MXFP4: launch_gemv_f<QMOE_MXFP4>(g, act, cpl, epi, units, s); break;
     case QMOE_FP8: launch_gemv_f<QMOE_FP8>(g, act, cpl, epi, units, s); break;

@@ -126,6 +126,89 @@ int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint
   return QMOE_OK;
 }
 
+// Q4_K (the pages name the format only; read as the GGUF k-quant block):
+// 144-byte blocks [fp16 d][fp16 dmin][12 packed bytes of six-bit sub-block
+// scales and mins][128 code bytes: element e in byte 32*(e/64) + e%32, low
+// nibble when e%64 < 32].  Tiled, t = (R/16) * k/256 + super-block, r = R%16:
+// qs [t][4][16][32] (quarter h of row r = its code bytes 32h .. 32h+31),
+// scales [t][16][16] (row r's 8 scales, then its 8 mins, one byte each),
+// d, dmin [t][16].
+int qmoe_split_q4_k(const void* aos, int64_t rows, int64_t k, uint8_t* qs, uint8_t* scales, uint16_t* d,
+                    uint16_t* dmin) {
+  if (!aos || !qs || !scales || !d || !dmin || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (k % 256) return QMOE_ERR_BLOCK;
+  const int64_t SB = k / 256;
+  {
+    const int64_t r0 = rows / 16 * 16, np = pad16(rows) - r0;  // rows of the last, partial block
+    memset(qs + r0 * SB * 128, 0, (size_t)(np * SB * 128));
+    memset(scales + r0 * SB * 16, 0, (size_t)(np * SB * 16));
+    memset(d + r0 * SB, 0, (size_t)(np * SB) * 2);
+    memset(dmin + r0 * SB, 0, (size_t)(np * SB) * 2);
+  }
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t sb = 0; sb < SB; ++sb) {
+      const uint8_t* p = (const uint8_t*)aos + (R * SB + sb) * 144;
+      const int64_t base = rb * SB + sb;
+      memcpy(&d[base * 16 + r], p, 2);
+      memcpy(&dmin[base * 16 + r], p + 2, 2);
+      const uint8_t* b = p + 4;
+      uint8_t* sm = &scales[(base * 16 + r) * 16];
+      for (int j = 0; j < 4; ++j) {
+        sm[j] = b[j] & 63;
+        sm[8 + j] = b[j + 4] & 63;
+        sm[j + 4] = (uint8_t)((b[j + 8] & 15) | ((b[j] >> 6) << 4));
+        sm[8 + j + 4] = (uint8_t)((b[j + 8] >> 4) | ((b[j + 4] >> 6) << 4));
+      }
+      for (int h = 0; h < 4; ++h) memcpy(&qs[((base * 4 + h) * 16 + r) * 32], p + 16 + 32 * h, 32);
+    }
+  }
+  return QMOE_OK;
+}
+
+// Q6_K (named only; read as the GGUF k-quant block): 210-byte blocks [128
+// bytes of low nibbles][64 bytes of top bit pairs][16 int8 scales][fp16 d];
+// element e = 128n + 32p + l takes its low 4 bits from byte 64n + 32(p%2) + l
+// of the first array (high nibble when p >= 2) and its top 2 bits from byte
+// 32n + l of the second (bits 2p, 2p+1).  Tiled: qs [t][4][16][32] low
+// nibbles in the Q4_K code arrangement (byte i of quarter h: element 64h+i
+// in the low nibble, 64h+32+i in the high), qh [t][2][16][32] top bit pairs
+// as on disk (half n of row r = its bytes 32n .. 32n+31), scales int8
+// [t][16][16], d [t][16].
+int qmoe_split_q6_k(const void* aos, int64_t rows, int64_t k, uint8_t* qs, uint8_t* qh, int8_t* scales,
+                    uint16_t* d) {
+  if (!aos || !qs || !qh || !scales || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
+  if (k % 256) return QMOE_ERR_BLOCK;
+  const int64_t SB = k / 256;
+  {
+    const int64_t r0 = rows / 16 * 16, np = pad16(rows) - r0;
+    memset(qs + r0 * SB * 128, 0, (size_t)(np * SB * 128));
+    memset(qh + r0 * SB * 64, 0, (size_t)(np * SB * 64));
+    memset(scales + r0 * SB * 16, 0, (size_t)(np * SB * 16));
+    memset(d + r0 * SB, 0, (size_t)(np * SB) * 2);
+  }
+  for (int64_t R = 0; R < rows; ++R) {
+    const int64_t rb = R / 16, r = R % 16;
+    for (int64_t sb = 0; sb < SB; ++sb) {
+      const uint8_t* p = (const uint8_t*)aos + (R * SB + sb) * 210;
+      const int64_t base = rb * SB + sb;
+      uint8_t lo[256];
+      for (int e = 0; e < 256; ++e) {
+        const int n = e / 128, pp = (e % 128) / 32, l = e % 32;
+        const uint8_t b = p[64 * n + 32 * (pp % 2) + l];
+        lo[e] = pp < 2 ? (b & 15) : (b >> 4);
+      }
+      for (int h = 0; h < 4; ++h)
+        for (int i = 0; i < 32; ++i)
+          qs[((base * 4 + h) * 16 + r) * 32 + i] = (uint8_t)(lo[64 * h + i] | (lo[64 * h + 32 + i] << 4));
+      for (int n = 0; n < 2; ++n) memcpy(&qh[((base * 2 + n) * 16 + r) * 32], p + 128 + 32 * n, 32);
+      memcpy(&scales[(base * 16 + r) * 16], p + 192, 16);
+      memcpy(&d[base * 16 + r], p + 208, 2);
+    }
+  }
+  return QMOE_OK;
+}
+
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* ia, uint16_t* d) {
   if (!aos || !ia || !d || rows < 0 || k < 0) return QMOE_ERR_ARG;
   if (k % 256) return QMOE_ERR_BLOCK;

@@ -65,7 +65,11 @@ typedef enum {
                         groups with an even-parity 8th sign, 4-bit scale [GGUF Kernels 3] */
   QMOE_INT4 = 3,     /* MLX-style affine int4: s*q + b per group         [BAGEL]          */
   QMOE_MXFP4 = 4,    /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 values [GGUF MXFP4]     */
-  QMOE_FP8 = 5       /* FP8 E4M3 bytes, fp32 scale per 128 x 128 block   [GGUF FP8 block] */
+  QMOE_FP8 = 5,      /* FP8 E4M3 bytes, fp32 scale per 128 x 128 block   [GGUF FP8 block] */
+  QMOE_Q4_K = 6,     /* 256-value super-blocks, 4-bit codes, 6-bit scale/min per 32,
+                        fp16 d/dmin  (named by [DSV4]; layout read as the GGUF k-quant) */
+  QMOE_Q6_K = 7      /* 256-value super-blocks, 6-bit codes, int8 scale per 16, fp16 d
+                        (named by [DSV4]; layout read as the GGUF k-quant) */
 } qmoe_format;
 
 /* Epilogues of the matmul entry points. */
@@ -126,6 +130,23 @@ enum {
  *            d      fp16  [t][16]
  *            grid   u8    [256, 8]               magnitude rows
  *            signs  u8    [128]                  sign masks (qmoe_iq2_signs_table)
+ *   Q4_K     value = (d*sc_j)*q - dmin*m_j over 32-value sub-blocks j, tiled by
+ *            qmoe_split_q4_k (k a multiple of 256); t, r as for Q2_K:
+ *            qs     u8    [t][4][16][32]         quarter h of row r's 128 code bytes
+ *                                                (byte i: element 64h+i in the low
+ *                                                nibble, 64h+32+i in the high)
+ *            scales u8    [t][16][16]            row r's 8 six-bit scales, then its
+ *                                                8 six-bit mins, one byte each
+ *            d,dmin fp16  [t][16]
+ *   Q6_K     value = (d*sc_s)*(q - 32) over 16-value sub-blocks s (q = 6-bit
+ *            code), tiled by qmoe_split_q6_k (k a multiple of 256):
+ *            qs     u8    [t][4][16][32]         low 4 bits of the codes in the Q4_K
+ *                                                code arrangement
+ *            aux    u8    [t][2][16][32]         top 2 bits: half h of row r's 64
+ *                                                bytes, element 128h + 32p + i at
+ *                                                byte i, bits 2p, 2p+1
+ *            scales int8  [t][16][16]
+ *            d      fp16  [t][16]
  *   INT4     value = s*q + b per group of `group` values along k, tiled by
  *            qmoe_split_int4 (k a multiple of 64 and of group).  Global row R = e*n + row, block rb = R/16,
  *            r = R%16, 64-wide k tile kt:
@@ -187,12 +208,24 @@ typedef struct qmoe_weights {
  *   IQ2_XXS  66 B: fp16 d, then 8 x (4 grid-index bytes, u32 aux)
  *   MXFP4    17 B: E8M0 exponent, 16 code bytes (element 2i in the low
  *            nibble of byte i, 2i+1 in its high nibble)  [GGUF MXFP4 "Format"]
+ *   Q4_K    144 B: fp16 d, fp16 dmin, 12 bytes of packed six-bit scales and
+ *            mins (sub-blocks 0-3: low 6 bits of bytes j and j+4; 4-7: the
+ *            nibbles of byte j+8 plus the top 2 bits of bytes j-4 and j), 128
+ *            code bytes (element e in byte 32*(e/64) + e%32, low nibble when
+ *            e%64 < 32)
+ *   Q6_K    210 B: 128 bytes of low nibbles, 64 bytes of top bit pairs, 16
+ *            int8 scales, fp16 d (element 128n + 32p + l: low bits in byte
+ *            64n + 32(p%2) + l, high nibble when p >= 2; top bits in byte
+ *            32n + l at bits 2p, 2p+1)
+ *   (the pages only name Q4_K and Q6_K; these are the GGUF k-quant blocks)
  * They come out in the tiled forms above (so that each wave-wide load of
  * the matmul kernels reads contiguous bytes), with R = qmoe_split_rows(rows):
  * Q8_0 qs R*k bytes, scales R*k/32; Q2_K qs R*k/4 bytes, scales R*k/16
  * bytes, d and dmin R*k/256; IQ2_XXS qs R*k/16 u32, d R*k/256; MXFP4 qs
- * R*k/8 u32, e R*k/32 bytes.  Returns QMOE_ERR_ARG on NULL / negative sizes,
- * QMOE_ERR_BLOCK unless k is a multiple of 64 (Q8_0, MXFP4) or 256.
+ * R*k/8 u32, e R*k/32 bytes; Q4_K qs R*k/2 bytes, scales R*k/16 bytes, d and
+ * dmin R*k/256; Q6_K qs R*k/2 bytes, qh R*k/4 bytes, scales R*k/16, d R*k/256.  Returns QMOE_ERR_ARG on NULL / negative sizes,
+ * QMOE_ERR_BLOCK unless k is a multiple of 64 (Q8_0, MXFP4) or 256 (Q2_K,
+ * IQ2_XXS, Q4_K, Q6_K).
  * ------------------------------------------------------------------------ */
 /* rows rounded up to a multiple of 16: the row count every tiled array of
  * the splitters is sized for (-1 for a negative count). */
@@ -202,6 +235,10 @@ int qmoe_split_q2_k(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint
                     uint16_t* d, uint16_t* dmin);
 int qmoe_split_iq2_xxs(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint16_t* d);
 int qmoe_split_mxfp4(const void* aos, int64_t rows, int64_t k, uint32_t* qs, uint8_t* e);
+int qmoe_split_q4_k(const void* aos, int64_t rows, int64_t k, uint8_t* qs, uint8_t* scales,
+                    uint16_t* d, uint16_t* dmin);
+int qmoe_split_q6_k(const void* aos, int64_t rows, int64_t k, uint8_t* qs, uint8_t* qh,
+                    int8_t* scales, uint16_t* d);
 /* FP8 block weights ([GGUF] FP8 block dequant commit: one E4M3 byte per
  * weight, row-major [rows][k], and one fp32 scale per 128 x 128 block) ->
  * the tiled code array above (rows*k bytes); the scales need no split.
@@ -240,6 +277,15 @@ int qmoe_dequant_q2_k(const uint32_t* qs, const uint8_t* scales, const uint16_t*
 int qmoe_dequant_iq2_xxs(const uint32_t* qs, const uint16_t* d, const uint8_t* grid,
                          const uint8_t* signs, int64_t rows, int64_t k,
                          void* out, int32_t out_dtype, void* stream);
+/* Q4_K / Q6_K (k a multiple of 256): the tiled arrays of qmoe_split_q4_k /
+ * qmoe_split_q6_k.  Q4_K values round once (the subtraction), Q6_K once (the
+ * product of d*scale with q - 32). */
+int qmoe_dequant_q4_k(const uint8_t* qs, const uint8_t* scales, const uint16_t* d,
+                      const uint16_t* dmin, int64_t rows, int64_t k,
+                      void* out, int32_t out_dtype, void* stream);
+int qmoe_dequant_q6_k(const uint8_t* qs, const uint8_t* qh, const int8_t* scales,
+                      const uint16_t* d, int64_t rows, int64_t k,
+                      void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_int4(const uint32_t* qs, const uint32_t* sb, int64_t rows, int64_t k,
                       int32_t group, void* out, int32_t out_dtype, void* stream);
 int qmoe_dequant_mxfp4(const uint32_t* qs, const uint8_t* e, int64_t rows, int64_t k,

@@ -106,6 +106,53 @@ def test_split_mxfp4_tiled_layout():
         qm.split_mxfp4(W.blocks[:, :8], 8 * 2 // 2, k)
 
 
+def test_split_q4_k_tiled_layout():
+    """Decoding the tiled arrays as the header lays them out gives the
+    oracle's values for every element (the oracle reads the on-disk blocks)."""
+    rows, k = 32, 512
+    W = synth.q4_k(np.random.default_rng(5), 2, rows // 2, k)
+    qs, sm, d, dmin = qm.split_q4_k(W.blocks, rows, k)
+    SB = k // 256
+    qs = qs.reshape(rows // 16, SB, 4, 16, 32)
+    sm = sm.reshape(rows // 16, SB, 16, 16)
+    d = d.reshape(rows // 16, SB, 16).view(np.float16).astype(np.float32)
+    dmin = dmin.reshape(rows // 16, SB, 16).view(np.float16).astype(np.float32)
+    e = np.arange(256)
+    R = np.arange(rows)
+    byte = qs[R[:, None, None] // 16, np.arange(SB)[None, :, None], (e // 64)[None, None, :], R[:, None, None] % 16,
+              (e % 32)[None, None, :]]
+    q = np.where(e % 64 < 32, byte & 15, byte >> 4).astype(np.float32)
+    rb, r, sb = R[:, None, None] // 16, R[:, None, None] % 16, np.arange(SB)[None, :, None]
+    sc = sm[rb, sb, r, (e // 32)[None, None, :]].astype(np.float32)
+    mn = sm[rb, sb, r, 8 + (e // 32)[None, None, :]].astype(np.float32)
+    v = (d[rb, sb, r] * sc) * q - dmin[rb, sb, r] * mn
+    assert np.array_equal(v.reshape(rows, k), oracle.dequant(W).reshape(rows, k))
+    with pytest.raises(qm.QmoeError):
+        qm.split_q4_k(W.blocks[:, :, :1], rows, k)
+
+
+def test_split_q6_k_tiled_layout():
+    rows, k = 32, 512
+    W = synth.q6_k(np.random.default_rng(6), 2, rows // 2, k)
+    qs, qh, sc, d = qm.split_q6_k(W.blocks, rows, k)
+    SB = k // 256
+    qs = qs.reshape(rows // 16, SB, 4, 16, 32)
+    qh = qh.reshape(rows // 16, SB, 2, 16, 32)
+    sc = sc.reshape(rows // 16, SB, 16, 16).astype(np.float32)
+    d = d.reshape(rows // 16, SB, 16).view(np.float16).astype(np.float32)
+    e = np.arange(256)[None, None, :]
+    R = np.arange(rows)
+    rb, r, sb = R[:, None, None] // 16, R[:, None, None] % 16, np.arange(SB)[None, :, None]
+    lo = qs[rb, sb, e // 64, r, e % 32]
+    lo = np.where(e % 64 < 32, lo & 15, lo >> 4)
+    hi = (qh[rb, sb, e // 128, r, e % 32] >> (2 * ((e % 128) // 32)).astype(np.uint8)) & 3
+    q = (lo | (hi << 4)).astype(np.float32) - 32
+    v = (d[rb, sb, r] * sc[rb, sb, r, e // 16]) * q
+    assert np.array_equal(v.reshape(rows, k), oracle.dequant(W).reshape(rows, k))
+    with pytest.raises(qm.QmoeError):
+        qm.split_q6_k(W.blocks[:, :, :1], rows, k)
+
+
 def test_split_fp8_tiled_layout():
     """Every code lands where the header's tiled layout says (the Q8_0 code tiling)."""
     rows, k = 256, 384
@@ -276,7 +323,8 @@ def test_split_any_row_count_pads_with_zero_rows(rows):
     rng = np.random.default_rng(rows)
     k = 512
     for fmt, bv, bb, split in (("q8_0", 32, 34, qm.split_q8_0), ("q2_k", 256, 84, qm.split_q2_k),
-                               ("iq2_xxs", 256, 66, qm.split_iq2_xxs), ("mxfp4", 32, 17, qm.split_mxfp4)):
+                               ("iq2_xxs", 256, 66, qm.split_iq2_xxs), ("mxfp4", 32, 17, qm.split_mxfp4),
+                               ("q4_k", 256, 144, qm.split_q4_k), ("q6_k", 256, 210, qm.split_q6_k)):
         W = synth.weights(fmt, rng, 1, rows, k)
         got = split(W.blocks, rows, k)
         ref = split(_with_zero_rows(W.blocks, rows, k, bv, bb, R - rows), R, k)

@@ -36,7 +36,7 @@ def _bits_equal(gpu, ref, dtype):
 
 
 def _weights(fmt, rng):
-    if fmt in ("q2_k", "iq2_xxs"):
+    if fmt in ("q2_k", "iq2_xxs", "q4_k", "q6_k"):
         W = synth.weights(fmt, rng, 2, 40, 512)   # E*N a multiple of 16 (tiled layout)
     elif fmt == "int4":
         W = synth.int4(rng, 2, 40, 512, 64)   # E*N a multiple of 16 (tiled int4 layout)
@@ -72,6 +72,17 @@ def _plant_specials(W):
         W.scale[1, 0, 0] = f(3e38)                            # 3e38 * 448 overflows fp32
         W.qs[0, 0, 0:4] = [0x7F, 0xFF, 0x80, 0x01]          # NaN, NaN, -0, smallest subnormal
         W.qs[0, 1, 128:136] = [0x00, 0x07, 0x08, 0x7E, 0xFE, 0x87, 0x88, 0xF7]
+    elif W.fmt == "q4_k":
+        W.blocks[0, 0, 0, 0:2] = h(0x7E00)    # NaN d
+        W.blocks[0, 1, 0, 2:4] = h(0x0001)    # subnormal dmin
+        W.blocks[0, 2, 0, 0:2] = h(0x0003)    # subnormal d
+        W.blocks[0, 3, 0, 0:4] = 0            # zero d and dmin
+        W.blocks[0, 4, 1, 0:2] = h(0x7C00)    # inf d
+    elif W.fmt == "q6_k":
+        W.blocks[0, 0, 0, 208:210] = h(0x7E00)
+        W.blocks[0, 1, 0, 208:210] = h(0x0001)
+        W.blocks[0, 2, 0, 208:210] = h(0x8000)  # -0: values +-0
+        W.blocks[0, 3, 1, 192:208] = 0x80       # scales -128
     elif W.fmt == "iq2_xxs":
         W.blocks[0, 0, 0, 0:2] = h(0x7E00)
         W.blocks[0, 1, 0, 0:2] = h(0x0001)
@@ -84,7 +95,7 @@ def _plant_specials(W):
     return W
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8", "q4_k", "q6_k"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_dequant_bit_exact(fmt, dtype):
     W = _plant_specials(_weights(fmt, np.random.default_rng(17)))

@@ -21,7 +21,7 @@ from _helpers import TOL, normwise_err, report, to_f64, torch_act, upload
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8"]
+FMTS = ["q8_0", "q2_k", "iq2_xxs", "int4", "mxfp4", "fp8", "q4_k", "q6_k"]
 
 
 def _w(fmt, rng, E, N, K):
@@ -67,6 +67,10 @@ def _exact_weights(fmt, rng, E, N, K):
     elif fmt == "q2_k":
         W.blocks[..., 80:82] = h(1.0)
         W.blocks[..., 82:84] = h(1.0)
+    elif fmt == "q4_k":
+        W.blocks[..., 0:4] = np.concatenate([h(1.0), h(1.0)])   # values scale*q - min, at most 945
+    elif fmt == "q6_k":
+        W.blocks[..., 208:210] = h(1.0)                          # values scale*(q - 32), |v| <= 2048
     elif fmt == "mxfp4":
         W.blocks[..., 0] = 128         # scale 2: values 0, +-1, +-2, +-3, +-4, +-6, +-8, +-12
     elif fmt == "fp8":
@@ -199,7 +203,8 @@ def _check_moe(x, ids, w, Wgu, Wd, act, **kw):
                                        ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
                                        ("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
                                        ("mxfp4", "mxfp4", "bf16"), ("mxfp4", "mxfp4", "f16"),
-                                       ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16")])
+                                       ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16"),
+                                       ("q4_k", "q6_k", "f16"), ("q6_k", "q4_k", "bf16")])
 def test_moe_stagewise(gu, dn, act):
     x, ids, w, Wgu, Wd = _moe_case(gu, dn, act, seed=len(gu) + len(act))
     _check_moe(x, ids, w, Wgu, Wd, act)

@@ -56,7 +56,9 @@ def test_gemv_qwen_decode_int4_full_size(B):
 @pytest.mark.parametrize("gu,dn,act", [("q8_0", "q8_0", "f16"), ("q8_0", "q8_0", "bf16"),
                                        ("iq2_xxs", "q2_k", "f16"), ("iq2_xxs", "q2_k", "bf16"),
                                        ("int4", "int4", "f16"), ("mxfp4", "mxfp4", "bf16"),
-                                       ("mxfp4", "mxfp4", "f16"), ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16")])
+                                       ("mxfp4", "mxfp4", "f16"), ("fp8", "fp8", "bf16"), ("fp8", "fp8", "f16"),
+                                       ("q4_k", "q6_k", "f16"), ("q6_k", "q4_k", "bf16"), ("q4_k", "q4_k", "bf16"),
+                                       ("q6_k", "q6_k", "f16")])
 def test_gemv_formats(gu, dn, act):
     rng = np.random.default_rng(len(gu) * 7 + len(act))
     B, E, k, H, I = 4, 16, 4, 1024, 512
