@@ -27,7 +27,7 @@ Also in the same JSON line:
                    bounded samples of the others (1-core and all-core C1).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-extra]
-                    [--only {qwen,dense,decode,dsv4,dsv4-mxfp4,dsv4-fp8,mixed,router}]
+                    [--only {qwen,dense,decode,dsv4,dsv4-mxfp4,dsv4-fp8,dsv4-kquant,mixed,router}]
 
 Counter calibration and traffic records (see profiles/):
     python bench.py --copy-probe MIB
@@ -739,7 +739,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the DSv4-shaped and mixed-format prefill lines")
-    ap.add_argument("--only", choices=["qwen", "dense", "decode", "dsv4", "dsv4-mxfp4", "dsv4-fp8", "mixed", "router"],
+    ap.add_argument("--only", choices=["qwen", "dense", "decode", "dsv4", "dsv4-mxfp4", "dsv4-fp8", "dsv4-kquant",
+                                       "mixed", "router"],
                     help="run one workload (for per-workload profiles); prints its own JSON, not the bench line")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a device copy of MIB MiB (counter calibration) and exit")
@@ -815,6 +816,7 @@ def main():
         for name, make, R in (("dsv4", lambda: synth.dsv4_flash_prefill(2048), 2),
                               ("dsv4-mxfp4", lambda: synth.dsv4_flash_mxfp4_prefill(2048), 2),
                               ("dsv4-fp8", lambda: synth.dsv4_flash_fp8_prefill(2048), 2),
+                              ("dsv4-kquant", lambda: synth.dsv4_flash_kquant_prefill(2048), 2),
                               ("mixed", lambda: synth.mixed_ffn(8192), 2)):
             if not want(name):
                 continue
@@ -831,7 +833,7 @@ def main():
             if not args.no_cpu and only is None and name in ("dsv4", "mixed"):
                 log(f"cpu oracle sample ({name})")
                 cpu_other.append(cpu_sample_experts(inp_o, np.arange(8)))
-            if name in ("dsv4-mxfp4", "dsv4-fp8"):
+            if name in ("dsv4-mxfp4", "dsv4-fp8", "dsv4-kquant"):
                 decode_inputs[name] = inp_o  # its weights also serve the decode lines of the format
             else:
                 del inp_o

@@ -381,5 +381,12 @@ def dsv4_flash_fp8_prefill(T: int = 2048, **over) -> MoEInputs:
     return moe(6, T=T, name="dsv4-flash-fp8-prefill", **{**DSV4_FLASH, **fmt, **over})
 
 
+def dsv4_flash_kquant_prefill(T: int = 2048, **over) -> MoEInputs:
+    """The DSv4-Flash expert shapes with Q4_K gate/up and Q6_K down weights
+    (the k-quant formats the pages name; layouts read as GGUF's)."""
+    fmt = dict(gate_up_fmt="q4_k", down_fmt="q6_k")
+    return moe(7, T=T, name="dsv4-flash-kquant-prefill", **{**DSV4_FLASH, **fmt, **over})
+
+
 def mixed_ffn(T: int = 8192, **over) -> MoEInputs:
     return moe(4, T=T, name="mixed-format-moe-ffn", **{**MIXED_FFN, **over})
