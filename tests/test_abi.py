@@ -255,6 +255,18 @@ def test_argument_validation_before_launch():
     P16 = ctypes.c_void_p(16)
     assert L.qmoe_dequant_q2_k(P16, P16, P16, P16, 8, 320, P16, 1, None) == -3
     assert L.qmoe_dequant_iq2_xxs(P16, P16, P16, P16, 16, 128, P16, 1, None) == -3
+    assert L.qmoe_dequant_q4_k(P16, P16, P16, P16, 16, 320, P16, 1, None) == -3
+    assert L.qmoe_dequant_q6_k(P16, P16, P16, P16, 16, 512 + 64, P16, 1, None) == -3
+    assert L.qmoe_dequant_q4_k(P16, P16, P16, None, 16, 256, P16, 1, None) == E
+    assert L.qmoe_dequant_q6_k(P16, None, P16, P16, 16, 256, P16, 1, None) == E
+    assert L.qmoe_dequant_q6_k(P16, ctypes.c_void_p(8), P16, P16, 16, 256, P16, 1, None) == -6
+    # k-quant weights in a matmul: k a multiple of 256; Q4_K needs d and dmin, Q6_K the top-bit array
+    w = qm._Weights(qm.Q4_K, 1, 64, 320, 0, 0, 16, 0, 16, 0, 16, 16, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == -3
+    w = qm._Weights(qm.Q4_K, 1, 64, 256, 0, 0, 16, 0, 16, 0, 16, 0, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == E
+    w = qm._Weights(qm.Q6_K, 1, 64, 256, 0, 0, 16, 0, 16, 0, 16, 0, 0, 0)
+    assert L.qmoe_qmm_dense(ctypes.byref(w), ctypes.c_void_p(16), 1, 4, 0, ctypes.c_void_p(16), 1, None) == E
     # FP8: rows and k multiples of the 128 x 128 scale block; scales required
     assert L.qmoe_dequant_fp8(P16, P16, 64, 128, P16, 1, None) == -3
     assert L.qmoe_dequant_fp8(P16, P16, 128, 192, P16, 1, None) == -3
