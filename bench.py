@@ -657,7 +657,7 @@ def summarize_stats(run_dir, name, command, note, out_dir):
               "`qmm_kernel<format, act, epilogue>`, "
               "`gemv_int4_split_kernel<act, epilogue>`: act 0 = fp16, 1 = bf16; epilogue 0 = STORE, 1 = SWIGLU, "
               "2 = WEIGHTED_COMBINE, 3 = ACCUMULATE; format 0 = Q8_0, 1 = Q2_K, 2 = IQ2_XXS, 3 = int4, 4 = MXFP4, "
-              "5 = FP8 E4M3 block."]
+              "5 = FP8 E4M3 block, 6 = Q4_K, 7 = Q6_K."]
     os.makedirs(out_dir, exist_ok=True)
     open(os.path.join(out_dir, f"{name}.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
