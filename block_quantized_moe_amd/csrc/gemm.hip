@@ -1161,16 +1161,21 @@ __device__ __forceinline__ bool work_of_block(int b, int n_tiles, int n_nt, int 
 }
 
 // The ring kernel's body for int4 (either activation type) and for IQ2_XXS
-// with fp16 activations.  IQ2_XXS on the tiled layout has one contiguous
-// 256-byte run per 16-row block and K tile (two 32-value groups of
+// and Q2_K with fp16 activations.  IQ2_XXS on the tiled layout has one
+// contiguous 256-byte run per 16-row block and K tile (two 32-value groups of
 // (index word, aux word) pairs) and one fp16 d per row and 256-value
 // super-block; the magnitudes and sign masks are expanded into LDS tables
-// once per workgroup, as in the generic kernel.
+// once per workgroup, as in the generic kernel.  Q2_K keeps a 16-row block's
+// codes of one super-block as two contiguous 512-byte halves (16 rows x 32
+// bytes, four 2-bit fields per byte), each holding two K tiles; the tile
+// reads its half (the odd tile of a pair fetches it again, from L2) and the
+// row's four scale|min bytes, d and dmin.
 template <int FMT, int ACT, int EPI>
 __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool BF = (ACT == ACT_BF16);
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
-  static_assert(FMT == QMOE_INT4 || (IQ2 && !BF), "ring formats: int4, IQ2_XXS with fp16 activations");
+  constexpr bool Q2K = (FMT == QMOE_Q2_K);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K) && !BF), "ring formats: int4, IQ2_XXS and Q2_K with fp16 activations");
   __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
@@ -1272,9 +1277,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     rbk[b] = ((int64_t)expert * g.N + block_base(b)) >> 4;
   }
 
-  // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS: in
-  // super-block kt >> 2
-  const int gsh = IQ2 ? 2 : __builtin_ctz((unsigned)g.group) - 6;
+  // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS and
+  // Q2_K: in super-block kt >> 2
+  const int gsh = (IQ2 || Q2K) ? 2 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1296,10 +1301,11 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // lanes 0-15 block 0, 16-31 block 1 (lanes 32-63 repeat them).  IQ2_XXS
   // runs (256 bytes): lanes 0-15 block 0, 16-31 block 1; d halves (32 bytes
   // per block and super-block): lanes 0-7 block 0, 8-15 block 1 (the other
-  // lanes repeat them into unused LDS).  The base (block 0's run) is
-  // wave-uniform and lives in SGPRs; each lane adds a 32-bit byte offset
-  // (block 1's run lies at most one expert's codes further)
-  constexpr int WRUN = IQ2 ? 256 : 512, SRUN = IQ2 ? 32 : 64;
+  // lanes repeat them into unused LDS).  Q2_K runs (512 bytes per block and
+  // pair of K tiles, so 256 per tile on average) as int4's.  The base (block
+  // 0's run) is wave-uniform and lives in SGPRs; each lane adds a 32-bit byte
+  // offset (block 1's run lies at most one expert's codes further)
+  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : 512, SRUN = IQ2 ? 32 : 64;
   const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
   const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
   const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * WRUN;
@@ -1308,14 +1314,39 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   const uint8_t* sbase = (const uint8_t*)(IQ2 ? g.d : g.scales) + rb0 * G * SRUN;
   const uint32_t soff = IQ2 ? (uint32_t)(((lane >> 3) & 1) * (rb1 - rb0) * G * SRUN + (lane & 7) * 4)
                             : (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * G * SRUN + lr * 4);
+  // Q2_K metadata of a tile, 256 bytes per wave from three arrays, so each
+  // lane keeps its own 64-bit address: lanes 0-15 (16-31) take row lr's four
+  // scale|min bytes of the tile's sub-blocks in block 0 (1), at 256 bytes per
+  // super-block and 4 per tile; lanes 32-47 (48-63) take block 0's (1's) d
+  // then dmin halves, two rows per lane, at 32 bytes per super-block.
+  const uint8_t* mptr = nullptr;
+  uint32_t mstride = 0, minc = 0;
+  if constexpr (Q2K) {
+    const int b = lane < 32 ? (lane >> 4) : ((lane - 32) >> 4);
+    const int64_t rb = b ? rb1 : rb0;
+    if (lane < 32) {
+      mptr = (const uint8_t*)g.scales + rb * G * 256 + lr * 16;
+      mstride = 256;
+      minc = 4;
+    } else {
+      const int i = lane & 15;
+      mptr = (const uint8_t*)(i < 8 ? g.d : g.dmin) + rb * G * 32 + (i & 7) * 4;
+      mstride = 32;
+    }
+  }
 
   // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
   auto issue = [&](int kt, int stage) {
     const uint32_t st = lds_addr(ring) + (uint32_t)(stage * R_STAGE);
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
-    dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
-    dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * 256);
+    if constexpr (Q2K) {
+      dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * 1024);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * 256);
+    } else {
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
+      dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * 256);
+    }
   };
 
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
@@ -1351,6 +1382,35 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
           rw.x1 = p[1];
           rw.x4 = Ds[b * 16 + lr];
           frag_f16<QMOE_IQ2_XXS>(rw, lg, lut_grid, lut_sign, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+          }
+        }
+        return;
+      }
+      if constexpr (Q2K) {
+        // lane group lg takes sub-block 4 (kt & 3) + lg: bytes 16 (lg & 1) ..
+        // +15 of the row's half, 2-bit field 2 (kt & 1) + (lg >> 1)
+        const uint8_t* Sc = (const uint8_t*)Ss;          // [block][row][4] scale|min bytes
+        const uint16_t* Dh = (const uint16_t*)Ss + 64;   // [block][d, dmin][16]
+        const uint32_t shift = 4u * (uint32_t)(kt & 1) + 2u * (uint32_t)(lg >> 1);
+        u4_t bf[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          Raw rw;
+          rw.v = *(const u4_t*)((const uint8_t*)Bs + b * 512 + lr * 32 + 16 * (lg & 1));
+          rw.x0 = Sc[b * 64 + lr * 4 + lg];
+          rw.x1 = shift;
+          rw.x2 = Dh[b * 32 + lr];
+          rw.x3 = Dh[b * 32 + 16 + lr];
+          frag_f16<QMOE_Q2_K>(rw, lg, nullptr, nullptr, bf[b][0], bf[b][1]);
         }
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
@@ -1665,6 +1725,12 @@ void qmm_iq2_ring_kernel(GemmArgs g) {
   ring_body<QMOE_IQ2_XXS, ACT_F16, EPI>(g);
 }
 
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_q2k_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_Q2_K, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -1674,8 +1740,9 @@ static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   return true;
 }
 
-// Whether the LDS-ring IQ2_XXS kernel takes this call (fp16 activations).
-static bool iq2_ring_ok(const GemmArgs& g, int act, int epi) {
+// Whether the LDS-ring IQ2_XXS or Q2_K kernel takes this call (fp16
+// activations; both keep K/4 code bytes per row).
+static bool k256_ring_ok(const GemmArgs& g, int act, int epi) {
   if (act != QMOE_F16) return false;
   if (g.N * g.K / 4 >= (1ll << 31)) return false;  // per-lane byte offsets within one expert's codes
   if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
@@ -1689,6 +1756,16 @@ static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+static void launch_q2k_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -1774,8 +1851,9 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.sk_tickets = nullptr;
   g.sk_part = nullptr;
   if (g.n_blocks == 0) return;
-  const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && iq2_ring_ok(g, act, epi);
-  if (iq2_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
+  const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && k256_ring_ok(g, act, epi);
+  const bool q2k_ring = w->fmt == QMOE_Q2_K && k256_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -1788,6 +1866,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
       g.n_blocks += 8 * (3 * g.sk_slots_xcd / 4);
     }
     if (iq2_ring) launch_iq2_ring(g, epi, s);
+    else if (q2k_ring) launch_q2k_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;
