@@ -175,6 +175,16 @@ __device__ __forceinline__ u4_t fp4x8_pairs(uint32_t q) {
   return fp4x8_pairs_scaled<ACT>(q, 1.0f);
 }
 
+// Four small unsigned integers (bytes holding 0..15) -> two packed fp16
+// pairs (bytes 0, 1 and 2, 3), exactly.  Read as E4M3 such a byte is c * 2^-9
+// (0..7 are the subnormals m * 2^-9, 8..15 the first normal binade
+// (8 + m) * 2^-9), so the hardware conversion scaled by 2^9 yields c: one
+// instruction per pair instead of a magic-number splice and a subtraction.
+template <bool HI>
+__device__ __forceinline__ uint32_t u8x2_small_f16(uint32_t t) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 512.0f, HI));
+}
+
 // ---------------------------------------------------------------- FP8 E4M3
 
 // Four E4M3 codes (byte i = element i) -> two packed pairs of fp16 (ACT_F16)

@@ -281,13 +281,12 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
     const _Float16 dl = (_Float16)(d * (float)(sc & 15u));
     const _Float16 ml = (_Float16)(-(dm * (float)(sc >> 4)));
     const h2_t dl2 = h2_t{dl, dl}, ml2 = h2_t{ml, ml};
-    const h2_t off = h2_t{(_Float16)1024.0f, (_Float16)1024.0f};
     const uint32_t shift = r.x1;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t t = (r.v[w] >> shift) & 0x03030303u;
-      const h2_t lo = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B01)) - off;
-      const h2_t hi = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B23)) - off;
+      const h2_t lo = __builtin_bit_cast(h2_t, u8x2_small_f16<false>(t));
+      const h2_t hi = __builtin_bit_cast(h2_t, u8x2_small_f16<true>(t));
       const uint32_t vl = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, dl2, ml2));
       const uint32_t vh = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(hi, dl2, ml2));
       if (w < 2) { o0[2 * w] = vl; o0[2 * w + 1] = vh; }
@@ -298,12 +297,11 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
     const _Float16 dl = (_Float16)(d * (float)(r.x0 & 255u));
     const _Float16 ml = (_Float16)(-(dm * (float)((r.x0 >> 8) & 255u)));
     const h2_t dl2 = h2_t{dl, dl}, ml2 = h2_t{ml, ml};
-    const h2_t off = h2_t{(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t t = (r.v[w] >> r.x1) & 0x0F0F0F0Fu;
-      const h2_t lo = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B01)) - off;
-      const h2_t hi = __builtin_bit_cast(h2_t, perm_b32(0x64646464u, t, SEL_B23)) - off;
+      const h2_t lo = __builtin_bit_cast(h2_t, u8x2_small_f16<false>(t));
+      const h2_t hi = __builtin_bit_cast(h2_t, u8x2_small_f16<true>(t));
       const uint32_t vl = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(lo, dl2, ml2));
       const uint32_t vh = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(hi, dl2, ml2));
       if (w < 2) { o0[2 * w] = vl; o0[2 * w + 1] = vh; }
@@ -326,15 +324,17 @@ __device__ __forceinline__ void frag_f16(const Raw& r, int lg, const uint32_t* l
     }
   } else {  // IQ2_XXS: octets j0, j0+1 of the group, j0 = 2 * (lg & 1)
     const uint32_t idx = r.x0, aux = r.x1;
-    const float db = f16_to_f32(r.x4) * (0.5f + (float)(aux >> 28)) * 0.25f;
-    const _Float16 dbh = (_Float16)db;
+    // d (0.5 + s) / 4: the second factor is exact in fp32, so the product
+    // rounds once, to fp16
+    const float bs = __builtin_fmaf((float)(aux >> 28), 0.25f, 0.125f);
+    const _Float16 dbh = (_Float16)(f16_to_f32(r.x4) * bs);
     const h2_t db2 = h2_t{dbh, dbh};
     const int j0 = 2 * (lg & 1);
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const int j = j0 + o;
-      const uint32_t gi = (idx >> (8 * j)) & 0xFFu;
-      const uint32_t si = (aux >> (7 * j)) & 0x7Fu;
+      const uint32_t gi = __builtin_amdgcn_ubfe(idx, 8 * j, 8);
+      const uint32_t si = __builtin_amdgcn_ubfe(aux, 7 * j, 7);
       const u4_t row = *(const u4_t*)(lut_grid + 4 * gi);
       const u4_t msk = *(const u4_t*)(lut_sign + 4 * si);
 #pragma unroll
