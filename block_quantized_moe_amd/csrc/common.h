@@ -16,6 +16,7 @@ typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t s2u_t __attribute__((ext_vector_type(2)));
 
 enum { ACT_F16 = 0, ACT_BF16 = 1 };
 

@@ -1182,7 +1182,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   __shared__ float wts[BM];
   __shared__ __attribute__((aligned(16))) float xg[BF ? XG4 * BM : 4];  // [group][row] activation sums
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t lut_sign[IQ2 ? 128 * 4 : 4];
+  __shared__ uint32_t lut_sbit[IQ2 ? 128 : 1];  // sign byte in both halves
   __shared__ int sk_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1239,12 +1239,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
         const uint32_t w = b[i >> 1] >> (16 * (i & 1));
         lut_grid[4 * tid + i] = (uint32_t)f32_to_f16((float)(w & 0xFFu)) | ((uint32_t)f32_to_f16((float)((w >> 8) & 0xFFu)) << 16);
       }
-    } else if (tid < 384) {  // sign mask tid - 256 as fp16 sign bits
-      const int si = tid - 256;
-      const uint32_t m = g.signs[si];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lut_sign[4 * si + i] = (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+    } else if (tid < 384) {
+      const uint32_t m = g.signs[tid - 256];
+      lut_sbit[tid - 256] = m | (m << 16);
     }
   }
   __syncthreads();
@@ -1371,17 +1368,34 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
       const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 1024);
       const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * 256);
       if constexpr (IQ2) {
-        // lane group lg takes group lg >> 1 of the tile (its octets 2(lg & 1), +1)
+        // lane group lg takes group lg >> 1 of the tile (its octets 2(lg & 1),
+        // +1).  The octet's eight sign bits come from a 128-word table (the
+        // sign byte in both halves); pair i's two bits are shifted to the
+        // halves' fp16 sign positions in registers and inserted into the
+        // (positive) magnitudes, which keeps the LDS reads per octet at one
+        // 16-byte grid row and one word.
         const uint16_t* Ds = (const uint16_t*)Ss;
         u4_t bf[RNB][2];
 #pragma unroll
         for (int b = 0; b < RNB; ++b) {
-          Raw rw;
           const u2_t p = *(const u2_t*)(Bs + b * 64 + (lg >> 1) * 32 + lr * 2);
-          rw.x0 = p[0];
-          rw.x1 = p[1];
-          rw.x4 = Ds[b * 16 + lr];
-          frag_f16<QMOE_IQ2_XXS>(rw, lg, lut_grid, lut_sign, bf[b][0], bf[b][1]);
+          const uint32_t idx = p[0], aux = p[1];
+          const float bs = __builtin_fmaf((float)(aux >> 28), 0.25f, 0.125f);
+          const _Float16 dbh = (_Float16)(f16_to_f32(Ds[b * 16 + lr]) * bs);
+          const h2_t db2 = h2_t{dbh, dbh};
+          const int j0 = 2 * (lg & 1);
+#pragma unroll
+          for (int o = 0; o < 2; ++o) {
+            const int j = j0 + o;
+            const u4_t row = *(const u4_t*)(lut_grid + 4 * __builtin_amdgcn_ubfe(idx, 8 * j, 8));
+            const s2u_t sb = __builtin_bit_cast(s2u_t, lut_sbit[__builtin_amdgcn_ubfe(aux, 7 * j, 7)]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t sm = __builtin_bit_cast(uint32_t, sb << s2u_t{(uint16_t)(15 - 2 * i), (uint16_t)(14 - 2 * i)});
+              const uint32_t w = (sm & 0x80008000u) | (row[i] & 0x7FFF7FFFu);
+              bf[b][o][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, w) * db2);
+            }
+          }
         }
 #pragma unroll
         for (int m = 0; m < MBV; ++m) {
