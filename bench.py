@@ -114,12 +114,13 @@ def algorithmic(inp, wbytes_gu=None, wbytes_dn=None):
     flops_gu = 2.0 * P * (2 * I) * H
     flops_dn = 2.0 * P * H * I
     ob = 2 if inp.out in ("f16", "bf16") else 4
+    base = T * H * 4 if inp.shared_gate_up is not None else 0  # the shared expert's fp32 rows, read by the combine
     return dict(P=P, flops=flops_gu + flops_dn, flops_gu=flops_gu, flops_dn=flops_dn,
                 # the method's bytes: weights, x, h written and read once, out
                 bytes=wgu + wdn + T * H * act + 2 * P * I * act + T * H * ob,
                 bytes_gu=wgu + T * H * act + P * I * act,                 # weights + x read + h write
                 bytes_dn=wdn + P * I * act + P * H * act,                 # weights + h read + y rows write
-                bytes_cb=P * H * act + T * inp.k * 8 + T * H * ob)        # y rows read + plan/w + out write
+                bytes_cb=P * H * act + T * inp.k * 8 + base + T * H * ob)  # y rows + plan/w (+ base) read, out write
 
 
 def run_prefill(args, torch, qm, inp, R, steps, warmup, bm=80):
