@@ -1175,7 +1175,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool BF = (ACT == ACT_BF16);
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
   constexpr bool Q2K = (FMT == QMOE_Q2_K);
-  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K) && !BF), "ring formats: int4, IQ2_XXS and Q2_K with fp16 activations");
+  constexpr bool MX = (FMT == QMOE_MXFP4);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX) && !BF),
+                "ring formats: int4, IQ2_XXS, Q2_K and MXFP4 with fp16 activations");
   __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
@@ -1275,8 +1277,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   }
 
   // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS and
-  // Q2_K: in super-block kt >> 2
-  const int gsh = (IQ2 || Q2K) ? 2 : __builtin_ctz((unsigned)g.group) - 6;
+  // Q2_K: in super-block kt >> 2; MXFP4: the tile holds two 32-value blocks
+  // (its own 32 exponent bytes per 16-row block)
+  const int gsh = (IQ2 || Q2K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1299,18 +1302,40 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // runs (256 bytes): lanes 0-15 block 0, 16-31 block 1; d halves (32 bytes
   // per block and super-block): lanes 0-7 block 0, 8-15 block 1 (the other
   // lanes repeat them into unused LDS).  Q2_K runs (512 bytes per block and
-  // pair of K tiles, so 256 per tile on average) as int4's.  The base (block
+  // pair of K tiles, so 256 per tile on average) and MXFP4 runs (512 bytes)
+  // as int4's; MXFP4 exponents (32 bytes per block and tile) as IQ2_XXS's d
+  // halves.  The base (block
   // 0's run) is wave-uniform and lives in SGPRs; each lane adds a 32-bit byte
   // offset (block 1's run lies at most one expert's codes further)
-  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : 512, SRUN = IQ2 ? 32 : 64;
+  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : 512, SRUN = (IQ2 || MX) ? 32 : 64;
   const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
   const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
   const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * WRUN;
   const uint32_t woff = IQ2 ? (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * T * WRUN + (lane & 15) * 16)
                             : (uint32_t)((lane >> 5) * (rb1 - rb0) * T * WRUN + (lane & 31) * 16);
   const uint8_t* sbase = (const uint8_t*)(IQ2 ? g.d : g.scales) + rb0 * G * SRUN;
-  const uint32_t soff = IQ2 ? (uint32_t)(((lane >> 3) & 1) * (rb1 - rb0) * G * SRUN + (lane & 7) * 4)
+  const uint32_t soff = (IQ2 || MX) ? (uint32_t)(((lane >> 3) & 1) * (rb1 - rb0) * G * SRUN + (lane & 7) * 4)
                             : (uint32_t)(((lane >> 4) & 1) * (rb1 - rb0) * G * SRUN + lr * 4);
+  // MXFP4: whether every exponent of the workgroup's weight rows (all of K)
+  // lets the scale go into the B operand exactly (2^-13 .. 2^13)
+  bool fold = true;
+  if constexpr (MX) {
+    const int64_t KB = K / 32;  // 16-byte exponent vectors per 16-row block
+    bool ok = true;
+#pragma unroll
+    for (int b = 0; b < RNB; ++b) {
+      const u4_t* run_e = (const u4_t*)((const uint8_t*)g.scales + (b ? rb1 : rb0) * KB * 16);
+      for (int64_t i = lane; i < KB; i += 64) {
+        const u4_t v = run_e[i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ok = ok && ((v[q] >> (8 * j)) & 0xFFu) - 114u <= 26u;
+      }
+    }
+    fold = __syncthreads_and(ok);
+  }
+
   // Q2_K metadata of a tile, 256 bytes per wave from three arrays, so each
   // lane keeps its own 64-bit address: lanes 0-15 (16-31) take row lr's four
   // scale|min bytes of the tile's sub-blocks in block 0 (1), at 256 bytes per
@@ -1349,7 +1374,8 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // The K loop and epilogue for a tile of exactly MBV 16-row blocks (a
   // compile-time count keeps the m loops straight-line, so MFMA results are
   // consumed late enough to need no pipeline stalls).
-  auto run = [&](auto mbv_c, auto part_c) {
+  auto run = [&](auto mbv_c, auto part_c, auto fold_c) {
+    constexpr bool FOLD = decltype(fold_c)::value;  // MXFP4: the scales go into the B operand
     constexpr int MBV = decltype(mbv_c)::value;
     constexpr bool PART = decltype(part_c)::value;  // a K part of a split unit (whole units keep the plain loop)
     const int kb = PART ? wk.kb : 0, ke = PART ? wk.ke : KT;
@@ -1361,7 +1387,10 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
 
     // chunk slots of this lane's activation reads in MFMA sub-tile 0 (sub-tile
     // m adds 128 m: the swizzle depends on the row mod 16 only)
-    const int slot_a0 = ring_slot(lr, 2 * lg), slot_a1 = ring_slot(lr, 2 * lg + 1);
+    // (MXFP4 takes the plain k order: MFMA step s covers values 32s .. 32s+31,
+    // lane group lg its chunk 4s + lg)
+    const int slot_a0 = MX ? ring_slot(lr, lg) : ring_slot(lr, 2 * lg);
+    const int slot_a1 = MX ? ring_slot(lr, 4 + lg) : ring_slot(lr, 2 * lg + 1);
     auto compute = [&](int kt, int stage) {
       const uint8_t* st = ring + stage * R_STAGE;
       const uint16_t* As = (const uint16_t*)st;
@@ -1405,6 +1434,64 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
           for (int b = 0; b < RNB; ++b) {
             acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
             acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+          }
+        }
+        return;
+      }
+      if constexpr (MX) {
+        // word lg of each 32-value block of row lr: eight E2M1 codes.  When
+        // every exponent of the workgroup's weight rows lies in 2^-13 ..
+        // 2^13 (FOLD) each code times its scale is an exact fp16 normal
+        // number, so the scale goes into the hardware conversion and the
+        // MFMAs accumulate directly; otherwise the exact codes enter the
+        // MFMAs and the scale multiplies the fp32 partial sums.
+        const uint8_t* Es = (const uint8_t*)Ss;  // [block][32-value block j][row] exponents
+        uint32_t wd[RNB][2], ex[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            wd[b][j] = Bs[b * 128 + j * 64 + lr * 4 + lg];
+            ex[b][j] = Es[b * 32 + j * 16 + lr];
+          }
+        if constexpr (FOLD) {
+          u4_t bf[RNB][2];
+#pragma unroll
+          for (int b = 0; b < RNB; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[b][j] = fp4x8_pairs_scaled<ACT_F16>(wd[b][j], e8m0_to_f32(ex[b][j]));
+#pragma unroll
+          for (int m = 0; m < MBV; ++m) {
+            const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+            const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+            for (int b = 0; b < RNB; ++b) {
+              acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+              acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
+            }
+          }
+        } else {
+          u4_t cc[RNB][2];
+          float dd[RNB][2];
+#pragma unroll
+          for (int b = 0; b < RNB; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              cc[b][j] = fp4x8_pairs<ACT_F16>(wd[b][j]);
+              dd[b][j] = e8m0_to_f32(ex[b][j]);
+            }
+#pragma unroll
+          for (int m = 0; m < MBV; ++m) {
+            const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+            const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+            for (int b = 0; b < RNB; ++b) {
+              const f4_t t0 = mfma(a0, __builtin_bit_cast(h8_t, cc[b][0]), f4_t{0, 0, 0, 0});
+              const f4_t t1 = mfma(a1, __builtin_bit_cast(h8_t, cc[b][1]), f4_t{0, 0, 0, 0});
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                acc[m][b][rr] = __builtin_fmaf(dd[b][1], t1[rr], __builtin_fmaf(dd[b][0], t0[rr], acc[m][b][rr]));
+            }
           }
         }
         return;
@@ -1714,13 +1801,21 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
       }
     }
   };
-  auto dispatch = [&](auto part_c) {
+  auto dispatch2 = [&](auto part_c, auto fold_c) {
     switch (mbn) {
-      case 1: run(std::integral_constant<int, 1>{}, part_c); break;
-      case 2: run(std::integral_constant<int, 2>{}, part_c); break;
-      case 3: run(std::integral_constant<int, 3>{}, part_c); break;
-      case 4: run(std::integral_constant<int, 4>{}, part_c); break;
-      default: run(std::integral_constant<int, 5>{}, part_c); break;
+      case 1: run(std::integral_constant<int, 1>{}, part_c, fold_c); break;
+      case 2: run(std::integral_constant<int, 2>{}, part_c, fold_c); break;
+      case 3: run(std::integral_constant<int, 3>{}, part_c, fold_c); break;
+      case 4: run(std::integral_constant<int, 4>{}, part_c, fold_c); break;
+      default: run(std::integral_constant<int, 5>{}, part_c, fold_c); break;
+    }
+  };
+  auto dispatch = [&](auto part_c) {
+    if constexpr (MX) {
+      if (fold) dispatch2(part_c, std::true_type{});
+      else dispatch2(part_c, std::false_type{});
+    } else {
+      dispatch2(part_c, std::true_type{});
     }
   };
   if (wk.part >= 0) dispatch(std::true_type{});
@@ -1743,6 +1838,12 @@ template <int EPI>
 __global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void qmm_q2k_ring_kernel(GemmArgs g) {
   ring_body<QMOE_Q2_K, ACT_F16, EPI>(g);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_mxfp4_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_MXFP4, ACT_F16, EPI>(g);
 }
 
 // Whether the LDS-ring int4 kernel takes this call.
@@ -1770,6 +1871,25 @@ static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+// Whether the LDS-ring MXFP4 kernel takes this call (fp16 activations; K/2
+// code bytes per row, as int4).
+static bool mx_ring_ok(const GemmArgs& g, int act, int epi) {
+  if (act != QMOE_F16) return false;
+  if (g.N * g.K / 2 >= (1ll << 31)) return false;
+  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
+  return true;
+}
+
+static void launch_mx_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -1867,7 +1987,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   if (g.n_blocks == 0) return;
   const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && k256_ring_ok(g, act, epi);
   const bool q2k_ring = w->fmt == QMOE_Q2_K && k256_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
+  const bool mx_ring = w->fmt == QMOE_MXFP4 && mx_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || mx_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -1881,6 +2002,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     }
     if (iq2_ring) launch_iq2_ring(g, epi, s);
     else if (q2k_ring) launch_q2k_ring(g, epi, s);
+    else if (mx_ring) launch_mx_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;
