@@ -1088,8 +1088,8 @@ constexpr int RS = 3;                      // ring stages
 constexpr int R_ACH = BM * 8;              // activation chunks per stage (640)
 constexpr int R_A = R_ACH * 16;            // 10240 B
 constexpr int R_B = RW * RNB * 512;        // 8192 B
-constexpr int R_SB = RW * 256;             // 2048 B (one 64-lane dword load per wave)
-constexpr int R_STAGE = R_A + R_B + R_SB;  // 20480 B
+// then the scale / metadata region: 256 bytes per wave (Q4_K: 512), so a
+// stage is 20480 bytes (22528)
 constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
 
 // Chunk swizzle of the activation rows in a ring stage (rows 128 bytes
@@ -1176,9 +1176,14 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool IQ2 = (FMT == QMOE_IQ2_XXS);
   constexpr bool Q2K = (FMT == QMOE_Q2_K);
   constexpr bool MX = (FMT == QMOE_MXFP4);
-  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX) && !BF),
-                "ring formats: int4, IQ2_XXS, Q2_K and MXFP4 with fp16 activations");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[RS * R_STAGE];
+  constexpr bool Q4K = (FMT == QMOE_Q4_K);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K) && !BF),
+                "ring formats: int4, IQ2_XXS, Q2_K, MXFP4 and Q4_K with fp16 activations");
+  // metadata per wave and stage: one 64-lane dword load (Q4_K: two)
+  constexpr int NMETA = Q4K ? 2 : 1;
+  constexpr int SBW = 256 * NMETA;
+  constexpr int STAGE = R_A + R_B + RW * SBW;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RS * STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
   __shared__ float wts[BM];
@@ -1279,7 +1284,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS and
   // Q2_K: in super-block kt >> 2; MXFP4: the tile holds two 32-value blocks
   // (its own 32 exponent bytes per 16-row block)
-  const int gsh = (IQ2 || Q2K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
+  const int gsh = (IQ2 || Q2K || Q4K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1341,8 +1346,21 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // scale|min bytes of the tile's sub-blocks in block 0 (1), at 256 bytes per
   // super-block and 4 per tile; lanes 32-47 (48-63) take block 0's (1's) d
   // then dmin halves, two rows per lane, at 32 bytes per super-block.
+  // Q4_K: load 1, lanes 0-15 (16-31) take row lr's scale word and
+  // 32-47 (48-63) its min word holding the tile's two sub-blocks (word
+  // (kt >> 1) & 1 of the row's 8 scales, resp. mins), block 0 then block 1;
+  // load 2, lanes 0-7 (8-15) block 0's d (dmin) halves, 16-31 block 1's (the
+  // upper lanes repeat them into unused LDS).
   const uint8_t* mptr = nullptr;
+  const uint8_t* mptr2 = nullptr;
   uint32_t mstride = 0, minc = 0;
+  if constexpr (Q4K) {
+    const int64_t rb = (lane >> 5) ? rb1 : rb0;
+    mptr = (const uint8_t*)g.scales + rb * G * 256 + lr * 16 + ((lane >> 4) & 1) * 8;
+    const int i = lane & 31;
+    const int64_t rb2 = (i >> 4) ? rb1 : rb0;
+    mptr2 = (const uint8_t*)(((i >> 3) & 1) ? g.dmin : g.d) + rb2 * G * 32 + (i & 7) * 4;
+  }
   if constexpr (Q2K) {
     const int b = lane < 32 ? (lane >> 4) : ((lane - 32) >> 4);
     const int64_t rb = b ? rb1 : rb0;
@@ -1359,15 +1377,19 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
 
   // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
   auto issue = [&](int kt, int stage) {
-    const uint32_t st = lds_addr(ring) + (uint32_t)(stage * R_STAGE);
+    const uint32_t st = lds_addr(ring) + (uint32_t)(stage * STAGE);
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
     if constexpr (Q2K) {
       dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * 1024);
-      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * 256);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * SBW);
+    } else if constexpr (Q4K) {
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * 256 + (uint32_t)((kt >> 1) & 1) * 4, st + R_A + R_B + wave * SBW);
+      dma_glb4(mptr2 + (uint32_t)(kt >> 2) * 32, st + R_A + R_B + wave * SBW + 256);
     } else {
       dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
-      dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * 256);
+      dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * SBW);
     }
   };
 
@@ -1392,10 +1414,10 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     const int slot_a0 = MX ? ring_slot(lr, lg) : ring_slot(lr, 2 * lg);
     const int slot_a1 = MX ? ring_slot(lr, 4 + lg) : ring_slot(lr, 2 * lg + 1);
     auto compute = [&](int kt, int stage) {
-      const uint8_t* st = ring + stage * R_STAGE;
+      const uint8_t* st = ring + stage * STAGE;
       const uint16_t* As = (const uint16_t*)st;
       const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 1024);
-      const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * 256);
+      const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * SBW);
       if constexpr (IQ2) {
         // lane group lg takes group lg >> 1 of the tile (its octets 2(lg & 1),
         // +1).  The octet's eight sign bits come from a 128-word table (the
@@ -1492,6 +1514,36 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
               for (int rr = 0; rr < 4; ++rr)
                 acc[m][b][rr] = __builtin_fmaf(dd[b][1], t1[rr], __builtin_fmaf(dd[b][0], t0[rr], acc[m][b][rr]));
             }
+          }
+        }
+        return;
+      }
+      if constexpr (Q4K) {
+        // the tile is quarter kt & 3 of the super-block: lane group lg takes
+        // bytes 16 (lg & 1) .. +15 of the row's 32, low nibbles (sub-block
+        // 2 (kt & 3)) for lg < 2, high nibbles (the next sub-block) above
+        const uint8_t* M8 = (const uint8_t*)Ss;             // [block][scale words, min words][row][4]
+        const uint16_t* Dh = (const uint16_t*)Ss + 128;     // [block][d, dmin][16]
+        u4_t bf[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          Raw rw;
+          rw.v = *(const u4_t*)((const uint8_t*)Bs + b * 512 + lr * 32 + 16 * (lg & 1));
+          const int sj = b * 128 + lr * 4 + 2 * (kt & 1) + (lg >> 1);
+          rw.x0 = (uint32_t)M8[sj] | ((uint32_t)M8[sj + 64] << 8);
+          rw.x1 = 4u * (uint32_t)(lg >> 1);
+          rw.x2 = Dh[b * 32 + lr];
+          rw.x3 = Dh[b * 32 + 16 + lr];
+          frag_f16<QMOE_Q4_K>(rw, lg, nullptr, nullptr, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
           }
         }
         return;
@@ -1600,8 +1652,8 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     // last two tiles are peeled off so the steady-state loop has no tests;
     // `sc` is the ring stage of tile kt.
     auto wait_next = [&]() {  // only the next tile's loads may be outstanding
-      if (n_aload == 2) wait_vmcnt<4>();
-      else wait_vmcnt<3>();
+      if (n_aload == 2) wait_vmcnt<3 + NMETA>();
+      else wait_vmcnt<2 + NMETA>();
     };
     if constexpr (BF && PART) {  // a K part sums only its own groups: the others stay zero
       for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
@@ -1741,7 +1793,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
         constexpr int W = swiglu ? BN / 2 : BN;  // output columns per workgroup
         constexpr int CPR = W / 8;               // 16-byte pieces per row
         constexpr int LROW = 2 * W + 16;         // LDS row stride in bytes
-        static_assert(BM * LROW <= RS * R_STAGE, "output tile fits in the ring");
+        static_assert(BM * LROW <= RS * STAGE, "output tile fits in the ring");
         const bool half = (g.out_dtype == QMOE_F16);
         ring_barrier();  // every wave is done with the ring
 #pragma unroll
@@ -1846,6 +1898,12 @@ void qmm_mxfp4_ring_kernel(GemmArgs g) {
   ring_body<QMOE_MXFP4, ACT_F16, EPI>(g);
 }
 
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_q4k_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_Q4_K, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -1874,8 +1932,8 @@ static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
   }
 }
 
-// Whether the LDS-ring MXFP4 kernel takes this call (fp16 activations; K/2
-// code bytes per row, as int4).
+// Whether the LDS-ring MXFP4 or Q4_K kernel takes this call (fp16
+// activations; K/2 code bytes per row, as int4).
 static bool mx_ring_ok(const GemmArgs& g, int act, int epi) {
   if (act != QMOE_F16) return false;
   if (g.N * g.K / 2 >= (1ll << 31)) return false;
@@ -1890,6 +1948,16 @@ static void launch_mx_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+static void launch_q4k_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -1988,7 +2056,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && k256_ring_ok(g, act, epi);
   const bool q2k_ring = w->fmt == QMOE_Q2_K && k256_ring_ok(g, act, epi);
   const bool mx_ring = w->fmt == QMOE_MXFP4 && mx_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || mx_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
+  const bool q4k_ring = w->fmt == QMOE_Q4_K && mx_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -2003,6 +2072,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     if (iq2_ring) launch_iq2_ring(g, epi, s);
     else if (q2k_ring) launch_q2k_ring(g, epi, s);
     else if (mx_ring) launch_mx_ring(g, epi, s);
+    else if (q4k_ring) launch_q4k_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;

@@ -1,5 +1,5 @@
 """GPU checks of the split units of the LDS-ring gathered matmul (int4, and
-IQ2_XXS, Q2_K and MXFP4 with fp16 activations).
+IQ2_XXS, Q2_K, MXFP4 and Q4_K with fp16 activations).
 
 With a routing plan of at least 2048 pairs (which carries a work-balancing
 area), the ring kernel looks at each XCD's units (tiles x, x + 8,
@@ -21,8 +21,9 @@ units are split:
   * the IQ2_XXS ring kernel (fp16 activations, SwiGLU, K = 1280: parts start
     inside a 256-value super-block) and the Q2_K one (STORE into fp32, parts
     starting on the odd tile of a pair that shares a 512-byte code half) and
-    the MXFP4 one (SwiGLU, scales folded into the fp16 operands) against the
-    fp64 oracle;
+    the MXFP4 one (SwiGLU, scales folded into the fp16 operands) and the
+    Q4_K one (SwiGLU, parts starting inside a super-block) against the fp64
+    oracle;
   * two calls give bit-identical outputs (the parts are summed in a fixed
     order whichever finishes last);
   * the plan's tickets are zero after every call.
@@ -205,6 +206,26 @@ def test_split_units_mxfp4_swiglu_f16():
     x = synth.activations(rng, T, K, "f16")
     ids, w = synth.routing_softmax(rng, T, E, k)
     W = synth.mxfp4(rng, E, N, K)
+    plan, v = _plan(ids, T, k, E, n_nt=N // 2 // 128, KT=K // 64)
+    gu = upload(W)
+    xd = torch_act(x, "f16")
+    h1 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    h2 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    torch.cuda.synchronize()
+    _tickets_zero(plan, T, k, E)
+    assert torch.equal(h1, h2)
+    srt = v["sorted"].cpu().numpy()
+    href = oracle.moe_gate_up(oracle.act_to_f64(x, "f16"), ids, W)[srt]
+    err = normwise_err(to_f64(h1), href, "f16")
+    assert err <= TOL, (err, report(to_f64(h1), href))
+
+
+def test_split_units_q4_k_swiglu_f16():
+    N, K, T, E, k = 4096, 1280, 512, 64, 8
+    rng = np.random.default_rng(16)
+    x = synth.activations(rng, T, K, "f16")
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    W = synth.q4_k(rng, E, N, K)
     plan, v = _plan(ids, T, k, E, n_nt=N // 2 // 128, KT=K // 64)
     gu = upload(W)
     xd = torch_act(x, "f16")
