@@ -1177,8 +1177,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool Q2K = (FMT == QMOE_Q2_K);
   constexpr bool MX = (FMT == QMOE_MXFP4);
   constexpr bool Q4K = (FMT == QMOE_Q4_K);
-  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K) && !BF),
-                "ring formats: int4, IQ2_XXS, Q2_K, MXFP4 and Q4_K with fp16 activations");
+  constexpr bool Q6K = (FMT == QMOE_Q6_K);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K || Q6K) && !BF),
+                "ring formats: int4, IQ2_XXS, Q2_K, MXFP4, Q4_K and Q6_K with fp16 activations");
   // metadata per wave and stage: one 64-lane dword load (Q4_K: two)
   constexpr int NMETA = Q4K ? 2 : 1;
   constexpr int SBW = 256 * NMETA;
@@ -1190,6 +1191,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16))) float xg[BF ? XG4 * BM : 4];  // [group][row] activation sums
   __shared__ __attribute__((aligned(16))) uint32_t lut_grid[IQ2 ? 256 * 4 : 4];
   __shared__ uint32_t lut_sbit[IQ2 ? 128 : 1];  // sign byte in both halves
+  // Q6_K: the top-bit halves of two tile pairs (slot p & 1 holds pair p's
+  // 512 bytes per 16-row block, per wave), outside the ring stages
+  __shared__ __attribute__((aligned(16))) uint8_t qh_ring[Q6K ? 2 * RW * 1024 : 16];
   __shared__ int sk_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1284,7 +1288,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS and
   // Q2_K: in super-block kt >> 2; MXFP4: the tile holds two 32-value blocks
   // (its own 32 exponent bytes per 16-row block)
-  const int gsh = (IQ2 || Q2K || Q4K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
+  const int gsh = (IQ2 || Q2K || Q4K || Q6K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1361,6 +1365,25 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     const int64_t rb2 = (i >> 4) ? rb1 : rb0;
     mptr2 = (const uint8_t*)(((i >> 3) & 1) ? g.dmin : g.d) + rb2 * G * 32 + (i & 7) * 4;
   }
+  // Q6_K: lanes 0-31 as Q2_K's (the tile's four int8 sub-block scales of a
+  // row), lanes 32-39 (40-47) block 0's (1's) d halves, 48-63 repeat them.
+  // Its top-bit halves (512 bytes per block and tile pair) go by a 16-byte
+  // load per lane into qh_ring for the first tile of a pair (and the first
+  // tile of a K part): lanes 0-31 block 0, 32-63 block 1.
+  const uint8_t* qbase = nullptr;
+  uint32_t qoff = 0;
+  if constexpr (Q6K) {
+    if (lane < 32) {
+      mptr = (const uint8_t*)g.scales + ((lane >> 4) ? rb1 : rb0) * G * 256 + lr * 16;
+      mstride = 256;
+      minc = 4;
+    } else {
+      mptr = (const uint8_t*)g.d + (((lane & 15) >> 3) ? rb1 : rb0) * G * 32 + (lane & 7) * 4;
+      mstride = 32;
+    }
+    qbase = (const uint8_t*)g.aux + rb0 * T * 256;
+    qoff = (uint32_t)((lane >> 5) * (rb1 - rb0) * T * 256 + (lane & 31) * 16);
+  }
   if constexpr (Q2K) {
     const int b = lane < 32 ? (lane >> 4) : ((lane - 32) >> 4);
     const int64_t rb = b ? rb1 : rb0;
@@ -1375,14 +1398,21 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     }
   }
 
-  // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller)
-  auto issue = [&](int kt, int stage) {
+  // issue tile kt into ring stage `stage` (kt % RS, tracked by the caller);
+  // `first`: the first tile of the K range
+  auto issue = [&](int kt, int stage, bool first) {
     const uint32_t st = lds_addr(ring) + (uint32_t)(stage * STAGE);
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
     if constexpr (Q2K) {
       dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * 1024);
       dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * SBW);
+    } else if constexpr (Q6K) {
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * SBW);
+      if (!(kt & 1) || first)
+        dma_glb16_s(qbase + (int64_t)(kt >> 1) * 512, qoff,
+                    lds_addr(qh_ring) + (uint32_t)(((kt >> 1) & 1) * RW * 1024 + wave * 1024));
     } else if constexpr (Q4K) {
       dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
       dma_glb4(mptr + (uint32_t)(kt >> 2) * 256 + (uint32_t)((kt >> 1) & 1) * 4, st + R_A + R_B + wave * SBW);
@@ -1514,6 +1544,36 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
               for (int rr = 0; rr < 4; ++rr)
                 acc[m][b][rr] = __builtin_fmaf(dd[b][1], t1[rr], __builtin_fmaf(dd[b][0], t0[rr], acc[m][b][rr]));
             }
+          }
+        }
+        return;
+      }
+      if constexpr (Q6K) {
+        // lane group lg takes sub-block 4 (kt & 3) + lg: low bits as Q4_K's
+        // (bytes 16 (lg & 1) .. +15, nibble lg >> 1), top bits from the same
+        // bytes of the pair's half, bit pair 2 (kt & 1) + (lg >> 1)
+        const uint8_t* Sc8 = (const uint8_t*)Ss;         // [block][row][4] int8 scales
+        const uint16_t* Dh = (const uint16_t*)Ss + 64;   // [block][16] d
+        const uint8_t* QH = qh_ring + ((kt >> 1) & 1) * (RW * 1024) + wave * 1024;
+        u4_t bf[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          Raw rw;
+          rw.v = *(const u4_t*)((const uint8_t*)Bs + b * 512 + lr * 32 + 16 * (lg & 1));
+          rw.v2 = *(const u4_t*)(QH + b * 512 + lr * 32 + 16 * (lg & 1));
+          rw.x0 = Sc8[b * 64 + lr * 4 + lg];
+          rw.x1 = 4u * (uint32_t)(lg >> 1) | ((2u * (2u * (uint32_t)(kt & 1) + (uint32_t)(lg >> 1))) << 8);
+          rw.x2 = Dh[b * 16 + lr];
+          frag_f16<QMOE_Q6_K>(rw, lg, nullptr, nullptr, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
           }
         }
         return;
@@ -1651,7 +1711,14 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     // ---- the K loop: tiles kt+1 and kt+2 stream while kt is computed.  The
     // last two tiles are peeled off so the steady-state loop has no tests;
     // `sc` is the ring stage of tile kt.
-    auto wait_next = [&]() {  // only the next tile's loads may be outstanding
+    auto wait_next = [&](int kt) {  // only tile kt + 1's loads may be outstanding
+      if constexpr (Q6K) {
+        if (kt & 1) {  // tile kt + 1 starts a pair: one more load (its top bits)
+          if (n_aload == 2) wait_vmcnt<4 + NMETA>();
+          else wait_vmcnt<3 + NMETA>();
+          return;
+        }
+      }
       if (n_aload == 2) wait_vmcnt<3 + NMETA>();
       else wait_vmcnt<2 + NMETA>();
     };
@@ -1659,18 +1726,18 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
       for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
     }
     const int nk = ke - kb;
-    if (nk > 0) issue(kb, 0);
-    if (nk > 1) issue(kb + 1, 1);
+    if (nk > 0) issue(kb, 0, true);
+    if (nk > 1) issue(kb + 1, 1, false);
     int sc = 0;
     for (int kt = kb; kt + 2 < ke; ++kt) {
-      wait_next();
+      wait_next(kt);
       ring_barrier();
-      issue(kt + 2, sc == 0 ? 2 : sc - 1);
+      issue(kt + 2, sc == 0 ? 2 : sc - 1, false);
       compute(kt, sc);
       sc = sc == 2 ? 0 : sc + 1;
     }
     if (nk > 1) {
-      wait_next();
+      wait_next(ke - 2);
       ring_barrier();
       compute(ke - 2, sc);
       sc = sc == 2 ? 0 : sc + 1;
@@ -1904,6 +1971,12 @@ void qmm_q4k_ring_kernel(GemmArgs g) {
   ring_body<QMOE_Q4_K, ACT_F16, EPI>(g);
 }
 
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_q6k_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_Q6_K, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -1932,8 +2005,8 @@ static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
   }
 }
 
-// Whether the LDS-ring MXFP4 or Q4_K kernel takes this call (fp16
-// activations; K/2 code bytes per row, as int4).
+// Whether the LDS-ring MXFP4, Q4_K or Q6_K kernel takes this call (fp16
+// activations; K/2 code bytes per row in qs, as int4).
 static bool mx_ring_ok(const GemmArgs& g, int act, int epi) {
   if (act != QMOE_F16) return false;
   if (g.N * g.K / 2 >= (1ll << 31)) return false;
@@ -1958,6 +2031,16 @@ static void launch_q4k_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+static void launch_q6k_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -2057,7 +2140,9 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   const bool q2k_ring = w->fmt == QMOE_Q2_K && k256_ring_ok(g, act, epi);
   const bool mx_ring = w->fmt == QMOE_MXFP4 && mx_ring_ok(g, act, epi);
   const bool q4k_ring = w->fmt == QMOE_Q4_K && mx_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
+  const bool q6k_ring = w->fmt == QMOE_Q6_K && mx_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring ||
+      (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -2073,6 +2158,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     else if (q2k_ring) launch_q2k_ring(g, epi, s);
     else if (mx_ring) launch_mx_ring(g, epi, s);
     else if (q4k_ring) launch_q4k_ring(g, epi, s);
+    else if (q6k_ring) launch_q6k_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;

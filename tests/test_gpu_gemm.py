@@ -371,7 +371,7 @@ def test_dense_mxfp4_f16_scale_ranges(planted):
     assert err <= TOL, (err, report(got, ref))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "q8_0", "mxfp4", "fp8", "q2_k", "iq2_xxs", "q4_k"])
+@pytest.mark.parametrize("fmt", ["int4", "q8_0", "mxfp4", "fp8", "q2_k", "iq2_xxs", "q4_k", "q6_k"])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("epi", ["store", "swiglu"])
 def test_two_byte_outputs_whole_rows(fmt, act, epi):
