@@ -1178,12 +1178,18 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool MX = (FMT == QMOE_MXFP4);
   constexpr bool Q4K = (FMT == QMOE_Q4_K);
   constexpr bool Q6K = (FMT == QMOE_Q6_K);
-  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K || Q6K) && !BF),
-                "ring formats: int4, IQ2_XXS, Q2_K, MXFP4, Q4_K and Q6_K with fp16 activations");
-  // metadata per wave and stage: one 64-lane dword load (Q4_K: two)
+  constexpr bool F8 = (FMT == QMOE_FP8);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K || Q6K || F8) && !BF),
+                "ring formats: int4, and IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K, FP8 with fp16 activations");
+  // weight codes per wave and stage (FP8: two 1 KB blocks), then metadata: one
+  // 64-lane dword load (Q4_K: two; FP8: none, its block scales are
+  // wave-uniform and come by scalar loads).  NMETA + 1 loads per wave and
+  // tile besides the activation chunks.
+  constexpr int BW = F8 ? 2048 : 1024;
+  constexpr int RBB = RW * BW;
   constexpr int NMETA = Q4K ? 2 : 1;
-  constexpr int SBW = 256 * NMETA;
-  constexpr int STAGE = R_A + R_B + RW * SBW;
+  constexpr int SBW = F8 ? 0 : 256 * NMETA;
+  constexpr int STAGE = R_A + RBB + RW * SBW;
   __shared__ __attribute__((aligned(16))) uint8_t ring[RS * STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
@@ -1316,7 +1322,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // halves.  The base (block
   // 0's run) is wave-uniform and lives in SGPRs; each lane adds a 32-bit byte
   // offset (block 1's run lies at most one expert's codes further)
-  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : 512, SRUN = (IQ2 || MX) ? 32 : 64;
+  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : F8 ? 1024 : 512, SRUN = (IQ2 || MX) ? 32 : 64;
   const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
   const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
   const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * WRUN;
@@ -1365,6 +1371,19 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     const int64_t rb2 = (i >> 4) ? rb1 : rb0;
     mptr2 = (const uint8_t*)(((i >> 3) & 1) ? g.dmin : g.d) + rb2 * G * 32 + (i & 7) * 4;
   }
+  // FP8: a 16-row block's codes of a tile are 1 KB (the Q8_0 tiling), one
+  // 16-byte load per lane and block; the block's scale (its 128 x 128 scale
+  // block's) by a scalar load per tile
+  uint32_t woff2 = 0;
+  const __attribute__((address_space(4))) float* fsc[RNB] = {nullptr, nullptr};
+  if constexpr (F8) {
+    woff2 = (uint32_t)((rb1 - rb0) * T * 1024 + lane * 16);
+#pragma unroll
+    for (int b = 0; b < RNB; ++b) {
+      const int64_t si = (((int64_t)expert * g.N + block_base(b)) >> 7) * (K >> 7);
+      fsc[b] = (const __attribute__((address_space(4))) float*)(uintptr_t)sgpr_ptr((const float*)g.scales + si);
+    }
+  }
   // Q6_K: lanes 0-31 as Q2_K's (the tile's four int8 sub-block scales of a
   // row), lanes 32-39 (40-47) block 0's (1's) d halves, 48-63 repeat them.
   // Its top-bit halves (512 bytes per block and tile pair) go by a 16-byte
@@ -1405,21 +1424,24 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     dma_buf16(arsrc, st + 64 * 16 * wave, aoff[0] + (uint32_t)kt * 128);
     if (n_aload == 2) dma_buf16(arsrc, st + 64 * 16 * (wave + RW), aoff[1] + (uint32_t)kt * 128);
     if constexpr (Q2K) {
-      dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * 1024);
-      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * SBW);
+      dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * BW);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + RBB + wave * SBW);
+    } else if constexpr (F8) {
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, (uint32_t)lane * 16, st + R_A + wave * BW);
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff2, st + R_A + wave * BW + 1024);
     } else if constexpr (Q6K) {
-      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
-      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + R_B + wave * SBW);
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * BW);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + RBB + wave * SBW);
       if (!(kt & 1) || first)
         dma_glb16_s(qbase + (int64_t)(kt >> 1) * 512, qoff,
                     lds_addr(qh_ring) + (uint32_t)(((kt >> 1) & 1) * RW * 1024 + wave * 1024));
     } else if constexpr (Q4K) {
-      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
-      dma_glb4(mptr + (uint32_t)(kt >> 2) * 256 + (uint32_t)((kt >> 1) & 1) * 4, st + R_A + R_B + wave * SBW);
-      dma_glb4(mptr2 + (uint32_t)(kt >> 2) * 32, st + R_A + R_B + wave * SBW + 256);
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * BW);
+      dma_glb4(mptr + (uint32_t)(kt >> 2) * 256 + (uint32_t)((kt >> 1) & 1) * 4, st + R_A + RBB + wave * SBW);
+      dma_glb4(mptr2 + (uint32_t)(kt >> 2) * 32, st + R_A + RBB + wave * SBW + 256);
     } else {
-      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * 1024);
-      dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + R_B + wave * SBW);
+      dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * BW);
+      dma_glb4_s(sbase + (int64_t)(kt >> gsh) * SRUN, soff, st + R_A + RBB + wave * SBW);
     }
   };
 
@@ -1446,8 +1468,8 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     auto compute = [&](int kt, int stage) {
       const uint8_t* st = ring + stage * STAGE;
       const uint16_t* As = (const uint16_t*)st;
-      const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * 1024);
-      const uint32_t* Ss = (const uint32_t*)(st + R_A + R_B + wave * SBW);
+      const uint32_t* Bs = (const uint32_t*)(st + R_A + wave * BW);
+      const uint32_t* Ss = (const uint32_t*)(st + R_A + RBB + wave * SBW);
       if constexpr (IQ2) {
         // lane group lg takes group lg >> 1 of the tile (its octets 2(lg & 1),
         // +1).  The octet's eight sign bits come from a 128-word table (the
@@ -1544,6 +1566,35 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
               for (int rr = 0; rr < 4; ++rr)
                 acc[m][b][rr] = __builtin_fmaf(dd[b][1], t1[rr], __builtin_fmaf(dd[b][0], t0[rr], acc[m][b][rr]));
             }
+          }
+        }
+        return;
+      }
+      if constexpr (F8) {
+        // chunk order: lane group lg takes chunk lg (values 16 lg .. +15) of
+        // row lr; the E4M3 values enter the MFMAs exactly and the block scale
+        // multiplies the tile's fp32 partial sums
+        u4_t cc[RNB][2];
+        float fs[RNB];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          const u4_t v = *(const u4_t*)((const uint8_t*)Bs + b * 1024 + 256 * lg + 16 * lr);
+          const u2_t p0 = fp8x4_pairs<ACT_F16>(v[0]), p1 = fp8x4_pairs<ACT_F16>(v[1]);
+          const u2_t p2 = fp8x4_pairs<ACT_F16>(v[2]), p3 = fp8x4_pairs<ACT_F16>(v[3]);
+          cc[b][0] = u4_t{p0[0], p0[1], p1[0], p1[1]};
+          cc[b][1] = u4_t{p2[0], p2[1], p3[0], p3[1]};
+          fs[b] = fsc[b][kt >> 1];
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            f4_t t = mfma(a0, __builtin_bit_cast(h8_t, cc[b][0]), f4_t{0, 0, 0, 0});
+            t = mfma(a1, __builtin_bit_cast(h8_t, cc[b][1]), t);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[m][b][rr] = __builtin_fmaf(fs[b], t[rr], acc[m][b][rr]);
           }
         }
         return;
@@ -1977,6 +2028,12 @@ void qmm_q6k_ring_kernel(GemmArgs g) {
   ring_body<QMOE_Q6_K, ACT_F16, EPI>(g);
 }
 
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_fp8_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_FP8, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -2041,6 +2098,25 @@ static void launch_q6k_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+// Whether the LDS-ring FP8 kernel takes this call (fp16 activations; K code
+// bytes per row).
+static bool f8_ring_ok(const GemmArgs& g, int act, int epi) {
+  if (act != QMOE_F16) return false;
+  if (g.N * g.K >= (1ll << 31)) return false;
+  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
+  return true;
+}
+
+static void launch_f8_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -2141,7 +2217,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   const bool mx_ring = w->fmt == QMOE_MXFP4 && mx_ring_ok(g, act, epi);
   const bool q4k_ring = w->fmt == QMOE_Q4_K && mx_ring_ok(g, act, epi);
   const bool q6k_ring = w->fmt == QMOE_Q6_K && mx_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring ||
+  const bool f8_ring = w->fmt == QMOE_FP8 && f8_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring || f8_ring ||
       (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
@@ -2159,6 +2236,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     else if (mx_ring) launch_mx_ring(g, epi, s);
     else if (q4k_ring) launch_q4k_ring(g, epi, s);
     else if (q6k_ring) launch_q6k_ring(g, epi, s);
+    else if (f8_ring) launch_f8_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;

@@ -1,5 +1,5 @@
 """GPU checks of the split units of the LDS-ring gathered matmul (int4, and
-IQ2_XXS, Q2_K, MXFP4, Q4_K and Q6_K with fp16 activations).
+IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K and FP8 with fp16 activations).
 
 With a routing plan of at least 2048 pairs (which carries a work-balancing
 area), the ring kernel looks at each XCD's units (tiles x, x + 8,
@@ -24,7 +24,8 @@ units are split:
     the MXFP4 one (SwiGLU, scales folded into the fp16 operands) and the
     Q4_K one (SwiGLU, parts starting inside a super-block) and the Q6_K one
     (STORE into fp32; a part starting on an odd tile loads its pair's top
-    bits itself) against the fp64 oracle;
+    bits itself) and the FP8 one (STORE into fp32, parts starting inside a
+    128-value scale block) against the fp64 oracle;
   * two calls give bit-identical outputs (the parts are summed in a fixed
     order whichever finishes last);
   * the plan's tickets are zero after every call.
@@ -247,6 +248,26 @@ def test_split_units_q6_k_store_f16():
     x = synth.activations(rng, T, K, "f16")
     ids, w = synth.routing_softmax(rng, T, E, k)
     W = synth.q6_k(rng, E, N, K)
+    plan, v = _plan(ids, T, k, E, n_nt=N // 256, KT=K // 64)
+    dw = upload(W)
+    xd = torch_act(x, "f16")
+    y1 = qm.moe_gather_qmm(dw, plan, T, k, xd, epilogue=qm.EPI_STORE, out_dtype=qm.F32)
+    y2 = qm.moe_gather_qmm(dw, plan, T, k, xd, epilogue=qm.EPI_STORE, out_dtype=qm.F32)
+    torch.cuda.synchronize()
+    _tickets_zero(plan, T, k, E)
+    assert torch.equal(y1, y2)
+    srt = v["sorted"].cpu().numpy()
+    yref = _pair_rows(oracle.act_to_f64(x, "f16"), ids, W)[srt]
+    err = normwise_err(to_f64(y1), yref, "f32")
+    assert err <= TOL, (err, report(to_f64(y1), yref))
+
+
+def test_split_units_fp8_store_f16():
+    N, K, T, E, k = 2048, 1280, 512, 64, 8
+    rng = np.random.default_rng(12)
+    x = synth.activations(rng, T, K, "f16")
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    W = synth.fp8(rng, E, N, K)
     plan, v = _plan(ids, T, k, E, n_nt=N // 256, KT=K // 64)
     dw = upload(W)
     xd = torch_act(x, "f16")
