@@ -654,7 +654,7 @@ def summarize_stats(run_dir, name, command, note, out_dir):
         short = k if len(k) < 90 else k[:87] + "..."
         lines.append(f"| `{short}` | {len(v)} | {v[len(v) // 2]:.1f} | {sum(v) / len(v):.1f} | {v[0]:.1f} | "
                      f"{v[-1]:.1f} | {100 * sum(v) / total:.2f} |")
-    lines += ["", "Template arguments: `qmm_int4_kernel<act, epilogue>`, `qmm_iq2_ring_kernel<epilogue>` and `qmm_q2k_ring_kernel<epilogue>` (fp16), "
+    lines += ["", "Template arguments: `qmm_int4_kernel<act, epilogue>`, `qmm_{iq2,q2k,mxfp4,q4k,q6k,fp8}_ring_kernel<epilogue>` (fp16), "
               "`qmm_kernel<format, act, epilogue>`, "
               "`gemv_int4_split_kernel<act, epilogue>`: act 0 = fp16, 1 = bf16; epilogue 0 = STORE, 1 = SWIGLU, "
               "2 = WEIGHTED_COMBINE, 3 = ACCUMULATE; format 0 = Q8_0, 1 = Q2_K, 2 = IQ2_XXS, 3 = int4, 4 = MXFP4, "
