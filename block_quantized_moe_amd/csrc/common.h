@@ -47,6 +47,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
+// Two fp32 values -> two fp16 (HALF) or bf16 values in one word (a in the
+// low half), each rounded to nearest even from its fp32 value by the packed
+// hardware conversion.  The empty asm keeps the compiler from fusing a
+// producing multiply into a mixed-precision conversion that would round once.
+template <bool HALF>
+__device__ __forceinline__ uint32_t f32x2_to_16(float a, float b) {
+  asm("" : "+v"(a), "+v"(b));
+  if constexpr (HALF) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, b2_t));
+}
 __device__ __forceinline__ void store_out(void* out, int dtype, int64_t i, float v) {
   if (dtype == QMOE_F32) ((float*)out)[i] = v;
   else if (dtype == QMOE_F16) ((uint16_t*)out)[i] = f32_to_f16(v);

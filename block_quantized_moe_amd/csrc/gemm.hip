@@ -844,7 +844,9 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
 #pragma unroll
       for (int h = 0; h < (swiglu ? 1 : 2); ++h) {
         __syncthreads();  // the K loop (or the previous pass) is done with the tile
-        if (swiglu || (wave >> 1) == h) {
+        // two values per packed conversion: the wave's column blocks in pairs
+        auto stage_rows = [&](auto half_c) {
+          constexpr bool HALF = decltype(half_c)::value;
 #pragma unroll
           for (int m = 0; m < MBV; ++m) {
             if (m >= c.mbn) break;
@@ -852,18 +854,24 @@ __device__ __forceinline__ void qmm_body(const GemmArgs& g, const TileCtx& c) {
             for (int r = 0; r < 4; ++r) {
               uint16_t* dst = (uint16_t*)(stg + (16 * m + 4 * lg + r) * LROW);
               if constexpr (swiglu) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                  const float v = silu_f32(acc[m][j][r]) * acc[m][2 + j][r];
-                  dst[32 * wave + 16 * j + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
-                }
+                const uint32_t p = f32x2_to_16<HALF>(silu_f32(acc[m][0][r]) * acc[m][2][r],
+                                                   silu_f32(acc[m][1][r]) * acc[m][3][r]);
+                dst[32 * wave + lr] = (uint16_t)p;
+                dst[32 * wave + 16 + lr] = (uint16_t)(p >> 16);
               } else {
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                  dst[64 * (wave & 1) + 16 * b + lr] = half ? f32_to_f16(acc[m][b][r]) : f32_to_bf16(acc[m][b][r]);
+                for (int b = 0; b < NB; b += 2) {
+                  const uint32_t p = f32x2_to_16<HALF>(acc[m][b][r], acc[m][b + 1][r]);
+                  dst[64 * (wave & 1) + 16 * b + lr] = (uint16_t)p;
+                  dst[64 * (wave & 1) + 16 * (b + 1) + lr] = (uint16_t)(p >> 16);
+                }
               }
             }
           }
+        };
+        if (swiglu || (wave >> 1) == h) {
+          if (half) stage_rows(std::true_type{});
+          else stage_rows(std::false_type{});
         }
         __syncthreads();
         for (int i = tid; i < c.nrows * (HW / 8); i += 256) {
@@ -1912,26 +1920,36 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
         constexpr int CPR = W / 8;               // 16-byte pieces per row
         constexpr int LROW = 2 * W + 16;         // LDS row stride in bytes
         static_assert(BM * LROW <= RS * STAGE, "output tile fits in the ring");
-        const bool half = (g.out_dtype == QMOE_F16);
         ring_barrier();  // every wave is done with the ring
+        // two values per packed conversion: SwiGLU rows rr and rr + 1, STORE
+        // the wave's two column blocks of one row
+        auto stage_rows = [&](auto half_c) {
+          constexpr bool HALF = decltype(half_c)::value;
+          constexpr int LR16 = LROW / 2;
 #pragma unroll
-        for (int m = 0; m < MBV; ++m) {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int row = 16 * m + 4 * lg + rr;
-            uint16_t* dst = (uint16_t*)(ring + row * LROW);
+          for (int m = 0; m < MBV; ++m) {
+            uint16_t* dst = (uint16_t*)(ring + (16 * m + 4 * lg) * LROW);
             if constexpr (swiglu) {
-              const float v = silu_f32(acc[m][0][rr]) * acc[m][1][rr];
-              dst[16 * wave + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
-            } else {
 #pragma unroll
-              for (int b = 0; b < RNB; ++b) {
-                const float v = acc[m][b][rr];
-                dst[32 * wave + 16 * b + lr] = half ? f32_to_f16(v) : f32_to_bf16(v);
+              for (int rr = 0; rr < 4; rr += 2) {
+                const uint32_t p = f32x2_to_16<HALF>(silu_f32(acc[m][0][rr]) * acc[m][1][rr],
+                                                   silu_f32(acc[m][0][rr + 1]) * acc[m][1][rr + 1]);
+                dst[rr * LR16 + 16 * wave + lr] = (uint16_t)p;
+                dst[(rr + 1) * LR16 + 16 * wave + lr] = (uint16_t)(p >> 16);
+              }
+            } else {
+              static_assert(RNB == 2, "two column blocks per wave");
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const uint32_t p = f32x2_to_16<HALF>(acc[m][0][rr], acc[m][1][rr]);
+                dst[rr * LR16 + 32 * wave + lr] = (uint16_t)p;
+                dst[rr * LR16 + 32 * wave + 16 + lr] = (uint16_t)(p >> 16);
               }
             }
           }
-        }
+        };
+        if (g.out_dtype == QMOE_F16) stage_rows(std::true_type{});
+        else stage_rows(std::false_type{});
         ring_barrier();
         const int64_t nlim = swiglu ? Nh : g.N;
         for (int i = tid; i < nrows * CPR; i += RW * 64) {
