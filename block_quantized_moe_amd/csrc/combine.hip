@@ -31,12 +31,9 @@ __global__ __launch_bounds__(256) void combine_cast_kernel(float* __restrict__ a
     ((f4_t*)acc)[i] = f4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (OUT == QMOE_F32) {
       ((f4_t*)out)[i] = v;
-    } else if constexpr (OUT == QMOE_F16) {
-      ((u2_t*)out)[i] = u2_t{(uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16),
-                             (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16)};
     } else {
-      ((u2_t*)out)[i] = u2_t{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                             (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+      constexpr bool HALF = (OUT == QMOE_F16);
+      ((u2_t*)out)[i] = u2_t{f32x2_to_16<HALF>(v[0], v[1]), f32x2_to_16<HALF>(v[2], v[3])};
     }
   }
 }
@@ -157,11 +154,12 @@ __global__ __launch_bounds__(256) void moe_combine_vec_kernel(const void* __rest
     ((f4_t*)out)[o / 4 + 1] = f4_t{acc[4], acc[5], acc[6], acc[7]};
   } else {
     u4_t r;
+    if (out_dtype == QMOE_F16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = out_dtype == QMOE_F16 ? f32_to_f16(acc[2 * i]) : f32_to_bf16(acc[2 * i]);
-      const uint32_t hi = out_dtype == QMOE_F16 ? f32_to_f16(acc[2 * i + 1]) : f32_to_bf16(acc[2 * i + 1]);
-      r[i] = lo | (hi << 16);
+      for (int i = 0; i < 4; ++i) r[i] = f32x2_to_16<true>(acc[2 * i], acc[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = f32x2_to_16<false>(acc[2 * i], acc[2 * i + 1]);
     }
     ((u4_t*)out)[o / 8] = r;
   }

@@ -69,7 +69,9 @@ __device__ __forceinline__ void store_out_t(void* out, int64_t i, float v) {
   else ((uint16_t*)out)[i] = f32_to_bf16(v);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exponential and reciprocal
+// (each within about an ulp) instead of an IEEE division sequence
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
 // Element i of an f32 / f16 / bf16 array.
 __device__ __forceinline__ float load_act(const void* p, int dtype, int64_t i) {
