@@ -1187,18 +1187,22 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   constexpr bool Q4K = (FMT == QMOE_Q4_K);
   constexpr bool Q6K = (FMT == QMOE_Q6_K);
   constexpr bool F8 = (FMT == QMOE_FP8);
-  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K || Q6K || F8) && !BF),
-                "ring formats: int4, and IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K, FP8 with fp16 activations");
+  constexpr bool Q8 = (FMT == QMOE_Q8_0);
+  static_assert(FMT == QMOE_INT4 || ((IQ2 || Q2K || MX || Q4K || Q6K || F8 || Q8) && !BF),
+                "ring formats: int4, and IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K, FP8, Q8_0 with fp16 activations");
   // weight codes per wave and stage (FP8: two 1 KB blocks), then metadata: one
   // 64-lane dword load (Q4_K: two; FP8: none, its block scales are
   // wave-uniform and come by scalar loads).  NMETA + 1 loads per wave and
   // tile besides the activation chunks.
-  constexpr int BW = F8 ? 2048 : 1024;
+  constexpr int BW = (F8 || Q8) ? 2048 : 1024;
   constexpr int RBB = RW * BW;
   constexpr int NMETA = Q4K ? 2 : 1;
   constexpr int SBW = F8 ? 0 : 256 * NMETA;
   constexpr int STAGE = R_A + RBB + RW * SBW;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[RS * STAGE];
+  // Q8_0's 28 KB stages fit two workgroups per CU only as two stages (one
+  // tile in flight while one is computed); the others keep three
+  constexpr int NST = Q8 ? 2 : RS;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NST * STAGE];
   __shared__ int rows_a[BM];
   __shared__ int rows_o[BM];
   __shared__ float wts[BM];
@@ -1302,7 +1306,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // int4 (group >= 64): tile kt lies in scale group kt >> gsh; IQ2_XXS and
   // Q2_K: in super-block kt >> 2; MXFP4: the tile holds two 32-value blocks
   // (its own 32 exponent bytes per 16-row block)
-  const int gsh = (IQ2 || Q2K || Q4K || Q6K) ? 2 : MX ? 0 : __builtin_ctz((unsigned)g.group) - 6;
+  const int gsh = (IQ2 || Q2K || Q4K || Q6K) ? 2 : (MX || Q8) ? 0 : __builtin_ctz((unsigned)g.group) - 6;
   const int64_t K = g.K;
   const int T = KT, G = T >> gsh;
 
@@ -1330,7 +1334,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // halves.  The base (block
   // 0's run) is wave-uniform and lives in SGPRs; each lane adds a 32-bit byte
   // offset (block 1's run lies at most one expert's codes further)
-  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : F8 ? 1024 : 512, SRUN = (IQ2 || MX) ? 32 : 64;
+  constexpr int WRUN = IQ2 ? 256 : Q2K ? 256 : (F8 || Q8) ? 1024 : 512, SRUN = (IQ2 || MX) ? 32 : 64;
   const int64_t rb0 = ((int64_t)expert * g.N + block_base(0)) >> 4;
   const int64_t rb1 = ((int64_t)expert * g.N + block_base(1)) >> 4;
   const uint8_t* wbase = (const uint8_t*)g.qs + rb0 * T * WRUN;
@@ -1382,10 +1386,12 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
   // FP8: a 16-row block's codes of a tile are 1 KB (the Q8_0 tiling), one
   // 16-byte load per lane and block; the block's scale (its 128 x 128 scale
   // block's) by a scalar load per tile
+  // (Q8_0 takes the same two code loads; its fp16 scales, 64 bytes per block
+  // and tile, come as int4's scale words do)
   uint32_t woff2 = 0;
+  if constexpr (F8 || Q8) woff2 = (uint32_t)((rb1 - rb0) * T * 1024 + lane * 16);
   const __attribute__((address_space(4))) float* fsc[RNB] = {nullptr, nullptr};
   if constexpr (F8) {
-    woff2 = (uint32_t)((rb1 - rb0) * T * 1024 + lane * 16);
 #pragma unroll
     for (int b = 0; b < RNB; ++b) {
       const int64_t si = (((int64_t)expert * g.N + block_base(b)) >> 7) * (K >> 7);
@@ -1434,9 +1440,10 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
     if constexpr (Q2K) {
       dma_glb16_s(wbase + (int64_t)(kt >> 1) * 512, woff, st + R_A + wave * BW);
       dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + RBB + wave * SBW);
-    } else if constexpr (F8) {
+    } else if constexpr (F8 || Q8) {
       dma_glb16_s(wbase + (int64_t)kt * WRUN, (uint32_t)lane * 16, st + R_A + wave * BW);
       dma_glb16_s(wbase + (int64_t)kt * WRUN, woff2, st + R_A + wave * BW + 1024);
+      if constexpr (Q8) dma_glb4_s(sbase + (int64_t)kt * SRUN, soff, st + R_A + RBB + wave * SBW);
     } else if constexpr (Q6K) {
       dma_glb16_s(wbase + (int64_t)kt * WRUN, woff, st + R_A + wave * BW);
       dma_glb4(mptr + (uint32_t)(kt >> 2) * mstride + (uint32_t)(kt & 3) * minc, st + R_A + RBB + wave * SBW);
@@ -1574,6 +1581,30 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
               for (int rr = 0; rr < 4; ++rr)
                 acc[m][b][rr] = __builtin_fmaf(dd[b][1], t1[rr], __builtin_fmaf(dd[b][0], t0[rr], acc[m][b][rr]));
             }
+          }
+        }
+        return;
+      }
+      if constexpr (Q8) {
+        // chunk order: lane group lg takes chunk lg (values 16 lg .. +15) of
+        // row lr and the d of its 32-value block lg >> 1
+        const uint16_t* Dh = (const uint16_t*)Ss;  // [block][32-value block][row] fp16 d
+        u4_t bf[RNB][2];
+#pragma unroll
+        for (int b = 0; b < RNB; ++b) {
+          Raw rw;
+          rw.v = *(const u4_t*)((const uint8_t*)Bs + b * 1024 + 256 * lg + 16 * lr);
+          rw.x0 = Dh[b * 32 + (lg >> 1) * 16 + lr];
+          frag_f16<QMOE_Q8_0>(rw, lg, nullptr, nullptr, bf[b][0], bf[b][1]);
+        }
+#pragma unroll
+        for (int m = 0; m < MBV; ++m) {
+          const h8_t a0 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a0 + 128 * m)));
+          const h8_t a1 = __builtin_bit_cast(h8_t, *(const u4_t*)(As + 8 * (slot_a1 + 128 * m)));
+#pragma unroll
+          for (int b = 0; b < RNB; ++b) {
+            acc[m][b] = mfma(a0, __builtin_bit_cast(h8_t, bf[b][0]), acc[m][b]);
+            acc[m][b] = mfma(a1, __builtin_bit_cast(h8_t, bf[b][1]), acc[m][b]);
           }
         }
         return;
@@ -1785,6 +1816,22 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
       for (int i = tid; i < XG4 * BM; i += RW * 64) xg[i] = 0.f;
     }
     const int nk = ke - kb;
+    if constexpr (NST == 2) {  // one tile in flight: wait for it, then refill the other stage
+      if (nk > 0) issue(kb, 0, true);
+      int sc = 0;
+      for (int kt = kb; kt + 1 < ke; ++kt) {
+        wait_vmcnt<0>();
+        ring_barrier();
+        issue(kt + 1, sc ^ 1, false);
+        compute(kt, sc);
+        sc ^= 1;
+      }
+      if (nk > 0) {
+        wait_vmcnt<0>();
+        ring_barrier();
+        compute(ke - 1, sc);
+      }
+    } else {
     if (nk > 0) issue(kb, 0, true);
     if (nk > 1) issue(kb + 1, 1, false);
     int sc = 0;
@@ -1805,6 +1852,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
       wait_vmcnt<0>();
       ring_barrier();
       compute(ke - 1, sc);
+    }
     }
 
     // ---- bf16 bias term: sum_g (b - 128 s)[n, g] * X[m, g] by MFMA with hi/lo
@@ -1919,7 +1967,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& g) {
         constexpr int W = swiglu ? BN / 2 : BN;  // output columns per workgroup
         constexpr int CPR = W / 8;               // 16-byte pieces per row
         constexpr int LROW = 2 * W + 16;         // LDS row stride in bytes
-        static_assert(BM * LROW <= RS * STAGE, "output tile fits in the ring");
+        static_assert(BM * LROW <= NST * STAGE, "output tile fits in the ring");
         ring_barrier();  // every wave is done with the ring
         // two values per packed conversion: SwiGLU rows rr and rr + 1, STORE
         // the wave's two column blocks of one row
@@ -2052,6 +2100,12 @@ void qmm_fp8_ring_kernel(GemmArgs g) {
   ring_body<QMOE_FP8, ACT_F16, EPI>(g);
 }
 
+template <int EPI>
+__global__ __launch_bounds__(RW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void qmm_q8_ring_kernel(GemmArgs g) {
+  ring_body<QMOE_Q8_0, ACT_F16, EPI>(g);
+}
+
 // Whether the LDS-ring int4 kernel takes this call.
 static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
   if (g.group < 64) return false;
@@ -2119,8 +2173,8 @@ static void launch_q6k_ring(const GemmArgs& g, int epi, hipStream_t s) {
   }
 }
 
-// Whether the LDS-ring FP8 kernel takes this call (fp16 activations; K code
-// bytes per row).
+// Whether the LDS-ring FP8 or Q8_0 kernel takes this call (fp16 activations;
+// K code bytes per row).
 static bool f8_ring_ok(const GemmArgs& g, int act, int epi) {
   if (act != QMOE_F16) return false;
   if (g.N * g.K >= (1ll << 31)) return false;
@@ -2135,6 +2189,16 @@ static void launch_f8_ring(const GemmArgs& g, int epi, hipStream_t s) {
     case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
     case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
     default: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+  }
+}
+
+static void launch_q8_ring(const GemmArgs& g, int epi, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(RW * 64);
+  switch (epi) {
+    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
+    default: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
   }
 }
 
@@ -2236,7 +2300,8 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   const bool q4k_ring = w->fmt == QMOE_Q4_K && mx_ring_ok(g, act, epi);
   const bool q6k_ring = w->fmt == QMOE_Q6_K && mx_ring_ok(g, act, epi);
   const bool f8_ring = w->fmt == QMOE_FP8 && f8_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring || f8_ring ||
+  const bool q8_ring = w->fmt == QMOE_Q8_0 && f8_ring_ok(g, act, epi);
+  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring || f8_ring || q8_ring ||
       (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
@@ -2255,6 +2320,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
     else if (q4k_ring) launch_q4k_ring(g, epi, s);
     else if (q6k_ring) launch_q6k_ring(g, epi, s);
     else if (f8_ring) launch_f8_ring(g, epi, s);
+    else if (q8_ring) launch_q8_ring(g, epi, s);
     else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
     else launch_int4_ring<ACT_BF16>(g, epi, s);
     return;

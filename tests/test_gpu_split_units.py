@@ -1,5 +1,5 @@
 """GPU checks of the split units of the LDS-ring gathered matmul (int4, and
-IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K and FP8 with fp16 activations).
+IQ2_XXS, Q2_K, MXFP4, Q4_K, Q6_K, FP8 and Q8_0 with fp16 activations).
 
 With a routing plan of at least 2048 pairs (which carries a work-balancing
 area), the ring kernel looks at each XCD's units (tiles x, x + 8,
@@ -24,8 +24,9 @@ units are split:
     the MXFP4 one (SwiGLU, scales folded into the fp16 operands) and the
     Q4_K one (SwiGLU, parts starting inside a super-block) and the Q6_K one
     (STORE into fp32; a part starting on an odd tile loads its pair's top
-    bits itself) and the FP8 one (STORE into fp32, parts starting inside a
-    128-value scale block) against the fp64 oracle;
+    bits itself), the FP8 one (STORE into fp32, parts starting inside a
+    128-value scale block) and the two-stage Q8_0 one (SwiGLU) against the
+    fp64 oracle;
   * two calls give bit-identical outputs (the parts are summed in a fixed
     order whichever finishes last);
   * the plan's tickets are zero after every call.
@@ -280,6 +281,26 @@ def test_split_units_fp8_store_f16():
     yref = _pair_rows(oracle.act_to_f64(x, "f16"), ids, W)[srt]
     err = normwise_err(to_f64(y1), yref, "f32")
     assert err <= TOL, (err, report(to_f64(y1), yref))
+
+
+def test_split_units_q8_0_swiglu_f16():
+    N, K, T, E, k = 4096, 1280, 512, 64, 8
+    rng = np.random.default_rng(16)
+    x = synth.activations(rng, T, K, "f16")
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    W = synth.q8_0(rng, E, N, K)
+    plan, v = _plan(ids, T, k, E, n_nt=N // 2 // 128, KT=K // 64)
+    gu = upload(W)
+    xd = torch_act(x, "f16")
+    h1 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    h2 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F16)
+    torch.cuda.synchronize()
+    _tickets_zero(plan, T, k, E)
+    assert torch.equal(h1, h2)
+    srt = v["sorted"].cpu().numpy()
+    href = oracle.moe_gate_up(oracle.act_to_f64(x, "f16"), ids, W)[srt]
+    err = normwise_err(to_f64(h1), href, "f16")
+    assert err <= TOL, (err, report(to_f64(h1), href))
 
 
 def test_model_of_the_split_rule():
