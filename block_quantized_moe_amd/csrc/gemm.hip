@@ -2106,121 +2106,54 @@ void qmm_q8_ring_kernel(GemmArgs g) {
   ring_body<QMOE_Q8_0, ACT_F16, EPI>(g);
 }
 
-// Whether the LDS-ring int4 kernel takes this call.
-static bool int4_ring_ok(const GemmArgs& g, int act, int epi) {
-  if (g.group < 64) return false;
-  if (g.N * g.K / 2 >= (1ll << 31)) return false;  // per-lane byte offsets within one expert's codes
+// Whether the LDS-ring kernel takes this call: int4 with either activation
+// type (groups of at least 64 values; bf16 keeps at most XG4 groups per row
+// for the bias term), every other format with fp16 activations.  N must be
+// whole 16-row blocks (32 with SwiGLU), and the per-lane byte offsets within
+// one expert's codes must fit 31 bits.
+static bool ring_ok(const GemmArgs& g, int fmt, int act, int epi) {
   if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
-  if (act == QMOE_BF16 && g.K / g.group > XG4) return false;
-  return true;
+  if (fmt != QMOE_INT4 && act != QMOE_F16) return false;
+  int64_t row_bytes;  // code bytes per weight row
+  switch (fmt) {
+    case QMOE_INT4:
+      if (g.group < 64 || (act == QMOE_BF16 && g.K / g.group > XG4)) return false;
+      row_bytes = g.K / 2;
+      break;
+    case QMOE_IQ2_XXS: case QMOE_Q2_K: row_bytes = g.K / 4; break;
+    case QMOE_MXFP4: case QMOE_Q4_K: case QMOE_Q6_K: row_bytes = g.K / 2; break;
+    case QMOE_FP8: case QMOE_Q8_0: row_bytes = g.K; break;
+    default: return false;
+  }
+  return g.N * row_bytes < (1ll << 31);
 }
 
-// Whether the LDS-ring IQ2_XXS or Q2_K kernel takes this call (fp16
-// activations; both keep K/4 code bytes per row).
-static bool k256_ring_ok(const GemmArgs& g, int act, int epi) {
-  if (act != QMOE_F16) return false;
-  if (g.N * g.K / 4 >= (1ll << 31)) return false;  // per-lane byte offsets within one expert's codes
-  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
-  return true;
-}
+using KernelFn = void (*)(GemmArgs);
 
-static void launch_iq2_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_iq2_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+// The ring kernel of a format and epilogue.
+template <int EPI>
+static KernelFn ring_kernel(int fmt, int act) {
+  switch (fmt) {
+    case QMOE_IQ2_XXS: return qmm_iq2_ring_kernel<EPI>;
+    case QMOE_Q2_K: return qmm_q2k_ring_kernel<EPI>;
+    case QMOE_MXFP4: return qmm_mxfp4_ring_kernel<EPI>;
+    case QMOE_Q4_K: return qmm_q4k_ring_kernel<EPI>;
+    case QMOE_Q6_K: return qmm_q6k_ring_kernel<EPI>;
+    case QMOE_FP8: return qmm_fp8_ring_kernel<EPI>;
+    case QMOE_Q8_0: return qmm_q8_ring_kernel<EPI>;
+    default: return act == QMOE_F16 ? qmm_int4_kernel<ACT_F16, EPI> : qmm_int4_kernel<ACT_BF16, EPI>;
   }
 }
 
-// Whether the LDS-ring MXFP4, Q4_K or Q6_K kernel takes this call (fp16
-// activations; K/2 code bytes per row in qs, as int4).
-static bool mx_ring_ok(const GemmArgs& g, int act, int epi) {
-  if (act != QMOE_F16) return false;
-  if (g.N * g.K / 2 >= (1ll << 31)) return false;
-  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
-  return true;
-}
-
-static void launch_mx_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
+static void launch_ring(const GemmArgs& g, int fmt, int act, int epi, hipStream_t s) {
+  KernelFn k;
   switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_mxfp4_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
+    case QMOE_EPI_STORE: k = ring_kernel<QMOE_EPI_STORE>(fmt, act); break;
+    case QMOE_EPI_SWIGLU: k = ring_kernel<QMOE_EPI_SWIGLU>(fmt, act); break;
+    case QMOE_EPI_WEIGHTED_COMBINE: k = ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>(fmt, act); break;
+    default: k = ring_kernel<QMOE_EPI_ACCUMULATE>(fmt, act); break;
   }
-}
-
-static void launch_q4k_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_q4k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
-}
-
-static void launch_q6k_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_q6k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
-}
-
-// Whether the LDS-ring FP8 or Q8_0 kernel takes this call (fp16 activations;
-// K code bytes per row).
-static bool f8_ring_ok(const GemmArgs& g, int act, int epi) {
-  if (act != QMOE_F16) return false;
-  if (g.N * g.K >= (1ll << 31)) return false;
-  if (g.N % (epi == QMOE_EPI_SWIGLU ? 32 : 16)) return false;
-  return true;
-}
-
-static void launch_f8_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_fp8_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
-}
-
-static void launch_q8_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_q8_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
-}
-
-static void launch_q2k_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_q2k_ring_kernel<QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
-}
-
-template <int ACT>
-static void launch_int4_ring(const GemmArgs& g, int epi, hipStream_t s) {
-  const dim3 grid(g.n_blocks), block(RW * 64);
-  switch (epi) {
-    case QMOE_EPI_STORE: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_STORE>), grid, block, 0, s, g); break;
-    case QMOE_EPI_SWIGLU: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_SWIGLU>), grid, block, 0, s, g); break;
-    case QMOE_EPI_WEIGHTED_COMBINE: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_WEIGHTED_COMBINE>), grid, block, 0, s, g); break;
-    default: hipLaunchKernelGGL((qmm_int4_kernel<ACT, QMOE_EPI_ACCUMULATE>), grid, block, 0, s, g); break;
-  }
+  hipLaunchKernelGGL(k, dim3(g.n_blocks), dim3(RW * 64), 0, s, g);
 }
 
 template <int FMT, int ACT>
@@ -2294,15 +2227,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
   g.sk_tickets = nullptr;
   g.sk_part = nullptr;
   if (g.n_blocks == 0) return;
-  const bool iq2_ring = w->fmt == QMOE_IQ2_XXS && k256_ring_ok(g, act, epi);
-  const bool q2k_ring = w->fmt == QMOE_Q2_K && k256_ring_ok(g, act, epi);
-  const bool mx_ring = w->fmt == QMOE_MXFP4 && mx_ring_ok(g, act, epi);
-  const bool q4k_ring = w->fmt == QMOE_Q4_K && mx_ring_ok(g, act, epi);
-  const bool q6k_ring = w->fmt == QMOE_Q6_K && mx_ring_ok(g, act, epi);
-  const bool f8_ring = w->fmt == QMOE_FP8 && f8_ring_ok(g, act, epi);
-  const bool q8_ring = w->fmt == QMOE_Q8_0 && f8_ring_ok(g, act, epi);
-  if (iq2_ring || q2k_ring || mx_ring || q4k_ring || q6k_ring || f8_ring || q8_ring ||
-      (w->fmt == QMOE_INT4 && int4_ring_ok(g, act, epi))) {
+  if (ring_ok(g, w->fmt, act, epi)) {
     // Plans of SK_MIN_PAIRS pairs and more carry a balancing area: the units
     // of a short last round are split along K (work_of_block), which needs
     // up to 3 * sx / 4 more workgroups per XCD.
@@ -2314,15 +2239,7 @@ void launch_qmm(const qmoe_weights* w, const void* a, int act, int amode, const 
       g.sk_part = (float*)(sk + SK_SLOTS);
       g.n_blocks += 8 * (3 * g.sk_slots_xcd / 4);
     }
-    if (iq2_ring) launch_iq2_ring(g, epi, s);
-    else if (q2k_ring) launch_q2k_ring(g, epi, s);
-    else if (mx_ring) launch_mx_ring(g, epi, s);
-    else if (q4k_ring) launch_q4k_ring(g, epi, s);
-    else if (q6k_ring) launch_q6k_ring(g, epi, s);
-    else if (f8_ring) launch_f8_ring(g, epi, s);
-    else if (q8_ring) launch_q8_ring(g, epi, s);
-    else if (act == QMOE_F16) launch_int4_ring<ACT_F16>(g, epi, s);
-    else launch_int4_ring<ACT_BF16>(g, epi, s);
+    launch_ring(g, w->fmt, act, epi, s);
     return;
   }
   switch (w->fmt) {
