@@ -173,7 +173,9 @@ def _plan_case(T, k, E, bm, seed, bad=True, skew=False):
 
 @pytest.mark.parametrize("T,k,E,bm,skew", [(300, 8, 64, 80, False), (1, 1, 4, 16, False),
                                            (2048, 8, 256, 64, False), (4096, 8, 256, 48, True),
-                                           (513, 6, 1024, 32, False)])
+                                           (513, 6, 1024, 32, False),
+                                           # 64 and 66 chunks of 1024 pairs, Zipf-skewed
+                                           (8192, 8, 256, 80, True), (8448, 8, 256, 80, True)])
 def test_plan_exact(T, k, E, bm, skew):
     ids = _plan_case(T, k, E, bm, 7 + T, skew=skew)
     ref = oracle.plan(ids, E, bm)
