@@ -732,7 +732,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed steps before the timed ones: on MI355X the kernels keep speeding
+    # up over the first tens of milliseconds of load (C2 step 244 us after 5
+    # steps, 223 after 50, 216 after 200), so the default runs about 65 ms
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--decode-layers", type=int, default=40)
     ap.add_argument("--decode-reps", type=int, default=5)
@@ -823,7 +826,9 @@ def main():
                 continue
             log(f"prefill ({name}): building inputs")
             inp_o = make()
-            res = run_prefill(args, torch, qm, inp_o, R, max(3, args.steps // 4), 2)
+            # a fifth of the warm-up: 60 steps by default (66 ms of the
+            # DSv4-shaped step, 265 ms of the mixed block)
+            res = run_prefill(args, torch, qm, inp_o, R, max(3, args.steps // 4), max(2, args.warmup // 5))
             line_o, rl = prefill_line(name, inp_o, res, R)
             if name == "mixed":
                 imb = imbalance(inp_o)
