@@ -365,9 +365,10 @@ int qmoe_moe_plan(const int32_t* ids, int64_t t, int32_t topk, int32_t n_experts
  * format's block; any n (as qmoe_qmm_dense).  Determinism is chosen by entry
  * point rather than a flag: STORE + qmoe_moe_combine is bit-reproducible,
  * WEIGHTED_COMBINE (atomics) is not.
- * int4 weights, and IQ2_XXS weights with fp16 activations, on a plan with a
- * work-balancing area: when an XCD's (tile,
- * column block) units fill its resident workgroups' rounds plus a short last
+ * int4 weights, and weights of every other format with fp16 activations (N
+ * a multiple of 16, of 32 with SwiGLU), on a plan with a work-balancing area:
+ * when an XCD's (tile, column block) units fill its resident workgroups'
+ * rounds plus a short last
  * round, those last units are split into 4 parts along K that meet through
  * the plan's area (fp32 partial sums added in part order, so the result is
  * the same on every run on the same device; it can differ in the last bits
