@@ -1095,9 +1095,9 @@ constexpr int RNB = 2;                     // 16-row weight blocks per wave
 constexpr int RS = 3;                      // ring stages
 constexpr int R_ACH = BM * 8;              // activation chunks per stage (640)
 constexpr int R_A = R_ACH * 16;            // 10240 B
-constexpr int R_B = RW * RNB * 512;        // 8192 B
-// then the scale / metadata region: 256 bytes per wave (Q4_K: 512), so a
-// stage is 20480 bytes (22528)
+// then per wave the weight codes of its RNB blocks (1 KB; FP8 and Q8_0: 2 KB)
+// and the scale / metadata region (256 bytes; Q4_K 512, FP8 none), so a stage
+// is 20480 bytes for int4 (see ring_body)
 constexpr int XG4 = 32;                    // int4 groups per row kept for the bf16 bias term
 
 // Chunk swizzle of the activation rows in a ring stage (rows 128 bytes

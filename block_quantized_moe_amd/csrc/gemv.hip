@@ -958,13 +958,12 @@ static bool int4_tiled_ok(const GemvArgs& g, int epi) {
 }
 
 template <int ACT, int EPI>
-static void launch_gemv_split(const GemvArgs& g, int waves, hipStream_t s) {
-  static bool attr_set = false;  // raise the dynamic LDS limit once per process
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)gemv_int4_split_kernel<ACT, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    attr_set = true;
-  }
+static int launch_gemv_split(const GemvArgs& g, int waves, hipStream_t s) {
+  // the dynamic LDS limit is raised once per process (a function-local static
+  // is initialised once, also when several threads launch)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)gemv_int4_split_kernel<ACT, EPI>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return QMOE_ERR_LAUNCH;
   constexpr bool CMB = EPI == QMOE_EPI_WEIGHTED_COMBINE;
   const int64_t units = EPI == QMOE_EPI_SWIGLU ? g.N / 2 : g.N;
   const int64_t tokens = g.nslots / g.topk;
@@ -972,14 +971,15 @@ static void launch_gemv_split(const GemvArgs& g, int waves, hipStream_t s) {
   const dim3 grid((unsigned)((units / 16) * (CMB ? tokens : g.nslots)));
   const size_t lds = (size_t)gs_lds_bytes(waves, rows, EPI == QMOE_EPI_SWIGLU ? 2 : 1, CMB);
   hipLaunchKernelGGL((gemv_int4_split_kernel<ACT, EPI>), grid, dim3(waves * 64), lds, s, g, rows);
+  return QMOE_OK;
 }
 
 template <int ACT>
-static void launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
+static int launch_gemv_int4_tiled(const GemvArgs& g, int epi, hipStream_t s) {
   const int w = gs_waves(g, epi);
-  if (epi == QMOE_EPI_WEIGHTED_COMBINE) launch_gemv_split<ACT, QMOE_EPI_WEIGHTED_COMBINE>(g, w, s);
-  else if (epi == QMOE_EPI_SWIGLU) launch_gemv_split<ACT, QMOE_EPI_SWIGLU>(g, w, s);
-  else launch_gemv_split<ACT, QMOE_EPI_STORE>(g, w, s);
+  if (epi == QMOE_EPI_WEIGHTED_COMBINE) return launch_gemv_split<ACT, QMOE_EPI_WEIGHTED_COMBINE>(g, w, s);
+  if (epi == QMOE_EPI_SWIGLU) return launch_gemv_split<ACT, QMOE_EPI_SWIGLU>(g, w, s);
+  return launch_gemv_split<ACT, QMOE_EPI_STORE>(g, w, s);
 }
 
 template <int FMT, int ACT, int CPL, int MT>
@@ -1057,9 +1057,7 @@ int launch_gemv(const qmoe_weights* w, const void* a, int act, int64_t b, const 
   if (upw > 64) upw = 64 > step ? 64 : step;
   g.units_per_wg = (int)upw;
   if (w->fmt == QMOE_INT4 && (chunks & (chunks - 1)) == 0 && int4_tiled_ok(g, epi)) {
-    if (act == QMOE_F16) launch_gemv_int4_tiled<ACT_F16>(g, epi, s);
-    else launch_gemv_int4_tiled<ACT_BF16>(g, epi, s);
-    return QMOE_OK;
+    return act == QMOE_F16 ? launch_gemv_int4_tiled<ACT_F16>(g, epi, s) : launch_gemv_int4_tiled<ACT_BF16>(g, epi, s);
   }
   switch (w->fmt) {
     case QMOE_Q8_0: launch_gemv_f<QMOE_Q8_0>(g, act, cpl, epi, units, s); break;
