@@ -6,7 +6,8 @@ on sampled outputs that the fp64 oracle computes one by one:
   * Qwen3.6-A3B-shaped int4 prefill: T = 2048, H = 2048, E = 256, I = 512, k = 8
   * DSv4-flash-shaped prefill: T = 2048, H = 4096, E = 256, I = 2048, k = 6,
     IQ2_XXS gate/up, Q2_K down, fp16 activations; the same shapes with MXFP4
-    experts and with FP8 E4M3 block experts
+    experts, with FP8 E4M3 block experts and with Q4_K gate/up and Q6_K down
+    (k-quant oracle parity unpinned)
   * mixed-format FFN block: T = 8192, H = 4096, E = 256, I = 2048, k = 8, Zipf
     routing, plus a Q8_0 shared expert and four Q8_0 4096 x 4096 projections,
     bf16 combine output
@@ -104,10 +105,10 @@ def test_fullsize_qwen_a3b_int4_prefill():
     _check_end_to_end(inp, out, rng, 16)
 
 
-@pytest.mark.parametrize("experts", ["iq2_xxs/q2_k", "mxfp4", "fp8"])
+@pytest.mark.parametrize("experts", ["iq2_xxs/q2_k", "mxfp4", "fp8", "q4_k/q6_k"])
 def test_fullsize_dsv4_flash_prefill(experts):
     make = {"iq2_xxs/q2_k": synth.dsv4_flash_prefill, "mxfp4": synth.dsv4_flash_mxfp4_prefill,
-            "fp8": synth.dsv4_flash_fp8_prefill}[experts]
+            "fp8": synth.dsv4_flash_fp8_prefill, "q4_k/q6_k": synth.dsv4_flash_kquant_prefill}[experts]
     inp = make(2048)
     rng = np.random.default_rng(102)
     x, plan, h, out = _run_moe(inp)
