@@ -21,7 +21,8 @@ units are split:
   * the IQ2_XXS ring kernel (fp16 activations, SwiGLU, K = 1280: parts start
     inside a 256-value super-block) and the Q2_K one (STORE into fp32, parts
     starting on the odd tile of a pair that shares a 512-byte code half) and
-    the MXFP4 one (SwiGLU, scales folded into the fp16 operands) and the
+    the MXFP4 one (SwiGLU, scales folded into the fp16 operands, and with
+    every exponent out of that range, the fp32-scale loop) and the
     Q4_K one (SwiGLU, parts starting inside a super-block) and the Q6_K one
     (STORE into fp32; a part starting on an odd tile loads its pair's top
     bits itself), the FP8 one (STORE into fp32, parts starting inside a
@@ -220,6 +221,30 @@ def test_split_units_mxfp4_swiglu_f16():
     srt = v["sorted"].cpu().numpy()
     href = oracle.moe_gate_up(oracle.act_to_f64(x, "f16"), ids, W)[srt]
     err = normwise_err(to_f64(h1), href, "f16")
+    assert err <= TOL, (err, report(to_f64(h1), href))
+
+
+def test_split_units_mxfp4_unfolded_scales():
+    # every block exponent at 2^-14, below the range the fp16 operands can
+    # carry exactly: each workgroup runs the fp32-scale loop, split parts too
+    # (SwiGLU into fp32, where the small products keep full precision)
+    N, K, T, E, k = 4096, 1280, 512, 64, 8
+    rng = np.random.default_rng(16)
+    x = synth.activations(rng, T, K, "f16")
+    ids, w = synth.routing_softmax(rng, T, E, k)
+    W = synth.mxfp4(rng, E, N, K)
+    W.blocks[..., 0] = 113
+    plan, v = _plan(ids, T, k, E, n_nt=N // 2 // 128, KT=K // 64)
+    gu = upload(W)
+    xd = torch_act(x, "f16")
+    h1 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F32)
+    h2 = qm.moe_gather_qmm(gu, plan, T, k, xd, epilogue=qm.EPI_SWIGLU, out_dtype=qm.F32)
+    torch.cuda.synchronize()
+    _tickets_zero(plan, T, k, E)
+    assert torch.equal(h1, h2)
+    srt = v["sorted"].cpu().numpy()
+    href = oracle.moe_gate_up(oracle.act_to_f64(x, "f16"), ids, W)[srt]
+    err = normwise_err(to_f64(h1), href, "f32")
     assert err <= TOL, (err, report(to_f64(h1), href))
 
 
